@@ -1,0 +1,263 @@
+"""Throughput of the masked second-order HLA forward on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the chunk-parallel forward over the whole workload:
+segment summaries -> exclusive Blelloch scan -> outputs (three C-ABI calls
+on one stream; inputs already resident in HBM).  The decode workload times
+one streaming decode step for every (sequence, head).  Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HLA fwd tokens/s (B·H·T/s) at 1 MI355X; % MFMA peak (chunk) / % HBM peak (decode)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "fwd_decay_bf16_b4h16t16384d128"
+
+
+def credited_flops_per_token(c, d, dv):
+    """Credited (algorithmic) flops per token of the masked chunk algorithm at
+    chunk length c: exact multiply-adds x 2 with triangles and the symmetry of
+    K^T K exploited, one combine per chunk."""
+    f = (c * d * (d + 1) + 2 * c * d * dv + 2 * c * c * d + c * (c - 1) * dv + 2 * c * d * dv
+         + 2 * d * d * dv + 2 * c * d * d + c * (c + 1) * d + c * (c + 1) * (c + 2) / 3
+         + c * (c + 1) * dv + min(2 * d * d * dv + 2 * c * d * dv, 4 * c * d * dv))
+    return f / c
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--chunk", type=int, default=0, help="override the segment length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens per unit in the oracle sample (forward workloads)")
+    return ap.parse_args()
+
+
+def cpu_baseline_fwd(inp, ntok):
+    """The oracle's serial recurrence on a bounded sample: every unit, first ntok tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import hla_oracle as O
+    uq, uk, uv, ug = inp.units()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.serial(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
+        dt = time.perf_counter() - t0
+    U = uq.shape[0]
+    return {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 serial recurrence, all {U} (batch, head) units, first {ntok} of "
+                      f"{uq.shape[1]} tokens ({dt:.1f} s)", "seconds": round(dt, 2)}
+
+
+def cpu_baseline_decode(states64, toks, steps):
+    from threadpoolctl import threadpool_limits
+    from oracle import hla_oracle as O
+    U = toks[0][0].shape[0]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        st = states64
+        for s in range(steps):
+            _, _, st = O.decode_step(st, *toks[s])
+        dt = time.perf_counter() - t0
+    return {"value": U * steps / dt, "unit": "unit-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 decode steps, {U} units x {steps} steps ({dt:.1f} s)",
+            "seconds": round(dt, 2)}
+
+
+def bench_fwd(args, torch, np):
+    from causal_prefix_scan_amd import hla, synth
+    cfg = dict(synth.FWD_WORKLOADS[args.workload])
+    if args.chunk:
+        cfg["chunk"] = args.chunk
+    B, H, T, d, dv, chunk = (cfg[x] for x in ("B", "H", "T", "d", "dv", "chunk"))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"],
+                                k_l2norm=cfg["k_l2norm"], decay=cfg["decay"])
+    if cfg["dtype"] == "bf16":
+        cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+        q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(x).cuda() for x in (inp.q, inp.k, inp.v))
+    g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
+    dcode = hla.HLA_BF16 if cfg["dtype"] == "bf16" else hla.HLA_F32
+    n = T // chunk
+    summ = hla.alloc_state((B, H, n), d, dv, "cuda")
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
+    den = torch.empty(B, H, T, dtype=torch.float32, device="cuda") if cfg["normalize"] else None
+
+    import ctypes
+    L = hla.lib()
+    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
+    st = hla._state_struct(summ)
+    ws_bytes = L.hla_scan_workspace_bytes(ctypes.byref(p))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
+        if ev:
+            ev[1].record(stream)
+        r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
+        if ev:
+            ev[2].record(stream)
+        r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
+                              ptr(den), None, ctypes.c_size_t(0), sp)
+        if ev:
+            ev[3].record(stream)
+        if r1 or r2 or r3:
+            raise RuntimeError(f"HLA call failed: {r1} {r2} {r3}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1 = [e[0].elapsed_time(e[1]) for e in evs]
+    k2 = [e[1].elapsed_time(e[2]) for e in evs]
+    k3 = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    tokens = B * H * T
+    value = tokens / (step_ms / 1e3)
+
+    U = B * H
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    summ_bytes = U * n * (d * d + 2 * d * dv + 2 * d) * 4
+    io_bytes = tokens * ((2 * d + dv) * es)
+    kernels = {
+        "hla_fwd_chunk_summaries": dict(ms=sum(k1) / len(k1), bytes=io_bytes + summ_bytes),
+        "hla_scan": dict(ms=sum(k2) / len(k2), bytes=None),
+        "hla_fwd_output": dict(ms=sum(k3) / len(k3),
+                               bytes=io_bytes + summ_bytes + tokens * dv * 4
+                               + (tokens * 4 if den is not None else 0)),
+    }
+    dom = max(("hla_fwd_chunk_summaries", "hla_fwd_output"), key=lambda kname: kernels[kname]["ms"])
+    kd = kernels[dom]
+    achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
+    f_tok = credited_flops_per_token(64, d, dv)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
+                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
+                   "path": "hla_fwd_chunk_summaries + hla_scan + hla_fwd_output"},
+        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
+                          "peak_tflops": BF16_PEAK_TFLOPS,
+                          "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_fwd(inp, min(args.cpu_tokens, T))
+    return out
+
+
+def bench_decode(args, torch, np):
+    from causal_prefix_scan_amd import hla, synth
+    name, cfg = synth.DECODE_WORKLOAD
+    Nq, H, d, dv, P, seed = (cfg[x] for x in ("n_seq", "H", "d", "dv", "prefix_len", "seed"))
+    U = Nq * H
+    steps = args.steps
+    # prefill on the GPU: one segment summary of the 2048-token prefix is the
+    # state after the prefix (hla_fwd with chunk = prefix length)
+    pre = synth.make_fwd_inputs(Nq, H, P, d, dv, "bf16", seed)
+    cv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    pq, pk, pv = cv(pre.q_bits), cv(pre.k_bits), cv(pre.v_bits)
+    _, _, state = hla.fwd(pq, pk, pv, P, None, want_state=True)
+    del pq, pk, pv
+    n_tok = args.warmup + steps
+    toks_host = [synth.make_decode_step(Nq, H, d, dv, seed, s) for s in range(n_tok)]
+    tq = torch.stack([cv(t[3][0]).reshape(Nq, H, d) for t in toks_host])
+    tk = torch.stack([cv(t[3][1]).reshape(Nq, H, d) for t in toks_host])
+    tv = torch.stack([cv(t[3][2]).reshape(Nq, H, dv) for t in toks_host])
+    o = torch.empty(Nq, H, dv, dtype=torch.float32, device="cuda")
+    den = torch.empty(Nq, H, dtype=torch.float32, device="cuda")
+    states64 = None
+    if not args.no_cpu_baseline:
+        states64 = {key: val.double().cpu().numpy().reshape(U, *val.shape[2:])
+                    for key, val in state.items()}
+    for s in range(args.warmup):
+        hla.decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(args.warmup, n_tok):
+        hla.decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / steps
+    value = U / (step_ms / 1e3)
+    state_bytes = (d * d + 2 * d * dv + 2 * d) * 4
+    bytes_step = U * (2 * state_bytes + (2 * d + dv) * 2 + dv * 4 + 4)
+    achieved = bytes_step / (step_ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "unit-tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "n_seq": Nq, "H": H, "d": d, "dv": dv, "prefix_len": P,
+                   "normalize": True, "path": "hla_decode_step"},
+        "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "hla_decode_step", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": bytes_step,
+                     "avg_launch_ms": round(step_ms, 4)},
+    }
+    if states64 is not None:
+        nb = 8
+        toks = [(t[0], t[1], t[2]) for t in toks_host[:nb]]
+        out["cpu_baseline"] = cpu_baseline_decode(states64, toks, nb)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.workload.startswith("decode"):
+        out = bench_decode(args, torch, np)
+    else:
+        out = bench_fwd(args, torch, np)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,355 @@
+// C ABI of the masked second-order HLA forward (declarations and the
+// contract of every entry point are in include/hla.h).
+//
+// This layer validates every argument on the host, sizes workspaces and
+// enqueues the kernels; it owns no memory and keeps no state between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "hla.h"
+#include "hla_internal.h"
+
+namespace {
+
+using hla::ChunkArgs;
+using hla::DecodeArgs;
+using hla::ScanArgs;
+
+constexpr int64_t kMaxGrid = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (both non-empty)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t dtype_size(int dt) { return dt == HLA_BF16 ? 2 : 4; }
+
+bool head_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+
+// Shape/dtype validation shared by the forward entry points.
+hla_status check_problem(const hla_problem* p) {
+  if (!p) return HLA_ERR_NULL_POINTER;
+  if (p->B < 0 || p->H < 0 || p->T < 0 || p->d <= 0 || p->dv <= 0) return HLA_ERR_BAD_SHAPE;
+  if (p->chunk <= 0) return HLA_ERR_BAD_SHAPE;
+  if (p->T % p->chunk != 0) return HLA_ERR_BAD_SHAPE;
+  if (p->in_dtype != HLA_F32 && p->in_dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (p->normalize != 0 && p->normalize != 1) return HLA_ERR_BAD_VALUE;
+  if (!std::isfinite(p->eps)) return HLA_ERR_BAD_VALUE;
+  if (!head_ok(p->d) || !head_ok(p->dv)) return HLA_ERR_UNSUPPORTED;
+  if (!hla::chunk_shape_supported(p->in_dtype, p->d, p->dv)) return HLA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)p->B * p->H;
+  const int64_t n = p->T / p->chunk;
+  if (units * n > kMaxGrid) return HLA_ERR_BAD_VALUE;
+  if (units > 65535) return HLA_ERR_BAD_VALUE;   // grid.y of the scan levels
+  if (p->gamma && !aligned16(p->gamma)) return HLA_ERR_MISALIGNED;
+  return HLA_OK;
+}
+
+bool empty_problem(const hla_problem* p) { return p->B == 0 || p->H == 0 || p->T == 0; }
+
+hla_status device_ready() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return HLA_ERR_HIP;
+  }
+  return HLA_OK;
+}
+
+hla_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return HLA_OK;
+  (void)hipGetLastError();
+  return HLA_ERR_HIP;
+}
+
+struct Sizes {
+  int64_t units, n, N;
+  size_t qk_bytes, v_bytes, o_bytes, den_bytes;
+  size_t S, C, m;   // floats per summary field
+};
+
+Sizes sizes_of(const hla_problem* p) {
+  Sizes s;
+  s.units = (int64_t)p->B * p->H;
+  s.n = p->T / p->chunk;
+  s.N = 1;
+  while (s.N < s.n) s.N *= 2;
+  const size_t tok = (size_t)s.units * (size_t)p->T;
+  s.qk_bytes = tok * p->d * dtype_size(p->in_dtype);
+  s.v_bytes = tok * p->dv * dtype_size(p->in_dtype);
+  s.o_bytes = tok * p->dv * 4;
+  s.den_bytes = tok * 4;
+  s.S = (size_t)p->d * p->d;
+  s.C = (size_t)p->d * p->dv;
+  s.m = (size_t)p->d;
+  return s;
+}
+
+hla_status check_state(const hla_state* st, bool all_required, int64_t count, const Sizes& z,
+                       const void* const* inputs, const size_t* in_bytes, int n_inputs) {
+  if (!st) return HLA_ERR_NULL_POINTER;
+  float* f[5] = {st->S, st->C, st->m, st->G, st->h};
+  const size_t per[5] = {z.S, z.C, z.m, z.C, z.m};
+  for (int i = 0; i < 5; ++i) {
+    if (!f[i]) {
+      if (all_required) return HLA_ERR_NULL_POINTER;
+      continue;
+    }
+    if (!aligned16(f[i])) return HLA_ERR_MISALIGNED;
+    const size_t bytes = (size_t)count * per[i] * 4;
+    for (int j = 0; j < n_inputs; ++j)
+      if (overlap(f[i], bytes, inputs[j], in_bytes[j])) return HLA_ERR_ALIASING;
+    for (int j = 0; j < i; ++j)
+      if (f[j] && overlap(f[i], bytes, f[j], (size_t)count * per[j] * 4)) return HLA_ERR_ALIASING;
+  }
+  return HLA_OK;
+}
+
+hla_status check_qkv(const void* q, const void* k, const void* v) {
+  if (!q || !k || !v) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return HLA_ERR_MISALIGNED;
+  return HLA_OK;
+}
+
+ChunkArgs chunk_args(const hla_problem* p, const void* q, const void* k, const void* v,
+                     const hla_state* st, float* o, float* den) {
+  ChunkArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.gamma = p->gamma;
+  a.H = p->H; a.T = p->T; a.chunk = p->chunk; a.nspan = p->T / p->chunk;
+  a.normalize = p->normalize; a.eps = p->eps;
+  a.S = st->S; a.C = st->C; a.m = st->m; a.G = st->G; a.h = st->h;
+  a.o = o; a.den = den;
+  return a;
+}
+
+size_t scan_ws_bytes(const hla_problem* p) {
+  const Sizes z = sizes_of(p);
+  return (size_t)z.units * (size_t)(z.N - z.n) * (z.S + 2 * z.C + 2 * z.m) * 4;
+}
+
+hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state* total,
+                   void* ws, hipStream_t s) {
+  const Sizes z = sizes_of(p);
+  ScanArgs a;
+  a.S = inout->S; a.C = inout->C; a.m = inout->m; a.G = inout->G; a.h = inout->h;
+  float* w = static_cast<float*>(ws);
+  const size_t pad = (size_t)z.units * (size_t)(z.N - z.n);
+  a.wS = w; a.wC = a.wS + pad * z.S; a.wm = a.wC + pad * z.C; a.wG = a.wm + pad * z.m;
+  a.wh = a.wG + pad * z.C;
+  a.gamma = p->gamma;
+  a.H = p->H; a.n = (int)z.n; a.N = (int)z.N; a.chunk = p->chunk; a.step = 1;
+  a.d = p->d; a.dv = p->dv;
+  float* t[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (total) { t[0] = total->S; t[1] = total->C; t[2] = total->m; t[3] = total->G; t[4] = total->h; }
+  return from_hip(hla::launch_scan((int)z.units, p->d, p->dv, a, t[0], t[1], t[2], t[3], t[4], s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hla_status_string(hla_status s) {
+  switch (s) {
+    case HLA_OK: return "HLA_OK";
+    case HLA_ERR_NULL_POINTER: return "HLA_ERR_NULL_POINTER: a required pointer is NULL";
+    case HLA_ERR_BAD_SHAPE: return "HLA_ERR_BAD_SHAPE: negative size, chunk <= 0 or T % chunk != 0";
+    case HLA_ERR_BAD_DTYPE: return "HLA_ERR_BAD_DTYPE: in_dtype is not HLA_F32 or HLA_BF16";
+    case HLA_ERR_MISALIGNED: return "HLA_ERR_MISALIGNED: a device pointer is not 16-byte aligned";
+    case HLA_ERR_UNSUPPORTED: return "HLA_ERR_UNSUPPORTED: head sizes / dtype not built";
+    case HLA_ERR_WORKSPACE_TOO_SMALL: return "HLA_ERR_WORKSPACE_TOO_SMALL";
+    case HLA_ERR_ALIASING: return "HLA_ERR_ALIASING: an output overlaps an input";
+    case HLA_ERR_HIP: return "HLA_ERR_HIP: no usable HIP device or a HIP call failed";
+    case HLA_ERR_BAD_VALUE: return "HLA_ERR_BAD_VALUE: eps/normalize invalid or sizes too large";
+  }
+  return "HLA_ERR_UNKNOWN";
+}
+
+const char* hla_version(void) { return "hla-mi355x 0.1 (gfx950)"; }
+
+hla_status hla_fwd_chunk_summaries(const hla_problem* p, const void* q, const void* k,
+                                   const void* v, const hla_state* out, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  const Sizes z = sizes_of(p);
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {z.qk_bytes, z.qk_bytes, z.v_bytes};
+  if (hla_status e = check_state(out, true, z.units * z.n, z, ins, inb, 3)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = device_ready()) return e;
+  const ChunkArgs a = chunk_args(p, q, k, v, out, nullptr, nullptr);
+  return from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a,
+                                              static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+size_t hla_scan_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  return scan_ws_bytes(p);
+}
+
+hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_state* total_out,
+                    void* workspace, size_t workspace_bytes, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_state(inout, true, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  if (total_out) {
+    const void* ins[5] = {inout->S, inout->C, inout->m, inout->G, inout->h};
+    const size_t inb[5] = {z.units * z.n * z.S * 4, z.units * z.n * z.C * 4,
+                           z.units * z.n * z.m * 4, z.units * z.n * z.C * 4,
+                           z.units * z.n * z.m * 4};
+    if (hla_status e = check_state(total_out, false, z.units, z, ins, inb, 5)) return e;
+  }
+  const size_t need = empty_problem(p) ? 0 : scan_ws_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0) {
+    if (!workspace) return HLA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  }
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = device_ready()) return e;
+  return do_scan(p, inout, total_out, workspace, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+size_t hla_fwd_output_workspace_bytes(const hla_problem* p) {
+  (void)p;
+  return 0;
+}
+
+hla_status hla_fwd_output(const hla_problem* p, const void* q, const void* k, const void* v,
+                          const hla_state* prefixes, float* o, float* den, void* workspace,
+                          size_t workspace_bytes, void* stream) try {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_state(prefixes, true, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  const void* ins[8] = {q, k, v, prefixes->S, prefixes->C, prefixes->m, prefixes->G, prefixes->h};
+  const size_t inb[8] = {z.qk_bytes, z.qk_bytes, z.v_bytes,
+                         z.units * z.n * z.S * 4, z.units * z.n * z.C * 4, z.units * z.n * z.m * 4,
+                         z.units * z.n * z.C * 4, z.units * z.n * z.m * 4};
+  for (int j = 0; j < 8; ++j) {
+    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = device_ready()) return e;
+  const ChunkArgs a = chunk_args(p, q, k, v, prefixes, o, den);
+  return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a,
+                                            static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+size_t hla_fwd_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  const Sizes z = sizes_of(p);
+  const size_t summ = (size_t)z.units * (size_t)z.n * (z.S + 2 * z.C + 2 * z.m) * 4;
+  return summ + scan_ws_bytes(p);
+}
+
+hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v, float* o,
+                   float* den, const hla_state* final_state, void* workspace,
+                   size_t workspace_bytes, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  const size_t need = hla_fwd_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0) {
+    if (!workspace) return HLA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  }
+  const void* ins[4] = {q, k, v, workspace};
+  const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
+  for (int j = 0; j < 4; ++j) {
+    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
+  if (final_state) {
+    const void* fins[6] = {q, k, v, workspace, o, den};
+    const size_t finb[6] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need, z.o_bytes,
+                            den ? z.den_bytes : 0};
+    if (hla_status e = check_state(final_state, false, z.units, z, fins, finb, 6)) return e;
+  }
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = device_ready()) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* w = static_cast<float*>(workspace);
+  const size_t cnt = (size_t)z.units * (size_t)z.n;
+  hla_state sm;
+  sm.S = w; sm.C = sm.S + cnt * z.S; sm.m = sm.C + cnt * z.C; sm.G = sm.m + cnt * z.m;
+  sm.h = sm.G + cnt * z.C;
+  void* scan_ws = sm.h + cnt * z.m;
+  const ChunkArgs a1 = chunk_args(p, q, k, v, &sm, nullptr, nullptr);
+  if (hla_status e = from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
+    return e;
+  if (hla_status e = do_scan(p, &sm, final_state, scan_ws, s)) return e;
+  const ChunkArgs a3 = chunk_args(p, q, k, v, &sm, o, den);
+  return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                           int32_t normalize, float eps, const float* gamma, const void* q,
+                           const void* k, const void* v, const hla_state* state, float* o,
+                           float* den, void* stream) try {
+  if (N < 0 || H < 0) return HLA_ERR_BAD_SHAPE;
+  if (in_dtype != HLA_F32 && in_dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (normalize != 0 && normalize != 1) return HLA_ERR_BAD_VALUE;
+  if (!std::isfinite(eps)) return HLA_ERR_BAD_VALUE;
+  if (!head_ok(d) || !head_ok(dv) || d > 2 * dv || dv > 2 * d) return HLA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)N * H;
+  if (units > kMaxGrid) return HLA_ERR_BAD_VALUE;
+  if (units == 0) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den)) || (gamma && !aligned16(gamma)))
+    return HLA_ERR_MISALIGNED;
+  Sizes z;
+  z.S = (size_t)d * d; z.C = (size_t)d * dv; z.m = (size_t)d;
+  const size_t es = dtype_size(in_dtype);
+  const void* ins[5] = {q, k, v, o, den};
+  const size_t uu = (size_t)units;
+  const size_t inb[5] = {uu * d * es, uu * d * es, uu * dv * es, uu * dv * 4,
+                         den ? (size_t)units * 4 : 0};
+  if (hla_status e = check_state(state, true, units, z, ins, inb, 5)) return e;
+  for (int j = 0; j < 3; ++j) {
+    if (overlap(o, inb[3], ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, inb[4], ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, inb[3], den, inb[4])) return HLA_ERR_ALIASING;
+  if (units == 0) return HLA_OK;
+  if (hla_status e = device_ready()) return e;
+  DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.gamma = gamma;
+  a.S = state->S; a.C = state->C; a.m = state->m; a.G = state->G; a.h = state->h;
+  a.o = o; a.den = den; a.H = H; a.normalize = normalize; a.eps = eps;
+  return from_hip(hla::launch_decode(in_dtype, d, dv, (int)units, a, static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+"""Thin ctypes binding of libhla.so (the C ABI declared in include/hla.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the current
+stream.  There is no CPU fallback: if the library is missing or no GPU is
+present, the calls raise.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhla.so")
+
+HLA_F32 = 0
+HLA_BF16 = 1
+
+STATUS = {
+    0: "HLA_OK", 1: "HLA_ERR_NULL_POINTER", 2: "HLA_ERR_BAD_SHAPE", 3: "HLA_ERR_BAD_DTYPE",
+    4: "HLA_ERR_MISALIGNED", 5: "HLA_ERR_UNSUPPORTED", 6: "HLA_ERR_WORKSPACE_TOO_SMALL",
+    7: "HLA_ERR_ALIASING", 8: "HLA_ERR_HIP", 9: "HLA_ERR_BAD_VALUE",
+}
+
+EXPORTS = (
+    "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
+    "hla_scan", "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
+    "hla_fwd", "hla_decode_step",
+)
+
+
+class HlaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("normalize", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("gamma", ctypes.c_void_p),
+    ]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_void_p), ("C", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("G", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libhla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run `python -m causal_prefix_scan_amd.build_lib`)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    pp, ps = ctypes.POINTER(Problem), ctypes.POINTER(State)
+    L.hla_status_string.argtypes, L.hla_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.hla_version.argtypes, L.hla_version.restype = [], ctypes.c_char_p
+    L.hla_fwd_chunk_summaries.argtypes = [pp, vp, vp, vp, ps, vp]
+    L.hla_scan_workspace_bytes.argtypes, L.hla_scan_workspace_bytes.restype = [pp], sz
+    L.hla_scan.argtypes = [pp, ps, ps, vp, sz, vp]
+    L.hla_fwd_output_workspace_bytes.argtypes, L.hla_fwd_output_workspace_bytes.restype = [pp], sz
+    L.hla_fwd_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, sz, vp]
+    L.hla_fwd_workspace_bytes.argtypes, L.hla_fwd_workspace_bytes.restype = [pp], sz
+    L.hla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, ps, vp, sz, vp]
+    L.hla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, ps, vp, vp, vp]
+    for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_fwd_output", "hla_fwd",
+                 "hla_decode_step"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().hla_status_string(int(status)).decode()
+
+
+def version():
+    return lib().hla_version().decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise HlaError(status, where)
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HLA_BF16
+    if t.dtype == torch.float32:
+        return HLA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise RuntimeError("HLA kernels need CUDA/HIP tensors (no CPU path)")
+        if not t.is_contiguous():
+            raise RuntimeError("HLA kernels need contiguous tensors")
+
+
+def make_problem(q, v, chunk, gamma=None, normalize=False, eps=0.0):
+    B, H, T, d = q.shape
+    return Problem(B, H, T, d, v.shape[3], int(chunk), _dtype_code(q), int(bool(normalize)),
+                   float(eps), None if gamma is None else gamma.data_ptr())
+
+
+def _state_struct(st):
+    if st is None:
+        return None
+    return State(*(None if st.get(k) is None else st[k].data_ptr() for k in ("S", "C", "m", "G", "h")))
+
+
+def alloc_state(lead, d, dv, device):
+    """fp32 state / summary tensors with leading dims `lead` (a tuple)."""
+    torch = _torch()
+    z = lambda *s: torch.zeros(*lead, *s, dtype=torch.float32, device=device)
+    return {"S": z(d, d), "C": z(d, dv), "m": z(d), "G": z(d, dv), "h": z(d)}
+
+
+def fwd_chunk_summaries(q, k, v, chunk, gamma=None, out=None):
+    """Segment summaries [B, H, n, ...] (fp32 dict S, C, m, G, h)."""
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma)
+    if out is None:
+        out = alloc_state((B, H, T // chunk), d, v.shape[3], q.device)
+    st = _state_struct(out)
+    _check(lib().hla_fwd_chunk_summaries(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                         ctypes.byref(st), _stream()), "hla_fwd_chunk_summaries")
+    return out
+
+
+def scan(summaries, q_shape, dv, chunk, dtype_code, gamma=None, want_total=False):
+    """In-place exclusive scan of `summaries`; returns the inclusive total (or None)."""
+    torch = _torch()
+    B, H, T, d = q_shape
+    p = Problem(B, H, T, d, dv, int(chunk), dtype_code, 0, 0.0,
+                None if gamma is None else gamma.data_ptr())
+    dev = summaries["S"].device
+    total = alloc_state((B, H), d, dv, dev) if want_total else None
+    nbytes = lib().hla_scan_workspace_bytes(ctypes.byref(p))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st = _state_struct(summaries)
+    tt = _state_struct(total)
+    _check(lib().hla_scan(ctypes.byref(p), ctypes.byref(st),
+                          ctypes.byref(tt) if tt is not None else None,
+                          _ptr(ws), ctypes.c_size_t(nbytes), _stream()), "hla_scan")
+    return total
+
+
+def fwd_output(q, k, v, prefixes, chunk, gamma=None, normalize=False, eps=0.0, want_den=False):
+    """Outputs from exclusive prefixes: (o [B,H,T,dv] fp32, den [B,H,T] or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    o = torch.empty(B, H, T, v.shape[3], dtype=torch.float32, device=q.device)
+    den = torch.empty(B, H, T, dtype=torch.float32, device=q.device) if want_den else None
+    st = _state_struct(prefixes)
+    _check(lib().hla_fwd_output(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
+                                _ptr(o), _ptr(den), None, ctypes.c_size_t(0), _stream()),
+           "hla_fwd_output")
+    return o, den
+
+
+def fwd_workspace(q, v, chunk, gamma=None):
+    torch = _torch()
+    p = make_problem(q, v, chunk, gamma)
+    nbytes = lib().hla_fwd_workspace_bytes(ctypes.byref(p))
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+
+
+def fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False, want_state=False,
+        workspace=None, o=None, den=None):
+    """Whole chunk-parallel forward: (o, den or None, final state dict or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    if den is None and want_den:
+        den = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = fwd_workspace(q, v, chunk, gamma)
+    final = alloc_state((B, H), d, dv, q.device) if want_state else None
+    fs = _state_struct(final)
+    _check(lib().hla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                         ctypes.byref(fs) if fs is not None else None, _ptr(workspace),
+                         ctypes.c_size_t(workspace.numel()), _stream()), "hla_fwd")
+    return o, den, final
+
+
+def decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, den=None):
+    """One decode step; q, k [N, H, d], v [N, H, dv]; `state` is updated in place.
+    Returns (o [N, H, dv] fp32, den [N, H] or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    N, H, d = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=torch.float32, device=q.device)
+    st = _state_struct(state)
+    _check(lib().hla_decode_step(N, H, d, dv, _dtype_code(q), int(bool(normalize)), float(eps),
+                                 _ptr(gamma), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
+                                 _ptr(o), _ptr(den), _stream()), "hla_decode_step")
+    return o, den

@@ -1,0 +1,180 @@
+/*
+ * hla.h -- C ABI of the masked second-order Higher-order Linear Attention
+ * (HLA) forward for AMD Instinct MI355X (gfx950).
+ *
+ * The method (summaries of "Higher-order Linear Attention", arXiv 2510.27258,
+ * gist.science, Japanese and French pages):
+ *   - method section 1 (second-order HLA): per (batch, head) the prefix
+ *     moments S_t = sum_{i<=t} k_i k_i^T, C_t = sum_{i<=t} q_i v_i^T,
+ *     m_t = sum_{i<=t} q_i and the cross summaries G_t, h_t that remove the
+ *     future terms of S_t C_t; the output o_t = q_t^T (S_t C_t - G_t) and a
+ *     ratio-normalised variant divided by a masked denominator;
+ *   - method section 4 (parallel training by associative scans): segment
+ *     summaries joined by an associative semidirect-product operator whose
+ *     cross term is S_B C_A, and an exclusive Blelloch scan of the summaries
+ *     that reproduces the serial activations exactly;
+ *   - key contribution 2: the same operators with exponential decay;
+ *   - results and claims: O(d^2 + d dv) work and memory per token.
+ *
+ * Readings used where the pages are silent (decay gamma per head, in [0, 1]):
+ *   G_t = g^2 G_{t-1} + g k_t (k_t^T C_{t-1}),  h_t = g^2 h_{t-1} + g k_t (k_t^T m_{t-1}),
+ *   S_t = g S_{t-1} + k_t k_t^T,  C_t = g C_{t-1} + q_t v_t^T,  m_t = g m_{t-1} + q_t,
+ *   num_t = q_t^T (S_t C_t - G_t),  den_t = q_t^T (S_t m_t - h_t),
+ *   o_t = num_t (unnormalised) or num_t / (den_t + eps) (ratio-normalised).
+ * Equivalently num_t = sum_{j<=t} sum_{i<=j} g^((t-i)+(t-j)) (q_t.k_i)(q_j.k_i) v_j.
+ * Segment combine (A then B, a = g^(length of B)):
+ *   S = a S_A + S_B, C = a C_A + C_B, m = a m_A + m_B,
+ *   G = a^2 G_A + G_B + a S_B C_A, h = a^2 h_A + h_B + a S_B m_A.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer (memory of the current HIP device)
+ *     unless stated otherwise; struct arguments are HOST pointers read during
+ *     the call only.  The caller owns every buffer; the library allocates no
+ *     device memory and keeps no pointer after it returns.
+ *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t
+ *     passed as void*; NULL = the default stream).  The caller synchronises.
+ *   - All arguments are validated on the host before anything is enqueued;
+ *     on any error nothing is launched and a non-zero hla_status is
+ *     returned.  A HIP launch/runtime failure returns HLA_ERR_HIP.  No C++
+ *     exception crosses the ABI.
+ *   - Layouts are dense row-major (C order).  Every device pointer must be
+ *     16-byte aligned (HLA_ERR_MISALIGNED).
+ *   - Numerical conditions (den + eps = 0, NaN/Inf inputs) are not errors and
+ *     follow IEEE arithmetic.
+ *   - An empty problem (B, H, T or N equal to 0) is valid once its sizes and
+ *     options pass validation: nothing is launched, pointers are not
+ *     checked (they may be NULL) and HLA_OK is returned.
+ *   - Supported head sizes: d, dv in {16, 32, 64, 128} with d/dv in
+ *     {1/2, 1, 2}; fp32 inputs need d, dv <= 64 (HLA_ERR_UNSUPPORTED).
+ *   - Calls on one device that share output or state buffers must be
+ *     ordered by the caller (same stream or events); the library holds no
+ *     global mutable state, so distinct calls are otherwise independent.
+ */
+#ifndef HLA_H
+#define HLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HLA_OK = 0,
+  HLA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  HLA_ERR_BAD_SHAPE = 2,          /* negative size, T % chunk != 0, chunk <= 0 */
+  HLA_ERR_BAD_DTYPE = 3,          /* in_dtype is not an hla_dtype */
+  HLA_ERR_MISALIGNED = 4,         /* a device pointer is not 16-byte aligned */
+  HLA_ERR_UNSUPPORTED = 5,        /* d / dv / dtype combination not built */
+  HLA_ERR_WORKSPACE_TOO_SMALL = 6,
+  HLA_ERR_ALIASING = 7,           /* an output overlaps an input it must not */
+  HLA_ERR_HIP = 8,                /* no usable device, or a HIP call failed */
+  HLA_ERR_BAD_VALUE = 9           /* eps not finite, normalize not 0/1, sizes too large */
+} hla_status;
+
+typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
+
+/* One forward problem: q, k [B, H, T, d], v [B, H, T, dv] of in_dtype. */
+typedef struct {
+  int32_t B, H, T, d, dv;
+  int32_t chunk;        /* tokens per segment summary; T % chunk == 0 */
+  int32_t in_dtype;     /* hla_dtype of q, k, v */
+  int32_t normalize;    /* 0: o = num; 1: o = num / (den + eps) */
+  float eps;            /* used when normalize == 1; must be finite */
+  const float* gamma;   /* device [H] per-head decay in [0, 1]; NULL means 1.
+                           Values are not range-checked (they live on the device). */
+} hla_problem;
+
+/* Struct of device arrays, fp32.  For segment summaries / prefixes:
+ *   S [B, H, n, d, d], C [B, H, n, d, dv], m [B, H, n, d], G [B, H, n, d, dv],
+ *   h [B, H, n, d] with n = T / chunk.
+ * For decode state the leading dims are [N, H] instead of [B, H, n]. */
+typedef struct { float *S, *C, *m, *G, *h; } hla_state;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* hla_status_string(hla_status s);
+
+/* Library version string (static). */
+const char* hla_version(void);
+
+/*
+ * Segment summaries (method section 4: the summary of a token segment; its
+ * moments and cross summaries are those of method section 1).  For every
+ * (b, h) and every segment s of `chunk` tokens, writes the state the serial
+ * recurrence reaches from the zero state after that segment's tokens:
+ *   S = sum_i g^(c-i) k_i k_i^T, C = sum_j g^(c-j) q_j v_j^T, m = sum_j g^(c-j) q_j,
+ *   G = sum_{j<i} g^((c-i)+(c-j)) k_i (k_i.q_j) v_j^T, h = the same without v_j
+ * (1-based positions i, j inside the segment, c = chunk).
+ * `out` fields are all required ([B,H,n,...] as above) and must not overlap
+ * q, k or v.
+ */
+hla_status hla_fwd_chunk_summaries(const hla_problem* p, const void* q, const void* k,
+                                   const void* v, const hla_state* out, void* stream);
+
+/* Bytes of scratch hla_scan needs for this problem (0 when n is a power of
+ * two).  Host-only; returns 0 for an invalid problem. */
+size_t hla_scan_workspace_bytes(const hla_problem* p);
+
+/*
+ * Exclusive Blelloch scan (method section 4: the exclusive scan of segment
+ * summaries under the semidirect-product combine with cross term S_B C_A;
+ * decay per key contribution 2 as read above).  In place: on entry `inout`
+ * holds the n segment summaries of every (b, h); on return it holds the
+ * exclusive prefixes P_s = s_0 (+) ... (+) s_{s-1} (P_0 = 0).  If
+ * `total_out` is non-NULL, each of its non-NULL fields receives the
+ * inclusive total of all n segments ([B, H, ...], the state after T tokens).
+ * `workspace` must hold hla_scan_workspace_bytes(p) bytes (may be NULL when
+ * that is 0).
+ */
+hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_state* total_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch hla_fwd_output needs (0 today; kept for ABI stability). */
+size_t hla_fwd_output_workspace_bytes(const hla_problem* p);
+
+/*
+ * Outputs from the exclusive prefixes (method section 1: o_t = q_t^T (S_t C_t
+ * - G_t) and the ratio-normalised variant; section 4: each segment continues
+ * from its exclusive prefix).  o [B, H, T, dv] fp32 receives num (normalize
+ * == 0) or num / (den + eps) (normalize == 1).  den [B, H, T] fp32 is
+ * optional (NULL to skip) and receives the denominator before eps is added.
+ * `prefixes` is what hla_scan leaves in `inout`.
+ */
+hla_status hla_fwd_output(const hla_problem* p, const void* q, const void* k, const void* v,
+                          const hla_state* prefixes, float* o, float* den,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch hla_fwd needs: the n summaries plus hla_scan's scratch. */
+size_t hla_fwd_workspace_bytes(const hla_problem* p);
+
+/*
+ * The whole chunk-parallel forward (method section 4): segment summaries,
+ * exclusive Blelloch scan, outputs -- the three calls above on one stream,
+ * with the summaries kept in `workspace` (hla_fwd_workspace_bytes(p) bytes).
+ * o and den as in hla_fwd_output.  If `final_state` is non-NULL its non-NULL
+ * fields receive the state after all T tokens ([B, H, ...]), ready for
+ * hla_decode_step.
+ */
+hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                   float* o, float* den, const hla_state* final_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One streaming decode step (method section 1: the online update of the
+ * prefix state; results and claims: constant work and memory per token).
+ * For each of the N*H units: applies one token (q, k [N, H, d], v [N, H, dv]
+ * of in_dtype) to `state` ([N, H, ...] fp32, updated in place) and writes
+ * o [N, H, dv] fp32 (num, or num / (den + eps) when normalize == 1) and the
+ * optional den [N, H] fp32 (before eps).  gamma: device [H] or NULL.
+ */
+hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                           int32_t normalize, float eps, const float* gamma,
+                           const void* q, const void* k, const void* v,
+                           const hla_state* state, float* o, float* den, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H */

@@ -1,0 +1,170 @@
+"""C-ABI contract checks that need no GPU.
+
+Every declared symbol is exported; argument validation returns the documented
+status before anything is launched (fake, never-dereferenced device
+pointers are used); on a host without a HIP device a valid call returns
+HLA_ERR_HIP instead of crashing.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_prefix_scan_amd import hla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hla.h")
+
+OK, NULLP, SHAPE, DTYPE, MISAL, UNSUP, WS, ALIAS, HIP, VALUE = range(10)
+
+# Fake device addresses: 16-byte aligned, far apart, never dereferenced on the host.
+Q, K, V, O, DEN, GAM = (0x10000000 * (i + 1) for i in range(6))
+S_BASE = 0x100000000
+
+
+def state(base=S_BASE):
+    step = 0x1000000
+    return hla.State(base, base + step, base + 2 * step, base + 3 * step, base + 4 * step)
+
+
+def problem(**kw):
+    p = dict(B=2, H=3, T=256, d=64, dv=64, chunk=64, in_dtype=hla.HLA_BF16, normalize=0,
+             eps=0.0, gamma=None)
+    p.update(kw)
+    return hla.Problem(**p)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return hla.lib()
+
+
+def no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+def test_every_declared_symbol_is_exported(L):
+    decl = set(re.findall(r"\b(hla_[a-z_]+)\s*\(", open(HEADER).read()))
+    assert decl == set(hla.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in hla.STATUS.items():
+        assert hla.status_string(code).startswith(name)
+    assert hla.status_string(12345) == "HLA_ERR_UNKNOWN"
+    assert "gfx950" in hla.version()
+
+
+def summaries(L, p, out=None, q=Q, k=K, v=V):
+    return L.hla_fwd_chunk_summaries(ctypes.byref(p) if p is not None else None, q, k, v,
+                                     ctypes.byref(out or state()), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=250), SHAPE),                 # T % chunk != 0
+    (dict(chunk=0), SHAPE),
+    (dict(B=-1), SHAPE),
+    (dict(d=0), SHAPE),
+    (dict(in_dtype=7), DTYPE),
+    (dict(normalize=2), VALUE),
+    (dict(eps=float("nan")), VALUE),
+    (dict(eps=float("inf")), VALUE),
+    (dict(d=48), UNSUP),
+    (dict(d=256, dv=256), UNSUP),
+    (dict(d=16, dv=64), UNSUP),           # ratio 4 not built
+    (dict(d=128, dv=128, in_dtype=hla.HLA_F32), UNSUP),
+    (dict(gamma=GAM + 4), MISAL),
+    (dict(B=70000, H=1, T=64), VALUE),    # grid.y of the scan
+])
+def test_problem_validation(L, kw, code):
+    assert summaries(L, problem(**kw)) == code
+    assert L.hla_fwd_output(ctypes.byref(problem(**kw)), Q, K, V, ctypes.byref(state()), O, None,
+                            None, 0, None) == code
+
+
+def test_pointer_validation(L):
+    p = problem()
+    assert summaries(L, None) == NULLP
+    assert summaries(L, p, q=None) == NULLP
+    assert summaries(L, p, v=V + 8) == MISAL
+    bad = state()
+    bad.G = None
+    assert summaries(L, p, out=bad) == NULLP
+    bad = state()
+    bad.m = bad.m + 4
+    assert summaries(L, p, out=bad) == MISAL
+    # summaries overlapping an input
+    assert summaries(L, p, out=state(base=Q)) == ALIAS
+    # o overlapping q
+    assert L.hla_fwd_output(ctypes.byref(p), Q, K, V, ctypes.byref(state()), Q + 64, None,
+                            None, 0, None) == ALIAS
+    assert L.hla_fwd_output(ctypes.byref(p), Q, K, V, ctypes.byref(state()), None, None,
+                            None, 0, None) == NULLP
+
+
+def test_workspace_sizes(L):
+    p = problem(T=256, chunk=64)                      # n = 4: power of two
+    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 0
+    p = problem(B=1, H=2, T=5 * 64, chunk=64, d=32, dv=16)   # n = 5 -> N = 8: 3 pad slots
+    per = 32 * 32 + 2 * 32 * 16 + 2 * 32
+    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 2 * 3 * per * 4
+    summ = 2 * 5 * per * 4
+    assert L.hla_fwd_workspace_bytes(ctypes.byref(p)) == summ + 2 * 3 * per * 4
+    assert L.hla_scan_workspace_bytes(ctypes.byref(problem(T=10))) == 0   # invalid -> 0
+    # too small a workspace is rejected before anything runs
+    assert L.hla_scan(ctypes.byref(p), ctypes.byref(state()), None, 0x7000000000, 16, None) == WS
+    assert L.hla_fwd(ctypes.byref(p), Q, K, V, O, None, None, 0x7000000000, 16, None) == WS
+
+
+def test_empty_problem_is_a_no_op(L):
+    for kw in (dict(T=0), dict(B=0), dict(H=0)):
+        assert summaries(L, problem(**kw)) == OK
+        assert L.hla_fwd(ctypes.byref(problem(**kw)), Q, K, V, O, None, None, None, 0, None) == OK
+    assert L.hla_decode_step(0, 4, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V,
+                             ctypes.byref(state()), O, None, None) == OK
+
+
+def test_decode_validation(L):
+    st = state()
+    args = lambda **kw: dict(dict(N=2, H=2, d=128, dv=128, dt=hla.HLA_BF16, norm=1, eps=1e-6,
+                                  gamma=None, q=Q, k=K, v=V, st=st, o=O, den=None), **kw)
+
+    def call(a):
+        return L.hla_decode_step(a["N"], a["H"], a["d"], a["dv"], a["dt"], a["norm"], a["eps"],
+                                 a["gamma"], a["q"], a["k"], a["v"], ctypes.byref(a["st"]),
+                                 a["o"], a["den"], None)
+    assert call(args(N=-1)) == SHAPE
+    assert call(args(dt=3)) == DTYPE
+    assert call(args(norm=5)) == VALUE
+    assert call(args(eps=float("nan"))) == VALUE
+    assert call(args(d=96)) == UNSUP
+    assert call(args(k=None)) == NULLP
+    assert call(args(o=None)) == NULLP
+    assert call(args(o=O + 2)) == MISAL
+    assert call(args(o=Q)) == ALIAS
+    assert call(args(den=O + 64)) == ALIAS
+    assert call(args(st=state(base=Q))) == ALIAS
+
+
+@pytest.mark.skipif(not no_gpu(), reason="checks the behaviour on a host without a GPU")
+def test_valid_call_without_device_returns_hip_error(L):
+    assert summaries(L, problem()) == HIP
+    assert L.hla_fwd(ctypes.byref(problem()), Q, K, V, O, None, None, 0x7000000000, 1 << 40,
+                     None) == HIP
+    assert L.hla_decode_step(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V,
+                             ctypes.byref(state()), O, None, None) == HIP
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 64, 16)
+    with pytest.raises(RuntimeError, match="CUDA/HIP"):
+        hla.fwd(q, q, q, 64)
