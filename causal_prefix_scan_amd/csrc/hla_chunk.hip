@@ -62,7 +62,8 @@ struct ChunkLayout {
   static constexpr size_t F_END = FC + (size_t)D * LFC * 4;
   static constexpr size_t BIG = TILE_END > F_END ? TILE_END : F_END;
   static constexpr size_t W = (BIG + 15) / 16 * 16;
-  static constexpr size_t TOTAL = W + (size_t)(8 * TT + 3 * D) * 4;
+  // w1, w2, wS, wM, pw, pw2, qn [TT]; bpart [TR][TT]; pcol [TR][D]; nst, mst [D]
+  static constexpr size_t TOTAL = W + (size_t)(7 * TT + (TT / 16) * TT + (TT / 16) * D + 2 * D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -109,10 +110,10 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
   float* wM = wS + TT;
   float* pw = wM + TT;
   float* pw2 = pw + TT;
-  float* bsum = pw2 + TT;
-  float* qn = bsum + TT;
-  float* ncol = qn + TT;
-  float* nst = ncol + D;
+  float* qn = pw2 + TT;
+  float* bpart = qn + TT;        // [TR][TT]: row sums of B per 16-column block (fixed order)
+  float* pcol = bpart + TR * TT; // [TR][D]: weighted column sums of P per 16-row block
+  float* nst = pcol + TR * D;
   float* mst = nst + D;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -279,7 +280,6 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
         store4<T>(SM + (c0 + lr) * L::LDSM + r0 + 4 * lg4, Sreg[s]);
       }
     }
-    for (int i = tid; i < D; i += NTHR) ncol[i] = 0.f;
     __syncthreads();
 
     if (need_n && MODE == MODE_OUTPUT && tid < TT) {
@@ -338,11 +338,10 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
         }
         if (need_n) {
           const float cs = sum_rows4(pwv[0] + pwv[1] + pwv[2] + pwv[3]);
-          if (lg4 == 0) atomicAdd(&ncol[n0 + lr], cs);
+          if (lg4 == 0) pcol[r * D + n0 + lr] = cs;
         }
       }
     }
-    if (tid < TT) bsum[tid] = 0.f;
     __syncthreads();
 
     // ---- step 3: state updates, B = (Q P^T) o decay, M operand ---------------
@@ -372,7 +371,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
           AB[tau * L::LDT + jj] = (T)val;
           if (need_n) {
             const float rs = sum16(val);
-            if (lr == 0 && c <= r) atomicAdd(&bsum[tau], rs);
+            if (lr == 0) bpart[c * TT + tau] = rs;
           }
         }
       }
@@ -418,7 +417,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
         }
       }
       if (need_n) {
-        for (int r = tid; r < D; r += NTHR) nst[r] = g2L * nst[r] + ncol[r];
+        for (int r = tid; r < D; r += NTHR) {
+          float acc = 0.f;
+#pragma unroll
+          for (int rr = 0; rr < TR; ++rr) acc += pcol[rr * D + r];
+          nst[r] = g2L * nst[r] + acc;
+        }
       }
     }
     __syncthreads();
@@ -426,6 +430,13 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     // ---- step 4: outputs ------------------------------------------------------
     if (MODE == MODE_OUTPUT) {
       float* go = a.o + (tok0 + t0) * E;
+      // denominator of row tau: the B row sums of the column blocks c <= tau/16 in
+      // a fixed order, plus the prefix term
+      auto den_of = [&](int tau) {
+        float acc = 0.f;
+        for (int c = 0; c <= tau / 16; ++c) acc += bpart[c * TT + tau];
+        return acc + w2[tau] * qn[tau];
+      };
 #pragma unroll
       for (int s = 0; s < OT; ++s) {
         const int id = wave + NWAVE * s;
@@ -444,12 +455,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
           for (int j = 0; j < 4; ++j) {
             const int tau = 16 * r + 4 * lg4 + j;
             float val = acc[j];
-            if (a.normalize) val = val / (bsum[tau] + w2[tau] * qn[tau] + a.eps);
+            if (a.normalize) val = val / (den_of(tau) + a.eps);
             if (tau < Lt) go[(size_t)tau * E + e0 + lr] = val;
           }
         }
       }
-      if (a.den != nullptr && tid < Lt) a.den[tok0 + t0 + tid] = bsum[tid] + w2[tid] * qn[tid];
+      if (a.den != nullptr && tid < Lt) a.den[tok0 + t0 + tid] = den_of(tid);
       __syncthreads();
     }
   }

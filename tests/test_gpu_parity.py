@@ -185,7 +185,7 @@ def test_fwd_gamma_zero_keeps_the_diagonal(gpu):
     torch.cuda.synchronize()
     uq, uk, uv, ug = inp.units()
     num, den, _ = O.serial(uq, uk, uv, ug)
-    s = np.sum(uq[0] * uk[0], axis=-1)
+    s = np.sum(uq[0].astype(np.float64) * uk[0], axis=-1)
     assert rel_err(num[0], (s * s)[:, None] * uv[0]) < 1e-12     # oracle special case
     assert rel_err(host(o)[0], num) <= 2e-2
     assert rel_err(host(dn)[0], den) <= 2e-2
