@@ -32,17 +32,17 @@
 namespace hla {
 
 constexpr int TT = 64;      // tokens per tile
-constexpr int NWAVE = 8;
-constexpr int NTHR = 64 * NWAVE;
 
 enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1 };
 
 template <typename T, int D, int E, int MODE>
 struct ChunkLayout {
   static constexpr int PADT = 16 / (int)sizeof(T);
-  static constexpr int LDD = D + PADT;       // [tok][d] buffers
+  // d-contractions run in steps of MM<T>::KS; a smaller d is zero-padded to one step
+  static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;
+  static constexpr int LDD = DP + PADT;      // [tok][d] buffers
   static constexpr int LDT = TT + PADT;      // [d][tok] buffers
-  static constexpr int LDSM = D + PADT;      // S operand [d][d'] / M operand [e][d]
+  static constexpr int LDSM = DP + PADT;     // S operand [d][d'] / M operand [e][d]
   static constexpr size_t Qs = 0;
   static constexpr size_t Ks = Qs + (size_t)TT * LDD * sizeof(T);
   static constexpr size_t Kt = Ks + (size_t)TT * LDD * sizeof(T);
@@ -80,25 +80,65 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
   *reinterpret_cast<f32x4*>(p) = x;
 }
 
-template <typename T, int D, int E, int MODE>
-__global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
+// Four consecutive elements of one LDS row (8 bytes for bf16, 16 for fp32).
+template <typename T>
+__device__ __forceinline__ void store4_raw(T* p, T a, T b, T c, T d);
+template <>
+__device__ __forceinline__ void store4_raw<__bf16>(__bf16* p, __bf16 a, __bf16 b, __bf16 c, __bf16 d) {
+  bf16x4 y;
+  y[0] = a; y[1] = b; y[2] = c; y[3] = d;
+  *reinterpret_cast<bf16x4*>(p) = y;
+}
+template <>
+__device__ __forceinline__ void store4_raw<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Ownership of the 16x16 tiles of an R x CB grid (R row blocks, CB column
+// blocks) by the NW waves of a workgroup.  Slot s of wave w holds tile (rb, cb):
+//   CB >= NW: cb = w + NW * (s / R), rb = s % R
+//   CB <  NW: cb = w % CB,          rb = w / CB + (NW / CB) * s
+// so consecutive slots of a wave share a column block, and therefore the B
+// fragments of a product whose B operand depends only on the column.
+template <int R, int CB, int NW>
+struct Owner {
+  static constexpr int SLOTS = (R * CB + NW - 1) / NW;
+  __device__ static __forceinline__ bool tile(int w, int s, int& rb, int& cb) {
+    if (CB >= NW) {
+      cb = w + NW * (s / R);
+      rb = s % R;
+      return cb < CB;
+    }
+    cb = w % CB;
+    rb = w / CB + (NW / CB) * s;
+    return rb < R;
+  }
+  __device__ static __forceinline__ bool new_col(int s) { return CB >= NW ? (s % R) == 0 : s == 0; }
+};
+
+template <typename T, int D, int E, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
+  constexpr int NTHR = 64 * NW;
   using L = ChunkLayout<T, D, E, MODE>;
   using MMT = MM<T>;
+  using F = typename MMT::F;
   constexpr int KS = MMT::KS;
   constexpr int CH = MMT::CH;
-  constexpr int DT = D / 16, ET = E / 16, TR = TT / 16;
-  constexpr int PT = (TR * DT + NWAVE - 1) / NWAVE;   // P tiles per wave
-  constexpr int OT = (TR * ET + NWAVE - 1) / NWAVE;   // O tiles per wave
-  constexpr int ST = (DT * DT + NWAVE - 1) / NWAVE;   // S tiles per wave
-  constexpr int MT = (DT * ET + NWAVE - 1) / NWAVE;   // M, C, G tiles per wave
-  constexpr int CT = MODE == MODE_SUMMARY ? MT : 1;
+  constexpr int DP = L::DP;
+  constexpr int DT = D / 16, ET = E / 16, TR = TT / 16, NKS = TT / KS;
+  static_assert(NW % TR == 0, "row-block ownership of P and O tiles needs TR | NW");
+  using OS = Owner<DT, DT, NW>;                   // S tiles
+  using OM = Owner<DT, ET, NW>;                   // M, C and G tiles
+  constexpr int PSL = (TR * DT + NW - 1) / NW;    // P slots per wave (row block wave % TR)
+  constexpr int OSL = (TR * ET + NW - 1) / NW;    // O slots per wave
+  constexpr int CT = MODE == MODE_SUMMARY ? OM::SLOTS : 1;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
   T* Ks = reinterpret_cast<T*>(smem + L::Ks);
   T* Kt = reinterpret_cast<T*>(smem + L::Kt);
   T* Vt = reinterpret_cast<T*>(smem + L::Vt);
-  T* X1 = reinterpret_cast<T*>(smem + L::X1);   // Qt or Ps
+  T* X1 = reinterpret_cast<T*>(smem + L::X1);   // Qt (summary) or Ps (output)
   T* Pt = reinterpret_cast<T*>(smem + L::Pt);
   T* AB = reinterpret_cast<T*>(smem + L::AB);
   T* SM = reinterpret_cast<T*>(smem + L::SM);
@@ -111,7 +151,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
   float* pw = wM + TT;
   float* pw2 = pw + TT;
   float* qn = pw2 + TT;
-  float* bpart = qn + TT;        // [TR][TT]: row sums of B per 16-column block (fixed order)
+  float* bpart = qn + TT;        // [TR][TT]: row sums of B per 16-column block
   float* pcol = bpart + TR * TT; // [TR][D]: weighted column sums of P per 16-row block
   float* nst = pcol + TR * D;
   float* mst = nst + D;
@@ -131,7 +171,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
   const size_t sidx = (size_t)unit * nspan + span;
   const bool need_n = MODE == MODE_SUMMARY || a.normalize || a.den != nullptr;
 
-  f32x4 Sreg[ST], Mreg[MT], Creg[CT];
+  f32x4 Sreg[OS::SLOTS], Mreg[OM::SLOTS], Creg[CT];
 
   if (tid < TT) {
     pw[tid] = gpow(g, lgg, tid);
@@ -143,9 +183,9 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
   // ---- initial state -------------------------------------------------------
   if (MODE == MODE_SUMMARY) {
 #pragma unroll
-    for (int s = 0; s < ST; ++s) Sreg[s] = zero4();
+    for (int s = 0; s < OS::SLOTS; ++s) Sreg[s] = zero4();
 #pragma unroll
-    for (int s = 0; s < MT; ++s) Mreg[s] = zero4();
+    for (int s = 0; s < OM::SLOTS; ++s) Mreg[s] = zero4();
 #pragma unroll
     for (int s = 0; s < CT; ++s) Creg[s] = zero4();
     for (int i = tid; i < D; i += NTHR) { nst[i] = 0.f; mst[i] = 0.f; }
@@ -163,22 +203,20 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int id = wave + NWAVE * s;
-      if (id < DT * DT) {
-        const int r0 = 16 * (id / DT), c0 = 16 * (id % DT);
+    for (int s = 0; s < OS::SLOTS; ++s) {
+      int rb, cb;
+      if (OS::tile(wave, s, rb, cb)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Sreg[s][j] = FS[(r0 + 4 * lg4 + j) * L::LFS + c0 + lr];
+        for (int j = 0; j < 4; ++j) Sreg[s][j] = FS[(16 * rb + 4 * lg4 + j) * L::LFS + 16 * cb + lr];
       }
     }
 #pragma unroll
-    for (int s = 0; s < MT; ++s) {
-      const int id = wave + NWAVE * s;
-      if (id < DT * ET) {
-        const int r0 = 16 * (id / ET), c0 = 16 * (id % ET);
-        f32x4 acc = gemm_f32_tile<D>(FS, L::LFS, FC, L::LFC, r0, c0, lane, zero4());
+    for (int s = 0; s < OM::SLOTS; ++s) {
+      int rb, cb;
+      if (OM::tile(wave, s, rb, cb)) {
+        f32x4 acc = gemm_f32_tile<D>(FS, L::LFS, FC, L::LFC, 16 * rb, 16 * cb, lane, zero4());
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] -= pG[(size_t)(r0 + 4 * lg4 + j) * E + c0 + lr];
+        for (int j = 0; j < 4; ++j) acc[j] -= pG[(size_t)(16 * rb + 4 * lg4 + j) * E + 16 * cb + lr];
         Mreg[s] = acc;
       }
     }
@@ -195,77 +233,101 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
   __syncthreads();
 
   // ---- tile staging (global -> registers -> LDS) -----------------------------
-  constexpr int QCH = TT * D / CH, VCH = TT * E / CH;
-  constexpr int QPT = (QCH + NTHR - 1) / NTHR, VPT = (VCH + NTHR - 1) / NTHR;
-  uint4 rq[QPT], rk[QPT], rv[VPT];
+  // The next tile is not prefetched into registers: with the state held in
+  // accumulators the extra live registers spill, which costs more than the
+  // exposed load latency.
+  // Row-major copies (Qs, Ks): thread <-> consecutive 16-byte chunks of a row,
+  // so both the global loads and the LDS writes are contiguous.
+  // Transposed copies (Kt, Vt and, for summaries, Qt = X1): one item is 4 rows x
+  // one 16-byte column chunk; the 16 lanes of a quarter-wave take 16 row
+  // quads of the same column chunk, so each packed 4-row write of a column is
+  // one 8-byte (bf16) / 16-byte (fp32) store into consecutive LDS words.
+  constexpr int RCH = TT * D / CH;                       // row chunks per tensor
+  constexpr int RPT = (2 * RCH + NTHR - 1) / NTHR;
+  constexpr int IK = (TT / 4) * (D / CH), IV = (TT / 4) * (E / CH);
+  constexpr int NIT = IK + IV + (MODE == MODE_SUMMARY ? IK : 0);
+  constexpr int TPT = (NIT + NTHR - 1) / NTHR;
+  uint4 rrow[RPT];
+  uint4 rtr[TPT][4];
   auto load_tile = [&](int t0, int Lt) {
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
+    for (int i = 0; i < RPT; ++i) {
       const int c = tid + NTHR * i;
-      rq[i] = make_uint4(0, 0, 0, 0);
-      rk[i] = make_uint4(0, 0, 0, 0);
-      if (c < QCH) {
-        const int row = c / (D / CH), col = (c % (D / CH)) * CH;
-        if (row < Lt) {
-          rq[i] = *reinterpret_cast<const uint4*>(gq + (size_t)(t0 + row) * D + col);
-          rk[i] = *reinterpret_cast<const uint4*>(gk + (size_t)(t0 + row) * D + col);
-        }
+      rrow[i] = make_uint4(0, 0, 0, 0);
+      if (c < 2 * RCH) {
+        const int cl = c < RCH ? c : c - RCH;
+        const T* src = c < RCH ? gq : gk;
+        const int row = cl / (D / CH), col = (cl % (D / CH)) * CH;
+        if (row < Lt) rrow[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * D + col);
       }
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + NTHR * i;
-      rv[i] = make_uint4(0, 0, 0, 0);
-      if (c < VCH) {
-        const int row = c / (E / CH), col = (c % (E / CH)) * CH;
-        if (row < Lt) rv[i] = *reinterpret_cast<const uint4*>(gv + (size_t)(t0 + row) * E + col);
+    for (int i = 0; i < TPT; ++i) {
+      const int it = tid + NTHR * i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rtr[i][r] = make_uint4(0, 0, 0, 0);
+      if (it < NIT) {
+        const T* src;
+        int loc, W;
+        if (it < IK) { src = gk; loc = it; W = D; }
+        else if (it < IK + IV) { src = gv; loc = it - IK; W = E; }
+        else { src = gq; loc = it - IK - IV; W = D; }
+        const int rq4 = 4 * (loc % (TT / 4)), col = (loc / (TT / 4)) * CH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (rq4 + r < Lt)
+            rtr[i][r] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + rq4 + r) * W + col);
       }
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
+    for (int i = 0; i < RPT; ++i) {
       const int c = tid + NTHR * i;
-      if (c < QCH) {
-        const int row = c / (D / CH), col = (c % (D / CH)) * CH;
-        *reinterpret_cast<uint4*>(Qs + row * L::LDD + col) = rq[i];
-        *reinterpret_cast<uint4*>(Ks + row * L::LDD + col) = rk[i];
-        const T* ke = reinterpret_cast<const T*>(&rk[i]);
-#pragma unroll
-        for (int e = 0; e < CH; ++e) Kt[(col + e) * L::LDT + row] = ke[e];
-        if (MODE == MODE_SUMMARY) {
-          const T* qe = reinterpret_cast<const T*>(&rq[i]);
-#pragma unroll
-          for (int e = 0; e < CH; ++e) X1[(col + e) * L::LDT + row] = qe[e];
-        }
+      if (c < 2 * RCH) {
+        const int cl = c < RCH ? c : c - RCH;
+        T* dst = c < RCH ? Qs : Ks;
+        const int row = cl / (D / CH), col = (cl % (D / CH)) * CH;
+        *reinterpret_cast<uint4*>(dst + row * L::LDD + col) = rrow[i];
       }
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + NTHR * i;
-      if (c < VCH) {
-        const int row = c / (E / CH), col = (c % (E / CH)) * CH;
-        const T* ve = reinterpret_cast<const T*>(&rv[i]);
+    for (int i = 0; i < TPT; ++i) {
+      const int it = tid + NTHR * i;
+      if (it < NIT) {
+        T* dst;
+        int loc;
+        if (it < IK) { dst = Kt; loc = it; }
+        else if (it < IK + IV) { dst = Vt; loc = it - IK; }
+        else { dst = X1; loc = it - IK - IV; }
+        const int rq4 = 4 * (loc % (TT / 4)), col = (loc / (TT / 4)) * CH;
+        const T* e0 = reinterpret_cast<const T*>(&rtr[i][0]);
+        const T* e1 = reinterpret_cast<const T*>(&rtr[i][1]);
+        const T* e2 = reinterpret_cast<const T*>(&rtr[i][2]);
+        const T* e3 = reinterpret_cast<const T*>(&rtr[i][3]);
 #pragma unroll
-        for (int e = 0; e < CH; ++e) Vt[(col + e) * L::LDT + row] = ve[e];
+        for (int e = 0; e < CH; ++e) store4_raw<T>(dst + (col + e) * L::LDT + rq4, e0[e], e1[e], e2[e], e3[e]);
       }
     }
   };
 
+  if (DP > D) {
+    // padding columns [D, DP) of the d-contraction buffers must read as zero
+    for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
+      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
   const int ntiles = (Lspan + TT - 1) / TT;
-  load_tile(0, Lspan < TT ? Lspan : TT);
   int Lt_prev = -1;
+  const int rw = wave % TR;   // row block of the wave's P and O tiles
 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = ti * TT;
     const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
 
     // ---- step 0: stage tile, state operand, per-tile weights ----------------
+    load_tile(t0, Lt);
     store_tile();
-    if (ti + 1 < ntiles) {
-      const int t1 = t0 + TT;
-      load_tile(t1, (Lspan - t1) < TT ? (Lspan - t1) : TT);
-    }
     if (Lt != Lt_prev && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
       wM[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
@@ -273,30 +335,32 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     Lt_prev = Lt;
     // S operand: SM[n][k] = S[k][n]
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int id = wave + NWAVE * s;
-      if (id < DT * DT) {
-        const int r0 = 16 * (id / DT), c0 = 16 * (id % DT);
-        store4<T>(SM + (c0 + lr) * L::LDSM + r0 + 4 * lg4, Sreg[s]);
-      }
+    for (int s = 0; s < OS::SLOTS; ++s) {
+      int rb, cb;
+      if (OS::tile(wave, s, rb, cb)) store4<T>(SM + (16 * cb + lr) * L::LDSM + 16 * rb + 4 * lg4, Sreg[s]);
     }
     __syncthreads();
 
-    if (need_n && MODE == MODE_OUTPUT && tid < TT) {
+    if (need_n && MODE == MODE_OUTPUT) {
       // q_tau . n_prev for the denominator (n is updated later in the tile)
+      constexpr int LPR = NTHR / TT;
+      const int tau = tid / LPR, part = tid % LPR;
       float acc = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < D; ++c) acc += (float)Qs[tid * L::LDD + c] * nst[c];
-      qn[tid] = acc;
+#pragma unroll
+      for (int c = part * (D / LPR); c < (part + 1) * (D / LPR); ++c)
+        acc += (float)Qs[tau * L::LDD + c] * nst[c];
+#pragma unroll
+      for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
+      if (part == 0) qn[tau] = acc;
     }
 
     // ---- step 1: A' = (Q K^T) o decay, lower triangle ------------------------
-    for (int id = wave; id < TR * TR; id += NWAVE) {
+    for (int id = wave; id < TR * TR; id += NW) {
       const int r = id / TR, c = id % TR;
       f32x4 acc = zero4();
       if (c <= r) {
 #pragma unroll
-        for (int k0 = 0; k0 < D; k0 += KS)
+        for (int k0 = 0; k0 < DP; k0 += KS)
           acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * r, k0, lane), MMT::ld(Ks, L::LDD, 16 * c, k0, lane), acc);
       }
       const int i = 16 * c + lr;
@@ -310,35 +374,36 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
 
     // ---- step 2: P = g^(tau+1) Q S_prev + A' K ---------------------------------
-    f32x4 Preg[PT];
+    {
+      F qf[DP / KS];
 #pragma unroll
-    for (int s = 0; s < PT; ++s) {
-      const int id = wave + NWAVE * s;
-      Preg[s] = zero4();
-      if (id < TR * DT) {
-        const int r = id % TR, n0 = 16 * (id / TR);
-        f32x4 acc = zero4();
+      for (int kk = 0; kk < DP / KS; ++kk) qf[kk] = MMT::ld(Qs, L::LDD, 16 * rw, kk * KS, lane);
+      const f32x4 w1v = *reinterpret_cast<const f32x4*>(w1 + 16 * rw + 4 * lg4);
+      const f32x4 wMv = *reinterpret_cast<const f32x4*>(wM + 16 * rw + 4 * lg4);
 #pragma unroll
-        for (int k0 = 0; k0 < D; k0 += KS)
-          acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * r, k0, lane), MMT::ld(SM, L::LDSM, n0, k0, lane), acc);
+      for (int s = 0; s < PSL; ++s) {
+        const int cb = wave / TR + (NW / TR) * s;
+        if (cb < DT) {
+          const int n0 = 16 * cb;
+          f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] *= w1[16 * r + 4 * lg4 + j];
-        const int kend = 16 * r + 16;
-        for (int k0 = 0; k0 < kend; k0 += KS)
-          acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), MMT::ld(Kt, L::LDT, n0, k0, lane), acc);
-        Preg[s] = acc;
-        // Pt[d][tau] = g^(2(Lt-1-tau)) p_tau[d] (M update operand, weighted once)
-        f32x4 pwv;
+          for (int kk = 0; kk < DP / KS; ++kk)
+            acc = MMT::mma(qf[kk], MMT::ld(SM, L::LDSM, n0, kk * KS, lane), acc);
+          acc *= w1v;
+          const int kend = 16 * rw + 16;
+          for (int k0 = 0; k0 < kend; k0 += KS)
+            acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * rw, k0, lane), MMT::ld(Kt, L::LDT, n0, k0, lane), acc);
+          // Pt[d][tau] = g^(2(Lt-1-tau)) p_tau[d] (M update operand, weighted once)
+          const f32x4 pwv = acc * wMv;
+          store4<T>(Pt + (n0 + lr) * L::LDT + 16 * rw + 4 * lg4, pwv);
+          if (MODE == MODE_OUTPUT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pwv[j] = acc[j] * wM[16 * r + 4 * lg4 + j];
-        store4<T>(Pt + (n0 + lr) * L::LDT + 16 * r + 4 * lg4, pwv);
-        if (MODE == MODE_OUTPUT) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) X1[(16 * r + 4 * lg4 + j) * L::LDD + n0 + lr] = (T)acc[j];
-        }
-        if (need_n) {
-          const float cs = sum_rows4(pwv[0] + pwv[1] + pwv[2] + pwv[3]);
-          if (lg4 == 0) pcol[r * D + n0 + lr] = cs;
+            for (int j = 0; j < 4; ++j) X1[(16 * rw + 4 * lg4 + j) * L::LDD + n0 + lr] = (T)acc[j];
+          }
+          if (need_n) {
+            const float cs = sum_rows4(pwv[0] + pwv[1] + pwv[2] + pwv[3]);
+            if (lg4 == 0) pcol[rw * D + n0 + lr] = cs;
+          }
         }
       }
     }
@@ -348,19 +413,16 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     if (MODE == MODE_OUTPUT) {
       // M operand (state before this tile): SM[e][d] = M[d][e]
 #pragma unroll
-      for (int s = 0; s < MT; ++s) {
-        const int id = wave + NWAVE * s;
-        if (id < DT * ET) {
-          const int r0 = 16 * (id / ET), c0 = 16 * (id % ET);
-          store4<T>(SM + (c0 + lr) * L::LDSM + r0 + 4 * lg4, Mreg[s]);
-        }
+      for (int s = 0; s < OM::SLOTS; ++s) {
+        int rb, cb;
+        if (OM::tile(wave, s, rb, cb)) store4<T>(SM + (16 * cb + lr) * L::LDSM + 16 * rb + 4 * lg4, Mreg[s]);
       }
-      for (int id = wave; id < TR * TR; id += NWAVE) {
+      for (int id = wave; id < TR * TR; id += NW) {
         const int r = id / TR, c = id % TR;
         f32x4 acc = zero4();
         if (c <= r) {
 #pragma unroll
-          for (int k0 = 0; k0 < D; k0 += KS)
+          for (int k0 = 0; k0 < DP; k0 += KS)
             acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * r, k0, lane), MMT::ld(X1, L::LDD, 16 * c, k0, lane), acc);
         }
         const int jj = 16 * c + lr;
@@ -378,43 +440,65 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     }
     {
       const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+      // S <- g^Lt S + K^T diag(wS) K; the weights ride on the B fragments,
+      // which a wave shares across the tiles of one column block
+      {
+        F bk[NKS];
 #pragma unroll
-      for (int s = 0; s < ST; ++s) {
-        const int id = wave + NWAVE * s;
-        if (id < DT * DT) {
-          const int r0 = 16 * (id / DT), c0 = 16 * (id % DT);
-          f32x4 acc = Sreg[s] * gL;
+        for (int s = 0; s < OS::SLOTS; ++s) {
+          int rb, cb;
+          if (OS::tile(wave, s, rb, cb)) {
+            if (OS::new_col(s)) {
 #pragma unroll
-          for (int k0 = 0; k0 < TT; k0 += KS)
-            acc = MMT::mma(MMT::ldw(Kt, L::LDT, r0, k0, lane, wS), MMT::ld(Kt, L::LDT, c0, k0, lane), acc);
-          Sreg[s] = acc;
+              for (int kk = 0; kk < NKS; ++kk) bk[kk] = MMT::ldw(Kt, L::LDT, 16 * cb, kk * KS, lane, wS);
+            }
+            f32x4 acc = Sreg[s] * gL;
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk)
+              acc = MMT::mma(MMT::ld(Kt, L::LDT, 16 * rb, kk * KS, lane), bk[kk], acc);
+            Sreg[s] = acc;
+          }
         }
       }
+      // M <- g^2Lt M + Pt V (Pt carries the weights); C <- g^Lt C + Q^T diag(wS) V
+      {
+        F bv[NKS], bvw[MODE == MODE_SUMMARY ? NKS : 1];
 #pragma unroll
-      for (int s = 0; s < MT; ++s) {
-        const int id = wave + NWAVE * s;
-        if (id < DT * ET) {
-          const int r0 = 16 * (id / ET), c0 = 16 * (id % ET);
-          f32x4 acc = Mreg[s] * g2L;
+        for (int s = 0; s < OM::SLOTS; ++s) {
+          int rb, cb;
+          if (OM::tile(wave, s, rb, cb)) {
+            if (OM::new_col(s)) {
 #pragma unroll
-          for (int k0 = 0; k0 < TT; k0 += KS)
-            acc = MMT::mma(MMT::ld(Pt, L::LDT, r0, k0, lane), MMT::ld(Vt, L::LDT, c0, k0, lane), acc);
-          Mreg[s] = acc;
-          if (MODE == MODE_SUMMARY) {
-            f32x4 cacc = Creg[s] * gL;
+              for (int kk = 0; kk < NKS; ++kk) {
+                bv[kk] = MMT::ld(Vt, L::LDT, 16 * cb, kk * KS, lane);
+                if (MODE == MODE_SUMMARY) bvw[kk] = MMT::ldw(Vt, L::LDT, 16 * cb, kk * KS, lane, wS);
+              }
+            }
+            f32x4 acc = Mreg[s] * g2L;
 #pragma unroll
-            for (int k0 = 0; k0 < TT; k0 += KS)
-              cacc = MMT::mma(MMT::ldw(X1, L::LDT, r0, k0, lane, wS), MMT::ld(Vt, L::LDT, c0, k0, lane), cacc);
-            Creg[s] = cacc;
+            for (int kk = 0; kk < NKS; ++kk)
+              acc = MMT::mma(MMT::ld(Pt, L::LDT, 16 * rb, kk * KS, lane), bv[kk], acc);
+            Mreg[s] = acc;
+            if (MODE == MODE_SUMMARY) {
+              f32x4 cacc = Creg[s] * gL;
+#pragma unroll
+              for (int kk = 0; kk < NKS; ++kk)
+                cacc = MMT::mma(MMT::ld(X1, L::LDT, 16 * rb, kk * KS, lane), bvw[kk], cacc);
+              Creg[s] = cacc;
+            }
           }
         }
       }
       if (MODE == MODE_SUMMARY) {
-        for (int r = tid; r < D; r += NTHR) {
-          float acc = 0.f;
-          for (int t = 0; t < Lt; ++t) acc += wS[t] * (float)Qs[t * L::LDD + r];
-          mst[r] = gL * mst[r] + acc;
-        }
+        // m <- g^Lt m + sum_tau wS[tau] q_tau: NTHR / D lanes per column,
+        // interleaved rows, then a shuffle reduction
+        constexpr int LPC = NTHR / D;
+        const int col = tid / LPC, part = tid % LPC;
+        float acc = 0.f;
+        for (int t = part; t < Lt; t += LPC) acc += wS[t] * (float)Qs[t * L::LDD + col];
+#pragma unroll
+        for (int off = 1; off < LPC; off *= 2) acc += __shfl_xor(acc, off, 64);
+        if (part == 0) mst[col] = gL * mst[col] + acc;
       }
       if (need_n) {
         for (int r = tid; r < D; r += NTHR) {
@@ -437,23 +521,26 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
         for (int c = 0; c <= tau / 16; ++c) acc += bpart[c * TT + tau];
         return acc + w2[tau] * qn[tau];
       };
+      F qf[DP / KS];
 #pragma unroll
-      for (int s = 0; s < OT; ++s) {
-        const int id = wave + NWAVE * s;
-        if (id < TR * ET) {
-          const int r = id % TR, e0 = 16 * (id / TR);
+      for (int kk = 0; kk < DP / KS; ++kk) qf[kk] = MMT::ld(Qs, L::LDD, 16 * rw, kk * KS, lane);
+      const f32x4 w2v = *reinterpret_cast<const f32x4*>(w2 + 16 * rw + 4 * lg4);
+#pragma unroll
+      for (int s = 0; s < OSL; ++s) {
+        const int cb = wave / TR + (NW / TR) * s;
+        if (cb < ET) {
+          const int e0 = 16 * cb;
           f32x4 acc = zero4();
 #pragma unroll
-          for (int k0 = 0; k0 < D; k0 += KS)
-            acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * r, k0, lane), MMT::ld(SM, L::LDSM, e0, k0, lane), acc);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] *= w2[16 * r + 4 * lg4 + j];
-          const int kend = 16 * r + 16;
+          for (int kk = 0; kk < DP / KS; ++kk)
+            acc = MMT::mma(qf[kk], MMT::ld(SM, L::LDSM, e0, kk * KS, lane), acc);
+          acc *= w2v;
+          const int kend = 16 * rw + 16;
           for (int k0 = 0; k0 < kend; k0 += KS)
-            acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), MMT::ld(Vt, L::LDT, e0, k0, lane), acc);
+            acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * rw, k0, lane), MMT::ld(Vt, L::LDT, e0, k0, lane), acc);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int tau = 16 * r + 4 * lg4 + j;
+            const int tau = 16 * rw + 4 * lg4 + j;
             float val = acc[j];
             if (a.normalize) val = val / (den_of(tau) + a.eps);
             if (tau < Lt) go[(size_t)tau * E + e0 + lr] = val;
@@ -471,40 +558,38 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
     float* oC = a.C + sidx * D * E;
     float* oG = a.G + sidx * D * E;
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int id = wave + NWAVE * s;
-      if (id < DT * DT) {
-        const int r0 = 16 * (id / DT), c0 = 16 * (id % DT);
+    for (int s = 0; s < OS::SLOTS; ++s) {
+      int rb, cb;
+      if (OS::tile(wave, s, rb, cb)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = r0 + 4 * lg4 + j;
-          FS[r * L::LFS + c0 + lr] = Sreg[s][j];
-          oS[(size_t)r * D + c0 + lr] = Sreg[s][j];
+          const int r = 16 * rb + 4 * lg4 + j;
+          FS[r * L::LFS + 16 * cb + lr] = Sreg[s][j];
+          oS[(size_t)r * D + 16 * cb + lr] = Sreg[s][j];
         }
       }
     }
 #pragma unroll
     for (int s = 0; s < CT; ++s) {
-      const int id = wave + NWAVE * s;
-      if (id < DT * ET) {
-        const int r0 = 16 * (id / ET), c0 = 16 * (id % ET);
+      int rb, cb;
+      if (OM::tile(wave, s, rb, cb)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = r0 + 4 * lg4 + j;
-          FC[r * L::LFC + c0 + lr] = Creg[s][j];
-          oC[(size_t)r * E + c0 + lr] = Creg[s][j];
+          const int r = 16 * rb + 4 * lg4 + j;
+          FC[r * L::LFC + 16 * cb + lr] = Creg[s][j];
+          oC[(size_t)r * E + 16 * cb + lr] = Creg[s][j];
         }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < MT; ++s) {
-      const int id = wave + NWAVE * s;
-      if (id < DT * ET) {
-        const int r0 = 16 * (id / ET), c0 = 16 * (id % ET);
-        f32x4 acc = gemm_f32_tile<D>(FS, L::LFS, FC, L::LFC, r0, c0, lane, zero4());
+    for (int s = 0; s < OM::SLOTS; ++s) {
+      int rb, cb;
+      if (OM::tile(wave, s, rb, cb)) {
+        f32x4 acc = gemm_f32_tile<D>(FS, L::LFS, FC, L::LFC, 16 * rb, 16 * cb, lane, zero4());
 #pragma unroll
-        for (int j = 0; j < 4; ++j) oG[(size_t)(r0 + 4 * lg4 + j) * E + c0 + lr] = acc[j] - Mreg[s][j];
+        for (int j = 0; j < 4; ++j)
+          oG[(size_t)(16 * rb + 4 * lg4 + j) * E + 16 * cb + lr] = acc[j] - Mreg[s][j];
       }
     }
     for (int r = tid; r < D; r += NTHR) {
@@ -520,11 +605,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(ChunkArgs a) {
 
 template <int MODE>
 static hipError_t launch_mode(int dtype, int d, int dv, int units, const ChunkArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)units * (unsigned)a.nspan), block(NTHR);
-#define HLA_CASE(T, D, E)                                                            \
-  if (d == D && dv == E) {                                                           \
-    hipLaunchKernelGGL((chunk_kernel<T, D, E, MODE>), grid, block, 0, s, a);         \
-    return hipGetLastError();                                                        \
+  const dim3 grid((unsigned)units * (unsigned)a.nspan);
+#define HLA_CASE(T, D, E)                                                                    \
+  if (d == D && dv == E) {                                                                   \
+    constexpr int NW = 8;                                                                    \
+    hipLaunchKernelGGL((chunk_kernel<T, D, E, MODE, NW>), grid, dim3(64 * NW), 0, s, a);     \
+    return hipGetLastError();                                                                \
   }
   if (dtype == 1) {
     HLA_CASE(__bf16, 16, 16) HLA_CASE(__bf16, 16, 32) HLA_CASE(__bf16, 32, 16)

@@ -11,18 +11,23 @@
 //
 // The n summaries of each (b, h) unit are scanned as an array of N = 2^ceil(log2 n)
 // slots; slots >= n are identities kept in a caller-provided workspace.  Each
-// tree level is one launch (grid: pairs x units, one workgroup per combine),
-// so the whole array level finishes before the next starts.  A workgroup
-// reads everything it needs (the cross-term operands into LDS) before it
-// writes, so the in-place down-sweep (left <- parent, right <- parent (+) left)
-// has no read/write race.  The D x D by D x dv cross term runs on fp32 MFMA.
+// tree level is one or two launches, so a level finishes before the next one
+// starts:
+//   up-sweep level:   x[j] <- x[i] (+) x[j]
+//   down-sweep level: swap x[i] and x[j] (left <- parent prefix, right <- left
+//                     sum), then x[j] <- x[i] (+) x[j] (= parent (+) left sum)
+// with i = j - step for every pair of the level.  The combine is split over
+// workgroups by 16-row blocks of the D-row state: a workgroup reads and writes
+// only rows of x[j] it owns, and x[i] is read-only, so there is no race.  The
+// cross terms S_B C_A and S_B m_A run on fp32 MFMA with C_A staged in LDS.
 #include "hla_device.h"
 #include "hla_internal.h"
 
 namespace hla {
 
-constexpr int SCAN_THR = 512;
+constexpr int SCAN_THR = 256;
 constexpr int SCAN_WAVES = SCAN_THR / 64;
+constexpr int SCAN_RB = 16;      // state rows per combine workgroup
 
 struct Slot {
   float *S, *C, *m, *G, *h;
@@ -49,79 +54,95 @@ __device__ __forceinline__ int real_len(int lo, int hi, int n) {
   return h >= lo ? h - lo + 1 : 0;
 }
 
+// x[j] <- x[i] (+) x[j] for every pair of one level; blockIdx.x = pair * (D/RB) + row block.
+// a = gamma^(tokens in x[j]'s subtree): the right subtree (up-sweep) or, after
+// the swap, the left subtree (down-sweep).
 template <int D, int E>
-__global__ __launch_bounds__(SCAN_THR) void scan_level_kernel(ScanArgs a, int down) {
-  constexpr int LDS_ = D + 4, LDC = E + 4;
-  constexpr int DT = D / 16, ET = E / 16;
-  __shared__ __attribute__((aligned(16))) float sS[D * LDS_];
+__global__ __launch_bounds__(SCAN_THR) void scan_combine_kernel(ScanArgs a, int down) {
+  constexpr int LDC = E + 4, LDS_ = D + 4, ET = E / 16, NRB = D / SCAN_RB;
   __shared__ __attribute__((aligned(16))) float sC[D * LDC];
+  __shared__ __attribute__((aligned(16))) float sS[SCAN_RB * LDS_];
   __shared__ float sm[D];
 
   const int unit = blockIdx.y;
   const int step = a.step;
-  const int j = (blockIdx.x + 1) * 2 * step - 1;
+  const int pair = blockIdx.x / NRB, rb = blockIdx.x % NRB;
+  const int j = (pair + 1) * 2 * step - 1;
   const int i = j - step;
   if (i - step + 1 >= a.n) return;   // both subtrees are padding: identity (+) identity
-
-  // up-sweep:   x[j] <- x[i] (+) x[j]                    (A = x[i], B = x[j])
-  // down-sweep: x[i] <- x[j];  x[j] <- x[j] (+) old x[i]  (A = x[j], B = x[i])
-  const Slot xi = slot_ptr(a, unit, i), xj = slot_ptr(a, unit, j);
-  const Slot A = down ? xj : xi;
-  const Slot B = down ? xi : xj;
+  const Slot A = slot_ptr(a, unit, i), B = slot_ptr(a, unit, j);
   const int lenB = down ? real_len(i - step + 1, i, a.n) : real_len(j - step + 1, j, a.n);
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float al = gpow(g, log2f(g), lenB * a.chunk);
   const float al2 = al * al;
+  const int r0 = rb * SCAN_RB;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int t = tid; t < D * D / 4; t += SCAN_THR) {
-    const int r = (4 * t) / D, c = (4 * t) % D;
-    *reinterpret_cast<f32x4*>(sS + r * LDS_ + c) = reinterpret_cast<const f32x4*>(B.S)[t];
-  }
   for (int t = tid; t < D * E / 4; t += SCAN_THR) {
     const int r = (4 * t) / E, c = (4 * t) % E;
     *reinterpret_cast<f32x4*>(sC + r * LDC + c) = reinterpret_cast<const f32x4*>(A.C)[t];
   }
+  for (int t = tid; t < SCAN_RB * D / 4; t += SCAN_THR) {
+    const int r = (4 * t) / D, c = (4 * t) % D;
+    *reinterpret_cast<f32x4*>(sS + r * LDS_ + c) =
+        reinterpret_cast<const f32x4*>(B.S + (size_t)r0 * D)[t];
+  }
   for (int t = tid; t < D; t += SCAN_THR) sm[t] = A.m[t];
   __syncthreads();
 
-  // G = a^2 G_A + G_B + a S_B C_A
-  for (int id = wave; id < DT * ET; id += SCAN_WAVES) {
-    const int r0 = 16 * (id / ET), c0 = 16 * (id % ET);
-    const f32x4 acc = gemm_f32_tile<D>(sS, LDS_, sC, LDC, r0, c0, lane, zero4());
+  // G rows [r0, r0 + 16): a^2 G_A + G_B + a S_B C_A
+  for (int et = wave; et < ET; et += SCAN_WAVES) {
+    const f32x4 acc = gemm_f32_tile<D>(sS, LDS_, sC, LDC, 0, 16 * et, lane, zero4());
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const size_t e = (size_t)(r0 + 4 * (lane >> 4) + q) * E + c0 + (lane & 15);
-      const float gA = A.G[e], gB = B.G[e];
-      xj.G[e] = al2 * gA + gB + al * acc[q];
-      if (down) xi.G[e] = gA;
+      const size_t e = (size_t)(r0 + 4 * (lane >> 4) + q) * E + 16 * et + (lane & 15);
+      B.G[e] = al2 * A.G[e] + B.G[e] + al * acc[q];
     }
   }
-  // h = a^2 h_A + h_B + a S_B m_A
-  for (int r = tid; r < D; r += SCAN_THR) {
+  // h rows: a^2 h_A + h_B + a S_B m_A
+  for (int r = tid; r < SCAN_RB; r += SCAN_THR) {
     float acc = 0.f;
     for (int c = 0; c < D; ++c) acc += sS[r * LDS_ + c] * sm[c];
-    const float hA = A.h[r], hB = B.h[r];
-    xj.h[r] = al2 * hA + hB + al * acc;
-    if (down) xi.h[r] = hA;
+    B.h[r0 + r] = al2 * A.h[r0 + r] + B.h[r0 + r] + al * acc;
   }
-  // S, C, m: a X_A + X_B
-  for (int t = tid; t < D * D / 4; t += SCAN_THR) {
-    const f32x4 sa = reinterpret_cast<const f32x4*>(A.S)[t];
-    const f32x4 sb = reinterpret_cast<const f32x4*>(B.S)[t];
-    reinterpret_cast<f32x4*>(xj.S)[t] = sa * al + sb;
-    if (down) reinterpret_cast<f32x4*>(xi.S)[t] = sa;
+  // S, C, m rows: a X_A + X_B
+  for (int t = tid; t < SCAN_RB * D / 4; t += SCAN_THR) {
+    const size_t e = (size_t)r0 * D / 4 + t;
+    reinterpret_cast<f32x4*>(B.S)[e] = reinterpret_cast<const f32x4*>(A.S)[e] * al +
+                                       reinterpret_cast<const f32x4*>(B.S)[e];
   }
-  for (int t = tid; t < D * E / 4; t += SCAN_THR) {
-    const f32x4 ca = reinterpret_cast<const f32x4*>(A.C)[t];
-    const f32x4 cb = reinterpret_cast<const f32x4*>(B.C)[t];
-    reinterpret_cast<f32x4*>(xj.C)[t] = ca * al + cb;
-    if (down) reinterpret_cast<f32x4*>(xi.C)[t] = ca;
+  for (int t = tid; t < SCAN_RB * E / 4; t += SCAN_THR) {
+    const size_t e = (size_t)r0 * E / 4 + t;
+    reinterpret_cast<f32x4*>(B.C)[e] = reinterpret_cast<const f32x4*>(A.C)[e] * al +
+                                       reinterpret_cast<const f32x4*>(B.C)[e];
   }
-  for (int t = tid; t < D; t += SCAN_THR) {
-    const float ma = A.m[t], mb = B.m[t];
-    xj.m[t] = al * ma + mb;
-    if (down) xi.m[t] = ma;
+  for (int t = tid; t < SCAN_RB; t += SCAN_THR) B.m[r0 + t] = al * A.m[r0 + t] + B.m[r0 + t];
+}
+
+// Down-sweep first half: x[i] <-> x[j] for every pair of one level.
+// blockIdx.x = pair * parts + part; every element is swapped by one thread.
+__global__ __launch_bounds__(256) void scan_swap_kernel(ScanArgs a, int parts) {
+  const int unit = blockIdx.y;
+  const int pair = blockIdx.x / parts, part = blockIdx.x % parts;
+  const int j = (pair + 1) * 2 * a.step - 1;
+  const int i = j - a.step;
+  if (i - a.step + 1 >= a.n) return;
+  const Slot x = slot_ptr(a, unit, i), y = slot_ptr(a, unit, j);
+  const int d = a.d, dv = a.dv;
+  const int nS = d * d / 4, nC = d * dv / 4;
+  const int stride = parts * 256;
+  for (int t = part * 256 + threadIdx.x; t < nS + 2 * nC + d / 2; t += stride) {
+    f32x4* p;
+    f32x4* q;
+    int o;
+    if (t < nS) { p = reinterpret_cast<f32x4*>(x.S); q = reinterpret_cast<f32x4*>(y.S); o = t; }
+    else if (t < nS + nC) { p = reinterpret_cast<f32x4*>(x.C); q = reinterpret_cast<f32x4*>(y.C); o = t - nS; }
+    else if (t < nS + 2 * nC) { p = reinterpret_cast<f32x4*>(x.G); q = reinterpret_cast<f32x4*>(y.G); o = t - nS - nC; }
+    else if (t < nS + 2 * nC + d / 4) { p = reinterpret_cast<f32x4*>(x.m); q = reinterpret_cast<f32x4*>(y.m); o = t - nS - 2 * nC; }
+    else { p = reinterpret_cast<f32x4*>(x.h); q = reinterpret_cast<f32x4*>(y.h); o = t - nS - 2 * nC - d / 4; }
+    const f32x4 u = p[o], w = q[o];
+    p[o] = w;
+    q[o] = u;
   }
 }
 
@@ -158,6 +179,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, size_t count) 
 template <int D, int E>
 static hipError_t run_scan(int units, ScanArgs a, float* tS, float* tC, float* tm, float* tG,
                            float* th, hipStream_t s) {
+  constexpr int NRB = D / SCAN_RB;
+  constexpr int VEC = (D * D + 2 * D * E + 2 * D) / 4;       // f32x4 per summary
+  constexpr int PARTS = VEC / 1024 > 0 ? VEC / 1024 : 1;    // swap workgroups per pair
   if (a.N > a.n) {
     // padding slots start as identities (one contiguous workspace region)
     const size_t per = (size_t)D * D + 2 * (size_t)D * E + 2 * (size_t)D;
@@ -169,16 +193,19 @@ static hipError_t run_scan(int units, ScanArgs a, float* tS, float* tC, float* t
   }
   for (int step = 1; step < a.N; step *= 2) {
     a.step = step;
-    hipLaunchKernelGGL((scan_level_kernel<D, E>), dim3(a.N / (2 * step), units), dim3(SCAN_THR), 0, s,
-                       a, 0);
+    hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
+                       dim3(SCAN_THR), 0, s, a, 0);
     if (hipError_t e = hipGetLastError()) return e;
   }
   hipLaunchKernelGGL(scan_root_kernel, dim3(units), dim3(256), 0, s, a, tS, tC, tm, tG, th);
   if (hipError_t e = hipGetLastError()) return e;
   for (int step = a.N / 2; step >= 1; step /= 2) {
     a.step = step;
-    hipLaunchKernelGGL((scan_level_kernel<D, E>), dim3(a.N / (2 * step), units), dim3(SCAN_THR), 0, s,
-                       a, 1);
+    hipLaunchKernelGGL(scan_swap_kernel, dim3(a.N / (2 * step) * PARTS, units), dim3(256), 0, s, a,
+                       PARTS);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
+                       dim3(SCAN_THR), 0, s, a, 1);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

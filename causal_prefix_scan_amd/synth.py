@@ -120,7 +120,7 @@ FWD_WORKLOADS = {
                                        chunk=64, normalize=True, eps=1e-6, k_l2norm=True,
                                        decay=False, tol=2e-2),
     "fwd_decay_bf16_b4h16t16384d128": dict(B=4, H=16, T=16384, d=128, dv=128, dtype="bf16",
-                                           seed=2, chunk=1024, normalize=False, eps=0.0,
+                                           seed=2, chunk=4096, normalize=False, eps=0.0,
                                            k_l2norm=False, decay=True, tol=2e-2),
     "fwd_bf16_b1h32t65536d64": dict(B=1, H=32, T=65536, d=64, dv=64, dtype="bf16", seed=3,
                                     chunk=128, normalize=False, eps=0.0, k_l2norm=False,
