@@ -4,10 +4,10 @@
 // for segment summaries and the chunk-parallel scheme, key contribution 2 for
 // decay).
 //
-// One workgroup (8 waves) owns one segment of `chunk` tokens of one
-// (batch, head) unit and walks it in tiles of TT = 64 tokens.  Inside a
-// segment it does not carry (S, C, m, G, h) but the equivalent pair (S, M)
-// with M_t = S_t C_t - G_t, using the identity
+// One workgroup owns one segment of `chunk` tokens of one (batch, head) unit
+// and walks it in tiles of TT = 64 tokens.  Inside a segment it does not carry
+// (S, C, m, G, h) but the equivalent pair (S, M) with M_t = S_t C_t - G_t,
+// using the identity
 //     S_t C_t - G_t = sum_{j<=t} g^(2(t-j)) S_j q_j v_j^T,
 // so that per tile (tau, i, j = 0-based positions inside the tile, Lt tokens):
 //     A'[tau,i] = g^(tau-i) q_tau.k_i            (i <= tau)
@@ -22,10 +22,21 @@
 // The output kernel starts from the segment's exclusive prefix
 // (S_P, C_P, m_P, G_P, h_P) with M = S_P C_P - G_P and n = S_P m_P - h_P.
 //
-// All products of the tile run on MFMA (bf16 operands for bf16 inputs, fp32
-// operands for fp32 inputs) with fp32 accumulation; the state (S, M, C) is
-// kept in fp32 accumulator registers and copied to LDS as an MFMA operand
-// once per tile.  Segment-boundary products (S C, S m) run on fp32 MFMA.
+// Layout on chip.  The tile is staged row-major only (Q, K, V in LDS);
+// operands that need the token index contiguous per lane are read with the
+// transposing LDS read.  The state lives in fp32 MFMA accumulators: wave w
+// owns column block w (16 columns, all rows) of S and of M (and C), and feeds
+// those accumulators straight back into the MFMA as the B operand of Q S and
+// Q M (Frag::acc_b), so the state never goes through LDS inside the loop.
+// The wave that owns S column block w also produces column block w of P and
+// writes it transposed (P^T, token-contiguous) to LDS; the wave that owns M
+// column block w produces column block w of the output.  Score tiles are
+// computed transposed (K Q^T, P Q^T) so that each lane stores four
+// consecutive positions and sums its column in registers.
+//
+// All products run on MFMA (bf16 operands for bf16 inputs, fp32 operands for
+// fp32 inputs) with fp32 accumulation; segment-boundary products (S C, S m)
+// run on fp32 MFMA.
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -40,30 +51,22 @@ struct ChunkLayout {
   static constexpr int PADT = 16 / (int)sizeof(T);
   // d-contractions run in steps of MM<T>::KS; a smaller d is zero-padded to one step
   static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;
-  static constexpr int LDD = DP + PADT;      // [tok][d] buffers
-  static constexpr int LDT = TT + PADT;      // [d][tok] buffers
-  static constexpr int LDSM = DP + PADT;     // S operand [d][d'] / M operand [e][d]
+  static constexpr int LDD = DP + PADT;      // Qs, Ks: [tok][d]
+  static constexpr int LDV = E + PADT;       // Vs: [tok][e]
+  static constexpr int LDT = TT + PADT;      // PsT: [d][tok], AB: [tok][tok]
   static constexpr size_t Qs = 0;
   static constexpr size_t Ks = Qs + (size_t)TT * LDD * sizeof(T);
-  static constexpr size_t Kt = Ks + (size_t)TT * LDD * sizeof(T);
-  static constexpr size_t Vt = Kt + (size_t)D * LDT * sizeof(T);
-  static constexpr size_t X1 = Vt + (size_t)E * LDT * sizeof(T);  // Qt (summary) / Ps (output)
-  static constexpr size_t X1B = MODE == MODE_SUMMARY ? (size_t)D * LDT * sizeof(T)
-                                                     : (size_t)TT * LDD * sizeof(T);
-  static constexpr size_t Pt = X1 + X1B;
-  static constexpr size_t AB = Pt + (size_t)D * LDT * sizeof(T);
-  static constexpr size_t SM = AB + (size_t)TT * LDT * sizeof(T);
-  static constexpr int SMROWS = (MODE == MODE_OUTPUT && E > D) ? E : D;
-  static constexpr size_t TILE_END = SM + (size_t)SMROWS * LDSM * sizeof(T);
-  // fp32 overlay used at segment boundaries: S [D][D+4], C [D][E+4]
-  static constexpr int LFS = D + 4, LFC = E + 4;
-  static constexpr size_t FS = 0;
-  static constexpr size_t FC = FS + (size_t)D * LFS * 4;
-  static constexpr size_t F_END = FC + (size_t)D * LFC * 4;
+  static constexpr size_t Vs = Ks + (size_t)TT * LDD * sizeof(T);
+  static constexpr size_t PsT = Vs + (size_t)TT * LDV * sizeof(T);
+  static constexpr size_t AB = PsT + (size_t)DP * LDT * sizeof(T);
+  static constexpr size_t TILE_END = AB + (size_t)TT * LDT * sizeof(T);
+  // fp32 overlay used at segment boundaries: S [D][D+4]
+  static constexpr int LFS = D + 4;
+  static constexpr size_t F_END = (size_t)D * LFS * 4;
   static constexpr size_t BIG = TILE_END > F_END ? TILE_END : F_END;
   static constexpr size_t W = (BIG + 15) / 16 * 16;
-  // w1, w2, wS, wM, pw, pw2, qn [TT]; bpart [TR][TT]; pcol [TR][D]; nst, mst [D]
-  static constexpr size_t TOTAL = W + (size_t)(7 * TT + (TT / 16) * TT + (TT / 16) * D + 2 * D) * 4;
+  // w1, w2, wS, wM, pw, pw2, qn [TT]; bpart [TR][TT]; pcol, nst, mst [D]
+  static constexpr size_t TOTAL = W + (size_t)(7 * TT + (TT / 16) * TT + 3 * D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -80,70 +83,36 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
   *reinterpret_cast<f32x4*>(p) = x;
 }
 
-// Four consecutive elements of one LDS row (8 bytes for bf16, 16 for fp32).
-template <typename T>
-__device__ __forceinline__ void store4_raw(T* p, T a, T b, T c, T d);
-template <>
-__device__ __forceinline__ void store4_raw<__bf16>(__bf16* p, __bf16 a, __bf16 b, __bf16 c, __bf16 d) {
-  bf16x4 y;
-  y[0] = a; y[1] = b; y[2] = c; y[3] = d;
-  *reinterpret_cast<bf16x4*>(p) = y;
+// Lower-triangular 16x16 tile number idx (row block r of the later position,
+// column block c <= r) of the TR*(TR+1)/2 such tiles.
+__device__ __forceinline__ void tri_tile(int idx, int& r, int& c) {
+  r = 0;
+  while (idx > r) { idx -= r + 1; ++r; }
+  c = idx;
 }
-template <>
-__device__ __forceinline__ void store4_raw<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
-}
-
-// Ownership of the 16x16 tiles of an R x CB grid (R row blocks, CB column
-// blocks) by the NW waves of a workgroup.  Slot s of wave w holds tile (rb, cb):
-//   CB >= NW: cb = w + NW * (s / R), rb = s % R
-//   CB <  NW: cb = w % CB,          rb = w / CB + (NW / CB) * s
-// so consecutive slots of a wave share a column block, and therefore the B
-// fragments of a product whose B operand depends only on the column.
-template <int R, int CB, int NW>
-struct Owner {
-  static constexpr int SLOTS = (R * CB + NW - 1) / NW;
-  __device__ static __forceinline__ bool tile(int w, int s, int& rb, int& cb) {
-    if (CB >= NW) {
-      cb = w + NW * (s / R);
-      rb = s % R;
-      return cb < CB;
-    }
-    cb = w % CB;
-    rb = w / CB + (NW / CB) * s;
-    return rb < R;
-  }
-  __device__ static __forceinline__ bool new_col(int s) { return CB >= NW ? (s % R) == 0 : s == 0; }
-};
 
 template <typename T, int D, int E, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   constexpr int NTHR = 64 * NW;
   using L = ChunkLayout<T, D, E, MODE>;
   using MMT = MM<T>;
+  using FR = Frag<T>;
   using F = typename MMT::F;
   constexpr int KS = MMT::KS;
   constexpr int CH = MMT::CH;
   constexpr int DP = L::DP;
   constexpr int DT = D / 16, ET = E / 16, TR = TT / 16, NKS = TT / KS;
-  static_assert(NW % TR == 0, "row-block ownership of P and O tiles needs TR | NW");
-  using OS = Owner<DT, DT, NW>;                   // S tiles
-  using OM = Owner<DT, ET, NW>;                   // M, C and G tiles
-  constexpr int PSL = (TR * DT + NW - 1) / NW;    // P slots per wave (row block wave % TR)
-  constexpr int OSL = (TR * ET + NW - 1) / NW;    // O slots per wave
-  constexpr int CT = MODE == MODE_SUMMARY ? OM::SLOTS : 1;
+  constexpr int NTRI = TR * (TR + 1) / 2;
+  constexpr int QSK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps of Q S and Q M
+  static_assert(DT <= NW && ET <= NW, "one state column block per wave");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
   T* Ks = reinterpret_cast<T*>(smem + L::Ks);
-  T* Kt = reinterpret_cast<T*>(smem + L::Kt);
-  T* Vt = reinterpret_cast<T*>(smem + L::Vt);
-  T* X1 = reinterpret_cast<T*>(smem + L::X1);   // Qt (summary) or Ps (output)
-  T* Pt = reinterpret_cast<T*>(smem + L::Pt);
+  T* Vs = reinterpret_cast<T*>(smem + L::Vs);
+  T* PsT = reinterpret_cast<T*>(smem + L::PsT);
   T* AB = reinterpret_cast<T*>(smem + L::AB);
-  T* SM = reinterpret_cast<T*>(smem + L::SM);
-  float* FS = reinterpret_cast<float*>(smem + L::FS);
-  float* FC = reinterpret_cast<float*>(smem + L::FC);
+  float* FS = reinterpret_cast<float*>(smem);
   float* w1 = reinterpret_cast<float*>(smem + L::W);
   float* w2 = w1 + TT;
   float* wS = w2 + TT;
@@ -151,9 +120,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   float* pw = wM + TT;
   float* pw2 = pw + TT;
   float* qn = pw2 + TT;
-  float* bpart = qn + TT;        // [TR][TT]: row sums of B per 16-column block
-  float* pcol = bpart + TR * TT; // [TR][D]: weighted column sums of P per 16-row block
-  float* nst = pcol + TR * D;
+  float* bpart = qn + TT;        // [TR][TT]: B column sums per 16-row block of j
+  float* pcol = bpart + TR * TT; // [D]: weighted column sums of P (one writer per column)
+  float* nst = pcol + D;
   float* mst = nst + D;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -170,8 +139,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
   const size_t sidx = (size_t)unit * nspan + span;
   const bool need_n = MODE == MODE_SUMMARY || a.normalize || a.den != nullptr;
+  const bool ownS = wave < DT, ownM = wave < ET;   // column block `wave` of S / of M, C, G
+  const int cs0 = 16 * wave;                        // first column of the owned block
 
-  f32x4 Sreg[OS::SLOTS], Mreg[OM::SLOTS], Creg[CT];
+  f32x4 Sreg[DT], Mreg[DT], Creg[MODE == MODE_SUMMARY ? DT : 1];
 
   if (tid < TT) {
     pw[tid] = gpow(g, lgg, tid);
@@ -181,15 +152,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   }
 
   // ---- initial state -------------------------------------------------------
+#pragma unroll
+  for (int t = 0; t < DT; ++t) { Sreg[t] = zero4(); Mreg[t] = zero4(); }
   if (MODE == MODE_SUMMARY) {
 #pragma unroll
-    for (int s = 0; s < OS::SLOTS; ++s) Sreg[s] = zero4();
-#pragma unroll
-    for (int s = 0; s < OM::SLOTS; ++s) Mreg[s] = zero4();
-#pragma unroll
-    for (int s = 0; s < CT; ++s) Creg[s] = zero4();
+    for (int t = 0; t < DT; ++t) Creg[t] = zero4();
     for (int i = tid; i < D; i += NTHR) { nst[i] = 0.f; mst[i] = 0.f; }
   } else {
+    // S from the prefix; M = S_P C_P - G_P with S_P staged in LDS (fp32) as the
+    // A operand and the wave's column block of C_P as the B operand
     const float* pS = a.S + sidx * D * D;
     const float* pC = a.C + sidx * D * E;
     const float* pG = a.G + sidx * D * E;
@@ -197,27 +168,29 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       const int r = (4 * i) / D, c = (4 * i) % D;
       *reinterpret_cast<f32x4*>(FS + r * L::LFS + c) = reinterpret_cast<const f32x4*>(pS)[i];
     }
-    for (int i = tid; i < D * E / 4; i += NTHR) {
-      const int r = (4 * i) / E, c = (4 * i) % E;
-      *reinterpret_cast<f32x4*>(FC + r * L::LFC + c) = reinterpret_cast<const f32x4*>(pC)[i];
-    }
     __syncthreads();
+    if (ownS) {
 #pragma unroll
-    for (int s = 0; s < OS::SLOTS; ++s) {
-      int rb, cb;
-      if (OS::tile(wave, s, rb, cb)) {
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Sreg[s][j] = FS[(16 * rb + 4 * lg4 + j) * L::LFS + 16 * cb + lr];
-      }
+        for (int j = 0; j < 4; ++j) Sreg[t][j] = FS[(16 * t + 4 * lg4 + j) * L::LFS + cs0 + lr];
     }
+    if (ownM) {
+      f32x4 cp[DT];
 #pragma unroll
-    for (int s = 0; s < OM::SLOTS; ++s) {
-      int rb, cb;
-      if (OM::tile(wave, s, rb, cb)) {
-        f32x4 acc = gemm_f32_tile<D>(FS, L::LFS, FC, L::LFC, 16 * rb, 16 * cb, lane, zero4());
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] -= pG[(size_t)(16 * rb + 4 * lg4 + j) * E + 16 * cb + lr];
-        Mreg[s] = acc;
+        for (int j = 0; j < 4; ++j) cp[t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + cs0 + lr];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk)
+          acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
+                               Frag<float>::acc_b(cp, kk), acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] -= pG[(size_t)(16 * t + 4 * lg4 + j) * E + cs0 + lr];
+        Mreg[t] = acc;
       }
     }
     if (need_n) {
@@ -229,120 +202,68 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         nst[r] = acc - ph[r];
       }
     }
-  }
-  __syncthreads();
-
-  // ---- tile staging (global -> registers -> LDS) -----------------------------
-  // The next tile is not prefetched into registers: with the state held in
-  // accumulators the extra live registers spill, which costs more than the
-  // exposed load latency.
-  // Row-major copies (Qs, Ks): thread <-> consecutive 16-byte chunks of a row,
-  // so both the global loads and the LDS writes are contiguous.
-  // Transposed copies (Kt, Vt and, for summaries, Qt = X1): one item is 4 rows x
-  // one 16-byte column chunk; the 16 lanes of a quarter-wave take 16 row
-  // quads of the same column chunk, so each packed 4-row write of a column is
-  // one 8-byte (bf16) / 16-byte (fp32) store into consecutive LDS words.
-  constexpr int RCH = TT * D / CH;                       // row chunks per tensor
-  constexpr int RPT = (2 * RCH + NTHR - 1) / NTHR;
-  constexpr int IK = (TT / 4) * (D / CH), IV = (TT / 4) * (E / CH);
-  constexpr int NIT = IK + IV + (MODE == MODE_SUMMARY ? IK : 0);
-  constexpr int TPT = (NIT + NTHR - 1) / NTHR;
-  uint4 rrow[RPT];
-  uint4 rtr[TPT][4];
-  auto load_tile = [&](int t0, int Lt) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int c = tid + NTHR * i;
-      rrow[i] = make_uint4(0, 0, 0, 0);
-      if (c < 2 * RCH) {
-        const int cl = c < RCH ? c : c - RCH;
-        const T* src = c < RCH ? gq : gk;
-        const int row = cl / (D / CH), col = (cl % (D / CH)) * CH;
-        if (row < Lt) rrow[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * D + col);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int it = tid + NTHR * i;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rtr[i][r] = make_uint4(0, 0, 0, 0);
-      if (it < NIT) {
-        const T* src;
-        int loc, W;
-        if (it < IK) { src = gk; loc = it; W = D; }
-        else if (it < IK + IV) { src = gv; loc = it - IK; W = E; }
-        else { src = gq; loc = it - IK - IV; W = D; }
-        const int rq4 = 4 * (loc % (TT / 4)), col = (loc / (TT / 4)) * CH;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (rq4 + r < Lt)
-            rtr[i][r] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + rq4 + r) * W + col);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int c = tid + NTHR * i;
-      if (c < 2 * RCH) {
-        const int cl = c < RCH ? c : c - RCH;
-        T* dst = c < RCH ? Qs : Ks;
-        const int row = cl / (D / CH), col = (cl % (D / CH)) * CH;
-        *reinterpret_cast<uint4*>(dst + row * L::LDD + col) = rrow[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int it = tid + NTHR * i;
-      if (it < NIT) {
-        T* dst;
-        int loc;
-        if (it < IK) { dst = Kt; loc = it; }
-        else if (it < IK + IV) { dst = Vt; loc = it - IK; }
-        else { dst = X1; loc = it - IK - IV; }
-        const int rq4 = 4 * (loc % (TT / 4)), col = (loc / (TT / 4)) * CH;
-        const T* e0 = reinterpret_cast<const T*>(&rtr[i][0]);
-        const T* e1 = reinterpret_cast<const T*>(&rtr[i][1]);
-        const T* e2 = reinterpret_cast<const T*>(&rtr[i][2]);
-        const T* e3 = reinterpret_cast<const T*>(&rtr[i][3]);
-#pragma unroll
-        for (int e = 0; e < CH; ++e) store4_raw<T>(dst + (col + e) * L::LDT + rq4, e0[e], e1[e], e2[e], e3[e]);
-      }
-    }
-  };
-
-  if (DP > D) {
-    // padding columns [D, DP) of the d-contraction buffers must read as zero
-    for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
-      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
   }
+  // zero the tile region once: the upper score tiles and any padding columns
+  // [D, DP) / rows of P^T are read as zeros and never written
+  for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  // ---- tile staging: global -> LDS, row-major, 16-byte chunks ---------------
+  // All loads of a tile are issued before the first LDS store.
+  constexpr int QCH = TT * D / CH, VCH = TT * E / CH;
+  constexpr int NCH = 2 * QCH + VCH;
+  constexpr int SPT = (NCH + NTHR - 1) / NTHR;
+  auto stage_tile = [&](int t0, int Lt) {
+    uint4 x[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int c = tid + NTHR * i;
+      x[i] = make_uint4(0, 0, 0, 0);
+      if (c < NCH) {
+        const T* src;
+        int cl, W;
+        if (c < QCH) { src = gq; cl = c; W = D; }
+        else if (c < 2 * QCH) { src = gk; cl = c - QCH; W = D; }
+        else { src = gv; cl = c - 2 * QCH; W = E; }
+        const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
+        if (row < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int c = tid + NTHR * i;
+      if (c < NCH) {
+        T* dst;
+        int cl, W, LD;
+        if (c < QCH) { dst = Qs; cl = c; W = D; LD = L::LDD; }
+        else if (c < 2 * QCH) { dst = Ks; cl = c - QCH; W = D; LD = L::LDD; }
+        else { dst = Vs; cl = c - 2 * QCH; W = E; LD = L::LDV; }
+        const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
+        *reinterpret_cast<uint4*>(dst + row * LD + col) = x[i];
+      }
+    }
+  };
+
   const int ntiles = (Lspan + TT - 1) / TT;
   int Lt_prev = -1;
-  const int rw = wave % TR;   // row block of the wave's P and O tiles
 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = ti * TT;
     const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
 
-    // ---- step 0: stage tile, state operand, per-tile weights ----------------
-    load_tile(t0, Lt);
-    store_tile();
+    // ---- step 0: stage the tile and the per-tile weights --------------------
+    stage_tile(t0, Lt);
     if (Lt != Lt_prev && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
       wM[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
     }
     Lt_prev = Lt;
-    // S operand: SM[n][k] = S[k][n]
-#pragma unroll
-    for (int s = 0; s < OS::SLOTS; ++s) {
-      int rb, cb;
-      if (OS::tile(wave, s, rb, cb)) store4<T>(SM + (16 * cb + lr) * L::LDSM + 16 * rb + 4 * lg4, Sreg[s]);
-    }
     __syncthreads();
 
+    // ---- step 1: A'^T = (K Q^T) o decay, q.n for the denominator ---------------
     if (need_n && MODE == MODE_OUTPUT) {
-      // q_tau . n_prev for the denominator (n is updated later in the tile)
       constexpr int LPR = NTHR / TT;
       const int tau = tid / LPR, part = tid % LPR;
       float acc = 0.f;
@@ -353,201 +274,168 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
       if (part == 0) qn[tau] = acc;
     }
-
-    // ---- step 1: A' = (Q K^T) o decay, lower triangle ------------------------
-    for (int id = wave; id < TR * TR; id += NW) {
-      const int r = id / TR, c = id % TR;
+    for (int idx = wave; idx < NTRI; idx += NW) {
+      int r, c;
+      tri_tile(idx, r, c);
       f32x4 acc = zero4();
-      if (c <= r) {
 #pragma unroll
-        for (int k0 = 0; k0 < DP; k0 += KS)
-          acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * r, k0, lane), MMT::ld(Ks, L::LDD, 16 * c, k0, lane), acc);
-      }
-      const int i = 16 * c + lr;
+      for (int k0 = 0; k0 < DP; k0 += KS)
+        acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+      // lane: position tau = 16 r + lr, keys i = 16 c + 4 lg4 + j
+      const int tau = 16 * r + lr;
+      f32x4 val;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tau = 16 * r + 4 * lg4 + j;
-        const float val = (i <= tau) ? acc[j] * pw[tau - i] : 0.f;
-        AB[tau * L::LDT + i] = (T)val;
+        const int i = 16 * c + 4 * lg4 + j;
+        val[j] = (i <= tau) ? acc[j] * pw[tau - i] : 0.f;
       }
+      store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
     }
     __syncthreads();
 
-    // ---- step 2: P = g^(tau+1) Q S_prev + A' K ---------------------------------
-    {
-      F qf[DP / KS];
+    // ---- step 2: P = g^(tau+1) Q S_prev + A' K; S update -----------------------
+    if (ownS) {
+      f32x4 pacc[TR];
 #pragma unroll
-      for (int kk = 0; kk < DP / KS; ++kk) qf[kk] = MMT::ld(Qs, L::LDD, 16 * rw, kk * KS, lane);
-      const f32x4 w1v = *reinterpret_cast<const f32x4*>(w1 + 16 * rw + 4 * lg4);
-      const f32x4 wMv = *reinterpret_cast<const f32x4*>(wM + 16 * rw + 4 * lg4);
+      for (int r = 0; r < TR; ++r) pacc[r] = zero4();
 #pragma unroll
-      for (int s = 0; s < PSL; ++s) {
-        const int cb = wave / TR + (NW / TR) * s;
-        if (cb < DT) {
-          const int n0 = 16 * cb;
-          f32x4 acc = zero4();
+      for (int kk = 0; kk < QSK; ++kk) {
+        const F b = FR::acc_b(Sreg, kk);
 #pragma unroll
-          for (int kk = 0; kk < DP / KS; ++kk)
-            acc = MMT::mma(qf[kk], MMT::ld(SM, L::LDSM, n0, kk * KS, lane), acc);
-          acc *= w1v;
-          const int kend = 16 * rw + 16;
-          for (int k0 = 0; k0 < kend; k0 += KS)
-            acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * rw, k0, lane), MMT::ld(Kt, L::LDT, n0, k0, lane), acc);
-          // Pt[d][tau] = g^(2(Lt-1-tau)) p_tau[d] (M update operand, weighted once)
-          const f32x4 pwv = acc * wMv;
-          store4<T>(Pt + (n0 + lr) * L::LDT + 16 * rw + 4 * lg4, pwv);
-          if (MODE == MODE_OUTPUT) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) X1[(16 * rw + 4 * lg4 + j) * L::LDD + n0 + lr] = (T)acc[j];
-          }
-          if (need_n) {
-            const float cs = sum_rows4(pwv[0] + pwv[1] + pwv[2] + pwv[3]);
-            if (lg4 == 0) pcol[rw * D + n0 + lr] = cs;
-          }
-        }
+        for (int r = 0; r < TR; ++r) pacc[r] = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), b, pacc[r]);
       }
-    }
-    __syncthreads();
-
-    // ---- step 3: state updates, B = (Q P^T) o decay, M operand ---------------
-    if (MODE == MODE_OUTPUT) {
-      // M operand (state before this tile): SM[e][d] = M[d][e]
+      float ncol = 0.f;
 #pragma unroll
-      for (int s = 0; s < OM::SLOTS; ++s) {
-        int rb, cb;
-        if (OM::tile(wave, s, rb, cb)) store4<T>(SM + (16 * cb + lr) * L::LDSM + 16 * rb + 4 * lg4, Mreg[s]);
-      }
-      for (int id = wave; id < TR * TR; id += NW) {
-        const int r = id / TR, c = id % TR;
-        f32x4 acc = zero4();
-        if (c <= r) {
-#pragma unroll
-          for (int k0 = 0; k0 < DP; k0 += KS)
-            acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * r, k0, lane), MMT::ld(X1, L::LDD, 16 * c, k0, lane), acc);
-        }
-        const int jj = 16 * c + lr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tau = 16 * r + 4 * lg4 + j;
-          const float val = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
-          AB[tau * L::LDT + jj] = (T)val;
-          if (need_n) {
-            const float rs = sum16(val);
-            if (lr == 0) bpart[c * TT + tau] = rs;
-          }
-        }
-      }
-    }
-    {
-      const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
-      // S <- g^Lt S + K^T diag(wS) K; the weights ride on the B fragments,
-      // which a wave shares across the tiles of one column block
-      {
-        F bk[NKS];
-#pragma unroll
-        for (int s = 0; s < OS::SLOTS; ++s) {
-          int rb, cb;
-          if (OS::tile(wave, s, rb, cb)) {
-            if (OS::new_col(s)) {
-#pragma unroll
-              for (int kk = 0; kk < NKS; ++kk) bk[kk] = MMT::ldw(Kt, L::LDT, 16 * cb, kk * KS, lane, wS);
-            }
-            f32x4 acc = Sreg[s] * gL;
-#pragma unroll
-            for (int kk = 0; kk < NKS; ++kk)
-              acc = MMT::mma(MMT::ld(Kt, L::LDT, 16 * rb, kk * KS, lane), bk[kk], acc);
-            Sreg[s] = acc;
-          }
-        }
-      }
-      // M <- g^2Lt M + Pt V (Pt carries the weights); C <- g^Lt C + Q^T diag(wS) V
-      {
-        F bv[NKS], bvw[MODE == MODE_SUMMARY ? NKS : 1];
-#pragma unroll
-        for (int s = 0; s < OM::SLOTS; ++s) {
-          int rb, cb;
-          if (OM::tile(wave, s, rb, cb)) {
-            if (OM::new_col(s)) {
-#pragma unroll
-              for (int kk = 0; kk < NKS; ++kk) {
-                bv[kk] = MMT::ld(Vt, L::LDT, 16 * cb, kk * KS, lane);
-                if (MODE == MODE_SUMMARY) bvw[kk] = MMT::ldw(Vt, L::LDT, 16 * cb, kk * KS, lane, wS);
-              }
-            }
-            f32x4 acc = Mreg[s] * g2L;
-#pragma unroll
-            for (int kk = 0; kk < NKS; ++kk)
-              acc = MMT::mma(MMT::ld(Pt, L::LDT, 16 * rb, kk * KS, lane), bv[kk], acc);
-            Mreg[s] = acc;
-            if (MODE == MODE_SUMMARY) {
-              f32x4 cacc = Creg[s] * gL;
-#pragma unroll
-              for (int kk = 0; kk < NKS; ++kk)
-                cacc = MMT::mma(MMT::ld(X1, L::LDT, 16 * rb, kk * KS, lane), bvw[kk], cacc);
-              Creg[s] = cacc;
-            }
-          }
-        }
-      }
-      if (MODE == MODE_SUMMARY) {
-        // m <- g^Lt m + sum_tau wS[tau] q_tau: NTHR / D lanes per column,
-        // interleaved rows, then a shuffle reduction
-        constexpr int LPC = NTHR / D;
-        const int col = tid / LPC, part = tid % LPC;
-        float acc = 0.f;
-        for (int t = part; t < Lt; t += LPC) acc += wS[t] * (float)Qs[t * L::LDD + col];
-#pragma unroll
-        for (int off = 1; off < LPC; off *= 2) acc += __shfl_xor(acc, off, 64);
-        if (part == 0) mst[col] = gL * mst[col] + acc;
+      for (int r = 0; r < TR; ++r) {
+        pacc[r] *= *reinterpret_cast<const f32x4*>(w1 + 16 * r + 4 * lg4);
+        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
+          pacc[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Ks, L::LDD, k0, cs0, lane), pacc[r]);
+        // P^T[d][tau], d = cs0 + lr, tau = 16 r + 4 lg4 + j
+        store4<T>(PsT + (cs0 + lr) * L::LDT + 16 * r + 4 * lg4, pacc[r]);
+        const f32x4 wm = *reinterpret_cast<const f32x4*>(wM + 16 * r + 4 * lg4);
+        ncol += pacc[r][0] * wm[0] + pacc[r][1] * wm[1] + pacc[r][2] * wm[2] + pacc[r][3] * wm[3];
       }
       if (need_n) {
-        for (int r = tid; r < D; r += NTHR) {
-          float acc = 0.f;
+        ncol = sum_rows4(ncol);
+        if (lg4 == 0) pcol[cs0 + lr] = ncol;
+      }
+      // S[:, block] <- g^Lt S + K^T diag(wS) K[:, block]
+      const float gL = gpow(g, lgg, Lt);
+      F bk[NKS];
 #pragma unroll
-          for (int rr = 0; rr < TR; ++rr) acc += pcol[rr * D + r];
-          nst[r] = g2L * nst[r] + acc;
-        }
+      for (int kk = 0; kk < NKS; ++kk) bk[kk] = FR::scale(FR::tr(Ks, L::LDD, kk * KS, cs0, lane), wS, kk * KS, lane);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        f32x4 acc = Sreg[t] * gL;
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bk[kk], acc);
+        Sreg[t] = acc;
       }
     }
     __syncthreads();
 
-    // ---- step 4: outputs ------------------------------------------------------
+    // ---- step 3: B^T = (P Q^T) o decay; M (and C, m) update; O = Q M_prev ------
+    const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+    f32x4 oacc[MODE == MODE_OUTPUT ? TR : 1];
     if (MODE == MODE_OUTPUT) {
-      float* go = a.o + (tok0 + t0) * E;
-      // denominator of row tau: the B row sums of the column blocks c <= tau/16 in
-      // a fixed order, plus the prefix term
-      auto den_of = [&](int tau) {
-        float acc = 0.f;
-        for (int c = 0; c <= tau / 16; ++c) acc += bpart[c * TT + tau];
-        return acc + w2[tau] * qn[tau];
-      };
-      F qf[DP / KS];
+      for (int idx = wave; idx < NTRI; idx += NW) {
+        int r, c;
+        tri_tile(idx, r, c);
+        f32x4 acc = zero4();
 #pragma unroll
-      for (int kk = 0; kk < DP / KS; ++kk) qf[kk] = MMT::ld(Qs, L::LDD, 16 * rw, kk * KS, lane);
-      const f32x4 w2v = *reinterpret_cast<const f32x4*>(w2 + 16 * rw + 4 * lg4);
+        for (int k0 = 0; k0 < DP; k0 += KS)
+          acc = MMT::mma(FR::tr(PsT, L::LDT, k0, 16 * c, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+        const int tau = 16 * r + lr;
+        f32x4 val;
 #pragma unroll
-      for (int s = 0; s < OSL; ++s) {
-        const int cb = wave / TR + (NW / TR) * s;
-        if (cb < ET) {
-          const int e0 = 16 * cb;
-          f32x4 acc = zero4();
+        for (int j = 0; j < 4; ++j) {
+          const int jj = 16 * c + 4 * lg4 + j;
+          val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
+        }
+        store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
+        if (need_n) {
+          const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+          if (lg4 == 0) bpart[c * TT + tau] = rs;
+        }
+      }
+      if (ownM) {
 #pragma unroll
-          for (int kk = 0; kk < DP / KS; ++kk)
-            acc = MMT::mma(qf[kk], MMT::ld(SM, L::LDSM, e0, kk * KS, lane), acc);
-          acc *= w2v;
-          const int kend = 16 * rw + 16;
-          for (int k0 = 0; k0 < kend; k0 += KS)
-            acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * rw, k0, lane), MMT::ld(Vt, L::LDT, e0, k0, lane), acc);
+        for (int r = 0; r < TR; ++r) oacc[r] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < QSK; ++kk) {
+          const F b = FR::acc_b(Mreg, kk);
+#pragma unroll
+          for (int r = 0; r < TR; ++r) oacc[r] = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), b, oacc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < TR; ++r) oacc[r] *= *reinterpret_cast<const f32x4*>(w2 + 16 * r + 4 * lg4);
+      }
+    }
+    if (ownM) {
+      // M[:, block] <- g^2Lt M + P^T diag(wM) V[:, block]; C likewise with Q and wS
+      F bv[NKS];
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, cs0, lane), wM, kk * KS, lane);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        f32x4 acc = Mreg[t] * g2L;
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane), bv[kk], acc);
+        Mreg[t] = acc;
+      }
+      if (MODE == MODE_SUMMARY) {
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, cs0, lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc = Creg[t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qs, L::LDD, kk * KS, 16 * t, lane), bv[kk], acc);
+          Creg[t] = acc;
+        }
+      }
+    }
+    if (MODE == MODE_SUMMARY) {
+      // m <- g^Lt m + sum_tau wS[tau] q_tau: NTHR / D lanes per column
+      constexpr int LPC = NTHR / D;
+      const int col = tid / LPC, part = tid % LPC;
+      float acc = 0.f;
+      for (int t = part; t < Lt; t += LPC) acc += wS[t] * (float)Qs[t * L::LDD + col];
+#pragma unroll
+      for (int off = 1; off < LPC; off *= 2) acc += __shfl_xor(acc, off, 64);
+      if (part == 0) mst[col] = gL * mst[col] + acc;
+    }
+    if (need_n) {
+      for (int r = tid; r < D; r += NTHR) nst[r] = g2L * nst[r] + pcol[r];
+    }
+    __syncthreads();
+
+    // ---- step 4: O += B V; write the outputs ------------------------------------
+    if (MODE == MODE_OUTPUT) {
+      if (ownM) {
+        float* go = a.o + (tok0 + t0) * E;
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
+            oacc[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, cs0, lane), oacc[r]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int tau = 16 * rw + 4 * lg4 + j;
-            float val = acc[j];
-            if (a.normalize) val = val / (den_of(tau) + a.eps);
-            if (tau < Lt) go[(size_t)tau * E + e0 + lr] = val;
+            const int tau = 16 * r + 4 * lg4 + j;
+            float val = oacc[r][j];
+            if (a.normalize) {
+              float dn = 0.f;
+              for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
+              val = val / (dn + w2[tau] * qn[tau] + a.eps);
+            }
+            if (tau < Lt) go[(size_t)tau * E + cs0 + lr] = val;
           }
         }
       }
-      if (a.den != nullptr && tid < Lt) a.den[tok0 + t0 + tid] = den_of(tid);
+      if (a.den != nullptr && tid < Lt) {
+        float dn = 0.f;
+        for (int c = 0; c <= tid / 16; ++c) dn += bpart[c * TT + tid];
+        a.den[tok0 + t0 + tid] = dn + w2[tid] * qn[tid];
+      }
       __syncthreads();
     }
   }
@@ -557,39 +445,32 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     float* oS = a.S + sidx * D * D;
     float* oC = a.C + sidx * D * E;
     float* oG = a.G + sidx * D * E;
+    // the tile region is free now: S goes to LDS (fp32) as the A operand of S C
+    if (ownS) {
 #pragma unroll
-    for (int s = 0; s < OS::SLOTS; ++s) {
-      int rb, cb;
-      if (OS::tile(wave, s, rb, cb)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * rb + 4 * lg4 + j;
-          FS[r * L::LFS + 16 * cb + lr] = Sreg[s][j];
-          oS[(size_t)r * D + 16 * cb + lr] = Sreg[s][j];
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < CT; ++s) {
-      int rb, cb;
-      if (OM::tile(wave, s, rb, cb)) {
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = 16 * rb + 4 * lg4 + j;
-          FC[r * L::LFC + 16 * cb + lr] = Creg[s][j];
-          oC[(size_t)r * E + 16 * cb + lr] = Creg[s][j];
+          const int r = 16 * t + 4 * lg4 + j;
+          FS[r * L::LFS + cs0 + lr] = Sreg[t][j];
+          oS[(size_t)r * D + cs0 + lr] = Sreg[t][j];
         }
-      }
     }
     __syncthreads();
+    if (ownM) {
 #pragma unroll
-    for (int s = 0; s < OM::SLOTS; ++s) {
-      int rb, cb;
-      if (OM::tile(wave, s, rb, cb)) {
-        f32x4 acc = gemm_f32_tile<D>(FS, L::LFS, FC, L::LFC, 16 * rb, 16 * cb, lane, zero4());
+      for (int t = 0; t < DT; ++t) {
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          oG[(size_t)(16 * rb + 4 * lg4 + j) * E + 16 * cb + lr] = acc[j] - Mreg[s][j];
+        for (int kk = 0; kk < D / 4; ++kk)
+          acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
+                               Frag<float>::acc_b(Creg, kk), acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t e = (size_t)(16 * t + 4 * lg4 + j) * E + cs0 + lr;
+          oC[e] = Creg[t][j];
+          oG[e] = acc[j] - Mreg[t][j];
+        }
       }
     }
     for (int r = tid; r < D; r += NTHR) {
@@ -603,12 +484,19 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
 
 // ---- dispatch ------------------------------------------------------------------
 
+template <int D, int E>
+struct Waves {
+  // one wave per 16-column block of the wider state, at least 4
+  static constexpr int M = D > E ? D / 16 : E / 16;
+  static constexpr int value = M > 4 ? M : 4;
+};
+
 template <int MODE>
 static hipError_t launch_mode(int dtype, int d, int dv, int units, const ChunkArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)units * (unsigned)a.nspan);
 #define HLA_CASE(T, D, E)                                                                    \
   if (d == D && dv == E) {                                                                   \
-    constexpr int NW = 8;                                                                    \
+    constexpr int NW = Waves<D, E>::value;                                                   \
     hipLaunchKernelGGL((chunk_kernel<T, D, E, MODE, NW>), grid, dim3(64 * NW), 0, s, a);     \
     return hipGetLastError();                                                                \
   }

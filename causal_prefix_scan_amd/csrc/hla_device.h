@@ -18,6 +18,9 @@ namespace hla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -58,6 +61,78 @@ template <> struct MM<float> {
   }
   __device__ static __forceinline__ f32x4 mma(F a, F b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---- operand fragments with other access patterns ------------------------------
+//
+// ld_tr: operand fragment of a matrix X stored row-major in LDS as X[k][n] (n
+// contiguous): lane (n = lane & 15, g = lane >> 4) gets X[k0 + KS/4*g + i][n0 + n].
+// For bf16 this is two 64-bit transposing LDS reads (ds_read_b64_tr_b16): inside
+// each 16-lane group, lane l receives element (l & 3) of the 4-element vectors
+// read by lanes 4j + (l >> 2), j = 0..3, so lane s of the group points at row
+// k + (s >> 2), columns n0 + 4 (s & 3) .. +3.
+//
+// ld_perm: operand fragment whose K order matches an fp32 accumulator used as
+// the other operand (see acc_b): for bf16 step kk the K slots of lane group g
+// are columns 32 kk + 4 g + [0, 4) and 32 kk + 16 + 4 g + [0, 4); for fp32 step
+// kk they are column 16 (kk >> 2) + 4 g + (kk & 3).
+//
+// acc_b: the same K order read out of 16x16 fp32 accumulator tiles stacked
+// along K (tile t covers K rows 16 t .. 16 t + 15): bf16 step kk takes the lane's
+// four rows of tiles 2 kk and 2 kk + 1; fp32 step kk takes row (kk & 3) of
+// tile kk >> 2.
+template <typename T> struct Frag;
+
+template <> struct Frag<__bf16> {
+  using F = bf16x8;
+  __device__ static __forceinline__ F tr(const __bf16* X, int ldm, int k0, int n0, int lane) {
+    const int l = lane & 15, g = lane >> 4;
+    __bf16* p0 = const_cast<__bf16*>(X) + (k0 + 8 * g + (l >> 2)) * ldm + n0 + 4 * (l & 3);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * ldm));
+    const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(F, c);
+  }
+  __device__ static __forceinline__ F perm(const __bf16* X, int ldm, int row0, int kk, int lane) {
+    const __bf16* p = X + (row0 + (lane & 15)) * ldm + 32 * kk + 4 * (lane >> 4);
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // tiles: accumulator tiles along K; ntiles: how many exist (missing ones read as 0)
+  template <int N>
+  __device__ static __forceinline__ F acc_b(const f32x4 (&tiles)[N], int kk) {
+    F r;
+    const f32x4 a = tiles[2 * kk];
+    const f32x4 b = (2 * kk + 1 < N) ? tiles[2 * kk + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = (__bf16)a[i]; r[4 + i] = (__bf16)b[i]; }
+    return r;
+  }
+  __device__ static __forceinline__ F scale(F x, const float* w, int k0, int lane) {
+    const float* ww = w + k0 + 8 * (lane >> 4);
+    F y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (__bf16)((float)x[i] * ww[i]);
+    return y;
+  }
+};
+
+template <> struct Frag<float> {
+  using F = float;
+  __device__ static __forceinline__ F tr(const float* X, int ldm, int k0, int n0, int lane) {
+    return X[(k0 + (lane >> 4)) * ldm + n0 + (lane & 15)];
+  }
+  __device__ static __forceinline__ F perm(const float* X, int ldm, int row0, int kk, int lane) {
+    return X[(row0 + (lane & 15)) * ldm + 16 * (kk >> 2) + 4 * (lane >> 4) + (kk & 3)];
+  }
+  template <int N>
+  __device__ static __forceinline__ F acc_b(const f32x4 (&tiles)[N], int kk) {
+    return tiles[kk >> 2][kk & 3];
+  }
+  __device__ static __forceinline__ F scale(F x, const float* w, int k0, int lane) {
+    return x * w[k0 + (lane >> 4)];
   }
 };
 
