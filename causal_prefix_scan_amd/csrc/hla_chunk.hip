@@ -210,17 +210,20 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  // ---- tile staging: global -> LDS, row-major, 16-byte chunks ---------------
-  // All loads of a tile are issued before the first LDS store.
+  // ---- tile staging: global -> registers -> LDS, row-major, 16-byte chunks ---
+  // The summary kernel issues the loads of tile t+1 in the middle of tile t
+  // (step 2) and writes them to LDS at the start of tile t+1.  The output
+  // kernel holds more state and would spill, so it loads and stores each
+  // tile at its start (all loads issued before the first store).
   constexpr int QCH = TT * D / CH, VCH = TT * E / CH;
   constexpr int NCH = 2 * QCH + VCH;
   constexpr int SPT = (NCH + NTHR - 1) / NTHR;
-  auto stage_tile = [&](int t0, int Lt) {
-    uint4 x[SPT];
+  uint4 xs[SPT];   // prefetched tile (summary kernel only)
+  auto load_tile = [&](uint4 (&xs)[SPT], int t0, int Lt) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int c = tid + NTHR * i;
-      x[i] = make_uint4(0, 0, 0, 0);
+      xs[i] = make_uint4(0, 0, 0, 0);
       if (c < NCH) {
         const T* src;
         int cl, W;
@@ -228,9 +231,11 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         else if (c < 2 * QCH) { src = gk; cl = c - QCH; W = D; }
         else { src = gv; cl = c - 2 * QCH; W = E; }
         const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
-        if (row < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
+        if (row < Lt) xs[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
       }
     }
+  };
+  auto store_tile = [&](const uint4 (&xs)[SPT]) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int c = tid + NTHR * i;
@@ -241,20 +246,31 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         else if (c < 2 * QCH) { dst = Ks; cl = c - QCH; W = D; LD = L::LDD; }
         else { dst = Vs; cl = c - 2 * QCH; W = E; LD = L::LDV; }
         const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
-        *reinterpret_cast<uint4*>(dst + row * LD + col) = x[i];
+        *reinterpret_cast<uint4*>(dst + row * LD + col) = xs[i];
       }
     }
+  };
+  auto prefetch_next = [&](int ti) {
+    const int t1 = (ti + 1) * TT;
+    if (t1 < Lspan) load_tile(xs, t1, (Lspan - t1) < TT ? (Lspan - t1) : TT);
   };
 
   const int ntiles = (Lspan + TT - 1) / TT;
   int Lt_prev = -1;
+  if constexpr (MODE == MODE_SUMMARY) load_tile(xs, 0, Lspan < TT ? Lspan : TT);
 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = ti * TT;
     const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
 
     // ---- step 0: stage the tile and the per-tile weights --------------------
-    stage_tile(t0, Lt);
+    if constexpr (MODE == MODE_SUMMARY) {
+      store_tile(xs);
+    } else {
+      uint4 xt[SPT];
+      load_tile(xt, t0, Lt);
+      store_tile(xt);
+    }
     if (Lt != Lt_prev && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
       wM[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
@@ -294,6 +310,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
 
     // ---- step 2: P = g^(tau+1) Q S_prev + A' K; S update -----------------------
+    if constexpr (MODE == MODE_SUMMARY) prefetch_next(ti);
     if (ownS) {
       f32x4 pacc[TR];
 #pragma unroll
