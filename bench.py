@@ -34,6 +34,21 @@ def credited_flops_per_token(c, d, dv):
     return f / c
 
 
+def measured_traffic(key):
+    """HBM bytes per launch measured with rocprofv3 counters for `key`, or None
+    if the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        entry = json.load(open(path))["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    m = hashlib.sha256()
+    for f in entry["sources"]:
+        m.update(open(os.path.join(ROOT, "causal_prefix_scan_amd", "csrc", f), "rb").read())
+    return entry["traffic_bytes"] if m.hexdigest() == entry["source_sha256"] else None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,7 +172,8 @@ def bench_fwd(args, torch, np):
     achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
     f_tok = credited_flops_per_token(64, d, dv)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
                 "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -230,7 +246,7 @@ def bench_decode(args, torch, np):
         "wall_ms_per_step": round(wall * 1e3 / steps, 4),
         "roofline": {"bound": "hbm", "kernel": "hla_decode_step", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": bytes_step,
+                     "traffic": measured_traffic(f"hla_decode_step@{name}"), "bytes_per_launch": bytes_step,
                      "avg_launch_ms": round(step_ms, 4)},
     }
     if states64 is not None:
@@ -238,6 +254,29 @@ def bench_decode(args, torch, np):
         toks = [(t[0], t[1], t[2]) for t in toks_host[:nb]]
         out["cpu_baseline"] = cpu_baseline_decode(states64, toks, nb)
     return out
+
+
+def bench_copy(args, torch):
+    """A plain device-to-device copy of a known size: the reference the HBM
+    traffic counters (FETCH_SIZE, WRITE_SIZE) are scaled by."""
+    nbytes = 1 << 30
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "device copy (counter calibration)", "value": round(2 * nbytes / ms / 1e6, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "copy", "bytes_read": nbytes, "bytes_written": nbytes}}
 
 
 def main():
@@ -252,7 +291,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.workload.startswith("decode"):
+    if args.workload == "copy":
+        out = bench_copy(args, torch)
+    elif args.workload.startswith("decode"):
         out = bench_decode(args, torch, np)
     else:
         out = bench_fwd(args, torch, np)
