@@ -24,19 +24,23 @@
 //
 // Layout on chip.  The tile is staged row-major only (Q, K, V in LDS);
 // operands that need the token index contiguous per lane are read with the
-// transposing LDS read.  The state lives in fp32 MFMA accumulators: wave w
-// owns column block w (16 columns, all rows) of S and of M (and C), and feeds
-// those accumulators straight back into the MFMA as the B operand of Q S and
-// Q M (Frag::acc_b), so the state never goes through LDS inside the loop.
-// The wave that owns S column block w also produces column block w of P and
-// writes it transposed (P^T, token-contiguous) to LDS; the wave that owns M
-// column block w produces column block w of the output.  Score tiles are
+// transposing LDS read.  The state lives in fp32 MFMA accumulators and never
+// goes through LDS inside the loop.  The waves split into two roles with a
+// tile loop each (same barriers): the S waves own column blocks of S, produce
+// the matching column blocks of P = Q S (S fed back as the MFMA B operand,
+// Frag::acc_b), write them transposed (P^T, token-contiguous) to LDS, and
+// compute the B score tiles; the M waves own column blocks of M (and of C in
+// the summary kernel), produce the matching column blocks of the output and
+// update M from P^T.  Each wave owns two column blocks when a head dimension
+// is 128, so every A fragment read from LDS feeds two MFMAs.  Score tiles are
 // computed transposed (K Q^T, P Q^T) so that each lane stores four
 // consecutive positions and sums its column in registers.
 //
 // All products run on MFMA (bf16 operands for bf16 inputs, fp32 operands for
 // fp32 inputs) with fp32 accumulation; segment-boundary products (S C, S m)
 // run on fp32 MFMA.
+#include <type_traits>
+
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -104,7 +108,14 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   constexpr int DT = D / 16, ET = E / 16, TR = TT / 16, NKS = TT / KS;
   constexpr int NTRI = TR * (TR + 1) / 2;
   constexpr int QSK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps of Q S and Q M
-  static_assert(DT <= NW && ET <= NW, "one state column block per wave");
+  // Two roles of NOWN waves each: S waves own column blocks of S, M waves own
+  // column blocks of M (and of C in the summary kernel).  Block b of the wave
+  // with role index rw is column block rw + NOWN * b.
+  constexpr int NOWN = NW / 2;
+  constexpr int SB = (DT + NOWN - 1) / NOWN, MB = (ET + NOWN - 1) / NOWN;
+  constexpr bool SUM = MODE == MODE_SUMMARY;
+  // every block index is in range when the blocks divide evenly over a role
+  constexpr bool SFULL = DT % NOWN == 0, MFULL = ET % NOWN == 0;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
@@ -125,7 +136,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   float* nst = pcol + D;
   float* mst = nst + D;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg4 = lane >> 4;
   const int nspan = a.nspan;
   const int unit = blockIdx.x / nspan, span = blockIdx.x - unit * nspan;
@@ -138,11 +150,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   const T* gk = reinterpret_cast<const T*>(a.k) + tok0 * D;
   const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
   const size_t sidx = (size_t)unit * nspan + span;
-  const bool need_n = MODE == MODE_SUMMARY || a.normalize || a.den != nullptr;
-  const bool ownS = wave < DT, ownM = wave < ET;   // column block `wave` of S / of M, C, G
-  const int cs0 = 16 * wave;                        // first column of the owned block
-
-  f32x4 Sreg[DT], Mreg[DT], Creg[MODE == MODE_SUMMARY ? DT : 1];
+  const bool need_n = SUM || a.normalize || a.den != nullptr;
+  const bool sRole = wave < NOWN;
+  const int rw = sRole ? wave : wave - NOWN;
+  const int ntiles = (Lspan + TT - 1) / TT;
 
   if (tid < TT) {
     pw[tid] = gpow(g, lgg, tid);
@@ -150,50 +161,25 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     w1[tid] = gpow(g, lgg, tid + 1);
     w2[tid] = gpow(g, lgg, 2 * tid + 2);
   }
-
-  // ---- initial state -------------------------------------------------------
-#pragma unroll
-  for (int t = 0; t < DT; ++t) { Sreg[t] = zero4(); Mreg[t] = zero4(); }
-  if (MODE == MODE_SUMMARY) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t) Creg[t] = zero4();
+  if (SUM) {
     for (int i = tid; i < D; i += NTHR) { nst[i] = 0.f; mst[i] = 0.f; }
   } else {
-    // S from the prefix; M = S_P C_P - G_P with S_P staged in LDS (fp32) as the
-    // A operand and the wave's column block of C_P as the B operand
+    // S_P to LDS (fp32): the S waves take their columns of it, the M waves use
+    // it as the A operand of S_P C_P, and n = S_P m_P - h_P reads it
     const float* pS = a.S + sidx * D * D;
-    const float* pC = a.C + sidx * D * E;
-    const float* pG = a.G + sidx * D * E;
     for (int i = tid; i < D * D / 4; i += NTHR) {
       const int r = (4 * i) / D, c = (4 * i) % D;
       *reinterpret_cast<f32x4*>(FS + r * L::LFS + c) = reinterpret_cast<const f32x4*>(pS)[i];
     }
-    __syncthreads();
-    if (ownS) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Sreg[t][j] = FS[(16 * t + 4 * lg4 + j) * L::LFS + cs0 + lr];
-    }
-    if (ownM) {
-      f32x4 cp[DT];
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cp[t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + cs0 + lr];
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk)
-          acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
-                               Frag<float>::acc_b(cp, kk), acc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] -= pG[(size_t)(16 * t + 4 * lg4 + j) * E + cs0 + lr];
-        Mreg[t] = acc;
-      }
-    }
-    if (need_n) {
+  }
+  __syncthreads();
+
+  // ---- pieces shared by both roles (every thread runs them) -----------------
+  // after the role's initial state: n from the prefix, then zero the tile
+  // region once (the upper score tiles and any padding columns [D, DP) / rows
+  // of P^T are read as zeros and never written)
+  auto finish_init = [&]() {
+    if (!SUM && need_n) {
       const float* pm = a.m + sidx * D;
       const float* ph = a.h + sidx * D;
       for (int r = tid; r < D; r += NTHR) {
@@ -203,73 +189,85 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-  }
-  // zero the tile region once: the upper score tiles and any padding columns
-  // [D, DP) / rows of P^T are read as zeros and never written
-  for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
-    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
+    for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
+      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  };
 
-  // ---- tile staging: global -> registers -> LDS, row-major, 16-byte chunks ---
-  // The summary kernel issues the loads of tile t+1 in the middle of tile t
-  // (step 2) and writes them to LDS at the start of tile t+1.  The output
-  // kernel holds more state and would spill, so it loads and stores each
-  // tile at its start (all loads issued before the first store).
+  // Tile staging: global -> registers -> LDS, row-major, 16-byte chunks (Q
+  // chunks [0, QCH), K chunks [QCH, 2 QCH), V chunks [2 QCH, NCH)).  The
+  // summary kernel issues the loads of tile t+1 in the middle of tile t and
+  // writes them to LDS at the start of tile t+1, its S waves carrying Q and K
+  // and its M waves V.  The output kernel loads and stores each tile at its
+  // start with all threads (all loads issued before the first store).
   constexpr int QCH = TT * D / CH, VCH = TT * E / CH;
   constexpr int NCH = 2 * QCH + VCH;
-  constexpr int SPT = (NCH + NTHR - 1) / NTHR;
-  uint4 xs[SPT];   // prefetched tile (summary kernel only)
-  auto load_tile = [&](uint4 (&xs)[SPT], int t0, int Lt) {
+  constexpr int HT = NTHR / 2;
+  constexpr int NXS = (2 * QCH + HT - 1) / HT, NXM = (VCH + HT - 1) / HT, NXA = (NCH + NTHR - 1) / NTHR;
+  using QK = std::integral_constant<int, 0>;
+  using VB = std::integral_constant<int, 2 * QCH>;
+  using END = std::integral_constant<int, NCH>;
+  using HALF = std::integral_constant<int, HT>;
+  using ALL = std::integral_constant<int, NTHR>;
+  // chunks [C0, C1) of tile ti by P threads, lt = this thread's index among them
+  auto load_part = [&](auto& x, int ti, int lt, auto C0, auto C1, auto P) {
+    constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
+    constexpr int n = (c1 - c0 + np - 1) / np;
+    const int t0 = ti * TT;
+    const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int c = tid + NTHR * i;
-      xs[i] = make_uint4(0, 0, 0, 0);
-      if (c < NCH) {
+    for (int i = 0; i < n; ++i) {
+      const int c = c0 + lt + np * i;
+      x[i] = make_uint4(0, 0, 0, 0);
+      if (c < c1) {
         const T* src;
         int cl, W;
         if (c < QCH) { src = gq; cl = c; W = D; }
         else if (c < 2 * QCH) { src = gk; cl = c - QCH; W = D; }
         else { src = gv; cl = c - 2 * QCH; W = E; }
         const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
-        if (row < Lt) xs[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
+        if (row < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
       }
     }
   };
-  auto store_tile = [&](const uint4 (&xs)[SPT]) {
+  auto store_part = [&](const auto& x, int lt, auto C0, auto C1, auto P) {
+    constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
+    constexpr int n = (c1 - c0 + np - 1) / np;
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int c = tid + NTHR * i;
-      if (c < NCH) {
+    for (int i = 0; i < n; ++i) {
+      const int c = c0 + lt + np * i;
+      if (c < c1) {
         T* dst;
         int cl, W, LD;
         if (c < QCH) { dst = Qs; cl = c; W = D; LD = L::LDD; }
         else if (c < 2 * QCH) { dst = Ks; cl = c - QCH; W = D; LD = L::LDD; }
         else { dst = Vs; cl = c - 2 * QCH; W = E; LD = L::LDV; }
         const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
-        *reinterpret_cast<uint4*>(dst + row * LD + col) = xs[i];
+        *reinterpret_cast<uint4*>(dst + row * LD + col) = x[i];
       }
     }
   };
-  auto prefetch_next = [&](int ti) {
-    const int t1 = (ti + 1) * TT;
-    if (t1 < Lspan) load_tile(xs, t1, (Lspan - t1) < TT ? (Lspan - t1) : TT);
+  // the summary kernel's share of the staging for the calling role
+  auto load_role = [&](auto& x, int ti, auto s_wave) {
+    if constexpr (decltype(s_wave)::value) load_part(x, ti, tid, QK{}, VB{}, HALF{});
+    else load_part(x, ti, tid - HT, VB{}, END{}, HALF{});
+  };
+  auto store_role = [&](const auto& x, auto s_wave) {
+    if constexpr (decltype(s_wave)::value) store_part(x, tid, QK{}, VB{}, HALF{});
+    else store_part(x, tid - HT, VB{}, END{}, HALF{});
   };
 
-  const int ntiles = (Lspan + TT - 1) / TT;
+  // steps 0 and 1 of tile ti: stage the tile and its weights, then
+  // A'^T = (K Q^T) o decay over all waves and q.n for the denominator
   int Lt_prev = -1;
-  if constexpr (MODE == MODE_SUMMARY) load_tile(xs, 0, Lspan < TT ? Lspan : TT);
-
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int t0 = ti * TT;
-    const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
-
-    // ---- step 0: stage the tile and the per-tile weights --------------------
-    if constexpr (MODE == MODE_SUMMARY) {
-      store_tile(xs);
+  // x: this role's prefetched part of the tile (summary kernel)
+  auto tile_head = [&](int ti, int Lt, auto& x, auto s_wave) {
+    if constexpr (SUM) {
+      store_role(x, s_wave);
     } else {
-      uint4 xt[SPT];
-      load_tile(xt, t0, Lt);
-      store_tile(xt);
+      uint4 xt[NXA];
+      load_part(xt, ti, tid, QK{}, END{}, ALL{});
+      store_part(xt, tid, QK{}, END{}, ALL{});
     }
     if (Lt != Lt_prev && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
@@ -278,8 +276,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     Lt_prev = Lt;
     __syncthreads();
 
-    // ---- step 1: A'^T = (K Q^T) o decay, q.n for the denominator ---------------
-    if (need_n && MODE == MODE_OUTPUT) {
+    if (need_n && !SUM) {
       constexpr int LPR = NTHR / TT;
       const int tau = tid / LPR, part = tid % LPR;
       float acc = 0.f;
@@ -308,111 +305,14 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
     }
     __syncthreads();
+    if constexpr (SUM) {
+      if (ti + 1 < ntiles) load_role(x, ti + 1, s_wave);
+    }
+  };
 
-    // ---- step 2: P = g^(tau+1) Q S_prev + A' K; S update -----------------------
-    if constexpr (MODE == MODE_SUMMARY) prefetch_next(ti);
-    if (ownS) {
-      f32x4 pacc[TR];
-#pragma unroll
-      for (int r = 0; r < TR; ++r) pacc[r] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < QSK; ++kk) {
-        const F b = FR::acc_b(Sreg, kk);
-#pragma unroll
-        for (int r = 0; r < TR; ++r) pacc[r] = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), b, pacc[r]);
-      }
-      float ncol = 0.f;
-#pragma unroll
-      for (int r = 0; r < TR; ++r) {
-        pacc[r] *= *reinterpret_cast<const f32x4*>(w1 + 16 * r + 4 * lg4);
-        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-          pacc[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Ks, L::LDD, k0, cs0, lane), pacc[r]);
-        // P^T[d][tau], d = cs0 + lr, tau = 16 r + 4 lg4 + j
-        store4<T>(PsT + (cs0 + lr) * L::LDT + 16 * r + 4 * lg4, pacc[r]);
-        const f32x4 wm = *reinterpret_cast<const f32x4*>(wM + 16 * r + 4 * lg4);
-        ncol += pacc[r][0] * wm[0] + pacc[r][1] * wm[1] + pacc[r][2] * wm[2] + pacc[r][3] * wm[3];
-      }
-      if (need_n) {
-        ncol = sum_rows4(ncol);
-        if (lg4 == 0) pcol[cs0 + lr] = ncol;
-      }
-      // S[:, block] <- g^Lt S + K^T diag(wS) K[:, block]
-      const float gL = gpow(g, lgg, Lt);
-      F bk[NKS];
-#pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) bk[kk] = FR::scale(FR::tr(Ks, L::LDD, kk * KS, cs0, lane), wS, kk * KS, lane);
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        f32x4 acc = Sreg[t] * gL;
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bk[kk], acc);
-        Sreg[t] = acc;
-      }
-    }
-    __syncthreads();
-
-    // ---- step 3: B^T = (P Q^T) o decay; M (and C, m) update; O = Q M_prev ------
-    const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
-    f32x4 oacc[MODE == MODE_OUTPUT ? TR : 1];
-    if (MODE == MODE_OUTPUT) {
-      for (int idx = wave; idx < NTRI; idx += NW) {
-        int r, c;
-        tri_tile(idx, r, c);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < DP; k0 += KS)
-          acc = MMT::mma(FR::tr(PsT, L::LDT, k0, 16 * c, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
-        const int tau = 16 * r + lr;
-        f32x4 val;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int jj = 16 * c + 4 * lg4 + j;
-          val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
-        }
-        store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
-        if (need_n) {
-          const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
-          if (lg4 == 0) bpart[c * TT + tau] = rs;
-        }
-      }
-      if (ownM) {
-#pragma unroll
-        for (int r = 0; r < TR; ++r) oacc[r] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < QSK; ++kk) {
-          const F b = FR::acc_b(Mreg, kk);
-#pragma unroll
-          for (int r = 0; r < TR; ++r) oacc[r] = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), b, oacc[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < TR; ++r) oacc[r] *= *reinterpret_cast<const f32x4*>(w2 + 16 * r + 4 * lg4);
-      }
-    }
-    if (ownM) {
-      // M[:, block] <- g^2Lt M + P^T diag(wM) V[:, block]; C likewise with Q and wS
-      F bv[NKS];
-#pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, cs0, lane), wM, kk * KS, lane);
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        f32x4 acc = Mreg[t] * g2L;
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane), bv[kk], acc);
-        Mreg[t] = acc;
-      }
-      if (MODE == MODE_SUMMARY) {
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, cs0, lane), wS, kk * KS, lane);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 acc = Creg[t] * gL;
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qs, L::LDD, kk * KS, 16 * t, lane), bv[kk], acc);
-          Creg[t] = acc;
-        }
-      }
-    }
-    if (MODE == MODE_SUMMARY) {
+  // end of step 3: m (summary) and n updates
+  auto vec_updates = [&](int Lt, float gL, float g2L) {
+    if (SUM) {
       // m <- g^Lt m + sum_tau wS[tau] q_tau: NTHR / D lanes per column
       constexpr int LPC = NTHR / D;
       const int col = tid / LPC, part = tid % LPC;
@@ -425,76 +325,374 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     if (need_n) {
       for (int r = tid; r < D; r += NTHR) nst[r] = g2L * nst[r] + pcol[r];
     }
-    __syncthreads();
+  };
 
-    // ---- step 4: O += B V; write the outputs ------------------------------------
-    if (MODE == MODE_OUTPUT) {
-      if (ownM) {
-        float* go = a.o + (tok0 + t0) * E;
-#pragma unroll
-        for (int r = 0; r < TR; ++r) {
-          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-            oacc[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, cs0, lane), oacc[r]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tau = 16 * r + 4 * lg4 + j;
-            float val = oacc[r][j];
-            if (a.normalize) {
-              float dn = 0.f;
-              for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
-              val = val / (dn + w2[tau] * qn[tau] + a.eps);
-            }
-            if (tau < Lt) go[(size_t)tau * E + cs0 + lr] = val;
-          }
-        }
-      }
-      if (a.den != nullptr && tid < Lt) {
-        float dn = 0.f;
-        for (int c = 0; c <= tid / 16; ++c) dn += bpart[c * TT + tid];
-        a.den[tok0 + t0 + tid] = dn + w2[tid] * qn[tid];
-      }
-      __syncthreads();
+  // step 4 for every thread: the denominator output
+  auto write_den = [&](int t0, int Lt) {
+    if (a.den != nullptr && tid < Lt) {
+      float dn = 0.f;
+      for (int c = 0; c <= tid / 16; ++c) dn += bpart[c * TT + tid];
+      a.den[tok0 + t0 + tid] = dn + w2[tid] * qn[tid];
     }
-  }
+  };
 
-  // ---- segment summary: S, C, m, G = S C - M, h = S m - n ----------------------
-  if (MODE == MODE_SUMMARY) {
-    float* oS = a.S + sidx * D * D;
-    float* oC = a.C + sidx * D * E;
-    float* oG = a.G + sidx * D * E;
-    // the tile region is free now: S goes to LDS (fp32) as the A operand of S C
-    if (ownS) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * t + 4 * lg4 + j;
-          FS[r * L::LFS + cs0 + lr] = Sreg[t][j];
-          oS[(size_t)r * D + cs0 + lr] = Sreg[t][j];
-        }
-    }
-    __syncthreads();
-    if (ownM) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk)
-          acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
-                               Frag<float>::acc_b(Creg, kk), acc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const size_t e = (size_t)(16 * t + 4 * lg4 + j) * E + cs0 + lr;
-          oC[e] = Creg[t][j];
-          oG[e] = acc[j] - Mreg[t][j];
-        }
-      }
-    }
+  // end of the segment, for every thread: m and h = S m - n (S in FS)
+  auto write_mh = [&]() {
     for (int r = tid; r < D; r += NTHR) {
       float acc = 0.f;
       for (int c = 0; c < D; ++c) acc += FS[r * L::LFS + c] * mst[c];
       a.m[sidx * D + r] = mst[r];
       a.h[sidx * D + r] = acc - nst[r];
+    }
+  };
+
+  if (sRole) {
+    // ======== S waves: P = g^(tau+1) Q S_prev + A' K, P^T to LDS, S update;
+    //          B^T = (P Q^T) o decay in the output kernel ========
+    f32x4 St[SB][DT];
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+      const int cb = rw + NOWN * b;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          St[b][t][j] = (!SUM && (SFULL || cb < DT)) ? FS[(16 * t + 4 * lg4 + j) * L::LFS + 16 * cb + lr] : 0.f;
+    }
+    uint4 xq[SUM ? NXS : 1];
+    if constexpr (SUM) load_role(xq, 0, std::true_type{});
+    finish_init();
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const int t0 = ti * TT;
+      const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+      const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+      tile_head(ti, Lt, xq, std::true_type{});
+
+      // ---- step 2 ----
+      f32x4 pacc[SB][TR];
+#pragma unroll
+      for (int b = 0; b < SB; ++b)
+#pragma unroll
+        for (int r = 0; r < TR; ++r) pacc[b][r] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < QSK; ++kk) {
+        F bs[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) bs[b] = FR::acc_b(St[b], kk);
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+          const F aq = FR::perm(Qs, L::LDD, 16 * r, kk, lane);
+#pragma unroll
+          for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
+        }
+      }
+      float ncol[SB];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) ncol[b] = 0.f;
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const f32x4 w1v = *reinterpret_cast<const f32x4*>(w1 + 16 * r + 4 * lg4);
+#pragma unroll
+        for (int b = 0; b < SB; ++b) pacc[b][r] *= w1v;
+        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+          const F aa = MMT::ld(AB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+          for (int b = 0; b < SB; ++b)
+            if (SFULL || rw + NOWN * b < DT)
+              pacc[b][r] = MMT::mma(aa, FR::tr(Ks, L::LDD, k0, 16 * (rw + NOWN * b), lane), pacc[b][r]);
+        }
+        const f32x4 wm = *reinterpret_cast<const f32x4*>(wM + 16 * r + 4 * lg4);
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+          const int cb = rw + NOWN * b;
+          if (SFULL || cb < DT) {
+            // P^T[d][tau], d = 16 cb + lr, tau = 16 r + 4 lg4 + j
+            store4<T>(PsT + (16 * cb + lr) * L::LDT + 16 * r + 4 * lg4, pacc[b][r]);
+            ncol[b] += pacc[b][r][0] * wm[0] + pacc[b][r][1] * wm[1] + pacc[b][r][2] * wm[2] +
+                       pacc[b][r][3] * wm[3];
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int cb = rw + NOWN * b;
+        if (need_n && (SFULL || cb < DT)) {
+          const float cs = sum_rows4(ncol[b]);
+          if (lg4 == 0) pcol[16 * cb + lr] = cs;
+        }
+      }
+      // S[:, blocks] <- g^Lt S + K^T diag(wS) K[:, blocks]; the K^T fragments are shared
+      {
+        F bk[SB][NKS];
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk)
+            bk[b][kk] = FR::scale(FR::tr(Ks, L::LDD, kk * KS, 16 * ((rw + NOWN * b) % DT), lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc[SB];
+#pragma unroll
+          for (int b = 0; b < SB; ++b) acc[b] = St[b][t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) {
+            const F ak = FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane);
+#pragma unroll
+            for (int b = 0; b < SB; ++b) acc[b] = MMT::mma(ak, bk[b][kk], acc[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < SB; ++b)
+            if (SFULL || rw + NOWN * b < DT) St[b][t] = acc[b];
+        }
+      }
+      __syncthreads();
+
+      // ---- step 3 ----
+      if (!SUM) {
+        for (int idx = rw; idx < NTRI; idx += NOWN) {
+          int r, c;
+          tri_tile(idx, r, c);
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < DP; k0 += KS)
+            acc = MMT::mma(FR::tr(PsT, L::LDT, k0, 16 * c, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+          const int tau = 16 * r + lr;
+          f32x4 val;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int jj = 16 * c + 4 * lg4 + j;
+            val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
+          }
+          store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
+          if (need_n) {
+            const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+            if (lg4 == 0) bpart[c * TT + tau] = rs;
+          }
+        }
+      }
+      vec_updates(Lt, gL, g2L);
+      __syncthreads();
+
+      // ---- step 4 ----
+      if (!SUM) {
+        write_den(t0, Lt);
+        __syncthreads();
+      }
+    }
+
+    if (SUM) {
+      // S to LDS (fp32, the tile region is free now) as the A operand of S C
+      float* oS = a.S + sidx * D * D;
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int cb = rw + NOWN * b;
+        if (SFULL || cb < DT) {
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 16 * t + 4 * lg4 + j;
+              FS[r * L::LFS + 16 * cb + lr] = St[b][t][j];
+              oS[(size_t)r * D + 16 * cb + lr] = St[b][t][j];
+            }
+        }
+      }
+      __syncthreads();
+      write_mh();
+    }
+  } else {
+    // ======== M waves: O = g^(2(tau+1)) Q M_prev + B V and the M update
+    //          (output kernel); C and M updates, G = S C - M (summary) ========
+    f32x4 St[MB][DT];
+    f32x4 Ct[SUM ? MB : 1][SUM ? DT : 1];
+    if (SUM) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) { St[b][t] = zero4(); Ct[b][t] = zero4(); }
+    } else {
+      // M = S_P C_P - G_P: S_P from LDS is the A operand, the block of C_P the B operand
+      const float* pC = a.C + sidx * D * E;
+      const float* pG = a.G + sidx * D * E;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int cb = rw + NOWN * b;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) St[b][t] = zero4();
+        if (MFULL || cb < ET) {
+          f32x4 cp[DT];
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cp[t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr];
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < D / 4; ++kk)
+              acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
+                                   Frag<float>::acc_b(cp, kk), acc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] -= pG[(size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr];
+            St[b][t] = acc;
+          }
+        }
+      }
+    }
+    uint4 xv[SUM ? NXM : 1];
+    if constexpr (SUM) load_role(xv, 0, std::false_type{});
+    finish_init();
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const int t0 = ti * TT;
+      const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+      const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+      tile_head(ti, Lt, xv, std::false_type{});
+
+      // ---- step 2 ----
+      f32x4 oacc[SUM ? 1 : MB][TR];
+      if constexpr (!SUM) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int r = 0; r < TR; ++r) oacc[b][r] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < QSK; ++kk) {
+          F bm[MB];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) bm[b] = FR::acc_b(St[b], kk);
+#pragma unroll
+          for (int r = 0; r < TR; ++r) {
+            const F aq = FR::perm(Qs, L::LDD, 16 * r, kk, lane);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) oacc[b][r] = MMT::mma(aq, bm[b], oacc[b][r]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+          const f32x4 w2v = *reinterpret_cast<const f32x4*>(w2 + 16 * r + 4 * lg4);
+#pragma unroll
+          for (int b = 0; b < MB; ++b) oacc[b][r] *= w2v;
+        }
+      } else {
+        // C[:, blocks] <- g^Lt C + Q^T diag(wS) V[:, blocks]; the Q^T fragments are shared
+        F bv[MB][NKS];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk)
+            bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc[MB];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) acc[b] = Ct[b][t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) {
+            const F aq = FR::tr(Qs, L::LDD, kk * KS, 16 * t, lane);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(aq, bv[b][kk], acc[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+            if (MFULL || rw + NOWN * b < ET) Ct[b][t] = acc[b];
+        }
+      }
+      __syncthreads();
+
+      // ---- step 3: M[:, blocks] <- g^2Lt M + P^T diag(wM) V[:, blocks] ----
+      {
+        F bv[MB][NKS];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk)
+            bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wM, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc[MB];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) acc[b] = St[b][t] * g2L;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) {
+            const F ap = MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(ap, bv[b][kk], acc[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+            if (MFULL || rw + NOWN * b < ET) St[b][t] = acc[b];
+        }
+      }
+      vec_updates(Lt, gL, g2L);
+      __syncthreads();
+
+      // ---- step 4: O += B V; normalise; write O and the denominator ----
+      if constexpr (!SUM) {
+        float* go = a.o + (tok0 + t0) * E;
+        // each store address = a wave-uniform row/column base + one per-lane offset
+        const int olane = 4 * lg4 * E + lr;
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+            const F ab = MMT::ld(AB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+              if (MFULL || rw + NOWN * b < ET)
+                oacc[b][r] = MMT::mma(ab, FR::tr(Vs, L::LDV, k0, 16 * (rw + NOWN * b), lane), oacc[b][r]);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int tau = 16 * r + 4 * lg4 + j;
+            float scale = 1.f;
+            if (a.normalize) {
+              float dn = 0.f;
+              for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
+              scale = 1.f / (dn + w2[tau] * qn[tau] + a.eps);
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+              const int cb = rw + NOWN * b;
+              if ((MFULL || cb < ET) && tau < Lt) {
+                const float val = a.normalize ? oacc[b][r][j] * scale : oacc[b][r][j];
+                float* rowp = go + ((16 * r + j) * E + 16 * cb);
+                rowp[olane] = val;
+              }
+            }
+          }
+        }
+        write_den(t0, Lt);
+        __syncthreads();
+      }
+    }
+
+    if (SUM) {
+      // G = S C - M with S from LDS (written by the S waves) as the A operand
+      float* oC = a.C + sidx * D * E;
+      float* oG = a.G + sidx * D * E;
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int cb = rw + NOWN * b;
+        if (MFULL || cb < ET) {
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < D / 4; ++kk)
+              acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
+                                   Frag<float>::acc_b(Ct[b], kk), acc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const size_t e = (size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr;
+              oC[e] = Ct[b][t][j];
+              oG[e] = acc[j] - St[b][t][j];
+            }
+          }
+        }
+      }
+      write_mh();
     }
   }
 }
@@ -503,9 +701,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
 
 template <int D, int E>
 struct Waves {
-  // one wave per 16-column block of the wider state, at least 4
-  static constexpr int M = D > E ? D / 16 : E / 16;
-  static constexpr int value = M > 4 ? M : 4;
+  // two roles (S waves, M waves) of 4 waves when a head dimension is 128, else of 2
+  static constexpr int value = (D == 128 || E == 128) ? 8 : 4;
 };
 
 template <int MODE>
