@@ -16,7 +16,6 @@ namespace {
 
 using hla::ChunkArgs;
 using hla::DecodeArgs;
-using hla::ScanArgs;
 
 constexpr int64_t kMaxGrid = 2147483647;
 
@@ -132,24 +131,22 @@ ChunkArgs chunk_args(const hla_problem* p, const void* q, const void* k, const v
 
 size_t scan_ws_bytes(const hla_problem* p) {
   const Sizes z = sizes_of(p);
-  return (size_t)z.units * (size_t)(z.N - z.n) * (z.S + 2 * z.C + 2 * z.m) * 4;
+  return hla::scan_workspace_floats(z.units, (int)z.n, p->d, p->dv) * 4;
 }
 
 hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state* total,
                    void* ws, hipStream_t s) {
   const Sizes z = sizes_of(p);
-  ScanArgs a;
+  hla::ScanPlan a;
   a.S = inout->S; a.C = inout->C; a.m = inout->m; a.G = inout->G; a.h = inout->h;
-  float* w = static_cast<float*>(ws);
-  const size_t pad = (size_t)z.units * (size_t)(z.N - z.n);
-  a.wS = w; a.wC = a.wS + pad * z.S; a.wm = a.wC + pad * z.C; a.wG = a.wm + pad * z.m;
-  a.wh = a.wG + pad * z.C;
+  a.tS = total ? total->S : nullptr; a.tC = total ? total->C : nullptr;
+  a.tm = total ? total->m : nullptr; a.tG = total ? total->G : nullptr;
+  a.th = total ? total->h : nullptr;
+  a.ws = static_cast<float*>(ws);
   a.gamma = p->gamma;
-  a.H = p->H; a.n = (int)z.n; a.N = (int)z.N; a.chunk = p->chunk; a.step = 1;
+  a.units = (int)z.units; a.H = p->H; a.n = (int)z.n; a.chunk = p->chunk;
   a.d = p->d; a.dv = p->dv;
-  float* t[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-  if (total) { t[0] = total->S; t[1] = total->C; t[2] = total->m; t[3] = total->G; t[4] = total->h; }
-  return from_hip(hla::launch_scan((int)z.units, p->d, p->dv, a, t[0], t[1], t[2], t[3], t[4], s));
+  return from_hip(hla::launch_scan(a, s));
 }
 
 }  // namespace

@@ -196,14 +196,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
 
   // Tile staging: global -> registers -> LDS, row-major, 16-byte chunks (Q
   // chunks [0, QCH), K chunks [QCH, 2 QCH), V chunks [2 QCH, NCH)).  The
-  // summary kernel issues the loads of tile t+1 in the middle of tile t and
-  // writes them to LDS at the start of tile t+1, its S waves carrying Q and K
-  // and its M waves V.  The output kernel loads and stores each tile at its
-  // start with all threads (all loads issued before the first store).
+  // loads of tile t+1 are issued in the middle of tile t and written to LDS at
+  // the start of tile t+1, the S waves carrying Q and K and the M waves V.
+  // Without prefetch each tile is loaded and stored at its start by all
+  // threads (all loads issued before the first store).
   constexpr int QCH = TT * D / CH, VCH = TT * E / CH;
   constexpr int NCH = 2 * QCH + VCH;
   constexpr int HT = NTHR / 2;
   constexpr int NXS = (2 * QCH + HT - 1) / HT, NXM = (VCH + HT - 1) / HT, NXA = (NCH + NTHR - 1) / NTHR;
+  // prefetch through registers: always in the summary kernel; in the output
+  // kernel only with 8 waves (with 4 it would cost the second workgroup per CU)
+  constexpr bool PF = SUM || NW == 8;
   using QK = std::integral_constant<int, 0>;
   using VB = std::integral_constant<int, 2 * QCH>;
   using END = std::integral_constant<int, NCH>;
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   int Lt_prev = -1;
   // x: this role's prefetched part of the tile (summary kernel)
   auto tile_head = [&](int ti, int Lt, auto& x, auto s_wave) {
-    if constexpr (SUM) {
+    if constexpr (PF) {
       store_role(x, s_wave);
     } else {
       uint4 xt[NXA];
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
     }
     __syncthreads();
-    if constexpr (SUM) {
+    if constexpr (PF) {
       if (ti + 1 < ntiles) load_role(x, ti + 1, s_wave);
     }
   };
@@ -359,8 +362,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         for (int j = 0; j < 4; ++j)
           St[b][t][j] = (!SUM && (SFULL || cb < DT)) ? FS[(16 * t + 4 * lg4 + j) * L::LFS + 16 * cb + lr] : 0.f;
     }
-    uint4 xq[SUM ? NXS : 1];
-    if constexpr (SUM) load_role(xq, 0, std::true_type{});
+    uint4 xq[PF ? NXS : 1];
+    if constexpr (PF) load_role(xq, 0, std::true_type{});
     finish_init();
 
     for (int ti = 0; ti < ntiles; ++ti) {
@@ -540,8 +543,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         }
       }
     }
-    uint4 xv[SUM ? NXM : 1];
-    if constexpr (SUM) load_role(xv, 0, std::false_type{});
+    uint4 xv[PF ? NXM : 1];
+    if constexpr (PF) load_role(xv, 0, std::false_type{});
     finish_init();
 
     for (int ti = 0; ti < ntiles; ++ti) {

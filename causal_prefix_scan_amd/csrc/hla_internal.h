@@ -23,13 +23,24 @@ struct ChunkArgs {
   float* den;  // [units, T] or nullptr
 };
 
+// One tree scan over slots (used for the run totals of the two-level scan).
 struct ScanArgs {
   float *S, *C, *m, *G, *h;             // [units, n, ...] in place
   float *wS, *wC, *wm, *wG, *wh;        // padding slots [units, N - n, ...]
   const float* gamma;
   int H, n, N, chunk;
+  int seg, nseg;                        // slot i holds segments [i seg, (i+1) seg) of nseg
   int step;                             // tree distance 2^level
   int d, dv;
+};
+
+// The whole exclusive scan of one problem.
+struct ScanPlan {
+  float *S, *C, *m, *G, *h;             // [units, n, ...] in place
+  float *tS, *tC, *tm, *tG, *th;        // inclusive totals [units, ...], each may be nullptr
+  float* ws;                            // scan_workspace_floats(...) floats (nullptr if 0)
+  const float* gamma;
+  int units, H, n, chunk, d, dv;
 };
 
 struct DecodeArgs {
@@ -51,11 +62,12 @@ hipError_t launch_chunk_outputs(int dtype, int d, int dv, int units, const Chunk
                                 hipStream_t s);
 bool chunk_shape_supported(int dtype, int d, int dv);
 
-// Runs the whole exclusive scan (all levels).  t* (each may be nullptr)
-// receive the inclusive totals [units, ...].  The padding slots w* must be
-// one contiguous region laid out S | C | m | G | h.
-hipError_t launch_scan(int units, int d, int dv, const ScanArgs& a, float* tS, float* tC, float* tm,
-                       float* tG, float* th, hipStream_t s);
+// Segments per run of the two-level scan, and the scratch it needs (run
+// totals and the tree's padding slots; 0 with a single run).
+int scan_run_length(int n);
+size_t scan_workspace_floats(int64_t units, int n, int d, int dv);
+// Runs the whole exclusive scan (every launch, in order, on stream s).
+hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 

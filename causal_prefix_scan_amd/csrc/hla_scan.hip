@@ -1,5 +1,5 @@
-// Exclusive Blelloch scan of segment summaries under the semidirect-product
-// combine ("Higher-order Linear Attention", arXiv 2510.27258, summaries on
+// Exclusive scan of segment summaries under the semidirect-product combine
+// ("Higher-order Linear Attention", arXiv 2510.27258, summaries on
 // gist.science: method section 4 -- associative operator with cross term
 // S_B C_A, exclusive Blelloch scan equal to the serial activations; key
 // contribution 2 -- decayed operators).
@@ -9,17 +9,24 @@
 //   G = a^2 G_A + G_B + a S_B C_A, h = a^2 h_A + h_B + a S_B m_A.
 // The identity is all zeros with length 0 (a = 1).
 //
-// The n summaries of each (b, h) unit are scanned as an array of N = 2^ceil(log2 n)
-// slots; slots >= n are identities kept in a caller-provided workspace.  Each
-// tree level is one or two launches, so a level finishes before the next one
-// starts:
-//   up-sweep level:   x[j] <- x[i] (+) x[j]
-//   down-sweep level: swap x[i] and x[j] (left <- parent prefix, right <- left
-//                     sum), then x[j] <- x[i] (+) x[j] (= parent (+) left sum)
-// with i = j - step for every pair of the level.  The combine is split over
-// workgroups by 16-row blocks of the D-row state: a workgroup reads and writes
-// only rows of x[j] it owns, and x[i] is read-only, so there is no race.  The
-// cross terms S_B C_A and S_B m_A run on fp32 MFMA with C_A staged in LDS.
+// Two levels.  The n segments of a (b, h) unit are cut into runs of R
+// consecutive segments (one run when n is small):
+//   1. run reduce:  each run's total, walking its segments in order;
+//   2. run scan:    exclusive Blelloch scan (up-sweep, root reset,
+//                   down-sweep) of the run totals, in place;
+//   3. run rescan:  each run walks its segments again from the run's
+//                   exclusive prefix and overwrites every segment with its
+//                   own exclusive prefix (rows of S, G, h);
+//   4. C, m pass:   the same for C and m, elementwise.
+// Steps 1-2 are skipped with a single run.  Each segment is read twice and
+// written once, in four launches; the tree's levels only see the run totals.
+//
+// Steps 1 and 3 split a run's state over workgroups by 16-row blocks: a
+// workgroup owns rows [r0, r0 + 16) of S, G and h, and keeps the whole
+// running C and m, which its rows of the cross terms S_B C_A, S_B m_A need.
+// C and m are therefore only read in step 3 (every workgroup of the run
+// reads them) and rewritten in step 4.  The cross term runs on fp32 MFMA with
+// the running C as the B operand straight from registers.
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -48,10 +55,13 @@ __device__ __forceinline__ Slot slot_ptr(const ScanArgs& a, int unit, int idx) {
   return s;
 }
 
-// Number of real segments in the slot range [lo, hi].
-__device__ __forceinline__ int real_len(int lo, int hi, int n) {
-  const int h = hi < n - 1 ? hi : n - 1;
-  return h >= lo ? h - lo + 1 : 0;
+// Tokens in the slot range [lo, hi]: slot i holds segments
+// [i seg, (i + 1) seg) of the nseg real ones, each of `chunk` tokens.
+__device__ __forceinline__ int slot_tokens(const ScanArgs& a, int lo, int hi) {
+  const int s0 = lo * a.seg;
+  if (s0 >= a.nseg) return 0;
+  const int s1 = (hi + 1) * a.seg < a.nseg ? (hi + 1) * a.seg : a.nseg;
+  return (s1 - s0) * a.chunk;
 }
 
 // x[j] <- x[i] (+) x[j] for every pair of one level; blockIdx.x = pair * (D/RB) + row block.
@@ -71,9 +81,9 @@ __global__ __launch_bounds__(SCAN_THR) void scan_combine_kernel(ScanArgs a, int 
   const int i = j - step;
   if (i - step + 1 >= a.n) return;   // both subtrees are padding: identity (+) identity
   const Slot A = slot_ptr(a, unit, i), B = slot_ptr(a, unit, j);
-  const int lenB = down ? real_len(i - step + 1, i, a.n) : real_len(j - step + 1, j, a.n);
+  const int lenB = down ? slot_tokens(a, i - step + 1, i) : slot_tokens(a, j - step + 1, j);
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
-  const float al = gpow(g, log2f(g), lenB * a.chunk);
+  const float al = gpow(g, log2f(g), lenB);
   const float al2 = al * al;
   const int r0 = rb * SCAN_RB;
 
@@ -176,45 +186,315 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, size_t count) 
   for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < count; t += stride) p[t] = 0.f;
 }
 
-template <int D, int E>
-static hipError_t run_scan(int units, ScanArgs a, float* tS, float* tC, float* tm, float* tG,
-                           float* th, hipStream_t s) {
-  constexpr int NRB = D / SCAN_RB;
-  constexpr int VEC = (D * D + 2 * D * E + 2 * D) / 4;       // f32x4 per summary
-  constexpr int PARTS = VEC / 1024 > 0 ? VEC / 1024 : 1;    // swap workgroups per pair
-  if (a.N > a.n) {
-    // padding slots start as identities (one contiguous workspace region)
-    const size_t per = (size_t)D * D + 2 * (size_t)D * E + 2 * (size_t)D;
-    const size_t count = per * (size_t)units * (size_t)(a.N - a.n);
-    size_t blocks = (count + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.wS, count);
-    if (hipError_t e = hipGetLastError()) return e;
+// ---- runs ----------------------------------------------------------------------
+
+struct RunArgs {
+  float *S, *C, *m, *G, *h;        // segments [units, n, ...]
+  float *aS, *aC, *am, *aG, *ah;   // run totals / exclusive run prefixes [units, runs, ...]
+  float *tS, *tC, *tm, *tG, *th;   // inclusive totals [units, ...], each may be nullptr
+  const float* gamma;
+  int H, n, R, runs, chunk, units;
+  int from_prefix;                 // rescan starts from a*[run] (else from the identity)
+};
+
+// Steps 1 (REDUCE) and 3: one workgroup per (unit, run, 16-row block), E/16
+// waves; wave w owns column block w of C and G.  blockIdx.x is laid out so
+// that the D/16 workgroups of one (unit, run) share blockIdx.x mod 8 and so
+// run on one XCD, where the C and m they all read stay in one L2.
+template <int D, int E, bool REDUCE>
+__global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
+  constexpr int NW = E / 16, NT = 64 * NW, DT = D / 16, NRB = D / 16, LS = D + 4;
+  constexpr int SV = 16 * D / 4;            // f32x4 in 16 rows of S
+  constexpr int SPT = (SV + NT - 1) / NT;
+  constexpr int PH = 4;                     // lanes per row of the S m product
+  __shared__ __attribute__((aligned(16))) float sS[16 * LS];
+  __shared__ float sm[2][D];
+
+  const int bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
+  const int grp = xcd + 8 * (qb / NRB), rb = qb % NRB;
+  if (grp >= a.units * a.runs) return;
+  const int unit = grp / a.runs, run = grp % a.runs;
+  const int k0 = run * a.R;
+  const int len = (a.n - k0) < a.R ? (a.n - k0) : a.R;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg4 = lane >> 4;
+  const int r0 = 16 * rb;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float al = gpow(g, log2f(g), a.chunk), al2 = al * al;
+
+  // running state: C column block (rows 16 t + 4 lg4 + j), G rows x column
+  // block, S rows (f32x4 e = tid + NT i: row e / (D/4), columns 4 (e % (D/4))),
+  // h row tid (tid < 16); m in LDS
+  f32x4 Cb[DT], Gb, Sb[SPT];
+  float hb = 0.f;
+  const bool pre = !REDUCE && a.from_prefix;
+  const size_t pr = (size_t)unit * a.runs + run;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      Cb[t][j] = pre ? a.aC[pr * D * E + (size_t)(16 * t + 4 * lg4 + j) * E + 16 * w + lr] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    Gb[j] = pre ? a.aG[pr * D * E + (size_t)(r0 + 4 * lg4 + j) * E + 16 * w + lr] : 0.f;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int e = tid + NT * i;
+    Sb[i] = zero4();
+    if (pre && e < SV)
+      Sb[i] = reinterpret_cast<const f32x4*>(a.aS + pr * D * D + (size_t)r0 * D)[e];
   }
-  for (int step = 1; step < a.N; step *= 2) {
-    a.step = step;
-    hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
-                       dim3(SCAN_THR), 0, s, a, 0);
-    if (hipError_t e = hipGetLastError()) return e;
+  if (pre && tid < 16) hb = a.ah[pr * D + r0 + tid];
+  for (int t = tid; t < D; t += NT) sm[0][t] = pre ? a.am[pr * D + t] : 0.f;
+
+  // loads of one segment
+  f32x4 xC[DT], xG, xS[SPT];
+  float xh = 0.f, xm = 0.f;
+  auto load = [&](int k) {
+    const size_t sl = (size_t)unit * a.n + k0 + k;
+    const float* pC = a.C + sl * D * E;
+    const float* pG = a.G + sl * D * E;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xC[t][j] = pC[(16 * t + 4 * lg4 + j) * E + 16 * w + lr];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xG[j] = pG[(r0 + 4 * lg4 + j) * E + 16 * w + lr];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = tid + NT * i;
+      xS[i] = e < SV ? reinterpret_cast<const f32x4*>(a.S + sl * D * D + (size_t)r0 * D)[e] : zero4();
+    }
+    xh = tid < 16 ? a.h[sl * D + r0 + tid] : 0.f;
+    xm = tid < D ? a.m[sl * D + tid] : 0.f;
+  };
+
+  int cur = 0;
+  if (len > 0) load(0);
+  __syncthreads();
+  for (int k = 0; k < len; ++k) {
+    // S rows of segment k to LDS: the A operand of S_B C_A and S_B m_A
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = tid + NT * i;
+      if (e < SV) *reinterpret_cast<f32x4*>(sS + (e / (D / 4)) * LS + 4 * (e % (D / 4))) = xS[i];
+    }
+    __syncthreads();
+    f32x4 cS[DT], cG = xG, cSr[SPT];
+    float ch = xh, cm = xm;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) cS[t] = xC[t];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) cSr[i] = xS[i];
+    if (k + 1 < len) load(k + 1);
+
+    // G rows += a S_B C_A (C_A = running C, before this segment)
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < D / 4; ++kk)
+      acc = MM<float>::mma(sS[lr * LS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)], Frag<float>::acc_b(Cb, kk), acc);
+    // h rows += a S_B m_A
+    float hm = 0.f;
+    if (tid < 16 * PH) {
+      const int row = tid / PH, part = tid % PH;
+      for (int c = part; c < D; c += PH) hm += sS[row * LS + c] * sm[cur][c];
+    }
+#pragma unroll
+    for (int off = 1; off < PH; off *= 2) hm += __shfl_xor(hm, off, 64);
+    hm = __shfl(hm, (tid * PH) & 63, 64);   // lane tid < 16 takes row tid's sum
+
+    const f32x4 oG = Gb;
+    f32x4 oS[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) oS[i] = Sb[i];
+    const float oh = hb;
+    Gb = Gb * al2 + cG + acc * al;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) Sb[i] = Sb[i] * al + cSr[i];
+    hb = al2 * hb + ch + al * hm;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) Cb[t] = Cb[t] * al + cS[t];
+    if (tid < D) sm[cur ^ 1][tid] = al * sm[cur][tid] + cm;
+    if (!REDUCE) {
+      // the segment's own rows become its exclusive prefix (read above, before the update)
+      const size_t sl = (size_t)unit * a.n + k0 + k;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a.G[sl * D * E + (size_t)(r0 + 4 * lg4 + j) * E + 16 * w + lr] = oG[j];
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int e = tid + NT * i;
+        if (e < SV) reinterpret_cast<f32x4*>(a.S + sl * D * D + (size_t)r0 * D)[e] = oS[i];
+      }
+      if (tid < 16) a.h[sl * D + r0 + tid] = oh;
+    }
+    cur ^= 1;
+    __syncthreads();
   }
-  hipLaunchKernelGGL(scan_root_kernel, dim3(units), dim3(256), 0, s, a, tS, tC, tm, tG, th);
-  if (hipError_t e = hipGetLastError()) return e;
-  for (int step = a.N / 2; step >= 1; step /= 2) {
-    a.step = step;
-    hipLaunchKernelGGL(scan_swap_kernel, dim3(a.N / (2 * step) * PARTS, units), dim3(256), 0, s, a,
-                       PARTS);
-    if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
-                       dim3(SCAN_THR), 0, s, a, 1);
-    if (hipError_t e = hipGetLastError()) return e;
+
+  // run total (step 1) or, for the last run, the inclusive total (step 3)
+  float *oS = nullptr, *oC = nullptr, *om = nullptr, *oG = nullptr, *oh = nullptr;
+  if (REDUCE) {
+    oS = a.aS + pr * D * D; oC = a.aC + pr * D * E; om = a.am + pr * D;
+    oG = a.aG + pr * D * E; oh = a.ah + pr * D;
+  } else if (run == a.runs - 1) {
+    const size_t u = unit;
+    if (a.tS) oS = a.tS + u * D * D;
+    if (a.tC) oC = a.tC + u * D * E;
+    if (a.tm) om = a.tm + u * D;
+    if (a.tG) oG = a.tG + u * D * E;
+    if (a.th) oh = a.th + u * D;
   }
-  return hipSuccess;
+  if (oS) {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = tid + NT * i;
+      if (e < SV) reinterpret_cast<f32x4*>(oS + (size_t)r0 * D)[e] = Sb[i];
+    }
+  }
+  if (oG) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) oG[(size_t)(r0 + 4 * lg4 + j) * E + 16 * w + lr] = Gb[j];
+  }
+  if (oh && tid < 16) oh[r0 + tid] = hb;
+  if (rb == 0) {
+    if (oC) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oC[(size_t)(16 * t + 4 * lg4 + j) * E + 16 * w + lr] = Cb[t][j];
+    }
+    if (om && tid < D) om[tid] = sm[cur][tid];
+  }
 }
 
-hipError_t launch_scan(int units, int d, int dv, const ScanArgs& a, float* tS, float* tC, float* tm,
-                       float* tG, float* th, hipStream_t s) {
+// Step 4: C and m of every segment become their exclusive prefixes.  One
+// thread per f32x4 of (C | m) per (unit, run); blockIdx.x = (unit * runs +
+// run) * NBLK + block.
+template <int D, int E>
+__global__ __launch_bounds__(256) void run_cm_kernel(RunArgs a) {
+  constexpr int VC = D * E / 4, VM = D / 4, NBLK = (VC + VM + 255) / 256;
+  const int grp = blockIdx.x / NBLK;
+  const int e = (blockIdx.x % NBLK) * 256 + threadIdx.x;
+  if (e >= VC + VM) return;
+  const int unit = grp / a.runs, run = grp % a.runs;
+  const int k0 = run * a.R;
+  const int len = (a.n - k0) < a.R ? (a.n - k0) : a.R;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float al = gpow(g, log2f(g), a.chunk);
+  const bool isC = e < VC;
+  const int o = isC ? e : e - VC;
+  const size_t per = isC ? (size_t)D * E : (size_t)D;
+  f32x4* base = reinterpret_cast<f32x4*>(isC ? a.C : a.m);
+  f32x4 p = zero4();
+  if (a.from_prefix) {
+    const float* pa = isC ? a.aC : a.am;
+    p = reinterpret_cast<const f32x4*>(pa + ((size_t)unit * a.runs + run) * per)[o];
+  }
+  constexpr int BATCH = 8;
+  for (int k = 0; k < len; k += BATCH) {
+    f32x4 x[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (k + b < len) x[b] = base[((size_t)unit * a.n + k0 + k + b) * (per / 4) + o];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (k + b < len) {
+        base[((size_t)unit * a.n + k0 + k + b) * (per / 4) + o] = p;
+        p = p * al + x[b];
+      }
+  }
+  if (run == a.runs - 1) {
+    float* t = isC ? a.tC : a.tm;
+    if (t) reinterpret_cast<f32x4*>(t + (size_t)unit * per)[o] = p;
+  }
+}
+
+int scan_run_length(int n) {
+  if (n <= 16) return n > 0 ? n : 1;
+  int r = 1;
+  while (r * r < n) r *= 2;
+  return r;
+}
+
+size_t scan_workspace_floats(int64_t units, int n, int d, int dv) {
+  const int R = scan_run_length(n);
+  const int runs = (n + R - 1) / R;
+  if (runs <= 1) return 0;
+  int N = 1;
+  while (N < runs) N *= 2;
+  const size_t per = (size_t)d * d + 2 * (size_t)d * dv + 2 * (size_t)d;
+  return (size_t)units * (size_t)N * per;   // run totals, then the tree's padding slots
+}
+
+template <int D, int E>
+static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
+  constexpr int NRB = D / 16, VEC = (D * D + 2 * D * E + 2 * D) / 4;
+  constexpr int PARTS = VEC / 1024 > 0 ? VEC / 1024 : 1;   // swap workgroups per pair
+  const int units = p.units;
+  RunArgs r;
+  r.S = p.S; r.C = p.C; r.m = p.m; r.G = p.G; r.h = p.h;
+  r.tS = p.tS; r.tC = p.tC; r.tm = p.tm; r.tG = p.tG; r.th = p.th;
+  r.gamma = p.gamma; r.H = p.H; r.n = p.n; r.chunk = p.chunk; r.units = units;
+  r.R = scan_run_length(p.n);
+  r.runs = (p.n + r.R - 1) / r.R;
+  r.from_prefix = r.runs > 1;
+  const size_t cnt = (size_t)units * r.runs;
+  r.aS = r.aC = r.am = r.aG = r.ah = nullptr;
+  if (r.runs > 1) {
+    r.aS = p.ws; r.aC = r.aS + cnt * D * D; r.am = r.aC + cnt * D * E; r.aG = r.am + cnt * D;
+    r.ah = r.aG + cnt * D * E;
+  }
+  const unsigned groups8 = (unsigned)((cnt + 7) / 8 * 8);
+  if (r.runs > 1) {
+    hipLaunchKernelGGL((run_rows_kernel<D, E, true>), dim3(groups8 * NRB), dim3(64 * (E / 16)), 0, s, r);
+    if (hipError_t e = hipGetLastError()) return e;
+    // exclusive Blelloch scan of the run totals; padding slots follow them
+    ScanArgs a;
+    a.S = r.aS; a.C = r.aC; a.m = r.am; a.G = r.aG; a.h = r.ah;
+    a.n = r.runs;
+    a.N = 1;
+    while (a.N < a.n) a.N *= 2;
+    const size_t pad = (size_t)units * (a.N - a.n);
+    a.wS = r.ah + cnt * D; a.wC = a.wS + pad * D * D; a.wm = a.wC + pad * D * E;
+    a.wG = a.wm + pad * D; a.wh = a.wG + pad * D * E;
+    a.gamma = p.gamma; a.H = p.H; a.chunk = p.chunk; a.seg = r.R; a.nseg = p.n;
+    a.d = D; a.dv = E;
+    if (pad > 0) {
+      const size_t count = pad * (size_t)(4 * VEC);
+      size_t blocks = (count + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.wS, count);
+      if (hipError_t e = hipGetLastError()) return e;
+    }
+    for (int step = 1; step < a.N; step *= 2) {
+      a.step = step;
+      hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
+                         dim3(SCAN_THR), 0, s, a, 0);
+      if (hipError_t e = hipGetLastError()) return e;
+    }
+    hipLaunchKernelGGL(scan_root_kernel, dim3(units), dim3(256), 0, s, a, nullptr, nullptr,
+                       nullptr, nullptr, nullptr);
+    if (hipError_t e = hipGetLastError()) return e;
+    for (int step = a.N / 2; step >= 1; step /= 2) {
+      a.step = step;
+      hipLaunchKernelGGL(scan_swap_kernel, dim3(a.N / (2 * step) * PARTS, units), dim3(256), 0, s,
+                         a, PARTS);
+      if (hipError_t e = hipGetLastError()) return e;
+      hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
+                         dim3(SCAN_THR), 0, s, a, 1);
+      if (hipError_t e = hipGetLastError()) return e;
+    }
+  }
+  hipLaunchKernelGGL((run_rows_kernel<D, E, false>), dim3(groups8 * NRB), dim3(64 * (E / 16)), 0, s, r);
+  if (hipError_t e = hipGetLastError()) return e;
+  constexpr int VCM = (D * E + D) / 4;
+  hipLaunchKernelGGL((run_cm_kernel<D, E>), dim3((unsigned)(cnt * ((VCM + 255) / 256))), dim3(256), 0,
+                     s, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
 #define HLA_CASE(D, E) \
-  if (d == D && dv == E) return run_scan<D, E>(units, a, tS, tC, tm, tG, th, s);
+  if (p.d == D && p.dv == E) return run_scan<D, E>(p, s);
   HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(32, 16) HLA_CASE(32, 32) HLA_CASE(32, 64)
   HLA_CASE(64, 32) HLA_CASE(64, 64) HLA_CASE(64, 128) HLA_CASE(128, 64) HLA_CASE(128, 128)
 #undef HLA_CASE

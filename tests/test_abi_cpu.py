@@ -111,13 +111,21 @@ def test_pointer_validation(L):
 
 
 def test_workspace_sizes(L):
-    p = problem(T=256, chunk=64)                      # n = 4: power of two
-    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 0
-    p = problem(B=1, H=2, T=5 * 64, chunk=64, d=32, dv=16)   # n = 5 -> N = 8: 3 pad slots
     per = 32 * 32 + 2 * 32 * 16 + 2 * 32
-    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 2 * 3 * per * 4
-    summ = 2 * 5 * per * 4
-    assert L.hla_fwd_workspace_bytes(ctypes.byref(p)) == summ + 2 * 3 * per * 4
+    # up to 16 segments per unit: one run, rescanned in place, no scratch
+    for n in (4, 5, 16):
+        p = problem(B=1, H=2, T=n * 64, chunk=64, d=32, dv=16)
+        assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 0
+        assert L.hla_fwd_workspace_bytes(ctypes.byref(p)) == 2 * n * per * 4
+    # n = 40: runs of 8 segments (8^2 >= 40), 5 run totals + 3 padding slots
+    # of the tree over them = 8 summaries per unit
+    p = problem(B=1, H=2, T=40 * 64, chunk=64, d=32, dv=16)
+    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 2 * 8 * per * 4
+    summ = 2 * 40 * per * 4
+    assert L.hla_fwd_workspace_bytes(ctypes.byref(p)) == summ + 2 * 8 * per * 4
+    # n = 512: runs of 32, 16 run totals (a power of two: no padding)
+    p = problem(B=1, H=2, T=512 * 64, chunk=64, d=32, dv=16)
+    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) == 2 * 16 * per * 4
     assert L.hla_scan_workspace_bytes(ctypes.byref(problem(T=10))) == 0   # invalid -> 0
     # too small a workspace is rejected before anything runs
     assert L.hla_scan(ctypes.byref(p), ctypes.byref(state()), None, 0x7000000000, 16, None) == WS

@@ -54,6 +54,10 @@ SMALL = [
     (1, 1, 96, 64, 128, 32, "bf16", False, False),    # chunk shorter than a tile
     (1, 2, 192, 64, 64, 64, "f32", True, True),
     (1, 1, 128, 32, 16, 128, "bf16", False, False),   # n = 1
+    # more than 16 segments: runs of 8, a scan over the run totals
+    (1, 2, 640, 32, 32, 32, "bf16", True, True),      # n = 20: runs 8, 8, 4; tree pads 3 -> 4
+    (1, 1, 640, 16, 16, 16, "f32", True, False),      # n = 40: 5 runs, tree pads 5 -> 8
+    (1, 1, 544, 128, 128, 32, "bf16", True, False),   # n = 17: runs 8, 8, 1
 ]
 
 
