@@ -60,17 +60,21 @@ struct ChunkLayout {
   static constexpr int LDT = TT + PADT;      // PsT: [d][tok], AB: [tok][tok]
   static constexpr size_t Qs = 0;
   static constexpr size_t Ks = Qs + (size_t)TT * LDD * sizeof(T);
-  static constexpr size_t Vs = Ks + (size_t)TT * LDD * sizeof(T);
-  static constexpr size_t PsT = Vs + (size_t)TT * LDV * sizeof(T);
-  static constexpr size_t AB = PsT + (size_t)DP * LDT * sizeof(T);
+  // V and P^T are double-buffered by tile parity: the M update of a tile runs
+  // while the next tile is staged and its P produced
+  static constexpr size_t Vs0 = Ks + (size_t)TT * LDD * sizeof(T);
+  static constexpr size_t Vs1 = Vs0 + (size_t)TT * LDV * sizeof(T);
+  static constexpr size_t PsT0 = Vs1 + (size_t)TT * LDV * sizeof(T);
+  static constexpr size_t PsT1 = PsT0 + (size_t)DP * LDT * sizeof(T);
+  static constexpr size_t AB = PsT1 + (size_t)DP * LDT * sizeof(T);
   static constexpr size_t TILE_END = AB + (size_t)TT * LDT * sizeof(T);
   // fp32 overlay used at segment boundaries: S [D][D+4]
   static constexpr int LFS = D + 4;
   static constexpr size_t F_END = (size_t)D * LFS * 4;
   static constexpr size_t BIG = TILE_END > F_END ? TILE_END : F_END;
   static constexpr size_t W = (BIG + 15) / 16 * 16;
-  // w1, w2, wS, wM, pw, pw2, qn [TT]; bpart [TR][TT]; pcol, nst, mst [D]
-  static constexpr size_t TOTAL = W + (size_t)(7 * TT + (TT / 16) * TT + 3 * D) * 4;
+  // w1, w2, wS, wM0, wM1, pw, pw2, qn [TT]; bpart [TR][TT]; nst, mst [D]
+  static constexpr size_t TOTAL = W + (size_t)(8 * TT + (TT / 16) * TT + 2 * D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -120,20 +124,20 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
   T* Ks = reinterpret_cast<T*>(smem + L::Ks);
-  T* Vs = reinterpret_cast<T*>(smem + L::Vs);
-  T* PsT = reinterpret_cast<T*>(smem + L::PsT);
+  // buffers of tile parity p
+  auto Vsb = [&](int p) { return reinterpret_cast<T*>(smem + (p ? L::Vs1 : L::Vs0)); };
+  auto PsTb = [&](int p) { return reinterpret_cast<T*>(smem + (p ? L::PsT1 : L::PsT0)); };
   T* AB = reinterpret_cast<T*>(smem + L::AB);
   float* FS = reinterpret_cast<float*>(smem);
   float* w1 = reinterpret_cast<float*>(smem + L::W);
   float* w2 = w1 + TT;
   float* wS = w2 + TT;
-  float* wM = wS + TT;
-  float* pw = wM + TT;
+  auto wMb = [&](int p) { return wS + (p ? 2 * TT : TT); };
+  float* pw = wS + 3 * TT;
   float* pw2 = pw + TT;
   float* qn = pw2 + TT;
   float* bpart = qn + TT;        // [TR][TT]: B column sums per 16-row block of j
-  float* pcol = bpart + TR * TT; // [D]: weighted column sums of P (one writer per column)
-  float* nst = pcol + D;
+  float* nst = bpart + TR * TT;
   float* mst = nst + D;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       }
     }
   };
-  auto store_part = [&](const auto& x, int lt, auto C0, auto C1, auto P) {
+  auto store_part = [&](const auto& x, int lt, T* Vs, auto C0, auto C1, auto P) {
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
     constexpr int n = (c1 - c0 + np - 1) / np;
 #pragma unroll
@@ -255,9 +259,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     if constexpr (decltype(s_wave)::value) load_part(x, ti, tid, QK{}, VB{}, HALF{});
     else load_part(x, ti, tid - HT, VB{}, END{}, HALF{});
   };
-  auto store_role = [&](const auto& x, auto s_wave) {
-    if constexpr (decltype(s_wave)::value) store_part(x, tid, QK{}, VB{}, HALF{});
-    else store_part(x, tid - HT, VB{}, END{}, HALF{});
+  auto store_role = [&](const auto& x, T* Vs, auto s_wave) {
+    if constexpr (decltype(s_wave)::value) store_part(x, tid, Vs, QK{}, VB{}, HALF{});
+    else store_part(x, tid - HT, Vs, VB{}, END{}, HALF{});
   };
 
   // steps 0 and 1 of tile ti: stage the tile and its weights, then
@@ -266,15 +270,16 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   // x: this role's prefetched part of the tile (summary kernel)
   auto tile_head = [&](int ti, int Lt, auto& x, auto s_wave) {
     if constexpr (PF) {
-      store_role(x, s_wave);
+      store_role(x, Vsb(ti & 1), s_wave);
     } else {
       uint4 xt[NXA];
       load_part(xt, ti, tid, QK{}, END{}, ALL{});
-      store_part(xt, tid, QK{}, END{}, ALL{});
+      store_part(xt, tid, Vsb(ti & 1), QK{}, END{}, ALL{});
     }
-    if (Lt != Lt_prev && tid < TT) {
+    // wS for this tile; wM[ti & 1] was last written for tile ti - 2
+    if ((ti < 2 || Lt != Lt_prev) && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
-      wM[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
+      wMb(ti & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
     }
     Lt_prev = Lt;
     __syncthreads();
@@ -313,21 +318,16 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     }
   };
 
-  // end of step 3: m (summary) and n updates
-  auto vec_updates = [&](int Lt, float gL, float g2L) {
-    if (SUM) {
-      // m <- g^Lt m + sum_tau wS[tau] q_tau: NTHR / D lanes per column
-      constexpr int LPC = NTHR / D;
-      const int col = tid / LPC, part = tid % LPC;
-      float acc = 0.f;
-      for (int t = part; t < Lt; t += LPC) acc += wS[t] * (float)Qs[t * L::LDD + col];
+  // m <- g^Lt m + sum_tau wS[tau] q_tau (summary), by the M waves' threads:
+  // HT / D lanes per column
+  auto m_vec_update = [&](int Lt, float gL) {
+    constexpr int LPC = HT / D;
+    const int mt = tid - HT, col = mt / LPC, part = mt % LPC;
+    float acc = 0.f;
+    for (int t = part; t < Lt; t += LPC) acc += wS[t] * (float)Qs[t * L::LDD + col];
 #pragma unroll
-      for (int off = 1; off < LPC; off *= 2) acc += __shfl_xor(acc, off, 64);
-      if (part == 0) mst[col] = gL * mst[col] + acc;
-    }
-    if (need_n) {
-      for (int r = tid; r < D; r += NTHR) nst[r] = g2L * nst[r] + pcol[r];
-    }
+    for (int off = 1; off < LPC; off *= 2) acc += __shfl_xor(acc, off, 64);
+    if (part == 0) mst[col] = gL * mst[col] + acc;
   };
 
   // step 4 for every thread: the denominator output
@@ -371,6 +371,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
       const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
       tile_head(ti, Lt, xq, std::true_type{});
+      T* PsT = PsTb(ti & 1);
 
       // ---- step 2 ----
       f32x4 pacc[SB][TR];
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
             if (SFULL || rw + NOWN * b < DT)
               pacc[b][r] = MMT::mma(aa, FR::tr(Ks, L::LDD, k0, 16 * (rw + NOWN * b), lane), pacc[b][r]);
         }
-        const f32x4 wm = *reinterpret_cast<const f32x4*>(wM + 16 * r + 4 * lg4);
+        const f32x4 wm = *reinterpret_cast<const f32x4*>(wMb(ti & 1) + 16 * r + 4 * lg4);
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
           const int cb = rw + NOWN * b;
@@ -421,8 +422,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       for (int b = 0; b < SB; ++b) {
         const int cb = rw + NOWN * b;
         if (need_n && (SFULL || cb < DT)) {
+          // n <- g^2Lt n + P^T wM: one writer per column; q.n of this tile is already taken
           const float cs = sum_rows4(ncol[b]);
-          if (lg4 == 0) pcol[16 * cb + lr] = cs;
+          if (lg4 == 0) nst[16 * cb + lr] = g2L * nst[16 * cb + lr] + cs;
         }
       }
       // S[:, blocks] <- g^Lt S + K^T diag(wS) K[:, blocks]; the K^T fragments are shared
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       }
       __syncthreads();
 
-      // ---- step 3 ----
+      // ---- step 3 (output kernel): B^T scores ----
       if (!SUM) {
         for (int idx = rw; idx < NTRI; idx += NOWN) {
           int r, c;
@@ -473,18 +475,16 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
             if (lg4 == 0) bpart[c * TT + tau] = rs;
           }
         }
-      }
-      vec_updates(Lt, gL, g2L);
-      __syncthreads();
+        __syncthreads();
 
-      // ---- step 4 ----
-      if (!SUM) {
+        // ---- step 4 ----
         write_den(t0, Lt);
         __syncthreads();
       }
     }
 
     if (SUM) {
+      __syncthreads();   // the M waves' last M update has read P^T and V
       // S to LDS (fp32, the tile region is free now) as the A operand of S C
       float* oS = a.S + sidx * D * D;
 #pragma unroll
@@ -547,13 +547,46 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     if constexpr (PF) load_role(xv, 0, std::false_type{});
     finish_init();
 
+    // M[:, blocks] <- g^2L M + P^T diag(wM) V[:, blocks] for tile tp (its P^T, V
+    // and wM are in the buffers of tp's parity); the P^T fragments are shared
+    auto m_update = [&](int tp, float g2Lp) {
+      const T* PsT = PsTb(tp & 1);
+      const T* Vs = Vsb(tp & 1);
+      const float* wM = wMb(tp & 1);
+        F bv[MB][NKS];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk)
+            bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wM, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc[MB];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) acc[b] = St[b][t] * g2Lp;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) {
+            const F ap = MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(ap, bv[b][kk], acc[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+            if (MFULL || rw + NOWN * b < ET) St[b][t] = acc[b];
+        }
+    };
+
+    float g2L_prev = 1.f;
     for (int ti = 0; ti < ntiles; ++ti) {
       const int t0 = ti * TT;
       const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
       const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
       tile_head(ti, Lt, xv, std::false_type{});
+      T* Vs = Vsb(ti & 1);
 
-      // ---- step 2 ----
+      // ---- step 2: the previous tile's M update, then Q M (output) or the C update ----
+      if (ti > 0) m_update(ti - 1, g2L_prev);
+      __builtin_amdgcn_sched_barrier(0);   // keep the two updates' operand loads apart
       f32x4 oacc[SUM ? 1 : MB][TR];
       if constexpr (!SUM) {
 #pragma unroll
@@ -602,37 +635,13 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
             if (MFULL || rw + NOWN * b < ET) Ct[b][t] = acc[b];
         }
       }
+      if constexpr (SUM) m_vec_update(Lt, gL);
+      g2L_prev = g2L;
       __syncthreads();
 
-      // ---- step 3: M[:, blocks] <- g^2Lt M + P^T diag(wM) V[:, blocks] ----
-      {
-        F bv[MB][NKS];
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk)
-            bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wM, kk * KS, lane);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 acc[MB];
-#pragma unroll
-          for (int b = 0; b < MB; ++b) acc[b] = St[b][t] * g2L;
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) {
-            const F ap = MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane);
-#pragma unroll
-            for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(ap, bv[b][kk], acc[b]);
-          }
-#pragma unroll
-          for (int b = 0; b < MB; ++b)
-            if (MFULL || rw + NOWN * b < ET) St[b][t] = acc[b];
-        }
-      }
-      vec_updates(Lt, gL, g2L);
-      __syncthreads();
-
-      // ---- step 4: O += B V; normalise; write O and the denominator ----
+      // ---- steps 3 (the S waves' B scores) and 4: O += B V; normalise; write O ----
       if constexpr (!SUM) {
+        __syncthreads();
         float* go = a.o + (tok0 + t0) * E;
         // each store address = a wave-uniform row/column base + one per-lane offset
         const int olane = 4 * lg4 * E + lr;
@@ -670,6 +679,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       }
     }
 
+    if (SUM) {
+      m_update(ntiles - 1, g2L_prev);
+      __syncthreads();
+    }
     if (SUM) {
       // G = S C - M with S from LDS (written by the S waves) as the A operand
       float* oC = a.C + sidx * D * E;
