@@ -55,7 +55,13 @@ struct ChunkLayout {
   static constexpr int PADT = 16 / (int)sizeof(T);
   // d-contractions run in steps of MM<T>::KS; a smaller d is zero-padded to one step
   static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;
-  static constexpr int LDD = DP + PADT;      // Qs, Ks: [tok][d]
+  // Q S and Q M take the state in the natural K order (lane swaps, bf16 with
+  // 8 waves) or read Q in the state's K order (otherwise; fewer registers)
+  static constexpr bool NAT = sizeof(T) == 2 && (D == 128 || E == 128);
+  // Qs, Ks: [tok][d].  With NAT, rows are padded by 32 bytes, which makes the
+  // row-major fragment reads free of LDS bank conflicts; the permuted reads
+  // prefer 16 (measured)
+  static constexpr int LDD = DP + (NAT ? 2 * PADT : PADT);
   static constexpr int LDV = E + PADT;       // Vs: [tok][e]
   static constexpr int LDT = TT + PADT;      // PsT: [d][tok], AB: [tok][tok]
   static constexpr size_t Qs = 0;
@@ -143,6 +149,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg4 = lane >> 4;
+  // Q times a register-resident state (Q S, Q M), the state tiles being the B
+  // operand: in the natural K order (lane swaps) with Q a plain row-major
+  // read, or in the accumulator's K order with Q read to match
+  auto state_b = [&](const auto& tiles, int kk) {
+    if constexpr (L::NAT) return FR::acc_b_nat(tiles, kk);
+    else return FR::acc_b(tiles, kk);
+  };
+  auto state_a = [&](const T* X, int row0, int kk) {
+    if constexpr (L::NAT) return MMT::ld(X, L::LDD, row0, 32 * kk, lane);
+    else return FR::perm(X, L::LDD, row0, kk, lane);
+  };
   const int nspan = a.nspan;
   const int unit = blockIdx.x / nspan, span = blockIdx.x - unit * nspan;
   const int head = unit % a.H;
@@ -383,10 +400,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       for (int kk = 0; kk < QSK; ++kk) {
         F bs[SB];
 #pragma unroll
-        for (int b = 0; b < SB; ++b) bs[b] = FR::acc_b(St[b], kk);
+        for (int b = 0; b < SB; ++b) bs[b] = state_b(St[b], kk);
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
-          const F aq = FR::perm(Qs, L::LDD, 16 * r, kk, lane);
+          const F aq = state_a(Qs, 16 * r, kk);
 #pragma unroll
           for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
         }
@@ -597,10 +614,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         for (int kk = 0; kk < QSK; ++kk) {
           F bm[MB];
 #pragma unroll
-          for (int b = 0; b < MB; ++b) bm[b] = FR::acc_b(St[b], kk);
+          for (int b = 0; b < MB; ++b) bm[b] = state_b(St[b], kk);
 #pragma unroll
           for (int r = 0; r < TR; ++r) {
-            const F aq = FR::perm(Qs, L::LDD, 16 * r, kk, lane);
+            const F aq = state_a(Qs, 16 * r, kk);
 #pragma unroll
             for (int b = 0; b < MB; ++b) oacc[b][r] = MMT::mma(aq, bm[b], oacc[b][r]);
           }

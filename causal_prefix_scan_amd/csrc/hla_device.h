@@ -17,6 +17,7 @@ namespace hla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -116,6 +117,27 @@ template <> struct Frag<__bf16> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = (__bf16)((float)x[i] * ww[i]);
     return y;
+  }
+  // B operand of step kk in the natural K order (lane group g: K rows 32 kk +
+  // 8 g + [0, 8)) from fp32 accumulator tiles 2 kk and 2 kk + 1 stacked along
+  // K.  Each lane packs its four rows of both tiles to bf16 (rows 4 g' + [0, 4)
+  // of group g'); one 32-lane and one 16-lane swap per dword pair then route
+  // group g' of tile 2 kk to group g' / 2 (half g' % 2) and of tile 2 kk + 1 to
+  // group 2 + g' / 2.
+  template <int N>
+  __device__ static __forceinline__ F acc_b_nat(const f32x4 (&tiles)[N], int kk) {
+    const f32x4 a = tiles[2 * kk];
+    const f32x4 b = (2 * kk + 1 < N) ? tiles[2 * kk + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+    auto pk = [](float x, float y) {
+      const bf16x2 v = {(__bf16)x, (__bf16)y};
+      return __builtin_bit_cast(unsigned, v);
+    };
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pk(a[0], a[1]), pk(b[0], b[1]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pk(a[2], a[3]), pk(b[2], b[3]), false, false);
+    const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+    const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+    const uint4 r = make_uint4(t0[0], t1[0], t0[1], t1[1]);
+    return __builtin_bit_cast(F, r);
   }
 };
 
