@@ -57,8 +57,10 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--chunk", type=int, default=0, help="override the segment length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
+    ap.add_argument("--cpu-tokens", type=int, default=3072,
                     help="tokens per unit in the oracle sample (forward workloads)")
+    ap.add_argument("--cpu-steps", type=int, default=40,
+                    help="decode steps in the oracle sample (decode workload)")
     return ap.parse_args()
 
 
@@ -250,7 +252,7 @@ def bench_decode(args, torch, np):
                      "avg_launch_ms": round(step_ms, 4)},
     }
     if states64 is not None:
-        nb = 8
+        nb = min(args.cpu_steps, len(toks_host))
         toks = [(t[0], t[1], t[2]) for t in toks_host[:nb]]
         out["cpu_baseline"] = cpu_baseline_decode(states64, toks, nb)
     return out

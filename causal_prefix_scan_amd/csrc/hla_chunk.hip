@@ -722,6 +722,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
               oC[e] = Ct[b][t][j];
               oG[e] = acc[j] - St[b][t][j];
             }
+            // one row block at a time: keeps the S loads of later blocks from
+            // being hoisted (and spilled) while C and M are both live
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }

@@ -112,20 +112,25 @@ const char* hla_version(void);
 hla_status hla_fwd_chunk_summaries(const hla_problem* p, const void* q, const void* k,
                                    const void* v, const hla_state* out, void* stream);
 
-/* Bytes of scratch hla_scan needs for this problem (0 when n is a power of
- * two).  Host-only; returns 0 for an invalid problem. */
+/* Bytes of scratch hla_scan needs for this problem: 0 with at most 16
+ * segments per (b, h); otherwise the run totals and the tree's padding slots,
+ * B*H*N summaries of (d*d + 2*d*dv + 2*d) floats, N the power of two >= the
+ * number of runs.  Host-only; returns 0 for an invalid problem. */
 size_t hla_scan_workspace_bytes(const hla_problem* p);
 
 /*
- * Exclusive Blelloch scan (method section 4: the exclusive scan of segment
+ * Exclusive scan (method section 4: the exclusive Blelloch scan of segment
  * summaries under the semidirect-product combine with cross term S_B C_A;
- * decay per key contribution 2 as read above).  In place: on entry `inout`
+ * decay per key contribution 2 as read above), in its blocked two-level form:
+ * runs of consecutive segments are reduced in order, the run totals go through
+ * the Blelloch tree, and each run is rescanned from its prefix; the result is
+ * the same up to fp32 rounding order.  In place: on entry `inout`
  * holds the n segment summaries of every (b, h); on return it holds the
  * exclusive prefixes P_s = s_0 (+) ... (+) s_{s-1} (P_0 = 0).  If
  * `total_out` is non-NULL, each of its non-NULL fields receives the
  * inclusive total of all n segments ([B, H, ...], the state after T tokens).
  * `workspace` must hold hla_scan_workspace_bytes(p) bytes (may be NULL when
- * that is 0).
+ * that is 0, i.e. with at most 16 segments per (b, h)).
  */
 hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_state* total_out,
                     void* workspace, size_t workspace_bytes, void* stream);
