@@ -73,14 +73,16 @@ struct ChunkLayout {
   static constexpr size_t PsT0 = Vs1 + (size_t)TT * LDV * sizeof(T);
   static constexpr size_t PsT1 = PsT0 + (size_t)DP * LDT * sizeof(T);
   static constexpr size_t AB = PsT1 + (size_t)DP * LDT * sizeof(T);
-  static constexpr size_t TILE_END = AB + (size_t)TT * LDT * sizeof(T);
+  // output kernel: B scores of a tile, read while the next tile's A' is in AB
+  static constexpr size_t BB = AB + (size_t)TT * LDT * sizeof(T);
+  static constexpr size_t TILE_END = BB + (MODE == 1 ? (size_t)TT * LDT * sizeof(T) : 0);
   // fp32 overlay used at segment boundaries: S [D][D+4]
   static constexpr int LFS = D + 4;
   static constexpr size_t F_END = (size_t)D * LFS * 4;
   static constexpr size_t BIG = TILE_END > F_END ? TILE_END : F_END;
   static constexpr size_t W = (BIG + 15) / 16 * 16;
-  // w1, w2, wS, wM0, wM1, pw, pw2, qn [TT]; bpart [TR][TT]; nst, mst [D]
-  static constexpr size_t TOTAL = W + (size_t)(8 * TT + (TT / 16) * TT + 2 * D) * 4;
+  // w1, w2, wS, wM0, wM1, pw, pw2, qn0, qn1 [TT]; bpart [TR][TT]; nst, mst [D]
+  static constexpr size_t TOTAL = W + (size_t)(9 * TT + (TT / 16) * TT + 2 * D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -124,6 +126,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   constexpr int NOWN = NW / 2;
   constexpr int SB = (DT + NOWN - 1) / NOWN, MB = (ET + NOWN - 1) / NOWN;
   constexpr bool SUM = MODE == MODE_SUMMARY;
+  // output kernel: add B V and write a tile's outputs during the next tile's
+  // main phase (8 waves), or in a phase of its own (4 waves: fewer registers)
+  constexpr bool DEFER = !SUM && NW == 8;
   // every block index is in range when the blocks divide evenly over a role
   constexpr bool SFULL = DT % NOWN == 0, MFULL = ET % NOWN == 0;
 
@@ -134,6 +139,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   auto Vsb = [&](int p) { return reinterpret_cast<T*>(smem + (p ? L::Vs1 : L::Vs0)); };
   auto PsTb = [&](int p) { return reinterpret_cast<T*>(smem + (p ? L::PsT1 : L::PsT0)); };
   T* AB = reinterpret_cast<T*>(smem + L::AB);
+  T* BB = reinterpret_cast<T*>(smem + L::BB);
   float* FS = reinterpret_cast<float*>(smem);
   float* w1 = reinterpret_cast<float*>(smem + L::W);
   float* w2 = w1 + TT;
@@ -141,8 +147,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   auto wMb = [&](int p) { return wS + (p ? 2 * TT : TT); };
   float* pw = wS + 3 * TT;
   float* pw2 = pw + TT;
-  float* qn = pw2 + TT;
-  float* bpart = qn + TT;        // [TR][TT]: B column sums per 16-row block of j
+  float* qn = pw2 + TT;          // [2][TT]: q.n by tile parity
+  auto qnb = [&](int p) { return qn + p * TT; };
+  float* bpart = qn + 2 * TT;    // [TR][TT]: B column sums per 16-row block of j
   float* nst = bpart + TR * TT;
   float* mst = nst + D;
 
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         acc += (float)Qs[tau * L::LDD + c] * nst[c];
 #pragma unroll
       for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
-      if (part == 0) qn[tau] = acc;
+      if (part == 0) qnb(ti & 1)[tau] = acc;
     }
     for (int idx = wave; idx < NTRI; idx += NW) {
       int r, c;
@@ -347,14 +354,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
     if (part == 0) mst[col] = gL * mst[col] + acc;
   };
 
-  // step 4 for every thread: the denominator output
-  auto write_den = [&](int t0, int Lt) {
-    if (a.den != nullptr && tid < Lt) {
-      float dn = 0.f;
-      for (int c = 0; c <= tid / 16; ++c) dn += bpart[c * TT + tid];
-      a.den[tok0 + t0 + tid] = dn + w2[tid] * qn[tid];
-    }
-  };
 
   // end of the segment, for every thread: m and h = S m - n (S in FS)
   auto write_mh = [&]() {
@@ -486,17 +485,14 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
             const int jj = 16 * c + 4 * lg4 + j;
             val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
           }
-          store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
+          store4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
           if (need_n) {
             const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
             if (lg4 == 0) bpart[c * TT + tau] = rs;
           }
         }
         __syncthreads();
-
-        // ---- step 4 ----
-        write_den(t0, Lt);
-        __syncthreads();
+        if constexpr (!DEFER) __syncthreads();   // step 4: the M waves write the outputs
       }
     }
 
@@ -593,6 +589,53 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         }
     };
 
+    // output kernel: oacc holds g^(2(tau+1)) Q M_prev of a tile until its B V
+    // is added one tile later (B scores in BB, V and q.n in the tile's parity
+    // buffers); then the tile is normalised and written with its denominator
+    f32x4 oacc[SUM ? 1 : MB][TR];
+    auto finish_out = [&](int tp, int Ltp) {
+      const T* Vs = Vsb(tp & 1);
+      const float* qnp = qnb(tp & 1);
+      float* go = a.o + (tok0 + (size_t)tp * TT) * E;
+      // each store address = a wave-uniform row/column base + one per-lane offset
+      const int olane = 4 * lg4 * E + lr;
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+          const F ab = MMT::ld(BB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+            if (MFULL || rw + NOWN * b < ET)
+              oacc[b][r] = MMT::mma(ab, FR::tr(Vs, L::LDV, k0, 16 * (rw + NOWN * b), lane), oacc[b][r]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tau = 16 * r + 4 * lg4 + j;
+          float scale = 1.f;
+          if (a.normalize) {
+            float dn = 0.f;
+            for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
+            scale = 1.f / (dn + w2[tau] * qnp[tau] + a.eps);
+          }
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            const int cb = rw + NOWN * b;
+            if ((MFULL || cb < ET) && tau < Ltp) {
+              const float val = a.normalize ? oacc[b][r][j] * scale : oacc[b][r][j];
+              float* rowp = go + ((16 * r + j) * E + 16 * cb);
+              rowp[olane] = val;
+            }
+          }
+        }
+      }
+      const int mt = tid - HT;
+      if (a.den != nullptr && mt < Ltp) {
+        float dn = 0.f;
+        for (int c = 0; c <= mt / 16; ++c) dn += bpart[c * TT + mt];
+        a.den[tok0 + (size_t)tp * TT + mt] = dn + w2[mt] * qnp[mt];
+      }
+    };
+
     float g2L_prev = 1.f;
     for (int ti = 0; ti < ntiles; ++ti) {
       const int t0 = ti * TT;
@@ -601,10 +644,14 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       tile_head(ti, Lt, xv, std::false_type{});
       T* Vs = Vsb(ti & 1);
 
-      // ---- step 2: the previous tile's M update, then Q M (output) or the C update ----
+      // ---- step 2: the previous tile's outputs (output kernel) and M update,
+      //      then Q M (output) or the C update (summary) ----
+      if constexpr (DEFER) {
+        if (ti > 0) finish_out(ti - 1, TT);   // only the last tile can be short
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (ti > 0) m_update(ti - 1, g2L_prev);
       __builtin_amdgcn_sched_barrier(0);   // keep the two updates' operand loads apart
-      f32x4 oacc[SUM ? 1 : MB][TR];
       if constexpr (!SUM) {
 #pragma unroll
         for (int b = 0; b < MB; ++b)
@@ -656,46 +703,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       g2L_prev = g2L;
       __syncthreads();
 
-      // ---- steps 3 (the S waves' B scores) and 4: O += B V; normalise; write O ----
-      if constexpr (!SUM) {
-        __syncthreads();
-        float* go = a.o + (tok0 + t0) * E;
-        // each store address = a wave-uniform row/column base + one per-lane offset
-        const int olane = 4 * lg4 * E + lr;
-#pragma unroll
-        for (int r = 0; r < TR; ++r) {
-          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
-            const F ab = MMT::ld(AB, L::LDT, 16 * r, k0, lane);
-#pragma unroll
-            for (int b = 0; b < MB; ++b)
-              if (MFULL || rw + NOWN * b < ET)
-                oacc[b][r] = MMT::mma(ab, FR::tr(Vs, L::LDV, k0, 16 * (rw + NOWN * b), lane), oacc[b][r]);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tau = 16 * r + 4 * lg4 + j;
-            float scale = 1.f;
-            if (a.normalize) {
-              float dn = 0.f;
-              for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
-              scale = 1.f / (dn + w2[tau] * qn[tau] + a.eps);
-            }
-#pragma unroll
-            for (int b = 0; b < MB; ++b) {
-              const int cb = rw + NOWN * b;
-              if ((MFULL || cb < ET) && tau < Lt) {
-                const float val = a.normalize ? oacc[b][r][j] * scale : oacc[b][r][j];
-                float* rowp = go + ((16 * r + j) * E + 16 * cb);
-                rowp[olane] = val;
-              }
-            }
-          }
-        }
-        write_den(t0, Lt);
+      // ---- step 3: the S waves' B scores; step 4 without DEFER ----
+      if constexpr (!SUM) __syncthreads();
+      if constexpr (!SUM && !DEFER) {
+        finish_out(ti, Lt);
         __syncthreads();
       }
     }
 
+    if constexpr (DEFER) finish_out(ntiles - 1, (Lspan - (ntiles - 1) * TT));
     if (SUM) {
       m_update(ntiles - 1, g2L_prev);
       __syncthreads();
