@@ -197,17 +197,30 @@ struct RunArgs {
   int from_prefix;                 // rescan starts from a*[run] (else from the identity)
 };
 
-// Steps 1 (REDUCE) and 3: one workgroup per (unit, run, 16-row block), E/16
-// waves; wave w owns column block w of C and G.  blockIdx.x is laid out so
-// that the D/16 workgroups of one (unit, run) share blockIdx.x mod 8 and so
-// run on one XCD, where the C and m they all read stay in one L2.
+// Row tiles (16 rows) per workgroup of steps 1 and 3: all rows up to d = 64,
+// a quarter of them at d = 128 (register budget).  Every workgroup reads the whole
+// running C each step, so fewer row blocks means fewer re-reads of it.
+template <int D>
+struct RunRT {
+  static constexpr int value = D <= 64 ? D / 16 : 2;
+};
+
+// Steps 1 (REDUCE) and 3: one workgroup per (unit, run, block of 16 RT rows),
+// E/16 waves; wave w owns column block w of C and G.  blockIdx.x is laid out
+// so that the row blocks of one (unit, run) share blockIdx.x mod 8 and so run
+// on one XCD, where the C and m they all read stay in one L2.
 template <int D, int E, bool REDUCE>
 __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
-  constexpr int NW = E / 16, NT = 64 * NW, DT = D / 16, NRB = D / 16, LS = D + 4;
-  constexpr int SV = 16 * D / 4;            // f32x4 in 16 rows of S
+  constexpr int RT = RunRT<D>::value, RB = 16 * RT;
+  constexpr int NW = E / 16, NT = 64 * NW, DT = D / 16, NRB = D / RB, LS = D + 4;
+  constexpr int SV = RB * D / 4;            // f32x4 in RB rows of S
   constexpr int SPT = (SV + NT - 1) / NT;
-  constexpr int PH = 4;                     // lanes per row of the S m product
-  __shared__ __attribute__((aligned(16))) float sS[16 * LS];
+  constexpr int PH = NT / RB;               // lanes per row of the S m product
+  static_assert(PH >= 1 && (PH & (PH - 1)) == 0 && PH <= 64, "rows per workgroup");
+  // one workgroup per run: nobody else reads the run's C and m, so step 3
+  // writes their prefixes too and step 4 is not needed
+  constexpr bool CM = !REDUCE && NRB == 1;
+  __shared__ __attribute__((aligned(16))) float sS[RB * LS];
   __shared__ float sm[2][D];
 
   const int bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
@@ -217,15 +230,18 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
   const int k0 = run * a.R;
   const int len = (a.n - k0) < a.R ? (a.n - k0) : a.R;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg4 = lane >> 4;
-  const int r0 = 16 * rb;
+  const int r0 = RB * rb;
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float al = gpow(g, log2f(g), a.chunk), al2 = al * al;
 
-  // running state: C column block (rows 16 t + 4 lg4 + j), G rows x column
-  // block, S rows (f32x4 e = tid + NT i: row e / (D/4), columns 4 (e % (D/4))),
-  // h row tid (tid < 16); m in LDS
-  f32x4 Cb[DT], Gb, Sb[SPT];
+  // running state: C column block (rows 16 t + 4 lg4 + j), G row tiles x
+  // column block (tile q: rows r0 + 16 q + 4 lg4 + j), S rows (f32x4 e = tid +
+  // NT i: row e / (D/4), columns 4 (e % (D/4))), h row hrow in the first of
+  // the row's PH lanes (hown); m in LDS
+  f32x4 Cb[DT], Gb[RT], Sb[SPT];
   float hb = 0.f;
+  const int hrow = tid / PH, hpart = tid % PH;
+  const bool hown = hpart == 0;
   const bool pre = !REDUCE && a.from_prefix;
   const size_t pr = (size_t)unit * a.runs + run;
 #pragma unroll
@@ -234,8 +250,10 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
     for (int j = 0; j < 4; ++j)
       Cb[t][j] = pre ? a.aC[pr * D * E + (size_t)(16 * t + 4 * lg4 + j) * E + 16 * w + lr] : 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    Gb[j] = pre ? a.aG[pr * D * E + (size_t)(r0 + 4 * lg4 + j) * E + 16 * w + lr] : 0.f;
+  for (int q = 0; q < RT; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      Gb[q][j] = pre ? a.aG[pr * D * E + (size_t)(r0 + 16 * q + 4 * lg4 + j) * E + 16 * w + lr] : 0.f;
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int e = tid + NT * i;
@@ -243,11 +261,11 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
     if (pre && e < SV)
       Sb[i] = reinterpret_cast<const f32x4*>(a.aS + pr * D * D + (size_t)r0 * D)[e];
   }
-  if (pre && tid < 16) hb = a.ah[pr * D + r0 + tid];
+  if (pre && hown) hb = a.ah[pr * D + r0 + hrow];
   for (int t = tid; t < D; t += NT) sm[0][t] = pre ? a.am[pr * D + t] : 0.f;
 
   // loads of one segment
-  f32x4 xC[DT], xG, xS[SPT];
+  f32x4 xC[DT], xG[RT], xS[SPT];
   float xh = 0.f, xm = 0.f;
   auto load = [&](int k) {
     const size_t sl = (size_t)unit * a.n + k0 + k;
@@ -258,13 +276,15 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) xC[t][j] = pC[(16 * t + 4 * lg4 + j) * E + 16 * w + lr];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xG[j] = pG[(r0 + 4 * lg4 + j) * E + 16 * w + lr];
+    for (int q = 0; q < RT; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xG[q][j] = pG[(r0 + 16 * q + 4 * lg4 + j) * E + 16 * w + lr];
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int e = tid + NT * i;
       xS[i] = e < SV ? reinterpret_cast<const f32x4*>(a.S + sl * D * D + (size_t)r0 * D)[e] : zero4();
     }
-    xh = tid < 16 ? a.h[sl * D + r0 + tid] : 0.f;
+    xh = hown ? a.h[sl * D + r0 + hrow] : 0.f;
     xm = tid < D ? a.m[sl * D + tid] : 0.f;
   };
 
@@ -279,53 +299,71 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
       if (e < SV) *reinterpret_cast<f32x4*>(sS + (e / (D / 4)) * LS + 4 * (e % (D / 4))) = xS[i];
     }
     __syncthreads();
-    f32x4 cS[DT], cG = xG, cSr[SPT];
+    f32x4 cS[DT], cG[RT], cSr[SPT];
     float ch = xh, cm = xm;
 #pragma unroll
     for (int t = 0; t < DT; ++t) cS[t] = xC[t];
 #pragma unroll
+    for (int q = 0; q < RT; ++q) cG[q] = xG[q];
+#pragma unroll
     for (int i = 0; i < SPT; ++i) cSr[i] = xS[i];
     if (k + 1 < len) load(k + 1);
 
-    // G rows += a S_B C_A (C_A = running C, before this segment)
-    f32x4 acc = zero4();
+    // G rows += a S_B C_A (C_A = running C, before this segment); RT
+    // independent accumulator chains (two when RT = 1)
+    f32x4 acc[RT], acc1 = zero4();
 #pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk)
-      acc = MM<float>::mma(sS[lr * LS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)], Frag<float>::acc_b(Cb, kk), acc);
-    // h rows += a S_B m_A
-    float hm = 0.f;
-    if (tid < 16 * PH) {
-      const int row = tid / PH, part = tid % PH;
-      for (int c = part; c < D; c += PH) hm += sS[row * LS + c] * sm[cur][c];
+    for (int q = 0; q < RT; ++q) acc[q] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < D / 4; ++kk) {
+      const float bk = Frag<float>::acc_b(Cb, kk);
+#pragma unroll
+      for (int q = 0; q < RT; ++q) {
+        const float ak = sS[(16 * q + lr) * LS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)];
+        if (RT == 1 && (kk & 1)) acc1 = MM<float>::mma(ak, bk, acc1);
+        else acc[q] = MM<float>::mma(ak, bk, acc[q]);
+      }
     }
+    if (RT == 1) acc[0] += acc1;
+    // h rows += a S_B m_A: PH lanes per row, D / PH products each
+    float hm = 0.f;
+#pragma unroll
+    for (int c = hpart; c < D; c += PH) hm += sS[hrow * LS + c] * sm[cur][c];
 #pragma unroll
     for (int off = 1; off < PH; off *= 2) hm += __shfl_xor(hm, off, 64);
-    hm = __shfl(hm, (tid * PH) & 63, 64);   // lane tid < 16 takes row tid's sum
 
-    const f32x4 oG = Gb;
-    f32x4 oS[SPT];
+    if (!REDUCE) {
+      // the segment's own rows become its exclusive prefix: the running state
+      // before this segment (the segment itself was read a step earlier)
+      const size_t sl = (size_t)unit * a.n + k0 + k;
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) oS[i] = Sb[i];
-    const float oh = hb;
-    Gb = Gb * al2 + cG + acc * al;
+      for (int q = 0; q < RT; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a.G[sl * D * E + (size_t)(r0 + 16 * q + 4 * lg4 + j) * E + 16 * w + lr] = Gb[q][j];
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int e = tid + NT * i;
+        if (e < SV) reinterpret_cast<f32x4*>(a.S + sl * D * D + (size_t)r0 * D)[e] = Sb[i];
+      }
+      if (hown) a.h[sl * D + r0 + hrow] = hb;
+      if constexpr (CM) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            a.C[sl * D * E + (size_t)(16 * t + 4 * lg4 + j) * E + 16 * w + lr] = Cb[t][j];
+        if (tid < D) a.m[sl * D + tid] = sm[cur][tid];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RT; ++q) Gb[q] = Gb[q] * al2 + cG[q] + acc[q] * al;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) Sb[i] = Sb[i] * al + cSr[i];
     hb = al2 * hb + ch + al * hm;
 #pragma unroll
     for (int t = 0; t < DT; ++t) Cb[t] = Cb[t] * al + cS[t];
     if (tid < D) sm[cur ^ 1][tid] = al * sm[cur][tid] + cm;
-    if (!REDUCE) {
-      // the segment's own rows become its exclusive prefix (read above, before the update)
-      const size_t sl = (size_t)unit * a.n + k0 + k;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a.G[sl * D * E + (size_t)(r0 + 4 * lg4 + j) * E + 16 * w + lr] = oG[j];
-#pragma unroll
-      for (int i = 0; i < SPT; ++i) {
-        const int e = tid + NT * i;
-        if (e < SV) reinterpret_cast<f32x4*>(a.S + sl * D * D + (size_t)r0 * D)[e] = oS[i];
-      }
-      if (tid < 16) a.h[sl * D + r0 + tid] = oh;
-    }
     cur ^= 1;
     __syncthreads();
   }
@@ -352,9 +390,11 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
   }
   if (oG) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) oG[(size_t)(r0 + 4 * lg4 + j) * E + 16 * w + lr] = Gb[j];
+    for (int q = 0; q < RT; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) oG[(size_t)(r0 + 16 * q + 4 * lg4 + j) * E + 16 * w + lr] = Gb[q][j];
   }
-  if (oh && tid < 16) oh[r0 + tid] = hb;
+  if (oh && hown) oh[r0 + hrow] = hb;
   if (rb == 0) {
     if (oC) {
 #pragma unroll
@@ -428,6 +468,7 @@ size_t scan_workspace_floats(int64_t units, int n, int d, int dv) {
 template <int D, int E>
 static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   constexpr int NRB = D / 16, VEC = (D * D + 2 * D * E + 2 * D) / 4;
+  constexpr int NRR = D / (16 * RunRT<D>::value);   // row blocks of the run kernels
   constexpr int PARTS = VEC / 1024 > 0 ? VEC / 1024 : 1;   // swap workgroups per pair
   const int units = p.units;
   RunArgs r;
@@ -445,7 +486,7 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   }
   const unsigned groups8 = (unsigned)((cnt + 7) / 8 * 8);
   if (r.runs > 1) {
-    hipLaunchKernelGGL((run_rows_kernel<D, E, true>), dim3(groups8 * NRB), dim3(64 * (E / 16)), 0, s, r);
+    hipLaunchKernelGGL((run_rows_kernel<D, E, true>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
     if (hipError_t e = hipGetLastError()) return e;
     // exclusive Blelloch scan of the run totals; padding slots follow them
     ScanArgs a;
@@ -484,8 +525,9 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
       if (hipError_t e = hipGetLastError()) return e;
     }
   }
-  hipLaunchKernelGGL((run_rows_kernel<D, E, false>), dim3(groups8 * NRB), dim3(64 * (E / 16)), 0, s, r);
+  hipLaunchKernelGGL((run_rows_kernel<D, E, false>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
   if (hipError_t e = hipGetLastError()) return e;
+  if (NRR == 1) return hipSuccess;   // the rescan wrote C and m
   constexpr int VCM = (D * E + D) / 4;
   hipLaunchKernelGGL((run_cm_kernel<D, E>), dim3((unsigned)(cnt * ((VCM + 255) / 256))), dim3(256), 0,
                      s, r);
