@@ -344,14 +344,54 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
 
   // m <- g^Lt m + sum_tau wS[tau] q_tau (summary), by the M waves' threads:
   // HT / D lanes per column
+  // (thread: 4 adjacent columns, every TPN-th token; the TPN partial sums of
+  // a column group sit in adjacent lanes)
   auto m_vec_update = [&](int Lt, float gL) {
-    constexpr int LPC = HT / D;
-    const int mt = tid - HT, col = mt / LPC, part = mt % LPC;
-    float acc = 0.f;
-    for (int t = part; t < Lt; t += LPC) acc += wS[t] * (float)Qs[t * L::LDD + col];
+    constexpr int NCG = D / 4, TPN = HT / NCG;
+    static_assert(TPN >= 1 && TPN <= 64 && (TPN & (TPN - 1)) == 0, "m update lanes");
+    const int mt = tid - HT, cg = mt / TPN, tp = mt % TPN;
+    f32x4 acc = zero4();
+    for (int t = tp; t < Lt; t += TPN) {
+      const T* qp = Qs + t * L::LDD + 4 * cg;
+      const float wt = wS[t];
 #pragma unroll
-    for (int off = 1; off < LPC; off *= 2) acc += __shfl_xor(acc, off, 64);
-    if (part == 0) mst[col] = gL * mst[col] + acc;
+      for (int i = 0; i < 4; ++i) acc[i] += wt * (float)qp[i];
+    }
+#pragma unroll
+    for (int off = 1; off < TPN; off *= 2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+    if (tp == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mst[4 * cg + i] = gL * mst[4 * cg + i] + acc[i];
+    }
+  };
+
+  // B^T = (P Q^T) o decay for tile ti (output kernel), the tiles shared by all
+  // waves with DEFER, else by the S waves (the M waves then hold Q M_prev)
+  constexpr int NBW = DEFER ? NW : NOWN;
+  auto b_scores = [&](int ti) {
+    const T* PsT = PsTb(ti & 1);
+    for (int idx = DEFER ? wave : rw; idx < NTRI; idx += NBW) {
+      int r, c;
+      tri_tile(idx, r, c);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DP; k0 += KS)
+        acc = MMT::mma(FR::tr(PsT, L::LDT, k0, 16 * c, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+      const int tau = 16 * r + lr;
+      f32x4 val;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int jj = 16 * c + 4 * lg4 + j;
+        val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
+      }
+      store4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
+      if (need_n) {
+        const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+        if (lg4 == 0) bpart[c * TT + tau] = rs;
+      }
+    }
   };
 
 
@@ -469,28 +509,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       }
       __syncthreads();
 
-      // ---- step 3 (output kernel): B^T scores ----
+      // ---- step 3 (output kernel): B^T scores, shared with the M waves ----
       if (!SUM) {
-        for (int idx = rw; idx < NTRI; idx += NOWN) {
-          int r, c;
-          tri_tile(idx, r, c);
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int k0 = 0; k0 < DP; k0 += KS)
-            acc = MMT::mma(FR::tr(PsT, L::LDT, k0, 16 * c, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
-          const int tau = 16 * r + lr;
-          f32x4 val;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int jj = 16 * c + 4 * lg4 + j;
-            val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
-          }
-          store4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
-          if (need_n) {
-            const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
-            if (lg4 == 0) bpart[c * TT + tau] = rs;
-          }
-        }
+        b_scores(ti);
         __syncthreads();
         if constexpr (!DEFER) __syncthreads();   // step 4: the M waves write the outputs
       }
@@ -703,8 +724,11 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       g2L_prev = g2L;
       __syncthreads();
 
-      // ---- step 3: the S waves' B scores; step 4 without DEFER ----
-      if constexpr (!SUM) __syncthreads();
+      // ---- step 3: B scores (with the S waves); step 4 without DEFER ----
+      if constexpr (!SUM) {
+        if constexpr (DEFER) b_scores(ti);
+        __syncthreads();
+      }
       if constexpr (!SUM && !DEFER) {
         finish_out(ti, Lt);
         __syncthreads();
