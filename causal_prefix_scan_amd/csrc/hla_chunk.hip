@@ -217,7 +217,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
+    // the score buffers' upper tiles are read as zeros and never written; with
+    // d < DP so are the padding columns of Q, K and rows of P^T
+    constexpr size_t Z0 = DP > D ? 0 : L::AB;
+    for (size_t i = Z0 / 16 + tid; i < L::TILE_END / 16; i += NTHR)
       reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
   };
@@ -749,23 +752,28 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
       for (int b = 0; b < MB; ++b) {
         const int cb = rw + NOWN * b;
         if (MFULL || cb < ET) {
+          // G = S C - M accumulated onto -M, the row blocks interleaved
 #pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            f32x4 acc = zero4();
+          for (int t = 0; t < DT; ++t) St[b][t] = -St[b][t];
 #pragma unroll
-            for (int kk = 0; kk < D / 4; ++kk)
-              acc = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
-                                   Frag<float>::acc_b(Ct[b], kk), acc);
+          for (int kk = 0; kk < D / 4; ++kk) {
+            const float bk = Frag<float>::acc_b(Ct[b], kk);
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+              St[b][t] = MM<float>::mma(FS[(16 * t + lr) * L::LFS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)],
+                                        bk, St[b][t]);
+          }
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const size_t e = (size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr;
               oC[e] = Ct[b][t][j];
-              oG[e] = acc[j] - St[b][t][j];
+              oG[e] = St[b][t][j];
             }
-            // one row block at a time: keeps the S loads of later blocks from
-            // being hoisted (and spilled) while C and M are both live
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          // one column block at a time: keeps the S loads of the next block from
+          // being hoisted (and spilled) while C and M are both live
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       write_mh();
