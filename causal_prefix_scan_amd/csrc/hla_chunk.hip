@@ -108,7 +108,8 @@ __device__ __forceinline__ void tri_tile(int idx, int& r, int& c) {
 }
 
 template <typename T, int D, int E, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
+// (4-wave kernels are held to two workgroups per CU: 256 registers per lane)
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkArgs a) {
   constexpr int NTHR = 64 * NW;
   using L = ChunkLayout<T, D, E, MODE>;
   using MMT = MM<T>;
@@ -183,21 +184,58 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
   const int rw = sRole ? wave : wave - NOWN;
   const int ntiles = (Lspan + TT - 1) / TT;
 
+  // output kernel with 4 waves (short segments are common there): the prefix
+  // S_P (every thread, to LDS) and the M waves' column blocks of C_P are
+  // loaded together before anything waits on them
+  constexpr bool EARLY = !SUM && NW == 4;
+  constexpr int FSN = (D * D / 4 + NTHR - 1) / NTHR;
+  f32x4 fsx[EARLY ? FSN : 1];
+  f32x4 cpx[EARLY ? MB : 1][EARLY ? DT : 1];
+  if constexpr (EARLY) {
+    const f32x4* pS = reinterpret_cast<const f32x4*>(a.S + sidx * D * D);
+#pragma unroll
+    for (int i = 0; i < FSN; ++i) {
+      const int e = tid + NTHR * i;
+      fsx[i] = e < D * D / 4 ? pS[e] : zero4();
+    }
+    if (!sRole) {
+      const float* pC = a.C + sidx * D * E;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int cb = (rw + NOWN * b) % ET;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cpx[b][t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr];
+      }
+    }
+  }
   if (tid < TT) {
     pw[tid] = gpow(g, lgg, tid);
     pw2[tid] = gpow(g, lgg, 2 * tid);
     w1[tid] = gpow(g, lgg, tid + 1);
     w2[tid] = gpow(g, lgg, 2 * tid + 2);
   }
-  if (SUM) {
+  if constexpr (SUM) {
     for (int i = tid; i < D; i += NTHR) { nst[i] = 0.f; mst[i] = 0.f; }
   } else {
     // S_P to LDS (fp32): the S waves take their columns of it, the M waves use
     // it as the A operand of S_P C_P, and n = S_P m_P - h_P reads it
-    const float* pS = a.S + sidx * D * D;
-    for (int i = tid; i < D * D / 4; i += NTHR) {
-      const int r = (4 * i) / D, c = (4 * i) % D;
-      *reinterpret_cast<f32x4*>(FS + r * L::LFS + c) = reinterpret_cast<const f32x4*>(pS)[i];
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int i = 0; i < FSN; ++i) {
+        const int e = tid + NTHR * i;
+        if (e < D * D / 4) {
+          const int r = (4 * e) / D, c = (4 * e) % D;
+          *reinterpret_cast<f32x4*>(FS + r * L::LFS + c) = fsx[i];
+        }
+      }
+    } else {
+      const float* pS = a.S + sidx * D * D;
+      for (int i = tid; i < D * D / 4; i += NTHR) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        *reinterpret_cast<f32x4*>(FS + r * L::LFS + c) = reinterpret_cast<const f32x4*>(pS)[i];
+      }
     }
   }
   __syncthreads();
@@ -553,7 +591,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         for (int t = 0; t < DT; ++t) { St[b][t] = zero4(); Ct[b][t] = zero4(); }
     } else {
       // M = S_P C_P - G_P: S_P from LDS is the A operand, the block of C_P the B operand
-      const float* pC = a.C + sidx * D * E;
       const float* pG = a.G + sidx * D * E;
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
@@ -563,9 +600,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(ChunkArgs a) {
         if (MFULL || cb < ET) {
           f32x4 cp[DT];
 #pragma unroll
-          for (int t = 0; t < DT; ++t)
+          for (int t = 0; t < DT; ++t) {
+            if constexpr (EARLY) {
+              cp[t] = cpx[b][t];
+            } else {
+              const float* pC = a.C + sidx * D * E;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cp[t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr];
+              for (int j = 0; j < 4; ++j) cp[t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + 16 * cb + lr];
+            }
+          }
 #pragma unroll
           for (int t = 0; t < DT; ++t) {
             f32x4 acc = zero4();
