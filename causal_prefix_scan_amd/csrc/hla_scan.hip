@@ -12,8 +12,10 @@
 // Two levels.  The n segments of a (b, h) unit are cut into runs of R
 // consecutive segments (one run when n is small):
 //   1. run reduce:  each run's total, walking its segments in order;
-//   2. run scan:    exclusive Blelloch scan (up-sweep, root reset,
-//                   down-sweep) of the run totals, in place;
+//   2. run scan:    exclusive Blelloch scan of the run totals, in place: the
+//                   up-sweep below the root, the top level (root = identity),
+//                   then each down-sweep level in one launch that both moves
+//                   the parent prefix left and combines it with the left sum;
 //   3. run rescan:  each run walks its segments again from the run's
 //                   exclusive prefix and overwrites every segment with its
 //                   own exclusive prefix (rows of S, G, h);
@@ -64,11 +66,10 @@ __device__ __forceinline__ int slot_tokens(const ScanArgs& a, int lo, int hi) {
   return (s1 - s0) * a.chunk;
 }
 
-// x[j] <- x[i] (+) x[j] for every pair of one level; blockIdx.x = pair * (D/RB) + row block.
-// a = gamma^(tokens in x[j]'s subtree): the right subtree (up-sweep) or, after
-// the swap, the left subtree (down-sweep).
+// Up-sweep level: x[j] <- x[i] (+) x[j] for every pair; blockIdx.x = pair *
+// (D/RB) + row block; a = gamma^(tokens in x[j]'s subtree).
 template <int D, int E>
-__global__ __launch_bounds__(SCAN_THR) void scan_combine_kernel(ScanArgs a, int down) {
+__global__ __launch_bounds__(SCAN_THR) void scan_combine_kernel(ScanArgs a) {
   constexpr int LDC = E + 4, LDS_ = D + 4, ET = E / 16, NRB = D / SCAN_RB;
   __shared__ __attribute__((aligned(16))) float sC[D * LDC];
   __shared__ __attribute__((aligned(16))) float sS[SCAN_RB * LDS_];
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(SCAN_THR) void scan_combine_kernel(ScanArgs a, int 
   const int i = j - step;
   if (i - step + 1 >= a.n) return;   // both subtrees are padding: identity (+) identity
   const Slot A = slot_ptr(a, unit, i), B = slot_ptr(a, unit, j);
-  const int lenB = down ? slot_tokens(a, i - step + 1, i) : slot_tokens(a, j - step + 1, j);
+  const int lenB = slot_tokens(a, j - step + 1, j);
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float al = gpow(g, log2f(g), lenB);
   const float al2 = al * al;
@@ -129,55 +130,114 @@ __global__ __launch_bounds__(SCAN_THR) void scan_combine_kernel(ScanArgs a, int 
   for (int t = tid; t < SCAN_RB; t += SCAN_THR) B.m[r0 + t] = al * A.m[r0 + t] + B.m[r0 + t];
 }
 
-// Down-sweep first half: x[i] <-> x[j] for every pair of one level.
-// blockIdx.x = pair * parts + part; every element is swapped by one thread.
-__global__ __launch_bounds__(256) void scan_swap_kernel(ScanArgs a, int parts) {
-  const int unit = blockIdx.y;
-  const int pair = blockIdx.x / parts, part = blockIdx.x % parts;
-  const int j = (pair + 1) * 2 * a.step - 1;
-  const int i = j - a.step;
-  if (i - a.step + 1 >= a.n) return;
-  const Slot x = slot_ptr(a, unit, i), y = slot_ptr(a, unit, j);
-  const int d = a.d, dv = a.dv;
-  const int nS = d * d / 4, nC = d * dv / 4;
-  const int stride = parts * 256;
-  for (int t = part * 256 + threadIdx.x; t < nS + 2 * nC + d / 2; t += stride) {
-    f32x4* p;
-    f32x4* q;
+// Top of the tree: the up-sweep stops below the root, whose value (the total)
+// the exclusive scan never uses; the down-sweep's first level, with the root
+// reset to the identity, is then x[N-1] <- x[N/2-1], x[N/2-1] <- identity.
+// blockIdx.x = unit * parts + part; one f32x4 of (S | C | G | m | h) per thread.
+__global__ __launch_bounds__(256) void scan_top_kernel(ScanArgs a, int parts) {
+  const int unit = blockIdx.x / parts, part = blockIdx.x % parts;
+  const Slot x = slot_ptr(a, unit, a.N / 2 - 1), y = slot_ptr(a, unit, a.N - 1);
+  const int nS = a.d * a.d / 4, nC = a.d * a.dv / 4, nm = a.d / 4;
+  for (int t = part * 256 + threadIdx.x; t < nS + 2 * nC + 2 * nm; t += parts * 256) {
+    f32x4 *px, *py;
     int o;
-    if (t < nS) { p = reinterpret_cast<f32x4*>(x.S); q = reinterpret_cast<f32x4*>(y.S); o = t; }
-    else if (t < nS + nC) { p = reinterpret_cast<f32x4*>(x.C); q = reinterpret_cast<f32x4*>(y.C); o = t - nS; }
-    else if (t < nS + 2 * nC) { p = reinterpret_cast<f32x4*>(x.G); q = reinterpret_cast<f32x4*>(y.G); o = t - nS - nC; }
-    else if (t < nS + 2 * nC + d / 4) { p = reinterpret_cast<f32x4*>(x.m); q = reinterpret_cast<f32x4*>(y.m); o = t - nS - 2 * nC; }
-    else { p = reinterpret_cast<f32x4*>(x.h); q = reinterpret_cast<f32x4*>(y.h); o = t - nS - 2 * nC - d / 4; }
-    const f32x4 u = p[o], w = q[o];
-    p[o] = w;
-    q[o] = u;
+    if (t < nS) { px = reinterpret_cast<f32x4*>(x.S); py = reinterpret_cast<f32x4*>(y.S); o = t; }
+    else if (t < nS + nC) { px = reinterpret_cast<f32x4*>(x.C); py = reinterpret_cast<f32x4*>(y.C); o = t - nS; }
+    else if (t < nS + 2 * nC) { px = reinterpret_cast<f32x4*>(x.G); py = reinterpret_cast<f32x4*>(y.G); o = t - nS - nC; }
+    else if (t < nS + 2 * nC + nm) { px = reinterpret_cast<f32x4*>(x.m); py = reinterpret_cast<f32x4*>(y.m); o = t - nS - 2 * nC; }
+    else { px = reinterpret_cast<f32x4*>(x.h); py = reinterpret_cast<f32x4*>(y.h); o = t - nS - 2 * nC - nm; }
+    py[o] = px[o];
+    px[o] = zero4();
   }
 }
 
-// Root handling between the sweeps: optionally copy the inclusive total
-// (slot N-1) out, then reset the root to the identity.
-__global__ __launch_bounds__(256) void scan_root_kernel(ScanArgs a, float* tS, float* tC, float* tm,
-                                                        float* tG, float* th) {
-  const int unit = blockIdx.x;
-  const Slot r = slot_ptr(a, unit, a.N - 1);
-  const int d = a.d, dv = a.dv;
-  for (int t = threadIdx.x; t < d * d; t += blockDim.x) {
-    if (tS) tS[(size_t)unit * d * d + t] = r.S[t];
-    r.S[t] = 0.f;
+// One down-sweep level below the top, one workgroup (16 waves) per pair
+// (i, j = i + step): with A = x[j] (the parent's prefix) and B = x[i] (the left
+// subtree's sum), x[i] <- A and x[j] <- A (+) B, a = gamma^(tokens in the left
+// subtree).  C_A, m_A and all of S_B are staged in LDS before anything is
+// written; every other element is read and then written by the same thread,
+// so the pair needs no second launch for the swap.  Groups of 4 waves take the
+// 16-row blocks round robin
+// (two groups at d = 128, where the 128 registers of a 16-wave workgroup
+// would not hold the row block's GEMM)
+template <int D>
+struct DownThreads {
+  static constexpr int value = D == 128 ? 2 * SCAN_THR : 4 * SCAN_THR;
+};
+template <int D, int E>
+__global__ __launch_bounds__(DownThreads<D>::value) void scan_down_kernel(ScanArgs a) {
+  constexpr int DOWN_THR = DownThreads<D>::value, DOWN_GROUPS = DOWN_THR / SCAN_THR;
+  constexpr int LDC = E + 4, LDS_ = D + 4, ET = E / 16, NRB = D / SCAN_RB;
+  __shared__ __attribute__((aligned(16))) float sC[D * LDC];
+  __shared__ __attribute__((aligned(16))) float sS[D * LDS_];
+  __shared__ float sm[D];
+
+  const int unit = blockIdx.y;
+  const int step = a.step;
+  const int j = (blockIdx.x + 1) * 2 * step - 1;
+  const int i = j - step;
+  if (i - step + 1 >= a.n) return;   // the left subtree is padding: nothing reads these prefixes
+  const Slot X = slot_ptr(a, unit, i), Y = slot_ptr(a, unit, j);
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float al = gpow(g, log2f(g), slot_tokens(a, i - step + 1, i));
+  const float al2 = al * al;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid / SCAN_THR, gt = tid % SCAN_THR, gw = gt >> 6;
+
+  for (int t = tid; t < D * E / 4; t += DOWN_THR) {
+    const int r = (4 * t) / E, c = (4 * t) % E;
+    *reinterpret_cast<f32x4*>(sC + r * LDC + c) = reinterpret_cast<const f32x4*>(Y.C)[t];
   }
-  for (int t = threadIdx.x; t < d * dv; t += blockDim.x) {
-    if (tC) tC[(size_t)unit * d * dv + t] = r.C[t];
-    if (tG) tG[(size_t)unit * d * dv + t] = r.G[t];
-    r.C[t] = 0.f;
-    r.G[t] = 0.f;
+  for (int t = tid; t < D * D / 4; t += DOWN_THR) {
+    const int r = (4 * t) / D, c = (4 * t) % D;
+    *reinterpret_cast<f32x4*>(sS + r * LDS_ + c) = reinterpret_cast<const f32x4*>(X.S)[t];
   }
-  for (int t = threadIdx.x; t < d; t += blockDim.x) {
-    if (tm) tm[(size_t)unit * d + t] = r.m[t];
-    if (th) th[(size_t)unit * d + t] = r.h[t];
-    r.m[t] = 0.f;
-    r.h[t] = 0.f;
+  for (int t = tid; t < D; t += DOWN_THR) sm[t] = Y.m[t];
+  __syncthreads();
+
+  for (int rb = grp; rb < NRB; rb += DOWN_GROUPS) {
+    const int r0 = rb * SCAN_RB;
+    // G rows: a^2 G_A + G_B + a S_B C_A
+    for (int et = gw; et < ET; et += SCAN_WAVES) {
+      const f32x4 acc = gemm_f32_tile<D>(sS, LDS_, sC, LDC, r0, 16 * et, lane, zero4());
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t e = (size_t)(r0 + 4 * (lane >> 4) + q) * E + 16 * et + (lane & 15);
+        const float gA = Y.G[e], gB = X.G[e];
+        X.G[e] = gA;
+        Y.G[e] = al2 * gA + gB + al * acc[q];
+      }
+    }
+    // h rows: a^2 h_A + h_B + a S_B m_A
+    for (int r = gt; r < SCAN_RB; r += SCAN_THR) {
+      float acc = 0.f;
+      for (int c = 0; c < D; ++c) acc += sS[(r0 + r) * LDS_ + c] * sm[c];
+      const float hA = Y.h[r0 + r], hB = X.h[r0 + r];
+      X.h[r0 + r] = hA;
+      Y.h[r0 + r] = al2 * hA + hB + al * acc;
+    }
+    // S and C rows: a X_A + X_B (S_B and C_A from LDS)
+    for (int t = gt; t < SCAN_RB * D / 4; t += SCAN_THR) {
+      const int r = (4 * t) / D, c = (4 * t) % D;
+      const size_t e = (size_t)r0 * D / 4 + t;
+      const f32x4 sA = reinterpret_cast<const f32x4*>(Y.S)[e];
+      const f32x4 sB = *reinterpret_cast<const f32x4*>(sS + (r0 + r) * LDS_ + c);
+      reinterpret_cast<f32x4*>(X.S)[e] = sA;
+      reinterpret_cast<f32x4*>(Y.S)[e] = sA * al + sB;
+    }
+    for (int t = gt; t < SCAN_RB * E / 4; t += SCAN_THR) {
+      const int r = (4 * t) / E, c = (4 * t) % E;
+      const size_t e = (size_t)r0 * E / 4 + t;
+      const f32x4 cA = *reinterpret_cast<const f32x4*>(sC + (r0 + r) * LDC + c);
+      const f32x4 cB = reinterpret_cast<const f32x4*>(X.C)[e];
+      reinterpret_cast<f32x4*>(X.C)[e] = cA;
+      reinterpret_cast<f32x4*>(Y.C)[e] = cA * al + cB;
+    }
+  }
+  for (int t = tid; t < D; t += DOWN_THR) {
+    const float mA = sm[t], mB = X.m[t];
+    X.m[t] = mA;
+    Y.m[t] = al * mA + mB;
   }
 }
 
@@ -469,7 +529,6 @@ template <int D, int E>
 static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   constexpr int NRB = D / 16, VEC = (D * D + 2 * D * E + 2 * D) / 4;
   constexpr int NRR = D / (16 * RunRT<D>::value);   // row blocks of the run kernels
-  constexpr int PARTS = VEC / 1024 > 0 ? VEC / 1024 : 1;   // swap workgroups per pair
   const int units = p.units;
   RunArgs r;
   r.S = p.S; r.C = p.C; r.m = p.m; r.G = p.G; r.h = p.h;
@@ -506,22 +565,20 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
       hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.wS, count);
       if (hipError_t e = hipGetLastError()) return e;
     }
-    for (int step = 1; step < a.N; step *= 2) {
+    // up-sweep below the root, the top level, then the down-sweep
+    for (int step = 1; step < a.N / 2; step *= 2) {
       a.step = step;
       hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
-                         dim3(SCAN_THR), 0, s, a, 0);
+                         dim3(SCAN_THR), 0, s, a);
       if (hipError_t e = hipGetLastError()) return e;
     }
-    hipLaunchKernelGGL(scan_root_kernel, dim3(units), dim3(256), 0, s, a, nullptr, nullptr,
-                       nullptr, nullptr, nullptr);
+    constexpr int TOP_PARTS = (VEC + 1023) / 1024;
+    hipLaunchKernelGGL(scan_top_kernel, dim3(units * TOP_PARTS), dim3(256), 0, s, a, TOP_PARTS);
     if (hipError_t e = hipGetLastError()) return e;
-    for (int step = a.N / 2; step >= 1; step /= 2) {
+    for (int step = a.N / 4; step >= 1; step /= 2) {
       a.step = step;
-      hipLaunchKernelGGL(scan_swap_kernel, dim3(a.N / (2 * step) * PARTS, units), dim3(256), 0, s,
-                         a, PARTS);
-      if (hipError_t e = hipGetLastError()) return e;
-      hipLaunchKernelGGL((scan_combine_kernel<D, E>), dim3(a.N / (2 * step) * NRB, units),
-                         dim3(SCAN_THR), 0, s, a, 1);
+      hipLaunchKernelGGL((scan_down_kernel<D, E>), dim3(a.N / (2 * step), units),
+                         dim3(DownThreads<D>::value), 0, s, a);
       if (hipError_t e = hipGetLastError()) return e;
     }
   }
