@@ -58,17 +58,23 @@ struct ChunkLayout {
   // Q S and Q M take the state in the natural K order (lane swaps, bf16 with
   // 8 waves) or read Q in the state's K order (otherwise; fewer registers)
   static constexpr bool NAT = sizeof(T) == 2 && (D == 128 || E == 128);
+  // 8-wave kernels (a head dimension of 128, one workgroup per CU) pipeline
+  // the score tiles: the next tile's Q (and K in the summary kernel) is staged
+  // while the current one is in use, so Q (and K) are double-buffered
+  static constexpr bool PIPE = D == 128 || E == 128;
+  static constexpr int NQB = PIPE ? 2 : 1, NKB = (PIPE && MODE == 0) ? 2 : 1;
   // Qs, Ks: [tok][d].  With NAT, rows are padded by 32 bytes, which makes the
   // row-major fragment reads free of LDS bank conflicts; the permuted reads
   // prefer 16 (measured)
   static constexpr int LDD = DP + (NAT ? 2 * PADT : PADT);
   static constexpr int LDV = E + PADT;       // Vs: [tok][e]
   static constexpr int LDT = TT + PADT;      // PsT: [d][tok], AB: [tok][tok]
+  static constexpr size_t QB = (size_t)TT * LDD * sizeof(T);   // one Q or K buffer
   static constexpr size_t Qs = 0;
-  static constexpr size_t Ks = Qs + (size_t)TT * LDD * sizeof(T);
+  static constexpr size_t Ks = Qs + NQB * QB;
   // V and P^T are double-buffered by tile parity: the M update of a tile runs
   // while the next tile is staged and its P produced
-  static constexpr size_t Vs0 = Ks + (size_t)TT * LDD * sizeof(T);
+  static constexpr size_t Vs0 = Ks + NKB * QB;
   static constexpr size_t Vs1 = Vs0 + (size_t)TT * LDV * sizeof(T);
   static constexpr size_t PsT0 = Vs1 + (size_t)TT * LDV * sizeof(T);
   static constexpr size_t PsT1 = PsT0 + (size_t)DP * LDT * sizeof(T);
@@ -136,6 +142,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
   T* Ks = reinterpret_cast<T*>(smem + L::Ks);
+  // Q and K buffers of tile parity p (one buffer each unless pipelined)
+  auto Qb = [&](int p) { return reinterpret_cast<T*>(smem + L::Qs + (L::NQB == 2 && p ? L::QB : 0)); };
+  auto Kb = [&](int p) { return reinterpret_cast<T*>(smem + L::Ks + (L::NKB == 2 && p ? L::QB : 0)); };
   // buffers of tile parity p
   auto Vsb = [&](int p) { return reinterpret_cast<T*>(smem + (p ? L::Vs1 : L::Vs0)); };
   auto PsTb = [&](int p) { return reinterpret_cast<T*>(smem + (p ? L::PsT1 : L::PsT0)); };
@@ -157,9 +166,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg4 = lane >> 4;
-  // Q times a register-resident state (Q S, Q M), the state tiles being the B
-  // operand: in the natural K order (lane swaps) with Q a plain row-major
-  // read, or in the accumulator's K order with Q read to match
+  // Q times a register-resident state (Q S, and Q M as (Q M)^T = M^T Q^T), the
+  // state tiles being the B operand (the A operand for M^T: the two operand
+  // layouts are alike): in the natural K order (lane swaps) with Q a plain
+  // row-major read, or in the accumulator's K order with Q read to match
   auto state_b = [&](const auto& tiles, int kk) {
     if constexpr (L::NAT) return FR::acc_b_nat(tiles, kk);
     else return FR::acc_b(tiles, kk);
@@ -178,6 +188,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   const T* gq = reinterpret_cast<const T*>(a.q) + tok0 * D;
   const T* gk = reinterpret_cast<const T*>(a.k) + tok0 * D;
   const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
+  // the segment's rows as raw buffers: rows at or past the segment end read as zeros
+  const auto rq = buf_rsrc(gq, Lspan * D * (int)sizeof(T));
+  const auto rk = buf_rsrc(gk, Lspan * D * (int)sizeof(T));
+  const auto rv = buf_rsrc(gv, Lspan * E * (int)sizeof(T));
   const size_t sidx = (size_t)unit * nspan + span;
   const bool need_n = SUM || a.normalize || a.den != nullptr;
   const bool sRole = wave < NOWN;
@@ -286,33 +300,42 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
     constexpr int n = (c1 - c0 + np - 1) / np;
     const int t0 = ti * TT;
-    const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+    // when every slot i (chunks c0 + np i + [0, np)) lies inside one of Q, K, V,
+    // the buffer is known per slot at compile time; otherwise plain loads with
+    // a row test (a per-lane choice of buffer would need a waterfall loop)
+    constexpr bool SLOT = c0 % np == 0 && QCH % np == 0 && (c1 - c0) % np == 0;
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      const int c = c0 + lt + np * i;
+      const int cb = c0 + np * i, c = cb + lt;
       x[i] = make_uint4(0, 0, 0, 0);
-      if (c < c1) {
+      if constexpr (SLOT) {
+        if (cb < QCH) x[i] = buf_load16(rq, (t0 * D + c * CH) * (int)sizeof(T));
+        else if (cb < 2 * QCH) x[i] = buf_load16(rk, (t0 * D + (c - QCH) * CH) * (int)sizeof(T));
+        else x[i] = buf_load16(rv, (t0 * E + (c - 2 * QCH) * CH) * (int)sizeof(T));
+      } else if (c < c1) {
+        const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
         const T* src;
         int cl, W;
         if (c < QCH) { src = gq; cl = c; W = D; }
         else if (c < 2 * QCH) { src = gk; cl = c - QCH; W = D; }
         else { src = gv; cl = c - 2 * QCH; W = E; }
-        const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
-        if (row < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
+        if (cl / (W / CH) < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)t0 * W + cl * CH);
       }
     }
   };
-  auto store_part = [&](const auto& x, int lt, T* Vs, auto C0, auto C1, auto P) {
+  auto store_part = [&](const auto& x, int lt, T* Qd, T* Kd, T* Vs, auto C0, auto C1, auto P) {
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
     constexpr int n = (c1 - c0 + np - 1) / np;
+    constexpr bool SLOT = c0 % np == 0 && QCH % np == 0 && (c1 - c0) % np == 0;
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      const int c = c0 + lt + np * i;
-      if (c < c1) {
+      const int cb = c0 + np * i, c = cb + lt;
+      if (SLOT || c < c1) {
         T* dst;
         int cl, W, LD;
-        if (c < QCH) { dst = Qs; cl = c; W = D; LD = L::LDD; }
-        else if (c < 2 * QCH) { dst = Ks; cl = c - QCH; W = D; LD = L::LDD; }
+        const int cs = SLOT ? cb : c;   // decides the buffer
+        if (cs < QCH) { dst = Qd; cl = c; W = D; LD = L::LDD; }
+        else if (cs < 2 * QCH) { dst = Kd; cl = c - QCH; W = D; LD = L::LDD; }
         else { dst = Vs; cl = c - 2 * QCH; W = E; LD = L::LDV; }
         const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
         *reinterpret_cast<uint4*>(dst + row * LD + col) = x[i];
@@ -325,8 +348,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     else load_part(x, ti, tid - HT, VB{}, END{}, HALF{});
   };
   auto store_role = [&](const auto& x, T* Vs, auto s_wave) {
-    if constexpr (decltype(s_wave)::value) store_part(x, tid, Vs, QK{}, VB{}, HALF{});
-    else store_part(x, tid - HT, Vs, VB{}, END{}, HALF{});
+    if constexpr (decltype(s_wave)::value) store_part(x, tid, Qs, Ks, Vs, QK{}, VB{}, HALF{});
+    else store_part(x, tid - HT, Qs, Ks, Vs, VB{}, END{}, HALF{});
   };
 
   // steps 0 and 1 of tile ti: stage the tile and its weights, then
@@ -339,7 +362,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     } else {
       uint4 xt[NXA];
       load_part(xt, ti, tid, QK{}, END{}, ALL{});
-      store_part(xt, tid, Vsb(ti & 1), QK{}, END{}, ALL{});
+      store_part(xt, tid, Qs, Ks, Vsb(ti & 1), QK{}, END{}, ALL{});
     }
     // wS for this tile; wM[ti & 1] was last written for tile ti - 2
     if ((ti < 2 || Lt != Lt_prev) && tid < TT) {
@@ -387,16 +410,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   // HT / D lanes per column
   // (thread: 4 adjacent columns, every TPN-th token; the TPN partial sums of
   // a column group sit in adjacent lanes)
-  auto m_vec_update = [&](int Lt, float gL) {
+  auto m_vec_update = [&](const T* Qx, int Lt, float gL) {
     constexpr int NCG = D / 4, TPN = HT / NCG;
     static_assert(TPN >= 1 && TPN <= 64 && (TPN & (TPN - 1)) == 0, "m update lanes");
     const int mt = tid - HT, cg = mt / TPN, tp = mt % TPN;
     f32x4 acc = zero4();
-    for (int t = tp; t < Lt; t += TPN) {
-      const T* qp = Qs + t * L::LDD + 4 * cg;
+    auto add_row = [&](int t) {
+      const T* qp = Qx + t * L::LDD + 4 * cg;
       const float wt = wS[t];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += wt * (float)qp[i];
+    };
+    if (Lt == TT) {
+#pragma unroll
+      for (int t = tp; t < TT; t += TPN) add_row(t);   // all row reads issued together
+    } else {
+      for (int t = tp; t < Lt; t += TPN) add_row(t);
     }
 #pragma unroll
     for (int off = 1; off < TPN; off *= 2)
@@ -446,6 +475,108 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     }
   };
 
+  // ---- pieces of the pipelined (8-wave) kernels ----
+  // decay weights of tile t (wS, and wM by parity), by the threads tid < TT;
+  // only the last tile can be short, so tiles 2 .. ntiles-2 reuse earlier values
+  auto weights = [&](int t) {
+    const int Lt = (Lspan - t * TT) < TT ? (Lspan - t * TT) : TT;
+    if ((t < 2 || t == ntiles - 1) && tid < TT) {
+      wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+      wMb(t & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
+    }
+  };
+  // A' score tile idx (rows 16 r + lr of the later position, masked and
+  // decayed) of the tile in buffers p, left in registers
+  auto a_tile = [&](int idx, int p) {
+    int r, c;
+    tri_tile(idx, r, c);
+    const T* Qx = Qb(p);
+    const T* Kx = Kb(p);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < DP; k0 += KS)
+      acc = MMT::mma(MMT::ld(Kx, L::LDD, 16 * c, k0, lane), MMT::ld(Qx, L::LDD, 16 * r, k0, lane), acc);
+    const int tau = 16 * r + lr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 16 * c + 4 * lg4 + j;
+      acc[j] = (i <= tau) ? acc[j] * pw[tau - i] : 0.f;
+    }
+    return acc;
+  };
+  auto a_store = [&](int idx, f32x4 val) {
+    int r, c;
+    tri_tile(idx, r, c);
+    store4<T>(AB + (16 * r + lr) * L::LDT + 16 * c + 4 * lg4, val);
+  };
+  // B^T score tile idx of the tile whose P^T and Q sit in buffers p, to BB
+  // (and its column sums to bpart)
+  auto b_tile = [&](int idx, int p) {
+    int r, c;
+    tri_tile(idx, r, c);
+    const T* PsT = PsTb(p);
+    const T* Qx = Qb(p);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < DP; k0 += KS)
+      acc = MMT::mma(FR::tr(PsT, L::LDT, k0, 16 * c, lane), MMT::ld(Qx, L::LDD, 16 * r, k0, lane), acc);
+    const int tau = 16 * r + lr;
+    f32x4 val;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int jj = 16 * c + 4 * lg4 + j;
+      val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
+    }
+    store4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
+    if (need_n) {
+      const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+      if (lg4 == 0) bpart[c * TT + tau] = rs;
+    }
+  };
+  // q.n of the tile in buffers p (n as it stands), for its denominator
+  auto q_dot_n = [&](int p) {
+    constexpr int LPR = NTHR / TT;
+    const T* Qx = Qb(p);
+    const int tau = tid / LPR, part = tid % LPR;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = part * (D / LPR); c < (part + 1) * (D / LPR); ++c) acc += (float)Qx[tau * L::LDD + c] * nst[c];
+#pragma unroll
+    for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
+    if (part == 0) qnb(p)[tau] = acc;
+  };
+  // tile 0 (and the summary kernel's tile 1 Q, K) to LDS, then A' of tile 0
+  auto prologue = [&]() {
+    {
+      uint4 xt[NXA];
+      load_part(xt, 0, tid, QK{}, END{}, ALL{});
+      store_part(xt, tid, Qb(0), Kb(0), Vsb(0), QK{}, END{}, ALL{});
+    }
+    if (SUM && ntiles > 1) {
+      constexpr int NXQ = (2 * QCH + NTHR - 1) / NTHR;
+      uint4 xt[NXQ];
+      load_part(xt, 1, tid, QK{}, VB{}, ALL{});
+      store_part(xt, tid, Qb(1), Kb(1), nullptr, QK{}, VB{}, ALL{});
+    }
+    weights(0);
+    __syncthreads();
+    for (int idx = wave; idx < NTRI; idx += NW) a_store(idx, a_tile(idx, 0));
+    if (!SUM && need_n) q_dot_n(0);
+    __syncthreads();
+  };
+  // output kernel, after tile ti's P^T is complete and tile ti + 1 is staged:
+  // B scores of ti and A' of ti + 1 (2 NTRI tiles over the waves), q.n of ti + 1
+  auto score_phase = [&](int ti) {
+    const bool nxt = ti + 1 < ntiles;
+#pragma unroll
+    for (int sl = 0; sl < (2 * NTRI + NW - 1) / NW; ++sl) {
+      const int idx = wave + NW * sl;
+      if (idx < NTRI) b_tile(idx, ti & 1);
+      else if (nxt && idx < 2 * NTRI) a_store(idx - NTRI, a_tile(idx - NTRI, (ti + 1) & 1));
+    }
+    if (need_n && nxt) q_dot_n((ti + 1) & 1);
+  };
+
   if (sRole) {
     // ======== S waves: P = g^(tau+1) Q S_prev + A' K, P^T to LDS, S update;
     //          B^T = (P Q^T) o decay in the output kernel ========
@@ -459,18 +590,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         for (int j = 0; j < 4; ++j)
           St[b][t][j] = (!SUM && (SFULL || cb < DT)) ? FS[(16 * t + 4 * lg4 + j) * L::LFS + 16 * cb + lr] : 0.f;
     }
-    uint4 xq[PF ? NXS : 1];
-    if constexpr (PF) load_role(xq, 0, std::true_type{});
-    finish_init();
-
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const int t0 = ti * TT;
-      const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
-      const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
-      tile_head(ti, Lt, xq, std::true_type{});
+    // step 2 of tile ti (tile in Qx, Kx; A' in AB): P, P^T to LDS, n and S updates
+    auto s_step2 = [&](int ti, float gL, float g2L, const T* Qx, const T* Kx) {
       T* PsT = PsTb(ti & 1);
-
-      // ---- step 2 ----
       f32x4 pacc[SB][TR];
 #pragma unroll
       for (int b = 0; b < SB; ++b)
@@ -483,7 +605,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         for (int b = 0; b < SB; ++b) bs[b] = state_b(St[b], kk);
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
-          const F aq = state_a(Qs, 16 * r, kk);
+          const F aq = state_a(Qx, 16 * r, kk);
 #pragma unroll
           for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
         }
@@ -501,7 +623,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
 #pragma unroll
           for (int b = 0; b < SB; ++b)
             if (SFULL || rw + NOWN * b < DT)
-              pacc[b][r] = MMT::mma(aa, FR::tr(Ks, L::LDD, k0, 16 * (rw + NOWN * b), lane), pacc[b][r]);
+              pacc[b][r] = MMT::mma(aa, FR::tr(Kx, L::LDD, k0, 16 * (rw + NOWN * b), lane), pacc[b][r]);
         }
         const f32x4 wm = *reinterpret_cast<const f32x4*>(wMb(ti & 1) + 16 * r + 4 * lg4);
 #pragma unroll
@@ -531,7 +653,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         for (int b = 0; b < SB; ++b)
 #pragma unroll
           for (int kk = 0; kk < NKS; ++kk)
-            bk[b][kk] = FR::scale(FR::tr(Ks, L::LDD, kk * KS, 16 * ((rw + NOWN * b) % DT), lane), wS, kk * KS, lane);
+            bk[b][kk] = FR::scale(FR::tr(Kx, L::LDD, kk * KS, 16 * ((rw + NOWN * b) % DT), lane), wS, kk * KS, lane);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
           f32x4 acc[SB];
@@ -539,7 +661,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           for (int b = 0; b < SB; ++b) acc[b] = St[b][t] * gL;
 #pragma unroll
           for (int kk = 0; kk < NKS; ++kk) {
-            const F ak = FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane);
+            const F ak = FR::tr(Kx, L::LDD, kk * KS, 16 * t, lane);
 #pragma unroll
             for (int b = 0; b < SB; ++b) acc[b] = MMT::mma(ak, bk[b][kk], acc[b]);
           }
@@ -548,16 +670,67 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
             if (SFULL || rw + NOWN * b < DT) St[b][t] = acc[b];
         }
       }
-      __syncthreads();
-
-      // ---- step 3 (output kernel): B^T scores, shared with the M waves ----
-      if (!SUM) {
-        b_scores(ti);
+    };
+    uint4 xq[PF ? NXS : 1];
+    if constexpr (L::PIPE) {
+      finish_init();
+      prologue();
+      // the S waves carry Q and K two tiles ahead (summary) or one (output)
+      constexpr int AHEAD = SUM ? 2 : 1;
+      if (AHEAD < ntiles) load_part(xq, AHEAD, tid, QK{}, VB{}, HALF{});
+      for (int ti = 0; ti < ntiles; ++ti) {
+        const int t0 = ti * TT;
+        const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+        s_step2(ti, gpow(g, lgg, Lt), gpow(g, lgg, 2 * Lt), Qb(ti & 1), Kb(ti & 1));
+        // summary: A' of the next tile (staged a tile ago), kept in registers
+        // until the S waves of this tile have all read AB
+        constexpr int NAS = SUM ? (NTRI + NOWN - 1) / NOWN : 1;
+        f32x4 an[NAS];
+        if constexpr (SUM) {
+          if (ti + 1 < ntiles) {
+#pragma unroll
+            for (int sl = 0; sl < NAS; ++sl)
+              if (rw + NOWN * sl < NTRI) an[sl] = a_tile(rw + NOWN * sl, (ti + 1) & 1);
+          }
+        }
         __syncthreads();
-        if constexpr (!DEFER) __syncthreads();   // step 4: the M waves write the outputs
+        // stage Q, K of tile ti + AHEAD (their buffers were last read in this step 2
+        // or, in the output kernel, by the B scores of tile ti - 1)
+        if (ti + AHEAD < ntiles)
+          store_part(xq, tid, Qb((ti + AHEAD) & 1), Kb((ti + AHEAD) & 1), nullptr, QK{}, VB{}, HALF{});
+        if constexpr (SUM) {
+          if (ti + 1 < ntiles) {
+#pragma unroll
+            for (int sl = 0; sl < NAS; ++sl)
+              if (rw + NOWN * sl < NTRI) a_store(rw + NOWN * sl, an[sl]);
+          }
+        }
+        if (ti + 1 < ntiles) weights(ti + 1);
+        __syncthreads();
+        if constexpr (!SUM) score_phase(ti);
+        if (ti + AHEAD + 1 < ntiles) load_part(xq, ti + AHEAD + 1, tid, QK{}, VB{}, HALF{});
+        if constexpr (!SUM) __syncthreads();
+      }
+    } else {
+      if constexpr (PF) load_role(xq, 0, std::true_type{});
+      finish_init();
+
+      for (int ti = 0; ti < ntiles; ++ti) {
+        const int t0 = ti * TT;
+        const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+        const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+        tile_head(ti, Lt, xq, std::true_type{});
+        s_step2(ti, gL, g2L, Qs, Ks);
+        __syncthreads();
+
+        // ---- step 3 (output kernel): B^T scores, shared with the M waves ----
+        if (!SUM) {
+          b_scores(ti);
+          __syncthreads();
+          if constexpr (!DEFER) __syncthreads();   // step 4: the M waves write the outputs
+        }
       }
     }
-
     if (SUM) {
       __syncthreads();   // the M waves' last M update has read P^T and V
       // S to LDS (fp32, the tile region is free now) as the A operand of S C
@@ -624,8 +797,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       }
     }
     uint4 xv[PF ? NXM : 1];
-    if constexpr (PF) load_role(xv, 0, std::false_type{});
-    finish_init();
 
     // M[:, blocks] <- g^2L M + P^T diag(wM) V[:, blocks] for tile tp (its P^T, V
     // and wM are in the buffers of tp's parity); the P^T fragments are shared
@@ -633,66 +804,68 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       const T* PsT = PsTb(tp & 1);
       const T* Vs = Vsb(tp & 1);
       const float* wM = wMb(tp & 1);
-        F bv[MB][NKS];
+      F bv[MB][NKS];
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk)
+          bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wM, kk * KS, lane);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        f32x4 acc[MB];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[b] = St[b][t] * g2Lp;
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) {
+          const F ap = MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane);
+#pragma unroll
+          for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(ap, bv[b][kk], acc[b]);
+        }
 #pragma unroll
         for (int b = 0; b < MB; ++b)
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk)
-            bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wM, kk * KS, lane);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 acc[MB];
-#pragma unroll
-          for (int b = 0; b < MB; ++b) acc[b] = St[b][t] * g2Lp;
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) {
-            const F ap = MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane);
-#pragma unroll
-            for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(ap, bv[b][kk], acc[b]);
-          }
-#pragma unroll
-          for (int b = 0; b < MB; ++b)
-            if (MFULL || rw + NOWN * b < ET) St[b][t] = acc[b];
-        }
+          if (MFULL || rw + NOWN * b < ET) St[b][t] = acc[b];
+      }
     };
 
-    // output kernel: oacc holds g^(2(tau+1)) Q M_prev of a tile until its B V
+    // output kernel: oacc holds g^(2(tau+1)) (Q M_prev)^T of a tile until its B V
     // is added one tile later (B scores in BB, V and q.n in the tile's parity
-    // buffers); then the tile is normalised and written with its denominator
+    // buffers); then the tile is normalised and written with its denominator.
+    // The outputs are accumulated transposed (O^T: the state or V^T is the A
+    // operand), so that a lane holds four adjacent output columns of one token
+    // and writes them with one 16-byte store.
     f32x4 oacc[SUM ? 1 : MB][TR];
     auto finish_out = [&](int tp, int Ltp) {
       const T* Vs = Vsb(tp & 1);
       const float* qnp = qnb(tp & 1);
       float* go = a.o + (tok0 + (size_t)tp * TT) * E;
-      // each store address = a wave-uniform row/column base + one per-lane offset
-      const int olane = 4 * lg4 * E + lr;
+      F vf[MB][NKS];
 #pragma unroll
-      for (int r = 0; r < TR; ++r) {
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) vf[b][kk] = FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane);
+#pragma unroll
+      for (int r = 0; r < TR; ++r)
+#pragma unroll
         for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
-          const F ab = MMT::ld(BB, L::LDT, 16 * r, k0, lane);
+          const F bb = MMT::ld(BB, L::LDT, 16 * r, k0, lane);
 #pragma unroll
           for (int b = 0; b < MB; ++b)
-            if (MFULL || rw + NOWN * b < ET)
-              oacc[b][r] = MMT::mma(ab, FR::tr(Vs, L::LDV, k0, 16 * (rw + NOWN * b), lane), oacc[b][r]);
+            if (MFULL || rw + NOWN * b < ET) oacc[b][r] = MMT::mma(vf[b][k0 / KS], bb, oacc[b][r]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tau = 16 * r + 4 * lg4 + j;
-          float scale = 1.f;
-          if (a.normalize) {
-            float dn = 0.f;
-            for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
-            scale = 1.f / (dn + w2[tau] * qnp[tau] + a.eps);
-          }
+      for (int r = 0; r < TR; ++r) {
+        const int tau = 16 * r + lr;
+        float scale = 1.f;
+        if (a.normalize) {
+          float dn = 0.f;
+          for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
+          scale = 1.f / (dn + w2[tau] * qnp[tau] + a.eps);
+        }
 #pragma unroll
-          for (int b = 0; b < MB; ++b) {
-            const int cb = rw + NOWN * b;
-            if ((MFULL || cb < ET) && tau < Ltp) {
-              const float val = a.normalize ? oacc[b][r][j] * scale : oacc[b][r][j];
-              float* rowp = go + ((16 * r + j) * E + 16 * cb);
-              rowp[olane] = val;
-            }
-          }
+        for (int b = 0; b < MB; ++b) {
+          const int cb = rw + NOWN * b;
+          if ((MFULL || cb < ET) && tau < Ltp)
+            *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * cb + 4 * lg4) = oacc[b][r] * scale;
         }
       }
       const int mt = tid - HT;
@@ -703,85 +876,125 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       }
     };
 
-    float g2L_prev = 1.f;
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const int t0 = ti * TT;
-      const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
-      const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
-      tile_head(ti, Lt, xv, std::false_type{});
-      T* Vs = Vsb(ti & 1);
-
-      // ---- step 2: the previous tile's outputs (output kernel) and M update,
-      //      then Q M (output) or the C update (summary) ----
-      if constexpr (DEFER) {
-        if (ti > 0) finish_out(ti - 1, TT);   // only the last tile can be short
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (ti > 0) m_update(ti - 1, g2L_prev);
-      __builtin_amdgcn_sched_barrier(0);   // keep the two updates' operand loads apart
-      if constexpr (!SUM) {
+    // (Q M_prev)^T of the tile in Qx, scaled by g^(2(tau+1)), into oacc (output kernel)
+    auto qm = [&](const T* Qx) {
 #pragma unroll
-        for (int b = 0; b < MB; ++b)
+      for (int b = 0; b < MB; ++b)
 #pragma unroll
-          for (int r = 0; r < TR; ++r) oacc[b][r] = zero4();
+        for (int r = 0; r < TR; ++r) oacc[b][r] = zero4();
 #pragma unroll
-        for (int kk = 0; kk < QSK; ++kk) {
-          F bm[MB];
+      for (int kk = 0; kk < QSK; ++kk) {
+        F bm[MB];
 #pragma unroll
-          for (int b = 0; b < MB; ++b) bm[b] = state_b(St[b], kk);
-#pragma unroll
-          for (int r = 0; r < TR; ++r) {
-            const F aq = state_a(Qs, 16 * r, kk);
-#pragma unroll
-            for (int b = 0; b < MB; ++b) oacc[b][r] = MMT::mma(aq, bm[b], oacc[b][r]);
-          }
-        }
+        for (int b = 0; b < MB; ++b) bm[b] = state_b(St[b], kk);
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
-          const f32x4 w2v = *reinterpret_cast<const f32x4*>(w2 + 16 * r + 4 * lg4);
+          const F aq = state_a(Qx, 16 * r, kk);
 #pragma unroll
-          for (int b = 0; b < MB; ++b) oacc[b][r] *= w2v;
+          for (int b = 0; b < MB; ++b) oacc[b][r] = MMT::mma(bm[b], aq, oacc[b][r]);
         }
-      } else {
-        // C[:, blocks] <- g^Lt C + Q^T diag(wS) V[:, blocks]; the Q^T fragments are shared
-        F bv[MB][NKS];
+      }
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const float w2t = w2[16 * r + lr];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) oacc[b][r] *= w2t;
+      }
+    };
+    // C[:, blocks] <- g^Lt C + Q^T diag(wS) V[:, blocks] (summary); the Q^T fragments are shared
+    auto c_update = [&](const T* Qx, const T* Vs, float gL) {
+      F bv[MB][NKS];
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk)
+          bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wS, kk * KS, lane);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        f32x4 acc[MB];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[b] = Ct[b][t] * gL;
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) {
+          const F aq = FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane);
+#pragma unroll
+          for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(aq, bv[b][kk], acc[b]);
+        }
 #pragma unroll
         for (int b = 0; b < MB; ++b)
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk)
-            bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wS, kk * KS, lane);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 acc[MB];
-#pragma unroll
-          for (int b = 0; b < MB; ++b) acc[b] = Ct[b][t] * gL;
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) {
-            const F aq = FR::tr(Qs, L::LDD, kk * KS, 16 * t, lane);
-#pragma unroll
-            for (int b = 0; b < MB; ++b) acc[b] = MMT::mma(aq, bv[b][kk], acc[b]);
-          }
-#pragma unroll
-          for (int b = 0; b < MB; ++b)
-            if (MFULL || rw + NOWN * b < ET) Ct[b][t] = acc[b];
+          if (MFULL || rw + NOWN * b < ET) Ct[b][t] = acc[b];
+      }
+    };
+
+    float g2L_prev = 1.f;
+    if constexpr (L::PIPE) {
+      finish_init();
+      prologue();
+      if (1 < ntiles) load_part(xv, 1, tid - HT, VB{}, END{}, HALF{});
+      for (int ti = 0; ti < ntiles; ++ti) {
+        const int t0 = ti * TT;
+        const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+        const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+        // summary: the previous tile's M update, the C update and m of this
+        // tile; output: the previous tile's outputs, the M update, then
+        // (Q M)^T of this tile
+        if constexpr (SUM) {
+          if (ti > 0) m_update(ti - 1, g2L_prev);
+          __builtin_amdgcn_sched_barrier(0);
+          c_update(Qb(ti & 1), Vsb(ti & 1), gL);
+          m_vec_update(Qb(ti & 1), Lt, gL);
+        } else {
+          if (ti > 0) finish_out(ti - 1, TT);   // only the last tile can be short
+          __builtin_amdgcn_sched_barrier(0);
+          if (ti > 0) m_update(ti - 1, g2L_prev);
+          __builtin_amdgcn_sched_barrier(0);
+          qm(Qb(ti & 1));
+        }
+        g2L_prev = g2L;
+        __syncthreads();
+        // V of tile ti + 1 to the buffer last read by this step's updates of tile ti - 1
+        if (ti + 1 < ntiles) store_part(xv, tid - HT, nullptr, nullptr, Vsb((ti + 1) & 1), VB{}, END{}, HALF{});
+        __syncthreads();
+        if constexpr (!SUM) score_phase(ti);
+        if (ti + 2 < ntiles) load_part(xv, ti + 2, tid - HT, VB{}, END{}, HALF{});
+        if constexpr (!SUM) __syncthreads();
+      }
+      if constexpr (!SUM) finish_out(ntiles - 1, (Lspan - (ntiles - 1) * TT));
+    } else {
+      if constexpr (PF) load_role(xv, 0, std::false_type{});
+      finish_init();
+      for (int ti = 0; ti < ntiles; ++ti) {
+        const int t0 = ti * TT;
+        const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
+        const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+        tile_head(ti, Lt, xv, std::false_type{});
+
+        // ---- step 2: the previous tile's outputs (output kernel) and M update,
+        //      then Q M (output) or the C update (summary) ----
+        if constexpr (DEFER) {
+          if (ti > 0) finish_out(ti - 1, TT);   // only the last tile can be short
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ti > 0) m_update(ti - 1, g2L_prev);
+        __builtin_amdgcn_sched_barrier(0);   // keep the two updates' operand loads apart
+        if constexpr (!SUM) qm(Qs);
+        else c_update(Qs, Vsb(ti & 1), gL);
+        if constexpr (SUM) m_vec_update(Qs, Lt, gL);
+        g2L_prev = g2L;
+        __syncthreads();
+
+        // ---- step 3: B scores (with the S waves); step 4 without DEFER ----
+        if constexpr (!SUM) {
+          if constexpr (DEFER) b_scores(ti);
+          __syncthreads();
+        }
+        if constexpr (!SUM && !DEFER) {
+          finish_out(ti, Lt);
+          __syncthreads();
         }
       }
-      if constexpr (SUM) m_vec_update(Lt, gL);
-      g2L_prev = g2L;
-      __syncthreads();
-
-      // ---- step 3: B scores (with the S waves); step 4 without DEFER ----
-      if constexpr (!SUM) {
-        if constexpr (DEFER) b_scores(ti);
-        __syncthreads();
-      }
-      if constexpr (!SUM && !DEFER) {
-        finish_out(ti, Lt);
-        __syncthreads();
-      }
+      if constexpr (DEFER) finish_out(ntiles - 1, (Lspan - (ntiles - 1) * TT));
     }
-
-    if constexpr (DEFER) finish_out(ntiles - 1, (Lspan - (ntiles - 1) * TT));
     if (SUM) {
       m_update(ntiles - 1, g2L_prev);
       __syncthreads();

@@ -25,6 +25,17 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Raw buffer over nbytes bytes at p (word 3 = 0x00020000, the CDNA data
+// format): a load whose byte offset is nbytes or more returns zeros, so a
+// ragged last tile needs no row test.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <typename T> struct MM;
 
 template <> struct MM<__bf16> {
