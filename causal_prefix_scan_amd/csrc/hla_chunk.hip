@@ -296,16 +296,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   using HALF = std::integral_constant<int, HT>;
   using ALL = std::integral_constant<int, NTHR>;
   // chunks [C0, C1) of tile ti by P threads, lt = this thread's index among them
-  auto load_part = [&](auto& x, int ti, int lt, auto C0, auto C1, auto P) {
+  // slots [I0, I1) of the n = ceil((C1 - C0) / P) slots (default: all)
+  auto load_slots = [&](auto& x, int ti, int lt, auto C0, auto C1, auto P, auto I0, auto I1) {
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
-    constexpr int n = (c1 - c0 + np - 1) / np;
+    constexpr int i0 = decltype(I0)::value, i1 = decltype(I1)::value;
     const int t0 = ti * TT;
     // when every slot i (chunks c0 + np i + [0, np)) lies inside one of Q, K, V,
     // the buffer is known per slot at compile time; otherwise plain loads with
     // a row test (a per-lane choice of buffer would need a waterfall loop)
     constexpr bool SLOT = c0 % np == 0 && QCH % np == 0 && (c1 - c0) % np == 0;
 #pragma unroll
-    for (int i = 0; i < n; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int cb = c0 + np * i, c = cb + lt;
       x[i] = make_uint4(0, 0, 0, 0);
       if constexpr (SLOT) {
@@ -322,6 +323,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         if (cl / (W / CH) < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)t0 * W + cl * CH);
       }
     }
+  };
+  auto load_part = [&](auto& x, int ti, int lt, auto C0, auto C1, auto P) {
+    constexpr int n = (decltype(C1)::value - decltype(C0)::value + decltype(P)::value - 1) / decltype(P)::value;
+    load_slots(x, ti, lt, C0, C1, P, std::integral_constant<int, 0>{}, std::integral_constant<int, n>{});
   };
   auto store_part = [&](const auto& x, int lt, T* Qd, T* Kd, T* Vs, auto C0, auto C1, auto P) {
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value, np = decltype(P)::value;
@@ -403,37 +408,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     __syncthreads();
     if constexpr (PF) {
       if (ti + 1 < ntiles) load_role(x, ti + 1, s_wave);
-    }
-  };
-
-  // m <- g^Lt m + sum_tau wS[tau] q_tau (summary), by the M waves' threads:
-  // HT / D lanes per column
-  // (thread: 4 adjacent columns, every TPN-th token; the TPN partial sums of
-  // a column group sit in adjacent lanes)
-  auto m_vec_update = [&](const T* Qx, int Lt, float gL) {
-    constexpr int NCG = D / 4, TPN = HT / NCG;
-    static_assert(TPN >= 1 && TPN <= 64 && (TPN & (TPN - 1)) == 0, "m update lanes");
-    const int mt = tid - HT, cg = mt / TPN, tp = mt % TPN;
-    f32x4 acc = zero4();
-    auto add_row = [&](int t) {
-      const T* qp = Qx + t * L::LDD + 4 * cg;
-      const float wt = wS[t];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += wt * (float)qp[i];
-    };
-    if (Lt == TT) {
-#pragma unroll
-      for (int t = tp; t < TT; t += TPN) add_row(t);   // all row reads issued together
-    } else {
-      for (int t = tp; t < Lt; t += TPN) add_row(t);
-    }
-#pragma unroll
-    for (int off = 1; off < TPN; off *= 2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
-    if (tp == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mst[4 * cg + i] = gL * mst[4 * cg + i] + acc[i];
     }
   };
 
@@ -590,8 +564,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         for (int j = 0; j < 4; ++j)
           St[b][t][j] = (!SUM && (SFULL || cb < DT)) ? FS[(16 * t + 4 * lg4 + j) * L::LFS + 16 * cb + lr] : 0.f;
     }
-    // step 2 of tile ti (tile in Qx, Kx; A' in AB): P, P^T to LDS, n and S updates
-    auto s_step2 = [&](int ti, float gL, float g2L, const T* Qx, const T* Kx) {
+    // step 2 of tile ti (tile in Qx, Kx; A' in AB): P, P^T to LDS, n and S
+    // updates; mid() runs between Q S and the rest
+    auto s_step2 = [&](int ti, float gL, float g2L, const T* Qx, const T* Kx, auto&& mid) {
       T* PsT = PsTb(ti & 1);
       f32x4 pacc[SB][TR];
 #pragma unroll
@@ -610,6 +585,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
         }
       }
+      mid();
       float ncol[SB];
 #pragma unroll
       for (int b = 0; b < SB; ++b) ncol[b] = 0.f;
@@ -675,22 +651,31 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     if constexpr (L::PIPE) {
       finish_init();
       prologue();
-      // the S waves carry Q and K two tiles ahead (summary) or one (output)
+      // the S waves carry Q and K two tiles ahead (summary) or one (output);
+      // in the summary kernel the loads of a tile are issued in two halves,
+      // the second one inside the next main phase, so that the vector memory
+      // queue drains meanwhile (the output kernel is slower that way: measured)
       constexpr int AHEAD = SUM ? 2 : 1;
-      if (AHEAD < ntiles) load_part(xq, AHEAD, tid, QK{}, VB{}, HALF{});
+      using H0 = std::integral_constant<int, 0>;
+      using H1 = std::integral_constant<int, SUM ? NXS / 2 : NXS>;
+      using H2 = std::integral_constant<int, NXS>;
+      if (AHEAD < ntiles) load_slots(xq, AHEAD, tid, QK{}, VB{}, HALF{}, H0{}, H1{});
+      // summary: A' tiles of the next tile, shared with the M waves
+      constexpr int NAS = SUM ? (NTRI + NW - 1) / NW : 1;
       for (int ti = 0; ti < ntiles; ++ti) {
         const int t0 = ti * TT;
         const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
-        s_step2(ti, gpow(g, lgg, Lt), gpow(g, lgg, 2 * Lt), Qb(ti & 1), Kb(ti & 1));
+        s_step2(ti, gpow(g, lgg, Lt), gpow(g, lgg, 2 * Lt), Qb(ti & 1), Kb(ti & 1), [&]() {
+          if (ti + AHEAD < ntiles) load_slots(xq, ti + AHEAD, tid, QK{}, VB{}, HALF{}, H1{}, H2{});
+        });
         // summary: A' of the next tile (staged a tile ago), kept in registers
-        // until the S waves of this tile have all read AB
-        constexpr int NAS = SUM ? (NTRI + NOWN - 1) / NOWN : 1;
+        // until every S wave of this tile has read AB
         f32x4 an[NAS];
         if constexpr (SUM) {
           if (ti + 1 < ntiles) {
 #pragma unroll
             for (int sl = 0; sl < NAS; ++sl)
-              if (rw + NOWN * sl < NTRI) an[sl] = a_tile(rw + NOWN * sl, (ti + 1) & 1);
+              if (wave + NW * sl < NTRI) an[sl] = a_tile(wave + NW * sl, (ti + 1) & 1);
           }
         }
         __syncthreads();
@@ -702,13 +687,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           if (ti + 1 < ntiles) {
 #pragma unroll
             for (int sl = 0; sl < NAS; ++sl)
-              if (rw + NOWN * sl < NTRI) a_store(rw + NOWN * sl, an[sl]);
+              if (wave + NW * sl < NTRI) a_store(wave + NW * sl, an[sl]);
           }
         }
         if (ti + 1 < ntiles) weights(ti + 1);
         __syncthreads();
         if constexpr (!SUM) score_phase(ti);
-        if (ti + AHEAD + 1 < ntiles) load_part(xq, ti + AHEAD + 1, tid, QK{}, VB{}, HALF{});
+        if (ti + AHEAD + 1 < ntiles) load_slots(xq, ti + AHEAD + 1, tid, QK{}, VB{}, HALF{}, H0{}, H1{});
         if constexpr (!SUM) __syncthreads();
       }
     } else {
@@ -720,7 +705,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
         const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
         tile_head(ti, Lt, xq, std::true_type{});
-        s_step2(ti, gL, g2L, Qs, Ks);
+        s_step2(ti, gL, g2L, Qs, Ks, []() {});
         __syncthreads();
 
         // ---- step 3 (output kernel): B^T scores, shared with the M waves ----
@@ -925,26 +910,68 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           if (MFULL || rw + NOWN * b < ET) Ct[b][t] = acc[b];
       }
     };
+    // m <- g^Lt m + Q^T wS (summary) on MFMA: the B operand is wS in column 0
+    // and zeros elsewhere, so column 0 of the product (lanes lr == 0) is m for
+    // the rows 16 t + [0, 16) of this wave's blocks t = rw + NOWN s
+    constexpr int MS = (DT + NOWN - 1) / NOWN;
+    f32x4 macc[SUM ? MS : 1];
+#pragma unroll
+    for (int sm = 0; sm < (SUM ? MS : 1); ++sm) macc[sm] = zero4();
+    auto m_mma = [&](const T* Qx, float gL) {
+      F wc[NKS];
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wc[kk][i] = (T)(lr == 0 ? wS[kk * KS + 8 * lg4 + i] : 0.f);
+        } else {
+          wc[kk] = lr == 0 ? wS[kk * KS + lg4] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int sm = 0; sm < MS; ++sm) {
+        const int t = rw + NOWN * sm;
+        if (t < DT) {
+          f32x4 acc = macc[sm] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane), wc[kk], acc);
+          macc[sm] = acc;
+        }
+      }
+    };
 
     float g2L_prev = 1.f;
     if constexpr (L::PIPE) {
       finish_init();
       prologue();
-      if (1 < ntiles) load_part(xv, 1, tid - HT, VB{}, END{}, HALF{});
+      // V one tile ahead, its loads issued in two halves like Q and K (summary)
+      using H0 = std::integral_constant<int, 0>;
+      using H1 = std::integral_constant<int, SUM ? NXM / 2 : NXM>;
+      using H2 = std::integral_constant<int, NXM>;
+      if (1 < ntiles) load_slots(xv, 1, tid - HT, VB{}, END{}, HALF{}, H0{}, H1{});
+      constexpr int NAS = SUM ? (NTRI + NW - 1) / NW : 1;
       for (int ti = 0; ti < ntiles; ++ti) {
         const int t0 = ti * TT;
         const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
         const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
-        // summary: the previous tile's M update, the C update and m of this
-        // tile; output: the previous tile's outputs, the M update, then
-        // (Q M)^T of this tile
+        // summary: the previous tile's M update, the C and m updates of this
+        // tile and A' tiles of the next one; output: the previous tile's
+        // outputs, the M update, then (Q M)^T of this tile
+        f32x4 an[NAS];
         if constexpr (SUM) {
           if (ti > 0) m_update(ti - 1, g2L_prev);
+          if (ti + 1 < ntiles) load_slots(xv, ti + 1, tid - HT, VB{}, END{}, HALF{}, H1{}, H2{});
           __builtin_amdgcn_sched_barrier(0);
           c_update(Qb(ti & 1), Vsb(ti & 1), gL);
-          m_vec_update(Qb(ti & 1), Lt, gL);
+          m_mma(Qb(ti & 1), gL);
+          if (ti + 1 < ntiles) {
+#pragma unroll
+            for (int sl = 0; sl < NAS; ++sl)
+              if (wave + NW * sl < NTRI) an[sl] = a_tile(wave + NW * sl, (ti + 1) & 1);
+          }
         } else {
           if (ti > 0) finish_out(ti - 1, TT);   // only the last tile can be short
+          if (ti + 1 < ntiles) load_slots(xv, ti + 1, tid - HT, VB{}, END{}, HALF{}, H1{}, H2{});
           __builtin_amdgcn_sched_barrier(0);
           if (ti > 0) m_update(ti - 1, g2L_prev);
           __builtin_amdgcn_sched_barrier(0);
@@ -953,10 +980,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         g2L_prev = g2L;
         __syncthreads();
         // V of tile ti + 1 to the buffer last read by this step's updates of tile ti - 1
-        if (ti + 1 < ntiles) store_part(xv, tid - HT, nullptr, nullptr, Vsb((ti + 1) & 1), VB{}, END{}, HALF{});
+        if (ti + 1 < ntiles) {
+          store_part(xv, tid - HT, nullptr, nullptr, Vsb((ti + 1) & 1), VB{}, END{}, HALF{});
+          if constexpr (SUM) {
+#pragma unroll
+            for (int sl = 0; sl < NAS; ++sl)
+              if (wave + NW * sl < NTRI) a_store(wave + NW * sl, an[sl]);
+          }
+        }
         __syncthreads();
         if constexpr (!SUM) score_phase(ti);
-        if (ti + 2 < ntiles) load_part(xv, ti + 2, tid - HT, VB{}, END{}, HALF{});
+        if (ti + 2 < ntiles) load_slots(xv, ti + 2, tid - HT, VB{}, END{}, HALF{}, H0{}, H1{});
         if constexpr (!SUM) __syncthreads();
       }
       if constexpr (!SUM) finish_out(ntiles - 1, (Lspan - (ntiles - 1) * TT));
@@ -979,7 +1013,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         __builtin_amdgcn_sched_barrier(0);   // keep the two updates' operand loads apart
         if constexpr (!SUM) qm(Qs);
         else c_update(Qs, Vsb(ti & 1), gL);
-        if constexpr (SUM) m_vec_update(Qs, Lt, gL);
+        if constexpr (SUM) m_mma(Qs, gL);
         g2L_prev = g2L;
         __syncthreads();
 
@@ -997,6 +1031,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     }
     if (SUM) {
       m_update(ntiles - 1, g2L_prev);
+      if (lr == 0) {
+#pragma unroll
+        for (int sm = 0; sm < MS; ++sm) {
+          const int t = rw + NOWN * sm;
+          if (t < DT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mst[16 * t + 4 * lg4 + j] = macc[sm][j];
+          }
+        }
+      }
       __syncthreads();
     }
     if (SUM) {
