@@ -119,8 +119,21 @@ def bench_fwd(args, torch, np):
     L = hla.lib()
     p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
     st = hla._state_struct(summ)
-    ws_bytes = L.hla_scan_workspace_bytes(ctypes.byref(p))
+    # more than one run of whole segments: the scan stops at the run prefixes
+    # and the output kernel walks whole runs (chunk R * chunk)
+    R = hla.scan_run_length(T, chunk)
+    runs = -(-n // R)
+    use_runs = runs > 1 and runs * R == n
+    if use_runs:
+        rprefix = hla.alloc_state((B, H, runs), d, dv, "cuda")
+        rst = hla._state_struct(rprefix)
+        p_out = hla.make_problem(q, v, chunk * R, g, cfg["normalize"], cfg["eps"])
+        ws_bytes = L.hla_scan_runs_workspace_bytes(ctypes.byref(p))
+    else:
+        rst, p_out = st, p
+        ws_bytes = L.hla_scan_workspace_bytes(ctypes.byref(p))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    scan_name = "hla_scan_runs" if use_runs else "hla_scan"
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -131,10 +144,14 @@ def bench_fwd(args, torch, np):
         r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
         if ev:
             ev[1].record(stream)
-        r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
+        if use_runs:
+            r2 = L.hla_scan_runs(ctypes.byref(p), ctypes.byref(st), ctypes.byref(rst), ptr(ws),
+                                 ctypes.c_size_t(ws_bytes), sp)
+        else:
+            r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
         if ev:
             ev[2].record(stream)
-        r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
+        r3 = L.hla_fwd_output(ctypes.byref(p_out), ptr(q), ptr(k), ptr(v), ctypes.byref(rst), ptr(o),
                               ptr(den), None, ctypes.c_size_t(0), sp)
         if ev:
             ev[3].record(stream)
@@ -161,12 +178,13 @@ def bench_fwd(args, torch, np):
     U = B * H
     es = 2 if cfg["dtype"] == "bf16" else 4
     summ_bytes = U * n * (d * d + 2 * d * dv + 2 * d) * 4
+    prefix_bytes = summ_bytes // n * (runs if use_runs else n)   # prefixes the output kernel reads
     io_bytes = tokens * ((2 * d + dv) * es)
     kernels = {
         "hla_fwd_chunk_summaries": dict(ms=sum(k1) / len(k1), bytes=io_bytes + summ_bytes),
-        "hla_scan": dict(ms=sum(k2) / len(k2), bytes=None),
+        scan_name: dict(ms=sum(k2) / len(k2), bytes=None),
         "hla_fwd_output": dict(ms=sum(k3) / len(k3),
-                               bytes=io_bytes + summ_bytes + tokens * dv * 4
+                               bytes=io_bytes + prefix_bytes + tokens * dv * 4
                                + (tokens * 4 if den is not None else 0)),
     }
     dom = max(("hla_fwd_chunk_summaries", "hla_fwd_output"), key=lambda kname: kernels[kname]["ms"])
@@ -184,7 +202,9 @@ def bench_fwd(args, torch, np):
         "dtype": cfg["dtype"], "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
                    "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
-                   "path": "hla_fwd_chunk_summaries + hla_scan + hla_fwd_output"},
+                   "path": ("hla_fwd_chunk_summaries + hla_scan_runs + hla_fwd_output over runs of "
+                            f"{R} segments" if use_runs
+                            else "hla_fwd_chunk_summaries + hla_scan + hla_fwd_output")},
         "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
                           "peak_tflops": BF16_PEAK_TFLOPS,
                           "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},

@@ -47,6 +47,9 @@ hla_status check_problem(const hla_problem* p) {
   const int64_t n = p->T / p->chunk;
   if (units * n > kMaxGrid) return HLA_ERR_BAD_VALUE;
   if (units > 65535) return HLA_ERR_BAD_VALUE;   // grid.y of the scan levels
+  // a segment's rows are addressed with 32-bit byte offsets
+  const int64_t row_bytes = (int64_t)(p->d > p->dv ? p->d : p->dv) * (int64_t)dtype_size(p->in_dtype);
+  if ((int64_t)p->chunk * row_bytes > 2147483647) return HLA_ERR_BAD_VALUE;
   if (p->gamma && !aligned16(p->gamma)) return HLA_ERR_MISALIGNED;
   return HLA_OK;
 }
@@ -142,6 +145,7 @@ hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state
   a.tS = total ? total->S : nullptr; a.tC = total ? total->C : nullptr;
   a.tm = total ? total->m : nullptr; a.tG = total ? total->G : nullptr;
   a.th = total ? total->h : nullptr;
+  a.rS = a.rC = a.rm = a.rG = a.rh = nullptr;
   a.ws = static_cast<float*>(ws);
   a.gamma = p->gamma;
   a.units = (int)z.units; a.H = p->H; a.n = (int)z.n; a.chunk = p->chunk;
@@ -216,6 +220,57 @@ hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_stat
   if (empty_problem(p)) return HLA_OK;
   if (hla_status e = device_ready()) return e;
   return do_scan(p, inout, total_out, workspace, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+int32_t hla_scan_run_length(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK) return 0;
+  return hla::scan_run_length((int)(p->T / p->chunk));
+}
+
+size_t hla_scan_runs_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  const Sizes z = sizes_of(p);
+  return hla::scan_runs_workspace_floats(z.units, (int)z.n, p->d, p->dv) * 4;
+}
+
+hla_status hla_scan_runs(const hla_problem* p, const hla_state* summaries,
+                         const hla_state* run_prefix_out, void* workspace, size_t workspace_bytes,
+                         void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  const Sizes z = sizes_of(p);
+  const int64_t R = hla::scan_run_length((int)z.n), runs = (z.n + R - 1) / R;
+  if (hla_status e = check_state(summaries, true, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  const void* ins[5] = {summaries->S, summaries->C, summaries->m, summaries->G, summaries->h};
+  const size_t inb[5] = {z.units * z.n * z.S * 4, z.units * z.n * z.C * 4, z.units * z.n * z.m * 4,
+                         z.units * z.n * z.C * 4, z.units * z.n * z.m * 4};
+  if (hla_status e = check_state(run_prefix_out, true, z.units * runs, z, ins, inb, 5)) return e;
+  const size_t need = hla_scan_runs_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0) {
+    if (!workspace) return HLA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+    const size_t pb[5] = {z.units * runs * z.S * 4, z.units * runs * z.C * 4, z.units * runs * z.m * 4,
+                          z.units * runs * z.C * 4, z.units * runs * z.m * 4};
+    const void* outs[5] = {run_prefix_out->S, run_prefix_out->C, run_prefix_out->m,
+                           run_prefix_out->G, run_prefix_out->h};
+    for (int j = 0; j < 5; ++j)
+      if (overlap(workspace, need, ins[j], inb[j]) || overlap(workspace, need, outs[j], pb[j]))
+        return HLA_ERR_ALIASING;
+  }
+  if (hla_status e = device_ready()) return e;
+  hla::ScanPlan a;
+  a.S = summaries->S; a.C = summaries->C; a.m = summaries->m; a.G = summaries->G; a.h = summaries->h;
+  a.tS = a.tC = a.tm = a.tG = a.th = nullptr;
+  a.rS = run_prefix_out->S; a.rC = run_prefix_out->C; a.rm = run_prefix_out->m;
+  a.rG = run_prefix_out->G; a.rh = run_prefix_out->h;
+  a.ws = static_cast<float*>(workspace);
+  a.gamma = p->gamma;
+  a.units = (int)z.units; a.H = p->H; a.n = (int)z.n; a.chunk = p->chunk;
+  a.d = p->d; a.dv = p->dv;
+  return from_hip(hla::launch_scan(a, static_cast<hipStream_t>(stream)));
 } catch (...) {
   return HLA_ERR_HIP;
 }
@@ -302,6 +357,31 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
   const ChunkArgs a1 = chunk_args(p, q, k, v, &sm, nullptr, nullptr);
   if (hla_status e = from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
     return e;
+  // Several runs of whole segments and no final state wanted: the run-level
+  // scan only, then the output kernel walks whole runs (chunk R * chunk),
+  // carrying the state across the segments of a run.  The run prefixes and
+  // the tree's padding fill exactly hla_scan's scratch.
+  const int64_t R = hla::scan_run_length((int)z.n), runs = (z.n + R - 1) / R;
+  const int64_t row_bytes = (int64_t)(p->d > p->dv ? p->d : p->dv) * (int64_t)dtype_size(p->in_dtype);
+  if (!final_state && runs > 1 && runs * R == z.n && (int64_t)p->chunk * R * row_bytes <= 2147483647) {
+    const size_t rc = (size_t)z.units * (size_t)runs;
+    hla_state rp;
+    rp.S = static_cast<float*>(scan_ws); rp.C = rp.S + rc * z.S; rp.m = rp.C + rc * z.C;
+    rp.G = rp.m + rc * z.m; rp.h = rp.G + rc * z.C;
+    hla::ScanPlan a;
+    a.S = sm.S; a.C = sm.C; a.m = sm.m; a.G = sm.G; a.h = sm.h;
+    a.tS = a.tC = a.tm = a.tG = a.th = nullptr;
+    a.rS = rp.S; a.rC = rp.C; a.rm = rp.m; a.rG = rp.G; a.rh = rp.h;
+    a.ws = rp.h + rc * z.m;
+    a.gamma = p->gamma;
+    a.units = (int)z.units; a.H = p->H; a.n = (int)z.n; a.chunk = p->chunk;
+    a.d = p->d; a.dv = p->dv;
+    if (hla_status e = from_hip(hla::launch_scan(a, s))) return e;
+    hla_problem pr = *p;
+    pr.chunk = (int32_t)(p->chunk * R);
+    const ChunkArgs a3 = chunk_args(&pr, q, k, v, &rp, o, den);
+    return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
+  }
   if (hla_status e = do_scan(p, &sm, final_state, scan_ws, s)) return e;
   const ChunkArgs a3 = chunk_args(p, q, k, v, &sm, o, den);
   return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));

@@ -34,11 +34,14 @@ struct ScanArgs {
   int d, dv;
 };
 
-// The whole exclusive scan of one problem.
+// The whole exclusive scan of one problem, or (rS set) only the exclusive
+// prefixes at the starts of the runs.
 struct ScanPlan {
-  float *S, *C, *m, *G, *h;             // [units, n, ...] in place
+  float *S, *C, *m, *G, *h;             // [units, n, ...] in place (read only with rS)
   float *tS, *tC, *tm, *tG, *th;        // inclusive totals [units, ...], each may be nullptr
-  float* ws;                            // scan_workspace_floats(...) floats (nullptr if 0)
+  float *rS, *rC, *rm, *rG, *rh;        // run prefixes [units, runs, ...], or all nullptr
+  float* ws;                            // scan_workspace_floats(...) floats (nullptr if 0),
+                                        // scan_runs_workspace_floats(...) with rS
   const float* gamma;
   int units, H, n, chunk, d, dv;
 };
@@ -66,6 +69,8 @@ bool chunk_shape_supported(int dtype, int d, int dv);
 // totals and the tree's padding slots; 0 with a single run).
 int scan_run_length(int n);
 size_t scan_workspace_floats(int64_t units, int n, int d, int dv);
+// Scratch of the run-prefix scan: the tree's padding slots only.
+size_t scan_runs_workspace_floats(int64_t units, int n, int d, int dv);
 // Runs the whole exclusive scan (every launch, in order, on stream s).
 hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 

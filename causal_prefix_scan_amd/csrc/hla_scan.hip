@@ -22,6 +22,10 @@
 //   4. C, m pass:   the same for C and m, elementwise.
 // Steps 1-2 are skipped with a single run.  Each segment is read twice and
 // written once, in four launches; the tree's levels only see the run totals.
+// The run-prefix form stops after step 2 (the run totals reduced into the
+// caller's run-prefix arrays and scanned there; segments only read): a
+// forward pass whose output kernel walks whole runs needs nothing more, as it
+// carries the state from one segment of a run to the next itself.
 //
 // Steps 1 and 3 split a run's state over workgroups by 16-row blocks: a
 // workgroup owns rows [r0, r0 + 16) of S, G and h, and keeps the whole
@@ -525,6 +529,16 @@ size_t scan_workspace_floats(int64_t units, int n, int d, int dv) {
   return (size_t)units * (size_t)N * per;   // run totals, then the tree's padding slots
 }
 
+size_t scan_runs_workspace_floats(int64_t units, int n, int d, int dv) {
+  const int R = scan_run_length(n);
+  const int runs = (n + R - 1) / R;
+  if (runs <= 1) return 0;
+  int N = 1;
+  while (N < runs) N *= 2;
+  const size_t per = (size_t)d * d + 2 * (size_t)d * dv + 2 * (size_t)d;
+  return (size_t)units * (size_t)(N - runs) * per;   // the tree's padding slots
+}
+
 template <int D, int E>
 static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   constexpr int NRB = D / 16, VEC = (D * D + 2 * D * E + 2 * D) / 4;
@@ -538,8 +552,25 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   r.runs = (p.n + r.R - 1) / r.R;
   r.from_prefix = r.runs > 1;
   const size_t cnt = (size_t)units * r.runs;
+  // run prefixes only: the run totals are reduced straight into the output
+  // arrays and scanned there; the segments are only read
+  const bool runs_only = p.rS != nullptr;
   r.aS = r.aC = r.am = r.aG = r.ah = nullptr;
-  if (r.runs > 1) {
+  if (runs_only) {
+    r.aS = p.rS; r.aC = p.rC; r.am = p.rm; r.aG = p.rG; r.ah = p.rh;
+    if (r.runs == 1) {   // one run: its exclusive prefix is the identity
+      float* const outs[5] = {p.rS, p.rC, p.rm, p.rG, p.rh};
+      const size_t per[5] = {(size_t)D * D, (size_t)D * E, (size_t)D, (size_t)D * E, (size_t)D};
+      for (int i = 0; i < 5; ++i) {
+        const size_t count = cnt * per[i];
+        size_t blocks = (count + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, outs[i], count);
+        if (hipError_t e = hipGetLastError()) return e;
+      }
+      return hipSuccess;
+    }
+  } else if (r.runs > 1) {
     r.aS = p.ws; r.aC = r.aS + cnt * D * D; r.am = r.aC + cnt * D * E; r.aG = r.am + cnt * D;
     r.ah = r.aG + cnt * D * E;
   }
@@ -554,7 +585,8 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
     a.N = 1;
     while (a.N < a.n) a.N *= 2;
     const size_t pad = (size_t)units * (a.N - a.n);
-    a.wS = r.ah + cnt * D; a.wC = a.wS + pad * D * D; a.wm = a.wC + pad * D * E;
+    a.wS = runs_only ? p.ws : r.ah + cnt * D;
+    a.wC = a.wS + pad * D * D; a.wm = a.wC + pad * D * E;
     a.wG = a.wm + pad * D; a.wh = a.wG + pad * D * E;
     a.gamma = p.gamma; a.H = p.H; a.chunk = p.chunk; a.seg = r.R; a.nseg = p.n;
     a.d = D; a.dv = E;
@@ -582,6 +614,7 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
       if (hipError_t e = hipGetLastError()) return e;
     }
   }
+  if (runs_only) return hipSuccess;
   hipLaunchKernelGGL((run_rows_kernel<D, E, false>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
   if (hipError_t e = hipGetLastError()) return e;
   if (NRR == 1) return hipSuccess;   // the rescan wrote C and m

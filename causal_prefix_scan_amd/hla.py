@@ -23,7 +23,8 @@ STATUS = {
 
 EXPORTS = (
     "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
-    "hla_scan", "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
+    "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
+    "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
     "hla_fwd", "hla_decode_step",
 )
 
@@ -67,13 +68,16 @@ def lib():
     L.hla_fwd_chunk_summaries.argtypes = [pp, vp, vp, vp, ps, vp]
     L.hla_scan_workspace_bytes.argtypes, L.hla_scan_workspace_bytes.restype = [pp], sz
     L.hla_scan.argtypes = [pp, ps, ps, vp, sz, vp]
+    L.hla_scan_run_length.argtypes, L.hla_scan_run_length.restype = [pp], i32
+    L.hla_scan_runs_workspace_bytes.argtypes, L.hla_scan_runs_workspace_bytes.restype = [pp], sz
+    L.hla_scan_runs.argtypes = [pp, ps, ps, vp, sz, vp]
     L.hla_fwd_output_workspace_bytes.argtypes, L.hla_fwd_output_workspace_bytes.restype = [pp], sz
     L.hla_fwd_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, sz, vp]
     L.hla_fwd_workspace_bytes.argtypes, L.hla_fwd_workspace_bytes.restype = [pp], sz
     L.hla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, ps, vp, sz, vp]
     L.hla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, ps, vp, vp, vp]
-    for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_fwd_output", "hla_fwd",
-                 "hla_decode_step"):
+    for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
+                 "hla_fwd", "hla_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -176,6 +180,31 @@ def scan(summaries, q_shape, dv, chunk, dtype_code, gamma=None, want_total=False
                           ctypes.byref(tt) if tt is not None else None,
                           _ptr(ws), ctypes.c_size_t(nbytes), _stream()), "hla_scan")
     return total
+
+
+def scan_run_length(T, chunk):
+    """Segments per run of the blocked scan for n = T // chunk segments (host only)."""
+    p = Problem(1, 1, int(T), 16, 16, int(chunk), HLA_F32, 0, 0.0, None)
+    return int(lib().hla_scan_run_length(ctypes.byref(p)))
+
+
+def scan_runs(summaries, q_shape, dv, chunk, dtype_code, gamma=None):
+    """Exclusive prefixes at the run starts [B, H, runs, ...]; `summaries` is only read."""
+    torch = _torch()
+    B, H, T, d = q_shape
+    p = Problem(B, H, T, d, dv, int(chunk), dtype_code, 0, 0.0,
+                None if gamma is None else gamma.data_ptr())
+    dev = summaries["S"].device
+    n = T // chunk
+    R = int(lib().hla_scan_run_length(ctypes.byref(p)))
+    runs = (n + R - 1) // R
+    out = alloc_state((B, H, runs), d, dv, dev)
+    nbytes = lib().hla_scan_runs_workspace_bytes(ctypes.byref(p))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st, rt = _state_struct(summaries), _state_struct(out)
+    _check(lib().hla_scan_runs(ctypes.byref(p), ctypes.byref(st), ctypes.byref(rt), _ptr(ws),
+                               ctypes.c_size_t(nbytes), _stream()), "hla_scan_runs")
+    return out
 
 
 def fwd_output(q, k, v, prefixes, chunk, gamma=None, normalize=False, eps=0.0, want_den=False):

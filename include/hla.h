@@ -135,6 +135,36 @@ size_t hla_scan_workspace_bytes(const hla_problem* p);
 hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_state* total_out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Segments per run of the blocked scan: n when n <= 16, else the smallest
+ * power of two R with R*R >= n (n = T / chunk).  Host-only; 0 for an
+ * invalid problem. */
+int32_t hla_scan_run_length(const hla_problem* p);
+
+/* Bytes of scratch hla_scan_runs needs: the tree's padding slots, B*H*(N -
+ * runs) summaries of (d*d + 2*d*dv + 2*d) floats (0 with a single run).
+ * Host-only; returns 0 for an invalid problem. */
+size_t hla_scan_runs_workspace_bytes(const hla_problem* p);
+
+/*
+ * The scan of method section 4 stopped at the run level: the n segments of
+ * every (b, h) are cut into runs of R = hla_scan_run_length(p) consecutive
+ * segments (the last run may be shorter), each run is reduced in order and
+ * the run totals go through the exclusive Blelloch tree.  `run_prefix_out`
+ * ([B, H, runs, ...], runs = ceil(n / R), all fields required, no overlap
+ * with `summaries`) receives for run r the exclusive prefix at its first
+ * segment, P_{rR} = s_0 (+) ... (+) s_{rR-1} (zero for r = 0).
+ * `summaries` (as hla_fwd_chunk_summaries writes them) is only read.
+ * When R divides n, hla_fwd_output called with chunk' = R * chunk and these
+ * prefixes gives the outputs of hla_scan + hla_fwd_output at `chunk`: inside
+ * a run the output kernel carries the state from one segment to the next
+ * itself, so the prefixes of the other segments are never written.
+ * `workspace` must hold hla_scan_runs_workspace_bytes(p) bytes and overlap
+ * neither argument.
+ */
+hla_status hla_scan_runs(const hla_problem* p, const hla_state* summaries,
+                         const hla_state* run_prefix_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Bytes of scratch hla_fwd_output needs (0 today; kept for ABI stability). */
 size_t hla_fwd_output_workspace_bytes(const hla_problem* p);
 
@@ -159,7 +189,11 @@ size_t hla_fwd_workspace_bytes(const hla_problem* p);
  * with the summaries kept in `workspace` (hla_fwd_workspace_bytes(p) bytes).
  * o and den as in hla_fwd_output.  If `final_state` is non-NULL its non-NULL
  * fields receive the state after all T tokens ([B, H, ...]), ready for
- * hla_decode_step.
+ * hla_decode_step.  Without a final state, and with more than one run of
+ * R = hla_scan_run_length(p) segments where R divides n, the scan is
+ * hla_scan_runs and the outputs are computed over whole runs (chunk R *
+ * chunk) from the run prefixes; the results agree up to fp32 rounding
+ * order.
  */
 hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
                    float* o, float* den, const hla_state* final_state,

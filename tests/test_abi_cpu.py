@@ -132,6 +132,31 @@ def test_workspace_sizes(L):
     assert L.hla_fwd(ctypes.byref(p), Q, K, V, O, None, None, 0x7000000000, 16, None) == WS
 
 
+def test_run_prefix_scan_sizes_and_checks(L):
+    per = 32 * 32 + 2 * 32 * 16 + 2 * 32
+    # run length: n up to 16 is one run; above, the power of two R with R^2 >= n
+    for n, R in ((1, 1), (5, 5), (16, 16), (17, 8), (64, 8), (65, 16), (512, 32)):
+        p = problem(B=1, H=2, T=n * 64, chunk=64, d=32, dv=16)
+        assert L.hla_scan_run_length(ctypes.byref(p)) == R, n
+    assert L.hla_scan_run_length(ctypes.byref(problem(T=10))) == 0   # invalid -> 0
+    # one run: no scratch; n = 40: 5 runs of 8, the tree pads them to 8 (3 slots)
+    p = problem(B=1, H=2, T=16 * 64, chunk=64, d=32, dv=16)
+    assert L.hla_scan_runs_workspace_bytes(ctypes.byref(p)) == 0
+    p = problem(B=1, H=2, T=40 * 64, chunk=64, d=32, dv=16)
+    assert L.hla_scan_runs_workspace_bytes(ctypes.byref(p)) == 2 * 3 * per * 4
+    # n = 512: 16 runs, a power of two: no padding
+    p = problem(B=1, H=2, T=512 * 64, chunk=64, d=32, dv=16)
+    assert L.hla_scan_runs_workspace_bytes(ctypes.byref(p)) == 0
+    # argument checks before anything runs
+    p = problem(B=1, H=2, T=40 * 64, chunk=64, d=32, dv=16)
+    assert L.hla_scan_runs(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(state(base=0x7100000000)),
+                           0x7000000000, 16, None) == WS
+    assert L.hla_scan_runs(ctypes.byref(p), None, ctypes.byref(state()), None, 0, None) == NULLP
+    # run prefixes overlapping the summaries
+    assert L.hla_scan_runs(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(state()),
+                           0x7000000000, 1 << 20, None) == ALIAS
+
+
 def test_empty_problem_is_a_no_op(L):
     for kw in (dict(T=0), dict(B=0), dict(H=0)):
         assert summaries(L, problem(**kw)) == OK

@@ -127,6 +127,66 @@ def test_stages_match_oracle(gpu, case):
         assert torch.equal(fs[key], total[key]), key
 
 
+# (B, H, T, d, dv, chunk, dtype, decay, normalize): more than 16 segments, so
+# more than one run; the first four have whole runs (R divides n)
+RUNS = [
+    (1, 2, 1024, 32, 32, 32, "bf16", True, True),     # n = 32: 4 runs of 8
+    (1, 1, 512, 16, 16, 16, "f32", True, False),      # n = 32, fp32
+    (1, 1, 1024, 128, 128, 32, "bf16", True, False),  # 8-wave kernels walking 256-token runs
+    (2, 1, 2048, 64, 64, 64, "bf16", False, True),    # n = 32, gamma = 1
+    (1, 2, 640, 32, 32, 32, "bf16", True, False),     # n = 20: runs 8, 8, 4 (prefixes only)
+]
+
+
+@pytest.mark.parametrize("case", RUNS, ids=[case_id(c) for c in RUNS])
+def test_run_prefixes_and_run_length_outputs(gpu, case):
+    torch = gpu
+    B, H, T, d, dv, chunk, dtype, decay, norm = case
+    say("case", case_id(case))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, dtype, seed=2000 + T + d, decay=decay)
+    q, k, v, g = to_dev(inp)
+    uq, uk, uv, ug = inp.units()
+    U, n = B * H, T // chunk
+    R = hla.scan_run_length(T, chunk)
+    runs = (n + R - 1) // R
+    assert R > 1 and runs > 1
+    tol = tol_of(dtype)
+    num, den, _ = O.serial(uq, uk, uv, ug)
+    pre = O.blelloch_exclusive_scan(O.chunk_summaries(uq, uk, uv, chunk, ug), ug)
+
+    gs = hla.fwd_chunk_summaries(q, k, v, chunk, g)
+    before = {key: gs[key].clone() for key in FIELDS}
+    rp = hla.scan_runs(gs, q.shape, dv, chunk, dcode(dtype), g)
+    torch.cuda.synchronize()
+    for key in FIELDS:
+        assert torch.equal(gs[key], before[key]), ("summaries must be left as they are", key)
+        got = host(rp[key]).reshape(U, runs, -1)
+        want = np.stack([pre[r * R][key].reshape(U, -1) for r in range(runs)], axis=1)
+        e = rel_err(got, want)
+        say(f"  run prefix {key}: {e:.2e}")
+        assert e <= tol, (key, e)
+    assert not torch.any(rp["S"][:, :, 0]).item(), "the first run starts from zero"
+    if runs * R != n:
+        return
+    # outputs with the output kernel walking whole runs from the run prefixes
+    o, dn = hla.fwd_output(q, k, v, rp, chunk * R, g, normalize=False, want_den=True)
+    torch.cuda.synchronize()
+    e_num = rel_err(host(o).reshape(U, T, dv), num)
+    e_den = rel_err(host(dn).reshape(U, T), den)
+    say(f"  run-length spans: num {e_num:.2e} den {e_den:.2e}")
+    assert e_num <= tol and e_den <= tol
+    # hla_fwd without a final state takes this path: the same bits
+    o2, dn2, _ = hla.fwd(q, k, v, chunk, g, normalize=False, want_den=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(dn2, dn)
+    if norm:
+        eps = 1e-6
+        on, _, _ = hla.fwd(q, k, v, chunk, g, normalize=True, eps=eps)
+        torch.cuda.synchronize()
+        ratio = host(o) / (host(dn)[..., None] + eps)
+        assert rel_err(host(on), ratio) <= 1e-5
+
+
 def full_or_sampled(name, sample_units):
     cfg = synth.FWD_WORKLOADS[name]
     return cfg, sample_units
