@@ -1,4 +1,5 @@
-"""CPU oracle for the masked second-order HLA forward and its decode step.
+"""CPU oracle for the masked second-order HLA forward, its decode step and
+the unmasked variant.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this module: only the tests, the smoke check and the CPU-baseline leg
@@ -55,6 +56,8 @@ __all__ = [
     "identity_summary", "combine", "blelloch_exclusive_scan",
     "chunk_summaries", "chunk_outputs", "chunk_scan_forward", "decode_step",
     "normalise", "powers",
+    "serial_unmasked", "brute_unmasked", "combine_unmasked",
+    "unmasked_chunk_forward",
 ]
 
 _F = np.float64
@@ -253,15 +256,17 @@ def combine(A, B, gamma=None):
     }
 
 
-def blelloch_exclusive_scan(summaries, gamma=None):
+def blelloch_exclusive_scan(summaries, gamma=None, op=None):
     """Exclusive Blelloch scan ([S4]) of a list of n segment summaries.
 
     Work-efficient up-sweep then down-sweep over an array padded to a power
     of two with identities.  The operator is not commutative: in the
     down-sweep a right child receives (parent prefix) combined with (left
     sum), in that order.  Returns the list of exclusive prefixes
-    P_i = s_0 (+) ... (+) s_{i-1}, P_0 = identity.
+    P_i = s_0 (+) ... (+) s_{i-1}, P_0 = identity.  `op` is the combine
+    (default: the masked one above; combine_unmasked for the unmasked variant).
     """
+    op = combine if op is None else op
     n = len(summaries)
     if n == 0:
         return []
@@ -273,7 +278,7 @@ def blelloch_exclusive_scan(summaries, gamma=None):
     step = 1
     while step < N:                                   # up-sweep
         for j in range(2 * step - 1, N, 2 * step):
-            x[j] = combine(x[j - step], x[j], gamma)
+            x[j] = op(x[j - step], x[j], gamma)
         step *= 2
     x[N - 1] = identity_summary(U, d, dv)
     step = N // 2
@@ -281,7 +286,7 @@ def blelloch_exclusive_scan(summaries, gamma=None):
         for j in range(2 * step - 1, N, 2 * step):
             left = x[j - step]
             x[j - step] = x[j]
-            x[j] = combine(x[j], left, gamma)
+            x[j] = op(x[j], left, gamma)
         step //= 2
     return x[:n]
 
@@ -334,3 +339,106 @@ def normalise(num, den, eps):
     """Ratio-normalised output of [S1]: numerator / (masked denominator + eps).
     No absolute value or clamp (the reading of the unstated placement)."""
     return _f64(num) / (_f64(den)[..., None] + float(eps))
+
+
+# ----------------------------------------------------------------------------
+# The unmasked second-order variant.  [S1] notes that the plain product
+# S^K_t C^QV_t includes future terms (pairs with key index i after the query
+# index j) -- that is the unmasked operator, o_t = q_t^T S_t C_t, which the
+# cross summaries G, h are there to remove; [C2] states that the associative
+# operators exist for the unmasked setting too, with and without decay.
+# Readings: the same decay placement as above (S, C, m decay once per token),
+# so the closed-form weight is again gamma^((t-i)+(t-j)); the ratio-normalised
+# form divides by q_t^T S_t m_t (v = 1) plus eps.
+# ----------------------------------------------------------------------------
+
+def serial_unmasked(q, k, v, gamma=None, state=None):
+    """Serial recurrence of the unmasked variant: for t = 1..T, in order,
+      S <- g S + k_t k_t^T,  C <- g C + q_t v_t^T,  m <- g m + q_t,
+      num_t = (q_t^T S) C,  den_t = (q_t^T S) m.
+    Returns (num [U,T,dv], den [U,T], final state {S, C, m}).  `state`
+    (optional, with S, C, m) is the state before the first token."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    U, T, d = q.shape
+    dv = v.shape[2]
+    g = _gamma(gamma, U)
+    g1 = g[:, None]
+    if state is None:
+        S, C, m = np.zeros((U, d, d), _F), np.zeros((U, d, dv), _F), np.zeros((U, d), _F)
+    else:
+        S, C, m = (_f64(state[key]).copy() for key in ("S", "C", "m"))
+    num = np.empty((U, T, dv), _F)
+    den = np.empty((U, T), _F)
+    for t in range(T):
+        qt, kt, vt = q[:, t, :], k[:, t, :], v[:, t, :]
+        S = g1[:, :, None] * S + kt[:, :, None] * kt[:, None, :]
+        C = g1[:, :, None] * C + qt[:, :, None] * vt[:, None, :]
+        m = g1 * m + qt
+        qS = np.matmul(qt[:, None, :], S)[:, 0, :]
+        num[:, t, :] = np.matmul(qS[:, None, :], C)[:, 0, :]
+        den[:, t] = np.sum(qS * m, axis=1)
+    return num, den, {"S": S, "C": C, "m": m}
+
+
+def brute_unmasked(q, k, v, gamma=None):
+    """Closed form of the unmasked variant as a triple sum (tiny inputs only):
+    num_t = sum_{i<=t} sum_{j<=t} w (q_t.k_i)(k_i.q_j) v_j, den_t without v_j,
+    w = gamma^((t-i)+(t-j)): the key index i and the value index j are both
+    bounded by t only, not ordered against each other."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    U, T, d = q.shape
+    dv = v.shape[2]
+    g = _gamma(gamma, U)
+    num = np.zeros((U, T, dv), _F)
+    den = np.zeros((U, T), _F)
+    for u in range(U):
+        for t in range(T):
+            for i in range(t + 1):
+                for j in range(t + 1):
+                    w = float(g[u]) ** ((t - i) + (t - j))
+                    s = w * float(q[u, t] @ k[u, i]) * float(k[u, i] @ q[u, j])
+                    num[u, t] += s * v[u, j]
+                    den[u, t] += s
+    return num, den
+
+
+def combine_unmasked(A, B, gamma=None):
+    """Segment A followed by segment B for the unmasked variant ([C2]): the
+    moments only, no cross term.  a = gamma^(L_B):
+      S = a S_A + S_B,  C = a C_A + C_B,  m = a m_A + m_B,  L = L_A + L_B."""
+    U = A["S"].shape[0]
+    a = powers(_gamma(gamma, U), B["L"])
+    return {
+        "S": a[:, None, None] * A["S"] + B["S"],
+        "C": a[:, None, None] * A["C"] + B["C"],
+        "m": a[:, None] * A["m"] + B["m"],
+        "G": np.zeros_like(A["G"]), "h": np.zeros_like(A["h"]),
+        "L": A["L"] + B["L"],
+    }
+
+
+def unmasked_chunk_forward(q, k, v, chunk, gamma=None):
+    """Chunk-parallel form of the unmasked variant ([S4], [C2]): per segment
+    the state the unmasked recurrence reaches from zero, an exclusive
+    Blelloch scan under combine_unmasked, then the recurrence continued
+    inside each segment from its prefix.  Returns (num, den, prefixes)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    U, T, d = q.shape
+    dv = v.shape[2]
+    assert chunk > 0 and T % chunk == 0
+    sums = []
+    for s in range(0, T, chunk):
+        _, _, st = serial_unmasked(q[:, s:s + chunk], k[:, s:s + chunk], v[:, s:s + chunk], gamma)
+        st["G"] = np.zeros((U, d, dv), _F)
+        st["h"] = np.zeros((U, d), _F)
+        st["L"] = np.full(U, chunk, dtype=np.int64)
+        sums.append(st)
+    pre = blelloch_exclusive_scan(sums, gamma, op=combine_unmasked)
+    num = np.empty((U, T, dv), _F)
+    den = np.empty((U, T), _F)
+    for c, s in enumerate(range(0, T, chunk)):
+        n_, d_, _ = serial_unmasked(q[:, s:s + chunk], k[:, s:s + chunk], v[:, s:s + chunk],
+                                    gamma, pre[c])
+        num[:, s:s + chunk] = n_
+        den[:, s:s + chunk] = d_
+    return num, den, pre
