@@ -389,6 +389,52 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
   return HLA_ERR_HIP;
 }
 
+size_t hla_unmasked_fwd_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  const Sizes z = sizes_of(p);
+  return (size_t)z.units * (size_t)z.n * (z.S + z.C + z.m) * 4;
+}
+
+hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                            float* o, float* den, void* workspace, size_t workspace_bytes,
+                            void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  const size_t need = hla_unmasked_fwd_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  const void* ins[4] = {q, k, v, workspace};
+  const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
+  for (int j = 0; j < 4; ++j) {
+    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  for (int j = 0; j < 3; ++j)
+    if (overlap(workspace, need, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
+  if (hla_status e = device_ready()) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t cnt = (size_t)z.units * (size_t)z.n;
+  hla_state sm;
+  sm.S = static_cast<float*>(workspace);
+  sm.C = sm.S + cnt * z.S;
+  sm.m = sm.C + cnt * z.C;
+  sm.G = sm.h = nullptr;
+  const ChunkArgs a1 = chunk_args(p, q, k, v, &sm, nullptr, nullptr);
+  if (hla_status e = from_hip(hla::launch_unmasked_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
+    return e;
+  if (hla_status e = from_hip(hla::launch_unmasked_scan(a1, (int)z.units, p->d, p->dv, s))) return e;
+  const ChunkArgs a3 = chunk_args(p, q, k, v, &sm, o, den);
+  return from_hip(hla::launch_unmasked_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
 hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
                            int32_t normalize, float eps, const float* gamma, const void* q,
                            const void* k, const void* v, const hla_state* state, float* o,

@@ -74,6 +74,15 @@ size_t scan_runs_workspace_floats(int64_t units, int n, int d, int dv);
 // Runs the whole exclusive scan (every launch, in order, on stream s).
 hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 
+// The unmasked variant: segment moments (S, C, m; G and h unused), the
+// exclusive decayed running sum over a unit's segments (in place on S, C, m),
+// and the outputs from the prefixes.
+hipError_t launch_unmasked_summaries(int dtype, int d, int dv, int units, const ChunkArgs& a,
+                                     hipStream_t s);
+hipError_t launch_unmasked_scan(const ChunkArgs& a, int units, int d, int dv, hipStream_t s);
+hipError_t launch_unmasked_outputs(int dtype, int d, int dv, int units, const ChunkArgs& a,
+                                   hipStream_t s);
+
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace hla

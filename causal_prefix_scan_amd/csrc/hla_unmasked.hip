@@ -1,0 +1,422 @@
+// The unmasked second-order HLA forward, o_t = q_t^T S_t C_t
+// ("Higher-order Linear Attention", arXiv 2510.27258, summaries on
+// gist.science: method section 1 -- the plain product of the key moment and
+// the query-value accumulator, before the cross summaries remove its future
+// terms; key contribution 2 -- associative operators for the unmasked
+// setting, with and without decay; method section 4 -- segment summaries
+// joined by an exclusive scan).
+//
+// With decay g per head (S, C, m each decay once per token), 0-based
+// positions tau, i, j inside a tile of Lt tokens and the tile's starting
+// state (S, C, m):
+//   p_tau   = g^(tau+1) S q_tau + sum_{i<=tau} g^(tau-i) (q_tau.k_i) k_i   (= S_tau q_tau)
+//   num_tau = g^(tau+1) C^T p_tau + sum_{j<=tau} g^(tau-j) (p_tau.q_j) v_j (= C_tau^T p_tau)
+//   den_tau = g^(tau+1) p_tau.m   + sum_{j<=tau} g^(tau-j) (p_tau.q_j)
+//   S <- g^Lt S + K^T diag(w) K,  C <- g^Lt C + Q^T diag(w) V,  m <- g^Lt m + Q^T w,
+//   w_i = g^(Lt-1-i).
+// A segment's summary is (S, C, m) reached from zero; the combine has no
+// cross term (S = a S_A + S_B, likewise C and m, a = g^(length of B)), so the
+// exclusive scan is a decayed running sum over the segments of a unit,
+// element by element.
+//
+// One workgroup owns one segment of one (batch, head) unit.  Its waves split
+// into S waves (column blocks of S; they produce the matching columns of P
+// and update S) and C waves (column blocks of C; they produce the matching
+// columns of the output and update C and m).  The state lives in fp32 MFMA
+// accumulators; P goes through LDS (row-major, bf16 for bf16 inputs) for the
+// score tiles and the state term C^T p.  Every phase is separated by a
+// barrier: this kernel favours a plain schedule over overlap.
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+constexpr int UT = 64;   // tokens per tile
+
+enum { U_SUMMARY = 0, U_OUTPUT = 1 };
+
+template <typename T, int D, int E>
+struct ULayout {
+  static constexpr int PADT = 16 / (int)sizeof(T);
+  static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;   // d zero-padded to one MFMA K step
+  static constexpr int LDD = DP + PADT;   // Qs, Ks, Ps: [tok][d]
+  static constexpr int LDV = E + PADT;    // Vs: [tok][e]
+  static constexpr int LDT = UT + PADT;   // AB, BB: [tok][tok]
+  static constexpr size_t QB = (size_t)UT * LDD * sizeof(T);
+  static constexpr size_t Qs = 0, Ks = QB, Vs = 2 * QB;
+  static constexpr size_t Ps = Vs + (size_t)UT * LDV * sizeof(T);
+  static constexpr size_t AB = Ps + QB;
+  static constexpr size_t BB = AB + (size_t)UT * LDT * sizeof(T);
+  static constexpr size_t TILE_END = BB + (size_t)UT * LDT * sizeof(T);
+  static constexpr size_t W = (TILE_END + 15) / 16 * 16;
+  // pw, w1, wS, pm [UT]; bpart [UT/16][UT]; mst [D]
+  static constexpr size_t TOTAL = W + (size_t)(4 * UT + (UT / 16) * UT + D) * 4;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+};
+
+// Lower-triangular 16x16 tile number idx: row block r, column block c <= r.
+__device__ __forceinline__ void utri(int idx, int& r, int& c) {
+  r = 0;
+  while (idx > r) { idx -= r + 1; ++r; }
+  c = idx;
+}
+
+template <typename T>
+__device__ __forceinline__ void ustore4(T* p, f32x4 x);
+template <>
+__device__ __forceinline__ void ustore4<__bf16>(__bf16* p, f32x4 x) {
+  bf16x4 y;
+  y[0] = (__bf16)x[0]; y[1] = (__bf16)x[1]; y[2] = (__bf16)x[2]; y[3] = (__bf16)x[3];
+  *reinterpret_cast<bf16x4*>(p) = y;
+}
+template <>
+__device__ __forceinline__ void ustore4<float>(float* p, f32x4 x) {
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+
+template <typename T, int D, int E, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
+  constexpr int NTHR = 64 * NW;
+  using L = ULayout<T, D, E>;
+  using MMT = MM<T>;
+  using FR = Frag<T>;
+  constexpr int KS = MMT::KS, CH = MMT::CH, DP = L::DP;
+  constexpr int DT = D / 16, ET = E / 16, TR = UT / 16, NKS = UT / KS;
+  constexpr int NTRI = TR * (TR + 1) / 2;
+  constexpr int QSK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps of a d-contraction
+  constexpr int NOWN = NW / 2, HT = NTHR / 2;
+  constexpr int SB = (DT + NOWN - 1) / NOWN, CB = (ET + NOWN - 1) / NOWN;
+  constexpr bool OUT = MODE == U_OUTPUT;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  T* Qs = reinterpret_cast<T*>(smem + L::Qs);
+  T* Ks = reinterpret_cast<T*>(smem + L::Ks);
+  T* Vs = reinterpret_cast<T*>(smem + L::Vs);
+  T* Ps = reinterpret_cast<T*>(smem + L::Ps);
+  T* AB = reinterpret_cast<T*>(smem + L::AB);
+  T* BB = reinterpret_cast<T*>(smem + L::BB);
+  float* pw = reinterpret_cast<float*>(smem + L::W);
+  float* w1 = pw + UT;
+  float* wS = w1 + UT;
+  float* pm = wS + UT;
+  float* bpart = pm + UT;
+  float* mst = bpart + TR * UT;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg4 = lane >> 4;
+  const bool sRole = wave < NOWN;
+  const int rw = sRole ? wave : wave - NOWN;
+  const int nspan = a.nspan;
+  const int unit = blockIdx.x / nspan, span = blockIdx.x - unit * nspan;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float lgg = log2f(g);
+  const int Lspan = a.chunk;
+  const size_t tok0 = (size_t)unit * (size_t)a.T + (size_t)span * (size_t)Lspan;
+  const T* gq = reinterpret_cast<const T*>(a.q) + tok0 * D;
+  const T* gk = reinterpret_cast<const T*>(a.k) + tok0 * D;
+  const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
+  const size_t sidx = (size_t)unit * nspan + span;
+  const int ntiles = (Lspan + UT - 1) / UT;
+
+  // zero the tile region once: padding columns [D, DP) of Q, K, P and the
+  // upper score tiles are read as zeros and never written
+  for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < UT) {
+    pw[tid] = gpow(g, lgg, tid);
+    w1[tid] = gpow(g, lgg, tid + 1);
+  }
+  for (int i = tid; i < D; i += NTHR) mst[i] = OUT ? a.m[sidx * D + i] : 0.f;
+
+  // the role's state: S waves hold S[:, 16 cb + lr], C waves C[:, 16 ce + lr]
+  // (accumulator tiles t over rows 16 t + 4 lg4 + [0, 4)), from the prefix or zero
+  constexpr int NB = SB > CB ? SB : CB;
+  f32x4 St[NB][DT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int cb = rw + NOWN * b;
+    const bool own = sRole ? (b < SB && cb < DT) : (b < CB && cb < ET);
+    const float* src = sRole ? a.S + sidx * D * D : a.C + sidx * D * E;
+    const int ld = sRole ? D : E;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        St[b][t][j] = (OUT && own) ? src[(size_t)(16 * t + 4 * lg4 + j) * ld + 16 * cb + lr] : 0.f;
+  }
+  __syncthreads();
+
+  constexpr int QCH = UT * D / CH, VCH = UT * E / CH, NCH = 2 * QCH + VCH;
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int t0 = ti * UT;
+    const int Lt = (Lspan - t0) < UT ? (Lspan - t0) : UT;
+    const float gL = gpow(g, lgg, Lt);
+    // ---- stage Q, K, V (rows past the segment end as zeros) and w ----
+    for (int c = tid; c < NCH; c += NTHR) {
+      const T* src;
+      T* dst;
+      int cl, W, LD;
+      if (c < QCH) { src = gq; dst = Qs; cl = c; W = D; LD = L::LDD; }
+      else if (c < 2 * QCH) { src = gk; dst = Ks; cl = c - QCH; W = D; LD = L::LDD; }
+      else { src = gv; dst = Vs; cl = c - 2 * QCH; W = E; LD = L::LDV; }
+      const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (row < Lt) x = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
+      *reinterpret_cast<uint4*>(dst + row * LD + col) = x;
+    }
+    if (tid < UT) wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+    __syncthreads();
+
+    if constexpr (OUT) {
+      // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) over all waves ----
+      for (int idx = wave; idx < NTRI; idx += NW) {
+        int r, c;
+        utri(idx, r, c);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DP; k0 += KS)
+          acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+        const int tau = 16 * r + lr;   // lane: position tau, keys i = 16 c + 4 lg4 + j
+        f32x4 val;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * c + 4 * lg4 + j;
+          val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
+        }
+        ustore4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
+      }
+      __syncthreads();
+
+      // ---- S waves: P[:, own] = g^(tau+1) Q S[:, own] + A' K[:, own] -> Ps ----
+      if (sRole) {
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+          const int cb = rw + NOWN * b;
+          if (cb < DT) {
+#pragma unroll
+            for (int r = 0; r < TR; ++r) {
+              f32x4 acc = zero4();
+#pragma unroll
+              for (int kk = 0; kk < QSK; ++kk)
+                acc = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), FR::acc_b(St[b], kk), acc);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[j] *= w1[16 * r + 4 * lg4 + j];
+              for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
+                acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Ks, L::LDD, k0, 16 * cb, lane), acc);
+              // lane: P[tau = 16 r + 4 lg4 + j][d = 16 cb + lr]
+#pragma unroll
+              for (int j = 0; j < 4; ++j) Ps[(16 * r + 4 * lg4 + j) * L::LDD + 16 * cb + lr] = (T)acc[j];
+            }
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- all waves: p.m and B[tau][j] = g^(tau-j) p_tau.q_j (j <= tau) ----
+      {
+        constexpr int LPR = NTHR / UT;
+        const int tau = tid / LPR, part = tid % LPR;
+        float acc = 0.f;
+#pragma unroll
+        for (int c = part * (D / LPR); c < (part + 1) * (D / LPR); ++c)
+          acc += (float)Ps[tau * L::LDD + c] * mst[c];
+#pragma unroll
+        for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
+        if (part == 0) pm[tau] = acc;
+      }
+      for (int idx = wave; idx < NTRI; idx += NW) {
+        int r, c;
+        utri(idx, r, c);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DP; k0 += KS)
+          acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * c, k0, lane), MMT::ld(Ps, L::LDD, 16 * r, k0, lane), acc);
+        const int tau = 16 * r + lr;   // lane: position tau, values j = 16 c + 4 lg4 + jj
+        f32x4 val;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 16 * c + 4 * lg4 + jj;
+          val[jj] = j <= tau ? acc[jj] * pw[tau - j] : 0.f;
+        }
+        ustore4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
+        const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+        if (lg4 == 0) bpart[c * UT + tau] = rs;
+      }
+      __syncthreads();
+    }
+
+    if (sRole) {
+      // ---- S[:, own] <- g^Lt S + K^T diag(w) K[:, own] ----
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int cb = rw + NOWN * b;
+        if (cb < DT) {
+          typename MMT::F bk[NKS];
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) bk[kk] = FR::scale(FR::tr(Ks, L::LDD, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            f32x4 acc = St[b][t] * gL;
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bk[kk], acc);
+            St[b][t] = acc;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        const int ce = rw + NOWN * b;
+        if (ce < ET) {
+          if constexpr (OUT) {
+            // ---- O[:, own] = g^(tau+1) P C[:, own] + B V[:, own] ----
+            float* go = a.o + (tok0 + (size_t)t0) * E;
+#pragma unroll
+            for (int r = 0; r < TR; ++r) {
+              f32x4 acc = zero4();
+#pragma unroll
+              for (int kk = 0; kk < QSK; ++kk)
+                acc = MMT::mma(FR::perm(Ps, L::LDD, 16 * r, kk, lane), FR::acc_b(St[b], kk), acc);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[j] *= w1[16 * r + 4 * lg4 + j];
+              for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
+                acc = MMT::mma(MMT::ld(BB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * ce, lane), acc);
+              // lane: O[tau = 16 r + 4 lg4 + j][e = 16 ce + lr]
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int tau = 16 * r + 4 * lg4 + j;
+                float o = acc[j];
+                if (a.normalize) {
+                  float dn = w1[tau] * pm[tau];
+                  for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
+                  o = o / (dn + a.eps);
+                }
+                if (tau < Lt) go[(size_t)tau * E + 16 * ce + lr] = o;
+              }
+            }
+          }
+          // ---- C[:, own] <- g^Lt C + Q^T diag(w) V[:, own] ----
+          typename MMT::F bv[NKS];
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ce, lane), wS, kk * KS, lane);
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            f32x4 acc = St[b][t] * gL;
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qs, L::LDD, kk * KS, 16 * t, lane), bv[kk], acc);
+            St[b][t] = acc;
+          }
+        }
+      }
+      if constexpr (OUT) {
+        const int mt = tid - HT;
+        if (a.den != nullptr && mt < Lt) {
+          float dn = w1[mt] * pm[mt];
+          for (int c = 0; c <= mt / 16; ++c) dn += bpart[c * UT + mt];
+          a.den[tok0 + (size_t)t0 + mt] = dn;
+        }
+      }
+      // ---- m <- g^Lt m + Q^T w (p.m of this tile was taken before) ----
+      for (int d = tid - HT; d < D; d += HT) {
+        float acc = 0.f;
+        for (int tau = 0; tau < UT; ++tau) acc += wS[tau] * (float)Qs[tau * L::LDD + d];
+        mst[d] = gL * mst[d] + acc;
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (!OUT) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int cb = rw + NOWN * b;
+      const bool own = sRole ? (b < SB && cb < DT) : (b < CB && cb < ET);
+      float* dst = sRole ? a.S + sidx * D * D : a.C + sidx * D * E;
+      const int ld = sRole ? D : E;
+      if (own) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[(size_t)(16 * t + 4 * lg4 + j) * ld + 16 * cb + lr] = St[b][t][j];
+      }
+    }
+    for (int i = tid; i < D; i += NTHR) a.m[sidx * D + i] = mst[i];
+  }
+}
+
+// Exclusive decayed running sum over the n segments of each unit, in place:
+// X[s] <- sum_{r<s} a^(s-1-r) X[r], a = g^chunk (the unmasked combine).
+// X is [units, n, F]; each thread owns four consecutive floats.
+__global__ __launch_bounds__(256) void unmasked_scan_kernel(float* X, int F, int n, const float* gamma,
+                                                            int H, int chunk) {
+  const int unit = blockIdx.y;
+  const int e4 = blockIdx.x * 256 + threadIdx.x;
+  if (4 * e4 >= F) return;
+  const float g = gamma ? gamma[unit % H] : 1.f;
+  const float sa = gpow(g, log2f(g), chunk);
+  f32x4 run = zero4();
+  f32x4* p = reinterpret_cast<f32x4*>(X + (size_t)unit * n * F) + e4;
+  const int step = F / 4;
+  for (int s = 0; s < n; ++s) {
+    const f32x4 x = p[(size_t)s * step];
+    p[(size_t)s * step] = run;
+    run = run * sa + x;
+  }
+}
+
+template <int D, int E>
+struct UWaves {
+  static constexpr int value = (D == 128 || E == 128) ? 8 : 4;
+};
+
+template <int MODE>
+hipError_t launch_unmasked_mode(int dtype, int d, int dv, int units, const ChunkArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)units * (unsigned)a.nspan);
+#define HLA_CASE(T, D, E)                                                                      \
+  if (d == D && dv == E) {                                                                     \
+    constexpr int NW = UWaves<D, E>::value;                                                    \
+    hipLaunchKernelGGL((unmasked_kernel<T, D, E, MODE, NW>), grid, dim3(64 * NW), 0, s, a);    \
+    return hipGetLastError();                                                                  \
+  }
+  if (dtype == 1) {
+    HLA_CASE(__bf16, 16, 16) HLA_CASE(__bf16, 16, 32) HLA_CASE(__bf16, 32, 16)
+    HLA_CASE(__bf16, 32, 32) HLA_CASE(__bf16, 32, 64) HLA_CASE(__bf16, 64, 32)
+    HLA_CASE(__bf16, 64, 64) HLA_CASE(__bf16, 64, 128) HLA_CASE(__bf16, 128, 64)
+    HLA_CASE(__bf16, 128, 128)
+  } else {
+    HLA_CASE(float, 16, 16) HLA_CASE(float, 16, 32) HLA_CASE(float, 32, 16)
+    HLA_CASE(float, 32, 32) HLA_CASE(float, 32, 64) HLA_CASE(float, 64, 32)
+    HLA_CASE(float, 64, 64)
+  }
+#undef HLA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_unmasked_summaries(int dtype, int d, int dv, int units, const ChunkArgs& a,
+                                     hipStream_t s) {
+  return launch_unmasked_mode<U_SUMMARY>(dtype, d, dv, units, a, s);
+}
+
+hipError_t launch_unmasked_outputs(int dtype, int d, int dv, int units, const ChunkArgs& a,
+                                   hipStream_t s) {
+  return launch_unmasked_mode<U_OUTPUT>(dtype, d, dv, units, a, s);
+}
+
+hipError_t launch_unmasked_scan(const ChunkArgs& a, int units, int d, int dv, hipStream_t s) {
+  float* fields[3] = {a.S, a.C, a.m};
+  const int F[3] = {d * d, d * dv, d};
+  for (int i = 0; i < 3; ++i) {
+    const dim3 grid((unsigned)((F[i] / 4 + 255) / 256), (unsigned)units);
+    hipLaunchKernelGGL(unmasked_scan_kernel, grid, dim3(256), 0, s, fields[i], F[i], a.nspan,
+                       a.gamma, a.H, a.chunk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace hla

@@ -25,7 +25,7 @@ EXPORTS = (
     "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
     "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
-    "hla_fwd", "hla_decode_step",
+    "hla_fwd", "hla_decode_step", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
 )
 
 
@@ -76,8 +76,11 @@ def lib():
     L.hla_fwd_workspace_bytes.argtypes, L.hla_fwd_workspace_bytes.restype = [pp], sz
     L.hla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, ps, vp, sz, vp]
     L.hla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, ps, vp, vp, vp]
+    L.hla_unmasked_fwd_workspace_bytes.argtypes = [pp]
+    L.hla_unmasked_fwd_workspace_bytes.restype = sz
+    L.hla_unmasked_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
-                 "hla_fwd", "hla_decode_step"):
+                 "hla_fwd", "hla_decode_step", "hla_unmasked_fwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -249,6 +252,28 @@ def fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False, wa
                          ctypes.byref(fs) if fs is not None else None, _ptr(workspace),
                          ctypes.c_size_t(workspace.numel()), _stream()), "hla_fwd")
     return o, den, final
+
+
+def unmasked_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False,
+                 workspace=None, o=None, den=None):
+    """The unmasked variant o = q^T S C (segment moments, scan, outputs on one
+    stream): (o [B, H, T, dv] fp32, den [B, H, T] or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    if den is None and want_den:
+        den = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = lib().hla_unmasked_fwd_workspace_bytes(ctypes.byref(p))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().hla_unmasked_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                                  _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()),
+           "hla_unmasked_fwd")
+    return o, den
 
 
 def decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, den=None):

@@ -200,6 +200,26 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The unmasked second-order variant (method section 1: the plain product
+ * S^K_t C^QV_t, whose future terms -- key index after value index -- the
+ * cross summaries G, h remove in the masked operator; key contribution 2:
+ * the associative operators of the unmasked setting, with and without decay;
+ * method section 4: segment summaries joined by an exclusive scan):
+ *   num_t = q_t^T S_t C_t = sum_{i<=t} sum_{j<=t} g^((t-i)+(t-j)) (q_t.k_i)(k_i.q_j) v_j,
+ *   den_t = q_t^T S_t m_t,
+ * with S, C, m decayed as above and o = num or num / (den + eps).  The
+ * segment combine has no cross term (S = a S_A + S_B, likewise C and m).
+ * Segment moments, the exclusive scan and the outputs run on one stream
+ * with the moments kept in `workspace`: hla_unmasked_fwd_workspace_bytes(p)
+ * bytes = B*H*n*(d*d + d*dv + d) floats, which must not overlap q, k, v, o
+ * or den.  Problem fields, o, den and errors as for hla_fwd.
+ */
+size_t hla_unmasked_fwd_workspace_bytes(const hla_problem* p);
+hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                            float* o, float* den, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * One streaming decode step (method section 1: the online update of the
  * prefix state; results and claims: constant work and memory per token).
  * For each of the N*H units: applies one token (q, k [N, H, d], v [N, H, dv]

@@ -196,6 +196,32 @@ def test_valid_call_without_device_returns_hip_error(L):
                              ctypes.byref(state()), O, None, None) == HIP
 
 
+def test_unmasked_sizes_and_checks(L):
+    p = problem()                       # B2 H3 T256 d64 dv64 chunk 64: n = 4
+    per = 64 * 64 + 64 * 64 + 64
+    assert L.hla_unmasked_fwd_workspace_bytes(ctypes.byref(p)) == 2 * 3 * 4 * per * 4
+    assert L.hla_unmasked_fwd_workspace_bytes(ctypes.byref(problem(T=10))) == 0
+    need = 2 * 3 * 4 * per * 4
+    W = 0x7000000000
+    f = L.hla_unmasked_fwd
+    assert f(ctypes.byref(problem(T=10)), Q, K, V, O, None, W, need, None) == SHAPE
+    assert f(ctypes.byref(problem(d=48)), Q, K, V, O, None, W, need, None) == UNSUP
+    assert f(ctypes.byref(problem(in_dtype=hla.HLA_F32, d=128, dv=128)), Q, K, V, O, None, W,
+             1 << 40, None) == UNSUP
+    assert f(ctypes.byref(p), None, K, V, O, None, W, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, None, None, W, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, O, None, None, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, O, None, W, need - 4, None) == WS
+    assert f(ctypes.byref(p), Q, K, V, O + 4, None, W, need, None) == MISAL
+    assert f(ctypes.byref(p), Q, K, V, O, None, W + 8, need, None) == MISAL
+    assert f(ctypes.byref(p), Q, K, V, Q + 64, None, W, need, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, O, None, K, need, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, O, O, W, need, None) == ALIAS
+    assert f(ctypes.byref(problem(B=0)), None, None, None, None, None, None, 0, None) == OK
+    if no_gpu():
+        assert f(ctypes.byref(p), Q, K, V, O, None, W, need, None) == HIP
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 64, 16)
