@@ -5,7 +5,8 @@
 A step is one pass of the chunk-parallel forward over the whole workload:
 segment summaries -> exclusive Blelloch scan -> outputs (three C-ABI calls
 on one stream; inputs already resident in HBM).  The decode workload times
-one streaming decode step for every (sequence, head).  Prints one JSON line.
+one streaming decode step for every (sequence, head); the unmasked workload
+times the unmasked variant's three calls.  Prints one JSON line.
 """
 
 import argparse
@@ -31,6 +32,15 @@ def credited_flops_per_token(c, d, dv):
     f = (c * d * (d + 1) + 2 * c * d * dv + 2 * c * c * d + c * (c - 1) * dv + 2 * c * d * dv
          + 2 * d * d * dv + 2 * c * d * d + c * (c + 1) * d + c * (c + 1) * (c + 2) / 3
          + c * (c + 1) * dv + min(2 * d * d * dv + 2 * c * d * dv, 4 * c * d * dv))
+    return f / c
+
+
+def credited_flops_per_token_unmasked(c, d, dv):
+    """Credited flops per token of the unmasked variant at chunk length c:
+    K^T K (symmetric) and Q^T V, Q S_P, the lower triangles of Q K^T, A' K,
+    P Q^T and B V, and P C_P; the combine has no cross term."""
+    f = (c * d * (d + 1) + 2 * c * d * dv + 2 * c * d * d + 3 * c * (c + 1) * d
+         + c * (c + 1) * dv + 2 * c * d * dv)
     return f / c
 
 
@@ -217,6 +227,112 @@ def bench_fwd(args, torch, np):
     return out
 
 
+UNMASKED_WORKLOADS = {"unmasked_decay_bf16_b4h16t16384d128": "fwd_decay_bf16_b4h16t16384d128"}
+
+
+def cpu_baseline_unmasked(inp, ntok):
+    from threadpoolctl import threadpool_limits
+    from oracle import hla_oracle as O
+    uq, uk, uv, ug = inp.units()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.serial_unmasked(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
+        dt = time.perf_counter() - t0
+    U = uq.shape[0]
+    return {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 serial recurrence of the unmasked variant, all {U} (batch, head) "
+                      f"units, first {ntok} of {uq.shape[1]} tokens ({dt:.1f} s)",
+            "seconds": round(dt, 2)}
+
+
+def bench_unmasked(args, torch, np):
+    """The unmasked variant on the inputs of a forward workload: segment
+    moments -> exclusive scan -> outputs (three C-ABI calls on one stream)."""
+    import ctypes
+    from causal_prefix_scan_amd import hla, synth
+    cfg = dict(synth.FWD_WORKLOADS[UNMASKED_WORKLOADS[args.workload]])
+    if args.chunk:
+        cfg["chunk"] = args.chunk
+    B, H, T, d, dv, chunk = (cfg[x] for x in ("B", "H", "T", "d", "dv", "chunk"))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"],
+                                k_l2norm=cfg["k_l2norm"], decay=cfg["decay"])
+    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
+    n = T // chunk
+    mo = hla.alloc_moments((B, H, n), d, dv, "cuda")
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
+    L = hla.lib()
+    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
+    st = hla._state_struct(mo)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        r1 = L.hla_unmasked_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
+        if ev:
+            ev[1].record(stream)
+        r2 = L.hla_unmasked_scan(ctypes.byref(p), ctypes.byref(st), sp)
+        if ev:
+            ev[2].record(stream)
+        r3 = L.hla_unmasked_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
+                                   None, sp)
+        if ev:
+            ev[3].record(stream)
+        if r1 or r2 or r3:
+            raise RuntimeError(f"HLA call failed: {r1} {r2} {r3}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
+    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    tokens = B * H * T
+    value = tokens / (step_ms / 1e3)
+    U = B * H
+    mom_bytes = U * n * (d * d + d * dv + d) * 4
+    io_bytes = tokens * (2 * d + dv) * 2
+    kernels = {
+        "hla_unmasked_chunk_summaries": dict(ms=ms[0], bytes=io_bytes + mom_bytes),
+        "hla_unmasked_scan": dict(ms=ms[1], bytes=2 * mom_bytes),
+        "hla_unmasked_output": dict(ms=ms[2], bytes=io_bytes + mom_bytes + tokens * dv * 4),
+    }
+    dom = max(kernels, key=lambda kname: kernels[kname]["ms"])
+    kd = kernels[dom]
+    achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
+    f_tok = credited_flops_per_token_unmasked(64, d, dv)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
+                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
+                   "path": "hla_unmasked_chunk_summaries + hla_unmasked_scan + hla_unmasked_output"},
+        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
+                          "peak_tflops": BF16_PEAK_TFLOPS,
+                          "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
+                     "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_unmasked(inp, min(args.cpu_tokens, T))
+    return out
+
+
 def bench_decode(args, torch, np):
     from causal_prefix_scan_amd import hla, synth
     name, cfg = synth.DECODE_WORKLOAD
@@ -317,6 +433,8 @@ def main():
         out = bench_copy(args, torch)
     elif args.workload.startswith("decode"):
         out = bench_decode(args, torch, np)
+    elif args.workload in UNMASKED_WORKLOADS:
+        out = bench_unmasked(args, torch, np)
     else:
         out = bench_fwd(args, torch, np)
     print(json.dumps(out), flush=True)

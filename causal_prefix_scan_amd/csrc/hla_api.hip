@@ -389,6 +389,107 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
   return HLA_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// S, C, m of `st` (G and h are not used by the unmasked variant) for `count`
+// segments: present, aligned, disjoint from each other and from the inputs.
+hla_status check_moments(const hla_state* st, int64_t count, const Sizes& z,
+                         const void* const* inputs, const size_t* in_bytes, int n_inputs) {
+  if (!st) return HLA_ERR_NULL_POINTER;
+  if (!st->S || !st->C || !st->m) return HLA_ERR_NULL_POINTER;
+  hla_state mo = *st;
+  mo.G = mo.h = nullptr;
+  return check_state(&mo, false, count, z, inputs, in_bytes, n_inputs);
+}
+
+hla_status unmasked_summaries(const hla_problem* p, const void* q, const void* k, const void* v,
+                              const hla_state* st, hipStream_t s) {
+  const Sizes z = sizes_of(p);
+  hla_state mo = *st;
+  mo.G = mo.h = nullptr;
+  const ChunkArgs a = chunk_args(p, q, k, v, &mo, nullptr, nullptr);
+  return from_hip(hla::launch_unmasked_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a, s));
+}
+
+hla_status unmasked_scan(const hla_problem* p, const hla_state* st, hipStream_t s) {
+  const Sizes z = sizes_of(p);
+  hla_state mo = *st;
+  mo.G = mo.h = nullptr;
+  const ChunkArgs a = chunk_args(p, nullptr, nullptr, nullptr, &mo, nullptr, nullptr);
+  return from_hip(hla::launch_unmasked_scan(a, (int)z.units, p->d, p->dv, s));
+}
+
+hla_status unmasked_outputs(const hla_problem* p, const void* q, const void* k, const void* v,
+                            const hla_state* st, float* o, float* den, hipStream_t s) {
+  const Sizes z = sizes_of(p);
+  hla_state mo = *st;
+  mo.G = mo.h = nullptr;
+  const ChunkArgs a = chunk_args(p, q, k, v, &mo, o, den);
+  return from_hip(hla::launch_unmasked_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a, s));
+}
+
+// o and den against the inputs (ins / inb) and each other
+hla_status check_outputs(const Sizes& z, float* o, float* den, const void* const* ins,
+                         const size_t* inb, int n) {
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
+  for (int j = 0; j < n; ++j) {
+    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
+  return HLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hla_status hla_unmasked_chunk_summaries(const hla_problem* p, const void* q, const void* k,
+                                        const void* v, const hla_state* out, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  const Sizes z = sizes_of(p);
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {z.qk_bytes, z.qk_bytes, z.v_bytes};
+  if (hla_status e = check_moments(out, z.units * z.n, z, ins, inb, 3)) return e;
+  if (hla_status e = device_ready()) return e;
+  return unmasked_summaries(p, q, k, v, out, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_unmasked_scan(const hla_problem* p, const hla_state* inout, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_moments(inout, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  if (hla_status e = device_ready()) return e;
+  return unmasked_scan(p, inout, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_unmasked_output(const hla_problem* p, const void* q, const void* k, const void* v,
+                               const hla_state* prefixes, float* o, float* den, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_moments(prefixes, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  const void* ins[6] = {q, k, v, prefixes->S, prefixes->C, prefixes->m};
+  const size_t inb[6] = {z.qk_bytes, z.qk_bytes, z.v_bytes, z.units * z.n * z.S * 4,
+                         z.units * z.n * z.C * 4, z.units * z.n * z.m * 4};
+  if (hla_status e = check_outputs(z, o, den, ins, inb, 6)) return e;
+  if (hla_status e = device_ready()) return e;
+  return unmasked_outputs(p, q, k, v, prefixes, o, den, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
 size_t hla_unmasked_fwd_workspace_bytes(const hla_problem* p) {
   if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
   const Sizes z = sizes_of(p);
@@ -402,7 +503,6 @@ hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, 
   if (empty_problem(p)) return HLA_OK;
   if (hla_status e = check_qkv(q, k, v)) return e;
   if (!o) return HLA_ERR_NULL_POINTER;
-  if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
   const Sizes z = sizes_of(p);
   const size_t need = hla_unmasked_fwd_workspace_bytes(p);
   if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
@@ -410,13 +510,9 @@ hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, 
   if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
   const void* ins[4] = {q, k, v, workspace};
   const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
-  for (int j = 0; j < 4; ++j) {
-    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
-    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
-  }
+  if (hla_status e = check_outputs(z, o, den, ins, inb, 4)) return e;
   for (int j = 0; j < 3; ++j)
     if (overlap(workspace, need, ins[j], inb[j])) return HLA_ERR_ALIASING;
-  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
   if (hla_status e = device_ready()) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t cnt = (size_t)z.units * (size_t)z.n;
@@ -425,12 +521,9 @@ hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, 
   sm.C = sm.S + cnt * z.S;
   sm.m = sm.C + cnt * z.C;
   sm.G = sm.h = nullptr;
-  const ChunkArgs a1 = chunk_args(p, q, k, v, &sm, nullptr, nullptr);
-  if (hla_status e = from_hip(hla::launch_unmasked_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
-    return e;
-  if (hla_status e = from_hip(hla::launch_unmasked_scan(a1, (int)z.units, p->d, p->dv, s))) return e;
-  const ChunkArgs a3 = chunk_args(p, q, k, v, &sm, o, den);
-  return from_hip(hla::launch_unmasked_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
+  if (hla_status e = unmasked_summaries(p, q, k, v, &sm, s)) return e;
+  if (hla_status e = unmasked_scan(p, &sm, s)) return e;
+  return unmasked_outputs(p, q, k, v, &sm, o, den, s);
 } catch (...) {
   return HLA_ERR_HIP;
 }

@@ -25,7 +25,8 @@ EXPORTS = (
     "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
     "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
-    "hla_fwd", "hla_decode_step", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
+    "hla_fwd", "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
+    "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
 )
 
 
@@ -79,8 +80,12 @@ def lib():
     L.hla_unmasked_fwd_workspace_bytes.argtypes = [pp]
     L.hla_unmasked_fwd_workspace_bytes.restype = sz
     L.hla_unmasked_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.hla_unmasked_chunk_summaries.argtypes = [pp, vp, vp, vp, ps, vp]
+    L.hla_unmasked_scan.argtypes = [pp, ps, vp]
+    L.hla_unmasked_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
-                 "hla_fwd", "hla_decode_step", "hla_unmasked_fwd"):
+                 "hla_fwd", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
+                 "hla_unmasked_scan", "hla_unmasked_output"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -252,6 +257,51 @@ def fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False, wa
                          ctypes.byref(fs) if fs is not None else None, _ptr(workspace),
                          ctypes.c_size_t(workspace.numel()), _stream()), "hla_fwd")
     return o, den, final
+
+
+def alloc_moments(lead, d, dv, device):
+    """fp32 S, C, m tensors with leading dims `lead` (the unmasked variant's state)."""
+    torch = _torch()
+    z = lambda *s: torch.zeros(*lead, *s, dtype=torch.float32, device=device)
+    return {"S": z(d, d), "C": z(d, dv), "m": z(d)}
+
+
+def unmasked_chunk_summaries(q, k, v, chunk, gamma=None, out=None):
+    """Segment moments of the unmasked variant [B, H, n, ...] (fp32 dict S, C, m)."""
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma)
+    if out is None:
+        out = alloc_moments((B, H, T // chunk), d, v.shape[3], q.device)
+    st = _state_struct(out)
+    _check(lib().hla_unmasked_chunk_summaries(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                              ctypes.byref(st), _stream()),
+           "hla_unmasked_chunk_summaries")
+    return out
+
+
+def unmasked_scan(moments, q_shape, dv, chunk, dtype_code, gamma=None):
+    """In-place exclusive scan of the unmasked variant's segment moments."""
+    B, H, T, d = q_shape
+    p = Problem(B, H, T, d, dv, int(chunk), dtype_code, 0, 0.0,
+                None if gamma is None else gamma.data_ptr())
+    st = _state_struct(moments)
+    _check(lib().hla_unmasked_scan(ctypes.byref(p), ctypes.byref(st), _stream()), "hla_unmasked_scan")
+
+
+def unmasked_output(q, k, v, prefixes, chunk, gamma=None, normalize=False, eps=0.0, want_den=False):
+    """Outputs of the unmasked variant from the exclusive prefixes: (o, den or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    den = torch.empty(B, H, T, dtype=torch.float32, device=q.device) if want_den else None
+    st = _state_struct(prefixes)
+    _check(lib().hla_unmasked_output(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
+                                     _ptr(o), _ptr(den), _stream()), "hla_unmasked_output")
+    return o, den
 
 
 def unmasked_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False,

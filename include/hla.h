@@ -207,13 +207,27 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
  * method section 4: segment summaries joined by an exclusive scan):
  *   num_t = q_t^T S_t C_t = sum_{i<=t} sum_{j<=t} g^((t-i)+(t-j)) (q_t.k_i)(k_i.q_j) v_j,
  *   den_t = q_t^T S_t m_t,
- * with S, C, m decayed as above and o = num or num / (den + eps).  The
- * segment combine has no cross term (S = a S_A + S_B, likewise C and m).
- * Segment moments, the exclusive scan and the outputs run on one stream
- * with the moments kept in `workspace`: hla_unmasked_fwd_workspace_bytes(p)
- * bytes = B*H*n*(d*d + d*dv + d) floats, which must not overlap q, k, v, o
- * or den.  Problem fields, o, den and errors as for hla_fwd.
+ * with S, C, m decayed as above and o = num or num / (den + eps).  Only the
+ * S, C and m fields of an hla_state are used (G and h are ignored and may be
+ * NULL); problem fields, o, den, errors and layouts are as for the masked
+ * calls of the same name.
+ *
+ * hla_unmasked_chunk_summaries: per segment, the moments the recurrence
+ *   reaches from zero: S = sum_i g^(c-i) k_i k_i^T, C = sum_j g^(c-j) q_j v_j^T,
+ *   m = sum_j g^(c-j) q_j ([B, H, n, ...], must not overlap q, k, v).
+ * hla_unmasked_scan: in place, the exclusive prefixes under the unmasked
+ *   combine S = a S_A + S_B, C = a C_A + C_B, m = a m_A + m_B (a = g^(length
+ *   of B); no cross term): P_s = sum_{r<s} a^(s-1-r) X_r with a = g^chunk.
+ * hla_unmasked_output: o (and den) from those prefixes.
+ * hla_unmasked_fwd: the three on one stream, the moments kept in `workspace`
+ *   (hla_unmasked_fwd_workspace_bytes(p) = B*H*n*(d*d + d*dv + d) floats, not
+ *   overlapping q, k or v).
  */
+hla_status hla_unmasked_chunk_summaries(const hla_problem* p, const void* q, const void* k,
+                                        const void* v, const hla_state* out, void* stream);
+hla_status hla_unmasked_scan(const hla_problem* p, const hla_state* inout, void* stream);
+hla_status hla_unmasked_output(const hla_problem* p, const void* q, const void* k, const void* v,
+                               const hla_state* prefixes, float* o, float* den, void* stream);
 size_t hla_unmasked_fwd_workspace_bytes(const hla_problem* p);
 hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
                             float* o, float* den, void* workspace, size_t workspace_bytes,

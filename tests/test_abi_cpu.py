@@ -218,8 +218,23 @@ def test_unmasked_sizes_and_checks(L):
     assert f(ctypes.byref(p), Q, K, V, O, None, K, need, None) == ALIAS
     assert f(ctypes.byref(p), Q, K, V, O, O, W, need, None) == ALIAS
     assert f(ctypes.byref(problem(B=0)), None, None, None, None, None, None, 0, None) == OK
+    # the three stages: S, C, m required, G and h ignored
+    mo = hla.State(S_BASE, S_BASE + 0x1000000, S_BASE + 0x2000000, None, None)
+    no_m = hla.State(S_BASE, S_BASE + 0x1000000, None, None, None)
+    assert L.hla_unmasked_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(no_m), None) == NULLP
+    assert L.hla_unmasked_chunk_summaries(ctypes.byref(p), Q, K, V, None, None) == NULLP
+    bad = hla.State(Q, S_BASE + 0x1000000, S_BASE + 0x2000000, None, None)
+    assert L.hla_unmasked_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(bad), None) == ALIAS
+    mis = hla.State(S_BASE + 4, S_BASE + 0x1000000, S_BASE + 0x2000000, None, None)
+    assert L.hla_unmasked_scan(ctypes.byref(p), ctypes.byref(mis), None) == MISAL
+    assert L.hla_unmasked_scan(ctypes.byref(problem(chunk=0)), ctypes.byref(mo), None) == SHAPE
+    assert L.hla_unmasked_output(ctypes.byref(p), Q, K, V, ctypes.byref(mo), None, None, None) == NULLP
+    assert L.hla_unmasked_output(ctypes.byref(p), Q, K, V, ctypes.byref(mo), S_BASE, None, None) == ALIAS
     if no_gpu():
         assert f(ctypes.byref(p), Q, K, V, O, None, W, need, None) == HIP
+        assert L.hla_unmasked_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(mo), None) == HIP
+        assert L.hla_unmasked_scan(ctypes.byref(p), ctypes.byref(mo), None) == HIP
+        assert L.hla_unmasked_output(ctypes.byref(p), Q, K, V, ctypes.byref(mo), O, DEN, None) == HIP
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,8 +1,9 @@
 """GPU parity of the unmasked variant (o = q^T S C) against the fp64 oracle.
 
-Calls go through the C ABI (hla_unmasked_fwd via the ctypes binding).  Small
-cases are compared element by element with the oracle's serial recurrence
-(ragged tiles, one or many segments, decay, both dtypes); the full-size
+Calls go through the C ABI (hla_unmasked_fwd and its three stages, via the
+ctypes binding).  Small cases are compared element by element with the
+oracle's serial recurrence (ragged tiles, one or many segments, decay, both
+dtypes), stage by stage for some of them; the full-size
 decayed workload runs in the launch configuration the benchmark times and is
 compared on sampled (batch, head) units.  Tolerances as for the masked
 operator: 1e-4 (fp32 inputs) and 2e-2 (bf16 inputs, fp32 state) on
@@ -74,6 +75,43 @@ def test_unmasked_matches_oracle(gpu, case):
         torch.cuda.synchronize()
         ratio = host(o) / (host(dn)[..., None] + eps)
         assert rel_err(host(on), ratio) <= 1e-5
+
+
+STAGED = [SMALL[1], SMALL[2], SMALL[5], SMALL[10], SMALL[12]]
+
+
+@pytest.mark.parametrize("case", STAGED, ids=[case_id(c) for c in STAGED])
+def test_unmasked_stages_match_oracle(gpu, case):
+    # segment moments, exclusive prefixes and outputs, each against the oracle
+    torch = gpu
+    B, H, T, d, dv, chunk, dt, decay, norm = case
+    say("unmasked stages", case_id(case))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, dt, seed=500 + T, decay=decay)
+    q, k, v, g = to_dev(inp)
+    mo = hla.unmasked_chunk_summaries(q, k, v, chunk, g)
+    torch.cuda.synchronize()
+    uq, uk, uv, ug = inp.units()
+    U, n = B * H, T // chunk
+    tol = 1e-4 if dt == "f32" else 2e-2
+    _, _, pre = O.unmasked_chunk_forward(uq, uk, uv, chunk, ug)
+    for s in range(n):
+        _, _, want = O.serial_unmasked(uq[:, s * chunk:(s + 1) * chunk], uk[:, s * chunk:(s + 1) * chunk],
+                                       uv[:, s * chunk:(s + 1) * chunk], ug)
+        for key in "SCm":
+            got = host(mo[key]).reshape(U, n, *want[key].shape[1:])[:, s]
+            assert rel_err(got, want[key]) <= tol, ("summary", s, key)
+    hla.unmasked_scan(mo, q.shape, dv, chunk, hla.HLA_F32 if dt == "f32" else hla.HLA_BF16, g)
+    torch.cuda.synchronize()
+    for s in range(1, n):
+        for key in "SCm":
+            got = host(mo[key]).reshape(U, n, *pre[s][key].shape[1:])[:, s]
+            assert rel_err(got, pre[s][key]) <= tol, ("prefix", s, key)
+    assert float(np.abs(host(mo["S"]).reshape(U, n, -1)[:, 0]).max()) == 0.0   # P_0 = 0
+    o, dn = hla.unmasked_output(q, k, v, mo, chunk, g, want_den=True)
+    torch.cuda.synchronize()
+    num, den, _ = O.serial_unmasked(uq, uk, uv, ug)
+    assert rel_err(host(o).reshape(num.shape), num) <= tol
+    assert rel_err(host(dn).reshape(den.shape), den) <= tol
 
 
 def test_unmasked_differs_from_masked(gpu):
