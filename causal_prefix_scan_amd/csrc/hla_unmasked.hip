@@ -24,8 +24,12 @@
 // and update S) and C waves (column blocks of C; they produce the matching
 // columns of the output and update C and m).  The state lives in fp32 MFMA
 // accumulators; P goes through LDS (row-major, bf16 for bf16 inputs) for the
-// score tiles and the state term C^T p.  Every phase is separated by a
-// barrier: this kernel favours a plain schedule over overlap.
+// score tiles and the state term C^T p.  Q, K and V are double-buffered by
+// tile parity: the next tile is loaded into registers one tile ahead and
+// staged while the current one is in use, and the C waves apply a tile's C and
+// m updates one tile late, while the S waves form the next tile's P.
+#include <type_traits>
+
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -40,18 +44,21 @@ template <typename T, int D, int E>
 struct ULayout {
   static constexpr int PADT = 16 / (int)sizeof(T);
   static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;   // d zero-padded to one MFMA K step
-  static constexpr int LDD = DP + PADT;   // Qs, Ks, Ps: [tok][d]
-  static constexpr int LDV = E + PADT;    // Vs: [tok][e]
-  static constexpr int LDT = UT + PADT;   // AB, BB: [tok][tok]
+  static constexpr int LDD = DP + PADT;   // Q, K, P: [tok][d]
+  static constexpr int LDV = E + PADT;    // V: [tok][e]
+  static constexpr int LDT = UT + PADT;   // A', B: [tok][tok]
   static constexpr size_t QB = (size_t)UT * LDD * sizeof(T);
-  static constexpr size_t Qs = 0, Ks = QB, Vs = 2 * QB;
-  static constexpr size_t Ps = Vs + (size_t)UT * LDV * sizeof(T);
+  static constexpr size_t VB = (size_t)UT * LDV * sizeof(T);
+  // Q, K, V double-buffered by tile parity: the next tile is staged while the
+  // current one is in use, and the C update of a tile runs one tile late
+  static constexpr size_t Qs = 0, Ks = 2 * QB, Vs = 4 * QB;
+  static constexpr size_t Ps = Vs + 2 * VB;
   static constexpr size_t AB = Ps + QB;
   static constexpr size_t BB = AB + (size_t)UT * LDT * sizeof(T);
   static constexpr size_t TILE_END = BB + (size_t)UT * LDT * sizeof(T);
   static constexpr size_t W = (TILE_END + 15) / 16 * 16;
-  // pw, w1, wS, pm [UT]; bpart [UT/16][UT]; mst [D]
-  static constexpr size_t TOTAL = W + (size_t)(4 * UT + (UT / 16) * UT + D) * 4;
+  // pw, w1, wS[2], pm [UT]; bpart [UT/16][UT]; mst [D]
+  static constexpr size_t TOTAL = W + (size_t)(5 * UT + (UT / 16) * UT + D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -90,16 +97,16 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE == U_OUTPUT;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  T* Qs = reinterpret_cast<T*>(smem + L::Qs);
-  T* Ks = reinterpret_cast<T*>(smem + L::Ks);
-  T* Vs = reinterpret_cast<T*>(smem + L::Vs);
+  auto Qb = [&](int p) { return reinterpret_cast<T*>(smem + L::Qs + p * L::QB); };
+  auto Kb = [&](int p) { return reinterpret_cast<T*>(smem + L::Ks + p * L::QB); };
+  auto Vb = [&](int p) { return reinterpret_cast<T*>(smem + L::Vs + p * L::VB); };
   T* Ps = reinterpret_cast<T*>(smem + L::Ps);
   T* AB = reinterpret_cast<T*>(smem + L::AB);
   T* BB = reinterpret_cast<T*>(smem + L::BB);
   float* pw = reinterpret_cast<float*>(smem + L::W);
   float* w1 = pw + UT;
-  float* wS = w1 + UT;
-  float* pm = wS + UT;
+  auto wSb = [&](int p) { return w1 + UT + p * UT; };
+  float* pm = w1 + 3 * UT;
   float* bpart = pm + UT;
   float* mst = bpart + TR * UT;
 
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
   const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
   const size_t sidx = (size_t)unit * nspan + span;
   const int ntiles = (Lspan + UT - 1) / UT;
+  auto tile_len = [&](int ti) { return (Lspan - ti * UT) < UT ? (Lspan - ti * UT) : UT; };
 
   // zero the tile region once: padding columns [D, DP) of Q, K, P and the
   // upper score tiles are read as zeros and never written
@@ -146,51 +154,156 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
       for (int j = 0; j < 4; ++j)
         St[b][t][j] = (OUT && own) ? src[(size_t)(16 * t + 4 * lg4 + j) * ld + 16 * cb + lr] : 0.f;
   }
-  __syncthreads();
 
-  constexpr int QCH = UT * D / CH, VCH = UT * E / CH, NCH = 2 * QCH + VCH;
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int t0 = ti * UT;
-    const int Lt = (Lspan - t0) < UT ? (Lspan - t0) : UT;
-    const float gL = gpow(g, lgg, Lt);
-    // ---- stage Q, K, V (rows past the segment end as zeros) and w ----
-    for (int c = tid; c < NCH; c += NTHR) {
-      const T* src;
-      T* dst;
-      int cl, W, LD;
-      if (c < QCH) { src = gq; dst = Qs; cl = c; W = D; LD = L::LDD; }
-      else if (c < 2 * QCH) { src = gk; dst = Ks; cl = c - QCH; W = D; LD = L::LDD; }
-      else { src = gv; dst = Vs; cl = c - 2 * QCH; W = E; LD = L::LDV; }
-      const int row = cl / (W / CH), col = (cl % (W / CH)) * CH;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < Lt) x = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
-      *reinterpret_cast<uint4*>(dst + row * LD + col) = x;
+  // ---- tile staging through registers: 16-byte chunks of Q, K and V, each
+  // buffer in a loop of its own (a buffer chosen per lane at run time would
+  // put a table of pointers in scratch memory); rows past the segment end
+  // read as zeros ----
+  constexpr int QCH = UT * D / CH, VCH = UT * E / CH;
+  constexpr int NQ = (QCH + NTHR - 1) / NTHR, NV = (VCH + NTHR - 1) / NTHR;
+  uint4 xq[NQ], xk[NQ], xv[NV];
+  auto load_rows = [&](uint4* x, auto n, const T* src, int W, int nch, int t0, int Lt) {
+#pragma unroll
+    for (int i = 0; i < decltype(n)::value; ++i) {
+      const int c = tid + NTHR * i;
+      const int row = c / (W / CH), col = (c % (W / CH)) * CH;
+      x[i] = make_uint4(0, 0, 0, 0);
+      if (c < nch && row < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
     }
-    if (tid < UT) wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
-    __syncthreads();
+  };
+  auto store_rows = [&](const uint4* x, auto n, T* dst, int W, int LD, int nch) {
+#pragma unroll
+    for (int i = 0; i < decltype(n)::value; ++i) {
+      const int c = tid + NTHR * i;
+      const int row = c / (W / CH), col = (c % (W / CH)) * CH;
+      if (c < nch) *reinterpret_cast<uint4*>(dst + row * LD + col) = x[i];
+    }
+  };
+  using NQc = std::integral_constant<int, NQ>;
+  using NVc = std::integral_constant<int, NV>;
+  auto load_tile = [&](int ti) {
+    const int t0 = ti * UT, Lt = tile_len(ti);
+    load_rows(xq, NQc{}, gq, D, QCH, t0, Lt);
+    load_rows(xk, NQc{}, gk, D, QCH, t0, Lt);
+    load_rows(xv, NVc{}, gv, E, VCH, t0, Lt);
+  };
+  auto store_tile = [&](int p) {
+    store_rows(xq, NQc{}, Qb(p), D, L::LDD, QCH);
+    store_rows(xk, NQc{}, Kb(p), D, L::LDD, QCH);
+    store_rows(xv, NVc{}, Vb(p), E, L::LDV, VCH);
+  };
+  // update weights w_i = g^(Lt-1-i) of tile ti (0 past its end)
+  auto set_weights = [&](int ti) {
+    const int Lt = tile_len(ti);
+    if (tid < UT) wSb(ti & 1)[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+  };
 
-    if constexpr (OUT) {
-      // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) over all waves ----
-      for (int idx = wave; idx < NTRI; idx += NW) {
-        int r, c;
-        utri(idx, r, c);
-        f32x4 acc = zero4();
+  // A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) of the tile in buffers p, over all waves
+  auto a_tiles = [&](int p) {
+    const T* Qx = Qb(p);
+    const T* Kx = Kb(p);
+    for (int idx = wave; idx < NTRI; idx += NW) {
+      int r, c;
+      utri(idx, r, c);
+      f32x4 acc = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < DP; k0 += KS)
-          acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
-        const int tau = 16 * r + lr;   // lane: position tau, keys i = 16 c + 4 lg4 + j
-        f32x4 val;
+      for (int k0 = 0; k0 < DP; k0 += KS)
+        acc = MMT::mma(MMT::ld(Kx, L::LDD, 16 * c, k0, lane), MMT::ld(Qx, L::LDD, 16 * r, k0, lane), acc);
+      const int tau = 16 * r + lr;   // lane: position tau, keys i = 16 c + 4 lg4 + j
+      f32x4 val;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 16 * c + 4 * lg4 + j;
-          val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
-        }
-        ustore4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
+      for (int j = 0; j < 4; ++j) {
+        const int i = 16 * c + 4 * lg4 + j;
+        val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
       }
-      __syncthreads();
+      ustore4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
+    }
+  };
+  // S waves: S[:, own] <- g^Lt S + K^T diag(w) K[:, own] for the tile in buffers p
+  auto s_update = [&](int p, float gL) {
+    const T* Kx = Kb(p);
+    const float* wS = wSb(p);
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+      const int cb = rw + NOWN * b;
+      if (cb < DT) {
+        typename MMT::F bk[NKS];
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) bk[kk] = FR::scale(FR::tr(Kx, L::LDD, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc = St[b][t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Kx, L::LDD, kk * KS, 16 * t, lane), bk[kk], acc);
+          St[b][t] = acc;
+        }
+      }
+    }
+  };
+  // C waves: C[:, own] <- g^Lt C + Q^T diag(w) V[:, own] and m <- g^Lt m + Q^T w
+  // for the tile in buffers p
+  auto c_update = [&](int p, float gL) {
+    const T* Qx = Qb(p);
+    const T* Vx = Vb(p);
+    const float* wS = wSb(p);
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      const int ce = rw + NOWN * b;
+      if (ce < ET) {
+        typename MMT::F bv[NKS];
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vx, L::LDV, kk * KS, 16 * ce, lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 acc = St[b][t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane), bv[kk], acc);
+          St[b][t] = acc;
+        }
+      }
+    }
+    // m: TPD threads per row d, each over UT / TPD tokens in four
+    // independent partial sums, then a fixed-order shuffle reduction
+    constexpr int TPD = HT / D < 1 ? 1 : (HT / D > 16 ? 16 : HT / D);
+    constexpr int TPT = UT / TPD;
+    const int ct = tid - HT;
+    if (ct >= 0 && ct < TPD * D) {
+      const int d = ct / TPD, part = ct % TPD;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int tau = part * TPT + i;
+        ps[i & 3] += wS[tau] * (float)Qx[tau * L::LDD + d];
+      }
+      float acc = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+      for (int off = 1; off < TPD; off *= 2) acc += __shfl_xor(acc, off, 64);
+      if (part == 0) mst[d] = gL * mst[d] + acc;
+    }
+  };
 
-      // ---- S waves: P[:, own] = g^(tau+1) Q S[:, own] + A' K[:, own] -> Ps ----
+  // prologue: tile 0 to LDS, tile 1 to registers (and A' of tile 0)
+  load_tile(0);
+  store_tile(0);
+  set_weights(0);
+  __syncthreads();
+  if (ntiles > 1) load_tile(1);
+  if constexpr (OUT) {
+    a_tiles(0);
+    __syncthreads();
+  }
+
+  float gL_prev = 1.f;
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int p = ti & 1;
+    const int t0 = ti * UT, Lt = tile_len(ti);
+    const float gL = gpow(g, lgg, Lt);
+    if constexpr (OUT) {
+      // ---- S waves: P[:, own] = g^(tau+1) Q S[:, own] + A' K[:, own] -> Ps;
+      //      C waves: C and m updates of the previous tile ----
       if (sRole) {
+        const T* Qx = Qb(p);
+        const T* Kx = Kb(p);
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
           const int cb = rw + NOWN * b;
@@ -200,17 +313,19 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
               f32x4 acc = zero4();
 #pragma unroll
               for (int kk = 0; kk < QSK; ++kk)
-                acc = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), FR::acc_b(St[b], kk), acc);
+                acc = MMT::mma(FR::perm(Qx, L::LDD, 16 * r, kk, lane), FR::acc_b(St[b], kk), acc);
 #pragma unroll
               for (int j = 0; j < 4; ++j) acc[j] *= w1[16 * r + 4 * lg4 + j];
               for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-                acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Ks, L::LDD, k0, 16 * cb, lane), acc);
+                acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Kx, L::LDD, k0, 16 * cb, lane), acc);
               // lane: P[tau = 16 r + 4 lg4 + j][d = 16 cb + lr]
 #pragma unroll
               for (int j = 0; j < 4; ++j) Ps[(16 * r + 4 * lg4 + j) * L::LDD + 16 * cb + lr] = (T)acc[j];
             }
           }
         }
+      } else if (ti > 0) {
+        c_update(p ^ 1, gL_prev);
       }
       __syncthreads();
 
@@ -218,99 +333,77 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
       {
         constexpr int LPR = NTHR / UT;
         const int tau = tid / LPR, part = tid % LPR;
-        float acc = 0.f;
+        float ps[2] = {0.f, 0.f};
 #pragma unroll
         for (int c = part * (D / LPR); c < (part + 1) * (D / LPR); ++c)
-          acc += (float)Ps[tau * L::LDD + c] * mst[c];
+          ps[c & 1] += (float)Ps[tau * L::LDD + c] * mst[c];
+        float acc = ps[0] + ps[1];
 #pragma unroll
         for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
         if (part == 0) pm[tau] = acc;
       }
-      for (int idx = wave; idx < NTRI; idx += NW) {
-        int r, c;
-        utri(idx, r, c);
-        f32x4 acc = zero4();
+      {
+        const T* Qx = Qb(p);
+        for (int idx = wave; idx < NTRI; idx += NW) {
+          int r, c;
+          utri(idx, r, c);
+          f32x4 acc = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < DP; k0 += KS)
-          acc = MMT::mma(MMT::ld(Qs, L::LDD, 16 * c, k0, lane), MMT::ld(Ps, L::LDD, 16 * r, k0, lane), acc);
-        const int tau = 16 * r + lr;   // lane: position tau, values j = 16 c + 4 lg4 + jj
-        f32x4 val;
+          for (int k0 = 0; k0 < DP; k0 += KS)
+            acc = MMT::mma(MMT::ld(Qx, L::LDD, 16 * c, k0, lane), MMT::ld(Ps, L::LDD, 16 * r, k0, lane), acc);
+          const int tau = 16 * r + lr;   // lane: position tau, values j = 16 c + 4 lg4 + jj
+          f32x4 val;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = 16 * c + 4 * lg4 + jj;
-          val[jj] = j <= tau ? acc[jj] * pw[tau - j] : 0.f;
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = 16 * c + 4 * lg4 + jj;
+            val[jj] = j <= tau ? acc[jj] * pw[tau - j] : 0.f;
+          }
+          ustore4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
+          const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+          if (lg4 == 0) bpart[c * UT + tau] = rs;
         }
-        ustore4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
-        const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
-        if (lg4 == 0) bpart[c * UT + tau] = rs;
       }
       __syncthreads();
-    }
 
-    if (sRole) {
-      // ---- S[:, own] <- g^Lt S + K^T diag(w) K[:, own] ----
-#pragma unroll
-      for (int b = 0; b < SB; ++b) {
-        const int cb = rw + NOWN * b;
-        if (cb < DT) {
-          typename MMT::F bk[NKS];
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) bk[kk] = FR::scale(FR::tr(Ks, L::LDD, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            f32x4 acc = St[b][t] * gL;
-#pragma unroll
-            for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bk[kk], acc);
-            St[b][t] = acc;
-          }
-        }
+      // ---- all: the next tile to the other buffers (before this phase's
+      //      output stores, so that waiting for its loads does not wait for
+      //      them); S waves: S update; C waves: O = g^(tau+1) P C + B V ----
+      if (ti + 1 < ntiles) {
+        store_tile(p ^ 1);
+        set_weights(ti + 1);
       }
-    } else {
+      if (sRole) {
+        s_update(p, gL);
+      } else {
+        const T* Vx = Vb(p);
+        float* go = a.o + (tok0 + (size_t)t0) * E;
 #pragma unroll
-      for (int b = 0; b < CB; ++b) {
-        const int ce = rw + NOWN * b;
-        if (ce < ET) {
-          if constexpr (OUT) {
-            // ---- O[:, own] = g^(tau+1) P C[:, own] + B V[:, own] ----
-            float* go = a.o + (tok0 + (size_t)t0) * E;
+        for (int b = 0; b < CB; ++b) {
+          const int ce = rw + NOWN * b;
+          if (ce < ET) {
+            // O^T = C^T P^T + V^T B^T (C^T from the accumulators as the A
+            // operand: the A and B layouts are alike), so that a lane holds
+            // four adjacent columns of one token and stores them at once
 #pragma unroll
             for (int r = 0; r < TR; ++r) {
+              const int tau = 16 * r + lr;
               f32x4 acc = zero4();
 #pragma unroll
               for (int kk = 0; kk < QSK; ++kk)
-                acc = MMT::mma(FR::perm(Ps, L::LDD, 16 * r, kk, lane), FR::acc_b(St[b], kk), acc);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[j] *= w1[16 * r + 4 * lg4 + j];
+                acc = MMT::mma(FR::acc_b(St[b], kk), FR::perm(Ps, L::LDD, 16 * r, kk, lane), acc);
+              acc *= w1[tau];
               for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-                acc = MMT::mma(MMT::ld(BB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * ce, lane), acc);
-              // lane: O[tau = 16 r + 4 lg4 + j][e = 16 ce + lr]
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int tau = 16 * r + 4 * lg4 + j;
-                float o = acc[j];
-                if (a.normalize) {
-                  float dn = w1[tau] * pm[tau];
-                  for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
-                  o = o / (dn + a.eps);
-                }
-                if (tau < Lt) go[(size_t)tau * E + 16 * ce + lr] = o;
+                acc = MMT::mma(FR::tr(Vx, L::LDV, k0, 16 * ce, lane), MMT::ld(BB, L::LDT, 16 * r, k0, lane), acc);
+              // lane: O[tau][e = 16 ce + 4 lg4 + j]
+              if (a.normalize) {
+                float dn = w1[tau] * pm[tau];
+                for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
+                acc *= 1.f / (dn + a.eps);
               }
+              if (tau < Lt) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * ce + 4 * lg4) = acc;
             }
           }
-          // ---- C[:, own] <- g^Lt C + Q^T diag(w) V[:, own] ----
-          typename MMT::F bv[NKS];
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ce, lane), wS, kk * KS, lane);
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            f32x4 acc = St[b][t] * gL;
-#pragma unroll
-            for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qs, L::LDD, kk * KS, 16 * t, lane), bv[kk], acc);
-            St[b][t] = acc;
-          }
         }
-      }
-      if constexpr (OUT) {
         const int mt = tid - HT;
         if (a.den != nullptr && mt < Lt) {
           float dn = w1[mt] * pm[mt];
@@ -318,14 +411,24 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
           a.den[tok0 + (size_t)t0 + mt] = dn;
         }
       }
-      // ---- m <- g^Lt m + Q^T w (p.m of this tile was taken before) ----
-      for (int d = tid - HT; d < D; d += HT) {
-        float acc = 0.f;
-        for (int tau = 0; tau < UT; ++tau) acc += wS[tau] * (float)Qs[tau * L::LDD + d];
-        mst[d] = gL * mst[d] + acc;
+      __syncthreads();
+      // ---- A' of the next tile; the tile after it to registers ----
+      if (ti + 1 < ntiles) {
+        if (ti + 2 < ntiles) load_tile(ti + 2);
+        a_tiles(p ^ 1);
+        __syncthreads();
       }
+    } else {
+      if (sRole) s_update(p, gL);
+      else c_update(p, gL);
+      if (ti + 1 < ntiles) {
+        store_tile(p ^ 1);
+        set_weights(ti + 1);
+      }
+      __syncthreads();
+      if (ti + 2 < ntiles) load_tile(ti + 2);
     }
-    __syncthreads();
+    gL_prev = gL;
   }
 
   if constexpr (!OUT) {
