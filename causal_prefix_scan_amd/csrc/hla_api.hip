@@ -528,6 +528,46 @@ hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, 
   return HLA_ERR_HIP;
 }
 
+hla_status hla_unmasked_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                                    int32_t normalize, float eps, const float* gamma,
+                                    const void* q, const void* k, const void* v,
+                                    const hla_state* state, float* o, float* den,
+                                    void* stream) try {
+  if (N < 0 || H < 0) return HLA_ERR_BAD_SHAPE;
+  if (in_dtype != HLA_F32 && in_dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (normalize != 0 && normalize != 1) return HLA_ERR_BAD_VALUE;
+  if (!std::isfinite(eps)) return HLA_ERR_BAD_VALUE;
+  if (!head_ok(d) || !head_ok(dv) || d > 2 * dv || dv > 2 * d) return HLA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)N * H;
+  if (units > kMaxGrid) return HLA_ERR_BAD_VALUE;
+  if (units == 0) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den)) || (gamma && !aligned16(gamma)))
+    return HLA_ERR_MISALIGNED;
+  Sizes z;
+  z.S = (size_t)d * d; z.C = (size_t)d * dv; z.m = (size_t)d;
+  const size_t es = dtype_size(in_dtype);
+  const size_t uu = (size_t)units;
+  const void* ins[5] = {q, k, v, o, den};
+  const size_t inb[5] = {uu * d * es, uu * d * es, uu * dv * es, uu * dv * 4, den ? uu * 4 : 0};
+  if (hla_status e = check_moments(state, units, z, ins, inb, 5)) return e;
+  for (int j = 0; j < 3; ++j) {
+    if (overlap(o, inb[3], ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, inb[4], ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, inb[3], den, inb[4])) return HLA_ERR_ALIASING;
+  if (hla_status e = device_ready()) return e;
+  DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.gamma = gamma;
+  a.S = state->S; a.C = state->C; a.m = state->m; a.G = nullptr; a.h = nullptr;
+  a.o = o; a.den = den; a.H = H; a.normalize = normalize; a.eps = eps;
+  return from_hip(hla::launch_unmasked_decode(in_dtype, d, dv, (int)units, a,
+                                              static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
 hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
                            int32_t normalize, float eps, const float* gamma, const void* q,
                            const void* k, const void* v, const hla_state* state, float* o,

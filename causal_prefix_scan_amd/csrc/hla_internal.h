@@ -82,6 +82,9 @@ hipError_t launch_unmasked_summaries(int dtype, int d, int dv, int units, const 
 hipError_t launch_unmasked_scan(const ChunkArgs& a, int units, int d, int dv, hipStream_t s);
 hipError_t launch_unmasked_outputs(int dtype, int d, int dv, int units, const ChunkArgs& a,
                                    hipStream_t s);
+// One decode step of the unmasked variant (S, C, m of `a`; G and h unused).
+hipError_t launch_unmasked_decode(int dtype, int d, int dv, int units, const DecodeArgs& a,
+                                  hipStream_t s);
 
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 

@@ -469,6 +469,104 @@ __global__ __launch_bounds__(256) void unmasked_scan_kernel(float* X, int F, int
   }
 }
 
+// One decode step of the unmasked variant per unit (one workgroup of UDEC
+// threads): S' = g S + k k^T, C' = g C + q v^T, m' = g m + q, a = S' q,
+// num = C'^T a, den = a.m'.  Every state element is read once and written
+// once (16-byte non-temporal accesses); the reductions go through shuffles
+// and LDS.
+constexpr int UDEC = 512;
+
+template <typename T, int D, int E>
+__global__ __launch_bounds__(UDEC) void unmasked_decode_kernel(DecodeArgs a) {
+  constexpr int CPR_S = D / 4, RP_S = UDEC / CPR_S, NP_S = (D + RP_S - 1) / RP_S;
+  constexpr int CPR_C = E / 4, RP_C = UDEC / CPR_C, NP_C = (D + RP_C - 1) / RP_C;
+  constexpr int NRG = RP_C < D ? RP_C : D;   // row groups that hold C rows
+  __shared__ __attribute__((aligned(16))) float sq[D], sk[D], sv[E], sm[D], aval[D];
+  __shared__ __attribute__((aligned(16))) float rz[NRG][E];
+  __shared__ float sden;
+
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  f32x4* S = reinterpret_cast<f32x4*>(a.S + (size_t)unit * D * D);
+  f32x4* C = reinterpret_cast<f32x4*>(a.C + (size_t)unit * D * E);
+  float* m = a.m + (size_t)unit * D;
+  const int ccS = tid % CPR_S, rgS = tid / CPR_S;
+  const int ccC = tid % CPR_C, rgC = tid / CPR_C;
+  f32x4 rS[NP_S], rC[NP_C];
+#pragma unroll
+  for (int i = 0; i < NP_S; ++i) {
+    const int d = rgS + RP_S * i;
+    if (d < D) rS[i] = __builtin_nontemporal_load(S + d * CPR_S + ccS);
+  }
+#pragma unroll
+  for (int i = 0; i < NP_C; ++i) {
+    const int d = rgC + RP_C * i;
+    if (d < D) rC[i] = __builtin_nontemporal_load(C + d * CPR_C + ccC);
+  }
+  const T* q = reinterpret_cast<const T*>(a.q) + (size_t)unit * D;
+  const T* k = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
+  const T* v = reinterpret_cast<const T*>(a.v) + (size_t)unit * E;
+  for (int t = tid; t < D; t += UDEC) {
+    sq[t] = (float)q[t];
+    sk[t] = (float)k[t];
+    sm[t] = m[t];
+  }
+  for (int t = tid; t < E; t += UDEC) sv[t] = (float)v[t];
+  __syncthreads();
+
+  // S' = g S + k k^T; a = S' q (row sums over the CPR_S lanes of a row)
+  {
+    const f32x4 q4 = *reinterpret_cast<const f32x4*>(sq + 4 * ccS);
+    const f32x4 k4 = *reinterpret_cast<const f32x4*>(sk + 4 * ccS);
+#pragma unroll
+    for (int i = 0; i < NP_S; ++i) {
+      const int d = rgS + RP_S * i;
+      float ap = 0.f;
+      if (d < D) {
+        const f32x4 sn = rS[i] * g + k4 * sk[d];
+        __builtin_nontemporal_store(sn, S + d * CPR_S + ccS);
+        ap = sn[0] * q4[0] + sn[1] * q4[1] + sn[2] * q4[2] + sn[3] * q4[3];
+      }
+#pragma unroll
+      for (int off = 1; off < CPR_S; off *= 2) ap += __shfl_xor(ap, off, 64);
+      if (d < D && ccS == 0) aval[d] = ap;
+    }
+  }
+  __syncthreads();
+
+  // C' = g C + q v^T; partial z = C'^T a over this thread's rows; m' and den
+  {
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(sv + 4 * ccC);
+    f32x4 pz = zero4();
+#pragma unroll
+    for (int i = 0; i < NP_C; ++i) {
+      const int d = rgC + RP_C * i;
+      if (d < D) {
+        const f32x4 cn = rC[i] * g + v4 * sq[d];
+        __builtin_nontemporal_store(cn, C + d * CPR_C + ccC);
+        pz += cn * aval[d];
+      }
+    }
+    if (rgC < NRG) *reinterpret_cast<f32x4*>(&rz[rgC][4 * ccC]) = pz;
+  }
+  for (int t = tid; t < D; t += UDEC) m[t] = g * sm[t] + sq[t];
+  if (tid < 64) {
+    float dn = 0.f;
+    for (int d = tid; d < D; d += 64) dn += aval[d] * (g * sm[d] + sq[d]);
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) dn += __shfl_xor(dn, off, 64);
+    if (tid == 0) sden = dn;
+  }
+  __syncthreads();
+  const float den = sden;
+  for (int e = tid; e < E; e += UDEC) {
+    float z = 0.f;
+    for (int r = 0; r < NRG; ++r) z += rz[r][e];
+    a.o[(size_t)unit * E + e] = a.normalize ? z / (den + a.eps) : z;
+  }
+  if (a.den != nullptr && tid == 0) a.den[unit] = den;
+}
+
 template <int D, int E>
 struct UWaves {
   static constexpr int value = (D == 128 || E == 128) ? 8 : 4;
@@ -507,6 +605,28 @@ hipError_t launch_unmasked_summaries(int dtype, int d, int dv, int units, const 
 hipError_t launch_unmasked_outputs(int dtype, int d, int dv, int units, const ChunkArgs& a,
                                    hipStream_t s) {
   return launch_unmasked_mode<U_OUTPUT>(dtype, d, dv, units, a, s);
+}
+
+hipError_t launch_unmasked_decode(int dtype, int d, int dv, int units, const DecodeArgs& a,
+                                  hipStream_t s) {
+#define HLA_CASE(T, D, E)                                                                       \
+  if (d == D && dv == E) {                                                                      \
+    hipLaunchKernelGGL((unmasked_decode_kernel<T, D, E>), dim3(units), dim3(UDEC), 0, s, a);    \
+    return hipGetLastError();                                                                   \
+  }
+  if (dtype == 1) {
+    HLA_CASE(__bf16, 16, 16) HLA_CASE(__bf16, 16, 32) HLA_CASE(__bf16, 32, 16)
+    HLA_CASE(__bf16, 32, 32) HLA_CASE(__bf16, 32, 64) HLA_CASE(__bf16, 64, 32)
+    HLA_CASE(__bf16, 64, 64) HLA_CASE(__bf16, 64, 128) HLA_CASE(__bf16, 128, 64)
+    HLA_CASE(__bf16, 128, 128)
+  } else {
+    HLA_CASE(float, 16, 16) HLA_CASE(float, 16, 32) HLA_CASE(float, 32, 16)
+    HLA_CASE(float, 32, 32) HLA_CASE(float, 32, 64) HLA_CASE(float, 64, 32)
+    HLA_CASE(float, 64, 64) HLA_CASE(float, 64, 128) HLA_CASE(float, 128, 64)
+    HLA_CASE(float, 128, 128)
+  }
+#undef HLA_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_unmasked_scan(const ChunkArgs& a, int units, int d, int dv, hipStream_t s) {

@@ -27,6 +27,7 @@ EXPORTS = (
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
     "hla_fwd", "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
     "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
+    "hla_unmasked_decode_step",
 )
 
 
@@ -83,9 +84,10 @@ def lib():
     L.hla_unmasked_chunk_summaries.argtypes = [pp, vp, vp, vp, ps, vp]
     L.hla_unmasked_scan.argtypes = [pp, ps, vp]
     L.hla_unmasked_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
+    L.hla_unmasked_decode_step.argtypes = L.hla_decode_step.argtypes
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
                  "hla_fwd", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
-                 "hla_unmasked_scan", "hla_unmasked_output"):
+                 "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -339,4 +341,21 @@ def decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, de
     _check(lib().hla_decode_step(N, H, d, dv, _dtype_code(q), int(bool(normalize)), float(eps),
                                  _ptr(gamma), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
                                  _ptr(o), _ptr(den), _stream()), "hla_decode_step")
+    return o, den
+
+
+def unmasked_decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, den=None):
+    """One decode step of the unmasked variant; q, k [N, H, d], v [N, H, dv];
+    `state` (dict with S, C, m) is updated in place.  Returns (o, den or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    N, H, d = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=torch.float32, device=q.device)
+    st = _state_struct(state)
+    _check(lib().hla_unmasked_decode_step(N, H, d, dv, _dtype_code(q), int(bool(normalize)),
+                                          float(eps), _ptr(gamma), _ptr(q), _ptr(k), _ptr(v),
+                                          ctypes.byref(st), _ptr(o), _ptr(den), _stream()),
+           "hla_unmasked_decode_step")
     return o, den

@@ -222,6 +222,11 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
  * hla_unmasked_fwd: the three on one stream, the moments kept in `workspace`
  *   (hla_unmasked_fwd_workspace_bytes(p) = B*H*n*(d*d + d*dv + d) floats, not
  *   overlapping q, k or v).
+ * hla_unmasked_decode_step: one token per unit applied to the state S, C, m
+ *   ([N, H, ...] fp32, in place; results and claims: constant work per
+ *   token), o = C'^T S' q (or divided by q^T S' m' + eps), den optional;
+ *   arguments and errors as for hla_decode_step.  The state after a prefix
+ *   is the moments hla_unmasked_chunk_summaries writes with chunk = T.
  */
 hla_status hla_unmasked_chunk_summaries(const hla_problem* p, const void* q, const void* k,
                                         const void* v, const hla_state* out, void* stream);
@@ -232,6 +237,10 @@ size_t hla_unmasked_fwd_workspace_bytes(const hla_problem* p);
 hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
                             float* o, float* den, void* workspace, size_t workspace_bytes,
                             void* stream);
+hla_status hla_unmasked_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                                    int32_t normalize, float eps, const float* gamma,
+                                    const void* q, const void* k, const void* v,
+                                    const hla_state* state, float* o, float* den, void* stream);
 
 /*
  * One streaming decode step (method section 1: the online update of the

@@ -237,6 +237,24 @@ def test_unmasked_sizes_and_checks(L):
         assert L.hla_unmasked_output(ctypes.byref(p), Q, K, V, ctypes.byref(mo), O, DEN, None) == HIP
 
 
+def test_unmasked_decode_validation(L):
+    f = L.hla_unmasked_decode_step
+    mo = hla.State(S_BASE, S_BASE + 0x1000000, S_BASE + 0x2000000, None, None)
+    no_c = hla.State(S_BASE, None, S_BASE + 0x2000000, None, None)
+    assert f(-1, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(mo), O, None, None) == SHAPE
+    assert f(2, 2, 64, 64, 7, 0, 0.0, None, Q, K, V, ctypes.byref(mo), O, None, None) == DTYPE
+    assert f(2, 2, 48, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(mo), O, None, None) == UNSUP
+    assert f(2, 2, 64, 64, hla.HLA_BF16, 2, 0.0, None, Q, K, V, ctypes.byref(mo), O, None, None) == VALUE
+    assert f(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(no_c), O, None, None) == NULLP
+    assert f(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(mo), None, None, None) == NULLP
+    assert f(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, GAM + 4, Q, K, V, ctypes.byref(mo), O, None, None) == MISAL
+    assert f(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(mo), Q, None, None) == ALIAS
+    assert f(0, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, None, None, None, None, None, None, None) == OK
+    if no_gpu():
+        assert f(2, 2, 64, 64, hla.HLA_BF16, 1, 1e-6, None, Q, K, V, ctypes.byref(mo), O, DEN,
+                 None) == HIP
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 64, 16)
