@@ -27,7 +27,10 @@
 // score tiles and the state term C^T p.  Q, K and V are double-buffered by
 // tile parity: the next tile is loaded into registers one tile ahead and
 // staged while the current one is in use, and the C waves apply a tile's C and
-// m updates one tile late, while the S waves form the next tile's P.
+// m updates one tile late, while the S waves form the next tile's P.  Three
+// barriers per tile in the output kernel: [P | C, m updates of the previous
+// tile] -> [p.m, B scores, staging of the next tile] -> [S update and the next
+// tile's A' | outputs].
 #include <type_traits>
 
 #include "hla_device.h"
@@ -198,11 +201,12 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
     if (tid < UT) wSb(ti & 1)[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
   };
 
-  // A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) of the tile in buffers p, over all waves
-  auto a_tiles = [&](int p) {
+  // A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) of the tile in buffers p, score
+  // tiles first, first + stride, ... of this wave
+  auto a_tiles = [&](int p, int first, int stride) {
     const T* Qx = Qb(p);
     const T* Kx = Kb(p);
-    for (int idx = wave; idx < NTRI; idx += NW) {
+    for (int idx = first; idx < NTRI; idx += stride) {
       int r, c;
       utri(idx, r, c);
       f32x4 acc = zero4();
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
   __syncthreads();
   if (ntiles > 1) load_tile(1);
   if constexpr (OUT) {
-    a_tiles(0);
+    a_tiles(0, wave, NW);
     __syncthreads();
   }
 
@@ -363,17 +367,21 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
           if (lg4 == 0) bpart[c * UT + tau] = rs;
         }
       }
-      __syncthreads();
-
-      // ---- all: the next tile to the other buffers (before this phase's
-      //      output stores, so that waiting for its loads does not wait for
-      //      them); S waves: S update; C waves: O = g^(tau+1) P C + B V ----
+      // the next tile to the other parity's buffers (their last readers, the
+      // C and m updates of the previous tile, finished before this phase),
+      // then the tile after it to registers
       if (ti + 1 < ntiles) {
         store_tile(p ^ 1);
         set_weights(ti + 1);
+        if (ti + 2 < ntiles) load_tile(ti + 2);
       }
+      __syncthreads();
+
+      // ---- S waves: S update, then A' of the next tile; C waves:
+      //      O = g^(tau+1) P C + B V for their columns ----
       if (sRole) {
         s_update(p, gL);
+        if (ti + 1 < ntiles) a_tiles(p ^ 1, rw, NOWN);
       } else {
         const T* Vx = Vb(p);
         float* go = a.o + (tok0 + (size_t)t0) * E;
@@ -412,12 +420,6 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
         }
       }
       __syncthreads();
-      // ---- A' of the next tile; the tile after it to registers ----
-      if (ti + 1 < ntiles) {
-        if (ti + 2 < ntiles) load_tile(ti + 2);
-        a_tiles(p ^ 1);
-        __syncthreads();
-      }
     } else {
       if (sRole) s_update(p, gL);
       else c_update(p, gL);
