@@ -97,6 +97,8 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
   constexpr int QSK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps of a d-contraction
   constexpr int NOWN = NW / 2, HT = NTHR / 2;
   constexpr int SB = (DT + NOWN - 1) / NOWN, CB = (ET + NOWN - 1) / NOWN;
+  // every block index is in range when the blocks divide evenly over a role
+  constexpr bool SFULL = DT % NOWN == 0, CFULL = ET % NOWN == 0;
   constexpr bool OUT = MODE == U_OUTPUT;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
@@ -227,21 +229,26 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
   auto s_update = [&](int p, float gL) {
     const T* Kx = Kb(p);
     const float* wS = wSb(p);
+    typename MMT::F bk[SB][NKS];
 #pragma unroll
-    for (int b = 0; b < SB; ++b) {
-      const int cb = rw + NOWN * b;
-      if (cb < DT) {
-        typename MMT::F bk[NKS];
+    for (int b = 0; b < SB; ++b)
 #pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) bk[kk] = FR::scale(FR::tr(Kx, L::LDD, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
+      for (int kk = 0; kk < NKS; ++kk)
+        bk[b][kk] = FR::scale(FR::tr(Kx, L::LDD, kk * KS, 16 * ((rw + NOWN * b) % DT), lane), wS, kk * KS, lane);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 acc = St[b][t] * gL;
+    for (int t = 0; t < DT; ++t) {
+      f32x4 acc[SB];
 #pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Kx, L::LDD, kk * KS, 16 * t, lane), bk[kk], acc);
-          St[b][t] = acc;
-        }
+      for (int b = 0; b < SB; ++b) acc[b] = St[b][t] * gL;
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) {
+        const auto ak = FR::tr(Kx, L::LDD, kk * KS, 16 * t, lane);   // shared by the blocks
+#pragma unroll
+        for (int b = 0; b < SB; ++b) acc[b] = MMT::mma(ak, bk[b][kk], acc[b]);
       }
+#pragma unroll
+      for (int b = 0; b < SB; ++b)
+        if (SFULL || rw + NOWN * b < DT) St[b][t] = acc[b];
     }
   };
   // C waves: C[:, own] <- g^Lt C + Q^T diag(w) V[:, own] and m <- g^Lt m + Q^T w
@@ -250,21 +257,26 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
     const T* Qx = Qb(p);
     const T* Vx = Vb(p);
     const float* wS = wSb(p);
+    typename MMT::F bv[CB][NKS];
 #pragma unroll
-    for (int b = 0; b < CB; ++b) {
-      const int ce = rw + NOWN * b;
-      if (ce < ET) {
-        typename MMT::F bv[NKS];
+    for (int b = 0; b < CB; ++b)
 #pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vx, L::LDV, kk * KS, 16 * ce, lane), wS, kk * KS, lane);
+      for (int kk = 0; kk < NKS; ++kk)
+        bv[b][kk] = FR::scale(FR::tr(Vx, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wS, kk * KS, lane);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 acc = St[b][t] * gL;
+    for (int t = 0; t < DT; ++t) {
+      f32x4 acc[CB];
 #pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane), bv[kk], acc);
-          St[b][t] = acc;
-        }
+      for (int b = 0; b < CB; ++b) acc[b] = St[b][t] * gL;
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) {
+        const auto aq = FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane);   // shared by the blocks
+#pragma unroll
+        for (int b = 0; b < CB; ++b) acc[b] = MMT::mma(aq, bv[b][kk], acc[b]);
       }
+#pragma unroll
+      for (int b = 0; b < CB; ++b)
+        if (CFULL || rw + NOWN * b < ET) St[b][t] = acc[b];
     }
     // m: TPD threads per row d, each over UT / TPD tokens in four
     // independent partial sums, then a fixed-order shuffle reduction
@@ -308,23 +320,42 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
       if (sRole) {
         const T* Qx = Qb(p);
         const T* Kx = Kb(p);
+        f32x4 pacc[SB][TR];
 #pragma unroll
-        for (int b = 0; b < SB; ++b) {
-          const int cb = rw + NOWN * b;
-          if (cb < DT) {
+        for (int b = 0; b < SB; ++b)
 #pragma unroll
-            for (int r = 0; r < TR; ++r) {
-              f32x4 acc = zero4();
+          for (int r = 0; r < TR; ++r) pacc[b][r] = zero4();
 #pragma unroll
-              for (int kk = 0; kk < QSK; ++kk)
-                acc = MMT::mma(FR::perm(Qx, L::LDD, 16 * r, kk, lane), FR::acc_b(St[b], kk), acc);
+        for (int kk = 0; kk < QSK; ++kk) {
+          typename MMT::F bs[SB];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) acc[j] *= w1[16 * r + 4 * lg4 + j];
-              for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-                acc = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Kx, L::LDD, k0, 16 * cb, lane), acc);
-              // lane: P[tau = 16 r + 4 lg4 + j][d = 16 cb + lr]
+          for (int b = 0; b < SB; ++b) bs[b] = FR::acc_b(St[b], kk);
 #pragma unroll
-              for (int j = 0; j < 4; ++j) Ps[(16 * r + 4 * lg4 + j) * L::LDD + 16 * cb + lr] = (T)acc[j];
+          for (int r = 0; r < TR; ++r) {
+            const auto aq = FR::perm(Qx, L::LDD, 16 * r, kk, lane);   // shared by the blocks
+#pragma unroll
+            for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+#pragma unroll
+          for (int b = 0; b < SB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pacc[b][r][j] *= w1[16 * r + 4 * lg4 + j];
+          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+            const auto aa = MMT::ld(AB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+            for (int b = 0; b < SB; ++b)
+              pacc[b][r] = MMT::mma(aa, FR::tr(Kx, L::LDD, k0, 16 * ((rw + NOWN * b) % DT), lane), pacc[b][r]);
+          }
+          // lane: P[tau = 16 r + 4 lg4 + j][d = 16 cb + lr]
+#pragma unroll
+          for (int b = 0; b < SB; ++b) {
+            const int cb = rw + NOWN * b;
+            if (SFULL || cb < DT) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) Ps[(16 * r + 4 * lg4 + j) * L::LDD + 16 * cb + lr] = (T)pacc[b][r][j];
             }
           }
         }
@@ -385,31 +416,49 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
       } else {
         const T* Vx = Vb(p);
         float* go = a.o + (tok0 + (size_t)t0) * E;
+        // O^T = C^T P^T + V^T B^T (C^T from the accumulators as the A
+        // operand: the A and B layouts are alike), so that a lane holds four
+        // adjacent columns of one token and stores them at once
+        f32x4 oacc[CB][TR];
 #pragma unroll
-        for (int b = 0; b < CB; ++b) {
-          const int ce = rw + NOWN * b;
-          if (ce < ET) {
-            // O^T = C^T P^T + V^T B^T (C^T from the accumulators as the A
-            // operand: the A and B layouts are alike), so that a lane holds
-            // four adjacent columns of one token and stores them at once
+        for (int b = 0; b < CB; ++b)
 #pragma unroll
-            for (int r = 0; r < TR; ++r) {
-              const int tau = 16 * r + lr;
-              f32x4 acc = zero4();
+          for (int r = 0; r < TR; ++r) oacc[b][r] = zero4();
 #pragma unroll
-              for (int kk = 0; kk < QSK; ++kk)
-                acc = MMT::mma(FR::acc_b(St[b], kk), FR::perm(Ps, L::LDD, 16 * r, kk, lane), acc);
-              acc *= w1[tau];
-              for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-                acc = MMT::mma(FR::tr(Vx, L::LDV, k0, 16 * ce, lane), MMT::ld(BB, L::LDT, 16 * r, k0, lane), acc);
-              // lane: O[tau][e = 16 ce + 4 lg4 + j]
-              if (a.normalize) {
-                float dn = w1[tau] * pm[tau];
-                for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
-                acc *= 1.f / (dn + a.eps);
-              }
-              if (tau < Lt) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * ce + 4 * lg4) = acc;
-            }
+        for (int kk = 0; kk < QSK; ++kk) {
+          typename MMT::F bc[CB];
+#pragma unroll
+          for (int b = 0; b < CB; ++b) bc[b] = FR::acc_b(St[b], kk);
+#pragma unroll
+          for (int r = 0; r < TR; ++r) {
+            const auto bp = FR::perm(Ps, L::LDD, 16 * r, kk, lane);   // shared by the blocks
+#pragma unroll
+            for (int b = 0; b < CB; ++b) oacc[b][r] = MMT::mma(bc[b], bp, oacc[b][r]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+          const int tau = 16 * r + lr;
+#pragma unroll
+          for (int b = 0; b < CB; ++b) oacc[b][r] *= w1[tau];
+          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+            const auto bb = MMT::ld(BB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+            for (int b = 0; b < CB; ++b)
+              oacc[b][r] = MMT::mma(FR::tr(Vx, L::LDV, k0, 16 * ((rw + NOWN * b) % ET), lane), bb, oacc[b][r]);
+          }
+          float scale = 1.f;
+          if (a.normalize) {
+            float dn = w1[tau] * pm[tau];
+            for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
+            scale = 1.f / (dn + a.eps);
+          }
+          // lane: O[tau][e = 16 ce + 4 lg4 + j]
+#pragma unroll
+          for (int b = 0; b < CB; ++b) {
+            const int ce = rw + NOWN * b;
+            if ((CFULL || ce < ET) && tau < Lt)
+              *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * ce + 4 * lg4) = oacc[b][r] * scale;
           }
         }
         const int mt = tid - HT;
