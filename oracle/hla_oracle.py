@@ -58,6 +58,8 @@ __all__ = [
     "normalise", "powers",
     "serial_unmasked", "brute_unmasked", "combine_unmasked",
     "unmasked_chunk_forward",
+    "serial_ahla", "brute_ahla", "ahla_segment_summary", "ahla_identity", "combine_ahla",
+    "ahla_chunk_forward",
 ]
 
 _F = np.float64
@@ -439,6 +441,134 @@ def unmasked_chunk_forward(q, k, v, chunk, gamma=None):
     for c, s in enumerate(range(0, T, chunk)):
         n_, d_, _ = serial_unmasked(q[:, s:s + chunk], k[:, s:s + chunk], v[:, s:s + chunk],
                                     gamma, pre[c])
+        num[:, s:s + chunk] = n_
+        den[:, s:s + chunk] = d_
+    return num, den, pre
+
+
+# ----------------------------------------------------------------------------
+# The asymmetric variant AHLA (method section 2 of the pages): the operator
+# Q (K^T Q)(K^T V), which weights the values along a single path through an
+# intermediate key index, with the streaming summaries P^KV, m^K, E, n and
+# the same linear cost per token.  Readings (not spelled out on the pages):
+#   * causal masking follows the path t -> i -> j back in time:
+#     o_t = sum_{i<=t} sum_{j<=i} (q_t.k_i)(q_i.k_j) v_j, the masked A A V
+#     with A = Q K^T (the symmetric HLA is the masked A A^T V);
+#   * P^KV_t = sum_{j<=t} k_j v_j^T and m^K_t = sum_{j<=t} k_j (inclusive),
+#     E_t = sum_{i<=t} k_i (q_i^T P^KV_i), n_t = sum_{i<=t} k_i (q_i.m^K_i),
+#     o_t = q_t^T E_t, den_t = q_t^T n_t (the same sums with v = 1);
+#   * decay: every prefix moment (P, m, E, n) decays once per token, so the
+#     closed-form weight is gamma^(t-j).
+# Segment combine (A then B, a = gamma^(length of B)), derived from these
+# definitions: P = a P_A + P_B, m = a m_A + m_B, E = a E_A + E_B + a X_B P_A,
+# n = a n_A + n_B + a X_B m_A with X_B = sum_{i in B} k_i q_i^T (no decay
+# weights: the decay of the path through i cancels), X = X_A + X_B.
+# ----------------------------------------------------------------------------
+
+def serial_ahla(q, k, v, gamma=None, state=None):
+    """Serial recurrence of AHLA: for t = 1..T, in order,
+      P <- g P + k_t v_t^T,  m <- g m + k_t,
+      r = P^T q_t,  rm = q_t.m,
+      E <- g E + k_t r^T,  n <- g n + k_t rm,
+      num_t = E^T q_t,  den_t = q_t.n.
+    Returns (num [U,T,dv], den [U,T], final state {P, m, E, n}); `state`
+    (optional, same keys) is the state before the first token."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    U, T, d = q.shape
+    dv = v.shape[2]
+    g1 = _gamma(gamma, U)[:, None]
+    if state is None:
+        P, m = np.zeros((U, d, dv), _F), np.zeros((U, d), _F)
+        E, n = np.zeros((U, d, dv), _F), np.zeros((U, d), _F)
+    else:
+        P, m, E, n = (_f64(state[key]).copy() for key in ("P", "m", "E", "n"))
+    num = np.empty((U, T, dv), _F)
+    den = np.empty((U, T), _F)
+    for t in range(T):
+        qt, kt, vt = q[:, t, :], k[:, t, :], v[:, t, :]
+        P = g1[:, :, None] * P + kt[:, :, None] * vt[:, None, :]
+        m = g1 * m + kt
+        r = np.matmul(qt[:, None, :], P)[:, 0, :]              # P^T q_t
+        rm = np.sum(qt * m, axis=1)
+        E = g1[:, :, None] * E + kt[:, :, None] * r[:, None, :]
+        n = g1 * n + kt * rm[:, None]
+        num[:, t, :] = np.matmul(qt[:, None, :], E)[:, 0, :]
+        den[:, t] = np.sum(qt * n, axis=1)
+    return num, den, {"P": P, "m": m, "E": E, "n": n}
+
+
+def brute_ahla(q, k, v, gamma=None):
+    """Closed form of AHLA as a triple sum (tiny inputs only):
+    num_t = sum_{i<=t} sum_{j<=i} gamma^(t-j) (q_t.k_i)(q_i.k_j) v_j, den_t
+    without v_j."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    U, T, d = q.shape
+    dv = v.shape[2]
+    g = _gamma(gamma, U)
+    num = np.zeros((U, T, dv), _F)
+    den = np.zeros((U, T), _F)
+    for u in range(U):
+        for t in range(T):
+            for i in range(t + 1):
+                for j in range(i + 1):
+                    w = float(g[u]) ** (t - j)
+                    s = w * float(q[u, t] @ k[u, i]) * float(q[u, i] @ k[u, j])
+                    num[u, t] += s * v[u, j]
+                    den[u, t] += s
+    return num, den
+
+
+def ahla_identity(U, d, dv):
+    """Neutral element of combine_ahla: zero summaries, length 0."""
+    z = lambda *s: np.zeros((U,) + s, _F)
+    return {"P": z(d, dv), "m": z(d), "E": z(d, dv), "n": z(d), "X": z(d, d),
+            "L": np.zeros(U, dtype=np.int64)}
+
+
+def ahla_segment_summary(q, k, v, gamma=None):
+    """Summary of one segment: the state the AHLA recurrence reaches from
+    zero, X = sum_i k_i q_i^T (undecayed) and the length L."""
+    _, _, st = serial_ahla(q, k, v, gamma)
+    st["X"] = np.matmul(np.swapaxes(_f64(k), 1, 2), _f64(q))
+    st["L"] = np.full(np.shape(q)[0], np.shape(q)[1], dtype=np.int64)
+    return st
+
+
+def combine_ahla(A, B, gamma=None):
+    """Segment A followed by segment B (see the section comment):
+      P = a P_A + P_B, m = a m_A + m_B, E = a E_A + E_B + a X_B P_A,
+      n = a n_A + n_B + a X_B m_A, X = X_A + X_B, L = L_A + L_B."""
+    U = A["P"].shape[0]
+    a = powers(_gamma(gamma, U), B["L"])
+    a1, a3 = a[:, None], a[:, None, None]
+    return {
+        "P": a3 * A["P"] + B["P"],
+        "m": a1 * A["m"] + B["m"],
+        "E": a3 * A["E"] + B["E"] + a3 * np.matmul(B["X"], A["P"]),
+        "n": a1 * A["n"] + B["n"] + a1 * np.matmul(B["X"], A["m"][:, :, None])[:, :, 0],
+        "X": A["X"] + B["X"],
+        "L": A["L"] + B["L"],
+    }
+
+
+def ahla_chunk_forward(q, k, v, chunk, gamma=None):
+    """Chunk-parallel AHLA: segment summaries, exclusive prefixes under
+    combine_ahla (left to right), then the recurrence continued inside each
+    segment from its prefix.  Returns (num, den, prefixes)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    U, T, d = q.shape
+    dv = v.shape[2]
+    assert chunk > 0 and T % chunk == 0
+    sums = [ahla_segment_summary(q[:, s:s + chunk], k[:, s:s + chunk], v[:, s:s + chunk], gamma)
+            for s in range(0, T, chunk)]
+    pre, run = [], ahla_identity(U, d, dv)
+    for sm in sums:
+        pre.append(run)
+        run = combine_ahla(run, sm, gamma)
+    num = np.empty((U, T, dv), _F)
+    den = np.empty((U, T), _F)
+    for c, s in enumerate(range(0, T, chunk)):
+        n_, d_, _ = serial_ahla(q[:, s:s + chunk], k[:, s:s + chunk], v[:, s:s + chunk], gamma, pre[c])
         num[:, s:s + chunk] = n_
         den[:, s:s + chunk] = d_
     return num, den, pre
