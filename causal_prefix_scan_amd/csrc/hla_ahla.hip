@@ -1,0 +1,528 @@
+// The asymmetric variant AHLA of the second-order forward ("Higher-order
+// Linear Attention", arXiv 2510.27258, summaries on gist.science: method
+// section 2 -- the operator Q (K^T Q)(K^T V), a single path through an
+// intermediate key index, streaming summaries P^KV, m^K, E, n; method
+// section 4 -- segment summaries joined by an exclusive scan).
+//
+// Causal form read here: o_t = sum_{i<=t} sum_{j<=i} (q_t.k_i)(q_i.k_j) v_j,
+// with P_t = sum_{j<=t} k_j v_j^T, m_t = sum_{j<=t} k_j, r_i = P_i^T q_i,
+// E_t = sum_{i<=t} k_i r_i^T, n_t = sum_{i<=t} k_i (q_i.m_i), o_t = E_t^T q_t,
+// den_t = q_t.n_t; decay g multiplies every moment once per token.  Per tile
+// (0-based tau, Lt tokens, A'[tau][i] = g^(tau-i) q_tau.k_i for i <= tau):
+//   R = g^(tau+1) Q P + A' V,   O = g^(tau+1) Q E + A' R,
+//   P <- g^Lt P + K^T diag(w) V,  E <- g^Lt E + K^T diag(w) R,  w_i = g^(Lt-1-i).
+// m and n ride along as one more value column: V is extended by a column of
+// ones, so the extra column of P is m, that of R is q.m, that of E is n and
+// that of O is den.  A segment's summary also carries X = sum_i k_i q_i^T
+// (no decay): the combine (A then B, a = g^(length of B)) is
+//   P = a P_A + P_B, E = a E_A + E_B + a X_B P_A (m, n likewise).
+//
+// One workgroup per (unit, segment) with one wave per 16-column block of the
+// extended values (dv / 16 + 1 waves); each wave keeps its blocks of P and E
+// in fp32 MFMA accumulators and its R tile in registers, so the waves share
+// only the staged tile and the A' scores.  The scan walks a unit's segments
+// in order, one workgroup per (unit, column block).
+#include <type_traits>
+
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+constexpr int AT = 64;   // tokens per tile
+
+enum { A_SUMMARY = 0, A_OUTPUT = 1 };
+
+template <typename T, int D, int E>
+struct ALayout {
+  static constexpr int PADT = 16 / (int)sizeof(T);
+  static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;
+  static constexpr int EX = E + 16;        // values plus the block holding the ones column
+  static constexpr int LDD = DP + PADT;    // Q, K: [tok][d]
+  static constexpr int LDV = EX + PADT;    // V and the ones column: [tok][e]
+  static constexpr int LDT = AT + PADT;    // A': [tok][tok]
+  static constexpr size_t Qs = 0;
+  static constexpr size_t Ks = Qs + (size_t)AT * LDD * sizeof(T);
+  static constexpr size_t Vs = Ks + (size_t)AT * LDD * sizeof(T);
+  static constexpr size_t AB = Vs + (size_t)AT * LDV * sizeof(T);
+  static constexpr size_t TILE_END = AB + (size_t)AT * LDT * sizeof(T);
+  static constexpr size_t W = (TILE_END + 15) / 16 * 16;
+  // pw, w1, wS, denv [AT]
+  static constexpr size_t TOTAL = W + (size_t)(4 * AT) * 4;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+};
+
+__device__ __forceinline__ void atri(int idx, int& r, int& c) {
+  r = 0;
+  while (idx > r) { idx -= r + 1; ++r; }
+  c = idx;
+}
+
+// K^T fragment (rows d = n0 + (lane & 15), K = tokens) in the K order of
+// Frag<T>::acc_b, from K stored [tok][d]: bf16 step kk holds tokens
+// 32 kk + 4 g + [0, 4) and 32 kk + 16 + 4 g + [0, 4) (two transposing reads
+// of four rows each); fp32 step kk holds token 16 (kk >> 2) + 4 g + (kk & 3).
+template <typename T>
+__device__ __forceinline__ typename MM<T>::F kt_acc_order(const T* X, int ldm, int kk, int n0, int lane);
+template <>
+__device__ __forceinline__ bf16x8 kt_acc_order<__bf16>(const __bf16* X, int ldm, int kk, int n0, int lane) {
+  const int l = lane & 15, g = lane >> 4;
+  __bf16* p0 = const_cast<__bf16*>(X) + (32 * kk + 4 * g + (l >> 2)) * ldm + n0 + 4 * (l & 3);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * ldm));
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+template <>
+__device__ __forceinline__ float kt_acc_order<float>(const float* X, int ldm, int kk, int n0, int lane) {
+  return X[(16 * (kk >> 2) + 4 * (lane >> 4) + (kk & 3)) * ldm + n0 + (lane & 15)];
+}
+
+template <typename T, int D, int E, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
+  constexpr int NTHR = 64 * NW;
+  using L = ALayout<T, D, E>;
+  using MMT = MM<T>;
+  using FR = Frag<T>;
+  using F = typename MMT::F;
+  constexpr int KS = MMT::KS, CH = MMT::CH, DP = L::DP;
+  constexpr int DT = D / 16, ET = E / 16, TR = AT / 16, NKS = AT / KS;
+  constexpr int NTRI = TR * (TR + 1) / 2;
+  constexpr int QSK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps over d
+  constexpr int TSK = KS == 32 ? TR / 2 : TR * 4;          // K steps over the tile's tokens
+  constexpr int XB = (DT + NW - 1) / NW;                   // X column blocks per wave
+  constexpr bool OUT = MODE == A_OUTPUT;
+  static_assert(NW == ET + 1, "one wave per 16-column block of the extended values");
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  T* Qs = reinterpret_cast<T*>(smem + L::Qs);
+  T* Ks = reinterpret_cast<T*>(smem + L::Ks);
+  T* Vs = reinterpret_cast<T*>(smem + L::Vs);
+  T* AB = reinterpret_cast<T*>(smem + L::AB);
+  float* pw = reinterpret_cast<float*>(smem + L::W);
+  float* w1 = pw + AT;
+  float* wS = w1 + AT;
+  float* denv = wS + AT;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg4 = lane >> 4;
+  const int nspan = a.nspan;
+  const int unit = blockIdx.x / nspan, span = blockIdx.x - unit * nspan;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float lgg = log2f(g);
+  const int Lspan = a.chunk;
+  const size_t tok0 = (size_t)unit * (size_t)a.T + (size_t)span * (size_t)Lspan;
+  const T* gq = reinterpret_cast<const T*>(a.q) + tok0 * D;
+  const T* gk = reinterpret_cast<const T*>(a.k) + tok0 * D;
+  const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
+  const size_t sidx = (size_t)unit * nspan + span;
+  const int ntiles = (Lspan + AT - 1) / AT;
+  const int cb = wave;                 // this wave's value block; block ET is (m, n)
+  const bool mblk = cb == ET;
+
+  for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < AT) {
+    pw[tid] = gpow(g, lgg, tid);
+    w1[tid] = gpow(g, lgg, tid + 1);
+  }
+
+  // P and E blocks of this wave (rows 16 t + 4 lg4 + j, column 16 cb + lr; in
+  // the (m, n) block only column 0 is non-zero), from the prefix or zero
+  f32x4 Pt[DT], Et[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * t + 4 * lg4 + j;
+      float p = 0.f, e = 0.f;
+      if (OUT) {
+        if (!mblk) {
+          p = a.P[(sidx * D + row) * E + 16 * cb + lr];
+          e = a.E[(sidx * D + row) * E + 16 * cb + lr];
+        } else if (lr == 0) {
+          p = a.m[sidx * D + row];
+          e = a.n[sidx * D + row];
+        }
+      }
+      Pt[t][j] = p;
+      Et[t][j] = e;
+    }
+  f32x4 Xt[XB][DT];
+#pragma unroll
+  for (int b = 0; b < XB; ++b)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) Xt[b][t] = zero4();
+  __syncthreads();   // the cleared tile region before the first staging
+
+  // tile staging through registers, one loop per buffer
+  constexpr int QCH = AT * D / CH, VCH = AT * E / CH;
+  constexpr int NQ = (QCH + NTHR - 1) / NTHR, NV = (VCH + NTHR - 1) / NTHR;
+  uint4 xq[NQ], xk[NQ], xv[NV];
+  auto load_rows = [&](uint4* x, auto n, const T* src, int W, int nch, int t0, int Lt) {
+#pragma unroll
+    for (int i = 0; i < decltype(n)::value; ++i) {
+      const int c = tid + NTHR * i;
+      const int row = c / (W / CH), col = (c % (W / CH)) * CH;
+      x[i] = make_uint4(0, 0, 0, 0);
+      if (c < nch && row < Lt) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + row) * W + col);
+    }
+  };
+  auto store_rows = [&](const uint4* x, auto n, T* dst, int W, int LD, int nch) {
+#pragma unroll
+    for (int i = 0; i < decltype(n)::value; ++i) {
+      const int c = tid + NTHR * i;
+      const int row = c / (W / CH), col = (c % (W / CH)) * CH;
+      if (c < nch) *reinterpret_cast<uint4*>(dst + row * LD + col) = x[i];
+    }
+  };
+  using NQc = std::integral_constant<int, NQ>;
+  using NVc = std::integral_constant<int, NV>;
+  auto tile_len = [&](int ti) { return (Lspan - ti * AT) < AT ? (Lspan - ti * AT) : AT; };
+  auto load_tile = [&](int ti) {
+    const int t0 = ti * AT, Lt = tile_len(ti);
+    load_rows(xq, NQc{}, gq, D, QCH, t0, Lt);
+    load_rows(xk, NQc{}, gk, D, QCH, t0, Lt);
+    load_rows(xv, NVc{}, gv, E, VCH, t0, Lt);
+  };
+
+  load_tile(0);
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int t0 = ti * AT, Lt = tile_len(ti);
+    const float gL = gpow(g, lgg, Lt);
+    // ---- stage the tile, the ones column and the update weights ----
+    store_rows(xq, NQc{}, Qs, D, L::LDD, QCH);
+    store_rows(xk, NQc{}, Ks, D, L::LDD, QCH);
+    store_rows(xv, NVc{}, Vs, E, L::LDV, VCH);
+    if (tid < AT) {
+      Vs[tid * L::LDV + E] = (T)(tid < Lt ? 1.f : 0.f);
+      wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+    }
+    __syncthreads();
+    if (ti + 1 < ntiles) load_tile(ti + 1);
+
+    if constexpr (OUT) {
+      // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau), over all waves ----
+      for (int idx = wave; idx < NTRI; idx += NW) {
+        int r, c;
+        atri(idx, r, c);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DP; k0 += KS)
+          acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+        const int tau = 16 * r + lr;
+        f32x4 val;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * c + 4 * lg4 + j;
+          val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
+        }
+        bf16x4 y;
+        if constexpr (sizeof(T) == 2) {
+          y[0] = (__bf16)val[0]; y[1] = (__bf16)val[1]; y[2] = (__bf16)val[2]; y[3] = (__bf16)val[3];
+          *reinterpret_cast<bf16x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = y;
+        } else {
+          *reinterpret_cast<f32x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = val;
+        }
+      }
+      __syncthreads();
+
+      // ---- R = g^(tau+1) Q P + A' V and O = g^(tau+1) Q E + A' R for this block ----
+      f32x4 Rt[TR], Ot[TR];
+#pragma unroll
+      for (int r = 0; r < TR; ++r) { Rt[r] = zero4(); Ot[r] = zero4(); }
+#pragma unroll
+      for (int kk = 0; kk < QSK; ++kk) {
+        const F bp = FR::acc_b(Pt, kk), be = FR::acc_b(Et, kk);
+#pragma unroll
+        for (int r = 0; r < TR; ++r) {
+          const F aq = FR::perm(Qs, L::LDD, 16 * r, kk, lane);
+          Rt[r] = MMT::mma(aq, bp, Rt[r]);
+          Ot[r] = MMT::mma(aq, be, Ot[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Rt[r][j] *= w1[16 * r + 4 * lg4 + j];
+          Ot[r][j] *= w1[16 * r + 4 * lg4 + j];
+        }
+        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
+          Rt[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * cb, lane), Rt[r]);
+      }
+      // A' R: R's tiles stacked along the tokens are the B operand
+#pragma unroll
+      for (int kk = 0; kk < TSK; ++kk) {
+        const F br = FR::acc_b(Rt, kk);
+#pragma unroll
+        for (int r = 0; r < TR; ++r)
+          if (KS * kk < 16 * r + 16) Ot[r] = MMT::mma(FR::perm(AB, L::LDT, 16 * r, kk, lane), br, Ot[r]);
+      }
+      // lane: O[tau = 16 r + 4 lg4 + j][16 cb + lr]; the (m, n) block's column 0 is den
+      if (mblk) {
+#pragma unroll
+        for (int r = 0; r < TR; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int tau = 16 * r + 4 * lg4 + j;
+            if (lr == 0) {
+              denv[tau] = Ot[r][j];
+              if (a.den != nullptr && tau < Lt) a.den[tok0 + (size_t)t0 + tau] = Ot[r][j];
+            }
+          }
+      }
+      // ---- P <- g^Lt P + K^T diag(w) V, E <- g^Lt E + K^T diag(w) R ----
+#pragma unroll
+      for (int r = 0; r < TR; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Rt[r][j] *= wS[16 * r + 4 * lg4 + j];
+      {
+        F bv[NKS], bw[TSK];
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int kk = 0; kk < TSK; ++kk) bw[kk] = FR::acc_b(Rt, kk);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 p = Pt[t] * gL, e = Et[t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) p = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bv[kk], p);
+#pragma unroll
+          for (int kk = 0; kk < TSK; ++kk) e = MMT::mma(kt_acc_order<T>(Ks, L::LDD, kk, 16 * t, lane), bw[kk], e);
+          Pt[t] = p;
+          Et[t] = e;
+        }
+      }
+      __syncthreads();
+      // ---- outputs (normalised by den when asked) ----
+      if (!mblk) {
+        float* go = a.o + (tok0 + (size_t)t0) * E;
+#pragma unroll
+        for (int r = 0; r < TR; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int tau = 16 * r + 4 * lg4 + j;
+            float o = Ot[r][j];
+            if (a.normalize) o = o / (denv[tau] + a.eps);
+            if (tau < Lt) go[(size_t)tau * E + 16 * cb + lr] = o;
+          }
+      }
+    } else {
+      // ---- summary: P, E (and R) as above from zero, and X += K^T Q ----
+      // A' is needed for R: computed here over all waves
+      for (int idx = wave; idx < NTRI; idx += NW) {
+        int r, c;
+        atri(idx, r, c);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DP; k0 += KS)
+          acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+        const int tau = 16 * r + lr;
+        f32x4 val;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * c + 4 * lg4 + j;
+          val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
+        }
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 y;
+          y[0] = (__bf16)val[0]; y[1] = (__bf16)val[1]; y[2] = (__bf16)val[2]; y[3] = (__bf16)val[3];
+          *reinterpret_cast<bf16x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = y;
+        } else {
+          *reinterpret_cast<f32x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = val;
+        }
+      }
+      __syncthreads();
+      f32x4 Rt[TR];
+#pragma unroll
+      for (int r = 0; r < TR; ++r) Rt[r] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < QSK; ++kk) {
+        const F bp = FR::acc_b(Pt, kk);
+#pragma unroll
+        for (int r = 0; r < TR; ++r) Rt[r] = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), bp, Rt[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Rt[r][j] *= w1[16 * r + 4 * lg4 + j] * wS[16 * r + 4 * lg4 + j];
+        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+          f32x4 av = zero4();
+          av = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * cb, lane), av);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Rt[r][j] += av[j] * wS[16 * r + 4 * lg4 + j];
+        }
+      }
+      {
+        F bv[NKS], bw[TSK];
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
+#pragma unroll
+        for (int kk = 0; kk < TSK; ++kk) bw[kk] = FR::acc_b(Rt, kk);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          f32x4 p = Pt[t] * gL, e = Et[t] * gL;
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) p = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bv[kk], p);
+#pragma unroll
+          for (int kk = 0; kk < TSK; ++kk) e = MMT::mma(kt_acc_order<T>(Ks, L::LDD, kk, 16 * t, lane), bw[kk], e);
+          Pt[t] = p;
+          Et[t] = e;
+        }
+      }
+      // X[:, blocks] += K^T Q[:, blocks] (rows past the segment end are zero)
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int xc = wave + NW * b;
+        if (xc < DT) {
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            f32x4 x = Xt[b][t];
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk)
+              x = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), FR::tr(Qs, L::LDD, kk * KS, 16 * xc, lane), x);
+            Xt[b][t] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  if constexpr (!OUT) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * t + 4 * lg4 + j;
+        if (!mblk) {
+          a.P[(sidx * D + row) * E + 16 * cb + lr] = Pt[t][j];
+          a.E[(sidx * D + row) * E + 16 * cb + lr] = Et[t][j];
+        } else if (lr == 0) {
+          a.m[sidx * D + row] = Pt[t][j];
+          a.n[sidx * D + row] = Et[t][j];
+        }
+      }
+#pragma unroll
+    for (int b = 0; b < XB; ++b) {
+      const int xc = wave + NW * b;
+      if (xc < DT) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            a.X[(sidx * D + 16 * t + 4 * lg4 + j) * D + 16 * xc + lr] = Xt[b][t][j];
+      }
+    }
+  }
+}
+
+// Exclusive scan of the AHLA summaries of each unit, in order, for one
+// 16-column block of (P, E) (block ET: m, n as a single column):
+// prefix_s = run; run <- a run + x_s, E picking up a X_s P_run (a = g^chunk).
+// In place; X is only read.  One workgroup of 256 threads per (unit, block).
+template <int D, int E>
+__global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
+  constexpr int ET = E / 16;
+  __shared__ float Xs[D][D + 1];
+  __shared__ float Pr[D][16];
+  const int unit = blockIdx.x / (ET + 1), cb = blockIdx.x % (ET + 1);
+  const bool mblk = cb == ET;
+  const int ncol = mblk ? 1 : 16;
+  const int n = a.nspan, tid = threadIdx.x;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float sa = gpow(g, log2f(g), a.chunk);
+  constexpr int PER = (D * 16 + 255) / 256;
+  float er[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) er[i] = 0.f;
+  for (int i = tid; i < D * 16; i += 256) Pr[i / 16][i % 16] = 0.f;
+  for (int s = 0; s < n; ++s) {
+    const size_t sidx = (size_t)unit * n + s;
+    for (int i = tid; i < D * D; i += 256) Xs[i / D][i % D] = a.X[sidx * D * D + i];
+    __syncthreads();
+    float pn[PER], en[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i, row = idx / 16, col = idx % 16;
+      pn[i] = en[i] = 0.f;
+      if (idx < D * 16 && col < ncol) {
+        float cross = 0.f;
+        for (int k = 0; k < D; ++k) cross += Xs[row][k] * Pr[k][col];
+        float* pp = mblk ? a.m + sidx * D + row : a.P + (sidx * D + row) * E + 16 * cb + col;
+        float* ep = mblk ? a.n + sidx * D + row : a.E + (sidx * D + row) * E + 16 * cb + col;
+        const float px = *pp, ex = *ep;
+        *pp = Pr[row][col];
+        *ep = er[i];
+        pn[i] = sa * Pr[row][col] + px;
+        en[i] = sa * er[i] + ex + sa * cross;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i, row = idx / 16, col = idx % 16;
+      if (idx < D * 16 && col < ncol) {
+        Pr[row][col] = pn[i];
+        er[i] = en[i];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int E>
+struct AWaves {
+  static constexpr int value = E / 16 + 1;
+};
+
+template <int MODE>
+hipError_t launch_ahla_mode(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)units * (unsigned)a.nspan);
+#define HLA_CASE(T, D, E)                                                                     \
+  if (d == D && dv == E) {                                                                    \
+    constexpr int NW = AWaves<D, E>::value;                                                   \
+    hipLaunchKernelGGL((ahla_kernel<T, D, E, MODE, NW>), grid, dim3(64 * NW), 0, s, a);       \
+    return hipGetLastError();                                                                 \
+  }
+  if (dtype == 1) {
+    HLA_CASE(__bf16, 16, 16) HLA_CASE(__bf16, 16, 32) HLA_CASE(__bf16, 32, 16)
+    HLA_CASE(__bf16, 32, 32) HLA_CASE(__bf16, 32, 64) HLA_CASE(__bf16, 64, 32)
+    HLA_CASE(__bf16, 64, 64) HLA_CASE(__bf16, 64, 128) HLA_CASE(__bf16, 128, 64)
+    HLA_CASE(__bf16, 128, 128)
+  } else {
+    HLA_CASE(float, 16, 16) HLA_CASE(float, 16, 32) HLA_CASE(float, 32, 16)
+    HLA_CASE(float, 32, 32) HLA_CASE(float, 32, 64) HLA_CASE(float, 64, 32)
+    HLA_CASE(float, 64, 64)
+  }
+#undef HLA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_ahla_summaries(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {
+  return launch_ahla_mode<A_SUMMARY>(dtype, d, dv, units, a, s);
+}
+
+hipError_t launch_ahla_outputs(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {
+  return launch_ahla_mode<A_OUTPUT>(dtype, d, dv, units, a, s);
+}
+
+hipError_t launch_ahla_scan(int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {
+#define HLA_CASE(D, E)                                                                         \
+  if (d == D && dv == E) {                                                                     \
+    hipLaunchKernelGGL((ahla_scan_kernel<D, E>), dim3((unsigned)units * (E / 16 + 1)), dim3(256), \
+                       0, s, a);                                                               \
+    return hipGetLastError();                                                                  \
+  }
+  HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(32, 16) HLA_CASE(32, 32) HLA_CASE(32, 64)
+  HLA_CASE(64, 32) HLA_CASE(64, 64) HLA_CASE(64, 128) HLA_CASE(128, 64) HLA_CASE(128, 128)
+#undef HLA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hla

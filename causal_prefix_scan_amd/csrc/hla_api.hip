@@ -528,6 +528,153 @@ hla_status hla_unmasked_fwd(const hla_problem* p, const void* q, const void* k, 
   return HLA_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct AhlaSizes {
+  size_t P, m, X;   // floats per segment of P (= E), m (= n), X
+};
+
+AhlaSizes ahla_sizes(const hla_problem* p) {
+  return AhlaSizes{(size_t)p->d * p->dv, (size_t)p->d, (size_t)p->d * p->d};
+}
+
+// every field present, aligned, disjoint from the others and from the inputs
+hla_status check_ahla_state(const hla_ahla_state* st, int64_t count, const hla_problem* p,
+                            const void* const* inputs, const size_t* in_bytes, int n_inputs) {
+  if (!st) return HLA_ERR_NULL_POINTER;
+  const AhlaSizes z = ahla_sizes(p);
+  float* f[5] = {st->P, st->m, st->E, st->n, st->X};
+  const size_t per[5] = {z.P, z.m, z.P, z.m, z.X};
+  for (int i = 0; i < 5; ++i) {
+    if (!f[i]) return HLA_ERR_NULL_POINTER;
+    if (!aligned16(f[i])) return HLA_ERR_MISALIGNED;
+    const size_t bytes = (size_t)count * per[i] * 4;
+    for (int j = 0; j < n_inputs; ++j)
+      if (overlap(f[i], bytes, inputs[j], in_bytes[j])) return HLA_ERR_ALIASING;
+    for (int j = 0; j < i; ++j)
+      if (overlap(f[i], bytes, f[j], (size_t)count * per[j] * 4)) return HLA_ERR_ALIASING;
+  }
+  return HLA_OK;
+}
+
+hla::AhlaArgs ahla_args(const hla_problem* p, const void* q, const void* k, const void* v,
+                        const hla_ahla_state* st, float* o, float* den) {
+  hla::AhlaArgs a;
+  a.q = q; a.k = k; a.v = v; a.gamma = p->gamma;
+  a.H = p->H; a.T = p->T; a.chunk = p->chunk; a.nspan = p->T / p->chunk;
+  a.normalize = p->normalize; a.eps = p->eps;
+  a.P = st->P; a.m = st->m; a.E = st->E; a.n = st->n; a.X = st->X;
+  a.o = o; a.den = den;
+  return a;
+}
+
+size_t ahla_summary_bytes(const hla_problem* p) {
+  const Sizes z = sizes_of(p);
+  const AhlaSizes a = ahla_sizes(p);
+  return (size_t)z.units * (size_t)z.n * (2 * a.P + 2 * a.m + a.X) * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+hla_status hla_ahla_chunk_summaries(const hla_problem* p, const void* q, const void* k,
+                                    const void* v, const hla_ahla_state* out, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  const Sizes z = sizes_of(p);
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {z.qk_bytes, z.qk_bytes, z.v_bytes};
+  if (hla_status e = check_ahla_state(out, z.units * z.n, p, ins, inb, 3)) return e;
+  if (hla_status e = device_ready()) return e;
+  return from_hip(hla::launch_ahla_summaries(p->in_dtype, p->d, p->dv, (int)z.units,
+                                             ahla_args(p, q, k, v, out, nullptr, nullptr),
+                                             static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_ahla_scan(const hla_problem* p, const hla_ahla_state* inout, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_ahla_state(inout, z.units * z.n, p, nullptr, nullptr, 0)) return e;
+  if (hla_status e = device_ready()) return e;
+  return from_hip(hla::launch_ahla_scan(p->d, p->dv, (int)z.units,
+                                        ahla_args(p, nullptr, nullptr, nullptr, inout, nullptr, nullptr),
+                                        static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_ahla_output(const hla_problem* p, const void* q, const void* k, const void* v,
+                           const hla_ahla_state* prefixes, float* o, float* den, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_ahla_state(prefixes, z.units * z.n, p, nullptr, nullptr, 0)) return e;
+  const AhlaSizes a = ahla_sizes(p);
+  const size_t cnt = (size_t)z.units * (size_t)z.n;
+  const void* ins[7] = {q, k, v, prefixes->P, prefixes->m, prefixes->E, prefixes->n};
+  const size_t inb[7] = {z.qk_bytes, z.qk_bytes, z.v_bytes, cnt * a.P * 4, cnt * a.m * 4,
+                         cnt * a.P * 4, cnt * a.m * 4};
+  if (hla_status e = check_outputs(z, o, den, ins, inb, 7)) return e;
+  if (hla_status e = device_ready()) return e;
+  return from_hip(hla::launch_ahla_outputs(p->in_dtype, p->d, p->dv, (int)z.units,
+                                           ahla_args(p, q, k, v, prefixes, o, den),
+                                           static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+size_t hla_ahla_fwd_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  return ahla_summary_bytes(p);
+}
+
+hla_status hla_ahla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                        float* o, float* den, void* workspace, size_t workspace_bytes,
+                        void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  const Sizes z = sizes_of(p);
+  const size_t need = hla_ahla_fwd_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  const void* ins[4] = {q, k, v, workspace};
+  const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
+  if (hla_status e = check_outputs(z, o, den, ins, inb, 4)) return e;
+  for (int j = 0; j < 3; ++j)
+    if (overlap(workspace, need, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  if (hla_status e = device_ready()) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AhlaSizes a = ahla_sizes(p);
+  const size_t cnt = (size_t)z.units * (size_t)z.n;
+  hla_ahla_state st;
+  st.P = static_cast<float*>(workspace);
+  st.E = st.P + cnt * a.P;
+  st.X = st.E + cnt * a.P;
+  st.m = st.X + cnt * a.X;
+  st.n = st.m + cnt * a.m;
+  if (hla_status e = from_hip(hla::launch_ahla_summaries(p->in_dtype, p->d, p->dv, (int)z.units,
+                                                         ahla_args(p, q, k, v, &st, nullptr, nullptr), s)))
+    return e;
+  if (hla_status e = from_hip(hla::launch_ahla_scan(p->d, p->dv, (int)z.units,
+                                                    ahla_args(p, q, k, v, &st, nullptr, nullptr), s)))
+    return e;
+  return from_hip(hla::launch_ahla_outputs(p->in_dtype, p->d, p->dv, (int)z.units,
+                                           ahla_args(p, q, k, v, &st, o, den), s));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
 hla_status hla_unmasked_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
                                     int32_t normalize, float eps, const float* gamma,
                                     const void* q, const void* k, const void* v,

@@ -86,6 +86,23 @@ hipError_t launch_unmasked_outputs(int dtype, int d, int dv, int units, const Ch
 hipError_t launch_unmasked_decode(int dtype, int d, int dv, int units, const DecodeArgs& a,
                                   hipStream_t s);
 
+// The asymmetric variant AHLA: summaries P [units, n, d, dv], m [units, n, d],
+// E [units, n, d, dv], n [units, n, d], X [units, n, d, d].
+struct AhlaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  int H, T, chunk, nspan, normalize;
+  float eps;
+  float *P, *m, *E, *n, *X;
+  float* o;
+  float* den;
+};
+hipError_t launch_ahla_summaries(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
+hipError_t launch_ahla_scan(int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
+hipError_t launch_ahla_outputs(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
+
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace hla

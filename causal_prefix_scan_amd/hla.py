@@ -27,7 +27,8 @@ EXPORTS = (
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
     "hla_fwd", "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
     "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
-    "hla_unmasked_decode_step",
+    "hla_unmasked_decode_step", "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output",
+    "hla_ahla_fwd_workspace_bytes", "hla_ahla_fwd",
 )
 
 
@@ -49,6 +50,11 @@ class Problem(ctypes.Structure):
 class State(ctypes.Structure):
     _fields_ = [("S", ctypes.c_void_p), ("C", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("G", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+
+
+class AhlaState(ctypes.Structure):
+    _fields_ = [("P", ctypes.c_void_p), ("m", ctypes.c_void_p), ("E", ctypes.c_void_p),
+                ("n", ctypes.c_void_p), ("X", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,9 +91,16 @@ def lib():
     L.hla_unmasked_scan.argtypes = [pp, ps, vp]
     L.hla_unmasked_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
     L.hla_unmasked_decode_step.argtypes = L.hla_decode_step.argtypes
+    pa = ctypes.POINTER(AhlaState)
+    L.hla_ahla_chunk_summaries.argtypes = [pp, vp, vp, vp, pa, vp]
+    L.hla_ahla_scan.argtypes = [pp, pa, vp]
+    L.hla_ahla_output.argtypes = [pp, vp, vp, vp, pa, vp, vp, vp]
+    L.hla_ahla_fwd_workspace_bytes.argtypes, L.hla_ahla_fwd_workspace_bytes.restype = [pp], sz
+    L.hla_ahla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
                  "hla_fwd", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
-                 "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step"):
+                 "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step",
+                 "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output", "hla_ahla_fwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -358,4 +371,73 @@ def unmasked_decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o
                                           float(eps), _ptr(gamma), _ptr(q), _ptr(k), _ptr(v),
                                           ctypes.byref(st), _ptr(o), _ptr(den), _stream()),
            "hla_unmasked_decode_step")
+    return o, den
+
+
+def alloc_ahla_state(lead, d, dv, device):
+    """fp32 AHLA summary tensors P, m, E, n, X with leading dims `lead`."""
+    torch = _torch()
+    z = lambda *s: torch.zeros(*lead, *s, dtype=torch.float32, device=device)
+    return {"P": z(d, dv), "m": z(d), "E": z(d, dv), "n": z(d), "X": z(d, d)}
+
+
+def _ahla_struct(st):
+    return AhlaState(*(st[k].data_ptr() for k in ("P", "m", "E", "n", "X")))
+
+
+def ahla_chunk_summaries(q, k, v, chunk, gamma=None, out=None):
+    """AHLA segment summaries [B, H, n, ...] (fp32 dict P, m, E, n, X)."""
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma)
+    if out is None:
+        out = alloc_ahla_state((B, H, T // chunk), d, v.shape[3], q.device)
+    st = _ahla_struct(out)
+    _check(lib().hla_ahla_chunk_summaries(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                          ctypes.byref(st), _stream()), "hla_ahla_chunk_summaries")
+    return out
+
+
+def ahla_scan(summaries, q_shape, dv, chunk, dtype_code, gamma=None):
+    """In-place exclusive scan of AHLA summaries."""
+    B, H, T, d = q_shape
+    p = Problem(B, H, T, d, dv, int(chunk), dtype_code, 0, 0.0,
+                None if gamma is None else gamma.data_ptr())
+    st = _ahla_struct(summaries)
+    _check(lib().hla_ahla_scan(ctypes.byref(p), ctypes.byref(st), _stream()), "hla_ahla_scan")
+
+
+def ahla_output(q, k, v, prefixes, chunk, gamma=None, normalize=False, eps=0.0, want_den=False):
+    """AHLA outputs from the exclusive prefixes: (o, den or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    den = torch.empty(B, H, T, dtype=torch.float32, device=q.device) if want_den else None
+    st = _ahla_struct(prefixes)
+    _check(lib().hla_ahla_output(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
+                                 _ptr(o), _ptr(den), _stream()), "hla_ahla_output")
+    return o, den
+
+
+def ahla_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False,
+             workspace=None, o=None, den=None):
+    """The AHLA forward (summaries, scan, outputs on one stream): (o, den or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    if den is None and want_den:
+        den = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = lib().hla_ahla_fwd_workspace_bytes(ctypes.byref(p))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().hla_ahla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                              _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()),
+           "hla_ahla_fwd")
     return o, den

@@ -244,6 +244,40 @@ hla_status hla_unmasked_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv,
                                     const hla_state* state, float* o, float* den, void* stream);
 
 /*
+ * The asymmetric variant AHLA (method section 2: the operator
+ * Q (K^T Q)(K^T V), whose single path runs through an intermediate key index,
+ * with the streaming summaries P^KV, m^K, E, n; method section 4: segment
+ * summaries and an exclusive scan).  Reading of the causal form:
+ *   num_t = sum_{i<=t} sum_{j<=i} g^(t-j) (q_t.k_i)(q_i.k_j) v_j,  den_t the same with v = 1,
+ * i.e. P_t = g P_{t-1} + k_t v_t^T, m_t = g m_{t-1} + k_t, r_t = P_t^T q_t,
+ * E_t = g E_{t-1} + k_t r_t^T, n_t = g n_{t-1} + k_t (q_t.m_t), num_t = E_t^T q_t,
+ * den_t = q_t.n_t.  A segment summary also carries X = sum_i k_i q_i^T (no
+ * decay); the combine (A then B, a = g^(length of B)) is P = a P_A + P_B,
+ * m = a m_A + m_B, E = a E_A + E_B + a X_B P_A, n = a n_A + n_B + a X_B m_A.
+ * State arrays (fp32, all required): P [B,H,n,d,dv], m [B,H,n,d],
+ * E [B,H,n,d,dv], n [B,H,n,d], X [B,H,n,d,d].  Problem fields, o, den and
+ * errors as for the masked calls of the same name.
+ *
+ * hla_ahla_chunk_summaries: per segment, the state reached from zero and X.
+ * hla_ahla_scan: in place, the exclusive prefixes of P, m, E, n (X only
+ *   read), walking each unit's segments in order.
+ * hla_ahla_output: o (and den) from those prefixes.
+ * hla_ahla_fwd: the three on one stream, the summaries kept in `workspace`
+ *   (hla_ahla_fwd_workspace_bytes(p) = B*H*n*(2 d dv + 2 d + d d) floats, not
+ *   overlapping q, k or v).
+ */
+typedef struct { float *P, *m, *E, *n, *X; } hla_ahla_state;
+hla_status hla_ahla_chunk_summaries(const hla_problem* p, const void* q, const void* k,
+                                    const void* v, const hla_ahla_state* out, void* stream);
+hla_status hla_ahla_scan(const hla_problem* p, const hla_ahla_state* inout, void* stream);
+hla_status hla_ahla_output(const hla_problem* p, const void* q, const void* k, const void* v,
+                           const hla_ahla_state* prefixes, float* o, float* den, void* stream);
+size_t hla_ahla_fwd_workspace_bytes(const hla_problem* p);
+hla_status hla_ahla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                        float* o, float* den, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * One streaming decode step (method section 1: the online update of the
  * prefix state; results and claims: constant work and memory per token).
  * For each of the N*H units: applies one token (q, k [N, H, d], v [N, H, dv]

@@ -255,6 +255,38 @@ def test_unmasked_decode_validation(L):
                  None) == HIP
 
 
+def test_ahla_sizes_and_checks(L):
+    p = problem()                       # B2 H3 T256 d64 dv64 chunk 64: n = 4
+    per = 2 * 64 * 64 + 2 * 64 + 64 * 64
+    need = 2 * 3 * 4 * per * 4
+    assert L.hla_ahla_fwd_workspace_bytes(ctypes.byref(p)) == need
+    assert L.hla_ahla_fwd_workspace_bytes(ctypes.byref(problem(T=10))) == 0
+    W = 0x7000000000
+    f = L.hla_ahla_fwd
+    assert f(ctypes.byref(problem(T=10)), Q, K, V, O, None, W, need, None) == SHAPE
+    assert f(ctypes.byref(problem(d=48)), Q, K, V, O, None, W, need, None) == UNSUP
+    assert f(ctypes.byref(p), Q, K, V, None, None, W, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, O, None, W, need - 4, None) == WS
+    assert f(ctypes.byref(p), Q, K, V, O + 4, None, W, need, None) == MISAL
+    assert f(ctypes.byref(p), Q, K, V, O, None, K, need, None) == ALIAS
+    step = 0x1000000
+    st = hla.AhlaState(S_BASE, S_BASE + step, S_BASE + 2 * step, S_BASE + 3 * step, S_BASE + 4 * step)
+    no_x = hla.AhlaState(S_BASE, S_BASE + step, S_BASE + 2 * step, S_BASE + 3 * step, None)
+    assert L.hla_ahla_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(no_x), None) == NULLP
+    over = hla.AhlaState(S_BASE, S_BASE + 8, S_BASE + 2 * step, S_BASE + 3 * step, S_BASE + 4 * step)
+    assert L.hla_ahla_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(over), None) == MISAL
+    over16 = hla.AhlaState(S_BASE, S_BASE + 16, S_BASE + 2 * step, S_BASE + 3 * step, S_BASE + 4 * step)
+    assert L.hla_ahla_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(over16), None) == ALIAS
+    assert L.hla_ahla_scan(ctypes.byref(problem(chunk=0)), ctypes.byref(st), None) == SHAPE
+    assert L.hla_ahla_output(ctypes.byref(p), Q, K, V, ctypes.byref(st), S_BASE, None, None) == ALIAS
+    assert f(ctypes.byref(problem(B=0)), None, None, None, None, None, None, 0, None) == OK
+    if no_gpu():
+        assert f(ctypes.byref(p), Q, K, V, O, None, W, need, None) == HIP
+        assert L.hla_ahla_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(st), None) == HIP
+        assert L.hla_ahla_scan(ctypes.byref(p), ctypes.byref(st), None) == HIP
+        assert L.hla_ahla_output(ctypes.byref(p), Q, K, V, ctypes.byref(st), O, DEN, None) == HIP
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 64, 16)
