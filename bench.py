@@ -44,6 +44,15 @@ def credited_flops_per_token_unmasked(c, d, dv):
     return f / c
 
 
+def credited_flops_per_token_ahla(c, d, dv):
+    """Credited flops per token of AHLA at chunk length c: the lower triangles
+    of Q K^T, A' V and A' R, the products Q P, Q E, K^T V, K^T R, the segment
+    moment X = K^T Q, and one combine per chunk (X_B P_A)."""
+    f = (c * (c + 1) * d + 2 * c * (c + 1) * dv + 8 * c * d * dv + 2 * c * d * d
+         + 2 * d * d * dv)
+    return f / c
+
+
 def measured_traffic(key):
     """HBM bytes per launch measured with rocprofv3 counters for `key`, or None
     if the kernel's sources changed since the counters were taken."""
@@ -333,6 +342,108 @@ def bench_unmasked(args, torch, np):
     return out
 
 
+AHLA_WORKLOADS = {"ahla_decay_bf16_b4h16t16384d128": "fwd_decay_bf16_b4h16t16384d128"}
+
+
+def bench_ahla(args, torch, np):
+    """AHLA on the inputs of a forward workload: segment summaries -> scan ->
+    outputs (three C-ABI calls on one stream)."""
+    import ctypes
+    from causal_prefix_scan_amd import hla, synth
+    cfg = dict(synth.FWD_WORKLOADS[AHLA_WORKLOADS[args.workload]])
+    if args.chunk:
+        cfg["chunk"] = args.chunk
+    B, H, T, d, dv, chunk = (cfg[x] for x in ("B", "H", "T", "d", "dv", "chunk"))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"],
+                                k_l2norm=cfg["k_l2norm"], decay=cfg["decay"])
+    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
+    n = T // chunk
+    st = hla.alloc_ahla_state((B, H, n), d, dv, "cuda")
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
+    L = hla.lib()
+    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
+    sst = hla._ahla_struct(st)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        r1 = L.hla_ahla_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(sst), sp)
+        if ev:
+            ev[1].record(stream)
+        r2 = L.hla_ahla_scan(ctypes.byref(p), ctypes.byref(sst), sp)
+        if ev:
+            ev[2].record(stream)
+        r3 = L.hla_ahla_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(sst), ptr(o), None, sp)
+        if ev:
+            ev[3].record(stream)
+        if r1 or r2 or r3:
+            raise RuntimeError(f"HLA call failed: {r1} {r2} {r3}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
+    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    tokens = B * H * T
+    value = tokens / (step_ms / 1e3)
+    U = B * H
+    summ_bytes = U * n * (2 * d * dv + 2 * d + d * d) * 4
+    pre_bytes = U * n * (2 * d * dv + 2 * d) * 4
+    io_bytes = tokens * (2 * d + dv) * 2
+    kernels = {
+        "hla_ahla_chunk_summaries": dict(ms=ms[0], bytes=io_bytes + summ_bytes),
+        "hla_ahla_scan": dict(ms=ms[1], bytes=summ_bytes + pre_bytes),
+        "hla_ahla_output": dict(ms=ms[2], bytes=io_bytes + pre_bytes + tokens * dv * 4),
+    }
+    dom = max(kernels, key=lambda kname: kernels[kname]["ms"])
+    kd = kernels[dom]
+    achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
+    f_tok = credited_flops_per_token_ahla(64, d, dv)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
+                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
+                   "path": "hla_ahla_chunk_summaries + hla_ahla_scan + hla_ahla_output"},
+        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
+                          "peak_tflops": BF16_PEAK_TFLOPS,
+                          "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
+                     "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import hla_oracle as O
+        uq, uk, uv, ug = inp.units()
+        ntok = min(args.cpu_tokens, T)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.serial_ahla(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"fp64 serial AHLA recurrence, all {U} (batch, head) units, "
+                                         f"first {ntok} of {T} tokens ({dt:.1f} s)",
+                               "seconds": round(dt, 2)}
+    return out
+
+
 def bench_decode(args, torch, np):
     from causal_prefix_scan_amd import hla, synth
     name, cfg = synth.DECODE_WORKLOAD
@@ -510,6 +621,8 @@ def main():
         out = bench_unmasked(args, torch, np)
     elif args.workload == "unmasked_decode_n64h32d128":
         out = bench_unmasked_decode(args, torch, np)
+    elif args.workload in AHLA_WORKLOADS:
+        out = bench_ahla(args, torch, np)
     else:
         out = bench_fwd(args, torch, np)
     print(json.dumps(out), flush=True)
