@@ -21,7 +21,8 @@
 // extended values (dv / 16 + 1 waves); each wave keeps its blocks of P and E
 // in fp32 MFMA accumulators and its R tile in registers, so the waves share
 // only the staged tile and the A' scores.  The scan walks a unit's segments
-// in order, one workgroup per (unit, column block).
+// in order, one workgroup per (unit, column block).  The decode step updates
+// (P, m, E, n) in place for one token per unit.
 #include <type_traits>
 
 #include "hla_device.h"
@@ -474,6 +475,112 @@ __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
   }
 }
 
+// One AHLA decode step per unit (one workgroup of ADEC threads):
+//   P' = g P + k v^T, m' = g m + k, r = P'^T q, E' = g E + k r^T,
+//   n' = g n + k (q.m'), o = E'^T q = g (E^T q) + (q.k) r, den = q.n'.
+// Each state element is read once and written once (16-byte non-temporal
+// accesses); E stays in registers until r is reduced.
+constexpr int ADEC = 512;
+
+template <typename T, int D, int E>
+__global__ __launch_bounds__(ADEC) void ahla_decode_kernel(AhlaArgs a) {
+  constexpr int CPR = E / 4, RP = ADEC / CPR, NP = (D + RP - 1) / RP;
+  constexpr int NRG = RP < D ? RP : D;
+  __shared__ __attribute__((aligned(16))) float sq[D], sk[D], sv[E], sm[D], sn[D], rr[E], yy[E];
+  __shared__ __attribute__((aligned(16))) float pr[NRG][E], py[NRG][E];
+  __shared__ float scal[3];
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  f32x4* P = reinterpret_cast<f32x4*>(a.P + (size_t)unit * D * E);
+  f32x4* Em = reinterpret_cast<f32x4*>(a.E + (size_t)unit * D * E);
+  float* m = a.m + (size_t)unit * D;
+  float* n = a.n + (size_t)unit * D;
+  const int cc = tid % CPR, rg = tid / CPR;
+  f32x4 rP[NP], rE[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int d = rg + RP * i;
+    if (d < D) {
+      rP[i] = __builtin_nontemporal_load(P + d * CPR + cc);
+      rE[i] = __builtin_nontemporal_load(Em + d * CPR + cc);
+    }
+  }
+  const T* q = reinterpret_cast<const T*>(a.q) + (size_t)unit * D;
+  const T* k = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
+  const T* v = reinterpret_cast<const T*>(a.v) + (size_t)unit * E;
+  for (int t = tid; t < D; t += ADEC) {
+    sq[t] = (float)q[t];
+    sk[t] = (float)k[t];
+    sm[t] = m[t];
+    sn[t] = n[t];
+  }
+  for (int t = tid; t < E; t += ADEC) sv[t] = (float)v[t];
+  __syncthreads();
+
+  // P' = g P + k v^T (stored); partial r = P'^T q and y = E^T q over this thread's rows
+  {
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(sv + 4 * cc);
+    f32x4 ar = zero4(), ay = zero4();
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int d = rg + RP * i;
+      if (d < D) {
+        const f32x4 pn = rP[i] * g + v4 * sk[d];
+        __builtin_nontemporal_store(pn, P + d * CPR + cc);
+        ar += pn * sq[d];
+        ay += rE[i] * sq[d];
+      }
+    }
+    if (rg < NRG) {
+      *reinterpret_cast<f32x4*>(&pr[rg][4 * cc]) = ar;
+      *reinterpret_cast<f32x4*>(&py[rg][4 * cc]) = ay;
+    }
+  }
+  if (tid < 64) {
+    float qk = 0.f, qm = 0.f, qn = 0.f;
+    for (int d = tid; d < D; d += 64) {
+      qk += sq[d] * sk[d];
+      qm += sq[d] * sm[d];
+      qn += sq[d] * sn[d];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) {
+      qk += __shfl_xor(qk, off, 64);
+      qm += __shfl_xor(qm, off, 64);
+      qn += __shfl_xor(qn, off, 64);
+    }
+    if (tid == 0) { scal[0] = qk; scal[1] = g * qm + qk; scal[2] = qn; }   // q.k, q.m', q.n
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += ADEC) {
+    float sr = 0.f, sy = 0.f;
+    for (int r = 0; r < NRG; ++r) { sr += pr[r][e]; sy += py[r][e]; }
+    rr[e] = sr;
+    yy[e] = sy;
+  }
+  __syncthreads();
+  const float qk = scal[0], rm = scal[1];
+  const float den = g * scal[2] + qk * rm;
+  // E' = g E + k r^T; m', n'; o = g y + (q.k) r
+  {
+    const f32x4 r4 = *reinterpret_cast<const f32x4*>(rr + 4 * cc);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int d = rg + RP * i;
+      if (d < D) __builtin_nontemporal_store(rE[i] * g + r4 * sk[d], Em + d * CPR + cc);
+    }
+  }
+  for (int t = tid; t < D; t += ADEC) {
+    m[t] = g * sm[t] + sk[t];
+    n[t] = g * sn[t] + sk[t] * rm;
+  }
+  for (int e = tid; e < E; e += ADEC) {
+    const float o = g * yy[e] + qk * rr[e];
+    a.o[(size_t)unit * E + e] = a.normalize ? o / (den + a.eps) : o;
+  }
+  if (a.den != nullptr && tid == 0) a.den[unit] = den;
+}
+
 template <int D, int E>
 struct AWaves {
   static constexpr int value = E / 16 + 1;
@@ -510,6 +617,27 @@ hipError_t launch_ahla_summaries(int dtype, int d, int dv, int units, const Ahla
 
 hipError_t launch_ahla_outputs(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {
   return launch_ahla_mode<A_OUTPUT>(dtype, d, dv, units, a, s);
+}
+
+hipError_t launch_ahla_decode(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {
+#define HLA_CASE(T, D, E)                                                                   \
+  if (d == D && dv == E) {                                                                  \
+    hipLaunchKernelGGL((ahla_decode_kernel<T, D, E>), dim3(units), dim3(ADEC), 0, s, a);    \
+    return hipGetLastError();                                                               \
+  }
+  if (dtype == 1) {
+    HLA_CASE(__bf16, 16, 16) HLA_CASE(__bf16, 16, 32) HLA_CASE(__bf16, 32, 16)
+    HLA_CASE(__bf16, 32, 32) HLA_CASE(__bf16, 32, 64) HLA_CASE(__bf16, 64, 32)
+    HLA_CASE(__bf16, 64, 64) HLA_CASE(__bf16, 64, 128) HLA_CASE(__bf16, 128, 64)
+    HLA_CASE(__bf16, 128, 128)
+  } else {
+    HLA_CASE(float, 16, 16) HLA_CASE(float, 16, 32) HLA_CASE(float, 32, 16)
+    HLA_CASE(float, 32, 32) HLA_CASE(float, 32, 64) HLA_CASE(float, 64, 32)
+    HLA_CASE(float, 64, 64) HLA_CASE(float, 64, 128) HLA_CASE(float, 128, 64)
+    HLA_CASE(float, 128, 128)
+  }
+#undef HLA_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ahla_scan(int d, int dv, int units, const AhlaArgs& a, hipStream_t s) {

@@ -675,6 +675,50 @@ hla_status hla_ahla_fwd(const hla_problem* p, const void* q, const void* k, cons
   return HLA_ERR_HIP;
 }
 
+hla_status hla_ahla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                                int32_t normalize, float eps, const float* gamma, const void* q,
+                                const void* k, const void* v, const hla_ahla_state* state,
+                                float* o, float* den, void* stream) try {
+  if (N < 0 || H < 0) return HLA_ERR_BAD_SHAPE;
+  if (in_dtype != HLA_F32 && in_dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (normalize != 0 && normalize != 1) return HLA_ERR_BAD_VALUE;
+  if (!std::isfinite(eps)) return HLA_ERR_BAD_VALUE;
+  if (!head_ok(d) || !head_ok(dv) || d > 2 * dv || dv > 2 * d) return HLA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)N * H;
+  if (units > kMaxGrid) return HLA_ERR_BAD_VALUE;
+  if (units == 0) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den)) || (gamma && !aligned16(gamma)))
+    return HLA_ERR_MISALIGNED;
+  if (!state) return HLA_ERR_NULL_POINTER;
+  // P, m, E, n are used (X is not): check them as a masked-style state S, C, m, G, h
+  Sizes z;
+  z.S = (size_t)d * dv; z.C = (size_t)d * dv; z.m = (size_t)d;
+  hla_state as{state->P, state->E, state->m, nullptr, state->n};
+  if (!as.S || !as.C || !as.m || !as.h) return HLA_ERR_NULL_POINTER;
+  const size_t es = dtype_size(in_dtype);
+  const size_t uu = (size_t)units;
+  const void* ins[5] = {q, k, v, o, den};
+  const size_t inb[5] = {uu * d * es, uu * d * es, uu * dv * es, uu * dv * 4, den ? uu * 4 : 0};
+  if (hla_status e = check_state(&as, false, units, z, ins, inb, 5)) return e;
+  for (int j = 0; j < 3; ++j) {
+    if (overlap(o, inb[3], ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, inb[4], ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, inb[3], den, inb[4])) return HLA_ERR_ALIASING;
+  if (hla_status e = device_ready()) return e;
+  hla::AhlaArgs a;
+  a.q = q; a.k = k; a.v = v; a.gamma = gamma;
+  a.H = H; a.T = 0; a.chunk = 0; a.nspan = 0; a.normalize = normalize; a.eps = eps;
+  a.P = state->P; a.m = state->m; a.E = state->E; a.n = state->n; a.X = nullptr;
+  a.o = o; a.den = den;
+  return from_hip(hla::launch_ahla_decode(in_dtype, d, dv, (int)units, a,
+                                          static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
 hla_status hla_unmasked_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
                                     int32_t normalize, float eps, const float* gamma,
                                     const void* q, const void* k, const void* v,

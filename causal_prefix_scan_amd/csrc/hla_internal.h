@@ -102,6 +102,7 @@ struct AhlaArgs {
 hipError_t launch_ahla_summaries(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
 hipError_t launch_ahla_scan(int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
 hipError_t launch_ahla_outputs(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
+hipError_t launch_ahla_decode(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
 
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 

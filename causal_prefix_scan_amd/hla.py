@@ -28,7 +28,7 @@ EXPORTS = (
     "hla_fwd", "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
     "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
     "hla_unmasked_decode_step", "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output",
-    "hla_ahla_fwd_workspace_bytes", "hla_ahla_fwd",
+    "hla_ahla_fwd_workspace_bytes", "hla_ahla_fwd", "hla_ahla_decode_step",
 )
 
 
@@ -97,10 +97,12 @@ def lib():
     L.hla_ahla_output.argtypes = [pp, vp, vp, vp, pa, vp, vp, vp]
     L.hla_ahla_fwd_workspace_bytes.argtypes, L.hla_ahla_fwd_workspace_bytes.restype = [pp], sz
     L.hla_ahla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.hla_ahla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, pa, vp, vp, vp]
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
                  "hla_fwd", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
                  "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step",
-                 "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output", "hla_ahla_fwd"):
+                 "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output", "hla_ahla_fwd",
+                 "hla_ahla_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -382,7 +384,8 @@ def alloc_ahla_state(lead, d, dv, device):
 
 
 def _ahla_struct(st):
-    return AhlaState(*(st[k].data_ptr() for k in ("P", "m", "E", "n", "X")))
+    return AhlaState(*(None if st.get(k) is None else st[k].data_ptr()
+                       for k in ("P", "m", "E", "n", "X")))
 
 
 def ahla_chunk_summaries(q, k, v, chunk, gamma=None, out=None):
@@ -440,4 +443,20 @@ def ahla_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=Fals
     _check(lib().hla_ahla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
                               _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()),
            "hla_ahla_fwd")
+    return o, den
+
+
+def ahla_decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, den=None):
+    """One AHLA decode step; q, k [N, H, d], v [N, H, dv]; `state` (dict with
+    P, m, E, n) is updated in place.  Returns (o [N, H, dv] fp32, den or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    N, H, d = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=torch.float32, device=q.device)
+    st = _ahla_struct(state)
+    _check(lib().hla_ahla_decode_step(N, H, d, dv, _dtype_code(q), int(bool(normalize)), float(eps),
+                                      _ptr(gamma), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
+                                      _ptr(o), _ptr(den), _stream()), "hla_ahla_decode_step")
     return o, den

@@ -265,6 +265,11 @@ hla_status hla_unmasked_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv,
  * hla_ahla_fwd: the three on one stream, the summaries kept in `workspace`
  *   (hla_ahla_fwd_workspace_bytes(p) = B*H*n*(2 d dv + 2 d + d d) floats, not
  *   overlapping q, k or v).
+ * hla_ahla_decode_step: one token per unit applied in place to P, m, E, n
+ *   ([N, H, ...] fp32; X is not used and may be NULL); o = E'^T q (or divided
+ *   by q.n' + eps), den optional; arguments and errors as for hla_decode_step.
+ *   The state after a prefix is what hla_ahla_chunk_summaries writes with
+ *   chunk = T.
  */
 typedef struct { float *P, *m, *E, *n, *X; } hla_ahla_state;
 hla_status hla_ahla_chunk_summaries(const hla_problem* p, const void* q, const void* k,
@@ -276,6 +281,10 @@ size_t hla_ahla_fwd_workspace_bytes(const hla_problem* p);
 hla_status hla_ahla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
                         float* o, float* den, void* workspace, size_t workspace_bytes,
                         void* stream);
+hla_status hla_ahla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                                int32_t normalize, float eps, const float* gamma, const void* q,
+                                const void* k, const void* v, const hla_ahla_state* state,
+                                float* o, float* den, void* stream);
 
 /*
  * One streaming decode step (method section 1: the online update of the

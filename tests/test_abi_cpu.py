@@ -280,7 +280,15 @@ def test_ahla_sizes_and_checks(L):
     assert L.hla_ahla_scan(ctypes.byref(problem(chunk=0)), ctypes.byref(st), None) == SHAPE
     assert L.hla_ahla_output(ctypes.byref(p), Q, K, V, ctypes.byref(st), S_BASE, None, None) == ALIAS
     assert f(ctypes.byref(problem(B=0)), None, None, None, None, None, None, 0, None) == OK
+    dec = L.hla_ahla_decode_step
+    no_n = hla.AhlaState(S_BASE, S_BASE + step, S_BASE + 2 * step, None, None)
+    assert dec(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(no_n), O, None, None) == NULLP
+    assert dec(2, 2, 48, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(st), O, None, None) == UNSUP
+    assert dec(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V, ctypes.byref(st), Q, None, None) == ALIAS
+    assert dec(0, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, None, None, None, None, None, None, None) == OK
     if no_gpu():
+        assert dec(2, 2, 64, 64, hla.HLA_BF16, 1, 1e-6, None, Q, K, V, ctypes.byref(no_x), O, DEN,
+                   None) == HIP
         assert f(ctypes.byref(p), Q, K, V, O, None, W, need, None) == HIP
         assert L.hla_ahla_chunk_summaries(ctypes.byref(p), Q, K, V, ctypes.byref(st), None) == HIP
         assert L.hla_ahla_scan(ctypes.byref(p), ctypes.byref(st), None) == HIP

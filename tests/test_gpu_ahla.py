@@ -154,3 +154,72 @@ def test_ahla_workload_b4h16t16384d128_decayed(gpu):
     e_den = rel_err(host(dn.reshape(B * H, T)[sel]), den)
     say(f"  num {e_num:.3e}  den {e_den:.3e}  (tol {cfg['tol']})")
     assert e_num <= cfg["tol"] and e_den <= cfg["tol"]
+
+
+# (N, H, d, dv, dtype, decay)
+DECODE = [
+    (2, 3, 64, 64, "bf16", True),
+    (1, 2, 128, 128, "bf16", False),
+    (2, 2, 16, 32, "f32", True),
+    (1, 4, 128, 64, "bf16", True),
+    (2, 1, 32, 32, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[f"N{c[0]}H{c[1]}d{c[2]}dv{c[3]}-{c[4]}"
+                                              f"{'-decay' if c[5] else ''}" for c in DECODE])
+def test_ahla_decode_matches_oracle(gpu, case):
+    # both sides start from the same fp32 state (the oracle's prefix state
+    # rounded to fp32) and apply the same tokens one at a time
+    torch = gpu
+    N, H, d, dv, dt, decay = case
+    say("ahla decode", case)
+    T0, steps, eps = 80, 12, 1e-6
+    inp = synth.make_fwd_inputs(N, H, T0 + steps, d, dv, dt, seed=800 + d + dv, decay=decay)
+    uq, uk, uv, ug = inp.units()
+    _, _, st = O.serial_ahla(uq[:, :T0], uk[:, :T0], uv[:, :T0], ug)
+    keys = ("P", "m", "E", "n")
+    st32 = {key: st[key].astype(np.float32) for key in keys}
+    state = {key: torch.from_numpy(st32[key].reshape(N, H, *st32[key].shape[1:])).cuda() for key in keys}
+    ref = {key: st32[key].astype(np.float64) for key in keys}
+    q, k, v, g = to_dev(inp)
+    tol = 1e-4 if dt == "f32" else 2e-2
+    den = torch.empty(N, H, device="cuda")
+    for t in range(T0, T0 + steps):
+        o, _ = hla.ahla_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                    v[:, :, t].contiguous(), state, g, den=den)
+        torch.cuda.synchronize()
+        num_r, den_r, ref = O.serial_ahla(uq[:, t:t + 1], uk[:, t:t + 1], uv[:, t:t + 1], ug, ref)
+        assert rel_err(host(o).reshape(N * H, dv), num_r[:, 0]) <= tol, t
+        assert rel_err(host(den).reshape(N * H), den_r[:, 0]) <= tol, t
+    for key in keys:
+        assert rel_err(host(state[key]).reshape(ref[key].shape), ref[key]) <= 1e-5, key
+    on, _ = hla.ahla_decode_step(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(),
+                                 v[:, :, 0].contiguous(), state, g, normalize=True, eps=eps, den=den)
+    torch.cuda.synchronize()
+    num_r, den_r, _ = O.serial_ahla(uq[:, :1], uk[:, :1], uv[:, :1], ug, ref)
+    assert rel_err(host(den).reshape(N * H), den_r[:, 0]) <= tol
+    got_num = host(on).reshape(N * H, dv) * (host(den).reshape(N * H, 1) + eps)
+    assert rel_err(got_num, num_r[:, 0]) <= tol
+
+
+def test_ahla_prefill_then_decode(gpu):
+    # the summary of a prefix (one segment) is the state after it; decode steps
+    # from there give the forward's outputs for the following tokens
+    torch = gpu
+    N, H, d, dv, T0, steps = 2, 2, 64, 64, 128, 8
+    inp = synth.make_fwd_inputs(N, H, T0 + steps, d, dv, "bf16", seed=88, decay=True)
+    q, k, v, g = to_dev(inp)
+    st = hla.ahla_chunk_summaries(q[:, :, :T0].contiguous(), k[:, :, :T0].contiguous(),
+                                  v[:, :, :T0].contiguous(), T0, g)
+    state = {key: st[key][:, :, 0].contiguous() for key in ("P", "m", "E", "n")}
+    outs = []
+    for t in range(T0, T0 + steps):
+        o, _ = hla.ahla_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                    v[:, :, t].contiguous(), state, g)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    uq, uk, uv, ug = inp.units()
+    num, _, _ = O.serial_ahla(uq, uk, uv, ug)
+    got = np.stack([host(x).reshape(N * H, dv) for x in outs], axis=1)
+    assert rel_err(got, num[:, T0:]) <= 2e-2
