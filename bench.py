@@ -578,6 +578,79 @@ def bench_unmasked_decode(args, torch, np):
     return out
 
 
+def bench_ahla_decode(args, torch, np):
+    """AHLA decode steps on the decode workload's shapes; the prefix state is
+    the summary of the prefix as one segment."""
+    from causal_prefix_scan_amd import hla, synth
+    _, cfg = synth.DECODE_WORKLOAD
+    Nq, H, d, dv, P, seed = (cfg[x] for x in ("n_seq", "H", "d", "dv", "prefix_len", "seed"))
+    U = Nq * H
+    steps = args.steps
+    pre = synth.make_fwd_inputs(Nq, H, P, d, dv, "bf16", seed)
+    cv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    pq, pk, pv = cv(pre.q_bits), cv(pre.k_bits), cv(pre.v_bits)
+    mo = hla.ahla_chunk_summaries(pq, pk, pv, P)
+    state = {key: mo[key][:, :, 0].contiguous() for key in ("P", "m", "E", "n")}
+    del pq, pk, pv, mo
+    n_tok = args.warmup + steps
+    toks_host = [synth.make_decode_step(Nq, H, d, dv, seed, s) for s in range(n_tok)]
+    tq = torch.stack([cv(t[3][0]).reshape(Nq, H, d) for t in toks_host])
+    tk = torch.stack([cv(t[3][1]).reshape(Nq, H, d) for t in toks_host])
+    tv = torch.stack([cv(t[3][2]).reshape(Nq, H, dv) for t in toks_host])
+    o = torch.empty(Nq, H, dv, dtype=torch.float32, device="cuda")
+    den = torch.empty(Nq, H, dtype=torch.float32, device="cuda")
+    states64 = None
+    if not args.no_cpu_baseline:
+        states64 = {key: val.double().cpu().numpy().reshape(U, *val.shape[2:])
+                    for key, val in state.items()}
+    for s in range(args.warmup):
+        hla.ahla_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(args.warmup, n_tok):
+        hla.ahla_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / steps
+    value = U / (step_ms / 1e3)
+    state_bytes = (2 * d * dv + 2 * d) * 4
+    bytes_step = U * (2 * state_bytes + (2 * d + dv) * 2 + dv * 4 + 4)
+    achieved = bytes_step / (step_ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "unit-tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_seq": Nq, "H": H, "d": d, "dv": dv,
+                   "prefix_len": P, "normalize": True, "path": "hla_ahla_decode_step"},
+        "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "hla_ahla_decode_step", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"hla_ahla_decode_step@{args.workload}"),
+                     "bytes_per_launch": bytes_step, "avg_launch_ms": round(step_ms, 4)},
+    }
+    if states64 is not None:
+        from threadpoolctl import threadpool_limits
+        from oracle import hla_oracle as O
+        nb = min(args.cpu_steps, len(toks_host))
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            st = states64
+            for s in range(nb):
+                tq_, tk_, tv_ = toks_host[s][:3]
+                _, _, st = O.serial_ahla(tq_[:, None], tk_[:, None], tv_[:, None], None, st)
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": U * nb / dt, "unit": "unit-tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"fp64 AHLA decode steps, {U} units x {nb} steps ({dt:.1f} s)",
+                               "seconds": round(dt, 2)}
+    return out
+
+
 def bench_copy(args, torch):
     """A plain device-to-device copy of a known size: the reference the HBM
     traffic counters (FETCH_SIZE, WRITE_SIZE) are scaled by."""
@@ -623,6 +696,8 @@ def main():
         out = bench_unmasked_decode(args, torch, np)
     elif args.workload in AHLA_WORKLOADS:
         out = bench_ahla(args, torch, np)
+    elif args.workload == "ahla_decode_n64h32d128":
+        out = bench_ahla_decode(args, torch, np)
     else:
         out = bench_fwd(args, torch, np)
     print(json.dumps(out), flush=True)

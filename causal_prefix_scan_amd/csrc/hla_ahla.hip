@@ -48,7 +48,10 @@ struct ALayout {
   static constexpr size_t Vs = Ks + (size_t)AT * LDD * sizeof(T);
   static constexpr size_t AB = Vs + (size_t)AT * LDV * sizeof(T);
   static constexpr size_t TILE_END = AB + (size_t)AT * LDT * sizeof(T);
-  static constexpr size_t W = (TILE_END + 15) / 16 * 16;
+  // output tiles of the value blocks, fp32 [block][tok][LDO], held until den is known
+  static constexpr int LDO = 20;
+  static constexpr size_t OB = (TILE_END + 15) / 16 * 16;
+  static constexpr size_t W = OB + (size_t)(E / 16) * AT * LDO * 4;
   // pw, w1, wS, denv [AT]
   static constexpr size_t TOTAL = W + (size_t)(4 * AT) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
@@ -105,6 +108,7 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
   float* w1 = pw + AT;
   float* wS = w1 + AT;
   float* denv = wS + AT;
+  float* OBs = reinterpret_cast<float*>(smem + L::OB);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,11 +193,12 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
     load_rows(xv, NVc{}, gv, E, VCH, t0, Lt);
   };
 
-  load_tile(0);
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = ti * AT, Lt = tile_len(ti);
     const float gL = gpow(g, lgg, Lt);
-    // ---- stage the tile, the ones column and the update weights ----
+    // ---- stage the tile (loaded here: registers held across the tile would
+    //      push the 9-wave kernels into scratch), the ones column, the weights ----
+    load_tile(ti);
     store_rows(xq, NQc{}, Qs, D, L::LDD, QCH);
     store_rows(xk, NQc{}, Ks, D, L::LDD, QCH);
     store_rows(xv, NVc{}, Vs, E, L::LDV, VCH);
@@ -202,7 +207,6 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
     }
     __syncthreads();
-    if (ti + 1 < ntiles) load_tile(ti + 1);
 
     if constexpr (OUT) {
       // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau), over all waves ----
@@ -244,6 +248,7 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
           Ot[r] = MMT::mma(aq, be, Ot[r]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
 #pragma unroll
@@ -254,6 +259,7 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
         for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
           Rt[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * cb, lane), Rt[r]);
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep each phase's operand loads apart
       // A' R: R's tiles stacked along the tokens are the B operand
 #pragma unroll
       for (int kk = 0; kk < TSK; ++kk) {
@@ -274,7 +280,16 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
               if (a.den != nullptr && tau < Lt) a.den[tok0 + (size_t)t0 + tau] = Ot[r][j];
             }
           }
+      } else {
+        // park the output tile in LDS until den is known (frees its registers
+        // for the updates; written back in rows of 16-byte stores)
+        float* ob = OBs + (size_t)cb * AT * L::LDO;
+#pragma unroll
+        for (int r = 0; r < TR; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ob[(16 * r + 4 * lg4 + j) * L::LDO + lr] = Ot[r][j];
       }
+      __builtin_amdgcn_sched_barrier(0);
       // ---- P <- g^Lt P + K^T diag(w) V, E <- g^Lt E + K^T diag(w) R ----
 #pragma unroll
       for (int r = 0; r < TR; ++r)
@@ -298,18 +313,18 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
         }
       }
       __syncthreads();
-      // ---- outputs (normalised by den when asked) ----
+      // ---- outputs (normalised by den when asked): lane l writes columns
+      //      4 (l & 3) .. +3 of rows 16 i + (l >> 2) of this wave's block ----
       if (!mblk) {
-        float* go = a.o + (tok0 + (size_t)t0) * E;
+        float* go = a.o + (tok0 + (size_t)t0) * E + 16 * cb;
+        const float* ob = OBs + (size_t)cb * AT * L::LDO;
 #pragma unroll
-        for (int r = 0; r < TR; ++r)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tau = 16 * r + 4 * lg4 + j;
-            float o = Ot[r][j];
-            if (a.normalize) o = o / (denv[tau] + a.eps);
-            if (tau < Lt) go[(size_t)tau * E + 16 * cb + lr] = o;
-          }
+        for (int i = 0; i < AT / 16; ++i) {
+          const int tau = 16 * i + (lane >> 2), c4 = 4 * (lane & 3);
+          f32x4 o = *reinterpret_cast<const f32x4*>(ob + tau * L::LDO + c4);
+          if (a.normalize) o *= 1.f / (denv[tau] + a.eps);
+          if (tau < Lt) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + c4) = o;
+        }
       }
     } else {
       // ---- summary: P, E (and R) as above from zero, and X += K^T Q ----
