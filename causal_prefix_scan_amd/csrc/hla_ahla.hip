@@ -439,51 +439,61 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
 // Exclusive scan of the AHLA summaries of each unit, in order, for one
 // 16-column block of (P, E) (block ET: m, n as a single column):
 // prefix_s = run; run <- a run + x_s, E picking up a X_s P_run (a = g^chunk).
-// In place; X is only read.  One workgroup of 256 threads per (unit, block).
+// In place; X is only read.  One workgroup of 4 waves per (unit, block): X_s
+// is staged in LDS and X_s P_run runs on fp32 MFMA, each wave owning row tiles
+// of the block; the running E stays in the owning lanes' registers.
 template <int D, int E>
 __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
-  constexpr int ET = E / 16;
-  __shared__ float Xs[D][D + 1];
-  __shared__ float Pr[D][16];
+  constexpr int ET = E / 16, DT = D / 16, LX = D + 4;
+  constexpr int RB = (DT + 3) / 4;   // row tiles per wave
+  __shared__ __attribute__((aligned(16))) float Xs[D * LX];
+  __shared__ __attribute__((aligned(16))) float Pr[D * 16];
   const int unit = blockIdx.x / (ET + 1), cb = blockIdx.x % (ET + 1);
   const bool mblk = cb == ET;
-  const int ncol = mblk ? 1 : 16;
-  const int n = a.nspan, tid = threadIdx.x;
+  const int n = a.nspan, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg4 = lane >> 4;
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float sa = gpow(g, log2f(g), a.chunk);
-  constexpr int PER = (D * 16 + 255) / 256;
-  float er[PER];
+  for (int i = tid; i < D * 16; i += 256) Pr[i] = 0.f;
+  f32x4 er[RB];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) er[i] = 0.f;
-  for (int i = tid; i < D * 16; i += 256) Pr[i / 16][i % 16] = 0.f;
+  for (int b = 0; b < RB; ++b) er[b] = zero4();
+  const bool col_ok = !mblk || lr == 0;
   for (int s = 0; s < n; ++s) {
     const size_t sidx = (size_t)unit * n + s;
-    for (int i = tid; i < D * D; i += 256) Xs[i / D][i % D] = a.X[sidx * D * D + i];
+    const float* X = a.X + sidx * D * D;
+    for (int i = tid; i < D * D / 4; i += 256) {
+      const int r = (4 * i) / D, c = (4 * i) % D;
+      *reinterpret_cast<f32x4*>(Xs + r * LX + c) = reinterpret_cast<const f32x4*>(X)[i];
+    }
     __syncthreads();
-    float pn[PER], en[PER];
+    f32x4 cross[RB], pold[RB];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, row = idx / 16, col = idx % 16;
-      pn[i] = en[i] = 0.f;
-      if (idx < D * 16 && col < ncol) {
-        float cross = 0.f;
-        for (int k = 0; k < D; ++k) cross += Xs[row][k] * Pr[k][col];
-        float* pp = mblk ? a.m + sidx * D + row : a.P + (sidx * D + row) * E + 16 * cb + col;
-        float* ep = mblk ? a.n + sidx * D + row : a.E + (sidx * D + row) * E + 16 * cb + col;
-        const float px = *pp, ex = *ep;
-        *pp = Pr[row][col];
-        *ep = er[i];
-        pn[i] = sa * Pr[row][col] + px;
-        en[i] = sa * er[i] + ex + sa * cross;
+    for (int b = 0; b < RB; ++b) {
+      const int t = wave + 4 * b;
+      cross[b] = zero4();
+      if (t < DT) {
+        cross[b] = gemm_f32_tile<D>(Xs, LX, Pr, 16, 16 * t, 0, lane, cross[b]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pold[b][j] = Pr[(16 * t + 4 * lg4 + j) * 16 + lr];
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, row = idx / 16, col = idx % 16;
-      if (idx < D * 16 && col < ncol) {
-        Pr[row][col] = pn[i];
-        er[i] = en[i];
+    for (int b = 0; b < RB; ++b) {
+      const int t = wave + 4 * b;
+      if (t < DT && col_ok) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * t + 4 * lg4 + j;
+          float* pp = mblk ? a.m + sidx * D + row : a.P + (sidx * D + row) * E + 16 * cb + lr;
+          float* ep = mblk ? a.n + sidx * D + row : a.E + (sidx * D + row) * E + 16 * cb + lr;
+          const float px = *pp, ex = *ep;
+          *pp = pold[b][j];
+          *ep = er[b][j];
+          Pr[row * 16 + lr] = sa * pold[b][j] + px;
+          er[b][j] = sa * er[b][j] + ex + sa * cross[b][j];
+        }
       }
     }
     __syncthreads();
