@@ -1,7 +1,7 @@
 /*
  * hla.h -- C ABI of the masked second-order Higher-order Linear Attention
- * (HLA) forward, its decode step and the unmasked variant, for AMD Instinct
- * MI355X (gfx950).
+ * (HLA) forward, its decode step, the unmasked variant and the asymmetric
+ * variant AHLA, for AMD Instinct MI355X (gfx950).
  *
  * The method (summaries of "Higher-order Linear Attention", arXiv 2510.27258,
  * gist.science, Japanese and French pages):
