@@ -11,18 +11,17 @@
 // (0-based tau, Lt tokens, A'[tau][i] = g^(tau-i) q_tau.k_i for i <= tau):
 //   R = g^(tau+1) Q P + A' V,   O = g^(tau+1) Q E + A' R,
 //   P <- g^Lt P + K^T diag(w) V,  E <- g^Lt E + K^T diag(w) R,  w_i = g^(Lt-1-i).
-// m and n ride along as one more value column: V is extended by a column of
-// ones, so the extra column of P is m, that of R is q.m, that of E is n and
-// that of O is den.  A segment's summary also carries X = sum_i k_i q_i^T
-// (no decay): the combine (A then B, a = g^(length of B)) is
-//   P = a P_A + P_B, E = a E_A + E_B + a X_B P_A (m, n likewise).
+// A segment's summary also carries X = sum_i k_i q_i^T (no decay): the
+// combine (A then B, a = g^(length of B)) is P = a P_A + P_B,
+// E = a E_A + E_B + a X_B P_A (m, n likewise with m in place of P).
 //
 // One workgroup per (unit, segment) with one wave per 16-column block of the
-// extended values (dv / 16 + 1 waves); each wave keeps its blocks of P and E
-// in fp32 MFMA accumulators and its R tile in registers, so the waves share
-// only the staged tile and the A' scores.  The scan walks a unit's segments
-// in order, one workgroup per (unit, column block).  The decode step updates
-// (P, m, E, n) in place for one token per unit.
+// values (at least four waves); each wave keeps its blocks of P and E in fp32
+// MFMA accumulators and its R tile in registers, so the waves share only the
+// staged tile and the A' scores.  m and n (and q.m, den) are vector work for
+// all threads, in LDS.  The scan walks a unit's segments in order, one
+// workgroup per (unit, column block).  The decode step updates (P, m, E, n)
+// in place for one token per unit.
 #include <type_traits>
 
 #include "hla_device.h"
@@ -39,9 +38,8 @@ template <typename T, int D, int E>
 struct ALayout {
   static constexpr int PADT = 16 / (int)sizeof(T);
   static constexpr int DP = D < MM<T>::KS ? MM<T>::KS : D;
-  static constexpr int EX = E + 16;        // values plus the block holding the ones column
   static constexpr int LDD = DP + PADT;    // Q, K: [tok][d]
-  static constexpr int LDV = EX + PADT;    // V and the ones column: [tok][e]
+  static constexpr int LDV = E + PADT;     // V: [tok][e]
   static constexpr int LDT = AT + PADT;    // A': [tok][tok]
   static constexpr size_t Qs = 0;
   static constexpr size_t Ks = Qs + (size_t)AT * LDD * sizeof(T);
@@ -52,8 +50,8 @@ struct ALayout {
   static constexpr int LDO = 20;
   static constexpr size_t OB = (TILE_END + 15) / 16 * 16;
   static constexpr size_t W = OB + (size_t)(E / 16) * AT * LDO * 4;
-  // pw, w1, wS, denv [AT]
-  static constexpr size_t TOTAL = W + (size_t)(4 * AT) * 4;
+  // pw, w1, wS, qm, qn, rm, den [AT]; bpart [AT / 16][AT]; m, n [D]
+  static constexpr size_t TOTAL = W + (size_t)(7 * AT + (AT / 16) * AT + 2 * D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -97,18 +95,24 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
   constexpr int TSK = KS == 32 ? TR / 2 : TR * 4;          // K steps over the tile's tokens
   constexpr int XB = (DT + NW - 1) / NW;                   // X column blocks per wave
   constexpr bool OUT = MODE == A_OUTPUT;
-  static_assert(NW == ET + 1, "one wave per 16-column block of the extended values");
+  static_assert(NW >= ET && NW >= 4, "one wave per 16-column block of the values, at least four");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
   T* Ks = reinterpret_cast<T*>(smem + L::Ks);
   T* Vs = reinterpret_cast<T*>(smem + L::Vs);
   T* AB = reinterpret_cast<T*>(smem + L::AB);
+  float* OBs = reinterpret_cast<float*>(smem + L::OB);
   float* pw = reinterpret_cast<float*>(smem + L::W);
   float* w1 = pw + AT;
   float* wS = w1 + AT;
-  float* denv = wS + AT;
-  float* OBs = reinterpret_cast<float*>(smem + L::OB);
+  float* qm = wS + AT;
+  float* qn = qm + AT;
+  float* rmv = qn + AT;
+  float* denv = rmv + AT;
+  float* bpart = denv + AT;
+  float* mst = bpart + TR * AT;
+  float* nst = mst + D;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,8 +128,8 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
   const T* gv = reinterpret_cast<const T*>(a.v) + tok0 * E;
   const size_t sidx = (size_t)unit * nspan + span;
   const int ntiles = (Lspan + AT - 1) / AT;
-  const int cb = wave;                 // this wave's value block; block ET is (m, n)
-  const bool mblk = cb == ET;
+  const int cb = wave;                 // this wave's value block (none past ET)
+  const bool vblk = cb < ET;
 
   for (size_t i = tid; i < L::TILE_END / 16; i += NTHR)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
@@ -133,27 +137,22 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
     pw[tid] = gpow(g, lgg, tid);
     w1[tid] = gpow(g, lgg, tid + 1);
   }
+  for (int i = tid; i < D; i += NTHR) {
+    mst[i] = OUT ? a.m[sidx * D + i] : 0.f;
+    nst[i] = OUT ? a.n[sidx * D + i] : 0.f;
+  }
 
-  // P and E blocks of this wave (rows 16 t + 4 lg4 + j, column 16 cb + lr; in
-  // the (m, n) block only column 0 is non-zero), from the prefix or zero
+  // P and E blocks of this wave (rows 16 t + 4 lg4 + j, column 16 cb + lr),
+  // from the prefix or zero
   f32x4 Pt[DT], Et[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * t + 4 * lg4 + j;
-      float p = 0.f, e = 0.f;
-      if (OUT) {
-        if (!mblk) {
-          p = a.P[(sidx * D + row) * E + 16 * cb + lr];
-          e = a.E[(sidx * D + row) * E + 16 * cb + lr];
-        } else if (lr == 0) {
-          p = a.m[sidx * D + row];
-          e = a.n[sidx * D + row];
-        }
-      }
-      Pt[t][j] = p;
-      Et[t][j] = e;
+      const bool ld = OUT && vblk;
+      Pt[t][j] = ld ? a.P[(sidx * D + row) * E + 16 * cb + lr] : 0.f;
+      Et[t][j] = ld ? a.E[(sidx * D + row) * E + 16 * cb + lr] : 0.f;
     }
   f32x4 Xt[XB][DT];
 #pragma unroll
@@ -186,209 +185,144 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
   using NQc = std::integral_constant<int, NQ>;
   using NVc = std::integral_constant<int, NV>;
   auto tile_len = [&](int ti) { return (Lspan - ti * AT) < AT ? (Lspan - ti * AT) : AT; };
-  auto load_tile = [&](int ti) {
-    const int t0 = ti * AT, Lt = tile_len(ti);
-    load_rows(xq, NQc{}, gq, D, QCH, t0, Lt);
-    load_rows(xk, NQc{}, gk, D, QCH, t0, Lt);
-    load_rows(xv, NVc{}, gv, E, VCH, t0, Lt);
-  };
 
+  load_rows(xq, NQc{}, gq, D, QCH, 0, tile_len(0));
+  load_rows(xk, NQc{}, gk, D, QCH, 0, tile_len(0));
+  load_rows(xv, NVc{}, gv, E, VCH, 0, tile_len(0));
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = ti * AT, Lt = tile_len(ti);
     const float gL = gpow(g, lgg, Lt);
-    // ---- stage the tile (loaded here: registers held across the tile would
-    //      push the 9-wave kernels into scratch), the ones column, the weights ----
-    load_tile(ti);
+    // ---- stage the tile and the update weights; the next tile to registers ----
     store_rows(xq, NQc{}, Qs, D, L::LDD, QCH);
     store_rows(xk, NQc{}, Ks, D, L::LDD, QCH);
     store_rows(xv, NVc{}, Vs, E, L::LDV, VCH);
-    if (tid < AT) {
-      Vs[tid * L::LDV + E] = (T)(tid < Lt ? 1.f : 0.f);
-      wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+    if (tid < AT) wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+    __syncthreads();
+    if (ti + 1 < ntiles) {
+      const int t1 = t0 + AT, L1 = tile_len(ti + 1);
+      load_rows(xq, NQc{}, gq, D, QCH, t1, L1);
+      load_rows(xk, NQc{}, gk, D, QCH, t1, L1);
+      load_rows(xv, NVc{}, gv, E, VCH, t1, L1);
+    }
+
+    // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) and its row sums, over
+    //      all waves; q.m (and q.n) by all threads ----
+    for (int idx = wave; idx < NTRI; idx += NW) {
+      int r, c;
+      atri(idx, r, c);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DP; k0 += KS)
+        acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
+      const int tau = 16 * r + lr;
+      f32x4 val;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 16 * c + 4 * lg4 + j;
+        val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
+      }
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 y;
+        y[0] = (__bf16)val[0]; y[1] = (__bf16)val[1]; y[2] = (__bf16)val[2]; y[3] = (__bf16)val[3];
+        *reinterpret_cast<bf16x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = y;
+      } else {
+        *reinterpret_cast<f32x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = val;
+      }
+      const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+      if (lg4 == 0) bpart[c * AT + tau] = rs;
+    }
+    {
+      constexpr int LPR = NTHR / AT;
+      const int tau = tid / LPR, part = tid % LPR;
+      float sm = 0.f, sn = 0.f;
+      for (int c = part; c < D; c += LPR) {
+        const float x = (float)Qs[tau * L::LDD + c];
+        sm += x * mst[c];
+        sn += x * nst[c];
+      }
+#pragma unroll
+      for (int off = 1; off < LPR; off *= 2) {
+        sm += __shfl_xor(sm, off, 64);
+        sn += __shfl_xor(sn, off, 64);
+      }
+      if (part == 0) {
+        qm[tau] = sm;
+        qn[tau] = sn;
+      }
     }
     __syncthreads();
 
-    if constexpr (OUT) {
-      // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau), over all waves ----
-      for (int idx = wave; idx < NTRI; idx += NW) {
-        int r, c;
-        atri(idx, r, c);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < DP; k0 += KS)
-          acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
-        const int tau = 16 * r + lr;
-        f32x4 val;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 16 * c + 4 * lg4 + j;
-          val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
-        }
-        bf16x4 y;
-        if constexpr (sizeof(T) == 2) {
-          y[0] = (__bf16)val[0]; y[1] = (__bf16)val[1]; y[2] = (__bf16)val[2]; y[3] = (__bf16)val[3];
-          *reinterpret_cast<bf16x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = y;
-        } else {
-          *reinterpret_cast<f32x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = val;
-        }
-      }
-      __syncthreads();
-
-      // ---- R = g^(tau+1) Q P + A' V and O = g^(tau+1) Q E + A' R for this block ----
+    // ---- rm = q.m at every token (threads); the waves' value blocks ----
+    if (tid < AT) {
+      float r = w1[tid] * qm[tid];
+      for (int c = 0; c <= tid / 16; ++c) r += bpart[c * AT + tid];
+      rmv[tid] = r;
+    }
+    if (vblk) {
+      // R = g^(tau+1) Q P + A' V (and O = g^(tau+1) Q E + A' R in the output kernel)
       f32x4 Rt[TR], Ot[TR];
 #pragma unroll
       for (int r = 0; r < TR; ++r) { Rt[r] = zero4(); Ot[r] = zero4(); }
 #pragma unroll
       for (int kk = 0; kk < QSK; ++kk) {
-        const F bp = FR::acc_b(Pt, kk), be = FR::acc_b(Et, kk);
+        const F bp = FR::acc_b(Pt, kk);
+        F be;
+        if constexpr (OUT) be = FR::acc_b(Et, kk);
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
           const F aq = FR::perm(Qs, L::LDD, 16 * r, kk, lane);
           Rt[r] = MMT::mma(aq, bp, Rt[r]);
-          Ot[r] = MMT::mma(aq, be, Ot[r]);
+          if constexpr (OUT) Ot[r] = MMT::mma(aq, be, Ot[r]);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           Rt[r][j] *= w1[16 * r + 4 * lg4 + j];
-          Ot[r][j] *= w1[16 * r + 4 * lg4 + j];
+          if constexpr (OUT) Ot[r][j] *= w1[16 * r + 4 * lg4 + j];
         }
         for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
           Rt[r] = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * cb, lane), Rt[r]);
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep each phase's operand loads apart
-      // A' R: R's tiles stacked along the tokens are the B operand
+      if constexpr (OUT) {
+        // A' R: R's tiles stacked along the tokens are the B operand
 #pragma unroll
-      for (int kk = 0; kk < TSK; ++kk) {
-        const F br = FR::acc_b(Rt, kk);
+        for (int kk = 0; kk < TSK; ++kk) {
+          const F br = FR::acc_b(Rt, kk);
 #pragma unroll
-        for (int r = 0; r < TR; ++r)
-          if (KS * kk < 16 * r + 16) Ot[r] = MMT::mma(FR::perm(AB, L::LDT, 16 * r, kk, lane), br, Ot[r]);
-      }
-      // lane: O[tau = 16 r + 4 lg4 + j][16 cb + lr]; the (m, n) block's column 0 is den
-      if (mblk) {
-#pragma unroll
-        for (int r = 0; r < TR; ++r)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tau = 16 * r + 4 * lg4 + j;
-            if (lr == 0) {
-              denv[tau] = Ot[r][j];
-              if (a.den != nullptr && tau < Lt) a.den[tok0 + (size_t)t0 + tau] = Ot[r][j];
-            }
-          }
-      } else {
-        // park the output tile in LDS until den is known (frees its registers
-        // for the updates; written back in rows of 16-byte stores)
+          for (int r = 0; r < TR; ++r)
+            if (KS * kk < 16 * r + 16) Ot[r] = MMT::mma(FR::perm(AB, L::LDT, 16 * r, kk, lane), br, Ot[r]);
+        }
+        // park the output tile in LDS until den is known
         float* ob = OBs + (size_t)cb * AT * L::LDO;
 #pragma unroll
         for (int r = 0; r < TR; ++r)
 #pragma unroll
           for (int j = 0; j < 4; ++j) ob[(16 * r + 4 * lg4 + j) * L::LDO + lr] = Ot[r][j];
       }
-      __builtin_amdgcn_sched_barrier(0);
       // ---- P <- g^Lt P + K^T diag(w) V, E <- g^Lt E + K^T diag(w) R ----
 #pragma unroll
       for (int r = 0; r < TR; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j) Rt[r][j] *= wS[16 * r + 4 * lg4 + j];
-      {
-        F bv[NKS], bw[TSK];
+      F bv[NKS], bw[TSK];
 #pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
+      for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
 #pragma unroll
-        for (int kk = 0; kk < TSK; ++kk) bw[kk] = FR::acc_b(Rt, kk);
+      for (int kk = 0; kk < TSK; ++kk) bw[kk] = FR::acc_b(Rt, kk);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 p = Pt[t] * gL, e = Et[t] * gL;
+      for (int t = 0; t < DT; ++t) {
+        f32x4 p = Pt[t] * gL, e = Et[t] * gL;
 #pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) p = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bv[kk], p);
+        for (int kk = 0; kk < NKS; ++kk) p = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bv[kk], p);
 #pragma unroll
-          for (int kk = 0; kk < TSK; ++kk) e = MMT::mma(kt_acc_order<T>(Ks, L::LDD, kk, 16 * t, lane), bw[kk], e);
-          Pt[t] = p;
-          Et[t] = e;
-        }
+        for (int kk = 0; kk < TSK; ++kk) e = MMT::mma(kt_acc_order<T>(Ks, L::LDD, kk, 16 * t, lane), bw[kk], e);
+        Pt[t] = p;
+        Et[t] = e;
       }
-      __syncthreads();
-      // ---- outputs (normalised by den when asked): lane l writes columns
-      //      4 (l & 3) .. +3 of rows 16 i + (l >> 2) of this wave's block ----
-      if (!mblk) {
-        float* go = a.o + (tok0 + (size_t)t0) * E + 16 * cb;
-        const float* ob = OBs + (size_t)cb * AT * L::LDO;
-#pragma unroll
-        for (int i = 0; i < AT / 16; ++i) {
-          const int tau = 16 * i + (lane >> 2), c4 = 4 * (lane & 3);
-          f32x4 o = *reinterpret_cast<const f32x4*>(ob + tau * L::LDO + c4);
-          if (a.normalize) o *= 1.f / (denv[tau] + a.eps);
-          if (tau < Lt) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + c4) = o;
-        }
-      }
-    } else {
-      // ---- summary: P, E (and R) as above from zero, and X += K^T Q ----
-      // A' is needed for R: computed here over all waves
-      for (int idx = wave; idx < NTRI; idx += NW) {
-        int r, c;
-        atri(idx, r, c);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < DP; k0 += KS)
-          acc = MMT::mma(MMT::ld(Ks, L::LDD, 16 * c, k0, lane), MMT::ld(Qs, L::LDD, 16 * r, k0, lane), acc);
-        const int tau = 16 * r + lr;
-        f32x4 val;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 16 * c + 4 * lg4 + j;
-          val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
-        }
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 y;
-          y[0] = (__bf16)val[0]; y[1] = (__bf16)val[1]; y[2] = (__bf16)val[2]; y[3] = (__bf16)val[3];
-          *reinterpret_cast<bf16x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = y;
-        } else {
-          *reinterpret_cast<f32x4*>(AB + tau * L::LDT + 16 * c + 4 * lg4) = val;
-        }
-      }
-      __syncthreads();
-      f32x4 Rt[TR];
-#pragma unroll
-      for (int r = 0; r < TR; ++r) Rt[r] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < QSK; ++kk) {
-        const F bp = FR::acc_b(Pt, kk);
-#pragma unroll
-        for (int r = 0; r < TR; ++r) Rt[r] = MMT::mma(FR::perm(Qs, L::LDD, 16 * r, kk, lane), bp, Rt[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < TR; ++r) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Rt[r][j] *= w1[16 * r + 4 * lg4 + j] * wS[16 * r + 4 * lg4 + j];
-        for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
-          f32x4 av = zero4();
-          av = MMT::mma(MMT::ld(AB, L::LDT, 16 * r, k0, lane), FR::tr(Vs, L::LDV, k0, 16 * cb, lane), av);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) Rt[r][j] += av[j] * wS[16 * r + 4 * lg4 + j];
-        }
-      }
-      {
-        F bv[NKS], bw[TSK];
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) bv[kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * cb, lane), wS, kk * KS, lane);
-#pragma unroll
-        for (int kk = 0; kk < TSK; ++kk) bw[kk] = FR::acc_b(Rt, kk);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          f32x4 p = Pt[t] * gL, e = Et[t] * gL;
-#pragma unroll
-          for (int kk = 0; kk < NKS; ++kk) p = MMT::mma(FR::tr(Ks, L::LDD, kk * KS, 16 * t, lane), bv[kk], p);
-#pragma unroll
-          for (int kk = 0; kk < TSK; ++kk) e = MMT::mma(kt_acc_order<T>(Ks, L::LDD, kk, 16 * t, lane), bw[kk], e);
-          Pt[t] = p;
-          Et[t] = e;
-        }
-      }
+    }
+    if constexpr (!OUT) {
       // X[:, blocks] += K^T Q[:, blocks] (rows past the segment end are zero)
 #pragma unroll
       for (int b = 0; b < XB; ++b) {
@@ -404,24 +338,77 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
           }
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+
+    // ---- den = g^(tau+1) q.n + A' rm (output kernel); m and n updates:
+    //      TPD threads per row d, each over AT / TPD tokens ----
+    if constexpr (OUT) {
+      if (tid < AT) {
+        float dn = w1[tid] * qn[tid];
+        for (int i = 0; i <= tid; ++i) dn += (float)AB[tid * L::LDT + i] * rmv[i];
+        denv[tid] = dn;
+        if (a.den != nullptr && tid < Lt) a.den[tok0 + (size_t)t0 + tid] = dn;
+      }
+    }
+    {
+      constexpr int TPD = NTHR / D > 16 ? 16 : NTHR / D;
+      constexpr int TPT = AT / TPD;
+      if (tid < TPD * D) {
+        const int d = tid / TPD, part = tid % TPD;
+        float sm = 0.f, sn = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const int tau = part * TPT + i;
+          const float kw = wS[tau] * (float)Ks[tau * L::LDD + d];
+          sm += kw;
+          sn += kw * rmv[tau];
+        }
+#pragma unroll
+        for (int off = 1; off < TPD; off *= 2) {
+          sm += __shfl_xor(sm, off, 64);
+          sn += __shfl_xor(sn, off, 64);
+        }
+        if (part == 0) {
+          mst[d] = gL * mst[d] + sm;
+          nst[d] = gL * nst[d] + sn;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- outputs (normalised by den when asked): lane l writes columns
+    //      4 (l & 3) .. +3 of rows 16 i + (l >> 2) of this wave's block ----
+    if constexpr (OUT) {
+      if (vblk) {
+        float* go = a.o + (tok0 + (size_t)t0) * E + 16 * cb;
+        const float* ob = OBs + (size_t)cb * AT * L::LDO;
+#pragma unroll
+        for (int i = 0; i < AT / 16; ++i) {
+          const int tau = 16 * i + (lane >> 2), c4 = 4 * (lane & 3);
+          f32x4 o = *reinterpret_cast<const f32x4*>(ob + tau * L::LDO + c4);
+          if (a.normalize) o *= 1.f / (denv[tau] + a.eps);
+          if (tau < Lt) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + c4) = o;
+        }
+      }
     }
   }
 
   if constexpr (!OUT) {
+    if (vblk) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * t + 4 * lg4 + j;
-        if (!mblk) {
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * t + 4 * lg4 + j;
           a.P[(sidx * D + row) * E + 16 * cb + lr] = Pt[t][j];
           a.E[(sidx * D + row) * E + 16 * cb + lr] = Et[t][j];
-        } else if (lr == 0) {
-          a.m[sidx * D + row] = Pt[t][j];
-          a.n[sidx * D + row] = Et[t][j];
         }
-      }
+    }
+    for (int i = tid; i < D; i += NTHR) {
+      a.m[sidx * D + i] = mst[i];
+      a.n[sidx * D + i] = nst[i];
+    }
 #pragma unroll
     for (int b = 0; b < XB; ++b) {
       const int xc = wave + NW * b;
@@ -608,7 +595,7 @@ __global__ __launch_bounds__(ADEC) void ahla_decode_kernel(AhlaArgs a) {
 
 template <int D, int E>
 struct AWaves {
-  static constexpr int value = E / 16 + 1;
+  static constexpr int value = E / 16 > 4 ? E / 16 : 4;
 };
 
 template <int MODE>
