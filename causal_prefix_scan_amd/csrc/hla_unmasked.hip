@@ -26,11 +26,11 @@
 // accumulators; P goes through LDS (row-major, bf16 for bf16 inputs) for the
 // score tiles and the state term C^T p.  Q, K and V are double-buffered by
 // tile parity: the next tile is loaded into registers one tile ahead and
-// staged while the current one is in use, and the C waves apply a tile's C and
-// m updates one tile late, while the S waves form the next tile's P.  Three
-// barriers per tile in the output kernel: [P | C, m updates of the previous
-// tile] -> [p.m, B scores, staging of the next tile] -> [S update and the next
-// tile's A' | outputs].
+// staged while the current one is in use.  Three barriers per tile in the
+// output kernel; with bf16 inputs (P double-buffered) the C waves produce a
+// tile's outputs and apply its C and m updates one tile late, beside the S
+// waves' P and S update of the next tile: [P, S update of t | outputs, C and m
+// updates of t - 1] -> [p.m, B scores of t; staging of t + 1] -> [A' of t + 1].
 #include <type_traits>
 
 #include "hla_device.h"
@@ -55,8 +55,12 @@ struct ULayout {
   // Q, K, V double-buffered by tile parity: the next tile is staged while the
   // current one is in use, and the C update of a tile runs one tile late
   static constexpr size_t Qs = 0, Ks = 2 * QB, Vs = 4 * QB;
+  // bf16: P double-buffered, so that a tile's outputs (C waves) run beside the
+  // next tile's P (S waves); fp32 tiles leave no room for a second P buffer
+  static constexpr bool DEFER = sizeof(T) == 2;
+  static constexpr int NPS = DEFER ? 2 : 1;
   static constexpr size_t Ps = Vs + 2 * VB;
-  static constexpr size_t AB = Ps + QB;
+  static constexpr size_t AB = Ps + NPS * QB;
   static constexpr size_t BB = AB + (size_t)UT * LDT * sizeof(T);
   static constexpr size_t TILE_END = BB + (size_t)UT * LDT * sizeof(T);
   static constexpr size_t W = (TILE_END + 15) / 16 * 16;
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
   auto Qb = [&](int p) { return reinterpret_cast<T*>(smem + L::Qs + p * L::QB); };
   auto Kb = [&](int p) { return reinterpret_cast<T*>(smem + L::Ks + p * L::QB); };
   auto Vb = [&](int p) { return reinterpret_cast<T*>(smem + L::Vs + p * L::VB); };
-  T* Ps = reinterpret_cast<T*>(smem + L::Ps);
+  auto Psb = [&](int p) { return reinterpret_cast<T*>(smem + L::Ps + (L::NPS == 2 && p ? L::QB : 0)); };
   T* AB = reinterpret_cast<T*>(smem + L::AB);
   T* BB = reinterpret_cast<T*>(smem + L::BB);
   float* pw = reinterpret_cast<float*>(smem + L::W);
@@ -298,6 +302,149 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
     }
   };
 
+  // ---- pieces of the output kernel ----
+  // S waves: P[:, own] = g^(tau+1) Q S[:, own] + A' K[:, own] of the tile in
+  // buffers p, to P buffer p
+  auto p_tile = [&](int p) {
+    T* Px = Psb(p);
+    const T* Qx = Qb(p);
+    const T* Kx = Kb(p);
+    f32x4 pacc[SB][TR];
+#pragma unroll
+    for (int b = 0; b < SB; ++b)
+#pragma unroll
+      for (int r = 0; r < TR; ++r) pacc[b][r] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < QSK; ++kk) {
+      typename MMT::F bs[SB];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) bs[b] = FR::acc_b(St[b], kk);
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const auto aq = FR::perm(Qx, L::LDD, 16 * r, kk, lane);   // shared by the blocks
+#pragma unroll
+        for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+#pragma unroll
+      for (int b = 0; b < SB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pacc[b][r][j] *= w1[16 * r + 4 * lg4 + j];
+      for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+        const auto aa = MMT::ld(AB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+          pacc[b][r] = MMT::mma(aa, FR::tr(Kx, L::LDD, k0, 16 * ((rw + NOWN * b) % DT), lane), pacc[b][r]);
+      }
+      // lane: P[tau = 16 r + 4 lg4 + j][d = 16 cb + lr]
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int cb = rw + NOWN * b;
+        if (SFULL || cb < DT) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Px[(16 * r + 4 * lg4 + j) * L::LDD + 16 * cb + lr] = (T)pacc[b][r][j];
+        }
+      }
+    }
+  };
+  // all waves: p.m and B[tau][j] = g^(tau-j) p_tau.q_j (j <= tau) of the tile in buffers p
+  auto score_tile = [&](int p) {
+    const T* Px = Psb(p);
+    {
+      constexpr int LPR = NTHR / UT;
+      const int tau = tid / LPR, part = tid % LPR;
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int c = part * (D / LPR); c < (part + 1) * (D / LPR); ++c)
+        ps[c & 1] += (float)Px[tau * L::LDD + c] * mst[c];
+      float acc = ps[0] + ps[1];
+#pragma unroll
+      for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
+      if (part == 0) pm[tau] = acc;
+    }
+    {
+      const T* Qx = Qb(p);
+      for (int idx = wave; idx < NTRI; idx += NW) {
+        int r, c;
+        utri(idx, r, c);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DP; k0 += KS)
+          acc = MMT::mma(MMT::ld(Qx, L::LDD, 16 * c, k0, lane), MMT::ld(Px, L::LDD, 16 * r, k0, lane), acc);
+        const int tau = 16 * r + lr;   // lane: position tau, values j = 16 c + 4 lg4 + jj
+        f32x4 val;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 16 * c + 4 * lg4 + jj;
+          val[jj] = j <= tau ? acc[jj] * pw[tau - j] : 0.f;
+        }
+        ustore4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
+        const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
+        if (lg4 == 0) bpart[c * UT + tau] = rs;
+      }
+    }
+  };
+  // C waves: O = g^(tau+1) P C + B V for tile tp (Ltp tokens, buffers pp), its
+  // B scores, p.m and row sums in BB, pm, bpart; written with its den
+  auto out_tile = [&](int tp, int Ltp, int pp) {
+    const T* Px = Psb(pp);
+    const T* Vx = Vb(pp);
+    float* go = a.o + (tok0 + (size_t)tp * UT) * E;
+    // O^T = C^T P^T + V^T B^T (C^T from the accumulators as the A
+    // operand: the A and B layouts are alike), so that a lane holds four
+    // adjacent columns of one token and stores them at once
+    f32x4 oacc[CB][TR];
+#pragma unroll
+    for (int b = 0; b < CB; ++b)
+#pragma unroll
+      for (int r = 0; r < TR; ++r) oacc[b][r] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < QSK; ++kk) {
+      typename MMT::F bc[CB];
+#pragma unroll
+      for (int b = 0; b < CB; ++b) bc[b] = FR::acc_b(St[b], kk);
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const auto bp = FR::perm(Px, L::LDD, 16 * r, kk, lane);   // shared by the blocks
+#pragma unroll
+        for (int b = 0; b < CB; ++b) oacc[b][r] = MMT::mma(bc[b], bp, oacc[b][r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+      const int tau = 16 * r + lr;
+#pragma unroll
+      for (int b = 0; b < CB; ++b) oacc[b][r] *= w1[tau];
+      for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
+        const auto bb = MMT::ld(BB, L::LDT, 16 * r, k0, lane);
+#pragma unroll
+        for (int b = 0; b < CB; ++b)
+          oacc[b][r] = MMT::mma(FR::tr(Vx, L::LDV, k0, 16 * ((rw + NOWN * b) % ET), lane), bb, oacc[b][r]);
+      }
+      float scale = 1.f;
+      if (a.normalize) {
+        float dn = w1[tau] * pm[tau];
+        for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
+        scale = 1.f / (dn + a.eps);
+      }
+      // lane: O[tau][e = 16 ce + 4 lg4 + j]
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        const int ce = rw + NOWN * b;
+        if ((CFULL || ce < ET) && tau < Ltp)
+          *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * ce + 4 * lg4) = oacc[b][r] * scale;
+      }
+    }
+    const int mt = tid - HT;
+    if (a.den != nullptr && mt < Ltp) {
+      float dn = w1[mt] * pm[mt];
+      for (int c = 0; c <= mt / 16; ++c) dn += bpart[c * UT + mt];
+      a.den[tok0 + (size_t)tp * UT + mt] = dn;
+    }
+  };
+
   // prologue: tile 0 to LDS, tile 1 to registers (and A' of tile 0)
   load_tile(0);
   store_tile(0);
@@ -314,159 +461,46 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
     const int p = ti & 1;
     const int t0 = ti * UT, Lt = tile_len(ti);
     const float gL = gpow(g, lgg, Lt);
-    if constexpr (OUT) {
-      // ---- S waves: P[:, own] = g^(tau+1) Q S[:, own] + A' K[:, own] -> Ps;
-      //      C waves: C and m updates of the previous tile ----
+    if constexpr (OUT && L::DEFER) {
+      // [S waves: P and S update of tile ti | C waves: outputs, C and m
+      // updates of tile ti - 1] -> [p.m, B scores of ti; stage ti + 1] -> [A' of ti + 1]
       if (sRole) {
-        const T* Qx = Qb(p);
-        const T* Kx = Kb(p);
-        f32x4 pacc[SB][TR];
-#pragma unroll
-        for (int b = 0; b < SB; ++b)
-#pragma unroll
-          for (int r = 0; r < TR; ++r) pacc[b][r] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < QSK; ++kk) {
-          typename MMT::F bs[SB];
-#pragma unroll
-          for (int b = 0; b < SB; ++b) bs[b] = FR::acc_b(St[b], kk);
-#pragma unroll
-          for (int r = 0; r < TR; ++r) {
-            const auto aq = FR::perm(Qx, L::LDD, 16 * r, kk, lane);   // shared by the blocks
-#pragma unroll
-            for (int b = 0; b < SB; ++b) pacc[b][r] = MMT::mma(aq, bs[b], pacc[b][r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < TR; ++r) {
-#pragma unroll
-          for (int b = 0; b < SB; ++b)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pacc[b][r][j] *= w1[16 * r + 4 * lg4 + j];
-          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
-            const auto aa = MMT::ld(AB, L::LDT, 16 * r, k0, lane);
-#pragma unroll
-            for (int b = 0; b < SB; ++b)
-              pacc[b][r] = MMT::mma(aa, FR::tr(Kx, L::LDD, k0, 16 * ((rw + NOWN * b) % DT), lane), pacc[b][r]);
-          }
-          // lane: P[tau = 16 r + 4 lg4 + j][d = 16 cb + lr]
-#pragma unroll
-          for (int b = 0; b < SB; ++b) {
-            const int cb = rw + NOWN * b;
-            if (SFULL || cb < DT) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) Ps[(16 * r + 4 * lg4 + j) * L::LDD + 16 * cb + lr] = (T)pacc[b][r][j];
-            }
-          }
-        }
+        p_tile(p);
+        s_update(p, gL);
       } else if (ti > 0) {
+        out_tile(ti - 1, UT, p ^ 1);   // only the last tile can be short
         c_update(p ^ 1, gL_prev);
       }
       __syncthreads();
-
-      // ---- all waves: p.m and B[tau][j] = g^(tau-j) p_tau.q_j (j <= tau) ----
-      {
-        constexpr int LPR = NTHR / UT;
-        const int tau = tid / LPR, part = tid % LPR;
-        float ps[2] = {0.f, 0.f};
-#pragma unroll
-        for (int c = part * (D / LPR); c < (part + 1) * (D / LPR); ++c)
-          ps[c & 1] += (float)Ps[tau * L::LDD + c] * mst[c];
-        float acc = ps[0] + ps[1];
-#pragma unroll
-        for (int off = 1; off < LPR; off *= 2) acc += __shfl_xor(acc, off, 64);
-        if (part == 0) pm[tau] = acc;
-      }
-      {
-        const T* Qx = Qb(p);
-        for (int idx = wave; idx < NTRI; idx += NW) {
-          int r, c;
-          utri(idx, r, c);
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int k0 = 0; k0 < DP; k0 += KS)
-            acc = MMT::mma(MMT::ld(Qx, L::LDD, 16 * c, k0, lane), MMT::ld(Ps, L::LDD, 16 * r, k0, lane), acc);
-          const int tau = 16 * r + lr;   // lane: position tau, values j = 16 c + 4 lg4 + jj
-          f32x4 val;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int j = 16 * c + 4 * lg4 + jj;
-            val[jj] = j <= tau ? acc[jj] * pw[tau - j] : 0.f;
-          }
-          ustore4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
-          const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
-          if (lg4 == 0) bpart[c * UT + tau] = rs;
-        }
-      }
-      // the next tile to the other parity's buffers (their last readers, the
-      // C and m updates of the previous tile, finished before this phase),
-      // then the tile after it to registers
+      score_tile(p);
       if (ti + 1 < ntiles) {
         store_tile(p ^ 1);
         set_weights(ti + 1);
         if (ti + 2 < ntiles) load_tile(ti + 2);
       }
       __syncthreads();
-
-      // ---- S waves: S update, then A' of the next tile; C waves:
-      //      O = g^(tau+1) P C + B V for their columns ----
+      if (ti + 1 < ntiles) {
+        a_tiles(p ^ 1, wave, NW);
+        __syncthreads();
+      }
+    } else if constexpr (OUT) {
+      // [S waves: P | C waves: C and m updates of the previous tile] ->
+      // [p.m, B scores; stage the next tile] -> [S waves: S update, next A' | C waves: outputs]
+      if (sRole) p_tile(p);
+      else if (ti > 0) c_update(p ^ 1, gL_prev);
+      __syncthreads();
+      score_tile(p);
+      if (ti + 1 < ntiles) {
+        store_tile(p ^ 1);
+        set_weights(ti + 1);
+        if (ti + 2 < ntiles) load_tile(ti + 2);
+      }
+      __syncthreads();
       if (sRole) {
         s_update(p, gL);
         if (ti + 1 < ntiles) a_tiles(p ^ 1, rw, NOWN);
       } else {
-        const T* Vx = Vb(p);
-        float* go = a.o + (tok0 + (size_t)t0) * E;
-        // O^T = C^T P^T + V^T B^T (C^T from the accumulators as the A
-        // operand: the A and B layouts are alike), so that a lane holds four
-        // adjacent columns of one token and stores them at once
-        f32x4 oacc[CB][TR];
-#pragma unroll
-        for (int b = 0; b < CB; ++b)
-#pragma unroll
-          for (int r = 0; r < TR; ++r) oacc[b][r] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < QSK; ++kk) {
-          typename MMT::F bc[CB];
-#pragma unroll
-          for (int b = 0; b < CB; ++b) bc[b] = FR::acc_b(St[b], kk);
-#pragma unroll
-          for (int r = 0; r < TR; ++r) {
-            const auto bp = FR::perm(Ps, L::LDD, 16 * r, kk, lane);   // shared by the blocks
-#pragma unroll
-            for (int b = 0; b < CB; ++b) oacc[b][r] = MMT::mma(bc[b], bp, oacc[b][r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < TR; ++r) {
-          const int tau = 16 * r + lr;
-#pragma unroll
-          for (int b = 0; b < CB; ++b) oacc[b][r] *= w1[tau];
-          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS) {
-            const auto bb = MMT::ld(BB, L::LDT, 16 * r, k0, lane);
-#pragma unroll
-            for (int b = 0; b < CB; ++b)
-              oacc[b][r] = MMT::mma(FR::tr(Vx, L::LDV, k0, 16 * ((rw + NOWN * b) % ET), lane), bb, oacc[b][r]);
-          }
-          float scale = 1.f;
-          if (a.normalize) {
-            float dn = w1[tau] * pm[tau];
-            for (int c = 0; c <= r; ++c) dn += bpart[c * UT + tau];
-            scale = 1.f / (dn + a.eps);
-          }
-          // lane: O[tau][e = 16 ce + 4 lg4 + j]
-#pragma unroll
-          for (int b = 0; b < CB; ++b) {
-            const int ce = rw + NOWN * b;
-            if ((CFULL || ce < ET) && tau < Lt)
-              *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * ce + 4 * lg4) = oacc[b][r] * scale;
-          }
-        }
-        const int mt = tid - HT;
-        if (a.den != nullptr && mt < Lt) {
-          float dn = w1[mt] * pm[mt];
-          for (int c = 0; c <= mt / 16; ++c) dn += bpart[c * UT + mt];
-          a.den[tok0 + (size_t)t0 + mt] = dn;
-        }
+        out_tile(ti, Lt, p);
       }
       __syncthreads();
     } else {
@@ -480,6 +514,9 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
       if (ti + 2 < ntiles) load_tile(ti + 2);
     }
     gL_prev = gL;
+  }
+  if constexpr (OUT && L::DEFER) {
+    if (!sRole) out_tile(ntiles - 1, tile_len(ntiles - 1), (ntiles - 1) & 1);
   }
 
   if constexpr (!OUT) {
