@@ -5,8 +5,9 @@
 A step is one pass of the chunk-parallel forward over the whole workload:
 segment summaries -> exclusive Blelloch scan -> outputs (three C-ABI calls
 on one stream; inputs already resident in HBM).  The decode workload times
-one streaming decode step for every (sequence, head); the unmasked workload
-times the unmasked variant's three calls.  Prints one JSON line.
+one streaming decode step for every (sequence, head); the unmasked_* and
+ahla_* workloads time the two further operators' calls on the same shapes.
+Prints one JSON line.
 """
 
 import argparse
@@ -236,214 +237,6 @@ def bench_fwd(args, torch, np):
     return out
 
 
-UNMASKED_WORKLOADS = {"unmasked_decay_bf16_b4h16t16384d128": "fwd_decay_bf16_b4h16t16384d128"}
-
-
-def cpu_baseline_unmasked(inp, ntok):
-    from threadpoolctl import threadpool_limits
-    from oracle import hla_oracle as O
-    uq, uk, uv, ug = inp.units()
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        O.serial_unmasked(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
-        dt = time.perf_counter() - t0
-    U = uq.shape[0]
-    return {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 serial recurrence of the unmasked variant, all {U} (batch, head) "
-                      f"units, first {ntok} of {uq.shape[1]} tokens ({dt:.1f} s)",
-            "seconds": round(dt, 2)}
-
-
-def bench_unmasked(args, torch, np):
-    """The unmasked variant on the inputs of a forward workload: segment
-    moments -> exclusive scan -> outputs (three C-ABI calls on one stream)."""
-    import ctypes
-    from causal_prefix_scan_amd import hla, synth
-    cfg = dict(synth.FWD_WORKLOADS[UNMASKED_WORKLOADS[args.workload]])
-    if args.chunk:
-        cfg["chunk"] = args.chunk
-    B, H, T, d, dv, chunk = (cfg[x] for x in ("B", "H", "T", "d", "dv", "chunk"))
-    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"],
-                                k_l2norm=cfg["k_l2norm"], decay=cfg["decay"])
-    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
-    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
-    g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
-    n = T // chunk
-    mo = hla.alloc_moments((B, H, n), d, dv, "cuda")
-    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
-    L = hla.lib()
-    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
-    st = hla._state_struct(mo)
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        r1 = L.hla_unmasked_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
-        if ev:
-            ev[1].record(stream)
-        r2 = L.hla_unmasked_scan(ctypes.byref(p), ctypes.byref(st), sp)
-        if ev:
-            ev[2].record(stream)
-        r3 = L.hla_unmasked_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
-                                   None, sp)
-        if ev:
-            ev[3].record(stream)
-        if r1 or r2 or r3:
-            raise RuntimeError(f"HLA call failed: {r1} {r2} {r3}")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
-    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
-    tokens = B * H * T
-    value = tokens / (step_ms / 1e3)
-    U = B * H
-    mom_bytes = U * n * (d * d + d * dv + d) * 4
-    io_bytes = tokens * (2 * d + dv) * 2
-    kernels = {
-        "hla_unmasked_chunk_summaries": dict(ms=ms[0], bytes=io_bytes + mom_bytes),
-        "hla_unmasked_scan": dict(ms=ms[1], bytes=2 * mom_bytes),
-        "hla_unmasked_output": dict(ms=ms[2], bytes=io_bytes + mom_bytes + tokens * dv * 4),
-    }
-    dom = max(kernels, key=lambda kname: kernels[kname]["ms"])
-    kd = kernels[dom]
-    achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
-    f_tok = credited_flops_per_token_unmasked(64, d, dv)
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg["dtype"], "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
-                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
-                   "path": "hla_unmasked_chunk_summaries + hla_unmasked_scan + hla_unmasked_output"},
-        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
-                          "peak_tflops": BF16_PEAK_TFLOPS,
-                          "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
-                     "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)},
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_unmasked(inp, min(args.cpu_tokens, T))
-    return out
-
-
-AHLA_WORKLOADS = {"ahla_decay_bf16_b4h16t16384d128": "fwd_decay_bf16_b4h16t16384d128"}
-
-
-def bench_ahla(args, torch, np):
-    """AHLA on the inputs of a forward workload: segment summaries -> scan ->
-    outputs (three C-ABI calls on one stream)."""
-    import ctypes
-    from causal_prefix_scan_amd import hla, synth
-    cfg = dict(synth.FWD_WORKLOADS[AHLA_WORKLOADS[args.workload]])
-    if args.chunk:
-        cfg["chunk"] = args.chunk
-    B, H, T, d, dv, chunk = (cfg[x] for x in ("B", "H", "T", "d", "dv", "chunk"))
-    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"],
-                                k_l2norm=cfg["k_l2norm"], decay=cfg["decay"])
-    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
-    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
-    g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
-    n = T // chunk
-    st = hla.alloc_ahla_state((B, H, n), d, dv, "cuda")
-    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
-    L = hla.lib()
-    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
-    sst = hla._ahla_struct(st)
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        r1 = L.hla_ahla_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(sst), sp)
-        if ev:
-            ev[1].record(stream)
-        r2 = L.hla_ahla_scan(ctypes.byref(p), ctypes.byref(sst), sp)
-        if ev:
-            ev[2].record(stream)
-        r3 = L.hla_ahla_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(sst), ptr(o), None, sp)
-        if ev:
-            ev[3].record(stream)
-        if r1 or r2 or r3:
-            raise RuntimeError(f"HLA call failed: {r1} {r2} {r3}")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
-    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
-    tokens = B * H * T
-    value = tokens / (step_ms / 1e3)
-    U = B * H
-    summ_bytes = U * n * (2 * d * dv + 2 * d + d * d) * 4
-    pre_bytes = U * n * (2 * d * dv + 2 * d) * 4
-    io_bytes = tokens * (2 * d + dv) * 2
-    kernels = {
-        "hla_ahla_chunk_summaries": dict(ms=ms[0], bytes=io_bytes + summ_bytes),
-        "hla_ahla_scan": dict(ms=ms[1], bytes=summ_bytes + pre_bytes),
-        "hla_ahla_output": dict(ms=ms[2], bytes=io_bytes + pre_bytes + tokens * dv * 4),
-    }
-    dom = max(kernels, key=lambda kname: kernels[kname]["ms"])
-    kd = kernels[dom]
-    achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
-    f_tok = credited_flops_per_token_ahla(64, d, dv)
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg["dtype"], "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
-                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
-                   "path": "hla_ahla_chunk_summaries + hla_ahla_scan + hla_ahla_output"},
-        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
-                          "peak_tflops": BF16_PEAK_TFLOPS,
-                          "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
-                     "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)},
-    }
-    if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_limits
-        from oracle import hla_oracle as O
-        uq, uk, uv, ug = inp.units()
-        ntok = min(args.cpu_tokens, T)
-        with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            O.serial_ahla(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
-            dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"fp64 serial AHLA recurrence, all {U} (batch, head) units, "
-                                         f"first {ntok} of {T} tokens ({dt:.1f} s)",
-                               "seconds": round(dt, 2)}
-    return out
-
-
 def bench_decode(args, torch, np):
     from causal_prefix_scan_amd import hla, synth
     name, cfg = synth.DECODE_WORKLOAD
@@ -505,83 +298,145 @@ def bench_decode(args, torch, np):
     return out
 
 
-def bench_unmasked_decode(args, torch, np):
-    """Decode steps of the unmasked variant on the decode workload's shapes;
-    the prefix state is the moments of the prefix as one segment."""
+# The two further operators on the same machinery: segment summaries, scan and
+# outputs through three C-ABI calls named <prefix>_chunk_summaries, _scan and
+# _output, and a decode step.
+def _variants():
+    from causal_prefix_scan_amd import hla
+    return {
+        "unmasked": dict(
+            prefix="hla_unmasked", keys=("S", "C", "m"), oracle="serial_unmasked",
+            alloc=hla.alloc_moments, struct=hla._state_struct,
+            summaries=hla.unmasked_chunk_summaries, decode=hla.unmasked_decode_step,
+            summary_floats=lambda d, dv: d * d + d * dv + d,
+            prefix_floats=lambda d, dv: d * d + d * dv + d,
+            flops=credited_flops_per_token_unmasked, name="unmasked variant"),
+        "ahla": dict(
+            prefix="hla_ahla", keys=("P", "m", "E", "n"), oracle="serial_ahla",
+            alloc=hla.alloc_ahla_state, struct=hla._ahla_struct,
+            summaries=hla.ahla_chunk_summaries, decode=hla.ahla_decode_step,
+            summary_floats=lambda d, dv: 2 * d * dv + 2 * d + d * d,
+            prefix_floats=lambda d, dv: 2 * d * dv + 2 * d,
+            flops=credited_flops_per_token_ahla, name="AHLA"),
+    }
+
+
+# variant workloads: name -> (variant, forward inputs they run on)
+VARIANT_FWD = {"unmasked_decay_bf16_b4h16t16384d128": ("unmasked", "fwd_decay_bf16_b4h16t16384d128"),
+               "ahla_decay_bf16_b4h16t16384d128": ("ahla", "fwd_decay_bf16_b4h16t16384d128")}
+VARIANT_DECODE = {"unmasked_decode_n64h32d128": "unmasked", "ahla_decode_n64h32d128": "ahla"}
+
+
+def bench_variant_fwd(args, torch, np):
+    """A variant on the inputs of a forward workload: segment summaries ->
+    scan -> outputs (three C-ABI calls on one stream), each timed with HIP events."""
+    import ctypes
     from causal_prefix_scan_amd import hla, synth
-    _, cfg = synth.DECODE_WORKLOAD
-    Nq, H, d, dv, P, seed = (cfg[x] for x in ("n_seq", "H", "d", "dv", "prefix_len", "seed"))
-    U = Nq * H
-    steps = args.steps
-    pre = synth.make_fwd_inputs(Nq, H, P, d, dv, "bf16", seed)
-    cv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
-    pq, pk, pv = cv(pre.q_bits), cv(pre.k_bits), cv(pre.v_bits)
-    mo = hla.unmasked_chunk_summaries(pq, pk, pv, P)
-    state = {key: val[:, :, 0].contiguous() for key, val in mo.items()}
-    del pq, pk, pv, mo
-    n_tok = args.warmup + steps
-    toks_host = [synth.make_decode_step(Nq, H, d, dv, seed, s) for s in range(n_tok)]
-    tq = torch.stack([cv(t[3][0]).reshape(Nq, H, d) for t in toks_host])
-    tk = torch.stack([cv(t[3][1]).reshape(Nq, H, d) for t in toks_host])
-    tv = torch.stack([cv(t[3][2]).reshape(Nq, H, dv) for t in toks_host])
-    o = torch.empty(Nq, H, dv, dtype=torch.float32, device="cuda")
-    den = torch.empty(Nq, H, dtype=torch.float32, device="cuda")
-    states64 = None
-    if not args.no_cpu_baseline:
-        states64 = {key: val.double().cpu().numpy().reshape(U, *val.shape[2:])
-                    for key, val in state.items()}
-    for s in range(args.warmup):
-        hla.unmasked_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
-    torch.cuda.synchronize()
+    vname, base = VARIANT_FWD[args.workload]
+    V = _variants()[vname]
+    cfg = dict(synth.FWD_WORKLOADS[base])
+    if args.chunk:
+        cfg["chunk"] = args.chunk
+    B, H, T, d, dv, chunk = (cfg[x] for x in ("B", "H", "T", "d", "dv", "chunk"))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"],
+                                k_l2norm=cfg["k_l2norm"], decay=cfg["decay"])
+    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
+    n = T // chunk
+    st = V["alloc"]((B, H, n), d, dv, "cuda")
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
+    L = hla.lib()
+    f_sum = getattr(L, V["prefix"] + "_chunk_summaries")
+    f_scan = getattr(L, V["prefix"] + "_scan")
+    f_out = getattr(L, V["prefix"] + "_output")
+    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
+    sst = V["struct"](st)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        r1 = f_sum(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(sst), sp)
+        if ev:
+            ev[1].record(stream)
+        r2 = f_scan(ctypes.byref(p), ctypes.byref(sst), sp)
+        if ev:
+            ev[2].record(stream)
+        r3 = f_out(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(sst), ptr(o), None, sp)
+        if ev:
+            ev[3].record(stream)
+        if r1 or r2 or r3:
+            raise RuntimeError(f"HLA call failed: {r1} {r2} {r3}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for s in range(args.warmup, n_tok):
-        hla.unmasked_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
-    e1.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = e0.elapsed_time(e1) / steps
-    value = U / (step_ms / 1e3)
-    state_bytes = (d * d + d * dv + d) * 4
-    bytes_step = U * (2 * state_bytes + (2 * d + dv) * 2 + dv * 4 + 4)
-    achieved = bytes_step / (step_ms / 1e3) / 1e9
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "unit-tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "n_seq": Nq, "H": H, "d": d, "dv": dv,
-                   "prefix_len": P, "normalize": True, "path": "hla_unmasked_decode_step"},
-        "wall_ms_per_step": round(wall * 1e3 / steps, 4),
-        "roofline": {"bound": "hbm", "kernel": "hla_unmasked_decode_step", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"hla_unmasked_decode_step@{args.workload}"),
-                     "bytes_per_launch": bytes_step, "avg_launch_ms": round(step_ms, 4)},
+    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
+    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    tokens = B * H * T
+    value = tokens / (step_ms / 1e3)
+    U = B * H
+    summ_bytes = U * n * V["summary_floats"](d, dv) * 4
+    pre_bytes = U * n * V["prefix_floats"](d, dv) * 4
+    io_bytes = tokens * (2 * d + dv) * 2
+    names = [V["prefix"] + x for x in ("_chunk_summaries", "_scan", "_output")]
+    kernels = {
+        names[0]: dict(ms=ms[0], bytes=io_bytes + summ_bytes),
+        names[1]: dict(ms=ms[1], bytes=summ_bytes + pre_bytes),
+        names[2]: dict(ms=ms[2], bytes=io_bytes + pre_bytes + tokens * dv * 4),
     }
-    if states64 is not None:
+    dom = max(kernels, key=lambda kname: kernels[kname]["ms"])
+    kd = kernels[dom]
+    achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
+    f_tok = V["flops"](64, d, dv)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
+                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
+                   "path": " + ".join(names)},
+        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
+                          "peak_tflops": BF16_PEAK_TFLOPS,
+                          "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
+                     "bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 4)},
+    }
+    if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import hla_oracle as O
-        nb = min(args.cpu_steps, len(toks_host))
+        uq, uk, uv, ug = inp.units()
+        ntok = min(args.cpu_tokens, T)
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            st = states64
-            for s in range(nb):
-                tq_, tk_, tv_ = toks_host[s][:3]
-                _, _, st = O.serial_unmasked(tq_[:, None], tk_[:, None], tv_[:, None], None, st)
+            getattr(O, V["oracle"])(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
             dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": U * nb / dt, "unit": "unit-tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"fp64 unmasked decode steps, {U} units x {nb} steps ({dt:.1f} s)",
+        out["cpu_baseline"] = {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"fp64 serial recurrence of the {V['name']}, all {U} "
+                                         f"(batch, head) units, first {ntok} of {T} tokens ({dt:.1f} s)",
                                "seconds": round(dt, 2)}
     return out
 
 
-def bench_ahla_decode(args, torch, np):
-    """AHLA decode steps on the decode workload's shapes; the prefix state is
-    the summary of the prefix as one segment."""
-    from causal_prefix_scan_amd import hla, synth
+def bench_variant_decode(args, torch, np):
+    """Decode steps of a variant on the decode workload's shapes; the prefix
+    state is the summary of the prefix as one segment."""
+    from causal_prefix_scan_amd import synth
+    V = _variants()[VARIANT_DECODE[args.workload]]
     _, cfg = synth.DECODE_WORKLOAD
     Nq, H, d, dv, P, seed = (cfg[x] for x in ("n_seq", "H", "d", "dv", "prefix_len", "seed"))
     U = Nq * H
@@ -589,9 +444,9 @@ def bench_ahla_decode(args, torch, np):
     pre = synth.make_fwd_inputs(Nq, H, P, d, dv, "bf16", seed)
     cv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
     pq, pk, pv = cv(pre.q_bits), cv(pre.k_bits), cv(pre.v_bits)
-    mo = hla.ahla_chunk_summaries(pq, pk, pv, P)
-    state = {key: mo[key][:, :, 0].contiguous() for key in ("P", "m", "E", "n")}
-    del pq, pk, pv, mo
+    sm = V["summaries"](pq, pk, pv, P)
+    state = {key: sm[key][:, :, 0].contiguous() for key in V["keys"]}
+    del pq, pk, pv, sm
     n_tok = args.warmup + steps
     toks_host = [synth.make_decode_step(Nq, H, d, dv, seed, s) for s in range(n_tok)]
     tq = torch.stack([cv(t[3][0]).reshape(Nq, H, d) for t in toks_host])
@@ -601,52 +456,54 @@ def bench_ahla_decode(args, torch, np):
     den = torch.empty(Nq, H, dtype=torch.float32, device="cuda")
     states64 = None
     if not args.no_cpu_baseline:
-        states64 = {key: val.double().cpu().numpy().reshape(U, *val.shape[2:])
-                    for key, val in state.items()}
+        states64 = {key: val.double().cpu().numpy().reshape(U, *val.shape[2:]) for key, val in state.items()}
+    dec = V["decode"]
     for s in range(args.warmup):
-        hla.ahla_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+        dec(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
     for s in range(args.warmup, n_tok):
-        hla.ahla_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+        dec(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / steps
     value = U / (step_ms / 1e3)
-    state_bytes = (2 * d * dv + 2 * d) * 4
+    state_bytes = V["prefix_floats"](d, dv) * 4
     bytes_step = U * (2 * state_bytes + (2 * d + dv) * 2 + dv * 4 + 4)
     achieved = bytes_step / (step_ms / 1e3) / 1e9
+    kname = V["prefix"] + "_decode_step"
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "unit-tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n_seq": Nq, "H": H, "d": d, "dv": dv,
-                   "prefix_len": P, "normalize": True, "path": "hla_ahla_decode_step"},
+                   "prefix_len": P, "normalize": True, "path": kname},
         "wall_ms_per_step": round(wall * 1e3 / steps, 4),
-        "roofline": {"bound": "hbm", "kernel": "hla_ahla_decode_step", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"hla_ahla_decode_step@{args.workload}"),
+                     "traffic": measured_traffic(f"{kname}@{args.workload}"),
                      "bytes_per_launch": bytes_step, "avg_launch_ms": round(step_ms, 4)},
     }
     if states64 is not None:
         from threadpoolctl import threadpool_limits
         from oracle import hla_oracle as O
+        serial = getattr(O, V["oracle"])
         nb = min(args.cpu_steps, len(toks_host))
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
             st = states64
             for s in range(nb):
                 tq_, tk_, tv_ = toks_host[s][:3]
-                _, _, st = O.serial_ahla(tq_[:, None], tk_[:, None], tv_[:, None], None, st)
+                _, _, st = serial(tq_[:, None], tk_[:, None], tv_[:, None], None, st)
             dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": U * nb / dt, "unit": "unit-tokens/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"fp64 AHLA decode steps, {U} units x {nb} steps ({dt:.1f} s)",
+                               "sample": f"fp64 {V['name']} decode steps, {U} units x {nb} steps ({dt:.1f} s)",
                                "seconds": round(dt, 2)}
     return out
 
@@ -677,8 +534,8 @@ def bench_copy(args, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
-              "multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures a single GPU (got --gpus {args.gpus}): the kernels run per "
+              "GPU with no collectives, so there is no multi-GPU step to time", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -690,14 +547,10 @@ def main():
         out = bench_copy(args, torch)
     elif args.workload.startswith("decode"):
         out = bench_decode(args, torch, np)
-    elif args.workload in UNMASKED_WORKLOADS:
-        out = bench_unmasked(args, torch, np)
-    elif args.workload == "unmasked_decode_n64h32d128":
-        out = bench_unmasked_decode(args, torch, np)
-    elif args.workload in AHLA_WORKLOADS:
-        out = bench_ahla(args, torch, np)
-    elif args.workload == "ahla_decode_n64h32d128":
-        out = bench_ahla_decode(args, torch, np)
+    elif args.workload in VARIANT_FWD:
+        out = bench_variant_fwd(args, torch, np)
+    elif args.workload in VARIANT_DECODE:
+        out = bench_variant_decode(args, torch, np)
     else:
         out = bench_fwd(args, torch, np)
     print(json.dumps(out), flush=True)
