@@ -1,5 +1,5 @@
-"""CPU oracle for the masked second-order HLA forward, its decode step and
-the unmasked variant.
+"""CPU oracle for the masked second-order HLA forward, its decode step, the
+unmasked variant and the asymmetric variant AHLA.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this module: only the tests, the smoke check and the CPU-baseline leg
