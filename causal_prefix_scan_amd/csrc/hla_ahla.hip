@@ -41,17 +41,19 @@ struct ALayout {
   static constexpr int LDD = DP + PADT;    // Q, K: [tok][d]
   static constexpr int LDV = E + PADT;     // V: [tok][e]
   static constexpr int LDT = AT + PADT;    // A': [tok][tok]
-  static constexpr size_t Qs = 0;
-  static constexpr size_t Ks = Qs + (size_t)AT * LDD * sizeof(T);
-  static constexpr size_t Vs = Ks + (size_t)AT * LDD * sizeof(T);
-  static constexpr size_t AB = Vs + (size_t)AT * LDV * sizeof(T);
+  // Q, K, V double-buffered by tile parity: a tile is staged while the
+  // previous one's den and m, n updates still read its buffers
+  static constexpr size_t QB = (size_t)AT * LDD * sizeof(T);
+  static constexpr size_t VB = (size_t)AT * LDV * sizeof(T);
+  static constexpr size_t Qs = 0, Ks = 2 * QB, Vs = 4 * QB;
+  static constexpr size_t AB = Vs + 2 * VB;
   static constexpr size_t TILE_END = AB + (size_t)AT * LDT * sizeof(T);
   // output tiles of the value blocks, fp32 [block][tok][LDO], held until den is known
   static constexpr int LDO = 20;
   static constexpr size_t OB = (TILE_END + 15) / 16 * 16;
   static constexpr size_t W = OB + (size_t)(E / 16) * AT * LDO * 4;
-  // pw, w1, wS, qm, qn, rm, den [AT]; bpart [AT / 16][AT]; m, n [D]
-  static constexpr size_t TOTAL = W + (size_t)(7 * AT + (AT / 16) * AT + 2 * D) * 4;
+  // pw, w1, wS[2], qm, qn, rm, den [AT]; bpart [AT / 16][AT]; m, n [D]
+  static constexpr size_t TOTAL = W + (size_t)(8 * AT + (AT / 16) * AT + 2 * D) * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -98,15 +100,15 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
   static_assert(NW >= ET && NW >= 4, "one wave per 16-column block of the values, at least four");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  T* Qs = reinterpret_cast<T*>(smem + L::Qs);
-  T* Ks = reinterpret_cast<T*>(smem + L::Ks);
-  T* Vs = reinterpret_cast<T*>(smem + L::Vs);
+  auto Qb = [&](int p) { return reinterpret_cast<T*>(smem + L::Qs + p * L::QB); };
+  auto Kb = [&](int p) { return reinterpret_cast<T*>(smem + L::Ks + p * L::QB); };
+  auto Vb = [&](int p) { return reinterpret_cast<T*>(smem + L::Vs + p * L::VB); };
   T* AB = reinterpret_cast<T*>(smem + L::AB);
   float* OBs = reinterpret_cast<float*>(smem + L::OB);
   float* pw = reinterpret_cast<float*>(smem + L::W);
   float* w1 = pw + AT;
-  float* wS = w1 + AT;
-  float* qm = wS + AT;
+  auto wSb = [&](int p) { return w1 + AT + p * AT; };
+  float* qm = w1 + 3 * AT;
   float* qn = qm + AT;
   float* rmv = qn + AT;
   float* denv = rmv + AT;
@@ -186,24 +188,49 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
   using NVc = std::integral_constant<int, NV>;
   auto tile_len = [&](int ti) { return (Lspan - ti * AT) < AT ? (Lspan - ti * AT) : AT; };
 
-  load_rows(xq, NQc{}, gq, D, QCH, 0, tile_len(0));
-  load_rows(xk, NQc{}, gk, D, QCH, 0, tile_len(0));
-  load_rows(xv, NVc{}, gv, E, VCH, 0, tile_len(0));
+  auto load_tile = [&](int ti) {
+    const int t0 = ti * AT, Lt = tile_len(ti);
+    load_rows(xq, NQc{}, gq, D, QCH, t0, Lt);
+    load_rows(xk, NQc{}, gk, D, QCH, t0, Lt);
+    load_rows(xv, NVc{}, gv, E, VCH, t0, Lt);
+  };
+  // tile ti from registers to the buffers of its parity, with its update weights
+  auto stage_tile = [&](int ti) {
+    const int p = ti & 1, Lt = tile_len(ti);
+    store_rows(xq, NQc{}, Qb(p), D, L::LDD, QCH);
+    store_rows(xk, NQc{}, Kb(p), D, L::LDD, QCH);
+    store_rows(xv, NVc{}, Vb(p), E, L::LDV, VCH);
+    if (tid < AT) wSb(p)[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
+  };
+  // outputs of tile tp (normalised by den when asked): lane l writes columns
+  // 4 (l & 3) .. +3 of rows 16 i + (l >> 2) of this wave's block
+  auto store_out = [&](int tp, int Ltp) {
+    float* go = a.o + (tok0 + (size_t)tp * AT) * E + 16 * cb;
+    const float* ob = OBs + (size_t)cb * AT * L::LDO;
+#pragma unroll
+    for (int i = 0; i < AT / 16; ++i) {
+      const int tau = 16 * i + (lane >> 2), c4 = 4 * (lane & 3);
+      f32x4 o = *reinterpret_cast<const f32x4*>(ob + tau * L::LDO + c4);
+      if (a.normalize) o *= 1.f / (denv[tau] + a.eps);
+      if (tau < Ltp) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + c4) = o;
+    }
+  };
+
+  // Three barriers per tile:
+  //   [A' and q.m, q.n of tile t; outputs of t - 1] -> [q.m at every token;
+  //   the value blocks of t] -> [den, m, n updates of t; stage t + 1].
+  load_tile(0);
+  stage_tile(0);
+  __syncthreads();
+  if (ntiles > 1) load_tile(1);
   for (int ti = 0; ti < ntiles; ++ti) {
+    const int p = ti & 1;
     const int t0 = ti * AT, Lt = tile_len(ti);
     const float gL = gpow(g, lgg, Lt);
-    // ---- stage the tile and the update weights; the next tile to registers ----
-    store_rows(xq, NQc{}, Qs, D, L::LDD, QCH);
-    store_rows(xk, NQc{}, Ks, D, L::LDD, QCH);
-    store_rows(xv, NVc{}, Vs, E, L::LDV, VCH);
-    if (tid < AT) wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
-    __syncthreads();
-    if (ti + 1 < ntiles) {
-      const int t1 = t0 + AT, L1 = tile_len(ti + 1);
-      load_rows(xq, NQc{}, gq, D, QCH, t1, L1);
-      load_rows(xk, NQc{}, gk, D, QCH, t1, L1);
-      load_rows(xv, NVc{}, gv, E, VCH, t1, L1);
-    }
+    const T* Qs = Qb(p);
+    const T* Ks = Kb(p);
+    const T* Vs = Vb(p);
+    const float* wS = wSb(p);
 
     // ---- A'[tau][i] = g^(tau-i) q_tau.k_i (i <= tau) and its row sums, over
     //      all waves; q.m (and q.n) by all threads ----
@@ -249,6 +276,9 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
         qm[tau] = sm;
         qn[tau] = sn;
       }
+    }
+    if constexpr (OUT) {
+      if (vblk && ti > 0) store_out(ti - 1, AT);   // only the last tile can be short
     }
     __syncthreads();
 
@@ -375,23 +405,14 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
         }
       }
     }
-    __syncthreads();
-
-    // ---- outputs (normalised by den when asked): lane l writes columns
-    //      4 (l & 3) .. +3 of rows 16 i + (l >> 2) of this wave's block ----
-    if constexpr (OUT) {
-      if (vblk) {
-        float* go = a.o + (tok0 + (size_t)t0) * E + 16 * cb;
-        const float* ob = OBs + (size_t)cb * AT * L::LDO;
-#pragma unroll
-        for (int i = 0; i < AT / 16; ++i) {
-          const int tau = 16 * i + (lane >> 2), c4 = 4 * (lane & 3);
-          f32x4 o = *reinterpret_cast<const f32x4*>(ob + tau * L::LDO + c4);
-          if (a.normalize) o *= 1.f / (denv[tau] + a.eps);
-          if (tau < Lt) *reinterpret_cast<f32x4*>(go + (size_t)tau * E + c4) = o;
-        }
-      }
+    if (ti + 1 < ntiles) {
+      stage_tile(ti + 1);
+      if (ti + 2 < ntiles) load_tile(ti + 2);
     }
+    __syncthreads();
+  }
+  if constexpr (OUT) {
+    if (vblk) store_out(ntiles - 1, tile_len(ntiles - 1));
   }
 
   if constexpr (!OUT) {
