@@ -6,7 +6,8 @@ A step is one pass of the chunk-parallel forward over the whole workload:
 segment summaries -> exclusive Blelloch scan -> outputs (three C-ABI calls
 on one stream; inputs already resident in HBM).  The decode workload times
 one streaming decode step for every (sequence, head); the unmasked_* and
-ahla_* workloads time the two further operators' calls on the same shapes.
+ahla_* workloads time the two further operators' calls on the same shapes;
+the bwd_* workload times the backward pass (one hla_bwd call).
 Prints one JSON line.
 """
 
@@ -24,6 +25,10 @@ METRIC = "HLA fwd tokens/s (B·H·T/s) at 1 MI355X; % MFMA peak (chunk) / % HBM 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "fwd_decay_bf16_b4h16t16384d128"
+FP32_MFMA_PEAK_TFLOPS = 157.3
+BWD_WORKLOAD = "bwd_decay_bf16_b4h16t16384d128"
+BWD_CHUNK = 1024          # segment length of the backward's first-order sums
+BWD_TILE = 32             # tokens per tile of its kernels
 
 
 def credited_flops_per_token(c, d, dv):
@@ -508,6 +513,95 @@ def bench_variant_decode(args, torch, np):
     return out
 
 
+def credited_flops_per_token_bwd(c, d, dv):
+    """Credited flops per token of the backward: seven first-order sums
+    y = sum lam^(t-s) (a_t.b_s) c_s with (width of a and b, width of c) =
+    (d, d) for p, (dv, d) for dp, (d, dv) for dv, (dv, d) and (d, d) for dq,
+    2 x (d, d) for dk.  Each costs, per token, the state product and the
+    state update (2 Da Dc each) and the causal c-token tile's scores and
+    score-value product (c + 1 terms of Da and of Dc on average, 2 flops
+    each, halved by the mask)."""
+    pairs = [(d, d), (dv, d), (d, dv), (dv, d), (d, d), (d, d), (d, d)]
+    return sum(4 * a * b + (c + 1) * (a + b) for a, b in pairs)
+
+
+def bench_bwd(args, torch, np):
+    """The backward pass on the B4 H16 T16384 d128 decayed inputs: one
+    hla_bwd call per step (21 kernel launches on one stream), HIP events."""
+    import ctypes
+    from causal_prefix_scan_amd import hla, synth
+    cfg = dict(synth.FWD_WORKLOADS["fwd_decay_bf16_b4h16t16384d128"])
+    chunk = args.chunk or BWD_CHUNK
+    B, H, T, d, dv = (cfg[x] for x in ("B", "H", "T", "d", "dv"))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, cfg["dtype"], cfg["seed"], decay=cfg["decay"])
+    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    g = torch.from_numpy(inp.gamma).cuda()
+    do = torch.from_numpy(synth.make_upstream_grad(B, H, T, dv, cfg["seed"])).cuda()
+    dq = torch.empty(B, H, T, d, dtype=torch.float32, device="cuda")
+    dk = torch.empty_like(dq)
+    dvv = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
+    L = hla.lib()
+    p = hla.make_problem(q, v, chunk, g, False, 0.0)
+    ws = torch.empty(L.hla_bwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step():
+        r = L.hla_bwd(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(do), ptr(dq), ptr(dk), ptr(dvv),
+                      ptr(ws), ctypes.c_size_t(ws.numel()), sp)
+        if r:
+            raise RuntimeError(f"hla_bwd failed: {hla.status_string(r)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / args.steps
+    tokens = B * H * T
+    value = tokens / (step_ms / 1e3)
+    f_tok = credited_flops_per_token_bwd(BWD_TILE, d, dv)
+    tflops = value * f_tok / 1e12
+    out = {
+        "metric": "HLA backward tokens/s (B·H·T/s) at 1 MI355X", "value": round(value, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (bf16 inputs)", "data": "synthetic",
+        "config": {"workload": BWD_WORKLOAD, "B": B, "H": H, "T": T, "d": d, "dv": dv,
+                   "chunk": chunk, "decay": True, "normalize": False, "path": "hla_bwd"},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": {"bound": "mfma", "kernel": "hla_bwd (all launches of one call)",
+                     "achieved": round(tflops, 2), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_token": round(f_tok), "avg_launch_ms": round(step_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import hla_backward_oracle as BO
+        uq, uk, uv, ug = inp.units()
+        dou = do.cpu().numpy().reshape(B * H, T, dv)
+        ntok = min(512, T)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            BO.grad_states(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], dou[:, :ntok], ug)
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": B * H * ntok / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"fp64 serial forward/reverse state recurrences, all {B * H} "
+                                         f"(batch, head) units, first {ntok} of {T} tokens ({dt:.1f} s)",
+                               "seconds": round(dt, 2)}
+    return out
+
+
 def bench_copy(args, torch):
     """A plain device-to-device copy of a known size: the reference the HBM
     traffic counters (FETCH_SIZE, WRITE_SIZE) are scaled by."""
@@ -551,6 +645,8 @@ def main():
         out = bench_variant_fwd(args, torch, np)
     elif args.workload in VARIANT_DECODE:
         out = bench_variant_decode(args, torch, np)
+    elif args.workload == BWD_WORKLOAD:
+        out = bench_bwd(args, torch, np)
     else:
         out = bench_fwd(args, torch, np)
     print(json.dumps(out), flush=True)

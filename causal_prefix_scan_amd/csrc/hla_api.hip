@@ -800,3 +800,82 @@ hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t 
 }
 
 }  // extern "C"
+
+namespace {
+
+size_t bwd_state_floats(const hla_problem* p, const Sizes& z) {
+  const size_t w = (size_t)(p->d > p->dv ? p->d : p->dv);
+  return (size_t)z.units * (size_t)z.n * w * w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hla_bwd_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  const Sizes z = sizes_of(p);
+  return (2 * (size_t)z.units * (size_t)p->T * (size_t)p->d + bwd_state_floats(p, z)) * 4;
+}
+
+hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                   const float* dout, float* dq, float* dk, float* dv, void* workspace,
+                   size_t workspace_bytes, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (p->normalize != 0) return HLA_ERR_UNSUPPORTED;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!dout || !dq || !dk || !dv) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  const size_t need = hla_bwd_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  const size_t tok = (size_t)z.units * (size_t)p->T;
+  const size_t gq = tok * p->d * 4, gv = tok * p->dv * 4;
+  const void* ins[5] = {q, k, v, dout, workspace};
+  const size_t inb[5] = {z.qk_bytes, z.qk_bytes, z.v_bytes, z.o_bytes, need};
+  float* outs[3] = {dq, dk, dv};
+  const size_t outb[3] = {gq, gq, gv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], outb[i], ins[j], inb[j])) return HLA_ERR_ALIASING;
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return HLA_ERR_ALIASING;
+  }
+  for (int j = 0; j < 4; ++j)
+    if (overlap(workspace, need, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  if (hla_status e = device_ready()) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float* pbuf = static_cast<float*>(workspace);
+  float* dpbuf = pbuf + tok * p->d;
+  float* hbuf = dpbuf + tok * p->d;
+  const int bf = p->in_dtype == HLA_BF16 ? 1 : 0;
+  const hla::LaOperand Q{q, bf}, K{k, bf}, V{v, bf}, DO{dout, 0}, P{pbuf, 0}, DP{dpbuf, 0};
+  auto run = [&](hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
+                 int reverse, float* y, int accumulate) -> hla_status {
+    hla::LaArgs la;
+    la.a = a; la.b = b; la.c = c;
+    la.y = y; la.Hp = hbuf; la.gamma = p->gamma;
+    la.H = p->H; la.gexp = gexp;
+    la.T = p->T; la.seg = p->chunk; la.nseg = (int)z.n;
+    la.reverse = reverse; la.accumulate = accumulate;
+    return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s));
+  };
+  const int d = p->d, e = p->dv;
+  // p = S q; dp, dv over the future tokens (weights g^2); dq = M dO + S dp;
+  // dk from the future tokens' q and dp (weights g)
+  if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0)) return r;
+  if (hla_status r = run(V, DO, Q, e, d, 2, 1, dpbuf, 0)) return r;
+  if (hla_status r = run(P, Q, DO, d, e, 2, 1, dv, 0)) return r;
+  if (hla_status r = run(DO, V, P, e, d, 2, 0, dq, 0)) return r;
+  if (hla_status r = run(DP, K, K, d, d, 1, 0, dq, 1)) return r;
+  if (hla_status r = run(K, Q, DP, d, d, 1, 1, dk, 0)) return r;
+  return run(K, DP, Q, d, d, 1, 1, dk, 1);
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+}  // extern "C"

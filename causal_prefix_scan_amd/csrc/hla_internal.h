@@ -106,4 +106,22 @@ hipError_t launch_ahla_decode(int dtype, int d, int dv, int units, const AhlaArg
 
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 
+// First-order decayed sum y_t = sum_{s<=t} lam^(t-s) (a_t.b_s) c_s over the
+// walk order (tokens 0..T-1, or T-1..0 when reverse), the building block of
+// the backward pass.  Operands are [unit][T][width] rows, bf16 or fp32.
+struct LaOperand {
+  const void* p;
+  int bf16;
+};
+struct LaArgs {
+  LaOperand a, b, c;      // a, b: width Da; c: width Dc
+  float* y;               // [unit][T][Dc] fp32, written or accumulated
+  float* Hp;              // segment states [unit][nseg][Da][Dc] (workspace)
+  const float* gamma;     // [H] or null (gamma = 1)
+  int H, gexp;            // lam = gamma[unit % H] ^ gexp, gexp in {1, 2}
+  int T, seg, nseg;       // tokens per unit, tokens per segment, segments
+  int reverse, accumulate;
+};
+hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s);
+
 }  // namespace hla

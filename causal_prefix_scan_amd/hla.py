@@ -29,6 +29,7 @@ EXPORTS = (
     "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
     "hla_unmasked_decode_step", "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output",
     "hla_ahla_fwd_workspace_bytes", "hla_ahla_fwd", "hla_ahla_decode_step",
+    "hla_bwd_workspace_bytes", "hla_bwd",
 )
 
 
@@ -98,11 +99,13 @@ def lib():
     L.hla_ahla_fwd_workspace_bytes.argtypes, L.hla_ahla_fwd_workspace_bytes.restype = [pp], sz
     L.hla_ahla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hla_ahla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, pa, vp, vp, vp]
+    L.hla_bwd_workspace_bytes.argtypes, L.hla_bwd_workspace_bytes.restype = [pp], sz
+    L.hla_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
                  "hla_fwd", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
                  "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step",
                  "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output", "hla_ahla_fwd",
-                 "hla_ahla_decode_step"):
+                 "hla_ahla_decode_step", "hla_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -341,6 +344,31 @@ def unmasked_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=
                                   _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()),
            "hla_unmasked_fwd")
     return o, den
+
+
+def bwd(q, k, v, dout, chunk, gamma=None, workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of the unnormalised masked forward for the upstream gradient
+    dout [B, H, T, dv] (fp32): (dq, dk [B, H, T, d], dv [B, H, T, dv]) fp32."""
+    torch = _torch()
+    _need_cuda(q, k, v, dout, gamma)
+    if dout.dtype != torch.float32:
+        raise RuntimeError("dout must be float32")
+    B, H, T, d = q.shape
+    e = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, False, 0.0)
+    if dq is None:
+        dq = torch.empty(B, H, T, d, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(B, H, T, d, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(B, H, T, e, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = lib().hla_bwd_workspace_bytes(ctypes.byref(p))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().hla_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                         _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()),
+           "hla_bwd")
+    return dq, dk, dv
 
 
 def decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, den=None):

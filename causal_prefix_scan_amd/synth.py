@@ -13,7 +13,9 @@ Recipe (the pages use no dataset; every workload is synthetic):
   * per-head decay gamma_h = 1 - exp(U[ln 1e-3, ln 1e-1]) in float32, the
     same for every batch element;
   * decode steps draw from default_rng([seed, 1 + step]) so any step can be
-    regenerated on its own.
+    regenerated on its own;
+  * an upstream gradient dO for the backward is float32 standard normal of
+    the output's shape, from default_rng([seed, 0]).
 """
 
 import math
@@ -21,7 +23,7 @@ import math
 import numpy as np
 
 __all__ = ["bf16_round", "FwdInputs", "make_fwd_inputs", "make_decode_prefix",
-           "make_decode_step", "FWD_WORKLOADS", "DECODE_WORKLOAD"]
+           "make_decode_step", "make_upstream_grad", "FWD_WORKLOADS", "DECODE_WORKLOAD"]
 
 
 def bf16_round(x):
@@ -88,6 +90,12 @@ def make_fwd_inputs(B, H, T, d, dv, dtype="bf16", seed=0, k_l2norm=False, decay=
     if dtype == "f32":
         return FwdInputs(q, k, v, gamma, dtype)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_upstream_grad(B, H, T, dv, seed):
+    """Upstream gradient dL/do, float32 [B, H, T, dv], standard normal."""
+    rng = np.random.default_rng([seed, 0])
+    return rng.standard_normal((B, H, T, dv), dtype=np.float32)
 
 
 def make_decode_prefix(n_seq, H, d, dv, prefix_len, seed, n_unique=None):

@@ -299,6 +299,32 @@ hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t 
                            const void* q, const void* k, const void* v,
                            const hla_state* state, float* o, float* den, void* stream);
 
+/*
+ * Backward pass of the masked forward (unnormalised numerator).  The method
+ * section on parallel training by associative scans motivates it; the pages
+ * give no formula, so it is the plain gradient of the closed form
+ *   num_t = sum_{j<=t} sum_{i<=j} g^((t-i)+(t-j)) (q_t.k_i)(q_j.k_i) v_j
+ * with respect to q, k and v, for an upstream gradient dout = dL/d num
+ * ([B, H, T, dv] fp32).  gamma is not differentiated.
+ *
+ * With p_t = S_t q_t the forward is o_t = sum_{j<=t} g^(2(t-j)) (q_t.p_j) v_j,
+ * and the gradient is seven first-order decayed sums over the tokens (p; the
+ * others over the future tokens: dp, dv, dk, or the past: dq), each computed
+ * chunk-parallel: segment states of `chunk` tokens, an exclusive decayed
+ * running sum over the segments, then the outputs per segment.
+ *
+ * hla_bwd: writes dq, dk [B, H, T, d] and dv [B, H, T, dv] (fp32; they must
+ *   not overlap each other, the inputs or the workspace).  Problem fields as
+ *   for hla_fwd; normalize must be 0 (HLA_ERR_UNSUPPORTED otherwise).
+ * hla_bwd_workspace_bytes: the workspace hla_bwd needs (p and dp, fp32
+ *   [B, H, T, d] each, and the segment states, B*H*n*max(d, dv)^2 floats);
+ *   0 for an invalid or empty problem.
+ */
+size_t hla_bwd_workspace_bytes(const hla_problem* p);
+hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,
+                   const float* dout, float* dq, float* dk, float* dv,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -300,3 +300,32 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 16)
     with pytest.raises(RuntimeError, match="CUDA/HIP"):
         hla.fwd(q, q, q, 64)
+
+
+def test_bwd_sizes_and_checks(L):
+    p = problem()                       # B2 H3 T256 d64 dv64 chunk 64: n = 4
+    need = (2 * 6 * 256 * 64 + 6 * 4 * 64 * 64) * 4
+    assert L.hla_bwd_workspace_bytes(ctypes.byref(p)) == need
+    assert L.hla_bwd_workspace_bytes(ctypes.byref(problem(dv=128))) == (2 * 6 * 256 * 64 + 6 * 4 * 128 * 128) * 4
+    assert L.hla_bwd_workspace_bytes(ctypes.byref(problem(T=10))) == 0
+    DO, DQ, DK, DV = S_BASE, S_BASE + 0x1000000, S_BASE + 0x2000000, S_BASE + 0x3000000
+    W = 0x7000000000
+    f = L.hla_bwd
+    assert f(ctypes.byref(problem(T=10)), Q, K, V, DO, DQ, DK, DV, W, need, None) == SHAPE
+    assert f(ctypes.byref(problem(normalize=1)), Q, K, V, DO, DQ, DK, DV, W, need, None) == UNSUP
+    assert f(ctypes.byref(problem(d=48)), Q, K, V, DO, DQ, DK, DV, W, need, None) == UNSUP
+    assert f(ctypes.byref(p), None, K, V, DO, DQ, DK, DV, W, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, None, DQ, DK, DV, W, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, None, DV, W, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, DK, DV, None, need, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, DK, DV, W, need - 4, None) == WS
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ + 4, DK, DV, W, need, None) == MISAL
+    assert f(ctypes.byref(p), Q, K, V, DO + 8, DQ, DK, DV, W, need, None) == MISAL
+    assert f(ctypes.byref(p), Q, K, V, DO, Q + 64, DK, DV, W, need, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, DQ + 64, DV, W, need, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, DK, DO, W, need, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, DK, DV, DV - 16, need, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, DO, DQ, DK, DV, K, need, None) == ALIAS
+    assert f(ctypes.byref(problem(B=0)), None, None, None, None, None, None, None, None, 0, None) == OK
+    if no_gpu():
+        assert f(ctypes.byref(p), Q, K, V, DO, DQ, DK, DV, W, need, None) == HIP

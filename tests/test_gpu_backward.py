@@ -1,0 +1,141 @@
+"""GPU parity of the backward pass (gradients of the unnormalised masked forward).
+
+Calls go through the C ABI (hla_bwd, via the ctypes binding).  Small cases
+are compared element by element with the oracle's float64 autograd of the
+masked matrix form (ragged tiles, one or many segments, d != dv, decay, both
+input dtypes); the full-size decayed B4 H16 T16384 d128 workload runs in the
+launch configuration the benchmark times and is compared on sampled
+(batch, head) units with the oracle's serial forward/reverse state form
+(pinned to autograd and to finite differences in the CPU tests).
+
+Tolerance: the backward computes in fp32 from inputs that are exact in fp32
+(bf16 inputs are widened exactly), so its error is fp32 rounding over sums of
+up to a few thousand terms: max|got - want| / max|want| <= 1e-4 on the small
+cases and <= 1e-3 at T = 16384.
+"""
+
+import numpy as np
+import pytest
+
+from causal_prefix_scan_amd import hla, synth
+from oracle import hla_backward_oracle as BO
+
+from gpu_util import host, rel_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hla.lib()          # raises if the HIP library is missing: no silent fallback
+    return torch
+
+
+# (B, H, T, d, dv, chunk, dtype, decay)
+SMALL = [
+    (1, 2, 256, 16, 16, 64, "f32", False),
+    (1, 1, 200, 32, 32, 100, "bf16", True),       # 3 tiles + ragged 4 per segment
+    (2, 1, 320, 64, 32, 64, "bf16", True),        # n = 5, d > dv
+    (1, 2, 256, 128, 128, 256, "bf16", False),    # n = 1 (no segment scan)
+    (1, 1, 384, 128, 64, 96, "bf16", True),       # n = 4
+    (1, 2, 192, 64, 128, 64, "bf16", True),       # d < dv
+    (1, 1, 96, 64, 64, 32, "f32", True),          # n = 3
+    (1, 1, 600, 32, 64, 200, "bf16", False),      # ragged 8-token last tile
+]
+
+
+def case_id(c):
+    B, H, T, d, dv, chunk, dt, dec = c
+    return f"B{B}H{H}T{T}d{d}dv{dv}c{chunk}-{dt}{'-decay' if dec else ''}"
+
+
+def upstream(torch, B, H, T, dv, seed):
+    do = synth.make_upstream_grad(B, H, T, dv, seed)
+    return do, torch.from_numpy(do).cuda()
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[case_id(c) for c in SMALL])
+def test_bwd_matches_autograd(gpu, case):
+    torch = gpu
+    B, H, T, d, dv, chunk, dt, decay = case
+    say("backward case", case_id(case))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, dt, seed=500 + T + d, decay=decay)
+    q, k, v, g = to_dev(inp)
+    do_h, do = upstream(torch, B, H, T, dv, 500 + T)
+    dq, dk, dvv = hla.bwd(q, k, v, do, chunk, g)
+    torch.cuda.synchronize()
+    uq, uk, uv, ug = inp.units()
+    want = BO.grad_autograd(uq, uk, uv, do_h.reshape(B * H, T, dv), ug)
+    for name, got, w in zip(("dq", "dk", "dv"), (dq, dk, dvv), want):
+        e = rel_err(host(got).reshape(w.shape), w)
+        say(f"  {name} {e:.3e}")
+        assert e <= 1e-4, name
+
+
+def test_bwd_gamma_zero_closed_form(gpu):
+    # gamma = 0 keeps only i = j = t: o_t = (q_t.k_t)^2 v_t
+    torch = gpu
+    B, H, T, d, dv = 1, 2, 192, 64, 64
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, "bf16", seed=531)
+    q, k, v, _ = to_dev(inp)
+    g = torch.zeros(H, dtype=torch.float32, device="cuda")
+    do_h, do = upstream(torch, B, H, T, dv, 531)
+    dq, dk, dvv = hla.bwd(q, k, v, do, 64, g)
+    torch.cuda.synchronize()
+    qh, kh, vh = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v))
+    qk = np.sum(qh * kh, axis=-1)
+    dov = np.sum(do_h * vh, axis=-1)
+    assert rel_err(host(dvv), (qk ** 2)[..., None] * do_h) <= 1e-5
+    assert rel_err(host(dq), (2 * qk * dov)[..., None] * kh) <= 1e-5
+    assert rel_err(host(dk), (2 * qk * dov)[..., None] * qh) <= 1e-5
+
+
+def test_bwd_is_deterministic(gpu):
+    torch = gpu
+    B, H, T, d, dv = 1, 2, 512, 128, 128
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, "bf16", seed=532, decay=True)
+    q, k, v, g = to_dev(inp)
+    _, do = upstream(torch, B, H, T, dv, 532)
+    a = hla.bwd(q, k, v, do, 128, g)
+    b = hla.bwd(q, k, v, do, 128, g)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_chunk_does_not_change_the_result(gpu):
+    # the segment length only regroups the sums
+    torch = gpu
+    B, H, T, d, dv = 1, 1, 1024, 64, 64
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, "bf16", seed=533, decay=True)
+    q, k, v, g = to_dev(inp)
+    _, do = upstream(torch, B, H, T, dv, 533)
+    a = hla.bwd(q, k, v, do, 1024, g)
+    b = hla.bwd(q, k, v, do, 64, g)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert rel_err(host(y), host(x)) <= 1e-5
+
+
+def test_bwd_full_size_sampled_units(gpu):
+    # B4 H16 T16384 d128, decayed: the benchmark's backward workload and chunk
+    torch = gpu
+    from bench import BWD_CHUNK
+    B, H, T, d, dv = 4, 16, 16384, 128, 128
+    say("backward full size B4 H16 T16384 d128, chunk", BWD_CHUNK)
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, "bf16", seed=2, decay=True)
+    q, k, v, g = to_dev(inp)
+    do_h, do = upstream(torch, B, H, T, dv, 2)
+    dq, dk, dvv = hla.bwd(q, k, v, do, BWD_CHUNK, g)
+    torch.cuda.synchronize()
+    uq, uk, uv, ug = inp.units()
+    dou = do_h.reshape(B * H, T, dv)
+    for u in (0, 37):
+        want = BO.grad_states(uq[u:u + 1], uk[u:u + 1], uv[u:u + 1], dou[u:u + 1], ug[u:u + 1])
+        for name, got, w in zip(("dq", "dk", "dv"), (dq, dk, dvv), want):
+            e = rel_err(host(got.reshape(B * H, T, -1)[u]), w[0])
+            say(f"  unit {u} {name} {e:.3e}")
+            assert e <= 1e-3, (u, name)
