@@ -862,6 +862,7 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
     la.H = p->H; la.gexp = gexp;
     la.T = p->T; la.seg = p->chunk; la.nseg = (int)z.n;
     la.reverse = reverse; la.accumulate = accumulate;
+    la.mfma_bf16 = bf;
     return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s));
   };
   const int d = p->d, e = p->dv;

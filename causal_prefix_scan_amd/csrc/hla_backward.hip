@@ -17,9 +17,11 @@
 // forward: segment states H = sum_s lam^(L-1-s) b_s c_s^T, an exclusive
 // decayed running sum over the segments, then per 32-token tile
 // Y = lam^(tau+1) A H_prev + ((A B^T) o decay) C and H <- lam^L H + B^T diag(w) C.
-// Operands are staged to LDS as fp32 (bf16 inputs widened exactly) and
-// contracted with v_mfma_f32_16x16x4_f32, so the intermediates p, dp and the
-// upstream gradient keep full fp32 precision.
+// Precision follows the forward: with bf16 inputs every operand (q, k, v and
+// the fp32 intermediates p, dp and the upstream gradient) is staged to LDS as
+// bf16 and contracted with v_mfma_f32_16x16x32_bf16 into fp32 accumulators;
+// with fp32 inputs everything stays fp32 (v_mfma_f32_16x16x4_f32).  States
+// and outputs are fp32 either way.
 
 #include "hla_device.h"
 #include "hla_internal.h"
@@ -28,66 +30,115 @@ namespace hla {
 namespace {
 
 constexpr int LT = 32;     // tokens per tile
-constexpr int LNW = 4;     // waves per workgroup
-constexpr int LCB = 64;    // columns of c (and of the state) per workgroup: 16 per wave
 
 enum { L_SUMMARY = 0, L_OUTPUT = 1 };
 
-template <int Da, int Dc>
+// waves per workgroup: one per 16 columns of c, at least four
+template <int Dc>
+struct LWaves {
+  static constexpr int value = Dc / 16 > 4 ? Dc / 16 : 4;
+};
+
+template <typename T, int Da, int Dc>
 struct LLayout {
-  static constexpr int CB = Dc < LCB ? Dc : LCB;
-  static constexpr int LDA = Da + 4;       // a, b rows: [tok][Da]
-  static constexpr int LDC = CB + 16;      // c rows: [tok][CB]
-  static constexpr int LDS_ = LT + 4;      // scores: [tau][s]
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int DP = Da < MM<T>::KS ? MM<T>::KS : Da;   // zero-padded to one MFMA step
+  static constexpr int LDA = DP + (BF ? 8 : 4);     // a, b rows: [tok][DP]
+  static constexpr int LDC = Dc + (BF ? 8 : 16);    // c rows: [tok][Dc]
+  static constexpr int LDS_ = LT + (BF ? 8 : 4);    // scores: [tau][s]
   static constexpr size_t As = 0;
-  static constexpr size_t Bs = As + (size_t)LT * LDA * 4;
-  static constexpr size_t Cs = Bs + (size_t)LT * LDA * 4;
-  static constexpr size_t Ss = Cs + (size_t)LT * LDC * 4;
-  static constexpr size_t W = Ss + (size_t)LT * LDS_ * 4;
+  static constexpr size_t Bs = As + (size_t)LT * LDA * sizeof(T);
+  static constexpr size_t Cs = Bs + (size_t)LT * LDA * sizeof(T);
+  static constexpr size_t Ss = Cs + (size_t)LT * LDC * sizeof(T);
+  static constexpr size_t W = (Ss + (size_t)LT * LDS_ * sizeof(T) + 15) / 16 * 16;
   // pw (lam^n), w1 (lam^(tau+1)), wS (lam^(L-1-tau)) [LT]
   static constexpr size_t TOTAL = W + 3 * LT * 4;
   static_assert(TOTAL <= 64 * 1024, "LDS budget of the first-order sum kernel");
 };
 
-// Rows [t0, t0 + LT) of the walk, columns [c0, c0 + width) of an operand with
-// `ld` elements per token, widened to fp32 into LDS (rows past `end` are zero).
-__device__ __forceinline__ void stage_rows(const LaOperand& x, size_t unit_row0, int T, bool rev,
-                                           int t0, int end, int ld, int c0, int width, float* dst,
-                                           int ldd, int tid) {
-  const int n4 = LT * width / 4;
-  for (int i = tid; i < n4; i += 64 * LNW) {
-    const int row = i / (width / 4), col = (i % (width / 4)) * 4;
-    const int l = t0 + row;
-    f32x4 val = zero4();
-    if (l < end) {
-      const int phys = rev ? T - 1 - l : l;
-      const size_t off = (unit_row0 + (size_t)phys) * (size_t)ld + (size_t)(c0 + col);
-      if (x.bf16) {
-        const bf16x4 b = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(x.p) + off);
-        val = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-      } else {
-        val = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x.p) + off);
+template <typename T> struct Vec4;
+template <> struct Vec4<float> { using V = f32x4; };
+template <> struct Vec4<__bf16> { using V = bf16x4; };
+
+// One operand's rows [t0, t0 + LT) of the walk, columns [0, W), held in
+// registers as raw 4-element groups (8 bytes from a bf16 source, 16 from an
+// fp32 one) between the global loads and the LDS stores, so that a whole
+// tile's loads are in flight together and the next tile's overlap the
+// current one's products.  Rows past `end` read as zero.
+template <int W, int NTHR>
+struct TileRows {
+  static constexpr int G = W / 4;                      // groups per row
+  static constexpr int N = (LT * G + NTHR - 1) / NTHR; // groups per thread
+  uint4 r[N];
+
+  __device__ __forceinline__ void load(const LaOperand& op, size_t urow, int nT, bool rev, int t0,
+                                       int end, int tid) {
+    if (op.bf16) {
+      const __bf16* base = reinterpret_cast<const __bf16*>(op.p);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;
+        uint2 v = make_uint2(0, 0);
+        if (idx < LT * G && l < end) {
+          const size_t phys = (size_t)(rev ? nT - 1 - l : l);
+          v = *reinterpret_cast<const uint2*>(base + (urow + phys) * W + col);
+        }
+        r[i] = make_uint4(v.x, v.y, 0, 0);
+      }
+    } else {
+      const float* base = reinterpret_cast<const float*>(op.p);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;
+        r[i] = make_uint4(0, 0, 0, 0);
+        if (idx < LT * G && l < end) {
+          const size_t phys = (size_t)(rev ? nT - 1 - l : l);
+          r[i] = *reinterpret_cast<const uint4*>(base + (urow + phys) * W + col);
+        }
       }
     }
-    *reinterpret_cast<f32x4*>(dst + row * ldd + col) = val;
   }
-}
 
-// One workgroup per (unit, segment, block of 64 columns of c).  MODE
-// L_SUMMARY writes the segment's state; L_OUTPUT starts from the exclusive
-// prefix (or zero when there is none) and writes (or adds) y.
-template <int Da, int Dc, int MODE>
-__global__ __launch_bounds__(64 * LNW) void la_kernel(LaArgs a) {
-  using L = LLayout<Da, Dc>;
-  using MMT = MM<float>;
-  using FR = Frag<float>;
-  constexpr int CB = L::CB, NCB = Dc / CB, DT = Da / 16, TR = LT / 16;
+  template <typename T>
+  __device__ __forceinline__ void store(bool src_bf16, T* dst, int ldd, int tid) const {
+    using V = typename Vec4<T>::V;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4;
+      if (idx < LT * G) {
+        V v;
+        if (src_bf16) {
+          const bf16x4 b = __builtin_bit_cast(bf16x4, make_uint2(r[i].x, r[i].y));
+          v = V{(T)b[0], (T)b[1], (T)b[2], (T)b[3]};
+        } else {
+          const f32x4 f = __builtin_bit_cast(f32x4, r[i]);
+          v = V{(T)f[0], (T)f[1], (T)f[2], (T)f[3]};
+        }
+        *reinterpret_cast<V*>(dst + row * ldd + col) = v;
+      }
+    }
+  }
+};
+
+// One workgroup per (unit, segment); wave w owns columns 16 w .. +15 of c and
+// of the state.  MODE L_SUMMARY writes the segment's state; L_OUTPUT starts
+// from the exclusive prefix (or zero when there is none) and writes (or
+// adds) y.
+template <typename T, int Da, int Dc, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
+  using L = LLayout<T, Da, Dc>;
+  using MMT = MM<T>;
+  using FR = Frag<T>;
+  constexpr int NTHR = 64 * NW;
+  constexpr int KS = MMT::KS;
+  constexpr int DT = Da / 16, TR = LT / 16;
+  constexpr int QK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps over Da against the state
   constexpr bool OUT = MODE == L_OUTPUT;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  float* As = reinterpret_cast<float*>(smem + L::As);
-  float* Bs = reinterpret_cast<float*>(smem + L::Bs);
-  float* Cs = reinterpret_cast<float*>(smem + L::Cs);
-  float* Ss = reinterpret_cast<float*>(smem + L::Ss);
+  T* As = reinterpret_cast<T*>(smem + L::As);
+  T* Bs = reinterpret_cast<T*>(smem + L::Bs);
+  T* Cs = reinterpret_cast<T*>(smem + L::Cs);
+  T* Ss = reinterpret_cast<T*>(smem + L::Ss);
   float* pw = reinterpret_cast<float*>(smem + L::W);
   float* w1 = pw + LT;
   float* wS = w1 + LT;
@@ -95,22 +146,26 @@ __global__ __launch_bounds__(64 * LNW) void la_kernel(LaArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int cb = blockIdx.x % NCB;
-  const int us = blockIdx.x / NCB;
+  const int us = blockIdx.x;
   const int unit = us / a.nseg, seg = us - unit * a.nseg;
   float lam = a.gamma ? a.gamma[unit % a.H] : 1.f;
   if (a.gexp == 2) lam *= lam;
   const float lgl = log2f(lam);
-  const int T = a.T;
+  const int nT = a.T;
   const bool rev = a.reverse != 0;
-  const int s0 = seg * a.seg, s1 = s0 + a.seg < T ? s0 + a.seg : T;
-  const size_t urow = (size_t)unit * (size_t)T;
-  const bool cols = wave * 16 < CB;       // this wave owns columns 16 wave .. +15 of the block
-  const int col = cb * CB + 16 * wave + lr;
+  const int s0 = seg * a.seg, s1 = s0 + a.seg < nT ? s0 + a.seg : nT;
+  const size_t urow = (size_t)unit * (size_t)nT;
+  const bool cols = wave * 16 < Dc;       // this wave owns columns 16 wave .. +15
+  const int col = 16 * wave + lr;
   const size_t hbase = (size_t)us * Da * Dc;
 
+  // padding columns past Da and the score block above the diagonal are read
+  // as zeros by whole MFMA steps and never written
+  for (size_t i = tid; i < L::W / 16; i += NTHR)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   if (tid < LT) pw[tid] = gpow(lam, lgl, tid);
   if (tid < LT) w1[tid] = gpow(lam, lgl, tid + 1);
+  __syncthreads();
 
   // this wave's columns of the state: H[16 t + 4 lg + j][col]
   f32x4 Ht[DT];
@@ -120,29 +175,52 @@ __global__ __launch_bounds__(64 * LNW) void la_kernel(LaArgs a) {
     for (int j = 0; j < 4; ++j)
       Ht[t][j] = (OUT && a.Hp && cols) ? a.Hp[hbase + (size_t)(16 * t + 4 * lg + j) * Dc + col] : 0.f;
 
+  TileRows<Da, NTHR> ra, rb;
+  TileRows<Dc, NTHR> rc;
+  auto load_tile = [&](int t0) {
+    if (OUT) ra.load(a.a, urow, nT, rev, t0, s1, tid);
+    rb.load(a.b, urow, nT, rev, t0, s1, tid);
+    rc.load(a.c, urow, nT, rev, t0, s1, tid);
+  };
+  load_tile(s0);
   for (int t0 = s0; t0 < s1; t0 += LT) {
     const int Lt = s1 - t0 < LT ? s1 - t0 : LT;
-    if (OUT) stage_rows(a.a, urow, T, rev, t0, s1, Da, 0, Da, As, L::LDA, tid);
-    stage_rows(a.b, urow, T, rev, t0, s1, Da, 0, Da, Bs, L::LDA, tid);
-    stage_rows(a.c, urow, T, rev, t0, s1, Dc, cb * CB, CB, Cs, L::LDC, tid);
+    if (OUT) ra.store(a.a.bf16 != 0, As, L::LDA, tid);
+    rb.store(a.b.bf16 != 0, Bs, L::LDA, tid);
+    rc.store(a.c.bf16 != 0, Cs, L::LDC, tid);
     if (tid < LT) wS[tid] = tid < Lt ? gpow(lam, lgl, Lt - 1 - tid) : 0.f;
     __syncthreads();
+    // the previous outputs of this tile's rows (accumulating calls), then
+    // the next tile's loads, which stay in flight during the products
+    float yold[TR][4];
+    if constexpr (OUT) {
+#pragma unroll
+      for (int r = 0; r < TR; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int l = t0 + 16 * r + 4 * lg + j;
+          yold[r][j] = 0.f;
+          if (a.accumulate && cols && l < s1)
+            yold[r][j] = a.y[(urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col];
+        }
+    }
+    if (t0 + LT < s1) load_tile(t0 + LT);
 
     if constexpr (OUT) {
       // scores Ss[tau][s] = lam^(tau-s) a_tau.b_s for s <= tau (the lower 16x16
-      // blocks; the block above the diagonal is never read)
-      for (int idx = wave; idx < TR * (TR + 1) / 2; idx += LNW) {
+      // blocks; the block above the diagonal stays zero)
+      for (int idx = wave; idx < TR * (TR + 1) / 2; idx += NW) {
         int r = 0, c = idx;
         while (c > r) { c -= r + 1; ++r; }
         f32x4 acc = zero4();
 #pragma unroll 8
-        for (int k0 = 0; k0 < Da; k0 += 4)
+        for (int k0 = 0; k0 < L::DP; k0 += KS)
           acc = MMT::mma(MMT::ld(As, L::LDA, 16 * r, k0, lane), MMT::ld(Bs, L::LDA, 16 * c, k0, lane), acc);
         const int s = 16 * c + lr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tau = 16 * r + 4 * lg + j;
-          Ss[tau * L::LDS_ + s] = s <= tau ? acc[j] * pw[tau - s] : 0.f;
+          Ss[tau * L::LDS_ + s] = (T)(s <= tau ? acc[j] * pw[tau - s] : 0.f);
         }
       }
       __syncthreads();
@@ -152,20 +230,16 @@ __global__ __launch_bounds__(64 * LNW) void la_kernel(LaArgs a) {
         for (int r = 0; r < TR; ++r) {
           f32x4 y = zero4();
 #pragma unroll
-          for (int kk = 0; kk < Da / 4; ++kk) y = MMT::mma(FR::perm(As, L::LDA, 16 * r, kk, lane), FR::acc_b(Ht, kk), y);
+          for (int kk = 0; kk < QK; ++kk) y = MMT::mma(FR::perm(As, L::LDA, 16 * r, kk, lane), FR::acc_b(Ht, kk), y);
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] *= w1[16 * r + 4 * lg + j];
 #pragma unroll
-          for (int k0 = 0; k0 < 16 * r + 16; k0 += 4)
+          for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
             y = MMT::mma(MMT::ld(Ss, L::LDS_, 16 * r, k0, lane), FR::tr(Cs, L::LDC, k0, 16 * wave, lane), y);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int l = t0 + 16 * r + 4 * lg + j;
-            if (l < s1) {
-              const int phys = rev ? T - 1 - l : l;
-              float* dst = a.y + (urow + (size_t)phys) * Dc + col;
-              *dst = a.accumulate ? *dst + y[j] : y[j];
-            }
+            if (l < s1) a.y[(urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col] = yold[r][j] + y[j];
           }
         }
       }
@@ -173,14 +247,14 @@ __global__ __launch_bounds__(64 * LNW) void la_kernel(LaArgs a) {
     if (cols) {
       // H <- lam^Lt H + B^T diag(w) C
       const float gL = gpow(lam, lgl, Lt);
-      float bw[LT / 4];
+      typename MMT::F bw[LT / KS];
 #pragma unroll
-      for (int kk = 0; kk < LT / 4; ++kk) bw[kk] = FR::scale(FR::tr(Cs, L::LDC, 4 * kk, 16 * wave, lane), wS, 4 * kk, lane);
+      for (int kk = 0; kk < LT / KS; ++kk) bw[kk] = FR::scale(FR::tr(Cs, L::LDC, KS * kk, 16 * wave, lane), wS, KS * kk, lane);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         f32x4 h = Ht[t] * gL;
 #pragma unroll
-        for (int kk = 0; kk < LT / 4; ++kk) h = MMT::mma(FR::tr(Bs, L::LDA, 4 * kk, 16 * t, lane), bw[kk], h);
+        for (int kk = 0; kk < LT / KS; ++kk) h = MMT::mma(FR::tr(Bs, L::LDA, KS * kk, 16 * t, lane), bw[kk], h);
         Ht[t] = h;
       }
     }
@@ -216,13 +290,13 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int elems) {
   }
 }
 
-template <int MODE>
+template <typename T, int MODE>
 hipError_t launch_la_mode(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
 #define HLA_CASE(DA, DC)                                                                     \
   if (Da == DA && Dc == DC) {                                                                \
-    constexpr int NCB = DC / LLayout<DA, DC>::CB;                                            \
-    hipLaunchKernelGGL((la_kernel<DA, DC, MODE>), dim3((unsigned)units * a.nseg * NCB),      \
-                       dim3(64 * LNW), 0, s, a);                                             \
+    constexpr int NW = LWaves<DC>::value;                                                    \
+    hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW>), dim3((unsigned)units * a.nseg),     \
+                       dim3(64 * NW), 0, s, a);                                              \
     return hipGetLastError();                                                                \
   }
   HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(16, 64) HLA_CASE(16, 128)
@@ -233,11 +307,17 @@ hipError_t launch_la_mode(int Da, int Dc, int units, const LaArgs& a, hipStream_
   return hipErrorInvalidValue;
 }
 
+template <int MODE>
+hipError_t launch_la(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
+  return a.mfma_bf16 ? launch_la_mode<__bf16, MODE>(Da, Dc, units, a, s)
+                     : launch_la_mode<float, MODE>(Da, Dc, units, a, s);
+}
+
 }  // namespace
 
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
   if (a.nseg > 1) {
-    if (hipError_t e = launch_la_mode<L_SUMMARY>(Da, Dc, units, a, s)) return e;
+    if (hipError_t e = launch_la<L_SUMMARY>(Da, Dc, units, a, s)) return e;
     const int elems = Da * Dc;
     hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)units * ((elems + 255) / 256)), dim3(256), 0, s,
                        a, elems);
@@ -245,7 +325,7 @@ hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hi
   }
   LaArgs b = a;
   if (a.nseg == 1) b.Hp = nullptr;
-  return launch_la_mode<L_OUTPUT>(Da, Dc, units, b, s);
+  return launch_la<L_OUTPUT>(Da, Dc, units, b, s);
 }
 
 }  // namespace hla

@@ -121,6 +121,7 @@ struct LaArgs {
   int H, gexp;            // lam = gamma[unit % H] ^ gexp, gexp in {1, 2}
   int T, seg, nseg;       // tokens per unit, tokens per segment, segments
   int reverse, accumulate;
+  int mfma_bf16;          // contract in bf16 (fp32 accumulate) rather than fp32
 };
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s);
 
