@@ -27,8 +27,8 @@ BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "fwd_decay_bf16_b4h16t16384d128"
 FP32_MFMA_PEAK_TFLOPS = 157.3
 BWD_WORKLOAD = "bwd_decay_bf16_b4h16t16384d128"
-BWD_CHUNK = 1024          # segment length of the backward's first-order sums
-BWD_TILE = 32             # tokens per tile of its kernels
+BWD_CHUNK = 2048          # segment length of the backward's first-order sums
+BWD_TILE = 64             # tokens per tile of its kernels (bf16 inputs)
 
 
 def credited_flops_per_token(c, d, dv):

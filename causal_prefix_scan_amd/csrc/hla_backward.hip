@@ -15,7 +15,7 @@
 // Each is y_t = sum_{s<=t} lam^(t-s) (a_t.b_s) c_s in a walk order (forward,
 // or reverse for the sums over the future), computed chunk-parallel like the
 // forward: segment states H = sum_s lam^(L-1-s) b_s c_s^T, an exclusive
-// decayed running sum over the segments, then per 32-token tile
+// decayed running sum over the segments, then per tile (64 tokens; 32 for fp32)
 // Y = lam^(tau+1) A H_prev + ((A B^T) o decay) C and H <- lam^L H + B^T diag(w) C.
 // Precision follows the forward: with bf16 inputs every operand (q, k, v and
 // the fp32 intermediates p, dp and the upstream gradient) is staged to LDS as
@@ -29,8 +29,6 @@
 namespace hla {
 namespace {
 
-constexpr int LT = 32;     // tokens per tile
-
 enum { L_SUMMARY = 0, L_OUTPUT = 1 };
 
 // waves per workgroup: one per 16 columns of c, at least four
@@ -42,6 +40,7 @@ struct LWaves {
 template <typename T, int Da, int Dc>
 struct LLayout {
   static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int LT = BF ? 64 : 32;           // tokens per tile
   static constexpr int DP = Da < MM<T>::KS ? MM<T>::KS : Da;   // zero-padded to one MFMA step
   static constexpr int LDA = DP + (BF ? 8 : 4);     // a, b rows: [tok][DP]
   static constexpr int LDC = Dc + (BF ? 8 : 16);    // c rows: [tok][Dc]
@@ -65,7 +64,7 @@ template <> struct Vec4<__bf16> { using V = bf16x4; };
 // fp32 one) between the global loads and the LDS stores, so that a whole
 // tile's loads are in flight together and the next tile's overlap the
 // current one's products.  Rows past `end` read as zero.
-template <int W, int NTHR>
+template <int W, int NTHR, int LT>
 struct TileRows {
   static constexpr int G = W / 4;                      // groups per row
   static constexpr int N = (LT * G + NTHR - 1) / NTHR; // groups per thread
@@ -130,6 +129,7 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
   using MMT = MM<T>;
   using FR = Frag<T>;
   constexpr int NTHR = 64 * NW;
+  constexpr int LT = L::LT;
   constexpr int KS = MMT::KS;
   constexpr int DT = Da / 16, TR = LT / 16;
   constexpr int QK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps over Da against the state
@@ -175,8 +175,8 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
     for (int j = 0; j < 4; ++j)
       Ht[t][j] = (OUT && a.Hp && cols) ? a.Hp[hbase + (size_t)(16 * t + 4 * lg + j) * Dc + col] : 0.f;
 
-  TileRows<Da, NTHR> ra, rb;
-  TileRows<Dc, NTHR> rc;
+  TileRows<Da, NTHR, LT> ra, rb;
+  TileRows<Dc, NTHR, LT> rc;
   auto load_tile = [&](int t0) {
     if (OUT) ra.load(a.a, urow, nT, rev, t0, s1, tid);
     rb.load(a.b, urow, nT, rev, t0, s1, tid);
