@@ -25,7 +25,6 @@ METRIC = "HLA fwd tokens/s (B·H·T/s) at 1 MI355X; % MFMA peak (chunk) / % HBM 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "fwd_decay_bf16_b4h16t16384d128"
-FP32_MFMA_PEAK_TFLOPS = 157.3
 BWD_WORKLOAD = "bwd_decay_bf16_b4h16t16384d128"
 BWD_CHUNK = 2048          # segment length of the backward's first-order sums
 BWD_TILE = 64             # tokens per tile of its kernels (bf16 inputs)
@@ -525,6 +524,28 @@ def credited_flops_per_token_bwd(c, d, dv):
     return sum(4 * a * b + (c + 1) * (a + b) for a, b in pairs)
 
 
+def bwd_bytes_per_token(d, dv, ib, chunk):
+    """Algorithmic HBM bytes per token of one hla_bwd call: for each of the
+    seven sums (operands a, b, c and output y; ib bytes per input element,
+    fp32 for p, dp and dO), the summary pass reads b and c, the output pass
+    reads a, b, c and writes y (accumulating sums also read y), and the
+    segment states are written, read and rewritten by the scan and read by
+    the output pass (4 Da Dc fp32 per segment).  The S dp sum reuses the
+    prefixes of the p sum (the same states), so it has no summary pass."""
+    f = 4
+    sums = [  # (a, b, c, y, Da, Dc, accumulate, summary pass)
+        (d * ib, d * ib, d * ib, d * f, d, d, False, True),       # p = S q
+        (dv * ib, dv * f, d * ib, d * f, dv, d, False, True),     # dp
+        (d * f, d * ib, dv * f, dv * f, d, dv, False, True),      # dv
+        (dv * f, dv * ib, d * f, d * f, dv, d, False, True),      # dq = M dO
+        (d * f, d * ib, d * ib, d * f, d, d, True, False),        # dq += S dp
+        (d * ib, d * ib, d * f, d * f, d, d, False, True),        # dk (q, dp)
+        (d * ib, d * f, d * ib, d * f, d, d, True, True),         # dk += (dp, q)
+    ]
+    return sum(((b + c) + 3 * Da * Dc * f / chunk if summ else 0) + (a + b + c) + Da * Dc * f / chunk
+               + y * (2 if acc else 1) for a, b, c, y, Da, Dc, acc, summ in sums)
+
+
 def bench_bwd(args, torch, np):
     """The backward pass on the B4 H16 T16384 d128 decayed inputs: one
     hla_bwd call per step (21 kernel launches on one stream), HIP events."""
@@ -571,25 +592,30 @@ def bench_bwd(args, torch, np):
     value = tokens / (step_ms / 1e3)
     f_tok = credited_flops_per_token_bwd(BWD_TILE, d, dv)
     tflops = value * f_tok / 1e12
+    b_tok = bwd_bytes_per_token(d, dv, 2, chunk)
+    achieved = b_tok * tokens / (step_ms / 1e3) / 1e9
     out = {
         "metric": "HLA backward tokens/s (B·H·T/s) at 1 MI355X", "value": round(value, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 (bf16 inputs)", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": BWD_WORKLOAD, "B": B, "H": H, "T": T, "d": d, "dv": dv,
                    "chunk": chunk, "decay": True, "normalize": False, "path": "hla_bwd"},
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": {"bound": "mfma", "kernel": "hla_bwd (all launches of one call)",
-                     "achieved": round(tflops, 2), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "flops_per_token": round(f_tok), "avg_launch_ms": round(step_ms, 4)},
+        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(tflops, 1),
+                          "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "hla_bwd (the 21 launches of one call)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"hla_bwd@{BWD_WORKLOAD}") if not args.chunk else None,
+                     "bytes_per_launch": round(b_tok * tokens), "avg_launch_ms": round(step_ms, 4)},
     }
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import hla_backward_oracle as BO
         uq, uk, uv, ug = inp.units()
         dou = do.cpu().numpy().reshape(B * H, T, dv)
-        ntok = min(512, T)
+        ntok = min(2048, T)
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
             BO.grad_states(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], dou[:, :ntok], ug)

@@ -815,7 +815,8 @@ extern "C" {
 size_t hla_bwd_workspace_bytes(const hla_problem* p) {
   if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
   const Sizes z = sizes_of(p);
-  return (2 * (size_t)z.units * (size_t)p->T * (size_t)p->d + bwd_state_floats(p, z)) * 4;
+  return (2 * (size_t)z.units * (size_t)p->T * (size_t)p->d + bwd_state_floats(p, z) +
+          (size_t)z.units * (size_t)z.n * (size_t)p->d * (size_t)p->d) * 4;
 }
 
 hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,
@@ -852,27 +853,30 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
   float* pbuf = static_cast<float*>(workspace);
   float* dpbuf = pbuf + tok * p->d;
   float* hbuf = dpbuf + tok * p->d;
+  // prefixes of the states sum g^(..) k k^T, shared by p = S q and S dp
+  float* hkk = hbuf + bwd_state_floats(p, z);
   const int bf = p->in_dtype == HLA_BF16 ? 1 : 0;
   const hla::LaOperand Q{q, bf}, K{k, bf}, V{v, bf}, DO{dout, 0}, P{pbuf, 0}, DP{dpbuf, 0};
   auto run = [&](hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
-                 int reverse, float* y, int accumulate) -> hla_status {
+                 int reverse, float* y, int accumulate, float* states = nullptr,
+                 bool ready = false) -> hla_status {
     hla::LaArgs la;
     la.a = a; la.b = b; la.c = c;
-    la.y = y; la.Hp = hbuf; la.gamma = p->gamma;
+    la.y = y; la.Hp = states ? states : hbuf; la.gamma = p->gamma;
     la.H = p->H; la.gexp = gexp;
     la.T = p->T; la.seg = p->chunk; la.nseg = (int)z.n;
     la.reverse = reverse; la.accumulate = accumulate;
     la.mfma_bf16 = bf;
-    return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s));
+    return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s, ready));
   };
   const int d = p->d, e = p->dv;
   // p = S q; dp, dv over the future tokens (weights g^2); dq = M dO + S dp;
   // dk from the future tokens' q and dp (weights g)
-  if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0)) return r;
+  if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0, hkk)) return r;
   if (hla_status r = run(V, DO, Q, e, d, 2, 1, dpbuf, 0)) return r;
   if (hla_status r = run(P, Q, DO, d, e, 2, 1, dv, 0)) return r;
   if (hla_status r = run(DO, V, P, e, d, 2, 0, dq, 0)) return r;
-  if (hla_status r = run(DP, K, K, d, d, 1, 0, dq, 1)) return r;
+  if (hla_status r = run(DP, K, K, d, d, 1, 0, dq, 1, hkk, true)) return r;
   if (hla_status r = run(K, Q, DP, d, d, 1, 1, dk, 0)) return r;
   return run(K, DP, Q, d, d, 1, 1, dk, 1);
 } catch (...) {

@@ -315,8 +315,9 @@ hipError_t launch_la(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) 
 
 }  // namespace
 
-hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
-  if (a.nseg > 1) {
+hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
+                                  bool prefixes_ready) {
+  if (a.nseg > 1 && !prefixes_ready) {
     if (hipError_t e = launch_la<L_SUMMARY>(Da, Dc, units, a, s)) return e;
     const int elems = Da * Dc;
     hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)units * ((elems + 255) / 256)), dim3(256), 0, s,

@@ -123,6 +123,9 @@ struct LaArgs {
   int reverse, accumulate;
   int mfma_bf16;          // contract in bf16 (fp32 accumulate) rather than fp32
 };
-hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s);
+// prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
+// same b, c and lam as an earlier call), so only the output pass runs.
+hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
+                                  bool prefixes_ready = false);
 
 }  // namespace hla

@@ -320,8 +320,9 @@ hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t 
  *   intermediates and dout rounded to bf16 as MFMA operands) with fp32
  *   accumulation and state; fp32 inputs stay fp32 throughout.
  * hla_bwd_workspace_bytes: the workspace hla_bwd needs (p and dp, fp32
- *   [B, H, T, d] each, and the segment states, B*H*n*max(d, dv)^2 floats);
- *   0 for an invalid or empty problem.
+ *   [B, H, T, d] each; the segment states, B*H*n*max(d, dv)^2 floats; and
+ *   the prefixes of the k k^T states, B*H*n*d*d floats, which p = S q and
+ *   S dp share); 0 for an invalid or empty problem.
  */
 size_t hla_bwd_workspace_bytes(const hla_problem* p);
 hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,
