@@ -37,7 +37,7 @@ struct LWaves {
   static constexpr int value = Dc / 16 > 4 ? Dc / 16 : 4;
 };
 
-template <typename T, int Da, int Dc>
+template <typename T, int Da, int Dc, bool SYM>
 struct LLayout {
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int LT = BF ? 64 : 32;           // tokens per tile
@@ -49,10 +49,12 @@ struct LLayout {
   static constexpr size_t Bs = As + (size_t)LT * LDA * sizeof(T);
   static constexpr size_t Cs = Bs + (size_t)LT * LDA * sizeof(T);
   static constexpr size_t Ss = Cs + (size_t)LT * LDC * sizeof(T);
-  static constexpr size_t W = (Ss + (size_t)LT * LDS_ * sizeof(T) + 15) / 16 * 16;
+  static constexpr size_t Ss2 = Ss + (size_t)LT * LDS_ * sizeof(T);   // scores against c (SYM)
+  static constexpr size_t W = (Ss2 + (SYM ? (size_t)LT * LDS_ * sizeof(T) : 0) + 15) / 16 * 16;
   // pw (lam^n), w1 (lam^(tau+1)), wS (lam^(L-1-tau)) [LT]
   static constexpr size_t TOTAL = W + 3 * LT * 4;
-  static_assert(TOTAL <= 64 * 1024, "LDS budget of the first-order sum kernel");
+  static_assert(TOTAL <= 80 * 1024, "LDS budget of the first-order sum kernel (two per CU)");
+  static_assert(!SYM || (Da == Dc && DP == Da), "mirrored pair: b and c rows share one layout");
 };
 
 template <typename T> struct Vec4;
@@ -122,10 +124,12 @@ struct TileRows {
 // One workgroup per (unit, segment); wave w owns columns 16 w .. +15 of c and
 // of the state.  MODE L_SUMMARY writes the segment's state; L_OUTPUT starts
 // from the exclusive prefix (or zero when there is none) and writes (or
-// adds) y.
-template <typename T, int Da, int Dc, int MODE, int NW>
+// adds) y.  SYM adds the mirrored pair (b and c swapped) from the same staged
+// tiles: a second score block against c weighting b, and C^T diag(w) B in
+// the state update.
+template <typename T, int Da, int Dc, int MODE, int NW, bool SYM>
 __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
-  using L = LLayout<T, Da, Dc>;
+  using L = LLayout<T, Da, Dc, SYM>;
   using MMT = MM<T>;
   using FR = Frag<T>;
   constexpr int NTHR = 64 * NW;
@@ -139,6 +143,7 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
   T* Bs = reinterpret_cast<T*>(smem + L::Bs);
   T* Cs = reinterpret_cast<T*>(smem + L::Cs);
   T* Ss = reinterpret_cast<T*>(smem + L::Ss);
+  T* Ss2 = reinterpret_cast<T*>(smem + L::Ss2);
   float* pw = reinterpret_cast<float*>(smem + L::W);
   float* w1 = pw + LT;
   float* wS = w1 + LT;
@@ -208,19 +213,25 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
 
     if constexpr (OUT) {
       // scores Ss[tau][s] = lam^(tau-s) a_tau.b_s for s <= tau (the lower 16x16
-      // blocks; the block above the diagonal stays zero)
-      for (int idx = wave; idx < TR * (TR + 1) / 2; idx += NW) {
-        int r = 0, c = idx;
+      // blocks; the block above the diagonal stays zero); with SYM also
+      // Ss2[tau][s] = lam^(tau-s) a_tau.c_s
+      constexpr int NB = TR * (TR + 1) / 2;
+      for (int idx = wave; idx < (SYM ? 2 * NB : NB); idx += NW) {
+        const bool mirror = SYM && idx >= NB;
+        const T* Xs = mirror ? Cs : Bs;
+        const int ldx = mirror ? L::LDC : L::LDA;
+        T* So = mirror ? Ss2 : Ss;
+        int r = 0, c = mirror ? idx - NB : idx;
         while (c > r) { c -= r + 1; ++r; }
         f32x4 acc = zero4();
 #pragma unroll 8
         for (int k0 = 0; k0 < L::DP; k0 += KS)
-          acc = MMT::mma(MMT::ld(As, L::LDA, 16 * r, k0, lane), MMT::ld(Bs, L::LDA, 16 * c, k0, lane), acc);
+          acc = MMT::mma(MMT::ld(As, L::LDA, 16 * r, k0, lane), MMT::ld(Xs, ldx, 16 * c, k0, lane), acc);
         const int s = 16 * c + lr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tau = 16 * r + 4 * lg + j;
-          Ss[tau * L::LDS_ + s] = (T)(s <= tau ? acc[j] * pw[tau - s] : 0.f);
+          So[tau * L::LDS_ + s] = (T)(s <= tau ? acc[j] * pw[tau - s] : 0.f);
         }
       }
       __syncthreads();
@@ -236,6 +247,11 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
 #pragma unroll
           for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
             y = MMT::mma(MMT::ld(Ss, L::LDS_, 16 * r, k0, lane), FR::tr(Cs, L::LDC, k0, 16 * wave, lane), y);
+          if constexpr (SYM) {
+#pragma unroll
+            for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
+              y = MMT::mma(MMT::ld(Ss2, L::LDS_, 16 * r, k0, lane), FR::tr(Bs, L::LDA, k0, 16 * wave, lane), y);
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int l = t0 + 16 * r + 4 * lg + j;
@@ -245,16 +261,24 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
       }
     }
     if (cols) {
-      // H <- lam^Lt H + B^T diag(w) C
+      // H <- lam^Lt H + B^T diag(w) C (+ C^T diag(w) B with SYM)
       const float gL = gpow(lam, lgl, Lt);
-      typename MMT::F bw[LT / KS];
+      typename MMT::F bw[LT / KS], bw2[SYM ? LT / KS : 1];
 #pragma unroll
       for (int kk = 0; kk < LT / KS; ++kk) bw[kk] = FR::scale(FR::tr(Cs, L::LDC, KS * kk, 16 * wave, lane), wS, KS * kk, lane);
+      if constexpr (SYM) {
+#pragma unroll
+        for (int kk = 0; kk < LT / KS; ++kk) bw2[kk] = FR::scale(FR::tr(Bs, L::LDA, KS * kk, 16 * wave, lane), wS, KS * kk, lane);
+      }
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         f32x4 h = Ht[t] * gL;
 #pragma unroll
         for (int kk = 0; kk < LT / KS; ++kk) h = MMT::mma(FR::tr(Bs, L::LDA, KS * kk, 16 * t, lane), bw[kk], h);
+        if constexpr (SYM) {
+#pragma unroll
+          for (int kk = 0; kk < LT / KS; ++kk) h = MMT::mma(FR::tr(Cs, L::LDC, KS * kk, 16 * t, lane), bw2[kk], h);
+        }
         Ht[t] = h;
       }
     }
@@ -295,7 +319,15 @@ hipError_t launch_la_mode(int Da, int Dc, int units, const LaArgs& a, hipStream_
 #define HLA_CASE(DA, DC)                                                                     \
   if (Da == DA && Dc == DC) {                                                                \
     constexpr int NW = LWaves<DC>::value;                                                    \
-    hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW>), dim3((unsigned)units * a.nseg),     \
+    if (a.sym) {                                                                             \
+      if constexpr (DA == DC && DA >= MM<T>::KS) {                                           \
+        hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, true>),                           \
+                           dim3((unsigned)units * a.nseg), dim3(64 * NW), 0, s, a);          \
+        return hipGetLastError();                                                            \
+      }                                                                                      \
+      return hipErrorInvalidValue;                                                           \
+    }                                                                                        \
+    hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, false>), dim3((unsigned)units * a.nseg), \
                        dim3(64 * NW), 0, s, a);                                              \
     return hipGetLastError();                                                                \
   }

@@ -122,6 +122,9 @@ struct LaArgs {
   int T, seg, nseg;       // tokens per unit, tokens per segment, segments
   int reverse, accumulate;
   int mfma_bf16;          // contract in bf16 (fp32 accumulate) rather than fp32
+  // add the mirrored pair: y_t = sum lam^(t-s) [(a_t.b_s) c_s + (a_t.c_s) b_s],
+  // one state sum (b c^T + c b^T); needs Da == Dc, at least one MFMA K step
+  int sym = 0;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
 // same b, c and lam as an earlier call), so only the output pass runs.
