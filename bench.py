@@ -531,13 +531,14 @@ def bwd_bytes_per_token(d, dv, ib, chunk):
     reads a, b, c and writes y (accumulating sums also read y), and the
     segment states are written, read and rewritten by the scan and read by
     the output pass (4 Da Dc fp32 per segment).  The S dp sum reuses the
-    prefixes of the p sum (the same states), so it has no summary pass; the
-    two dk sums are one sum over the symmetric states (q dp^T + dp q^T)."""
+    prefixes of the p sum (the same states) and the dv sum those of the dp
+    sum (their transposes), so neither has a summary pass; the two dk sums
+    are one sum over the symmetric states (q dp^T + dp q^T)."""
     f = 4
     sums = [  # (a, b, c, y, Da, Dc, accumulate, summary pass)
         (d * ib, d * ib, d * ib, d * f, d, d, False, True),       # p = S q
         (dv * ib, dv * f, d * ib, d * f, dv, d, False, True),     # dp
-        (d * f, d * ib, dv * f, dv * f, d, dv, False, True),      # dv
+        (d * f, d * ib, dv * f, dv * f, d, dv, False, False),     # dv (dp's prefixes, transposed)
         (dv * f, dv * ib, d * f, d * f, dv, d, False, True),      # dq = M dO
         (d * f, d * ib, d * ib, d * f, d, d, True, False),        # dq += S dp
         (d * ib, d * ib, d * f, d * f, d, d, False, True),        # dk (q, dp) + (dp, q)
@@ -548,7 +549,7 @@ def bwd_bytes_per_token(d, dv, ib, chunk):
 
 def bench_bwd(args, torch, np):
     """The backward pass on the B4 H16 T16384 d128 decayed inputs: one
-    hla_bwd call per step (16 kernel launches on one stream), HIP events."""
+    hla_bwd call per step (14 kernel launches on one stream), HIP events."""
     import ctypes
     from causal_prefix_scan_amd import hla, synth
     cfg = dict(synth.FWD_WORKLOADS["fwd_decay_bf16_b4h16t16384d128"])
@@ -604,7 +605,7 @@ def bench_bwd(args, torch, np):
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(tflops, 1),
                           "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "hla_bwd (the 16 launches of one call)",
+        "roofline": {"bound": "hbm", "kernel": "hla_bwd (the 14 launches of one call)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(f"hla_bwd@{BWD_WORKLOAD}") if not args.chunk else None,

@@ -178,7 +178,10 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      Ht[t][j] = (OUT && a.Hp && cols) ? a.Hp[hbase + (size_t)(16 * t + 4 * lg + j) * Dc + col] : 0.f;
+      Ht[t][j] = (OUT && a.Hp && cols)
+                     ? a.Hp[hbase + (a.hp_transposed ? (size_t)col * Da + (16 * t + 4 * lg + j)
+                                                     : (size_t)(16 * t + 4 * lg + j) * Dc + col)]
+                     : 0.f;
 
   TileRows<Da, NTHR, LT> ra, rb;
   TileRows<Dc, NTHR, LT> rc;

@@ -125,6 +125,9 @@ struct LaArgs {
   // add the mirrored pair: y_t = sum lam^(t-s) [(a_t.b_s) c_s + (a_t.c_s) b_s],
   // one state sum (b c^T + c b^T); needs Da == Dc, at least one MFMA K step
   int sym = 0;
+  // Hp holds the transposed states ([Dc][Da] per segment): the prefixes of an
+  // earlier sum with the same lam whose b and c are this one's c and b
+  int hp_transposed = 0;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
 // same b, c and lam as an earlier call), so only the output pass runs.
