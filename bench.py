@@ -526,8 +526,9 @@ def credited_flops_per_token_bwd(c, d, dv):
 
 def bwd_bytes_per_token(d, dv, ib, chunk):
     """Algorithmic HBM bytes per token of one hla_bwd call: for each of the
-    six sums (operands a, b, c and output y; ib bytes per input element,
-    fp32 for p, dp and dO), the summary pass reads b and c, the output pass
+    six sums (operands a, b, c and output y; ib bytes per input element and
+    per element of the intermediates p and dp, fp32 for dO and the outputs
+    dq, dk, dv), the summary pass reads b and c, the output pass
     reads a, b, c and writes y (accumulating sums also read y), and the
     segment states are written, read and rewritten by the scan and read by
     the output pass (4 Da Dc fp32 per segment).  The S dp sum reuses the
@@ -536,12 +537,12 @@ def bwd_bytes_per_token(d, dv, ib, chunk):
     are one sum over the symmetric states (q dp^T + dp q^T)."""
     f = 4
     sums = [  # (a, b, c, y, Da, Dc, accumulate, summary pass)
-        (d * ib, d * ib, d * ib, d * f, d, d, False, True),       # p = S q
-        (dv * ib, dv * f, d * ib, d * f, dv, d, False, True),     # dp
-        (d * f, d * ib, dv * f, dv * f, d, dv, False, False),     # dv (dp's prefixes, transposed)
-        (dv * f, dv * ib, d * f, d * f, dv, d, False, True),      # dq = M dO
-        (d * f, d * ib, d * ib, d * f, d, d, True, False),        # dq += S dp
-        (d * ib, d * ib, d * f, d * f, d, d, False, True),        # dk (q, dp) + (dp, q)
+        (d * ib, d * ib, d * ib, d * ib, d, d, False, True),      # p = S q
+        (dv * ib, dv * f, d * ib, d * ib, dv, d, False, True),    # dp
+        (d * ib, d * ib, dv * f, dv * f, d, dv, False, False),    # dv (dp's prefixes, transposed)
+        (dv * f, dv * ib, d * ib, d * f, dv, d, False, True),     # dq = M dO
+        (d * ib, d * ib, d * ib, d * f, d, d, True, False),       # dq += S dp
+        (d * ib, d * ib, d * ib, d * f, d, d, False, True),       # dk (q, dp) + (dp, q)
     ]
     return sum(((b + c) + 3 * Da * Dc * f / chunk if summ else 0) + (a + b + c) + Da * Dc * f / chunk
                + y * (2 if acc else 1) for a, b, c, y, Da, Dc, acc, summ in sums)

@@ -856,10 +856,12 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
   // prefixes of the states sum g^(..) k k^T, shared by p = S q and S dp
   float* hkk = hbuf + bwd_state_floats(p, z);
   const int bf = p->in_dtype == HLA_BF16 ? 1 : 0;
-  const hla::LaOperand Q{q, bf}, K{k, bf}, V{v, bf}, DO{dout, 0}, P{pbuf, 0}, DP{dpbuf, 0};
+  // with bf16 inputs p and dp are only ever read back as bf16 MFMA operands,
+  // so they are stored as bf16 (the same rounding, half the traffic)
+  const hla::LaOperand Q{q, bf}, K{k, bf}, V{v, bf}, DO{dout, 0}, P{pbuf, bf}, DP{dpbuf, bf};
   auto run = [&](hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
                  int reverse, float* y, int accumulate, float* states = nullptr,
-                 bool ready = false, int sym = 0, int hp_t = 0) -> hla_status {
+                 bool ready = false, int sym = 0, int hp_t = 0, int y_bf16 = 0) -> hla_status {
     hla::LaArgs la;
     la.a = a; la.b = b; la.c = c;
     la.y = y; la.Hp = states ? states : hbuf; la.gamma = p->gamma;
@@ -869,16 +871,17 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
     la.mfma_bf16 = bf;
     la.sym = sym;
     la.hp_transposed = hp_t;
+    la.y_bf16 = y_bf16;
     return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s, ready));
   };
   const int d = p->d, e = p->dv;
   // p = S q; dp, dv over the future tokens (weights g^2); dq = M dO + S dp;
   // dk from the future tokens' q and dp (weights g): one sum over the
   // symmetric states g^(..) (q dp^T + dp q^T) when d spans whole MFMA steps
-  if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0, hkk)) return r;
+  if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0, hkk, false, 0, 0, bf)) return r;
   // (dv's states g^(..) q dO^T are the transposes of dp's: its output pass
   // starts from dp's prefixes)
-  if (hla_status r = run(V, DO, Q, e, d, 2, 1, dpbuf, 0)) return r;
+  if (hla_status r = run(V, DO, Q, e, d, 2, 1, dpbuf, 0, nullptr, false, 0, 0, bf)) return r;
   if (hla_status r = run(P, Q, DO, d, e, 2, 1, dv, 0, nullptr, true, 0, 1)) return r;
   if (hla_status r = run(DO, V, P, e, d, 2, 0, dq, 0)) return r;
   if (hla_status r = run(DP, K, K, d, d, 1, 0, dq, 1, hkk, true)) return r;

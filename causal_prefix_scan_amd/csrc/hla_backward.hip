@@ -258,7 +258,13 @@ __global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int l = t0 + 16 * r + 4 * lg + j;
-            if (l < s1) a.y[(urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col] = yold[r][j] + y[j];
+            if (l < s1) {
+              const size_t o = (urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col;
+              if (a.y_bf16)
+                reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)y[j];
+              else
+                a.y[o] = yold[r][j] + y[j];
+            }
           }
         }
       }
@@ -352,6 +358,7 @@ hipError_t launch_la(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) 
 
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
                                   bool prefixes_ready) {
+  if (a.y_bf16 && a.accumulate) return hipErrorInvalidValue;
   if (a.nseg > 1 && !prefixes_ready) {
     if (hipError_t e = launch_la<L_SUMMARY>(Da, Dc, units, a, s)) return e;
     const int elems = Da * Dc;

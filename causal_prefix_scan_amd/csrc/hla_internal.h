@@ -115,7 +115,7 @@ struct LaOperand {
 };
 struct LaArgs {
   LaOperand a, b, c;      // a, b: width Da; c: width Dc
-  float* y;               // [unit][T][Dc] fp32, written or accumulated
+  float* y;               // [unit][T][Dc] fp32 (bf16 with y_bf16), written or accumulated
   float* Hp;              // segment states [unit][nseg][Da][Dc] (workspace)
   const float* gamma;     // [H] or null (gamma = 1)
   int H, gexp;            // lam = gamma[unit % H] ^ gexp, gexp in {1, 2}
@@ -128,6 +128,9 @@ struct LaArgs {
   // Hp holds the transposed states ([Dc][Da] per segment): the prefixes of an
   // earlier sum with the same lam whose b and c are this one's c and b
   int hp_transposed = 0;
+  // y is bf16 (an intermediate that is only ever read back as a bf16 MFMA
+  // operand); not with accumulate
+  int y_bf16 = 0;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
 // same b, c and lam as an earlier call), so only the output pass runs.

@@ -316,11 +316,13 @@ hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t 
  * hla_bwd: writes dq, dk [B, H, T, d] and dv [B, H, T, dv] (fp32; they must
  *   not overlap each other, the inputs or the workspace).  Problem fields as
  *   for hla_fwd; normalize must be 0 (HLA_ERR_UNSUPPORTED otherwise).
- *   Precision as in the forward: bf16 inputs contract in bf16 (the fp32
- *   intermediates and dout rounded to bf16 as MFMA operands) with fp32
- *   accumulation and state; fp32 inputs stay fp32 throughout.
+ *   Precision as in the forward: bf16 inputs contract in bf16 (the
+ *   intermediates p and dp are stored as bf16, dout is rounded to bf16 as an
+ *   MFMA operand) with fp32 accumulation and state; fp32 inputs stay fp32
+ *   throughout.
  * hla_bwd_workspace_bytes: the workspace hla_bwd needs (p and dp, fp32
- *   [B, H, T, d] each; the segment states, B*H*n*max(d, dv)^2 floats; and
+ *   [B, H, T, d] each, of which bf16 inputs use half; the segment states,
+ *   B*H*n*max(d, dv)^2 floats; and
  *   the prefixes of the k k^T states, B*H*n*d*d floats, which p = S q and
  *   S dp share); 0 for an invalid or empty problem.
  */
