@@ -127,8 +127,11 @@ struct TileRows {
 // adds) y.  SYM adds the mirrored pair (b and c swapped) from the same staged
 // tiles: a second score block against c weighting b, and C^T diag(w) B in
 // the state update.
+// The bf16 summary kernels fit 128 VGPRs without spills, which lets two
+// 8-wave workgroups share a CU; the output kernels (and fp32 ones) would spill.
 template <typename T, int Da, int Dc, int MODE, int NW, bool SYM>
-__global__ __launch_bounds__(64 * NW) void la_kernel(LaArgs a) {
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(MODE == L_SUMMARY && sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaArgs a) {
   using L = LLayout<T, Da, Dc, SYM>;
   using MMT = MM<T>;
   using FR = Frag<T>;
