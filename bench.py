@@ -534,14 +534,15 @@ def bwd_bytes_per_token(d, dv, ib, chunk):
     the output pass (4 Da Dc fp32 per segment).  The S dp sum reuses the
     prefixes of the p sum (the same states) and the dv sum those of the dp
     sum (their transposes), so neither has a summary pass; the two dk sums
-    are one sum over the symmetric states (q dp^T + dp q^T)."""
+    are one sum over the symmetric states (q dp^T + dp q^T).  Where b and c
+    are the same tensor (k in p = S q and S dp) it is read once."""
     f = 4
     sums = [  # (a, b, c, y, Da, Dc, accumulate, summary pass)
-        (d * ib, d * ib, d * ib, d * ib, d, d, False, True),      # p = S q
+        (d * ib, d * ib, 0, d * ib, d, d, False, True),           # p = S q (b = c = k)
         (dv * ib, dv * f, d * ib, d * ib, dv, d, False, True),    # dp
         (d * ib, d * ib, dv * f, dv * f, d, dv, False, False),    # dv (dp's prefixes, transposed)
         (dv * f, dv * ib, d * ib, d * f, dv, d, False, True),     # dq = M dO
-        (d * ib, d * ib, d * ib, d * f, d, d, True, False),       # dq += S dp
+        (d * ib, d * ib, 0, d * f, d, d, True, False),            # dq += S dp (b = c = k)
         (d * ib, d * ib, d * ib, d * f, d, d, False, True),       # dk (q, dp) + (dp, q)
     ]
     return sum(((b + c) + 3 * Da * Dc * f / chunk if summ else 0) + (a + b + c) + Da * Dc * f / chunk
