@@ -23,6 +23,8 @@
 // with fp32 inputs everything stays fp32 (v_mfma_f32_16x16x4_f32).  States
 // and outputs are fp32 either way.
 
+#include <type_traits>
+
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -63,57 +65,46 @@ template <> struct Vec4<__bf16> { using V = bf16x4; };
 
 // One operand's rows [t0, t0 + LT) of the walk, columns [0, W), held in
 // registers as raw 4-element groups (8 bytes from a bf16 source, 16 from an
-// fp32 one) between the global loads and the LDS stores, so that a whole
-// tile's loads are in flight together and the next tile's overlap the
-// current one's products.  Rows past `end` read as zero.
-template <int W, int NTHR, int LT>
+// fp32 one; the source type is fixed at compile time so that bf16 groups
+// take two registers) between the global loads and the LDS stores, so that
+// a whole tile's loads are in flight together and the next tile's overlap
+// the current one's products.  Rows past `end` read as zero.
+template <int W, int NTHR, int LT, bool F32>
 struct TileRows {
   static constexpr int G = W / 4;                      // groups per row
   static constexpr int N = (LT * G + NTHR - 1) / NTHR; // groups per thread
-  uint4 r[N];
+  using R = typename std::conditional<F32, uint4, uint2>::type;
+  R r[N];
 
   __device__ __forceinline__ void load(const LaOperand& op, size_t urow, int nT, bool rev, int t0,
                                        int end, int tid) {
-    if (op.bf16) {
-      const __bf16* base = reinterpret_cast<const __bf16*>(op.p);
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    const E* base = reinterpret_cast<const E*>(op.p);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;
-        uint2 v = make_uint2(0, 0);
-        if (idx < LT * G && l < end) {
-          const size_t phys = (size_t)(rev ? nT - 1 - l : l);
-          v = *reinterpret_cast<const uint2*>(base + (urow + phys) * W + col);
-        }
-        r[i] = make_uint4(v.x, v.y, 0, 0);
-      }
-    } else {
-      const float* base = reinterpret_cast<const float*>(op.p);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;
-        r[i] = make_uint4(0, 0, 0, 0);
-        if (idx < LT * G && l < end) {
-          const size_t phys = (size_t)(rev ? nT - 1 - l : l);
-          r[i] = *reinterpret_cast<const uint4*>(base + (urow + phys) * W + col);
-        }
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;
+      r[i] = R{};
+      if (idx < LT * G && l < end) {
+        const size_t phys = (size_t)(rev ? nT - 1 - l : l);
+        r[i] = *reinterpret_cast<const R*>(base + (urow + phys) * W + col);
       }
     }
   }
 
   template <typename T>
-  __device__ __forceinline__ void store(bool src_bf16, T* dst, int ldd, int tid) const {
+  __device__ __forceinline__ void store(T* dst, int ldd, int tid) const {
     using V = typename Vec4<T>::V;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4;
       if (idx < LT * G) {
         V v;
-        if (src_bf16) {
-          const bf16x4 b = __builtin_bit_cast(bf16x4, make_uint2(r[i].x, r[i].y));
-          v = V{(T)b[0], (T)b[1], (T)b[2], (T)b[3]};
-        } else {
+        if constexpr (F32) {
           const f32x4 f = __builtin_bit_cast(f32x4, r[i]);
           v = V{(T)f[0], (T)f[1], (T)f[2], (T)f[3]};
+        } else {
+          const bf16x4 b = __builtin_bit_cast(bf16x4, r[i]);
+          v = V{(T)b[0], (T)b[1], (T)b[2], (T)b[3]};
         }
         *reinterpret_cast<V*>(dst + row * ldd + col) = v;
       }
@@ -127,11 +118,12 @@ struct TileRows {
 // adds) y.  SYM adds the mirrored pair (b and c swapped) from the same staged
 // tiles: a second score block against c weighting b, and C^T diag(w) B in
 // the state update.
-// The bf16 summary kernels fit 128 VGPRs without spills, which lets two
-// 8-wave workgroups share a CU; the output kernels (and fp32 ones) would spill.
-template <typename T, int Da, int Dc, int MODE, int NW, bool SYM>
+// SRCF marks the fp32 sources (bit 0: a, 1: b, 2: c; the others are bf16).
+// The bf16 kernels other than the symmetric output one fit 128 VGPRs without
+// spills, which lets two 8-wave workgroups share a CU.
+template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(MODE == L_SUMMARY && sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaArgs a) {
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && !(SYM && MODE == L_OUTPUT) ? 4 : 1))) void la_kernel(LaArgs a) {
   using L = LLayout<T, Da, Dc, SYM>;
   using MMT = MM<T>;
   using FR = Frag<T>;
@@ -186,8 +178,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == L_SUMMARY && sizeof(T) == 2 ? 4 : 1))
                                                      : (size_t)(16 * t + 4 * lg + j) * Dc + col)]
                      : 0.f;
 
-  TileRows<Da, NTHR, LT> ra, rb;
-  TileRows<Dc, NTHR, LT> rc;
+  TileRows<Da, NTHR, LT, (SRCF & 1) != 0> ra;
+  TileRows<Da, NTHR, LT, (SRCF & 2) != 0> rb;
+  TileRows<Dc, NTHR, LT, (SRCF & 4) != 0> rc;
   auto load_tile = [&](int t0) {
     if (OUT) ra.load(a.a, urow, nT, rev, t0, s1, tid);
     rb.load(a.b, urow, nT, rev, t0, s1, tid);
@@ -196,25 +189,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == L_SUMMARY && sizeof(T) == 2 ? 4 : 1))
   load_tile(s0);
   for (int t0 = s0; t0 < s1; t0 += LT) {
     const int Lt = s1 - t0 < LT ? s1 - t0 : LT;
-    if (OUT) ra.store(a.a.bf16 != 0, As, L::LDA, tid);
-    rb.store(a.b.bf16 != 0, Bs, L::LDA, tid);
-    rc.store(a.c.bf16 != 0, Cs, L::LDC, tid);
+    if (OUT) ra.store(As, L::LDA, tid);
+    rb.store(Bs, L::LDA, tid);
+    rc.store(Cs, L::LDC, tid);
     if (tid < LT) wS[tid] = tid < Lt ? gpow(lam, lgl, Lt - 1 - tid) : 0.f;
     __syncthreads();
-    // the previous outputs of this tile's rows (accumulating calls), then
     // the next tile's loads, which stay in flight during the products
-    float yold[TR][4];
-    if constexpr (OUT) {
-#pragma unroll
-      for (int r = 0; r < TR; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int l = t0 + 16 * r + 4 * lg + j;
-          yold[r][j] = 0.f;
-          if (a.accumulate && cols && l < s1)
-            yold[r][j] = a.y[(urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col];
-        }
-    }
     if (t0 + LT < s1) load_tile(t0 + LT);
 
     if constexpr (OUT) {
@@ -266,7 +246,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == L_SUMMARY && sizeof(T) == 2 ? 4 : 1))
               if (a.y_bf16)
                 reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)y[j];
               else
-                a.y[o] = yold[r][j] + y[j];
+                a.y[o] = (a.accumulate ? a.y[o] : 0.f) + y[j];
             }
           }
         }
@@ -326,23 +306,53 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int elems) {
   }
 }
 
+template <typename T, int DA, int DC, int MODE, bool SYM, int SRCF>
+hipError_t launch_k(int units, const LaArgs& a, hipStream_t s) {
+  constexpr int NW = LWaves<DC>::value;
+  hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, SYM, SRCF>), dim3((unsigned)units * a.nseg),
+                     dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+// Picks the instantiation for the operands' source types.  fp32 MFMA takes
+// fp32 sources only; bf16 MFMA takes bf16 sources with at most one fp32
+// operand (the upstream gradient), and bf16 sources only for the symmetric
+// sum.
+template <typename T, int DA, int DC, int MODE>
+hipError_t launch_dims(int units, const LaArgs& a, hipStream_t s) {
+  int srcf = (a.a.bf16 ? 0 : 1) | (a.b.bf16 ? 0 : 2) | (a.c.bf16 ? 0 : 4);
+  if (MODE == L_SUMMARY) srcf &= 6;   // a is not read
+  if constexpr (sizeof(T) == 4) {
+    constexpr int F = MODE == L_SUMMARY ? 6 : 7;
+    if (srcf != F) return hipErrorInvalidValue;
+    if (a.sym) {
+      if constexpr (DA == DC) return launch_k<T, DA, DC, MODE, true, F>(units, a, s);
+      return hipErrorInvalidValue;
+    }
+    return launch_k<T, DA, DC, MODE, false, F>(units, a, s);
+  } else {
+    if (a.sym) {
+      if constexpr (DA == DC && DA >= MM<T>::KS) {
+        if (srcf == 0) return launch_k<T, DA, DC, MODE, true, 0>(units, a, s);
+      }
+      return hipErrorInvalidValue;
+    }
+    switch (srcf) {
+      case 0: return launch_k<T, DA, DC, MODE, false, 0>(units, a, s);
+      case 2: return launch_k<T, DA, DC, MODE, false, 2>(units, a, s);
+      case 4: return launch_k<T, DA, DC, MODE, false, 4>(units, a, s);
+      case 1:
+        if constexpr (MODE == L_OUTPUT) return launch_k<T, DA, DC, MODE, false, 1>(units, a, s);
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
 template <typename T, int MODE>
 hipError_t launch_la_mode(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
-#define HLA_CASE(DA, DC)                                                                     \
-  if (Da == DA && Dc == DC) {                                                                \
-    constexpr int NW = LWaves<DC>::value;                                                    \
-    if (a.sym) {                                                                             \
-      if constexpr (DA == DC && DA >= MM<T>::KS) {                                           \
-        hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, true>),                           \
-                           dim3((unsigned)units * a.nseg), dim3(64 * NW), 0, s, a);          \
-        return hipGetLastError();                                                            \
-      }                                                                                      \
-      return hipErrorInvalidValue;                                                           \
-    }                                                                                        \
-    hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, false>), dim3((unsigned)units * a.nseg), \
-                       dim3(64 * NW), 0, s, a);                                              \
-    return hipGetLastError();                                                                \
-  }
+#define HLA_CASE(DA, DC) \
+  if (Da == DA && Dc == DC) return launch_dims<T, DA, DC, MODE>(units, a, s);
   HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(16, 64) HLA_CASE(16, 128)
   HLA_CASE(32, 16) HLA_CASE(32, 32) HLA_CASE(32, 64) HLA_CASE(32, 128)
   HLA_CASE(64, 16) HLA_CASE(64, 32) HLA_CASE(64, 64) HLA_CASE(64, 128)
