@@ -119,11 +119,11 @@ struct TileRows {
 // tiles: a second score block against c weighting b, and C^T diag(w) B in
 // the state update.
 // SRCF marks the fp32 sources (bit 0: a, 1: b, 2: c; the others are bf16).
-// The bf16 kernels other than the symmetric output one fit 128 VGPRs without
-// spills, which lets two 8-wave workgroups share a CU.
+// The bf16 kernels fit 128 VGPRs without spills, which lets two 8-wave
+// workgroups share a CU.
 template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && !(SYM && MODE == L_OUTPUT) ? 4 : 1))) void la_kernel(LaArgs a) {
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaArgs a) {
   using L = LLayout<T, Da, Dc, SYM>;
   using MMT = MM<T>;
   using FR = Frag<T>;
