@@ -121,7 +121,7 @@ struct TileRows {
 // SRCF marks the fp32 sources (bit 0: a, 1: b, 2: c; the others are bf16).
 // The bf16 kernels fit 128 VGPRs without spills, which lets two 8-wave
 // workgroups share a CU.
-template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF>
+template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF, bool ACC>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaArgs a) {
   using L = LLayout<T, Da, Dc, SYM>;
@@ -225,6 +225,16 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
         // Y = lam^(tau+1) A H_prev + S C for this wave's 16 columns
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
+          // (accumulating calls) the previous outputs of the row block, in
+          // flight during its products
+          float yold[4];
+          if constexpr (ACC) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int l = t0 + 16 * r + 4 * lg + j;
+              yold[j] = l < s1 ? a.y[(urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col] : 0.f;
+            }
+          }
           f32x4 y = zero4();
 #pragma unroll
           for (int kk = 0; kk < QK; ++kk) y = MMT::mma(FR::perm(As, L::LDA, 16 * r, kk, lane), FR::acc_b(Ht, kk), y);
@@ -243,10 +253,12 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
             const int l = t0 + 16 * r + 4 * lg + j;
             if (l < s1) {
               const size_t o = (urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col;
-              if (a.y_bf16)
+              if constexpr (ACC)
+                a.y[o] = yold[j] + y[j];
+              else if (a.y_bf16)
                 reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)y[j];
               else
-                a.y[o] = (a.accumulate ? a.y[o] : 0.f) + y[j];
+                a.y[o] = y[j];
             }
           }
         }
@@ -306,10 +318,10 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int elems) {
   }
 }
 
-template <typename T, int DA, int DC, int MODE, bool SYM, int SRCF>
+template <typename T, int DA, int DC, int MODE, bool SYM, int SRCF, bool ACC = false>
 hipError_t launch_k(int units, const LaArgs& a, hipStream_t s) {
   constexpr int NW = LWaves<DC>::value;
-  hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, SYM, SRCF>), dim3((unsigned)units * a.nseg),
+  hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, SYM, SRCF, ACC>), dim3((unsigned)units * a.nseg),
                      dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
@@ -317,11 +329,19 @@ hipError_t launch_k(int units, const LaArgs& a, hipStream_t s) {
 // Picks the instantiation for the operands' source types.  fp32 MFMA takes
 // fp32 sources only; bf16 MFMA takes bf16 sources with at most one fp32
 // operand (the upstream gradient), and bf16 sources only for the symmetric
-// sum.
+// and the accumulating sums.
 template <typename T, int DA, int DC, int MODE>
 hipError_t launch_dims(int units, const LaArgs& a, hipStream_t s) {
   int srcf = (a.a.bf16 ? 0 : 1) | (a.b.bf16 ? 0 : 2) | (a.c.bf16 ? 0 : 4);
   if (MODE == L_SUMMARY) srcf &= 6;   // a is not read
+  if (MODE == L_OUTPUT && a.accumulate) {
+    if (a.sym) return hipErrorInvalidValue;
+    if constexpr (MODE == L_OUTPUT) {
+      constexpr int F = sizeof(T) == 4 ? 7 : 0;
+      if (srcf == F) return launch_k<T, DA, DC, MODE, false, F, true>(units, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if constexpr (sizeof(T) == 4) {
     constexpr int F = MODE == L_SUMMARY ? 6 : 7;
     if (srcf != F) return hipErrorInvalidValue;
