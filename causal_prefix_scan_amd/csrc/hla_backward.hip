@@ -17,11 +17,15 @@
 // forward: segment states H = sum_s lam^(L-1-s) b_s c_s^T, an exclusive
 // decayed running sum over the segments, then per tile (64 tokens; 32 for fp32)
 // Y = lam^(tau+1) A H_prev + ((A B^T) o decay) C and H <- lam^L H + B^T diag(w) C.
-// Precision follows the forward: with bf16 inputs every operand (q, k, v and
-// the fp32 intermediates p, dp and the upstream gradient) is staged to LDS as
-// bf16 and contracted with v_mfma_f32_16x16x32_bf16 into fp32 accumulators;
-// with fp32 inputs everything stays fp32 (v_mfma_f32_16x16x4_f32).  States
-// and outputs are fp32 either way.
+// Sums with the same states share them: S dp starts from the prefixes of p,
+// dv from those of dp read transposed, and the two dk sums are one sum over
+// the symmetric states lam^(..) (q dp^T + dp q^T).
+// Precision follows the forward: with bf16 inputs every operand (q, k, v, the
+// intermediates p and dp, which are stored as bf16, and the upstream
+// gradient) is staged to LDS as bf16 and contracted with
+// v_mfma_f32_16x16x32_bf16 into fp32 accumulators; with fp32 inputs
+// everything stays fp32 (v_mfma_f32_16x16x4_f32).  States and the outputs
+// dq, dk, dv are fp32 either way.
 
 #include <type_traits>
 
