@@ -467,13 +467,46 @@ __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
 #pragma unroll
   for (int b = 0; b < RB; ++b) er[b] = zero4();
   const bool col_ok = !mblk || lr == 0;
+  // X_s is loaded into registers one segment ahead, so its loads overlap the
+  // previous segment's products
+  constexpr int NXR = (D * D / 4 + 255) / 256;
+  f32x4 xr[NXR];
+  auto load_x = [&](int s) {
+    const f32x4* X = reinterpret_cast<const f32x4*>(a.X + ((size_t)unit * n + s) * D * D);
+#pragma unroll
+    for (int k = 0; k < NXR; ++k) {
+      const int i = tid + 256 * k;
+      if (i < D * D / 4) xr[k] = X[i];
+    }
+  };
+  if (n > 0) load_x(0);
   for (int s = 0; s < n; ++s) {
     const size_t sidx = (size_t)unit * n + s;
-    const float* X = a.X + sidx * D * D;
-    for (int i = tid; i < D * D / 4; i += 256) {
-      const int r = (4 * i) / D, c = (4 * i) % D;
-      *reinterpret_cast<f32x4*>(Xs + r * LX + c) = reinterpret_cast<const f32x4*>(X)[i];
+    // this segment's summary entries of the lanes' own rows, read before the
+    // products so that their loads overlap them
+    float px[RB][4], ex[RB][4];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int t = wave + 4 * b;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * t + 4 * lg4 + j;
+        px[b][j] = ex[b][j] = 0.f;
+        if (t < DT && col_ok) {
+          px[b][j] = mblk ? a.m[sidx * D + row] : a.P[(sidx * D + row) * E + 16 * cb + lr];
+          ex[b][j] = mblk ? a.n[sidx * D + row] : a.E[(sidx * D + row) * E + 16 * cb + lr];
+        }
+      }
     }
+#pragma unroll
+    for (int k = 0; k < NXR; ++k) {
+      const int i = tid + 256 * k;
+      if (i < D * D / 4) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        *reinterpret_cast<f32x4*>(Xs + r * LX + c) = xr[k];
+      }
+    }
+    if (s + 1 < n) load_x(s + 1);
     __syncthreads();
     f32x4 cross[RB], pold[RB];
 #pragma unroll
@@ -496,11 +529,10 @@ __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
           const int row = 16 * t + 4 * lg4 + j;
           float* pp = mblk ? a.m + sidx * D + row : a.P + (sidx * D + row) * E + 16 * cb + lr;
           float* ep = mblk ? a.n + sidx * D + row : a.E + (sidx * D + row) * E + 16 * cb + lr;
-          const float px = *pp, ex = *ep;
           *pp = pold[b][j];
           *ep = er[b][j];
-          Pr[row * 16 + lr] = sa * pold[b][j] + px;
-          er[b][j] = sa * er[b][j] + ex + sa * cross[b][j];
+          Pr[row * 16 + lr] = sa * pold[b][j] + px[b][j];
+          er[b][j] = sa * er[b][j] + ex[b][j] + sa * cross[b][j];
         }
       }
     }
