@@ -535,18 +535,22 @@ def bwd_bytes_per_token(d, dv, ib, chunk):
     prefixes of the p sum (the same states) and the dv sum those of the dp
     sum (their transposes), so neither has a summary pass; the two dk sums
     are one sum over the symmetric states (q dp^T + dp q^T).  Where b and c
-    are the same tensor (k in p = S q and S dp) it is read once."""
+    are the same tensor (k in p = S q and S dp) it is read once.  With bf16
+    inputs the dp summary pass reads dO in fp32 and writes it rounded to
+    bf16; every later pass reads that copy."""
     f = 4
-    sums = [  # (a, b, c, y, Da, Dc, accumulate, summary pass)
-        (d * ib, d * ib, 0, d * ib, d, d, False, True),           # p = S q (b = c = k)
-        (dv * ib, dv * f, d * ib, d * ib, dv, d, False, True),    # dp
-        (d * ib, d * ib, dv * f, dv * f, d, dv, False, False),    # dv (dp's prefixes, transposed)
-        (dv * f, dv * ib, d * ib, d * f, dv, d, False, True),     # dq = M dO
-        (d * ib, d * ib, 0, d * f, d, d, True, False),            # dq += S dp (b = c = k)
-        (d * ib, d * ib, d * ib, d * f, d, d, False, True),       # dk (q, dp) + (dp, q)
+    do = dv * ib                       # dO as the later passes read it
+    cp = dv * 2 if ib == 2 else 0      # the bf16 copy's write (bf16 inputs)
+    sums = [  # (a, b (summary pass), b (output pass), c, y, Da, Dc, accumulate, summary pass)
+        (d * ib, d * ib, d * ib, 0, d * ib, d, d, False, True),          # p = S q (b = c = k)
+        (dv * ib, dv * f + cp, do, d * ib, d * ib, dv, d, False, True),  # dp (+ the dO copy)
+        (d * ib, 0, d * ib, do, dv * f, d, dv, False, False),            # dv (dp's prefixes, transposed)
+        (do, dv * ib, dv * ib, d * ib, d * f, dv, d, False, True),       # dq = M dO
+        (d * ib, 0, d * ib, 0, d * f, d, d, True, False),                # dq += S dp (b = c = k)
+        (d * ib, d * ib, d * ib, d * ib, d * f, d, d, False, True),      # dk (q, dp) + (dp, q)
     ]
-    return sum(((b + c) + 3 * Da * Dc * f / chunk if summ else 0) + (a + b + c) + Da * Dc * f / chunk
-               + y * (2 if acc else 1) for a, b, c, y, Da, Dc, acc, summ in sums)
+    return sum(((bs + c) + 3 * Da * Dc * f / chunk if summ else 0) + (a + bo + c) + Da * Dc * f / chunk
+               + y * (2 if acc else 1) for a, bs, bo, c, y, Da, Dc, acc, summ in sums)
 
 
 def bench_bwd(args, torch, np):

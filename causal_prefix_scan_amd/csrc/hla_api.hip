@@ -815,8 +815,9 @@ extern "C" {
 size_t hla_bwd_workspace_bytes(const hla_problem* p) {
   if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
   const Sizes z = sizes_of(p);
+  const size_t do16 = p->in_dtype == HLA_BF16 ? (size_t)z.units * (size_t)p->T * (size_t)p->dv * 2 : 0;
   return (2 * (size_t)z.units * (size_t)p->T * (size_t)p->d + bwd_state_floats(p, z) +
-          (size_t)z.units * (size_t)z.n * (size_t)p->d * (size_t)p->d) * 4;
+          (size_t)z.units * (size_t)z.n * (size_t)p->d * (size_t)p->d) * 4 + do16;
 }
 
 hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,
@@ -861,7 +862,8 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
   const hla::LaOperand Q{q, bf}, K{k, bf}, V{v, bf}, DO{dout, 0}, P{pbuf, bf}, DP{dpbuf, bf};
   auto run = [&](hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
                  int reverse, float* y, int accumulate, float* states = nullptr,
-                 bool ready = false, int sym = 0, int hp_t = 0, int y_bf16 = 0) -> hla_status {
+                 bool ready = false, int sym = 0, int hp_t = 0, int y_bf16 = 0,
+                 void* b_copy = nullptr) -> hla_status {
     hla::LaArgs la;
     la.a = a; la.b = b; la.c = c;
     la.y = y; la.Hp = states ? states : hbuf; la.gamma = p->gamma;
@@ -872,18 +874,24 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
     la.sym = sym;
     la.hp_transposed = hp_t;
     la.y_bf16 = y_bf16;
+    la.b_copy = b_copy;
     return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s, ready));
   };
   const int d = p->d, e = p->dv;
+  // with bf16 inputs the dp sum writes dO rounded to bf16 as it stages it (the
+  // rounding every later use applies anyway); dv and dq read that copy
+  void* do16 = bf ? static_cast<void*>(hkk + (size_t)z.units * (size_t)z.n * (size_t)d * (size_t)d)
+                  : nullptr;
+  const hla::LaOperand DOb = bf ? hla::LaOperand{do16, 1} : DO;
   // p = S q; dp, dv over the future tokens (weights g^2); dq = M dO + S dp;
   // dk from the future tokens' q and dp (weights g): one sum over the
   // symmetric states g^(..) (q dp^T + dp q^T) when d spans whole MFMA steps
   if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0, hkk, false, 0, 0, bf)) return r;
   // (dv's states g^(..) q dO^T are the transposes of dp's: its output pass
   // starts from dp's prefixes)
-  if (hla_status r = run(V, DO, Q, e, d, 2, 1, dpbuf, 0, nullptr, false, 0, 0, bf)) return r;
-  if (hla_status r = run(P, Q, DO, d, e, 2, 1, dv, 0, nullptr, true, 0, 1)) return r;
-  if (hla_status r = run(DO, V, P, e, d, 2, 0, dq, 0)) return r;
+  if (hla_status r = run(V, DO, Q, e, d, 2, 1, dpbuf, 0, nullptr, false, 0, 0, bf, do16)) return r;
+  if (hla_status r = run(P, Q, DOb, d, e, 2, 1, dv, 0, nullptr, true, 0, 1)) return r;
+  if (hla_status r = run(DOb, V, P, e, d, 2, 0, dq, 0)) return r;
   if (hla_status r = run(DP, K, K, d, d, 1, 0, dq, 1, hkk, true)) return r;
   if (d >= (bf ? 32 : 4)) return run(K, Q, DP, d, d, 1, 1, dk, 0, nullptr, false, 1);
   if (hla_status r = run(K, Q, DP, d, d, 1, 1, dk, 0)) return r;

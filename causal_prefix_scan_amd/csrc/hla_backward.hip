@@ -95,6 +95,23 @@ struct TileRows {
     }
   }
 
+  // the held rows, rounded to bf16, to a dense [rows][W] copy (fp32 sources)
+  __device__ __forceinline__ void write_bf16_copy(void* dst, size_t urow, int nT, bool rev, int t0,
+                                                  int end, int tid) const {
+    static_assert(F32, "only fp32 sources are copied");
+    __bf16* base = reinterpret_cast<__bf16*>(dst);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;
+      if (idx < LT * G && l < end) {
+        const f32x4 f = __builtin_bit_cast(f32x4, r[i]);
+        const size_t phys = (size_t)(rev ? nT - 1 - l : l);
+        *reinterpret_cast<bf16x4*>(base + (urow + phys) * W + col) =
+            bf16x4{(__bf16)f[0], (__bf16)f[1], (__bf16)f[2], (__bf16)f[3]};
+      }
+    }
+  }
+
   template <typename T>
   __device__ __forceinline__ void store(T* dst, int ldd, int tid) const {
     using V = typename Vec4<T>::V;
@@ -195,6 +212,9 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
     const int Lt = s1 - t0 < LT ? s1 - t0 : LT;
     if (OUT) ra.store(As, L::LDA, tid);
     rb.store(Bs, L::LDA, tid);
+    if constexpr ((SRCF & 2) != 0 && sizeof(T) == 2) {
+      if (a.b_copy) rb.write_bf16_copy(a.b_copy, urow, nT, rev, t0, s1, tid);
+    }
     rc.store(Cs, L::LDC, tid);
     if (tid < LT) wS[tid] = tid < Lt ? gpow(lam, lgl, Lt - 1 - tid) : 0.f;
     __syncthreads();
@@ -396,14 +416,19 @@ hipError_t launch_la(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) 
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
                                   bool prefixes_ready) {
   if (a.y_bf16 && a.accumulate) return hipErrorInvalidValue;
+  if (a.b_copy && (!a.mfma_bf16 || a.b.bf16)) return hipErrorInvalidValue;
+  LaArgs b = a;
   if (a.nseg > 1 && !prefixes_ready) {
     if (hipError_t e = launch_la<L_SUMMARY>(Da, Dc, units, a, s)) return e;
     const int elems = Da * Dc;
     hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)units * ((elems + 255) / 256)), dim3(256), 0, s,
                        a, elems);
     if (hipError_t e = hipGetLastError()) return e;
+    if (a.b_copy) {   // the summary pass wrote the copy: read it
+      b.b = LaOperand{a.b_copy, 1};
+      b.b_copy = nullptr;
+    }
   }
-  LaArgs b = a;
   if (a.nseg == 1) b.Hp = nullptr;
   return launch_la<L_OUTPUT>(Da, Dc, units, b, s);
 }

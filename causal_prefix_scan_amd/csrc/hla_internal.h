@@ -131,6 +131,10 @@ struct LaArgs {
   // y is bf16 (an intermediate that is only ever read back as a bf16 MFMA
   // operand); not with accumulate
   int y_bf16 = 0;
+  // when set (bf16 MFMA, fp32 b): the first pass that stages b also writes
+  // it, rounded to bf16, here ([unit][T][Da]); after a summary pass the
+  // output pass reads this copy instead of b
+  void* b_copy = nullptr;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
 // same b, c and lam as an earlier call), so only the output pass runs.

@@ -322,9 +322,11 @@ hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t 
  *   throughout.
  * hla_bwd_workspace_bytes: the workspace hla_bwd needs (p and dp, fp32
  *   [B, H, T, d] each, of which bf16 inputs use half; the segment states,
- *   B*H*n*max(d, dv)^2 floats; and
- *   the prefixes of the k k^T states, B*H*n*d*d floats, which p = S q and
- *   S dp share); 0 for an invalid or empty problem.
+ *   B*H*n*max(d, dv)^2 floats; the prefixes of the k k^T states,
+ *   B*H*n*d*d floats, which p = S q and S dp share; and, with bf16 inputs,
+ *   dout rounded to bf16, B*H*T*dv values, written by the first pass that
+ *   reads dout and read by the later ones); 0 for an invalid or empty
+ *   problem.
  */
 size_t hla_bwd_workspace_bytes(const hla_problem* p);
 hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,

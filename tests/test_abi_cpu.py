@@ -304,10 +304,13 @@ def test_binding_refuses_cpu_tensors():
 
 def test_bwd_sizes_and_checks(L):
     p = problem()                       # B2 H3 T256 d64 dv64 chunk 64: n = 4
-    need = (2 * 6 * 256 * 64 + 2 * 6 * 4 * 64 * 64) * 4
+    # p, dp (fp32 slots), segment states, k k^T prefixes, and (bf16 inputs) a bf16 copy of dout
+    need = (2 * 6 * 256 * 64 + 2 * 6 * 4 * 64 * 64) * 4 + 6 * 256 * 64 * 2
     assert L.hla_bwd_workspace_bytes(ctypes.byref(p)) == need
     assert L.hla_bwd_workspace_bytes(ctypes.byref(problem(dv=128))) == \
-        (2 * 6 * 256 * 64 + 6 * 4 * 128 * 128 + 6 * 4 * 64 * 64) * 4
+        (2 * 6 * 256 * 64 + 6 * 4 * 128 * 128 + 6 * 4 * 64 * 64) * 4 + 6 * 256 * 128 * 2
+    assert L.hla_bwd_workspace_bytes(ctypes.byref(problem(in_dtype=hla.HLA_F32))) == \
+        (2 * 6 * 256 * 64 + 2 * 6 * 4 * 64 * 64) * 4
     assert L.hla_bwd_workspace_bytes(ctypes.byref(problem(T=10))) == 0
     DO, DQ, DK, DV = S_BASE, S_BASE + 0x1000000, S_BASE + 0x2000000, S_BASE + 0x3000000
     W = 0x7000000000
