@@ -335,10 +335,20 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int elems) {
   const float aL = gpow(lam, log2f(lam), a.seg);
   float run = 0.f;
   float* p = a.Hp + (size_t)unit * a.nseg * elems + e;
-  for (int s = 0; s < a.nseg; ++s) {
-    const float x = p[(size_t)s * elems];
-    p[(size_t)s * elems] = run;
-    run = aL * run + x;
+  // eight segments' loads in flight at a time rather than one dependent
+  // load per segment
+  constexpr int NB = 8;
+  for (int s0 = 0; s0 < a.nseg; s0 += NB) {
+    float x[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) x[i] = s0 + i < a.nseg ? p[(size_t)(s0 + i) * elems] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (s0 + i < a.nseg) {
+        p[(size_t)(s0 + i) * elems] = run;
+        run = aL * run + x[i];
+      }
+    }
   }
 }
 
