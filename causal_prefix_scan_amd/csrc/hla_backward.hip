@@ -139,7 +139,8 @@ struct TileRows {
 // adds) y.  SYM adds the mirrored pair (b and c swapped) from the same staged
 // tiles: a second score block against c weighting b, and C^T diag(w) B in
 // the state update.
-// SRCF marks the fp32 sources (bit 0: a, 1: b, 2: c; the others are bf16).
+// SRCF marks the fp32 sources (bit 0: a, 1: b, 2: c; the others are bf16)
+// and, with bit 3, that c is the same tensor as b.
 // The bf16 kernels fit 128 VGPRs without spills, which lets two 8-wave
 // workgroups share a CU.
 template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF, bool ACC>
@@ -157,7 +158,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* As = reinterpret_cast<T*>(smem + L::As);
   T* Bs = reinterpret_cast<T*>(smem + L::Bs);
-  T* Cs = reinterpret_cast<T*>(smem + L::Cs);
+  // SRCF bit 3: c is the same tensor as b (Da == Dc), so its tile is b's
+  constexpr bool CB = (SRCF & 8) != 0;
+  static_assert(!CB || (Da == Dc && !SYM), "c = b needs equal widths");
+  constexpr int LDC = CB ? L::LDA : L::LDC;
+  T* Cs = CB ? Bs : reinterpret_cast<T*>(smem + L::Cs);
   T* Ss = reinterpret_cast<T*>(smem + L::Ss);
   T* Ss2 = reinterpret_cast<T*>(smem + L::Ss2);
   float* pw = reinterpret_cast<float*>(smem + L::W);
@@ -205,7 +210,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
   auto load_tile = [&](int t0) {
     if (OUT) ra.load(a.a, urow, nT, rev, t0, s1, tid);
     rb.load(a.b, urow, nT, rev, t0, s1, tid);
-    rc.load(a.c, urow, nT, rev, t0, s1, tid);
+    if constexpr (!CB) rc.load(a.c, urow, nT, rev, t0, s1, tid);
   };
   load_tile(s0);
   for (int t0 = s0; t0 < s1; t0 += LT) {
@@ -215,7 +220,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
     if constexpr ((SRCF & 2) != 0 && sizeof(T) == 2) {
       if (a.b_copy) rb.write_bf16_copy(a.b_copy, urow, nT, rev, t0, s1, tid);
     }
-    rc.store(Cs, L::LDC, tid);
+    if constexpr (!CB) rc.store(Cs, LDC, tid);
     if (tid < LT) wS[tid] = tid < Lt ? gpow(lam, lgl, Lt - 1 - tid) : 0.f;
     __syncthreads();
     // the next tile's loads, which stay in flight during the products
@@ -229,7 +234,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
       for (int idx = wave; idx < (SYM ? 2 * NB : NB); idx += NW) {
         const bool mirror = SYM && idx >= NB;
         const T* Xs = mirror ? Cs : Bs;
-        const int ldx = mirror ? L::LDC : L::LDA;
+        const int ldx = mirror ? LDC : L::LDA;
         T* So = mirror ? Ss2 : Ss;
         int r = 0, c = mirror ? idx - NB : idx;
         while (c > r) { c -= r + 1; ++r; }
@@ -266,7 +271,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
           for (int j = 0; j < 4; ++j) y[j] *= w1[16 * r + 4 * lg + j];
 #pragma unroll
           for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-            y = MMT::mma(MMT::ld(Ss, L::LDS_, 16 * r, k0, lane), FR::tr(Cs, L::LDC, k0, 16 * wave, lane), y);
+            y = MMT::mma(MMT::ld(Ss, L::LDS_, 16 * r, k0, lane), FR::tr(Cs, LDC, k0, 16 * wave, lane), y);
           if constexpr (SYM) {
 #pragma unroll
             for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
@@ -293,7 +298,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
       const float gL = gpow(lam, lgl, Lt);
       typename MMT::F bw[LT / KS], bw2[SYM ? LT / KS : 1];
 #pragma unroll
-      for (int kk = 0; kk < LT / KS; ++kk) bw[kk] = FR::scale(FR::tr(Cs, L::LDC, KS * kk, 16 * wave, lane), wS, KS * kk, lane);
+      for (int kk = 0; kk < LT / KS; ++kk) bw[kk] = FR::scale(FR::tr(Cs, LDC, KS * kk, 16 * wave, lane), wS, KS * kk, lane);
       if constexpr (SYM) {
 #pragma unroll
         for (int kk = 0; kk < LT / KS; ++kk) bw2[kk] = FR::scale(FR::tr(Bs, L::LDA, KS * kk, 16 * wave, lane), wS, KS * kk, lane);
@@ -305,7 +310,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
         for (int kk = 0; kk < LT / KS; ++kk) h = MMT::mma(FR::tr(Bs, L::LDA, KS * kk, 16 * t, lane), bw[kk], h);
         if constexpr (SYM) {
 #pragma unroll
-          for (int kk = 0; kk < LT / KS; ++kk) h = MMT::mma(FR::tr(Cs, L::LDC, KS * kk, 16 * t, lane), bw2[kk], h);
+          for (int kk = 0; kk < LT / KS; ++kk) h = MMT::mma(FR::tr(Cs, LDC, KS * kk, 16 * t, lane), bw2[kk], h);
         }
         Ht[t] = h;
       }
@@ -368,13 +373,22 @@ template <typename T, int DA, int DC, int MODE>
 hipError_t launch_dims(int units, const LaArgs& a, hipStream_t s) {
   int srcf = (a.a.bf16 ? 0 : 1) | (a.b.bf16 ? 0 : 2) | (a.c.bf16 ? 0 : 4);
   if (MODE == L_SUMMARY) srcf &= 6;   // a is not read
+  // c the same tensor as b (k in p = S q and S dp): its tile is staged once
+  const bool cb = sizeof(T) == 2 && DA == DC && !a.sym && srcf == 0 && a.c.p == a.b.p &&
+                  a.c.bf16 == a.b.bf16;
   if (MODE == L_OUTPUT && a.accumulate) {
     if (a.sym) return hipErrorInvalidValue;
     if constexpr (MODE == L_OUTPUT) {
       constexpr int F = sizeof(T) == 4 ? 7 : 0;
+      if constexpr (sizeof(T) == 2 && DA == DC) {
+        if (cb) return launch_k<T, DA, DC, MODE, false, 8, true>(units, a, s);
+      }
       if (srcf == F) return launch_k<T, DA, DC, MODE, false, F, true>(units, a, s);
     }
     return hipErrorInvalidValue;
+  }
+  if constexpr (sizeof(T) == 2 && DA == DC) {
+    if (cb) return launch_k<T, DA, DC, MODE, false, 8>(units, a, s);
   }
   if constexpr (sizeof(T) == 4) {
     constexpr int F = MODE == L_SUMMARY ? 6 : 7;
