@@ -48,7 +48,7 @@ SMALL = [
     (1, 2, 192, 64, 128, 64, "bf16", True),       # d < dv
     (1, 1, 96, 64, 64, 32, "f32", True),          # n = 3
     (1, 1, 600, 32, 64, 200, "bf16", False),      # ragged 8-token last tile
-    (1, 1, 160, 128, 128, 64, "f32", True),       # fp32 at d = dv = 128, n = 3, ragged 32-token tile
+    (1, 2, 144, 64, 64, 48, "f32", True),         # fp32, n = 3, a 32-token tile + a ragged 16 per segment
 ]
 
 
