@@ -88,35 +88,58 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_threads():
+    """Threads the oracle may use: this process's CPU affinity, capped by the
+    host's thread budget for the job (OMP_NUM_THREADS when set)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(n, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_fwd(inp, ntok):
     """The oracle's serial recurrence on a bounded sample: every unit, first ntok tokens."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import hla_oracle as O
     uq, uk, uv, ug = inp.units()
-    with threadpool_limits(limits=1):
+    nt = cpu_threads()
+    with threadpool_limits(limits=nt):
         t0 = time.perf_counter()
         O.serial(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
         dt = time.perf_counter() - t0
     U = uq.shape[0]
-    return {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": U * ntok / dt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
             "sample": f"fp64 serial recurrence, all {U} (batch, head) units, first {ntok} of "
-                      f"{uq.shape[1]} tokens ({dt:.1f} s)", "seconds": round(dt, 2)}
+                      f"{uq.shape[1]} tokens ({dt:.1f} s)", "seconds": round(dt, 2),
+            "cpu_model": cpu_model()}
 
 
 def cpu_baseline_decode(states64, toks, steps):
     from threadpoolctl import threadpool_limits
     from oracle import hla_oracle as O
     U = toks[0][0].shape[0]
-    with threadpool_limits(limits=1):
+    nt = cpu_threads()
+    with threadpool_limits(limits=nt):
         t0 = time.perf_counter()
         st = states64
         for s in range(steps):
             _, _, st = O.decode_step(st, *toks[s])
         dt = time.perf_counter() - t0
-    return {"value": U * steps / dt, "unit": "unit-tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": U * steps / dt, "unit": "unit-tokens/s", "cores": nt, "kind": "oracle",
             "sample": f"fp64 decode steps, {U} units x {steps} steps ({dt:.1f} s)",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu_model": cpu_model()}
 
 
 def bench_fwd(args, torch, np):
@@ -214,7 +237,7 @@ def bench_fwd(args, torch, np):
     dom = max(("hla_fwd_chunk_summaries", "hla_fwd_output"), key=lambda kname: kernels[kname]["ms"])
     kd = kernels[dom]
     achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
-    f_tok = credited_flops_per_token(64, d, dv)
+    f_tok = credited_flops_per_token(cfg["credit_chunk"], d, dv)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(f"{dom}@{args.workload}") if not args.chunk else None,
@@ -229,7 +252,8 @@ def bench_fwd(args, torch, np):
                    "path": ("hla_fwd_chunk_summaries + hla_scan_runs + hla_fwd_output over runs of "
                             f"{R} segments" if use_runs
                             else "hla_fwd_chunk_summaries + hla_scan + hla_fwd_output")},
-        "mfma_credited": {"flops_per_token": round(f_tok), "tflops": round(value * f_tok / 1e12, 1),
+        "mfma_credited": {"flops_per_token": round(f_tok), "credit_chunk": cfg["credit_chunk"],
+                          "tflops": round(value * f_tok / 1e12, 1),
                           "peak_tflops": BF16_PEAK_TFLOPS,
                           "frac": round(value * f_tok / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "kernels_ms": {kname: round(kv["ms"], 4) for kname, kv in kernels.items()},
@@ -425,14 +449,15 @@ def bench_variant_fwd(args, torch, np):
         from oracle import hla_oracle as O
         uq, uk, uv, ug = inp.units()
         ntok = min(args.cpu_tokens, T)
-        with threadpool_limits(limits=1):
+        nt = cpu_threads()
+        with threadpool_limits(limits=nt):
             t0 = time.perf_counter()
             getattr(O, V["oracle"])(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
             dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": U * ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        out["cpu_baseline"] = {"value": U * ntok / dt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
                                "sample": f"fp64 serial recurrence of the {V['name']}, all {U} "
                                          f"(batch, head) units, first {ntok} of {T} tokens ({dt:.1f} s)",
-                               "seconds": round(dt, 2)}
+                               "seconds": round(dt, 2), "cpu_model": cpu_model()}
     return out
 
 
@@ -498,17 +523,18 @@ def bench_variant_decode(args, torch, np):
         from oracle import hla_oracle as O
         serial = getattr(O, V["oracle"])
         nb = min(args.cpu_steps, len(toks_host))
-        with threadpool_limits(limits=1):
+        nt = cpu_threads()
+        with threadpool_limits(limits=nt):
             t0 = time.perf_counter()
             st = states64
             for s in range(nb):
                 tq_, tk_, tv_ = toks_host[s][:3]
                 _, _, st = serial(tq_[:, None], tk_[:, None], tv_[:, None], None, st)
             dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": U * nb / dt, "unit": "unit-tokens/s", "cores": 1,
+        out["cpu_baseline"] = {"value": U * nb / dt, "unit": "unit-tokens/s", "cores": nt,
                                "kind": "oracle",
                                "sample": f"fp64 {V['name']} decode steps, {U} units x {nb} steps ({dt:.1f} s)",
-                               "seconds": round(dt, 2)}
+                               "seconds": round(dt, 2), "cpu_model": cpu_model()}
     return out
 
 
@@ -623,11 +649,13 @@ def bench_bwd(args, torch, np):
         uq, uk, uv, ug = inp.units()
         dou = do.cpu().numpy().reshape(B * H, T, dv)
         ntok = min(2048, T)
-        with threadpool_limits(limits=1):
+        nt = cpu_threads()
+        with threadpool_limits(limits=nt):
             t0 = time.perf_counter()
             BO.grad_states(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], dou[:, :ntok], ug)
             dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": B * H * ntok / dt, "unit": "tokens/s", "cores": 1,
+        out["cpu_baseline"] = {"value": B * H * ntok / dt, "unit": "tokens/s", "cores": nt,
+                               "cpu_model": cpu_model(),
                                "kind": "oracle",
                                "sample": f"fp64 serial forward/reverse state recurrences, all {B * H} "
                                          f"(batch, head) units, first {ntok} of {T} tokens ({dt:.1f} s)",

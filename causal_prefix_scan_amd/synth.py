@@ -119,20 +119,22 @@ def make_decode_step(n_seq, H, d, dv, seed, step):
 
 
 # The forward workloads, named by what they are.  `chunk` is the number of
-# tokens per materialised segment summary.
+# tokens per materialised segment summary; `credit_chunk` is the chunk length
+# at which the algorithmic flops per token are counted (the 64-token tile when
+# the segments are longer than that).
 FWD_WORKLOADS = {
     "fwd_f32_b1h1t256d16": dict(B=1, H=1, T=256, d=16, dv=16, dtype="f32", seed=0,
-                                chunk=32, normalize=False, eps=0.0, k_l2norm=False,
-                                decay=False, tol=1e-4),
+                                chunk=32, credit_chunk=32, normalize=False, eps=0.0,
+                                k_l2norm=False, decay=False, tol=1e-4),
     "fwd_norm_bf16_b2h8t4096d64": dict(B=2, H=8, T=4096, d=64, dv=64, dtype="bf16", seed=1,
-                                       chunk=64, normalize=True, eps=1e-6, k_l2norm=True,
-                                       decay=False, tol=2e-2),
+                                       chunk=64, credit_chunk=64, normalize=True, eps=1e-6,
+                                       k_l2norm=True, decay=False, tol=2e-2),
     "fwd_decay_bf16_b4h16t16384d128": dict(B=4, H=16, T=16384, d=128, dv=128, dtype="bf16",
-                                           seed=2, chunk=4096, normalize=False, eps=0.0,
-                                           k_l2norm=False, decay=True, tol=2e-2),
+                                           seed=2, chunk=4096, credit_chunk=64, normalize=False,
+                                           eps=0.0, k_l2norm=False, decay=True, tol=2e-2),
     "fwd_bf16_b1h32t65536d64": dict(B=1, H=32, T=65536, d=64, dv=64, dtype="bf16", seed=3,
-                                    chunk=128, normalize=False, eps=0.0, k_l2norm=False,
-                                    decay=False, tol=2e-2),
+                                    chunk=128, credit_chunk=128, normalize=False, eps=0.0,
+                                    k_l2norm=False, decay=False, tol=2e-2),
 }
 
 DECODE_WORKLOAD = ("decode_bf16_n64h32d128",

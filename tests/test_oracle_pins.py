@@ -60,6 +60,48 @@ def test_hand_example_exact():
 
 # --- closed form --------------------------------------------------------------
 
+def _golden_normalise_cases():
+    from fractions import Fraction
+    with open(os.path.join(GOLDEN, "hand_example_d1.json")) as f:
+        ex = json.load(f)
+    by_gamma = {c["gamma"]: c for c in ex["cases"]}
+    for c in ex["normalise"]["cases"]:
+        base = by_gamma[c["gamma"]]
+        want = np.array([float(Fraction(x)) for x in c["o"]])
+        yield np.array(base["num"]), np.array(base["den"]), c["eps"], want
+
+
+def test_normalise_hand_example():
+    """o = num / (den + eps) on the hand-worked example, eps != 0 and one
+    negative denominator (gamma = 1, t = 3: den = -5)."""
+    seen_negative = False
+    for num, den, eps, want in _golden_normalise_cases():
+        got = O.normalise(num[None, :, None], den[None, :], eps)[0, :, 0]
+        assert rel(got, want) < 1e-15, (eps, got, want)
+        seen_negative |= bool(np.any(den < 0))
+    assert seen_negative
+
+
+NORMALISE_MUTANTS = [
+    ("/ (_f64(den)[..., None] + float(eps))", "/ (np.abs(_f64(den))[..., None] + float(eps))"),
+    ("/ (_f64(den)[..., None] + float(eps))", "/ (_f64(den)[..., None] - float(eps))"),
+    ("return _f64(num) / (_f64(den)[..., None] + float(eps))",
+     "return (_f64(num) + float(eps)) / _f64(den)[..., None]"),
+    ("return _f64(num) / (_f64(den)[..., None] + float(eps))",
+     "return _f64(num) / _f64(den)[..., None] + float(eps)"),
+]
+
+
+@pytest.mark.parametrize("old,new", NORMALISE_MUTANTS)
+def test_normalise_pin_catches_planted_mistakes(old, new):
+    bad = _mutant(O.normalise, old, new)
+    caught = False
+    for num, den, eps, want in _golden_normalise_cases():
+        got = bad(num[None, :, None], den[None, :], eps)[0, :, 0]
+        caught |= rel(got, want) > 1e-9
+    assert caught
+
+
 @pytest.mark.parametrize("gamma", GAMMAS)
 def test_serial_matches_brute_triple_sum(gamma):
     q, k, v = rnd(3, 18, 4, 3, seed=1)
