@@ -320,13 +320,33 @@ size_t hla_fwd_workspace_bytes(const hla_problem* p) {
 hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v, float* o,
                    float* den, const hla_state* final_state, void* workspace,
                    size_t workspace_bytes, void* stream) try {
+  if (hla_status e = hla::fwd_validate(p, q, k, v, o, den, final_state, workspace,
+                                        workspace_bytes, true))
+    return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = device_ready()) return e;
+  return hla::fwd_enqueue(p, q, k, v, o, den, final_state, workspace, stream);
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace hla {
+
+// Host-side checks of hla_fwd's arguments.  With check_ws the workspace must
+// be present (when the problem needs one), aligned and disjoint from the
+// inputs and outputs; without it the caller supplies a workspace of its own.
+hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, const void* v,
+                        float* o, float* den, const hla_state* final_state, const void* workspace,
+                        size_t workspace_bytes, bool check_ws) {
   if (hla_status e = check_problem(p)) return e;
   if (empty_problem(p)) return HLA_OK;
   if (hla_status e = check_qkv(q, k, v)) return e;
   if (!o) return HLA_ERR_NULL_POINTER;
   if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
   const Sizes z = sizes_of(p);
-  const size_t need = hla_fwd_workspace_bytes(p);
+  const size_t need = check_ws ? hla_fwd_workspace_bytes(p) : 0;
   if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0) {
     if (!workspace) return HLA_ERR_NULL_POINTER;
@@ -345,8 +365,16 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
                             den ? z.den_bytes : 0};
     if (hla_status e = check_state(final_state, false, z.units, z, fins, finb, 6)) return e;
   }
-  if (empty_problem(p)) return HLA_OK;
-  if (hla_status e = device_ready()) return e;
+  return HLA_OK;
+}
+
+// Enqueues the whole forward on `stream` with the summaries and the scan's
+// scratch in `workspace` (at least hla_fwd_workspace_bytes(p) bytes; the
+// arguments have passed fwd_validate and the problem is not empty).
+hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const void* v,
+                       float* o, float* den, const hla_state* final_state, void* workspace,
+                       void* stream) {
+  const Sizes z = sizes_of(p);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* w = static_cast<float*>(workspace);
   const size_t cnt = (size_t)z.units * (size_t)z.n;
@@ -385,11 +413,9 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
   if (hla_status e = do_scan(p, &sm, final_state, scan_ws, s)) return e;
   const ChunkArgs a3 = chunk_args(p, q, k, v, &sm, o, den);
   return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
-} catch (...) {
-  return HLA_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace hla
 
 namespace {
 

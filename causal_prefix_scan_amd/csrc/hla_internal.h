@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "hla.h"
+
 namespace hla {
 
 // Arguments of the chunk kernels (segment summaries and outputs).  All
@@ -105,6 +107,18 @@ hipError_t launch_ahla_outputs(int dtype, int d, int dv, int units, const AhlaAr
 hipError_t launch_ahla_decode(int dtype, int d, int dv, int units, const AhlaArgs& a, hipStream_t s);
 
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
+
+// hla_fwd in two parts (both host code, in the ABI layer): the argument
+// checks (with check_ws, also those of a caller's workspace of
+// workspace_bytes bytes), and the launches of the whole forward with the
+// summaries and the scan's scratch in `workspace` (hla_fwd_workspace_bytes
+// bytes; called only for a validated, non-empty problem).
+hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, const void* v,
+                        float* o, float* den, const hla_state* final_state, const void* workspace,
+                        size_t workspace_bytes, bool check_ws);
+hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const void* v,
+                       float* o, float* den, const hla_state* final_state, void* workspace,
+                       void* stream);
 
 // First-order decayed sum y_t = sum_{s<=t} lam^(t-s) (a_t.b_s) c_s over the
 // walk order (tokens 0..T-1, or T-1..0 when reverse), the building block of

@@ -25,7 +25,8 @@ EXPORTS = (
     "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
     "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
-    "hla_fwd", "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
+    "hla_fwd", "hla_fwd_noalloc_max_workspace_bytes", "hla_fwd_noalloc",
+    "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
     "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
     "hla_unmasked_decode_step", "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output",
     "hla_ahla_fwd_workspace_bytes", "hla_ahla_fwd", "hla_ahla_decode_step",
@@ -84,6 +85,9 @@ def lib():
     L.hla_fwd_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, sz, vp]
     L.hla_fwd_workspace_bytes.argtypes, L.hla_fwd_workspace_bytes.restype = [pp], sz
     L.hla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, ps, vp, sz, vp]
+    L.hla_fwd_noalloc_max_workspace_bytes.argtypes = []
+    L.hla_fwd_noalloc_max_workspace_bytes.restype = sz
+    L.hla_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, ps, vp]
     L.hla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, ps, vp, vp, vp]
     L.hla_unmasked_fwd_workspace_bytes.argtypes = [pp]
     L.hla_unmasked_fwd_workspace_bytes.restype = sz
@@ -102,7 +106,7 @@ def lib():
     L.hla_bwd_workspace_bytes.argtypes, L.hla_bwd_workspace_bytes.restype = [pp], sz
     L.hla_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
-                 "hla_fwd", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
+                 "hla_fwd", "hla_fwd_noalloc", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
                  "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step",
                  "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output", "hla_ahla_fwd",
                  "hla_ahla_decode_step", "hla_bwd"):
@@ -276,6 +280,27 @@ def fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False, wa
     _check(lib().hla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
                          ctypes.byref(fs) if fs is not None else None, _ptr(workspace),
                          ctypes.c_size_t(workspace.numel()), _stream()), "hla_fwd")
+    return o, den, final
+
+
+def fwd_noalloc(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False,
+                want_state=False, o=None, den=None):
+    """hla_fwd_noalloc: the forward with the library's own fixed scratch (no
+    workspace argument).  Returns (o, den or None, final state dict or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    if den is None and want_den:
+        den = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    final = alloc_state((B, H), d, dv, q.device) if want_state else None
+    fs = _state_struct(final)
+    _check(lib().hla_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                                 ctypes.byref(fs) if fs is not None else None, _stream()),
+           "hla_fwd_noalloc")
     return o, den, final
 
 

@@ -48,8 +48,9 @@
  *   - Supported head sizes: d, dv in {16, 32, 64, 128} with d/dv in
  *     {1/2, 1, 2}; fp32 inputs need d, dv <= 64 (HLA_ERR_UNSUPPORTED).
  *   - Calls on one device that share output or state buffers must be
- *     ordered by the caller (same stream or events); the library holds no
- *     global mutable state, so distinct calls are otherwise independent.
+ *     ordered by the caller (same stream or events); apart from the scratch
+ *     array of hla_fwd_noalloc (below) the library holds no global mutable
+ *     state, so distinct calls are otherwise independent.
  */
 #ifndef HLA_H
 #define HLA_H
@@ -199,6 +200,25 @@ size_t hla_fwd_workspace_bytes(const hla_problem* p);
 hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
                    float* o, float* den, const hla_state* final_state,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hla_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments (minus the workspace), results and errors as
+ * hla_fwd, with the summaries and the scan's scratch kept in a device array
+ * that the library owns.  That array has a fixed size,
+ * hla_fwd_noalloc_max_workspace_bytes() = 64 MiB, per device: a problem with
+ * hla_fwd_workspace_bytes(p) above it returns HLA_ERR_WORKSPACE_TOO_SMALL
+ * before anything is enqueued.  Each device the library runs this on holds
+ * its own copy of the array until the process ends; the call allocates and
+ * frees nothing.  Every call on one device shares that device's array, which
+ * keeps the last call's contents: calls on one device whose executions
+ * overlap (different streams without ordering, or host threads) race on it
+ * and must be ordered by the caller.
+ */
+size_t hla_fwd_noalloc_max_workspace_bytes(void);
+hla_status hla_fwd_noalloc(const hla_problem* p, const void* q, const void* k, const void* v,
+                           float* o, float* den, const hla_state* final_state, void* stream);
 
 /*
  * The unmasked second-order variant (method section 1: the plain product

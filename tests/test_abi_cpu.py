@@ -132,6 +132,26 @@ def test_workspace_sizes(L):
     assert L.hla_fwd(ctypes.byref(p), Q, K, V, O, None, None, 0x7000000000, 16, None) == WS
 
 
+def test_noalloc_limits_and_checks(L):
+    cap = L.hla_fwd_noalloc_max_workspace_bytes()
+    assert cap == 64 << 20
+    f = L.hla_fwd_noalloc
+    # a problem whose workspace exceeds the fixed scratch is refused up front
+    big = problem(B=4, H=16, T=16384, d=128, dv=128, chunk=128)
+    assert L.hla_fwd_workspace_bytes(ctypes.byref(big)) > cap
+    assert f(ctypes.byref(big), Q, K, V, O, None, None, None) == WS
+    # the same argument checks as hla_fwd, before any HIP call
+    p = problem()
+    assert f(ctypes.byref(problem(T=10)), Q, K, V, O, None, None, None) == SHAPE
+    assert f(ctypes.byref(p), None, K, V, O, None, None, None) == NULLP
+    assert f(ctypes.byref(p), Q, K, V, None, None, None, None) == NULLP
+    assert f(ctypes.byref(p), Q + 8, K, V, O, None, None, None) == MISAL
+    assert f(ctypes.byref(p), Q, K, V, Q, None, None, None) == ALIAS
+    assert f(ctypes.byref(p), Q, K, V, O, None, ctypes.byref(state(base=K)), None) == ALIAS
+    # an empty problem is a no-op
+    assert f(ctypes.byref(problem(T=0)), None, None, None, None, None, None, None) == OK
+
+
 def test_run_prefix_scan_sizes_and_checks(L):
     per = 32 * 32 + 2 * 32 * 16 + 2 * 32
     # run length: n up to 16 is one run; above, the power of two R with R^2 >= n
@@ -192,6 +212,7 @@ def test_valid_call_without_device_returns_hip_error(L):
     assert summaries(L, problem()) == HIP
     assert L.hla_fwd(ctypes.byref(problem()), Q, K, V, O, None, None, 0x7000000000, 1 << 40,
                      None) == HIP
+    assert L.hla_fwd_noalloc(ctypes.byref(problem()), Q, K, V, O, None, None, None) == HIP
     assert L.hla_decode_step(2, 2, 64, 64, hla.HLA_BF16, 0, 0.0, None, Q, K, V,
                              ctypes.byref(state()), O, None, None) == HIP
 
