@@ -12,6 +12,7 @@ Prints one JSON line.
 """
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -157,30 +158,21 @@ def bench_fwd(args, torch, np):
         q, k, v = (torch.from_numpy(x).cuda() for x in (inp.q, inp.k, inp.v))
     g = None if inp.gamma is None else torch.from_numpy(inp.gamma).cuda()
     dcode = hla.HLA_BF16 if cfg["dtype"] == "bf16" else hla.HLA_F32
-    n = T // chunk
+    L = hla.lib()
+    # hla_fwd's plan: each workgroup walks a span of R chunks (forming and
+    # combining their summaries in order), hla_scan runs over the span totals,
+    # and the outputs walk each span from its prefix
+    p0 = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
+    R = L.hla_fwd_span_chunks(ctypes.byref(p0))
+    span = chunk * R
+    n = T // span
     summ = hla.alloc_state((B, H, n), d, dv, "cuda")
     o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
     den = torch.empty(B, H, T, dtype=torch.float32, device="cuda") if cfg["normalize"] else None
-
-    import ctypes
-    L = hla.lib()
-    p = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
+    p = hla.make_problem(q, v, span, g, cfg["normalize"], cfg["eps"])
     st = hla._state_struct(summ)
-    # more than one run of whole segments: the scan stops at the run prefixes
-    # and the output kernel walks whole runs (chunk R * chunk)
-    R = hla.scan_run_length(T, chunk)
-    runs = -(-n // R)
-    use_runs = runs > 1 and runs * R == n
-    if use_runs:
-        rprefix = hla.alloc_state((B, H, runs), d, dv, "cuda")
-        rst = hla._state_struct(rprefix)
-        p_out = hla.make_problem(q, v, chunk * R, g, cfg["normalize"], cfg["eps"])
-        ws_bytes = L.hla_scan_runs_workspace_bytes(ctypes.byref(p))
-    else:
-        rst, p_out = st, p
-        ws_bytes = L.hla_scan_workspace_bytes(ctypes.byref(p))
+    ws_bytes = L.hla_scan_workspace_bytes(ctypes.byref(p))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    scan_name = "hla_scan_runs" if use_runs else "hla_scan"
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -191,14 +183,10 @@ def bench_fwd(args, torch, np):
         r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
         if ev:
             ev[1].record(stream)
-        if use_runs:
-            r2 = L.hla_scan_runs(ctypes.byref(p), ctypes.byref(st), ctypes.byref(rst), ptr(ws),
-                                 ctypes.c_size_t(ws_bytes), sp)
-        else:
-            r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
+        r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
         if ev:
             ev[2].record(stream)
-        r3 = L.hla_fwd_output(ctypes.byref(p_out), ptr(q), ptr(k), ptr(v), ctypes.byref(rst), ptr(o),
+        r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
                               ptr(den), None, ctypes.c_size_t(0), sp)
         if ev:
             ev[3].record(stream)
@@ -225,11 +213,11 @@ def bench_fwd(args, torch, np):
     U = B * H
     es = 2 if cfg["dtype"] == "bf16" else 4
     summ_bytes = U * n * (d * d + 2 * d * dv + 2 * d) * 4
-    prefix_bytes = summ_bytes // n * (runs if use_runs else n)   # prefixes the output kernel reads
+    prefix_bytes = summ_bytes                                    # prefixes the output kernel reads
     io_bytes = tokens * ((2 * d + dv) * es)
     kernels = {
         "hla_fwd_chunk_summaries": dict(ms=sum(k1) / len(k1), bytes=io_bytes + summ_bytes),
-        scan_name: dict(ms=sum(k2) / len(k2), bytes=None),
+        "hla_scan": dict(ms=sum(k2) / len(k2), bytes=None),
         "hla_fwd_output": dict(ms=sum(k3) / len(k3),
                                bytes=io_bytes + prefix_bytes + tokens * dv * 4
                                + (tokens * 4 if den is not None else 0)),
@@ -248,10 +236,12 @@ def bench_fwd(args, torch, np):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg["dtype"], "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
-                   "chunk": chunk, "decay": cfg["decay"], "normalize": cfg["normalize"],
-                   "path": ("hla_fwd_chunk_summaries + hla_scan_runs + hla_fwd_output over runs of "
-                            f"{R} segments" if use_runs
-                            else "hla_fwd_chunk_summaries + hla_scan + hla_fwd_output")},
+                   "chunk": chunk, "span_chunks": R, "decay": cfg["decay"],
+                   "normalize": cfg["normalize"],
+                   "path": (f"hla_fwd's plan: hla_fwd_chunk_summaries over spans of {R} chunk(s) "
+                            f"({span} tokens; each workgroup forms its chunks' summaries and "
+                            f"combines them in order), hla_scan over the {n} span totals per "
+                            f"(b, h), hla_fwd_output walking each span from its prefix")},
         "mfma_credited": {"flops_per_token": round(f_tok), "credit_chunk": cfg["credit_chunk"],
                           "tflops": round(value * f_tok / 1e12, 1),
                           "peak_tflops": BF16_PEAK_TFLOPS,

@@ -153,6 +153,30 @@ hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state
   return from_hip(hla::launch_scan(a, s));
 }
 
+// Consecutive chunks that each workgroup of hla_fwd's summary and output
+// kernels walks (a power of two dividing n).  Inside a workgroup the chunk
+// summaries of its span are formed and combined in order as its tiles go by
+// (the first level of the scan, fused with forming them); the span totals
+// then go through hla_scan.  Preferred: the fewest chunks per span that leave
+// at most 16 span totals per (b, h) (a single-run scan: one launch), as long
+// as that keeps at least 256 workgroups (one per CU with 8-wave kernels, or
+// two with 4-wave kernels); otherwise the most chunks per span that keep 256
+// workgroups.
+int64_t fwd_span_chunks(const hla_problem* p) {
+  const Sizes z = sizes_of(p);
+  const int64_t row_bytes = (int64_t)(p->d > p->dv ? p->d : p->dv) * (int64_t)dtype_size(p->in_dtype);
+  auto fits = [&](int64_t R) {
+    return z.n % R == 0 && (int64_t)p->chunk * R * row_bytes <= 2147483647;
+  };
+  const int64_t want_wg = 256;
+  int64_t R1 = 1;
+  while (z.n / R1 > 16 && fits(R1 * 2)) R1 *= 2;
+  if (z.n / R1 <= 16 && z.units * (z.n / R1) >= want_wg) return R1;
+  int64_t R = 1;
+  while (fits(R * 2) && z.units * (z.n / (R * 2)) >= want_wg) R *= 2;
+  return R;
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +251,12 @@ hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_stat
 int32_t hla_scan_run_length(const hla_problem* p) {
   if (check_problem(p) != HLA_OK) return 0;
   return hla::scan_run_length((int)(p->T / p->chunk));
+}
+
+int32_t hla_fwd_span_chunks(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK) return 0;
+  if (empty_problem(p)) return 1;
+  return (int32_t)fwd_span_chunks(p);
 }
 
 size_t hla_scan_runs_workspace_bytes(const hla_problem* p) {
@@ -374,7 +404,10 @@ hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, cons
 hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const void* v,
                        float* o, float* den, const hla_state* final_state, void* workspace,
                        void* stream) {
-  const Sizes z = sizes_of(p);
+  // spans of R chunks: summaries of the spans, the scan over them, outputs
+  hla_problem ps = *p;
+  ps.chunk = (int32_t)(p->chunk * fwd_span_chunks(p));
+  const Sizes z = sizes_of(&ps);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* w = static_cast<float*>(workspace);
   const size_t cnt = (size_t)z.units * (size_t)z.n;
@@ -382,36 +415,11 @@ hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const
   sm.S = w; sm.C = sm.S + cnt * z.S; sm.m = sm.C + cnt * z.C; sm.G = sm.m + cnt * z.m;
   sm.h = sm.G + cnt * z.C;
   void* scan_ws = sm.h + cnt * z.m;
-  const ChunkArgs a1 = chunk_args(p, q, k, v, &sm, nullptr, nullptr);
+  const ChunkArgs a1 = chunk_args(&ps, q, k, v, &sm, nullptr, nullptr);
   if (hla_status e = from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
     return e;
-  // Several runs of whole segments and no final state wanted: the run-level
-  // scan only, then the output kernel walks whole runs (chunk R * chunk),
-  // carrying the state across the segments of a run.  The run prefixes and
-  // the tree's padding fill exactly hla_scan's scratch.
-  const int64_t R = hla::scan_run_length((int)z.n), runs = (z.n + R - 1) / R;
-  const int64_t row_bytes = (int64_t)(p->d > p->dv ? p->d : p->dv) * (int64_t)dtype_size(p->in_dtype);
-  if (!final_state && runs > 1 && runs * R == z.n && (int64_t)p->chunk * R * row_bytes <= 2147483647) {
-    const size_t rc = (size_t)z.units * (size_t)runs;
-    hla_state rp;
-    rp.S = static_cast<float*>(scan_ws); rp.C = rp.S + rc * z.S; rp.m = rp.C + rc * z.C;
-    rp.G = rp.m + rc * z.m; rp.h = rp.G + rc * z.C;
-    hla::ScanPlan a;
-    a.S = sm.S; a.C = sm.C; a.m = sm.m; a.G = sm.G; a.h = sm.h;
-    a.tS = a.tC = a.tm = a.tG = a.th = nullptr;
-    a.rS = rp.S; a.rC = rp.C; a.rm = rp.m; a.rG = rp.G; a.rh = rp.h;
-    a.ws = rp.h + rc * z.m;
-    a.gamma = p->gamma;
-    a.units = (int)z.units; a.H = p->H; a.n = (int)z.n; a.chunk = p->chunk;
-    a.d = p->d; a.dv = p->dv;
-    if (hla_status e = from_hip(hla::launch_scan(a, s))) return e;
-    hla_problem pr = *p;
-    pr.chunk = (int32_t)(p->chunk * R);
-    const ChunkArgs a3 = chunk_args(&pr, q, k, v, &rp, o, den);
-    return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
-  }
-  if (hla_status e = do_scan(p, &sm, final_state, scan_ws, s)) return e;
-  const ChunkArgs a3 = chunk_args(p, q, k, v, &sm, o, den);
+  if (hla_status e = do_scan(&ps, &sm, final_state, scan_ws, s)) return e;
+  const ChunkArgs a3 = chunk_args(&ps, q, k, v, &sm, o, den);
   return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
 }
 

@@ -24,6 +24,7 @@ STATUS = {
 EXPORTS = (
     "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
     "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
+    "hla_fwd_span_chunks",
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
     "hla_fwd", "hla_fwd_noalloc_max_workspace_bytes", "hla_fwd_noalloc",
     "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
@@ -79,6 +80,7 @@ def lib():
     L.hla_scan_workspace_bytes.argtypes, L.hla_scan_workspace_bytes.restype = [pp], sz
     L.hla_scan.argtypes = [pp, ps, ps, vp, sz, vp]
     L.hla_scan_run_length.argtypes, L.hla_scan_run_length.restype = [pp], i32
+    L.hla_fwd_span_chunks.argtypes, L.hla_fwd_span_chunks.restype = [pp], i32
     L.hla_scan_runs_workspace_bytes.argtypes, L.hla_scan_runs_workspace_bytes.restype = [pp], sz
     L.hla_scan_runs.argtypes = [pp, ps, ps, vp, sz, vp]
     L.hla_fwd_output_workspace_bytes.argtypes, L.hla_fwd_output_workspace_bytes.restype = [pp], sz
@@ -218,6 +220,12 @@ def scan_run_length(T, chunk):
     """Segments per run of the blocked scan for n = T // chunk segments (host only)."""
     p = Problem(1, 1, int(T), 16, 16, int(chunk), HLA_F32, 0, 0.0, None)
     return int(lib().hla_scan_run_length(ctypes.byref(p)))
+
+
+def fwd_span_chunks(q, v, chunk, gamma=None):
+    """Chunks per span that hla_fwd's kernels walk (see hla_fwd_span_chunks)."""
+    p = make_problem(q, v, chunk, gamma)
+    return int(lib().hla_fwd_span_chunks(ctypes.byref(p)))
 
 
 def scan_runs(summaries, q_shape, dv, chunk, dtype_code, gamma=None):

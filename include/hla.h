@@ -186,16 +186,28 @@ hla_status hla_fwd_output(const hla_problem* p, const void* q, const void* k, co
 size_t hla_fwd_workspace_bytes(const hla_problem* p);
 
 /*
+ * Chunks per span of hla_fwd (a power of two R dividing n = T / chunk): each
+ * workgroup of hla_fwd's summary and output kernels walks R consecutive
+ * chunks, forming their summaries and combining them in order as it goes
+ * (the first level of the scan of method section 4, fused with forming the
+ * chunk summaries).  R is the smallest that leaves at most 16 span totals per
+ * (b, h) while keeping at least 256 workgroups, else the largest that keeps
+ * 256 workgroups.  Host-only; 0 for an invalid problem, 1 for an empty one.
+ */
+int32_t hla_fwd_span_chunks(const hla_problem* p);
+
+/*
  * The whole chunk-parallel forward (method section 4): segment summaries,
- * exclusive Blelloch scan, outputs -- the three calls above on one stream,
- * with the summaries kept in `workspace` (hla_fwd_workspace_bytes(p) bytes).
- * o and den as in hla_fwd_output.  If `final_state` is non-NULL its non-NULL
- * fields receive the state after all T tokens ([B, H, ...]), ready for
- * hla_decode_step.  Without a final state, and with more than one run of
- * R = hla_scan_run_length(p) segments where R divides n, the scan is
- * hla_scan_runs and the outputs are computed over whole runs (chunk R *
- * chunk) from the run prefixes; the results agree up to fp32 rounding
- * order.
+ * exclusive scan, outputs -- the three calls above on one stream, with
+ * chunk' = R * chunk, R = hla_fwd_span_chunks(p): hla_fwd_chunk_summaries
+ * writes the n / R span totals (each the combine, in order, of R chunk
+ * summaries), hla_scan turns them into exclusive prefixes, and
+ * hla_fwd_output walks each span from its prefix.  The summaries are kept in
+ * `workspace` (hla_fwd_workspace_bytes(p) bytes).  o and den as in
+ * hla_fwd_output; the results equal those of the three calls at `chunk` up
+ * to fp32 rounding order.  If `final_state` is non-NULL its non-NULL fields
+ * receive the state after all T tokens ([B, H, ...]), ready for
+ * hla_decode_step.
  */
 hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v,
                    float* o, float* den, const hla_state* final_state,

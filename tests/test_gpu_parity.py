@@ -119,7 +119,9 @@ def test_stages_match_oracle(gpu, case):
         ratio = host(o) / (host(dn)[..., None] + eps)
         assert rel_err(host(on), ratio) <= 1e-5
 
-    # the composed entry point gives the same bits as the three calls
+    # the composed entry point gives the same bits as the three calls (these
+    # problems have too few units for spans of several chunks)
+    assert hla.fwd_span_chunks(q, v, chunk, g) == 1
     o3, dn3, fs = hla.fwd(q, k, v, chunk, g, normalize=False, want_den=True, want_state=True)
     torch.cuda.synchronize()
     assert torch.equal(o3, o) and torch.equal(dn3, dn)
@@ -175,16 +177,64 @@ def test_run_prefixes_and_run_length_outputs(gpu, case):
     e_den = rel_err(host(dn).reshape(U, T), den)
     say(f"  run-length spans: num {e_num:.2e} den {e_den:.2e}")
     assert e_num <= tol and e_den <= tol
-    # hla_fwd without a final state takes this path: the same bits
-    o2, dn2, _ = hla.fwd(q, k, v, chunk, g, normalize=False, want_den=True)
-    torch.cuda.synchronize()
-    assert torch.equal(o2, o) and torch.equal(dn2, dn)
     if norm:
         eps = 1e-6
-        on, _, _ = hla.fwd(q, k, v, chunk, g, normalize=True, eps=eps)
+        on, _ = hla.fwd_output(q, k, v, rp, chunk * R, g, normalize=True, eps=eps)
         torch.cuda.synchronize()
         ratio = host(o) / (host(dn)[..., None] + eps)
         assert rel_err(host(on), ratio) <= 1e-5
+
+
+# (B, H, T, d, dv, chunk, dtype, decay, normalize): enough units for hla_fwd
+# to walk spans of several chunks per workgroup
+SPANS = [
+    (4, 4, 2048, 32, 32, 32, "bf16", True, True),      # n = 64 -> spans of 4 chunks, 16 per head
+    (2, 8, 1024, 64, 64, 16, "bf16", False, False),    # n = 64 -> spans of 4
+    (1, 16, 4096, 64, 64, 32, "bf16", True, False),    # n = 128 -> spans of 8, 16 per head
+    (4, 8, 512, 16, 32, 16, "f32", True, True),        # n = 32 -> spans of 2
+]
+
+
+@pytest.mark.parametrize("case", SPANS, ids=[case_id(c) for c in SPANS])
+def test_fwd_spans_of_several_chunks(gpu, case):
+    """hla_fwd with spans of R > 1 chunks: the same bits as the three calls at
+    chunk R * chunk, the oracle's outputs and final state at the tolerance."""
+    torch = gpu
+    B, H, T, d, dv, chunk, dtype, decay, norm = case
+    say("case", case_id(case))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, dtype, seed=3000 + T + d, decay=decay)
+    q, k, v, g = to_dev(inp)
+    R = hla.fwd_span_chunks(q, v, chunk, g)
+    n = T // chunk
+    assert R > 1 and n % R == 0 and B * H * (n // R) >= 256
+    say(f"  spans of {R} chunks, {n // R} per head")
+    eps = 1e-6
+    o, dn, fs = hla.fwd(q, k, v, chunk, g, normalize=norm, eps=eps, want_den=True, want_state=True)
+    gs = hla.fwd_chunk_summaries(q, k, v, chunk * R, g)
+    tot = hla.scan(gs, q.shape, dv, chunk * R, dcode(dtype), g, want_total=True)
+    o3, dn3 = hla.fwd_output(q, k, v, gs, chunk * R, g, normalize=norm, eps=eps, want_den=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o3) and torch.equal(dn, dn3)
+    for key in FIELDS:
+        assert torch.equal(fs[key], tot[key]), key
+    uq, uk, uv, ug = inp.units()
+    U = B * H
+    num, den, fin = O.serial(uq, uk, uv, ug)
+    tol = tol_of(dtype)
+    e_den = rel_err(host(dn).reshape(U, T), den)
+    if norm:
+        assert rel_err(host(o), host(o3)) == 0.0
+        on, _, _ = hla.fwd(q, k, v, chunk, g, normalize=False)
+        torch.cuda.synchronize()
+        e_num = rel_err(host(on).reshape(U, T, dv), num)
+        assert rel_err(host(o), host(on) / (host(dn)[..., None] + eps)) <= 1e-5
+    else:
+        e_num = rel_err(host(o).reshape(U, T, dv), num)
+    say(f"  num {e_num:.2e} den {e_den:.2e}")
+    assert e_num <= tol and e_den <= tol
+    for key in FIELDS:
+        e = rel_err(host(fs[key]).reshape(U, -1), fin[key].reshape(U, -1))
+        assert e <= tol, ("final state", key, e)
 
 
 def full_or_sampled(name, sample_units):
