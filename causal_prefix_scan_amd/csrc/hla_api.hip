@@ -842,6 +842,40 @@ size_t bwd_state_floats(const hla_problem* p, const Sizes& z) {
   return (size_t)z.units * (size_t)z.n * w * w;
 }
 
+size_t bwd_core_bytes(const hla_problem* p, const Sizes& z) {
+  const size_t do16 = p->in_dtype == HLA_BF16 ? (size_t)z.units * (size_t)p->T * (size_t)p->dv * 2 : 0;
+  return (2 * (size_t)z.units * (size_t)p->T * (size_t)p->d + bwd_state_floats(p, z) +
+          (size_t)z.units * (size_t)z.n * (size_t)p->d * (size_t)p->d) * 4 + do16;
+}
+
+// Extra workspace of the ratio-normalised backward, after the core's: the
+// unnormalised num [tok, dv] and den [tok] (fp32), the upstream gradients
+// g_num [tok, dv], g_den [tok, 16] and the unit channel [tok, 16] (in the
+// MFMA operand type), dp rounded to bf16 [tok, d] (bf16 inputs), and the
+// forward's own workspace; every part 16-byte aligned.
+struct NormWs {
+  size_t num, den, gnum, gden, one, dp16, fwd, total;
+};
+
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+NormWs norm_ws(const hla_problem* p, const Sizes& z) {
+  NormWs w;
+  const size_t tok = (size_t)z.units * (size_t)p->T;
+  const size_t es = p->in_dtype == HLA_BF16 ? 2 : 4;
+  w.num = align16(bwd_core_bytes(p, z));
+  w.den = w.num + align16(tok * p->dv * 4);
+  w.gnum = w.den + align16(tok * 4);
+  w.gden = w.gnum + align16(tok * p->dv * es);
+  w.one = w.gden + align16(tok * 16 * es);
+  w.dp16 = w.one + align16(tok * 16 * es);
+  w.fwd = w.dp16 + align16(p->in_dtype == HLA_BF16 ? tok * p->d * 2 : 0);
+  hla_problem pf = *p;
+  pf.normalize = 0;
+  w.total = w.fwd + hla_fwd_workspace_bytes(&pf);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -849,16 +883,13 @@ extern "C" {
 size_t hla_bwd_workspace_bytes(const hla_problem* p) {
   if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
   const Sizes z = sizes_of(p);
-  const size_t do16 = p->in_dtype == HLA_BF16 ? (size_t)z.units * (size_t)p->T * (size_t)p->dv * 2 : 0;
-  return (2 * (size_t)z.units * (size_t)p->T * (size_t)p->d + bwd_state_floats(p, z) +
-          (size_t)z.units * (size_t)z.n * (size_t)p->d * (size_t)p->d) * 4 + do16;
+  return p->normalize ? norm_ws(p, z).total : bwd_core_bytes(p, z);
 }
 
 hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const void* v,
                    const float* dout, float* dq, float* dk, float* dv, void* workspace,
                    size_t workspace_bytes, void* stream) try {
   if (hla_status e = check_problem(p)) return e;
-  if (p->normalize != 0) return HLA_ERR_UNSUPPORTED;
   if (empty_problem(p)) return HLA_OK;
   if (hla_status e = check_qkv(q, k, v)) return e;
   if (!dout || !dq || !dk || !dv) return HLA_ERR_NULL_POINTER;
@@ -917,6 +948,44 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
   void* do16 = bf ? static_cast<void*>(hkk + (size_t)z.units * (size_t)z.n * (size_t)d * (size_t)d)
                   : nullptr;
   const hla::LaOperand DOb = bf ? hla::LaOperand{do16, 1} : DO;
+  if (p->normalize) {
+    // o = num / (den + eps): the gradient is that of the numerator with the
+    // value channel v = 1 appended (den is num with v = 1) and the upstream
+    // gradient [dO / (den + eps), -(dO . num) / (den + eps)^2].  The v = 1
+    // channel adds one term to dp and one to dq: two more first-order sums
+    // whose operands carry the scalar in column 0 of 16.
+    const NormWs nw = norm_ws(p, z);
+    char* wb = static_cast<char*>(workspace);
+    float* num = reinterpret_cast<float*>(wb + nw.num);
+    float* den = reinterpret_cast<float*>(wb + nw.den);
+    void* gnum = wb + nw.gnum;
+    void* gden = wb + nw.gden;
+    void* one = wb + nw.one;
+    void* dp16 = wb + nw.dp16;
+    hla_problem pf = *p;
+    pf.normalize = 0;
+    if (hla_status r = hla::fwd_enqueue(&pf, q, k, v, num, den, nullptr, wb + nw.fwd, stream)) return r;
+    if (hla_status r = from_hip(hla::launch_norm_grad(bf, num, den, dout, p->eps, tok, e, gnum, gden,
+                                                      one, s)))
+      return r;
+    const hla::LaOperand G{gnum, bf}, GD{gden, bf}, ONE{one, bf};
+    const hla::LaOperand DPn = bf ? hla::LaOperand{dp16, 1} : hla::LaOperand{dpbuf, 0};
+    if (hla_status r = run(Q, K, K, d, d, 1, 0, pbuf, 0, hkk, false, 0, 0, bf)) return r;
+    // dp = sum_{t>=j} g^2(t-j) (v_j.G_t + g_t) q_t, accumulated in fp32
+    if (hla_status r = run(V, G, Q, e, d, 2, 1, dpbuf, 0)) return r;
+    if (hla_status r = run(P, Q, G, d, e, 2, 1, dv, 0, nullptr, true, 0, 1)) return r;
+    if (hla_status r = run(ONE, GD, Q, 16, d, 2, 1, dpbuf, 1)) return r;
+    if (bf) {
+      if (hla_status r = from_hip(hla::launch_to_bf16(dpbuf, dp16, tok * d, s))) return r;
+    }
+    // dq = sum_{j<=t} g^2(t-j) (G_t.v_j + g_t) p_j + S_t dp_t
+    if (hla_status r = run(G, V, P, e, d, 2, 0, dq, 0)) return r;
+    if (hla_status r = run(GD, ONE, P, 16, d, 2, 0, dq, 1)) return r;
+    if (hla_status r = run(DPn, K, K, d, d, 1, 0, dq, 1, hkk, true)) return r;
+    if (d >= (bf ? 32 : 4)) return run(K, Q, DPn, d, d, 1, 1, dk, 0, nullptr, false, 1);
+    if (hla_status r = run(K, Q, DPn, d, d, 1, 1, dk, 0)) return r;
+    return run(K, DPn, Q, d, d, 1, 1, dk, 1);
+  }
   // p = S q; dp, dv over the future tokens (weights g^2); dq = M dO + S dp;
   // dk from the future tokens' q and dp (weights g): one sum over the
   // symmetric states g^(..) (q dp^T + dp q^T) when d spans whole MFMA steps

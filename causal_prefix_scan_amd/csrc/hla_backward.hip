@@ -435,7 +435,61 @@ hipError_t launch_la(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) 
                      : launch_la_mode<float, MODE>(Da, Dc, units, a, s);
 }
 
+// Upstream gradients of the ratio-normalised output o = num / (den + eps),
+// one thread per token: dL/dnum = dO / (den + eps) (row of dv values) and
+// dL/dden = -(dO . num) / (den + eps)^2, written as column 0 of a row of
+// NC values whose other columns are 0, beside a row holding 1 in column 0 (the
+// value channel v = 1 that turns num into den).  Out is bf16 or fp32 (the
+// MFMA operand type of the sums that read it).
+template <typename T>
+__global__ __launch_bounds__(256) void norm_grad_kernel(const float* num, const float* den,
+                                                        const float* dout, float eps, size_t tokens,
+                                                        int dv, T* g_num, T* g_den, T* one) {
+  constexpr int NC = 16;
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= tokens) return;
+  const float r = 1.f / (den[t] + eps);
+  const float* x = dout + t * dv;
+  const float* y = num + t * dv;
+  float dot = 0.f;
+  for (int e = 0; e < dv; ++e) {
+    dot += x[e] * y[e];
+    g_num[t * dv + e] = (T)(x[e] * r);
+  }
+  g_den[t * NC] = (T)(-dot * r * r);
+  one[t * NC] = (T)1.f;
+  for (int e = 1; e < NC; ++e) {
+    g_den[t * NC + e] = (T)0.f;
+    one[t * NC + e] = (T)0.f;
+  }
+}
+
+// dp (fp32, accumulated) to the operand type of the later sums
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* x, __bf16* y, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = (__bf16)x[i];
+}
+
 }  // namespace
+
+hipError_t launch_norm_grad(int bf16, const float* num, const float* den, const float* dout,
+                            float eps, size_t tokens, int dv, void* g_num, void* g_den, void* one,
+                            hipStream_t s) {
+  const dim3 grid((unsigned)((tokens + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(norm_grad_kernel<__bf16>, grid, dim3(256), 0, s, num, den, dout, eps, tokens,
+                       dv, (__bf16*)g_num, (__bf16*)g_den, (__bf16*)one);
+  else
+    hipLaunchKernelGGL(norm_grad_kernel<float>, grid, dim3(256), 0, s, num, den, dout, eps, tokens, dv,
+                       (float*)g_num, (float*)g_den, (float*)one);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* x, void* y, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x,
+                     (__bf16*)y, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
                                   bool prefixes_ready) {

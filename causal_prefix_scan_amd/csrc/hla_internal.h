@@ -154,5 +154,15 @@ struct LaArgs {
 // same b, c and lam as an earlier call), so only the output pass runs.
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
                                   bool prefixes_ready = false);
+// Upstream gradients of the ratio-normalised output from the unnormalised
+// num [tokens, dv] and den [tokens] (fp32): g_num [tokens, dv] = dO / (den +
+// eps); g_den [tokens, 16] holds -(dO . num) / (den + eps)^2 in column 0 and
+// zeros elsewhere; one [tokens, 16] holds 1 in column 0 and zeros elsewhere.
+// The three outputs are bf16 (bf16 != 0) or fp32.
+hipError_t launch_norm_grad(int bf16, const float* num, const float* den, const float* dout,
+                            float eps, size_t tokens, int dv, void* g_num, void* g_den, void* one,
+                            hipStream_t s);
+// y[i] = bf16(x[i]) for i < n.
+hipError_t launch_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
 
 }  // namespace hla

@@ -379,16 +379,18 @@ def unmasked_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=
     return o, den
 
 
-def bwd(q, k, v, dout, chunk, gamma=None, workspace=None, dq=None, dk=None, dv=None):
-    """Gradients of the unnormalised masked forward for the upstream gradient
-    dout [B, H, T, dv] (fp32): (dq, dk [B, H, T, d], dv [B, H, T, dv]) fp32."""
+def bwd(q, k, v, dout, chunk, gamma=None, workspace=None, dq=None, dk=None, dv=None,
+        normalize=False, eps=0.0):
+    """Gradients of the masked forward (unnormalised, or num / (den + eps) with
+    normalize) for the upstream gradient dout [B, H, T, dv] (fp32):
+    (dq, dk [B, H, T, d], dv [B, H, T, dv]) fp32."""
     torch = _torch()
     _need_cuda(q, k, v, dout, gamma)
     if dout.dtype != torch.float32:
         raise RuntimeError("dout must be float32")
     B, H, T, d = q.shape
     e = v.shape[3]
-    p = make_problem(q, v, chunk, gamma, False, 0.0)
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
     if dq is None:
         dq = torch.empty(B, H, T, d, dtype=torch.float32, device=q.device)
     if dk is None:

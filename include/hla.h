@@ -332,32 +332,39 @@ hla_status hla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t 
                            const hla_state* state, float* o, float* den, void* stream);
 
 /*
- * Backward pass of the masked forward (unnormalised numerator).  The method
- * section on parallel training by associative scans motivates it; the pages
- * give no formula, so it is the plain gradient of the closed form
+ * Backward pass of the masked forward.  The method section on parallel
+ * training by associative scans motivates it; the pages give no formula, so
+ * it is the plain gradient of the closed form
  *   num_t = sum_{j<=t} sum_{i<=j} g^((t-i)+(t-j)) (q_t.k_i)(q_j.k_i) v_j
- * with respect to q, k and v, for an upstream gradient dout = dL/d num
- * ([B, H, T, dv] fp32).  gamma is not differentiated.
+ * (den_t the same with v = 1) with respect to q, k and v, for an upstream
+ * gradient dout = dL/do ([B, H, T, dv] fp32), o = num (normalize == 0) or
+ * o = num / (den + eps) (normalize == 1, method section 1's ratio-normalised
+ * variant).  gamma is not differentiated.
  *
  * With p_t = S_t q_t the forward is o_t = sum_{j<=t} g^(2(t-j)) (q_t.p_j) v_j,
  * and the gradient is seven first-order decayed sums over the tokens (p; the
  * others over the future tokens: dp, dv, dk, or the past: dq), each computed
  * chunk-parallel: segment states of `chunk` tokens, an exclusive decayed
- * running sum over the segments, then the outputs per segment.
+ * running sum over the segments, then the outputs per segment.  For the
+ * ratio-normalised output the forward's num and den are recomputed first,
+ * and the gradient is that of the numerator with the value channel v = 1
+ * appended and upstream gradient [dout / (den + eps), -(dout . num) /
+ * (den + eps)^2]: two more first-order sums (the v = 1 channel's terms of dp
+ * and dq).
  *
  * hla_bwd: writes dq, dk [B, H, T, d] and dv [B, H, T, dv] (fp32; they must
  *   not overlap each other, the inputs or the workspace).  Problem fields as
- *   for hla_fwd; normalize must be 0 (HLA_ERR_UNSUPPORTED otherwise).
- *   Precision as in the forward: bf16 inputs contract in bf16 (the
- *   intermediates p and dp are stored as bf16, dout is rounded to bf16 as an
- *   MFMA operand) with fp32 accumulation and state; fp32 inputs stay fp32
- *   throughout.
+ *   for hla_fwd.  Precision as in the forward: bf16 inputs contract in bf16
+ *   (the intermediates p and dp are stored as bf16, the upstream gradients
+ *   are rounded to bf16 as MFMA operands) with fp32 accumulation and state;
+ *   fp32 inputs stay fp32 throughout.
  * hla_bwd_workspace_bytes: the workspace hla_bwd needs (p and dp, fp32
  *   [B, H, T, d] each, of which bf16 inputs use half; the segment states,
  *   B*H*n*max(d, dv)^2 floats; the prefixes of the k k^T states,
- *   B*H*n*d*d floats, which p = S q and S dp share; and, with bf16 inputs,
- *   dout rounded to bf16, B*H*T*dv values, written by the first pass that
- *   reads dout and read by the later ones); 0 for an invalid or empty
+ *   B*H*n*d*d floats, which p = S q and S dp share; with bf16 inputs, dout
+ *   rounded to bf16, B*H*T*dv values; with normalize == 1 also the
+ *   recomputed num and den, the two upstream gradients, the v = 1 channel,
+ *   dp rounded to bf16 and hla_fwd's workspace); 0 for an invalid or empty
  *   problem.
  */
 size_t hla_bwd_workspace_bytes(const hla_problem* p);

@@ -337,7 +337,14 @@ def test_bwd_sizes_and_checks(L):
     W = 0x7000000000
     f = L.hla_bwd
     assert f(ctypes.byref(problem(T=10)), Q, K, V, DO, DQ, DK, DV, W, need, None) == SHAPE
-    assert f(ctypes.byref(problem(normalize=1)), Q, K, V, DO, DQ, DK, DV, W, need, None) == UNSUP
+    # the ratio-normalised backward needs more workspace (recomputed num and
+    # den, the two upstream gradients, the v = 1 channel, bf16 dp, the forward's
+    # workspace); too little is refused before anything runs
+    pn = problem(normalize=1, eps=1e-6)
+    need_n = L.hla_bwd_workspace_bytes(ctypes.byref(pn))
+    tok = 6 * 256
+    assert need_n >= need + tok * 64 * 4 + tok * 4 + tok * 64 * 2 + 2 * tok * 16 * 2 + tok * 64 * 2
+    assert f(ctypes.byref(pn), Q, K, V, DO, DQ, DK, DV, W, need, None) == WS
     assert f(ctypes.byref(problem(d=48)), Q, K, V, DO, DQ, DK, DV, W, need, None) == UNSUP
     assert f(ctypes.byref(p), None, K, V, DO, DQ, DK, DV, W, need, None) == NULLP
     assert f(ctypes.byref(p), Q, K, V, None, DQ, DK, DV, W, need, None) == NULLP

@@ -81,6 +81,48 @@ def test_bwd_matches_autograd(gpu, case):
         assert e <= tol, name
 
 
+# (B, H, T, d, dv, chunk, dtype, decay): the ratio-normalised output
+NORM = [
+    (1, 2, 256, 64, 64, 64, "bf16", True),
+    (1, 1, 200, 32, 64, 100, "bf16", False),      # ragged tiles, d < dv
+    (1, 2, 384, 128, 128, 96, "bf16", True),      # n = 4, 8-wave forward
+    (2, 1, 192, 64, 32, 64, "f32", True),         # fp32, d > dv
+    (1, 1, 128, 16, 16, 32, "f32", False),        # d = 16 (the v = 1 sums at width 16)
+]
+
+
+@pytest.mark.parametrize("case", NORM, ids=[case_id(c) + "-norm" for c in NORM])
+def test_bwd_normalised_matches_autograd(gpu, case):
+    """Gradient of o = num / (den + eps) against float64 autograd of the same
+    quotient.  q and k are taken in absolute value (exact in bf16), so every
+    q.k is positive and den stays well away from 0: the quotient's gradient
+    is then as well conditioned as the numerator's."""
+    torch = gpu
+    B, H, T, d, dv, chunk, dt, decay = case
+    say("normalised backward case", case_id(case))
+    eps = 1e-6
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, dt, seed=700 + T + d, decay=decay)
+    inp.q, inp.k = np.abs(inp.q), np.abs(inp.k)
+    if dt == "bf16":
+        inp.q_bits = inp.q_bits & np.uint16(0x7FFF)
+        inp.k_bits = inp.k_bits & np.uint16(0x7FFF)
+    q, k, v, g = to_dev(inp)
+    do_h, do = upstream(torch, B, H, T, dv, 700 + T)
+    dq, dk, dvv = hla.bwd(q, k, v, do, chunk, g, normalize=True, eps=eps)
+    torch.cuda.synchronize()
+    uq, uk, uv, ug = inp.units()
+    want = BO.grad_autograd(uq, uk, uv, do_h.reshape(B * H, T, dv), ug, normalize=True, eps=eps)
+    tol = 1e-4 if dt == "f32" else 2e-2
+    for name, got, w in zip(("dq", "dk", "dv"), (dq, dk, dvv), want):
+        e = rel_err(host(got).reshape(w.shape), w)
+        say(f"  {name} {e:.3e}  (tol {tol})")
+        assert e <= tol, name
+    # the unnormalised gradient differs (the quotient is not a rescaling)
+    dq0, _, _ = hla.bwd(q, k, v, do, chunk, g)
+    torch.cuda.synchronize()
+    assert rel_err(host(dq0), host(dq)) > 1e-2
+
+
 def test_bwd_gamma_zero_closed_form(gpu):
     # gamma = 0 keeps only i = j = t: o_t = (q_t.k_t)^2 v_t
     torch = gpu
