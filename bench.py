@@ -29,6 +29,8 @@ DEFAULT_WORKLOAD = "fwd_decay_bf16_b4h16t16384d128"
 BWD_WORKLOAD = "bwd_decay_bf16_b4h16t16384d128"
 BWD_CHUNK = 2048          # segment length of the backward's first-order sums
 BWD_TILE = 64             # tokens per tile of its kernels (bf16 inputs)
+HLA3_WORKLOAD = "hla3_decay_bf16_b4h16t16384d128"
+HLA3_CHUNK = 2048         # segment length of the third-order forward
 
 
 def credited_flops_per_token(c, d, dv):

@@ -1004,3 +1004,335 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
 }
 
 }  // extern "C"
+
+// ---- third-order HLA ------------------------------------------------------------
+
+namespace {
+
+// Workspace of the third-order calls: the unit channel, p, u and u_m (local,
+// then global; the MFMA operand type), the segment summaries (fp32; m, z, r
+// in the 16-wide layout), den16 and the 16-wide total of m.
+struct Ws3 {
+  size_t one, p, u, um, S, Q, V, P, Z, R, m, z, r, den16, tm16, total;
+};
+
+Ws3 ws3_of(const hla_problem* p) {
+  const Sizes z = sizes_of(p);
+  const size_t tok = (size_t)z.units * (size_t)p->T, es = dtype_size(p->in_dtype);
+  const size_t cnt = (size_t)z.units * (size_t)z.n, d = p->d, e = p->dv;
+  Ws3 w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += align16(bytes); return at; };
+  w.one = take(tok * 16 * es);
+  w.p = take(tok * d * es);
+  w.u = take(tok * e * es);
+  w.um = take(tok * 16 * es);
+  w.S = take(cnt * d * d * 4);
+  w.Q = take(cnt * d * d * 4);
+  w.V = take(cnt * d * d * 4);
+  w.P = take(cnt * d * e * 4);
+  w.Z = take(cnt * d * e * 4);
+  w.R = take(cnt * d * e * 4);
+  w.m = take(cnt * d * 16 * 4);
+  w.z = take(cnt * d * 16 * 4);
+  w.r = take(cnt * d * 16 * 4);
+  w.den16 = take(tok * 16 * 4);
+  w.tm16 = take((size_t)z.units * d * 16 * 4);
+  w.total = off;
+  return w;
+}
+
+struct Third {
+  const hla_problem* p;
+  Sizes z;
+  hipStream_t s;
+  int bf;
+  hla::LaOperand Q, K, V, ONE, Pq, U, UM;
+  // one first-order sum over this problem's segments
+  hla_status sum(hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
+                 float* y, int y_bf16, float* Hp, bool states_only) const {
+    hla::LaArgs la;
+    la.a = a; la.b = b; la.c = c;
+    la.y = y; la.Hp = Hp; la.gamma = p->gamma;
+    la.H = p->H; la.gexp = gexp;
+    la.T = p->T; la.seg = p->chunk; la.nseg = (int)z.n;
+    la.reverse = 0; la.accumulate = 0;
+    la.mfma_bf16 = bf;
+    la.y_bf16 = y_bf16;
+    if (states_only) return from_hip(hla::launch_first_order_states(Da, Dc, (int)z.units, la, s));
+    return from_hip(hla::launch_first_order_sum(Da, Dc, (int)z.units, la, s, true));
+  }
+};
+
+// Segment summaries into the workspace arrays of `w` (S, Q, V, P, Z, R as
+// [units, n, ...], m, z, r 16 wide), through the local p, u, u_m.
+hla_status third_summaries(const Third& t, char* wb, const Ws3& w, float* S, float* Qm, float* V,
+                           float* P, float* Z, float* R) {
+  const int d = t.p->d, e = t.p->dv;
+  float* m = reinterpret_cast<float*>(wb + w.m);
+  float* z = reinterpret_cast<float*>(wb + w.z);
+  float* r = reinterpret_cast<float*>(wb + w.r);
+  float* py = reinterpret_cast<float*>(wb + w.p);
+  float* uy = reinterpret_cast<float*>(wb + w.u);
+  float* umy = reinterpret_cast<float*>(wb + w.um);
+  const size_t tok = (size_t)t.z.units * (size_t)t.p->T;
+  if (hla_status x = from_hip(hla::launch_unit_channel(t.bf, wb + w.one, tok, t.s))) return x;
+  // local p, u, u_m: every segment from the zero state
+  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, py, t.bf, nullptr, false)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, uy, t.bf, nullptr, false)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, umy, t.bf, nullptr, false)) return x;
+  // the summaries as segment states
+  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, nullptr, 0, S, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.Q, t.Q, d, d, 1, nullptr, 0, Qm, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, nullptr, 0, P, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, nullptr, 0, m, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.Pq, t.Q, d, d, 2, nullptr, 0, V, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.Q, t.U, d, e, 2, nullptr, 0, Z, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.Q, t.UM, d, 16, 2, nullptr, 0, z, true)) return x;
+  if (hla_status x = t.sum(t.Q, t.Pq, t.U, d, e, 3, nullptr, 0, R, true)) return x;
+  return t.sum(t.Q, t.Pq, t.UM, d, 16, 3, nullptr, 0, r, true);
+}
+
+hla_status third_setup(const hla_problem* p, const void* q, const void* k, const void* v,
+                       void* workspace, void* stream, Third& t, Ws3& w) {
+  t.p = p;
+  t.z = sizes_of(p);
+  t.s = static_cast<hipStream_t>(stream);
+  t.bf = p->in_dtype == HLA_BF16 ? 1 : 0;
+  w = ws3_of(p);
+  char* wb = static_cast<char*>(workspace);
+  t.Q = {q, t.bf}; t.K = {k, t.bf}; t.V = {v, t.bf};
+  t.ONE = {wb + w.one, t.bf}; t.Pq = {wb + w.p, t.bf}; t.U = {wb + w.u, t.bf};
+  t.UM = {wb + w.um, t.bf};
+  return HLA_OK;
+}
+
+hla_status check_state3(const hla3_state* st, bool all_required, int64_t count, const hla_problem* p,
+                        const void* const* ins, const size_t* inb, int nin) {
+  if (!st) return HLA_ERR_NULL_POINTER;
+  float* f[5] = {st->S, st->P, st->m, st->R, st->r};
+  const size_t d = p->d, e = p->dv;
+  const size_t per[5] = {d * d, d * e, d, d * e, d};
+  for (int i = 0; i < 5; ++i) {
+    if (!f[i]) {
+      if (all_required) return HLA_ERR_NULL_POINTER;
+      continue;
+    }
+    if (!aligned16(f[i])) return HLA_ERR_MISALIGNED;
+    const size_t b = (size_t)count * per[i] * 4;
+    for (int j = 0; j < nin; ++j)
+      if (overlap(f[i], b, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    for (int j = 0; j < i; ++j)
+      if (f[j] && overlap(f[i], b, f[j], (size_t)count * per[j] * 4)) return HLA_ERR_ALIASING;
+  }
+  return HLA_OK;
+}
+
+hla_status check_summary3(const hla3_summary* sm, int64_t count, const hla_problem* p,
+                          const void* const* ins, const size_t* inb, int nin) {
+  if (!sm) return HLA_ERR_NULL_POINTER;
+  float* f[9] = {sm->S, sm->Q, sm->P, sm->m, sm->V, sm->Z, sm->z, sm->R, sm->r};
+  const size_t d = p->d, e = p->dv;
+  const size_t per[9] = {d * d, d * d, d * e, d, d * d, d * e, d, d * e, d};
+  for (int i = 0; i < 9; ++i) {
+    if (!f[i]) return HLA_ERR_NULL_POINTER;
+    if (!aligned16(f[i])) return HLA_ERR_MISALIGNED;
+    const size_t b = (size_t)count * per[i] * 4;
+    for (int j = 0; j < nin; ++j)
+      if (overlap(f[i], b, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    for (int j = 0; j < i; ++j)
+      if (overlap(f[i], b, f[j], (size_t)count * per[j] * 4)) return HLA_ERR_ALIASING;
+  }
+  return HLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hla3_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  return ws3_of(p).total;
+}
+
+hla_status hla3_chunk_summaries(const hla_problem* p, const void* q, const void* k, const void* v,
+                                const hla3_summary* out, void* workspace, size_t workspace_bytes,
+                                void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  const Sizes z = sizes_of(p);
+  const size_t need = hla3_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  const void* ins[4] = {q, k, v, workspace};
+  const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
+  for (int j = 0; j < 3; ++j)
+    if (overlap(workspace, need, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  if (hla_status e = check_summary3(out, z.units * z.n, p, ins, inb, 4)) return e;
+  if (hla_status e = device_ready()) return e;
+  Third t;
+  Ws3 w;
+  third_setup(p, q, k, v, workspace, stream, t, w);
+  char* wb = static_cast<char*>(workspace);
+  if (hla_status e = third_summaries(t, wb, w, out->S, out->Q, out->V, out->P, out->Z, out->R)) return e;
+  const size_t cnt = (size_t)z.units * (size_t)z.n * (size_t)p->d;
+  if (hla_status e = from_hip(hla::launch_gather_col0(reinterpret_cast<float*>(wb + w.m), out->m, cnt, t.s)))
+    return e;
+  if (hla_status e = from_hip(hla::launch_gather_col0(reinterpret_cast<float*>(wb + w.z), out->z, cnt, t.s)))
+    return e;
+  return from_hip(hla::launch_gather_col0(reinterpret_cast<float*>(wb + w.r), out->r, cnt, t.s));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla3_scan(const hla_problem* p, const hla3_summary* inout, const hla3_state* total_out,
+                     void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_summary3(inout, z.units * z.n, p, nullptr, nullptr, 0)) return e;
+  if (total_out) {
+    const float* f[9] = {inout->S, inout->Q, inout->P, inout->m, inout->V, inout->Z, inout->z,
+                         inout->R, inout->r};
+    const size_t d = p->d, e = p->dv, cnt = (size_t)z.units * (size_t)z.n;
+    const size_t per[9] = {d * d, d * d, d * e, d, d * d, d * e, d, d * e, d};
+    const void* ins[9];
+    size_t inb[9];
+    for (int i = 0; i < 9; ++i) { ins[i] = f[i]; inb[i] = cnt * per[i] * 4; }
+    if (hla_status x = check_state3(total_out, false, z.units, p, ins, inb, 9)) return x;
+  }
+  if (hla_status e = device_ready()) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = p->d, e = p->dv, units = (int)z.units, n = (int)z.n;
+  const hla3_state* t = total_out;
+  if (hla_status x = from_hip(hla::launch_moments_scan(inout->S, t ? t->S : nullptr, p->gamma, p->H,
+                                                       p->chunk, n, d * d, units, s)))
+    return x;
+  if (hla_status x = from_hip(hla::launch_moments_scan(inout->P, t ? t->P : nullptr, p->gamma, p->H,
+                                                       p->chunk, n, d * e, units, s)))
+    return x;
+  if (hla_status x = from_hip(hla::launch_moments_scan(inout->m, t ? t->m : nullptr, p->gamma, p->H,
+                                                       p->chunk, n, d, units, s)))
+    return x;
+  hla::R3ScanArgs a;
+  a.Sp = inout->S; a.Pp = inout->P; a.mp = inout->m; a.Q = inout->Q; a.V = inout->V;
+  a.Z = inout->Z; a.z = inout->z; a.R = inout->R; a.r = inout->r;
+  a.tR = t ? t->R : nullptr; a.tr = t ? t->r : nullptr;
+  a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 1;
+  return from_hip(hla::launch_r_scan(d, e, units, a, s));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla3_fwd(const hla_problem* p, const void* q, const void* k, const void* v, float* o,
+                    float* den, const hla3_state* final_state, void* workspace,
+                    size_t workspace_bytes, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  const size_t need = hla3_workspace_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+  const void* ins[4] = {q, k, v, workspace};
+  const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
+  for (int j = 0; j < 4; ++j) {
+    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (j < 3 && overlap(workspace, need, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
+  if (final_state) {
+    const void* fins[6] = {q, k, v, workspace, o, den};
+    const size_t finb[6] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need, z.o_bytes, den ? z.den_bytes : 0};
+    if (hla_status e = check_state3(final_state, false, z.units, p, fins, finb, 6)) return e;
+  }
+  if (hla_status e = device_ready()) return e;
+  Third t;
+  Ws3 w;
+  third_setup(p, q, k, v, workspace, stream, t, w);
+  char* wb = static_cast<char*>(workspace);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(wb + off); };
+  const int d = p->d, e = p->dv, units = (int)z.units, n = (int)z.n;
+  if (hla_status x = third_summaries(t, wb, w, F(w.S), F(w.Q), F(w.V), F(w.P), F(w.Z), F(w.R))) return x;
+  // the scan: the moments elementwise, then R and r with the segment map
+  const hla3_state* fs = final_state;
+  if (hla_status x = from_hip(hla::launch_moments_scan(F(w.S), fs ? fs->S : nullptr, p->gamma, p->H,
+                                                       p->chunk, n, d * d, units, t.s)))
+    return x;
+  if (hla_status x = from_hip(hla::launch_moments_scan(F(w.P), fs ? fs->P : nullptr, p->gamma, p->H,
+                                                       p->chunk, n, d * e, units, t.s)))
+    return x;
+  const bool want_m = fs && fs->m;
+  if (hla_status x = from_hip(hla::launch_moments_scan(F(w.m), want_m ? F(w.tm16) : nullptr, p->gamma,
+                                                       p->H, p->chunk, n, d * 16, units, t.s)))
+    return x;
+  if (want_m) {
+    if (hla_status x = from_hip(hla::launch_gather_col0(F(w.tm16), fs->m, (size_t)units * d, t.s))) return x;
+  }
+  hla::R3ScanArgs a;
+  a.Sp = F(w.S); a.Pp = F(w.P); a.mp = F(w.m); a.Q = F(w.Q); a.V = F(w.V); a.Z = F(w.Z); a.z = F(w.z);
+  a.R = F(w.R); a.r = F(w.r);
+  a.tR = fs ? fs->R : nullptr; a.tr = fs ? fs->r : nullptr;
+  a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 16;
+  if (hla_status x = from_hip(hla::launch_r_scan(d, e, units, a, t.s))) return x;
+  // outputs: p, u, u_m from their moments' prefixes, then num and den from R, r
+  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, F(w.p), t.bf, F(w.S), false)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, F(w.u), t.bf, F(w.P), false)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, F(w.um), t.bf, F(w.m), false)) return x;
+  if (hla_status x = t.sum(t.Q, t.Pq, t.U, d, e, 3, o, 0, F(w.R), false)) return x;
+  if (hla_status x = t.sum(t.Q, t.Pq, t.UM, d, 16, 3, F(w.den16), 0, F(w.r), false)) return x;
+  return from_hip(hla::launch_finish3(o, F(w.den16), den, (size_t)units * p->T, e, p->normalize,
+                                      p->eps, t.s));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla3_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                            int32_t normalize, float eps, const float* gamma, const void* q,
+                            const void* k, const void* v, const hla3_state* state, float* o,
+                            float* den, void* stream) try {
+  if (N < 0 || H < 0) return HLA_ERR_BAD_SHAPE;
+  if (in_dtype != HLA_F32 && in_dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (normalize != 0 && normalize != 1) return HLA_ERR_BAD_VALUE;
+  if (!std::isfinite(eps)) return HLA_ERR_BAD_VALUE;
+  if (!head_ok(d) || !head_ok(dv) || d > 2 * dv || dv > 2 * d) return HLA_ERR_UNSUPPORTED;
+  if ((int64_t)N * H > kMaxGrid) return HLA_ERR_BAD_VALUE;
+  if (N == 0 || H == 0) return HLA_OK;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(o) || (den && !aligned16(den)) || (gamma && !aligned16(gamma))) return HLA_ERR_MISALIGNED;
+  const size_t units = (size_t)N * (size_t)H;
+  const size_t es = in_dtype == HLA_BF16 ? 2 : 4;
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {units * d * es, units * d * es, units * dv * es};
+  hla_problem pd{};
+  pd.d = d; pd.dv = dv;
+  if (hla_status e = check_state3(state, true, (int64_t)units, &pd, ins, inb, 3)) return e;
+  const void* outs_in[5] = {state->S, state->P, state->m, state->R, state->r};
+  const size_t outs_b[5] = {units * d * d * 4, units * d * dv * 4, units * d * 4, units * d * dv * 4,
+                            units * d * 4};
+  for (int j = 0; j < 5; ++j) {
+    if (overlap(o, units * dv * 4, outs_in[j], outs_b[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, units * 4, outs_in[j], outs_b[j])) return HLA_ERR_ALIASING;
+  }
+  for (int j = 0; j < 3; ++j) {
+    if (overlap(o, units * dv * 4, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, units * 4, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (hla_status e = device_ready()) return e;
+  hla::Decode3Args a;
+  a.q = q; a.k = k; a.v = v; a.gamma = gamma;
+  a.S = state->S; a.P = state->P; a.m = state->m; a.R = state->R; a.r = state->r;
+  a.o = o; a.den = den; a.H = H; a.normalize = normalize; a.eps = eps;
+  return from_hip(hla::launch_decode3(in_dtype, d, dv, (int)units, a, static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -175,7 +175,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
   const int us = blockIdx.x;
   const int unit = us / a.nseg, seg = us - unit * a.nseg;
   float lam = a.gamma ? a.gamma[unit % a.H] : 1.f;
-  if (a.gexp == 2) lam *= lam;
+  lam = a.gexp == 3 ? lam * lam * lam : a.gexp == 2 ? lam * lam : lam;
   const float lgl = log2f(lam);
   const int nT = a.T;
   const bool rev = a.reverse != 0;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int elems) {
   const int e = (blockIdx.x - unit * per) * 256 + threadIdx.x;
   if (e >= elems) return;
   float lam = a.gamma ? a.gamma[unit % a.H] : 1.f;
-  if (a.gexp == 2) lam *= lam;
+  lam = a.gexp == 3 ? lam * lam * lam : a.gexp == 2 ? lam * lam : lam;
   const float aL = gpow(lam, log2f(lam), a.seg);
   float run = 0.f;
   float* p = a.Hp + (size_t)unit * a.nseg * elems + e;
@@ -489,6 +489,11 @@ hipError_t launch_to_bf16(const float* x, void* y, size_t n, hipStream_t s) {
   hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x,
                      (__bf16*)y, n);
   return hipGetLastError();
+}
+
+hipError_t launch_first_order_states(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
+  if (a.y_bf16 || a.accumulate || a.sym || a.b_copy) return hipErrorInvalidValue;
+  return launch_la<L_SUMMARY>(Da, Dc, units, a, s);
 }
 
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,

@@ -108,6 +108,42 @@ hipError_t launch_ahla_decode(int dtype, int d, int dv, int units, const AhlaArg
 
 hipError_t launch_decode(int dtype, int d, int dv, int units, const DecodeArgs& a, hipStream_t s);
 
+// Third order: the scan of R and r over a unit's segments (in place:
+// summaries in, exclusive prefixes out), given the moments' exclusive
+// prefixes Sp, Pp, mp and the segments' Q, V, Z, z.  m, z, r arrays have row
+// stride ldm (16 in the first-order-sum layout, 1 for plain [.., d]).
+struct R3ScanArgs {
+  const float *Sp, *Pp, *mp, *Q, *V, *Z, *z;
+  float *R, *r;
+  float *tR, *tr;        // inclusive totals [units, d, dv] and [units, d], or null
+  const float* gamma;
+  int H, seg, nseg, ldm;
+};
+struct Decode3Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  float *S, *P, *m, *R, *r;
+  float* o;
+  float* den;
+  int H, normalize;
+  float eps;
+};
+// Exclusive decayed running sum (a = gamma^seg) over each unit's nseg
+// segments of `elems` floats, in place; totals [units, elems] when not null.
+hipError_t launch_moments_scan(float* x, float* total, const float* gamma, int H, int seg, int nseg,
+                               int elems, int units, hipStream_t s);
+hipError_t launch_r_scan(int d, int dv, int units, const R3ScanArgs& a, hipStream_t s);
+// [tokens][16] rows of (1, 0, ..., 0), bf16 (bf16 != 0) or fp32.
+hipError_t launch_unit_channel(int bf16, void* one, size_t tokens, hipStream_t s);
+// den[t] = den16[t][0] (den may be null); with normalize, o[t] /= den + eps.
+hipError_t launch_finish3(float* o, const float* den16, float* den, size_t tokens, int dv,
+                          int normalize, float eps, hipStream_t s);
+// y[i] = x[16 i] for i < n.
+hipError_t launch_gather_col0(const float* x, float* y, size_t n, hipStream_t s);
+hipError_t launch_decode3(int dtype, int d, int dv, int units, const Decode3Args& a, hipStream_t s);
+
 // hla_fwd in two parts (both host code, in the ABI layer): the argument
 // checks (with check_ws, also those of a caller's workspace of
 // workspace_bytes bytes), and the launches of the whole forward with the
@@ -132,7 +168,7 @@ struct LaArgs {
   float* y;               // [unit][T][Dc] fp32 (bf16 with y_bf16), written or accumulated
   float* Hp;              // segment states [unit][nseg][Da][Dc] (workspace)
   const float* gamma;     // [H] or null (gamma = 1)
-  int H, gexp;            // lam = gamma[unit % H] ^ gexp, gexp in {1, 2}
+  int H, gexp;            // lam = gamma[unit % H] ^ gexp, gexp in {1, 2, 3}
   int T, seg, nseg;       // tokens per unit, tokens per segment, segments
   int reverse, accumulate;
   int mfma_bf16;          // contract in bf16 (fp32 accumulate) rather than fp32
@@ -151,9 +187,15 @@ struct LaArgs {
   void* b_copy = nullptr;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
-// same b, c and lam as an earlier call), so only the output pass runs.
+// same b, c and lam as an earlier call), so only the output pass runs; with
+// Hp null every segment starts from the zero state.
 hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hipStream_t s,
                                   bool prefixes_ready = false);
+// The segment states alone: Hp[unit][s] = sum over segment s of
+// lam^(L-1-i) b_i c_i^T (i local to the segment), from the zero state; a is
+// not read.
+hipError_t launch_first_order_states(int Da, int Dc, int units, const LaArgs& a, hipStream_t s);
+
 // Upstream gradients of the ratio-normalised output from the unnormalised
 // num [tokens, dv] and den [tokens] (fp32): g_num [tokens, dv] = dO / (den +
 // eps); g_den [tokens, 16] holds -(dO . num) / (den + eps)^2 in column 0 and

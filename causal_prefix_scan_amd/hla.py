@@ -32,6 +32,7 @@ EXPORTS = (
     "hla_unmasked_decode_step", "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output",
     "hla_ahla_fwd_workspace_bytes", "hla_ahla_fwd", "hla_ahla_decode_step",
     "hla_bwd_workspace_bytes", "hla_bwd",
+    "hla3_workspace_bytes", "hla3_chunk_summaries", "hla3_scan", "hla3_fwd", "hla3_decode_step",
 )
 
 
@@ -58,6 +59,14 @@ class State(ctypes.Structure):
 class AhlaState(ctypes.Structure):
     _fields_ = [("P", ctypes.c_void_p), ("m", ctypes.c_void_p), ("E", ctypes.c_void_p),
                 ("n", ctypes.c_void_p), ("X", ctypes.c_void_p)]
+
+
+class Summary3(ctypes.Structure):
+    _fields_ = [(x, ctypes.c_void_p) for x in ("S", "Q", "P", "m", "V", "Z", "z", "R", "r")]
+
+
+class State3(ctypes.Structure):
+    _fields_ = [(x, ctypes.c_void_p) for x in ("S", "P", "m", "R", "r")]
 
 
 _lib = None
@@ -107,6 +116,14 @@ def lib():
     L.hla_ahla_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, pa, vp, vp, vp]
     L.hla_bwd_workspace_bytes.argtypes, L.hla_bwd_workspace_bytes.restype = [pp], sz
     L.hla_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    p3s, p3t = ctypes.POINTER(Summary3), ctypes.POINTER(State3)
+    L.hla3_workspace_bytes.argtypes, L.hla3_workspace_bytes.restype = [pp], sz
+    L.hla3_chunk_summaries.argtypes = [pp, vp, vp, vp, p3s, vp, sz, vp]
+    L.hla3_scan.argtypes = [pp, p3s, p3t, vp]
+    L.hla3_fwd.argtypes = [pp, vp, vp, vp, vp, vp, p3t, vp, sz, vp]
+    L.hla3_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, p3t, vp, vp, vp]
+    for name in ("hla3_chunk_summaries", "hla3_scan", "hla3_fwd", "hla3_decode_step"):
+        getattr(L, name).restype = ctypes.c_int
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
                  "hla_fwd", "hla_fwd_noalloc", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
                  "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step",
@@ -522,4 +539,104 @@ def ahla_decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=Non
     _check(lib().hla_ahla_decode_step(N, H, d, dv, _dtype_code(q), int(bool(normalize)), float(eps),
                                       _ptr(gamma), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st),
                                       _ptr(o), _ptr(den), _stream()), "hla_ahla_decode_step")
+    return o, den
+
+
+# ---- third order ------------------------------------------------------------
+
+SUMMARY3_FIELDS = ("S", "Q", "P", "m", "V", "Z", "z", "R", "r")
+STATE3_FIELDS = ("S", "P", "m", "R", "r")
+
+
+def alloc_summary3(lead, d, dv, device):
+    """fp32 third-order segment summaries with leading dims `lead`."""
+    torch = _torch()
+    shapes = {"S": (d, d), "Q": (d, d), "V": (d, d), "P": (d, dv), "Z": (d, dv), "R": (d, dv),
+              "m": (d,), "z": (d,), "r": (d,)}
+    return {x: torch.zeros(*lead, *shapes[x], dtype=torch.float32, device=device)
+            for x in SUMMARY3_FIELDS}
+
+
+def alloc_state3(lead, d, dv, device):
+    """fp32 third-order decode state (S, P, m, R, r) with leading dims `lead`."""
+    torch = _torch()
+    shapes = {"S": (d, d), "P": (d, dv), "m": (d,), "R": (d, dv), "r": (d,)}
+    return {x: torch.zeros(*lead, *shapes[x], dtype=torch.float32, device=device)
+            for x in STATE3_FIELDS}
+
+
+def _s3(st):
+    return None if st is None else Summary3(*(_ptr(st[x]) for x in SUMMARY3_FIELDS))
+
+
+def _t3(st):
+    return None if st is None else State3(*(_ptr(st.get(x)) for x in STATE3_FIELDS))
+
+
+def _ws3(p, device):
+    torch = _torch()
+    n = lib().hla3_workspace_bytes(ctypes.byref(p))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def hla3_chunk_summaries(q, k, v, chunk, gamma=None):
+    """Third-order segment summaries [B, H, n, ...] (dict of fp32 tensors)."""
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma)
+    out = alloc_summary3((B, H, T // chunk), d, v.shape[3], q.device)
+    ws = _ws3(p, q.device)
+    _check(lib().hla3_chunk_summaries(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(_s3(out)),
+                                      _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()),
+           "hla3_chunk_summaries")
+    return out
+
+
+def hla3_scan(summaries, q, v, chunk, gamma=None, want_total=False):
+    """In place: S, P, m, R, r become exclusive prefixes; returns the inclusive
+    totals (dict) or None."""
+    _need_cuda(q, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma)
+    total = alloc_state3((B, H), d, v.shape[3], q.device) if want_total else None
+    t = _t3(total)
+    _check(lib().hla3_scan(ctypes.byref(p), ctypes.byref(_s3(summaries)),
+                           ctypes.byref(t) if t is not None else None, _stream()), "hla3_scan")
+    return total
+
+
+def hla3_fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False, want_state=False,
+             o=None, den=None):
+    """Third-order chunk-parallel forward: (o, den or None, final state or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    dv = v.shape[3]
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=torch.float32, device=q.device)
+    if den is None and want_den:
+        den = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    final = alloc_state3((B, H), d, dv, q.device) if want_state else None
+    t = _t3(final)
+    ws = _ws3(p, q.device)
+    _check(lib().hla3_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                          ctypes.byref(t) if t is not None else None, _ptr(ws),
+                          ctypes.c_size_t(ws.numel()), _stream()), "hla3_fwd")
+    return o, den, final
+
+
+def hla3_decode_step(q, k, v, state, gamma=None, normalize=False, eps=0.0, o=None, den=None):
+    """One third-order decode step; q, k [N, H, d], v [N, H, dv]; `state`
+    (S, P, m, R, r) is updated in place.  Returns (o, den or None)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    N, H, d = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=torch.float32, device=q.device)
+    t = _t3(state)
+    _check(lib().hla3_decode_step(N, H, d, dv, _dtype_code(q), int(bool(normalize)), float(eps),
+                                  _ptr(gamma), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(t), _ptr(o),
+                                  _ptr(den), _stream()), "hla3_decode_step")
     return o, den

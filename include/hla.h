@@ -319,6 +319,71 @@ hla_status hla_ahla_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int
                                 float* o, float* den, void* stream);
 
 /*
+ * Third-order HLA (method section 3: the masked interaction A A^T A with
+ * A = Q K^T, its prefix moments S^K, S^Q, P^KV and cross summaries; method
+ * section 4: the third-order scan, whose associative operator carries the
+ * segment-level linear maps M^KQP, M^KQm; key contribution 3: online update,
+ * streaming kernel, exact chunk-parallel algorithm).  Reading of the masked
+ * output (decay g per head as for the second order):
+ *   num_t = sum_{j<=t} sum_{i<=j} sum_{l<=j} g^((t-i)+(t-j)+(t-l)) (q_t.k_i)(q_j.k_i)(q_j.k_l) v_l,
+ *   den_t the same with v = 1, o = num or num / (den + eps);
+ * equivalently num_t = q_t^T R_t with R_t = sum_{j<=t} g^(3(t-j)) p_j u_j^T,
+ * p_j = S_j q_j, u_j = P_j^T q_j (S = sum g^(..) k k^T, P = sum g^(..) k v^T),
+ * and den_t = q_t . r_t with u_j -> q_j . m_j (m = sum g^(..) k).
+ *
+ * A segment summary (from the zero state, 1-based positions j in a segment of
+ * c tokens, a = g^c): the moments S, Q = sum g^(c-j) q_j q_j^T, P, m and the
+ * cross summaries V = sum g^(2(c-j)) p_j q_j^T, Z = sum g^(2(c-j)) q_j u_j^T,
+ * z = sum g^(2(c-j)) (q_j.m_j) q_j, R = sum g^(3(c-j)) p_j u_j^T,
+ * r = sum g^(3(c-j)) (q_j.m_j) p_j (p, u, m local to the segment).  Combine
+ * (A then B): moments X = a X_A + X_B; R = a^3 R_A + R_B + a S_A Z_B + M P_A,
+ * r = a^3 r_A + r_B + a S_A z_B + M m_A with the segment map
+ * M = a^2 S_A Q_B + a V_B.
+ *
+ * hla3_summary holds fp32 [B, H, n, ...] arrays: S, Q, V [d, d]; P, Z, R [d, dv];
+ * m, z, r [d].  hla3_state holds fp32 S [.., d, d], P [.., d, dv], m [.., d],
+ * R [.., d, dv], r [.., d] with leading [B, H] (final state) or [N, H]
+ * (decode state).  Problem fields, layouts of q, k, v, o, den, errors and the
+ * supported head sizes are those of the second-order calls.
+ *
+ * hla3_workspace_bytes: scratch of hla3_chunk_summaries and hla3_fwd (the
+ *   unit channel, p, u and q.m per token in the input dtype, the summaries
+ *   with m, z, r 16 floats wide, den 16 wide, a 16-wide total of m); 0 for
+ *   an invalid or empty problem.
+ * hla3_chunk_summaries: every segment's summary into `out` (all fields
+ *   required, no overlap with q, k, v or the workspace).
+ * hla3_scan: in place, the exclusive prefixes of S, P, m, R, r (Q, V, Z, z
+ *   only read): the moments by a decayed running sum, R and r by the combine
+ *   with the segment map, walking each (b, h)'s segments in order; the
+ *   non-NULL fields of `total_out` ([B, H, ...]) receive the inclusive totals.
+ * hla3_fwd: summaries, scan and outputs on one stream (the outputs continue
+ *   p, u and q.m from the moments' prefixes and num, den from R's and r's);
+ *   o [B, H, T, dv] fp32, den [B, H, T] (optional, before eps); the
+ *   non-NULL fields of `final_state` receive the state after T tokens, ready
+ *   for hla3_decode_step.  Precision as in the second order (bf16 inputs:
+ *   bf16 MFMA operands, p, u and q.m stored as bf16, fp32 accumulation, state
+ *   and scan; fp32 inputs: fp32 throughout).
+ * hla3_decode_step: one token per unit applied in place to `state` ([N, H,
+ *   ...], all fields required), o [N, H, dv] (num or num / (den + eps)) and the
+ *   optional den [N, H]; arguments and errors as for hla_decode_step.
+ */
+typedef struct { float *S, *Q, *P, *m, *V, *Z, *z, *R, *r; } hla3_summary;
+typedef struct { float *S, *P, *m, *R, *r; } hla3_state;
+size_t hla3_workspace_bytes(const hla_problem* p);
+hla_status hla3_chunk_summaries(const hla_problem* p, const void* q, const void* k, const void* v,
+                                const hla3_summary* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+hla_status hla3_scan(const hla_problem* p, const hla3_summary* inout, const hla3_state* total_out,
+                     void* stream);
+hla_status hla3_fwd(const hla_problem* p, const void* q, const void* k, const void* v, float* o,
+                    float* den, const hla3_state* final_state, void* workspace,
+                    size_t workspace_bytes, void* stream);
+hla_status hla3_decode_step(int32_t N, int32_t H, int32_t d, int32_t dv, int32_t in_dtype,
+                            int32_t normalize, float eps, const float* gamma, const void* q,
+                            const void* k, const void* v, const hla3_state* state, float* o,
+                            float* den, void* stream);
+
+/*
  * One streaming decode step (method section 1: the online update of the
  * prefix state; results and claims: constant work and memory per token).
  * For each of the N*H units: applies one token (q, k [N, H, d], v [N, H, dv]
