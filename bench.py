@@ -655,6 +655,176 @@ def bench_bwd(args, torch, np):
     return out
 
 
+def hla3_bytes_per_token(d, dv, es, chunk):
+    """Algorithmic HBM bytes per token of one hla3_fwd call: every pass reads
+    its operand rows and writes its outputs once (a pass whose value operand
+    is its key operand stages it once), and the segment summaries (9 arrays,
+    m, z, r 16 floats wide) go through HBM four times (written, read and
+    written by the scan, read by the output passes), spread over the
+    segment's tokens."""
+    one = 16 * es
+    passes = [
+        # local p, u, q.m: read q, k (and v / the unit channel), write the result
+        2 * d * es + d * es, 2 * d * es + dv * es + dv * es, 2 * d * es + one + one,
+        # summaries: read the two operands of each state
+        d * es, d * es, d * es + dv * es, d * es + one, 2 * d * es, d * es + dv * es,
+        d * es + one, d * es + dv * es, d * es + one,
+        # global p, u, q.m from the moments' prefixes
+        2 * d * es + d * es, 2 * d * es + dv * es + dv * es, 2 * d * es + one + one,
+        # num (fp32 out), den16 (fp32 out), den
+        2 * d * es + dv * es + dv * 4, 2 * d * es + one + 16 * 4, 16 * 4 + 4,
+    ]
+    state = (3 * d * d + 3 * d * dv + 3 * 16 * d) * 4
+    return sum(passes) + 4 * state / chunk
+
+
+def bench_hla3(args, torch, np):
+    """The third-order forward (one hla3_fwd call per step) on the decayed
+    B4 H16 T16384 d128 inputs."""
+    from causal_prefix_scan_amd import hla, synth
+    cfg = synth.FWD_WORKLOADS["fwd_decay_bf16_b4h16t16384d128"]
+    B, H, T, d, dv = (cfg[x] for x in ("B", "H", "T", "d", "dv"))
+    chunk = args.chunk or HLA3_CHUNK
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, "bf16", cfg["seed"], decay=True)
+    cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    g = torch.from_numpy(inp.gamma).cuda()
+    L = hla.lib()
+    p = hla.make_problem(q, v, chunk, g)
+    ws_bytes = L.hla3_workspace_bytes(ctypes.byref(p))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, H, T, dv, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step():
+        r = L.hla3_fwd(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(o), None, None, ptr(ws),
+                       ctypes.c_size_t(ws_bytes), sp)
+        if r:
+            raise RuntimeError(f"hla3_fwd failed: {r}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / args.steps
+    tokens = B * H * T
+    value = tokens / (step_ms / 1e3)
+    b_tok = hla3_bytes_per_token(d, dv, 2, chunk)
+    achieved = b_tok * tokens / (step_ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HLA3_WORKLOAD, "B": B, "H": H, "T": T, "d": d, "dv": dv,
+                   "chunk": chunk, "decay": True, "normalize": False,
+                   "path": "hla3_fwd: local p, u, q.m; segment summaries; moment scan and R, r "
+                           "scan with the segment map; p, u, q.m and num, den from the prefixes"},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "hla3_fwd (whole call)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": round(b_tok * tokens),
+                     "avg_launch_ms": round(step_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import hla3_oracle as O3
+        uq, uk, uv, ug = inp.units()
+        ntok = min(2048, T)
+        nt = cpu_threads()
+        with threadpool_limits(limits=nt):
+            t1 = time.perf_counter()
+            O3.serial3(uq[:, :ntok], uk[:, :ntok], uv[:, :ntok], ug)
+            dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": B * H * ntok / dt, "unit": "tokens/s", "cores": nt,
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": f"fp64 pages-form serial recurrence of the third order, all "
+                                         f"{B * H} (batch, head) units, first {ntok} of {T} tokens "
+                                         f"({dt:.1f} s)", "seconds": round(dt, 2)}
+    return out
+
+
+def bench_hla3_decode(args, torch, np):
+    """Third-order decode steps on the decode workload's shapes (64 sequences
+    x 32 heads, d = dv = 128), from the state after the 2048-token prefix
+    (hla3_fwd with one segment per prefix and a final state)."""
+    from causal_prefix_scan_amd import hla, synth
+    _, cfg = synth.DECODE_WORKLOAD
+    Nq, H, d, dv, P, seed = (cfg[x] for x in ("n_seq", "H", "d", "dv", "prefix_len", "seed"))
+    U = Nq * H
+    steps = args.steps
+    pre = synth.make_fwd_inputs(Nq, H, P, d, dv, "bf16", seed)
+    cv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    pq, pk, pv = cv(pre.q_bits), cv(pre.k_bits), cv(pre.v_bits)
+    _, _, state = hla.hla3_fwd(pq, pk, pv, P, None, want_state=True)
+    del pq, pk, pv
+    n_tok = args.warmup + steps
+    toks_host = [synth.make_decode_step(Nq, H, d, dv, seed, s) for s in range(n_tok)]
+    tq = torch.stack([cv(t[3][0]).reshape(Nq, H, d) for t in toks_host])
+    tk = torch.stack([cv(t[3][1]).reshape(Nq, H, d) for t in toks_host])
+    tv = torch.stack([cv(t[3][2]).reshape(Nq, H, dv) for t in toks_host])
+    o = torch.empty(Nq, H, dv, dtype=torch.float32, device="cuda")
+    den = torch.empty(Nq, H, dtype=torch.float32, device="cuda")
+    states64 = None
+    if not args.no_cpu_baseline:
+        states64 = {key: val.double().cpu().numpy().reshape(U, *val.shape[2:]) for key, val in state.items()}
+    for s in range(args.warmup):
+        hla.hla3_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(args.warmup, n_tok):
+        hla.hla3_decode_step(tq[s], tk[s], tv[s], state, None, True, cfg["eps"], o=o, den=den)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / steps
+    value = U / (step_ms / 1e3)
+    state_bytes = (d * d + 2 * d * dv + 2 * d) * 4
+    bytes_step = U * (2 * state_bytes + (2 * d + dv) * 2 + dv * 4 + 4)
+    achieved = bytes_step / (step_ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "unit-tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "hla3_decode_n64h32d128", "n_seq": Nq, "H": H, "d": d, "dv": dv,
+                   "prefix_len": P, "normalize": True, "path": "hla3_decode_step"},
+        "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "hla3_decode_step", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("hla3_decode_step@hla3_decode_n64h32d128"),
+                     "bytes_per_launch": bytes_step, "avg_launch_ms": round(step_ms, 4)},
+    }
+    if states64 is not None:
+        from threadpoolctl import threadpool_limits
+        from oracle import hla3_oracle as O3
+        nb = min(args.cpu_steps, len(toks_host))
+        nt = cpu_threads()
+        with threadpool_limits(limits=nt):
+            t1 = time.perf_counter()
+            st = states64
+            for s in range(nb):
+                _, _, st = O3.decode_step3(st, *toks_host[s][:3])
+            dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": U * nb / dt, "unit": "unit-tokens/s", "cores": nt,
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": f"fp64 third-order decode steps, {U} units x {nb} steps ({dt:.1f} s)",
+                               "seconds": round(dt, 2)}
+    return out
+
+
 def bench_copy(args, torch):
     """A plain device-to-device copy of a known size: the reference the HBM
     traffic counters (FETCH_SIZE, WRITE_SIZE) are scaled by."""
@@ -698,6 +868,10 @@ def main():
         out = bench_variant_fwd(args, torch, np)
     elif args.workload in VARIANT_DECODE:
         out = bench_variant_decode(args, torch, np)
+    elif args.workload == HLA3_WORKLOAD:
+        out = bench_hla3(args, torch, np)
+    elif args.workload == "hla3_decode_n64h32d128":
+        out = bench_hla3_decode(args, torch, np)
     elif args.workload == BWD_WORKLOAD:
         out = bench_bwd(args, torch, np)
     else:

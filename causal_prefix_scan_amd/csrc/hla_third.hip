@@ -179,119 +179,148 @@ __global__ __launch_bounds__(256) void gather_col0_kernel(const float* x, float*
   if (i < n) y[i] = x[i * 16];
 }
 
-// One decode step per unit (one workgroup of 256 threads):
+// One decode step per unit (one workgroup of 512 threads):
 //   S' = g S + k k^T, P' = g P + k v^T, m' = g m + k,
 //   p = S' q = g S q + (k.q) k,  u = P'^T q = g P^T q + (k.q) v,  qm = q.m',
 //   R' = g^3 R + p u^T,  r' = g^3 r + qm p,
 //   num = R'^T q = g^3 R^T q + (q.p) u,  den = q.r' = g^3 q.r + qm (q.p).
-// S, P and R are each read and written once (16-byte accesses).
+// Every load of S, P and R is issued up front (16-byte, non-temporal); S' and
+// P' are stored at once, R is held in registers until p and u are reduced.
 template <typename T, int D, int E>
-__global__ __launch_bounds__(256) void decode3_kernel(Decode3Args a) {
-  constexpr int NT = 256;
-  __shared__ float qs[D], ks[D], vs[E], ps[D], us[E], part[NT];
-  __shared__ float red[8];
-  const int unit = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(512) void decode3_kernel(Decode3Args a) {
+  constexpr int NT = 512;
+  constexpr int DV4 = D / 4, EV4 = E / 4;
+  constexpr int NS = (D * DV4 + NT - 1) / NT;     // float4s of S per thread
+  constexpr int NP = (D * EV4 + NT - 1) / NT;     // float4s of P (and R) per thread
+  constexpr int RG = NT / EV4;                    // threads sharing a column group of P, R
+  __shared__ float qs[D], ks[D], vs[E], ps[D], us[E], rq[E];
+  __shared__ f32x4 part[2][NT];
+  __shared__ float red[8][4];
+  const int unit = blockIdx.x, tid = threadIdx.x, wv = tid >> 6;
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float g3 = g * g * g;
+  float* S = a.S + (size_t)unit * D * D;
+  float* P = a.P + (size_t)unit * D * E;
+  float* R = a.R + (size_t)unit * D * E;
+  // every state load in flight before any arithmetic waits on one
+  f32x4 xs[NS], xp[NP], xr[NP];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int idx = tid + NT * j;
+    xs[j] = idx < D * DV4 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S) + idx) : zero4();
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int idx = tid + NT * j;
+    xp[j] = idx < D * EV4 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(P) + idx) : zero4();
+    xr[j] = idx < D * EV4 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(R) + idx) : zero4();
+  }
   const T* q = reinterpret_cast<const T*>(a.q) + (size_t)unit * D;
   const T* k = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
   const T* v = reinterpret_cast<const T*>(a.v) + (size_t)unit * E;
-  for (int i = tid; i < D; i += NT) { qs[i] = (float)q[i]; ks[i] = (float)k[i]; }
-  for (int i = tid; i < E; i += NT) vs[i] = (float)v[i];
-  __syncthreads();
-  // block sum of one value per thread (all threads call it)
-  auto bsum = [&](float x) {
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    if ((tid & 63) == 0) red[tid >> 6] = x;
-    __syncthreads();
-    const float r = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    return r;
-  };
-  const float kq = bsum(tid < D ? qs[tid] * ks[tid] : 0.f);
-  // m' and q.m'
   float* m = a.m + (size_t)unit * D;
-  float mn = 0.f;
+  float* r = a.r + (size_t)unit * D;
+  float mo = 0.f, ro = 0.f;
   if (tid < D) {
-    mn = g * m[tid] + ks[tid];
-    m[tid] = mn;
+    qs[tid] = (float)q[tid];
+    ks[tid] = (float)k[tid];
+    mo = m[tid];
+    ro = r[tid];
   }
-  const float qm = bsum(tid < D ? qs[tid] * mn : 0.f);
-  // S: p_i = g (S q)_i + (k.q) k_i; S' written in place.  Threads cover rows
-  // in groups of TPR = NT / D lanes, each lane D / TPR columns as float4s.
-  {
-    constexpr int TPR = NT / D > 0 ? NT / D : 1;
-    constexpr int RPI = D / (NT / TPR);          // rows per thread pass
-    float* S = a.S + (size_t)unit * D * D;
-    const int lane_r = tid % TPR, r_base = tid / TPR;
+  if (tid < E) vs[tid] = (float)v[tid];
+  __syncthreads();
+  // up to four block sums at once (every thread calls it)
+  auto bsum4 = [&](f32x4 x) {
 #pragma unroll
-    for (int pass = 0; pass < (RPI > 0 ? RPI : 1); ++pass) {
-      const int i = r_base + pass * (NT / TPR);
-      if (i < D) {
-        float acc = 0.f;
-        f32x4* rowp = reinterpret_cast<f32x4*>(S + (size_t)i * D);
-        for (int c4 = lane_r; c4 < D / 4; c4 += TPR) {
-          const f32x4 x = __builtin_nontemporal_load(rowp + c4);
-          acc += x[0] * qs[4 * c4] + x[1] * qs[4 * c4 + 1] + x[2] * qs[4 * c4 + 2] + x[3] * qs[4 * c4 + 3];
-          f32x4 y;
+    for (int off = 32; off >= 1; off >>= 1)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = g * x[j] + ks[i] * ks[4 * c4 + j];
-          __builtin_nontemporal_store(y, rowp + c4);
-        }
-        for (int off = 1; off < TPR; off *= 2) acc += __shfl_xor(acc, off, 64);
-        if (lane_r == 0) ps[i] = g * acc + kq * ks[i];
-      }
-    }
-  }
-  // P: u_e = g (P^T q)_e + (k.q) v_e; P' in place.  Thread (column group cg of
-  // four columns, row group rg) sums its rows; the row groups meet in LDS.
-  // X' = gain X + rowv colv^T in place; out_cols = q^T X over the old X
-  auto col_pass = [&](float* X, const float* rowv, const float* colv, float gain, float* out_cols) {
-    constexpr int CG = E / 4, RG = NT / CG;
-    const int cg = tid % CG, rg = tid / CG;
-    f32x4 acc = zero4();
-    for (int i = rg; i < D; i += RG) {
-      f32x4* p4 = reinterpret_cast<f32x4*>(X + (size_t)i * E) + cg;
-      const f32x4 x = __builtin_nontemporal_load(p4);
+      for (int i = 0; i < 4; ++i) x[i] += __shfl_xor(x[i], off, 64);
+    if ((tid & 63) == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wv][i] = x[i];
+    __syncthreads();
+    f32x4 y = zero4();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] += red[w][i];
+    __syncthreads();
+    return y;
+  };
+  const float qd = tid < D ? qs[tid] : 0.f, kd = tid < D ? ks[tid] : 0.f;
+  const float mn = g * mo + kd;
+  if (tid < D) m[tid] = mn;
+  const f32x4 s1 = bsum4(f32x4{qd * kd, qd * mn, qd * ro, 0.f});
+  const float kq = s1[0], qm = s1[1], qr_old = s1[2];
+  // S: row sums against q (rows of DV4 lanes), S' stored at once
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int idx = tid + NT * j;
+    const int i = idx / DV4, c = 4 * (idx % DV4);
+    float acc = 0.f;
+    if (idx < D * DV4) {
+      const f32x4 x = xs[j];
+      acc = x[0] * qs[c] + x[1] * qs[c + 1] + x[2] * qs[c + 2] + x[3] * qs[c + 3];
       f32x4 y;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = gain * x[j] + rowv[i] * colv[4 * cg + j];
-      __builtin_nontemporal_store(y, p4);
-      acc += x * qs[i];
+      for (int t = 0; t < 4; ++t) y[t] = g * x[t] + ks[i] * ks[c + t];
+      __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(S) + idx);
     }
-    // reduce the RG row groups
-    for (int j = 0; j < 4; ++j) {
-      part[tid] = acc[j];
-      __syncthreads();
-      if (rg == 0) {
-        float s = 0.f;
-        for (int r = 0; r < RG; ++r) s += part[r * CG + cg];
-        out_cols[4 * cg + j] = s;
-      }
-      __syncthreads();
-    }
-  };
-  // u: sum_i q_i P_ie over the old P, then P' = g P + k v^T
-  col_pass(a.P + (size_t)unit * D * E, ks, vs, g, us);
-  for (int e = tid; e < E; e += NT) us[e] = g * us[e] + kq * vs[e];
-  __syncthreads();
-  const float qp = bsum(tid < D ? qs[tid] * ps[tid] : 0.f);
-  // R' = g^3 R + p u^T; num = g^3 R^T q + (q.p) u (R^T q over the old R)
-  __shared__ float rq[E];
-  col_pass(a.R + (size_t)unit * D * E, ps, us, g3, rq);
-  // r' = g^3 r + qm p; den = g^3 q.r + qm (q.p)
-  float* r = a.r + (size_t)unit * D;
-  float qr_old = 0.f;
-  if (tid < D) {
-    const float ro = r[tid];
-    qr_old = qs[tid] * ro;
-    r[tid] = g3 * ro + qm * ps[tid];
+#pragma unroll
+    for (int off = 1; off < DV4; off *= 2) acc += __shfl_xor(acc, off, 64);
+    if (idx < D * DV4 && (idx % DV4) == 0) ps[i] = g * acc + kq * ks[i];
   }
-  const float qr = bsum(qr_old);
-  const float den = g3 * qr + qm * qp;
+  // P and R: column partial sums against q over this thread's rows (the old
+  // values); P' stored at once
+  f32x4 up = zero4(), rp = zero4();
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int idx = tid + NT * j;
+    if (idx < D * EV4) {
+      const int i = idx / EV4, c = 4 * (idx % EV4);
+      up += xp[j] * qs[i];
+      rp += xr[j] * qs[i];
+      f32x4 y;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = g * xp[j][t] + ks[i] * vs[c + t];
+      __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(P) + idx);
+    }
+  }
+  part[0][tid] = up;
+  part[1][tid] = rp;
+  __syncthreads();
+  if (tid < 2 * EV4) {
+    const int which = tid / EV4, cg = tid % EV4;
+    f32x4 sum = zero4();
+    for (int t = cg; t < NT; t += EV4) sum += part[which][t];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (which == 0) us[4 * cg + t] = g * sum[t] + kq * vs[4 * cg + t];
+      else rq[4 * cg + t] = sum[t];
+    }
+  }
+  __syncthreads();
+  // R' = g^3 R + p u^T
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int idx = tid + NT * j;
+    if (idx < D * EV4) {
+      const int i = idx / EV4, c = 4 * (idx % EV4);
+      f32x4 y;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = g3 * xr[j][t] + ps[i] * us[c + t];
+      __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(R) + idx);
+    }
+  }
+  const float pd = tid < D ? ps[tid] : 0.f;
+  if (tid < D) r[tid] = g3 * ro + qm * pd;
+  const f32x4 s2 = bsum4(f32x4{qd * pd, 0.f, 0.f, 0.f});
+  const float qp = s2[0];
+  const float den = g3 * qr_old + qm * qp;
   const float sc = a.normalize ? 1.f / (den + a.eps) : 1.f;
-  for (int e = tid; e < E; e += NT) a.o[(size_t)unit * E + e] = (g3 * rq[e] + qp * us[e]) * sc;
+  if (tid < E) a.o[(size_t)unit * E + tid] = (g3 * rq[tid] + qp * us[tid]) * sc;
   if (a.den && tid == 0) a.den[unit] = den;
+  (void)RG;
 }
 
 }  // namespace
@@ -338,7 +367,7 @@ hipError_t launch_gather_col0(const float* x, float* y, size_t n, hipStream_t s)
 hipError_t launch_decode3(int dtype, int d, int dv, int units, const Decode3Args& a, hipStream_t s) {
 #define HLA_CASE(T, D, E)                                                                         \
   if (d == D && dv == E) {                                                                        \
-    hipLaunchKernelGGL((decode3_kernel<T, D, E>), dim3((unsigned)units), dim3(256), 0, s, a);     \
+    hipLaunchKernelGGL((decode3_kernel<T, D, E>), dim3((unsigned)units), dim3(512), 0, s, a);     \
     return hipGetLastError();                                                                     \
   }
   if (dtype == 1) {
