@@ -261,12 +261,16 @@ struct RunArgs {
   int from_prefix;                 // rescan starts from a*[run] (else from the identity)
 };
 
-// Row tiles (16 rows) per workgroup of steps 1 and 3: all rows up to d = 64,
-// a quarter of them at d = 128 (register budget).  Every workgroup reads the whole
-// running C each step, so fewer row blocks means fewer re-reads of it.
+// Row tiles (16 rows) per workgroup of steps 1 and 3: one up to d = 64, two at
+// d = 128.  Each step of a run is a chain (this segment's products, then its
+// prefix out, then the running state in): fewer rows per workgroup shortens
+// every link and puts more workgroups on the walk, at the cost of every
+// workgroup reading the whole running C each step (measured: 16 segments per
+// head at d = 64, 54 -> 28 us with one row tile instead of four; at d = 128 two
+// row tiles beat one and four).
 template <int D>
 struct RunRT {
-  static constexpr int value = D <= 64 ? D / 16 : 2;
+  static constexpr int value = D <= 64 ? 1 : 2;
 };
 
 // Steps 1 (REDUCE) and 3: one workgroup per (unit, run, block of 16 RT rows),
