@@ -1089,12 +1089,29 @@ struct Waves {
   static constexpr int value = (D == 128 || E == 128) ? 8 : 4;
 };
 
+// bf16 kernels with a head dimension of 64 (and none of 128) also come with 8
+// waves: a grid of at most one workgroup per CU (256) leaves the second
+// 4-wave workgroup of a CU unused, and 8 waves hide more latency (measured:
+// 16 spans of 256 tokens per head, B2 H8 d64: summaries 23 -> 20 us, outputs
+// 36 -> 27 us; with two workgroups per CU the 4-wave kernels stay faster)
+template <int D, int E>
+struct Wide8 {
+  static constexpr bool value = (D == 64 || E == 64) && D <= 64 && E <= 64 && D >= 32 && E >= 32;
+};
+
 template <int MODE>
 static hipError_t launch_mode(int dtype, int d, int dv, int units, const ChunkArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)units * (unsigned)a.nspan);
+  const bool one_per_cu = (long long)units * a.nspan <= 256;
 #define HLA_CASE(T, D, E)                                                                    \
   if (d == D && dv == E) {                                                                   \
     constexpr int NW = Waves<D, E>::value;                                                   \
+    if constexpr (sizeof(T) == 2 && Wide8<D, E>::value) {                                    \
+      if (one_per_cu) {                                                                      \
+        hipLaunchKernelGGL((chunk_kernel<T, D, E, MODE, 8>), grid, dim3(512), 0, s, a);      \
+        return hipGetLastError();                                                            \
+      }                                                                                      \
+    }                                                                                        \
     hipLaunchKernelGGL((chunk_kernel<T, D, E, MODE, NW>), grid, dim3(64 * NW), 0, s, a);     \
     return hipGetLastError();                                                                \
   }

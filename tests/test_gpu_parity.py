@@ -60,6 +60,10 @@ SMALL = [
     (1, 1, 544, 128, 128, 32, "bf16", True, False),   # n = 17: runs 8, 8, 1
     (1, 2, 288, 128, 128, 96, "bf16", True, True),    # 8 waves, a 32-token last tile per segment
     (2, 1, 200, 128, 64, 100, "bf16", False, True),   # 8 waves, d > dv, 36-token last tile
+    # more than 256 workgroups: the 4-wave d = 64 kernels (the cases above with
+    # d = 64 run the 8-wave ones, a grid of at most one workgroup per CU)
+    (4, 16, 320, 64, 64, 64, "bf16", True, True),     # 64 units x 5 segments = 320 workgroups
+    (4, 16, 480, 64, 32, 96, "bf16", False, False),   # 320 workgroups, d > dv, ragged 32-token tile
 ]
 
 
