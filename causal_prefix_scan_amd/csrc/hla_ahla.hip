@@ -57,12 +57,6 @@ struct ALayout {
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
-__device__ __forceinline__ void atri(int idx, int& r, int& c) {
-  r = 0;
-  while (idx > r) { idx -= r + 1; ++r; }
-  c = idx;
-}
-
 // K^T fragment (rows d = n0 + (lane & 15), K = tokens) in the K order of
 // Frag<T>::acc_b, from K stored [tok][d]: bf16 step kk holds tokens
 // 32 kk + 4 g + [0, 4) and 32 kk + 16 + 4 g + [0, 4) (two transposing reads
@@ -236,7 +230,7 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
     //      all waves; q.m (and q.n) by all threads ----
     for (int idx = wave; idx < NTRI; idx += NW) {
       int r, c;
-      atri(idx, r, c);
+      tri_block(idx, r, c);
       f32x4 acc = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < DP; k0 += KS)
@@ -246,7 +240,7 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 16 * c + 4 * lg4 + j;
-        val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
+        val[j] = acc[j] * masked_pow(pw, tau, i);
       }
       if constexpr (sizeof(T) == 2) {
         bf16x4 y;

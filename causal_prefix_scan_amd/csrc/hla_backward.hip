@@ -236,8 +236,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
         const T* Xs = mirror ? Cs : Bs;
         const int ldx = mirror ? LDC : L::LDA;
         T* So = mirror ? Ss2 : Ss;
-        int r = 0, c = mirror ? idx - NB : idx;
-        while (c > r) { c -= r + 1; ++r; }
+        int r, c;
+        tri_block(mirror ? idx - NB : idx, r, c);
         f32x4 acc = zero4();
 #pragma unroll 8
         for (int k0 = 0; k0 < L::DP; k0 += KS)
@@ -246,7 +246,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tau = 16 * r + 4 * lg + j;
-          So[tau * L::LDS_ + s] = (T)(s <= tau ? acc[j] * pw[tau - s] : 0.f);
+          So[tau * L::LDS_ + s] = (T)(acc[j] * masked_pow(pw, tau, s));
         }
       }
       __syncthreads();

@@ -105,14 +105,6 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
   *reinterpret_cast<f32x4*>(p) = x;
 }
 
-// Lower-triangular 16x16 tile number idx (row block r of the later position,
-// column block c <= r) of the TR*(TR+1)/2 such tiles.
-__device__ __forceinline__ void tri_tile(int idx, int& r, int& c) {
-  r = 0;
-  while (idx > r) { idx -= r + 1; ++r; }
-  c = idx;
-}
-
 template <typename T, int D, int E, int MODE, int NW>
 // (4-wave kernels are held to two workgroups per CU: 256 registers per lane)
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkArgs a) {
@@ -390,7 +382,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     }
     for (int idx = wave; idx < NTRI; idx += NW) {
       int r, c;
-      tri_tile(idx, r, c);
+      tri_block(idx, r, c);
       f32x4 acc = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < DP; k0 += KS)
@@ -401,7 +393,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 16 * c + 4 * lg4 + j;
-        val[j] = (i <= tau) ? acc[j] * pw[tau - i] : 0.f;
+        val[j] = acc[j] * masked_pow(pw, tau, i);
       }
       store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
     }
@@ -418,7 +410,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     const T* PsT = PsTb(ti & 1);
     for (int idx = DEFER ? wave : rw; idx < NTRI; idx += NBW) {
       int r, c;
-      tri_tile(idx, r, c);
+      tri_block(idx, r, c);
       f32x4 acc = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < DP; k0 += KS)
@@ -428,7 +420,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int jj = 16 * c + 4 * lg4 + j;
-        val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
+        val[j] = acc[j] * masked_pow(pw2, tau, jj);
       }
       store4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
       if (need_n) {
@@ -463,7 +455,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   // decayed) of the tile in buffers p, left in registers
   auto a_tile = [&](int idx, int p) {
     int r, c;
-    tri_tile(idx, r, c);
+    tri_block(idx, r, c);
     const T* Qx = Qb(p);
     const T* Kx = Kb(p);
     f32x4 acc = zero4();
@@ -474,20 +466,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = 16 * c + 4 * lg4 + j;
-      acc[j] = (i <= tau) ? acc[j] * pw[tau - i] : 0.f;
+      acc[j] = acc[j] * masked_pow(pw, tau, i);
     }
     return acc;
   };
   auto a_store = [&](int idx, f32x4 val) {
     int r, c;
-    tri_tile(idx, r, c);
+    tri_block(idx, r, c);
     store4<T>(AB + (16 * r + lr) * L::LDT + 16 * c + 4 * lg4, val);
   };
   // B^T score tile idx of the tile whose P^T and Q sit in buffers p, to BB
   // (and its column sums to bpart)
   auto b_tile = [&](int idx, int p) {
     int r, c;
-    tri_tile(idx, r, c);
+    tri_block(idx, r, c);
     const T* PsT = PsTb(p);
     const T* Qx = Qb(p);
     f32x4 acc = zero4();
@@ -499,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int jj = 16 * c + 4 * lg4 + j;
-      val[j] = (jj <= tau) ? acc[j] * pw2[tau - jj] : 0.f;
+      val[j] = acc[j] * masked_pow(pw2, tau, jj);
     }
     store4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
     if (need_n) {

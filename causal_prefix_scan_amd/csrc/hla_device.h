@@ -177,6 +177,22 @@ __device__ __forceinline__ float gpow(float gamma, float lg, int n) {
   return exp2f((float)n * lg);
 }
 
+// Lower-triangular 16x16 block number idx (row block r of the later position,
+// column block c <= r, numbered row by row: (0,0), (1,0), (1,1), (2,0), ...) of
+// a tile of at most 4 row blocks, without a loop: r is read from a packed table.
+__device__ __forceinline__ void tri_block(int idx, int& r, int& c) {
+  r = (int)((0x3333222110ull >> (4 * idx)) & 15ull);
+  c = idx - (r * (r + 1)) / 2;
+}
+
+// pw[tau - i] (pw[n] = gamma^n) for i <= tau, else 0.  The table is read at a
+// clamped index whatever the mask, so the read needs no branch around it.
+__device__ __forceinline__ float masked_pow(const float* pw, int tau, int i) {
+  const int e = tau - i;
+  const float w = pw[e > 0 ? e : 0];
+  return e >= 0 ? w : 0.f;
+}
+
 // fp32 GEMM tile from LDS with fp32 MFMA: acc += X[r0:r0+16, 0:K] * Y[0:K, c0:c0+16]
 // with X stored [row][k] (leading dim ldx) and Y stored [k][col] (leading dim ldy).
 template <int K>

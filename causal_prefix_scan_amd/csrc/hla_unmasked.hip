@@ -69,13 +69,6 @@ struct ULayout {
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
-// Lower-triangular 16x16 tile number idx: row block r, column block c <= r.
-__device__ __forceinline__ void utri(int idx, int& r, int& c) {
-  r = 0;
-  while (idx > r) { idx -= r + 1; ++r; }
-  c = idx;
-}
-
 template <typename T>
 __device__ __forceinline__ void ustore4(T* p, f32x4 x);
 template <>
@@ -214,7 +207,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
     const T* Kx = Kb(p);
     for (int idx = first; idx < NTRI; idx += stride) {
       int r, c;
-      utri(idx, r, c);
+      tri_block(idx, r, c);
       f32x4 acc = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < DP; k0 += KS)
@@ -224,7 +217,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 16 * c + 4 * lg4 + j;
-        val[j] = i <= tau ? acc[j] * pw[tau - i] : 0.f;
+        val[j] = acc[j] * masked_pow(pw, tau, i);
       }
       ustore4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
     }
@@ -368,7 +361,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
       const T* Qx = Qb(p);
       for (int idx = wave; idx < NTRI; idx += NW) {
         int r, c;
-        utri(idx, r, c);
+        tri_block(idx, r, c);
         f32x4 acc = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < DP; k0 += KS)
@@ -378,7 +371,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = 16 * c + 4 * lg4 + jj;
-          val[jj] = j <= tau ? acc[jj] * pw[tau - j] : 0.f;
+          val[jj] = acc[jj] * masked_pow(pw, tau, j);
         }
         ustore4<T>(BB + tau * L::LDT + 16 * c + 4 * lg4, val);
         const float rs = sum_rows4(val[0] + val[1] + val[2] + val[3]);
