@@ -278,9 +278,7 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
 
     // ---- rm = q.m at every token (threads); the waves' value blocks ----
     if (tid < AT) {
-      float r = w1[tid] * qm[tid];
-      for (int c = 0; c <= tid / 16; ++c) r += bpart[c * AT + tid];
-      rmv[tid] = r;
+      rmv[tid] = add_lower_blocks(w1[tid] * qm[tid], bpart, AT, tid);
     }
     if (vblk) {
       // R = g^(tau+1) Q P + A' V (and O = g^(tau+1) Q E + A' R in the output kernel)

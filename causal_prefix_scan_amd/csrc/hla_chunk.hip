@@ -151,6 +151,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   float* pw2 = pw + TT;
   float* qn = pw2 + TT;          // [2][TT]: q.n by tile parity
   auto qnb = [&](int p) { return qn + p * TT; };
+  float* wC = qn;                // summary kernel (no q.n there): C and m weights
   float* bpart = qn + 2 * TT;    // [TR][TT]: B column sums per 16-row block of j
   float* nst = bpart + TR * TT;
   float* mst = nst + D;
@@ -349,6 +350,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     else store_part(x, tid - HT, Qs, Ks, Vs, VB{}, END{}, HALF{});
   };
 
+  // Summary kernel: C, m, M and n are needed only at the end of the segment, so
+  // their updates weight each token by its decay to the segment end (the
+  // tile's rows of sum_j g^(L-1-j) q_j v_j^T and sum_j g^(2(L-1-j)) p_j v_j^T)
+  // and the running sums are never rescaled.  Tile t, thread tid < TT.
+  auto end_weights = [&](int t, int Lt) {
+    const int after = Lspan - t * TT - 1 - tid;   // tokens after this one
+    wC[tid] = tid < Lt ? gpow(g, lgg, after) : 0.f;
+    wMb(t & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * after) : 0.f;
+  };
+
   // steps 0 and 1 of tile ti: stage the tile and its weights, then
   // A'^T = (K Q^T) o decay over all waves and q.n for the denominator
   int Lt_prev = -1;
@@ -364,7 +375,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     // wS for this tile; wM[ti & 1] was last written for tile ti - 2
     if ((ti < 2 || Lt != Lt_prev) && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
-      wMb(ti & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
+      if constexpr (!SUM) wMb(ti & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
+    }
+    if constexpr (SUM) {
+      if (tid < TT) end_weights(ti, Lt);
     }
     Lt_prev = Lt;
     __syncthreads();
@@ -444,11 +458,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   // ---- pieces of the pipelined (8-wave) kernels ----
   // decay weights of tile t (wS, and wM by parity), by the threads tid < TT;
   // only the last tile can be short, so tiles 2 .. ntiles-2 reuse earlier values
+  // (the summary kernel's weights to the segment end change every tile)
   auto weights = [&](int t) {
     const int Lt = (Lspan - t * TT) < TT ? (Lspan - t * TT) : TT;
     if ((t < 2 || t == ntiles - 1) && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
-      wMb(t & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
+      if constexpr (!SUM) wMb(t & 1)[tid] = tid < Lt ? gpow(g, lgg, 2 * (Lt - 1 - tid)) : 0.f;
+    }
+    if constexpr (SUM) {
+      if (tid < TT) end_weights(t, Lt);
     }
   };
   // A' score tile idx (rows 16 r + lr of the later position, masked and
@@ -609,9 +627,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       for (int b = 0; b < SB; ++b) {
         const int cb = rw + NOWN * b;
         if (need_n && (SFULL || cb < DT)) {
-          // n <- g^2Lt n + P^T wM: one writer per column; q.n of this tile is already taken
+          // n <- g^2Lt n + P^T wM (summary: n + P^T wM, weights to the segment
+          // end): one writer per column; q.n of this tile is already taken
           const float cs = sum_rows4(ncol[b]);
-          if (lg4 == 0) nst[16 * cb + lr] = g2L * nst[16 * cb + lr] + cs;
+          if (lg4 == 0) nst[16 * cb + lr] = (SUM ? nst[16 * cb + lr] : g2L * nst[16 * cb + lr]) + cs;
         }
       }
       // S[:, blocks] <- g^Lt S + K^T diag(wS) K[:, blocks]; the K^T fragments are shared
@@ -776,7 +795,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     uint4 xv[PF ? NXM : 1];
 
     // M[:, blocks] <- g^2L M + P^T diag(wM) V[:, blocks] for tile tp (its P^T, V
-    // and wM are in the buffers of tp's parity); the P^T fragments are shared
+    // and wM are in the buffers of tp's parity); the P^T fragments are shared.
+    // Summary kernel: M + P^T diag(wM) V, wM the weights to the segment end
     auto m_update = [&](int tp, float g2Lp) {
       const T* PsT = PsTb(tp & 1);
       const T* Vs = Vsb(tp & 1);
@@ -791,7 +811,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       for (int t = 0; t < DT; ++t) {
         f32x4 acc[MB];
 #pragma unroll
-        for (int b = 0; b < MB; ++b) acc[b] = St[b][t] * g2Lp;
+        for (int b = 0; b < MB; ++b) acc[b] = SUM ? St[b][t] : St[b][t] * g2Lp;
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
           const F ap = MMT::ld(PsT, L::LDT, 16 * t, kk * KS, lane);
@@ -878,19 +898,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         for (int b = 0; b < MB; ++b) oacc[b][r] *= w2t;
       }
     };
-    // C[:, blocks] <- g^Lt C + Q^T diag(wS) V[:, blocks] (summary); the Q^T fragments are shared
-    auto c_update = [&](const T* Qx, const T* Vs, float gL) {
+    // C[:, blocks] <- C + Q^T diag(wC) V[:, blocks] (summary; wC: the weights to
+    // the segment end); the Q^T fragments are shared
+    auto c_update = [&](const T* Qx, const T* Vs) {
       F bv[MB][NKS];
 #pragma unroll
       for (int b = 0; b < MB; ++b)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk)
-          bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wS, kk * KS, lane);
+          bv[b][kk] = FR::scale(FR::tr(Vs, L::LDV, kk * KS, 16 * ((rw + NOWN * b) % ET), lane), wC, kk * KS, lane);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         f32x4 acc[MB];
 #pragma unroll
-        for (int b = 0; b < MB; ++b) acc[b] = Ct[b][t] * gL;
+        for (int b = 0; b < MB; ++b) acc[b] = Ct[b][t];
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
           const F aq = FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane);
@@ -902,29 +923,37 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           if (MFULL || rw + NOWN * b < ET) Ct[b][t] = acc[b];
       }
     };
-    // m <- g^Lt m + Q^T wS (summary) on MFMA: the B operand is wS in column 0
+    // m <- m + Q^T wC (summary) on MFMA: the B operand is wC in column 0
     // and zeros elsewhere, so column 0 of the product (lanes lr == 0) is m for
     // the rows 16 t + [0, 16) of this wave's blocks t = rw + NOWN s
     constexpr int MS = (DT + NOWN - 1) / NOWN;
     f32x4 macc[SUM ? MS : 1];
 #pragma unroll
     for (int sm = 0; sm < (SUM ? MS : 1); ++sm) macc[sm] = zero4();
-    auto m_mma = [&](const T* Qx, float gL) {
+    auto m_mma = [&](const T* Qx) {
+      // every lane reads its weights (32-byte aligned runs of wC) and keeps them
+      // only in column 0, so that no read waits behind a branch of its own
       F wc[NKS];
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk) {
         if constexpr (sizeof(T) == 2) {
+          const f32x4* w8 = reinterpret_cast<const f32x4*>(wC + kk * KS + 8 * lg4);
+          const f32x4 lo = w8[0], hi = w8[1];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) wc[kk][i] = (T)(lr == 0 ? wS[kk * KS + 8 * lg4 + i] : 0.f);
+          for (int i = 0; i < 4; ++i) {
+            wc[kk][i] = (T)(lr == 0 ? lo[i] : 0.f);
+            wc[kk][4 + i] = (T)(lr == 0 ? hi[i] : 0.f);
+          }
         } else {
-          wc[kk] = lr == 0 ? wS[kk * KS + lg4] : 0.f;
+          const float w = wC[kk * KS + lg4];
+          wc[kk] = lr == 0 ? w : 0.f;
         }
       }
 #pragma unroll
       for (int sm = 0; sm < MS; ++sm) {
         const int t = rw + NOWN * sm;
         if (t < DT) {
-          f32x4 acc = macc[sm] * gL;
+          f32x4 acc = macc[sm];
 #pragma unroll
           for (int kk = 0; kk < NKS; ++kk) acc = MMT::mma(FR::tr(Qx, L::LDD, kk * KS, 16 * t, lane), wc[kk], acc);
           macc[sm] = acc;
@@ -945,7 +974,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       for (int ti = 0; ti < ntiles; ++ti) {
         const int t0 = ti * TT;
         const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
-        const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+        const float g2L = gpow(g, lgg, 2 * Lt);
         // summary: the previous tile's M update, the C and m updates of this
         // tile and A' tiles of the next one; output: the previous tile's
         // outputs, the M update, then (Q M)^T of this tile
@@ -954,8 +983,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           if (ti > 0) m_update(ti - 1, g2L_prev);
           if (ti + 1 < ntiles) load_slots(xv, ti + 1, tid - HT, VB{}, END{}, HALF{}, H1{}, H2{});
           __builtin_amdgcn_sched_barrier(0);
-          c_update(Qb(ti & 1), Vsb(ti & 1), gL);
-          m_mma(Qb(ti & 1), gL);
+          c_update(Qb(ti & 1), Vsb(ti & 1));
+          m_mma(Qb(ti & 1));
           if (ti + 1 < ntiles) {
 #pragma unroll
             for (int sl = 0; sl < NAS; ++sl)
@@ -992,7 +1021,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       for (int ti = 0; ti < ntiles; ++ti) {
         const int t0 = ti * TT;
         const int Lt = (Lspan - t0) < TT ? (Lspan - t0) : TT;
-        const float gL = gpow(g, lgg, Lt), g2L = gpow(g, lgg, 2 * Lt);
+        const float g2L = gpow(g, lgg, 2 * Lt);
         tile_head(ti, Lt, xv, std::false_type{});
 
         // ---- step 2: the previous tile's outputs (output kernel) and M update,
@@ -1004,8 +1033,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         if (ti > 0) m_update(ti - 1, g2L_prev);
         __builtin_amdgcn_sched_barrier(0);   // keep the two updates' operand loads apart
         if constexpr (!SUM) qm(Qs);
-        else c_update(Qs, Vsb(ti & 1), gL);
-        if constexpr (SUM) m_mma(Qs, gL);
+        else c_update(Qs, Vsb(ti & 1));
+        if constexpr (SUM) m_mma(Qs);
         g2L_prev = g2L;
         __syncthreads();
 

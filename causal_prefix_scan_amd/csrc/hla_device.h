@@ -193,6 +193,19 @@ __device__ __forceinline__ float masked_pow(const float* pw, int tau, int i) {
   return e >= 0 ? w : 0.f;
 }
 
+// init + sum of part[c * ld + tau] over the column blocks c <= tau / 16 of a
+// 64-position tile, in the order c = 0, 1, ...; every block is read and the
+// ones past the diagonal are dropped by a select, so no read waits on a branch.
+__device__ __forceinline__ float add_lower_blocks(float init, const float* part, int ld, int tau) {
+  float s = init;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float x = part[c * ld + tau];
+    s += c <= tau / 16 ? x : 0.f;
+  }
+  return s;
+}
+
 // fp32 GEMM tile from LDS with fp32 MFMA: acc += X[r0:r0+16, 0:K] * Y[0:K, c0:c0+16]
 // with X stored [row][k] (leading dim ldx) and Y stored [k][col] (leading dim ldy).
 template <int K>

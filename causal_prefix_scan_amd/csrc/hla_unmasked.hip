@@ -432,9 +432,7 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
     }
     const int mt = tid - HT;
     if (a.den != nullptr && mt < Ltp) {
-      float dn = w1[mt] * pm[mt];
-      for (int c = 0; c <= mt / 16; ++c) dn += bpart[c * UT + mt];
-      a.den[tok0 + (size_t)tp * UT + mt] = dn;
+      a.den[tok0 + (size_t)tp * UT + mt] = add_lower_blocks(w1[mt] * pm[mt], bpart, UT, mt);
     }
   };
 
