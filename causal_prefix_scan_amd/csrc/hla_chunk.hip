@@ -552,11 +552,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   // B scores of ti and A' of ti + 1 (2 NTRI tiles over the waves), q.n of ti + 1
   auto score_phase = [&](int ti) {
     const bool nxt = ti + 1 < ntiles;
-#pragma unroll
-    for (int sl = 0; sl < (2 * NTRI + NW - 1) / NW; ++sl) {
-      const int idx = wave + NW * sl;
+    // 2 NTRI jobs (B tiles of ti, then A' tiles of ti + 1): the M waves take
+    // one each, as their main phase is the longer one (measured), the S waves
+    // the rest
+    constexpr int NJ = 2 * NTRI, SJ = NJ - NOWN;
+    auto job = [&](int idx) {
       if (idx < NTRI) b_tile(idx, ti & 1);
-      else if (nxt && idx < 2 * NTRI) a_store(idx - NTRI, a_tile(idx - NTRI, (ti + 1) & 1));
+      else if (nxt && idx < NJ) a_store(idx - NTRI, a_tile(idx - NTRI, (ti + 1) & 1));
+    };
+    if (sRole) {
+#pragma unroll
+      for (int sl = 0; sl < (SJ + NOWN - 1) / NOWN; ++sl) {
+        const int idx = rw + NOWN * sl;
+        if (idx < SJ) job(idx);
+      }
+    } else {
+      job(SJ + rw);
     }
     if (need_n && nxt) q_dot_n((ti + 1) & 1);
   };
@@ -834,7 +845,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
     auto finish_out = [&](int tp, int Ltp) {
       const T* Vs = Vsb(tp & 1);
       const float* qnp = qnb(tp & 1);
-      float* go = a.o + (tok0 + (size_t)tp * TT) * E;
+      // the tile's Ltp output rows as a raw buffer: rows past them are dropped
+      const auto ro = buf_rsrc(a.o + (tok0 + (size_t)tp * TT) * E, Ltp * E * (int)sizeof(float));
       F vf[MB][NKS];
 #pragma unroll
       for (int b = 0; b < MB; ++b)
@@ -852,17 +864,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
         const int tau = 16 * r + lr;
-        float scale = 1.f;
         if (a.normalize) {
           float dn = 0.f;
           for (int c = 0; c <= r; ++c) dn += bpart[c * TT + tau];
-          scale = 1.f / (dn + w2[tau] * qnp[tau] + a.eps);
+          const float scale = 1.f / (dn + w2[tau] * qnp[tau] + a.eps);
+#pragma unroll
+          for (int b = 0; b < MB; ++b) oacc[b][r] *= scale;
         }
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           const int cb = rw + NOWN * b;
-          if ((MFULL || cb < ET) && tau < Ltp)
-            *reinterpret_cast<f32x4*>(go + (size_t)tau * E + 16 * cb + 4 * lg4) = oacc[b][r] * scale;
+          if (MFULL || cb < ET)
+            buf_store16(ro, (tau * E + 16 * cb + 4 * lg4) * (int)sizeof(float), oacc[b][r]);
         }
       }
       const int mt = tid - HT;

@@ -35,6 +35,14 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_o
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// 16-byte store at byte_off; a store at or past the buffer's end is dropped.
+// The whole offset goes in the per-lane operand: the scalar offset of a buffer
+// access is left out of its range check.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 x) {
+  const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+}
 
 template <typename T> struct MM;
 
