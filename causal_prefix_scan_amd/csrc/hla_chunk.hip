@@ -273,16 +273,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   // Tile staging: global -> registers -> LDS, row-major, 16-byte chunks (Q
   // chunks [0, QCH), K chunks [QCH, 2 QCH), V chunks [2 QCH, NCH)).  The
   // loads of tile t+1 are issued in the middle of tile t and written to LDS at
-  // the start of tile t+1, the S waves carrying Q and K and the M waves V.
-  // Without prefetch each tile is loaded and stored at its start by all
-  // threads (all loads issued before the first store).
+  // the start of tile t+1, the S waves carrying Q and K and the M waves V
+  // (tile 0 is loaded and stored by all threads).  The 4-wave output kernels
+  // keep two workgroups per CU with these registers (measured: B1 H32 T65536
+  // d64, outputs 0.39 -> 0.36 ms against staging each tile at its start).
   constexpr int QCH = TT * D / CH, VCH = TT * E / CH;
   constexpr int NCH = 2 * QCH + VCH;
   constexpr int HT = NTHR / 2;
   constexpr int NXS = (2 * QCH + HT - 1) / HT, NXM = (VCH + HT - 1) / HT, NXA = (NCH + NTHR - 1) / NTHR;
-  // prefetch through registers: always in the summary kernel; in the output
-  // kernel only with 8 waves (with 4 it would cost the second workgroup per CU)
-  constexpr bool PF = SUM || NW == 8;
   using QK = std::integral_constant<int, 0>;
   using VB = std::integral_constant<int, 2 * QCH>;
   using END = std::integral_constant<int, NCH>;
@@ -363,15 +361,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   // steps 0 and 1 of tile ti: stage the tile and its weights, then
   // A'^T = (K Q^T) o decay over all waves and q.n for the denominator
   int Lt_prev = -1;
-  // x: this role's prefetched part of the tile (summary kernel)
+  // x: this role's prefetched part of the tile
   auto tile_head = [&](int ti, int Lt, auto& x, auto s_wave) {
-    if constexpr (PF) {
-      store_role(x, Vsb(ti & 1), s_wave);
-    } else {
-      uint4 xt[NXA];
-      load_part(xt, ti, tid, QK{}, END{}, ALL{});
-      store_part(xt, tid, Qs, Ks, Vsb(ti & 1), QK{}, END{}, ALL{});
-    }
+    store_role(x, Vsb(ti & 1), s_wave);
     // wS for this tile; wM[ti & 1] was last written for tile ti - 2
     if ((ti < 2 || Lt != Lt_prev) && tid < TT) {
       wS[tid] = tid < Lt ? gpow(g, lgg, Lt - 1 - tid) : 0.f;
@@ -412,9 +404,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       store4<T>(AB + tau * L::LDT + 16 * c + 4 * lg4, val);
     }
     __syncthreads();
-    if constexpr (PF) {
-      if (ti + 1 < ntiles) load_role(x, ti + 1, s_wave);
-    }
+    if (ti + 1 < ntiles) load_role(x, ti + 1, s_wave);
   };
 
   // B^T = (P Q^T) o decay for tile ti (output kernel), the tiles shared by all
@@ -669,7 +659,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         }
       }
     };
-    uint4 xq[PF ? NXS : 1];
+    uint4 xq[NXS];
     if constexpr (L::PIPE) {
       finish_init();
       prologue();
@@ -719,7 +709,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         if constexpr (!SUM) __syncthreads();
       }
     } else {
-      if constexpr (PF) load_role(xq, 0, std::true_type{});
+      load_role(xq, 0, std::true_type{});
       finish_init();
 
       for (int ti = 0; ti < ntiles; ++ti) {
@@ -803,7 +793,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         }
       }
     }
-    uint4 xv[PF ? NXM : 1];
+    uint4 xv[NXM];
 
     // M[:, blocks] <- g^2L M + P^T diag(wM) V[:, blocks] for tile tp (its P^T, V
     // and wM are in the buffers of tp's parity); the P^T fragments are shared.
@@ -1029,7 +1019,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       }
       if constexpr (!SUM) finish_out(ntiles - 1, (Lspan - (ntiles - 1) * TT));
     } else {
-      if constexpr (PF) load_role(xv, 0, std::false_type{});
+      load_role(xv, 0, std::false_type{});
       finish_init();
       for (int ti = 0; ti < ntiles; ++ti) {
         const int t0 = ti * TT;
