@@ -1220,7 +1220,7 @@ hla_status hla3_scan(const hla_problem* p, const hla3_summary* inout, const hla3
   a.Sp = inout->S; a.Pp = inout->P; a.mp = inout->m; a.Q = inout->Q; a.V = inout->V;
   a.Z = inout->Z; a.z = inout->z; a.R = inout->R; a.r = inout->r;
   a.tR = t ? t->R : nullptr; a.tr = t ? t->r : nullptr;
-  a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 1;
+  a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 1; a.units = (int)units;
   return from_hip(hla::launch_r_scan(d, e, units, a, s));
 } catch (...) {
   return HLA_ERR_HIP;
@@ -1279,7 +1279,7 @@ hla_status hla3_fwd(const hla_problem* p, const void* q, const void* k, const vo
   a.Sp = F(w.S); a.Pp = F(w.P); a.mp = F(w.m); a.Q = F(w.Q); a.V = F(w.V); a.Z = F(w.Z); a.z = F(w.z);
   a.R = F(w.R); a.r = F(w.r);
   a.tR = fs ? fs->R : nullptr; a.tr = fs ? fs->r : nullptr;
-  a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 16;
+  a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 16; a.units = (int)units;
   if (hla_status x = from_hip(hla::launch_r_scan(d, e, units, a, t.s))) return x;
   // outputs: p, u, u_m from their moments' prefixes, then num and den from R, r
   if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, F(w.p), t.bf, F(w.S), false)) return x;

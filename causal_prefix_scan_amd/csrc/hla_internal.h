@@ -117,7 +117,7 @@ struct R3ScanArgs {
   float *R, *r;
   float *tR, *tr;        // inclusive totals [units, d, dv] and [units, d], or null
   const float* gamma;
-  int H, seg, nseg, ldm;
+  int H, seg, nseg, ldm, units;
 };
 struct Decode3Args {
   const void* q;

@@ -66,24 +66,66 @@ __global__ __launch_bounds__(256) void moments_scan_kernel(float* x, float* tota
 // of 16 rows), four waves.  On entry R, r hold the segment summaries; on exit
 // their exclusive prefixes (each step reads its segment's rows before writing
 // the prefix over them).  Sp, Pp, mp: the moments' exclusive prefixes; Q, V,
-// Z, z: the segments' summaries.  All products on fp32 MFMA, operands read
-// from global memory (L2-resident) with the helper tile product.
+// Z, z: the segments' summaries.  All products on fp32 MFMA.  Per segment:
+// the 16 rows of S_A go to registers in the A-operand layout; Q_B is staged
+// in LDS with 16-byte loads and the map's rows M = a^2 S_A Q_B + a V_B are
+// formed; then Z_B (in Q_B's buffer) and P_A are staged and the R rows take
+// a S_A Z_B + M P_A.  The staged matrices' rows are padded by 16 floats, which
+// makes the MFMA B-operand reads (four rows of 16 columns) hit distinct banks.
+// blockIdx.x is laid out so that the row blocks of one unit share blockIdx.x
+// mod 8 and so run on one XCD, whose L2 then serves the Q_B, Z_B and P_A they
+// all read (with consecutive numbering each of them fetched its own copy).
 template <int D, int E>
 __global__ __launch_bounds__(256) void r_scan_kernel(R3ScanArgs a) {
-  constexpr int LS = D + 4;
-  __shared__ float Mk[16 * LS];      // the segment map's 16 rows
+  constexpr int NT = 256, LQ = D + 16, LZ = E + 16, LS = D + 4;
+  constexpr int BQ = (D * LQ > D * LZ) ? D * LQ : D * LZ;
+  __shared__ __attribute__((aligned(16))) float bQZ[BQ];      // Q_B, then Z_B
+  __shared__ __attribute__((aligned(16))) float bP[D * LZ];   // P_A
+  __shared__ float Mk[16 * LS];                                // the map's 16 rows
   __shared__ float rrun[16];
-  const int nrb = D / 16;
-  const int unit = blockIdx.x / nrb, rb = blockIdx.x - unit * nrb, r0 = 16 * rb;
+  constexpr int nrb = D / 16;
+  const int bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
+  const int unit = xcd + 8 * (qb / nrb), rb = qb % nrb, r0 = 16 * rb;
+  if (unit >= a.units) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float a1 = gpow(g, log2f(g), a.seg), a2 = a1 * a1, a3 = a2 * a1;
   constexpr int NCE = (E / 16 + 3) / 4;   // column blocks of R per wave
+  constexpr int NCD = (D / 16 + 3) / 4;   // column blocks of the map per wave
+  constexpr int KD = D / 4;               // K steps of a product over D
   f32x4 Rrun[NCE];
 #pragma unroll
   for (int i = 0; i < NCE; ++i) Rrun[i] = zero4();
   if (tid < 16) rrun[tid] = 0.f;
   const int row = tid >> 4, part = tid & 15;   // the r update: 16 lanes per row
+  // a row-major [D][W] fp32 matrix: loads to registers (16 bytes per thread
+  // and load), then stores to LDS with row stride LW
+  constexpr int PQ = (D * D / 4 + NT - 1) / NT, PZ = (D * E / 4 + NT - 1) / NT;
+  auto load_mat = [&](const float* src, f32x4* x, auto Wc) {
+    constexpr int W = decltype(Wc)::value, N4 = D * W / 4, PER = (N4 + NT - 1) / NT;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + NT * u;
+      if (i < N4) x[u] = reinterpret_cast<const f32x4*>(src)[i];
+    }
+  };
+  auto store_mat = [&](const f32x4* x, float* dst, auto Wc, auto LWc) {
+    constexpr int W = decltype(Wc)::value, LW = decltype(LWc)::value;
+    constexpr int N4 = D * W / 4, PER = (N4 + NT - 1) / NT;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + NT * u;
+      if (i < N4) {
+        const int rr = i / (W / 4), c4 = i - rr * (W / 4);
+        *reinterpret_cast<f32x4*>(dst + rr * LW + 4 * c4) = x[u];
+      }
+    }
+  };
+  using DC = std::integral_constant<int, D>;
+  using EC = std::integral_constant<int, E>;
+  using LQC = std::integral_constant<int, LQ>;
+  using LZC = std::integral_constant<int, LZ>;
+  constexpr int NRU = D / 16;   // r update: products per lane
   for (int s = 0; s < a.nseg; ++s) {
     const size_t us = (size_t)unit * a.nseg + s;
     const float* SA = a.Sp + us * D * D + (size_t)r0 * D;     // 16 rows of S_A
@@ -95,36 +137,81 @@ __global__ __launch_bounds__(256) void r_scan_kernel(R3ScanArgs a) {
     const float* zB = a.z + us * D * a.ldm;
     float* RB = a.R + us * D * E + (size_t)r0 * E;
     float* rB = a.r + us * D * a.ldm + (size_t)r0 * a.ldm;
-    // the map's rows: M = a^2 S_A Q_B + a V_B
-    for (int cb = wave; cb < D / 16; cb += 4) {
-      f32x4 acc = gemm_f32_tile<D>(SA, D, QB, D, 0, 16 * cb, lane, zero4());
+    // every global read of the segment, issued together: S_A rows as the A
+    // operand (lane: row lr, K slots 4 j + lg), Q_B, Z_B, P_A, V_B's and R_B's
+    // elements of this lane, the r update's operands
+    float sa[KD];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 4 * lg + j, cc = 16 * cb + lr;
-        Mk[rr * LS + cc] = a2 * acc[j] + a1 * VB[(size_t)rr * D + cc];
+    for (int j = 0; j < KD; ++j) sa[j] = SA[(size_t)lr * D + 4 * j + lg];
+    f32x4 xq[PQ], xz[PZ], xp[PZ];
+    load_mat(QB, xq, DC{});
+    load_mat(ZB, xz, EC{});
+    load_mat(PA, xp, EC{});
+    f32x4 vb[NCD], rb4[NCE];
+#pragma unroll
+    for (int i = 0; i < NCD; ++i) {
+      const int cb = wave + 4 * i;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) vb[i][jj] = cb < D / 16 ? VB[(size_t)(4 * lg + jj) * D + 16 * cb + lr] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NCE; ++i) {
+      const int ce = wave + 4 * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rb4[i][j] = ce < E / 16 ? RB[(size_t)(4 * lg + j) * E + 16 * ce + lr] : 0.f;
+    }
+    float su[NRU], zu[NRU], mu[NRU];
+#pragma unroll
+    for (int i = 0; i < NRU; ++i) {
+      const int c = part + 16 * i;
+      su[i] = SA[(size_t)row * D + c];
+      zu[i] = zB[(size_t)c * a.ldm];
+      mu[i] = mA[(size_t)c * a.ldm];
+    }
+    const float rbv = part == 0 ? rB[(size_t)row * a.ldm] : 0.f;
+    store_mat(xq, bQZ, DC{}, LQC{});
+    __syncthreads();
+    // the map's rows: M = a^2 S_A Q_B + a V_B
+#pragma unroll
+    for (int i = 0; i < NCD; ++i) {
+      const int cb = wave + 4 * i;
+      if (cb < D / 16) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < KD; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], bQZ[(4 * j + lg) * LQ + 16 * cb + lr], acc, 0, 0, 0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Mk[(4 * lg + jj) * LS + 16 * cb + lr] = a2 * acc[jj] + a1 * vb[i][jj];
       }
     }
+    __syncthreads();
+    store_mat(xz, bQZ, EC{}, LZC{});
+    store_mat(xp, bP, EC{}, LZC{});
     __syncthreads();
     // R rows: a^3 R_A + R_B + a S_A Z_B + M P_A; the prefix is R_A
 #pragma unroll
     for (int i = 0; i < NCE; ++i) {
       const int ce = wave + 4 * i;
       if (ce < E / 16) {
-        f32x4 rb4;
+        f32x4 t1 = zero4(), t2 = zero4();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rb4[j] = RB[(size_t)(4 * lg + j) * E + 16 * ce + lr];
-        f32x4 t1 = gemm_f32_tile<D>(SA, D, ZB, E, 0, 16 * ce, lane, zero4());
-        f32x4 t2 = gemm_f32_tile<D>(Mk, LS, PA, E, 0, 16 * ce, lane, zero4());
+        for (int j = 0; j < KD; ++j) {
+          const int kr = 4 * j + lg;
+          t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], bQZ[kr * LZ + 16 * ce + lr], t1, 0, 0, 0);
+          t2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Mk[lr * LS + kr], bP[kr * LZ + 16 * ce + lr], t2, 0, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) RB[(size_t)(4 * lg + j) * E + 16 * ce + lr] = Rrun[i][j];
-        Rrun[i] = Rrun[i] * a3 + rb4 + t1 * a1 + t2;
+        Rrun[i] = Rrun[i] * a3 + rb4[i] + t1 * a1 + t2;
       }
     }
     // r rows: a^3 r_A + r_B + a S_A z_B + M m_A
     float sz = 0.f, mm = 0.f;
-    for (int c = part; c < D; c += 16) {
-      sz += SA[(size_t)row * D + c] * zB[(size_t)c * a.ldm];
-      mm += Mk[row * LS + c] * mA[(size_t)c * a.ldm];
+#pragma unroll
+    for (int i = 0; i < NRU; ++i) {
+      const int c = part + 16 * i;
+      sz += su[i] * zu[i];
+      mm += Mk[row * LS + c] * mu[i];
     }
 #pragma unroll
     for (int off = 1; off < 16; off *= 2) {
@@ -132,7 +219,6 @@ __global__ __launch_bounds__(256) void r_scan_kernel(R3ScanArgs a) {
       mm += __shfl_xor(mm, off, 64);
     }
     if (part == 0) {
-      const float rbv = rB[(size_t)row * a.ldm];
       rB[(size_t)row * a.ldm] = rrun[row];
       rrun[row] = a3 * rrun[row] + rbv + a1 * sz + mm;
     }
@@ -334,7 +420,9 @@ hipError_t launch_moments_scan(float* x, float* total, const float* gamma, int H
 }
 
 hipError_t launch_r_scan(int d, int dv, int units, const R3ScanArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(units * (d / 16)));
+  // units rounded up to a multiple of 8 (the XCD-aware numbering); the extra
+  // workgroups return at once
+  const dim3 grid((unsigned)((units + 7) / 8 * 8 * (d / 16)));
 #define HLA_CASE(D, E) \
   if (d == D && dv == E) { hipLaunchKernelGGL((r_scan_kernel<D, E>), grid, dim3(256), 0, s, a); return hipGetLastError(); }
   HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(32, 16) HLA_CASE(32, 32) HLA_CASE(32, 64)
