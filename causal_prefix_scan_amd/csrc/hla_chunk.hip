@@ -19,6 +19,9 @@
 //     M <- g^(2Lt) M + sum_j g^(2(Lt-1-j)) p_j v_j^T,  n likewise with v = 1.
 // The summary kernel also accumulates C and m and, at the end of the
 // segment, converts back to the method's summary: G = S C - M, h = S m - n.
+// As it needs C, m, M and n only there, it weights each token by its decay
+// to the segment end (g^(L-1-j) for C and m, g^(2(L-1-j)) for M and n) and
+// never rescales those running sums; S is rescaled per tile as above.
 // The output kernel starts from the segment's exclusive prefix
 // (S_P, C_P, m_P, G_P, h_P) with M = S_P C_P - G_P and n = S_P m_P - h_P.
 //
