@@ -175,6 +175,12 @@ def bench_fwd(args, torch, np):
     st = hla._state_struct(summ)
     ws_bytes = L.hla_scan_workspace_bytes(ctypes.byref(p))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    # the shapes that have it (bf16, d = dv = 128) take hla_fwd's segment-local
+    # p path: the summary kernel also writes p = S q, the outputs come from it
+    p_bytes = L.hla_fwd_p_bytes(ctypes.byref(p))
+    plocal = torch.empty(max(p_bytes, 16), dtype=torch.uint8, device="cuda") if p_bytes else None
+    name_s = "hla_fwd_chunk_summaries_p" if p_bytes else "hla_fwd_chunk_summaries"
+    name_o = "hla_fwd_output_from_p" if p_bytes else "hla_fwd_output"
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -182,14 +188,22 @@ def bench_fwd(args, torch, np):
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
+        if p_bytes:
+            r1 = L.hla_fwd_chunk_summaries_p(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st),
+                                             ptr(plocal), sp)
+        else:
+            r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
         if ev:
             ev[1].record(stream)
         r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
         if ev:
             ev[2].record(stream)
-        r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
-                              ptr(den), None, ctypes.c_size_t(0), sp)
+        if p_bytes:
+            r3 = L.hla_fwd_output_from_p(ctypes.byref(p), ptr(q), ptr(v), ptr(plocal), ctypes.byref(st),
+                                         ptr(o), ptr(den), sp)
+        else:
+            r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
+                                  ptr(den), None, ctypes.c_size_t(0), sp)
         if ev:
             ev[3].record(stream)
         if r1 or r2 or r3:
@@ -217,14 +231,16 @@ def bench_fwd(args, torch, np):
     summ_bytes = U * n * (d * d + 2 * d * dv + 2 * d) * 4
     prefix_bytes = summ_bytes                                    # prefixes the output kernel reads
     io_bytes = tokens * ((2 * d + dv) * es)
+    # the segment-local p: written by the summaries, read by the outputs in
+    # place of k (bf16, 64-token tiles)
     kernels = {
-        "hla_fwd_chunk_summaries": dict(ms=sum(k1) / len(k1), bytes=io_bytes + summ_bytes),
+        name_s: dict(ms=sum(k1) / len(k1), bytes=io_bytes + summ_bytes + p_bytes),
         "hla_scan": dict(ms=sum(k2) / len(k2), bytes=None),
-        "hla_fwd_output": dict(ms=sum(k3) / len(k3),
-                               bytes=io_bytes + prefix_bytes + tokens * dv * 4
-                               + (tokens * 4 if den is not None else 0)),
+        name_o: dict(ms=sum(k3) / len(k3),
+                     bytes=io_bytes - (tokens * d * es if p_bytes else 0) + p_bytes + prefix_bytes
+                     + tokens * dv * 4 + (tokens * 4 if den is not None else 0)),
     }
-    dom = max(("hla_fwd_chunk_summaries", "hla_fwd_output"), key=lambda kname: kernels[kname]["ms"])
+    dom = max((name_s, name_o), key=lambda kname: kernels[kname]["ms"])
     kd = kernels[dom]
     achieved = kd["bytes"] / (kd["ms"] / 1e3) / 1e9
     f_tok = credited_flops_per_token(cfg["credit_chunk"], d, dv)
@@ -240,10 +256,10 @@ def bench_fwd(args, torch, np):
         "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "dv": dv,
                    "chunk": chunk, "span_chunks": R, "decay": cfg["decay"],
                    "normalize": cfg["normalize"],
-                   "path": (f"hla_fwd's plan: hla_fwd_chunk_summaries over spans of {R} chunk(s) "
+                   "path": (f"hla_fwd's plan: {name_s} over spans of {R} chunk(s) "
                             f"({span} tokens; each workgroup forms its chunks' summaries and "
                             f"combines them in order), hla_scan over the {n} span totals per "
-                            f"(b, h), hla_fwd_output walking each span from its prefix")},
+                            f"(b, h), {name_o} walking each span from its prefix")},
         "mfma_credited": {"flops_per_token": round(f_tok), "credit_chunk": cfg["credit_chunk"],
                           "tflops": round(value * f_tok / 1e12, 1),
                           "peak_tflops": BF16_PEAK_TFLOPS,

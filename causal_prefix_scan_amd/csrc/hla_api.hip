@@ -129,6 +129,7 @@ ChunkArgs chunk_args(const hla_problem* p, const void* q, const void* k, const v
   a.normalize = p->normalize; a.eps = p->eps;
   a.S = st->S; a.C = st->C; a.m = st->m; a.G = st->G; a.h = st->h;
   a.o = o; a.den = den;
+  a.pl = nullptr;
   return a;
 }
 
@@ -175,6 +176,28 @@ int64_t fwd_span_chunks(const hla_problem* p) {
   int64_t R = 1;
   while (fits(R * 2) && z.units * (z.n / (R * 2)) >= want_wg) R *= 2;
   return R;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// One segment's p blocks (64-token tiles of d bf16 rows) stay within the
+// 32-bit byte range of the kernels' buffer addressing.
+bool plocal_fits(int64_t chunk, int d) { return (chunk + 63) / 64 * 64 * (int64_t)d * 2 <= 2147483647; }
+
+// Bytes of the segment-local p over hla_fwd's spans (0 for shapes without
+// the path that uses it).
+size_t fwd_span_p_bytes(const hla_problem* p) {
+  if (!hla::outp_supported(p->in_dtype, p->d, p->dv)) return 0;
+  const int64_t span = (int64_t)p->chunk * fwd_span_chunks(p);
+  if (!plocal_fits(span, p->d)) return 0;
+  return hla::outp_plocal_bytes(sizes_of(p).units, p->T, (int)span, p->d);
+}
+
+// Bytes of a workspace of workspace_bytes that hla_fwd uses: the summaries
+// and the scan's scratch, plus the segment-local p when it fits.
+size_t fwd_used_bytes(const hla_problem* p, size_t workspace_bytes) {
+  const size_t base = hla_fwd_workspace_bytes(p), pb = fwd_span_p_bytes(p);
+  return (pb && workspace_bytes >= align256(base) + pb) ? align256(base) + pb : base;
 }
 
 }  // namespace
@@ -347,6 +370,73 @@ size_t hla_fwd_workspace_bytes(const hla_problem* p) {
   return summ + scan_ws_bytes(p);
 }
 
+size_t hla_fwd_p_workspace_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  const size_t base = hla_fwd_workspace_bytes(p), pb = fwd_span_p_bytes(p);
+  return pb ? align256(base) + pb : base;
+}
+
+size_t hla_fwd_p_bytes(const hla_problem* p) {
+  if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
+  if (!hla::outp_supported(p->in_dtype, p->d, p->dv) || !plocal_fits(p->chunk, p->d)) return 0;
+  return hla::outp_plocal_bytes(sizes_of(p).units, p->T, p->chunk, p->d);
+}
+
+hla_status hla_fwd_chunk_summaries_p(const hla_problem* p, const void* q, const void* k,
+                                     const void* v, const hla_state* out, void* plocal,
+                                     void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (!hla::outp_supported(p->in_dtype, p->d, p->dv)) return HLA_ERR_UNSUPPORTED;
+  if (!plocal_fits(p->chunk, p->d)) return HLA_ERR_BAD_VALUE;
+  if (hla_status e = check_qkv(q, k, v)) return e;
+  if (!plocal) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(plocal)) return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  const size_t pb = hla_fwd_p_bytes(p);
+  const void* ins[4] = {q, k, v, plocal};
+  const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, pb};
+  for (int j = 0; j < 3; ++j)
+    if (overlap(plocal, pb, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  if (hla_status e = check_state(out, true, z.units * z.n, z, ins, inb, 4)) return e;
+  if (hla_status e = device_ready()) return e;
+  ChunkArgs a = chunk_args(p, q, k, v, out, nullptr, nullptr);
+  a.pl = plocal;
+  return from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a,
+                                              static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_fwd_output_from_p(const hla_problem* p, const void* q, const void* v,
+                                 const void* plocal, const hla_state* prefixes, float* o,
+                                 float* den, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  if (!hla::outp_supported(p->in_dtype, p->d, p->dv)) return HLA_ERR_UNSUPPORTED;
+  if (!plocal_fits(p->chunk, p->d)) return HLA_ERR_BAD_VALUE;
+  if (!q || !v || !plocal || !o) return HLA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(v) || !aligned16(plocal) || !aligned16(o) || (den && !aligned16(den)))
+    return HLA_ERR_MISALIGNED;
+  const Sizes z = sizes_of(p);
+  if (hla_status e = check_state(prefixes, true, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  const void* ins[8] = {q, v, plocal, prefixes->S, prefixes->C, prefixes->m, prefixes->G, prefixes->h};
+  const size_t inb[8] = {z.qk_bytes, z.v_bytes, hla_fwd_p_bytes(p),
+                         z.units * z.n * z.S * 4, z.units * z.n * z.C * 4, z.units * z.n * z.m * 4,
+                         z.units * z.n * z.C * 4, z.units * z.n * z.m * 4};
+  for (int j = 0; j < 8; ++j) {
+    if (overlap(o, z.o_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+    if (den && overlap(den, z.den_bytes, ins[j], inb[j])) return HLA_ERR_ALIASING;
+  }
+  if (den && overlap(o, z.o_bytes, den, z.den_bytes)) return HLA_ERR_ALIASING;
+  if (hla_status e = device_ready()) return e;
+  ChunkArgs a = chunk_args(p, q, nullptr, v, prefixes, o, den);
+  a.pl = const_cast<void*>(plocal);
+  return from_hip(hla::launch_outputs_from_p((int)z.units, a, static_cast<hipStream_t>(stream)));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
 hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const void* v, float* o,
                    float* den, const hla_state* final_state, void* workspace,
                    size_t workspace_bytes, void* stream) try {
@@ -355,7 +445,7 @@ hla_status hla_fwd(const hla_problem* p, const void* q, const void* k, const voi
     return e;
   if (empty_problem(p)) return HLA_OK;
   if (hla_status e = device_ready()) return e;
-  return hla::fwd_enqueue(p, q, k, v, o, den, final_state, workspace, stream);
+  return hla::fwd_enqueue(p, q, k, v, o, den, final_state, workspace, workspace_bytes, stream);
 } catch (...) {
   return HLA_ERR_HIP;
 }
@@ -376,12 +466,14 @@ hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, cons
   if (!o) return HLA_ERR_NULL_POINTER;
   if (!aligned16(o) || (den && !aligned16(den))) return HLA_ERR_MISALIGNED;
   const Sizes z = sizes_of(p);
-  const size_t need = check_ws ? hla_fwd_workspace_bytes(p) : 0;
-  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0) {
+  const size_t minimum = check_ws ? hla_fwd_workspace_bytes(p) : 0;
+  if (workspace_bytes < minimum) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (minimum > 0) {
     if (!workspace) return HLA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
   }
+  // the part of the workspace the chosen plan uses
+  const size_t need = check_ws ? fwd_used_bytes(p, workspace_bytes) : 0;
   const void* ins[4] = {q, k, v, workspace};
   const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
   for (int j = 0; j < 4; ++j) {
@@ -399,11 +491,12 @@ hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, cons
 }
 
 // Enqueues the whole forward on `stream` with the summaries and the scan's
-// scratch in `workspace` (at least hla_fwd_workspace_bytes(p) bytes; the
+// scratch in `workspace` (workspace_bytes >= hla_fwd_workspace_bytes(p); the
+// segment-local p path when it also holds hla_fwd_p_workspace_bytes(p); the
 // arguments have passed fwd_validate and the problem is not empty).
 hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const void* v,
                        float* o, float* den, const hla_state* final_state, void* workspace,
-                       void* stream) {
+                       size_t workspace_bytes, void* stream) {
   // spans of R chunks: summaries of the spans, the scan over them, outputs
   hla_problem ps = *p;
   ps.chunk = (int32_t)(p->chunk * fwd_span_chunks(p));
@@ -415,11 +508,21 @@ hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const
   sm.S = w; sm.C = sm.S + cnt * z.S; sm.m = sm.C + cnt * z.C; sm.G = sm.m + cnt * z.m;
   sm.h = sm.G + cnt * z.C;
   void* scan_ws = sm.h + cnt * z.m;
-  const ChunkArgs a1 = chunk_args(&ps, q, k, v, &sm, nullptr, nullptr);
+  // the segment-local p after the summaries and the scan's scratch, when the
+  // workspace holds it: the output kernel then carries no S recurrence
+  void* plocal = fwd_used_bytes(p, workspace_bytes) > hla_fwd_workspace_bytes(p)
+                     ? static_cast<char*>(workspace) + align256(hla_fwd_workspace_bytes(p))
+                     : nullptr;
+  ChunkArgs a1 = chunk_args(&ps, q, k, v, &sm, nullptr, nullptr);
+  a1.pl = plocal;
   if (hla_status e = from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
     return e;
   if (hla_status e = do_scan(&ps, &sm, final_state, scan_ws, s)) return e;
-  const ChunkArgs a3 = chunk_args(&ps, q, k, v, &sm, o, den);
+  ChunkArgs a3 = chunk_args(&ps, q, k, v, &sm, o, den);
+  if (plocal) {
+    a3.pl = plocal;
+    return from_hip(hla::launch_outputs_from_p((int)z.units, a3, s));
+  }
   return from_hip(hla::launch_chunk_outputs(p->in_dtype, p->d, p->dv, (int)z.units, a3, s));
 }
 
@@ -964,7 +1067,9 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
     void* dp16 = wb + nw.dp16;
     hla_problem pf = *p;
     pf.normalize = 0;
-    if (hla_status r = hla::fwd_enqueue(&pf, q, k, v, num, den, nullptr, wb + nw.fwd, stream)) return r;
+    if (hla_status r = hla::fwd_enqueue(&pf, q, k, v, num, den, nullptr, wb + nw.fwd,
+                                        hla_fwd_workspace_bytes(&pf), stream))
+      return r;
     if (hla_status r = from_hip(hla::launch_norm_grad(bf, num, den, dout, p->eps, tok, e, gnum, gden,
                                                       one, s)))
       return r;

@@ -133,6 +133,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
   constexpr bool DEFER = !SUM && NW == 8;
   // every block index is in range when the blocks divide evenly over a role
   constexpr bool SFULL = DT % NOWN == 0, MFULL = ET % NOWN == 0;
+  // the summary kernel at bf16, d = dv = 128 can also write the segment-local p
+  constexpr bool WPK = SUM && sizeof(T) == 2 && D == 128 && E == 128;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   T* Qs = reinterpret_cast<T*>(smem + L::Qs);
@@ -600,6 +602,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
         }
       }
       mid();
+      // the segment-local p of this tile to global memory, when asked: per
+      // tile, (column block, row block) 16x16 fragments of 512 contiguous
+      // bytes in the accumulator's lane order (lane l: tokens 16 r + 4 (l >> 4)
+      // + [0, 4) of column 16 cb + (l & 15)), so each store is one coalesced run
+      T* plt = nullptr;
+      if constexpr (WPK) {
+        if (a.pl) plt = reinterpret_cast<T*>(a.pl) + (sidx * (size_t)ntiles + (size_t)ti) * (size_t)(D * TT);
+      }
       float ncol[SB];
 #pragma unroll
       for (int b = 0; b < SB; ++b) ncol[b] = 0.f;
@@ -622,6 +632,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
           if (SFULL || cb < DT) {
             // P^T[d][tau], d = 16 cb + lr, tau = 16 r + 4 lg4 + j
             store4<T>(PsT + (16 * cb + lr) * L::LDT + 16 * r + 4 * lg4, pacc[b][r]);
+            if constexpr (WPK) {
+              if (plt) store4<T>(plt + ((cb * TR + r) * 64 + lane) * 4, pacc[b][r]);
+            }
             ncol[b] += pacc[b][r][0] * wm[0] + pacc[b][r][1] * wm[1] + pacc[b][r][2] * wm[2] +
                        pacc[b][r][3] * wm[3];
           }

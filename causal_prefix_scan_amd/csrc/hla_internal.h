@@ -23,6 +23,10 @@ struct ChunkArgs {
   float *S, *C, *m, *G, *h;
   float* o;    // [units, T, dv]
   float* den;  // [units, T] or nullptr
+  // the segment-local p_t = S_t q_t (S from zero at the segment start), bf16,
+  // [units, nspan, tiles, d, 64] (token-contiguous 64-token tiles), written
+  // by the bf16 d = dv = 128 summary kernel when set; nullptr otherwise
+  void* pl;
 };
 
 // One tree scan over slots (used for the run totals of the two-level scan).
@@ -63,6 +67,12 @@ struct DecodeArgs {
 // Returns hipSuccess or the launch error.
 hipError_t launch_chunk_summaries(int dtype, int d, int dv, int units, const ChunkArgs& a,
                                   hipStream_t s);
+// Outputs from the segment-local p (ChunkArgs::pl) instead of the S
+// recurrence: bf16 inputs with d = dv = 128 only.
+bool outp_supported(int dtype, int d, int dv);
+// Bytes of the segment-local p for `units` units of T tokens in segments of `chunk`.
+size_t outp_plocal_bytes(int64_t units, int64_t T, int chunk, int d);
+hipError_t launch_outputs_from_p(int units, const ChunkArgs& a, hipStream_t s);
 hipError_t launch_chunk_outputs(int dtype, int d, int dv, int units, const ChunkArgs& a,
                                 hipStream_t s);
 bool chunk_shape_supported(int dtype, int d, int dv);
@@ -147,14 +157,16 @@ hipError_t launch_decode3(int dtype, int d, int dv, int units, const Decode3Args
 // hla_fwd in two parts (both host code, in the ABI layer): the argument
 // checks (with check_ws, also those of a caller's workspace of
 // workspace_bytes bytes), and the launches of the whole forward with the
-// summaries and the scan's scratch in `workspace` (hla_fwd_workspace_bytes
-// bytes; called only for a validated, non-empty problem).
+// summaries and the scan's scratch in `workspace` (workspace_bytes >=
+// hla_fwd_workspace_bytes; with at least hla_fwd_p_workspace_bytes, and a
+// shape that has it, the segment-local p path; called only for a validated,
+// non-empty problem).
 hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, const void* v,
                         float* o, float* den, const hla_state* final_state, const void* workspace,
                         size_t workspace_bytes, bool check_ws);
 hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const void* v,
                        float* o, float* den, const hla_state* final_state, void* workspace,
-                       void* stream);
+                       size_t workspace_bytes, void* stream);
 
 // First-order decayed sum y_t = sum_{s<=t} lam^(t-s) (a_t.b_s) c_s over the
 // walk order (tokens 0..T-1, or T-1..0 when reverse), the building block of

@@ -69,7 +69,7 @@ hla_status hla_fwd_noalloc(const hla_problem* p, const void* q, const void* k, c
   }
   void* ws = nullptr;
   if (hla_status e = scratch_on_current_device(&ws)) return e;
-  return hla::fwd_enqueue(p, q, k, v, o, den, final_state, ws, stream);
+  return hla::fwd_enqueue(p, q, k, v, o, den, final_state, ws, need, stream);
 } catch (...) {
   return HLA_ERR_HIP;
 }

@@ -26,6 +26,8 @@ EXPORTS = (
     "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
     "hla_fwd_span_chunks",
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
+    "hla_fwd_p_bytes", "hla_fwd_chunk_summaries_p", "hla_fwd_output_from_p",
+    "hla_fwd_p_workspace_bytes",
     "hla_fwd", "hla_fwd_noalloc_max_workspace_bytes", "hla_fwd_noalloc",
     "hla_decode_step", "hla_unmasked_chunk_summaries", "hla_unmasked_scan",
     "hla_unmasked_output", "hla_unmasked_fwd_workspace_bytes", "hla_unmasked_fwd",
@@ -95,6 +97,10 @@ def lib():
     L.hla_fwd_output_workspace_bytes.argtypes, L.hla_fwd_output_workspace_bytes.restype = [pp], sz
     L.hla_fwd_output.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp, sz, vp]
     L.hla_fwd_workspace_bytes.argtypes, L.hla_fwd_workspace_bytes.restype = [pp], sz
+    L.hla_fwd_p_bytes.argtypes, L.hla_fwd_p_bytes.restype = [pp], sz
+    L.hla_fwd_p_workspace_bytes.argtypes, L.hla_fwd_p_workspace_bytes.restype = [pp], sz
+    L.hla_fwd_chunk_summaries_p.argtypes = [pp, vp, vp, vp, ps, vp, vp]
+    L.hla_fwd_output_from_p.argtypes = [pp, vp, vp, vp, ps, vp, vp, vp]
     L.hla_fwd.argtypes = [pp, vp, vp, vp, vp, vp, ps, vp, sz, vp]
     L.hla_fwd_noalloc_max_workspace_bytes.argtypes = []
     L.hla_fwd_noalloc_max_workspace_bytes.restype = sz
@@ -125,6 +131,7 @@ def lib():
     for name in ("hla3_chunk_summaries", "hla3_scan", "hla3_fwd", "hla3_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     for name in ("hla_fwd_chunk_summaries", "hla_scan", "hla_scan_runs", "hla_fwd_output",
+                 "hla_fwd_chunk_summaries_p", "hla_fwd_output_from_p",
                  "hla_fwd", "hla_fwd_noalloc", "hla_decode_step", "hla_unmasked_fwd", "hla_unmasked_chunk_summaries",
                  "hla_unmasked_scan", "hla_unmasked_output", "hla_unmasked_decode_step",
                  "hla_ahla_chunk_summaries", "hla_ahla_scan", "hla_ahla_output", "hla_ahla_fwd",
@@ -279,11 +286,52 @@ def fwd_output(q, k, v, prefixes, chunk, gamma=None, normalize=False, eps=0.0, w
     return o, den
 
 
-def fwd_workspace(q, v, chunk, gamma=None):
+def fwd_workspace(q, v, chunk, gamma=None, with_p=True):
+    """hla_fwd's workspace: with room for the segment-local p where the shape
+    has that path (with_p), else the minimum (summaries and scan scratch)."""
     torch = _torch()
     p = make_problem(q, v, chunk, gamma)
-    nbytes = lib().hla_fwd_workspace_bytes(ctypes.byref(p))
+    f = lib().hla_fwd_p_workspace_bytes if with_p else lib().hla_fwd_workspace_bytes
+    nbytes = f(ctypes.byref(p))
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+
+
+def p_bytes(q, v, chunk):
+    """Bytes of the segment-local p (hla_fwd_p_bytes; 0 without that path)."""
+    return lib().hla_fwd_p_bytes(ctypes.byref(make_problem(q, v, chunk)))
+
+
+def fwd_chunk_summaries_p(q, k, v, chunk, gamma=None, out=None, plocal=None):
+    """Segment summaries and the segment-local p: (summaries dict, plocal bf16 tensor)."""
+    torch = _torch()
+    _need_cuda(q, k, v, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma)
+    if out is None:
+        out = alloc_state((B, H, T // chunk), d, v.shape[3], q.device)
+    if plocal is None:
+        plocal = torch.empty(max(p_bytes(q, v, chunk), 16) // 2, dtype=torch.bfloat16, device=q.device)
+    st = _state_struct(out)
+    _check(lib().hla_fwd_chunk_summaries_p(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                           ctypes.byref(st), _ptr(plocal), _stream()),
+           "hla_fwd_chunk_summaries_p")
+    return out, plocal
+
+
+def fwd_output_from_p(q, v, plocal, prefixes, chunk, gamma=None, normalize=False, eps=0.0,
+                      want_den=False):
+    """Outputs from the exclusive prefixes and the segment-local p: (o, den or None)."""
+    torch = _torch()
+    _need_cuda(q, v, plocal, gamma)
+    B, H, T, d = q.shape
+    p = make_problem(q, v, chunk, gamma, normalize, eps)
+    o = torch.empty(B, H, T, v.shape[3], dtype=torch.float32, device=q.device)
+    den = torch.empty(B, H, T, dtype=torch.float32, device=q.device) if want_den else None
+    st = _state_struct(prefixes)
+    _check(lib().hla_fwd_output_from_p(ctypes.byref(p), _ptr(q), _ptr(v), _ptr(plocal),
+                                       ctypes.byref(st), _ptr(o), _ptr(den), _stream()),
+           "hla_fwd_output_from_p")
+    return o, den
 
 
 def fwd(q, k, v, chunk, gamma=None, normalize=False, eps=0.0, want_den=False, want_state=False,

@@ -185,6 +185,48 @@ hla_status hla_fwd_output(const hla_problem* p, const void* q, const void* k, co
 /* Bytes of scratch hla_fwd needs: the n summaries plus hla_scan's scratch. */
 size_t hla_fwd_workspace_bytes(const hla_problem* p);
 
+/* Bytes of the segment-local p for segments of p->chunk tokens: bf16,
+ * [B, H, n, ceil(chunk / 64), d / 16, 4, 64, 4]: per 64-token tile, for
+ * column block cb (columns 16 cb .. 16 cb + 15) and row block r (tokens
+ * 16 r .. 16 r + 15 of the tile), 64 groups of 4 values, group l holding
+ * tokens 16 r + 4 (l / 16) + [0, 4) of column 16 cb + (l % 16) (the MFMA
+ * accumulator's lane order); tokens past the segment end are zero.  Only
+ * bf16 inputs with d = dv = 128 have this path: 0 otherwise, and 0 for an
+ * invalid or empty problem.  Host-only. */
+size_t hla_fwd_p_bytes(const hla_problem* p);
+
+/*
+ * hla_fwd_chunk_summaries that also writes the segment-local p (method
+ * section 1: p_t = S_t q_t with the state S_t of method section 4 formed
+ * from zero at each segment's start), which the summary kernel forms for
+ * every token anyway, to `plocal` (hla_fwd_p_bytes(p) bytes, 16-byte
+ * aligned, no overlap with q, k, v or `out`).  bf16 inputs with d = dv = 128
+ * only (HLA_ERR_UNSUPPORTED otherwise).
+ */
+hla_status hla_fwd_chunk_summaries_p(const hla_problem* p, const void* q, const void* k,
+                                     const void* v, const hla_state* out, void* plocal,
+                                     void* stream);
+
+/*
+ * hla_fwd_output from the segment-local p (as hla_fwd_chunk_summaries_p
+ * writes it) instead of k: with the segment's exclusive prefix S_P the state
+ * at position j of the segment is g^(j+1) S_P + S^loc_j (decay per key
+ * contribution 2), so p_j = g^(j+1) S_P q_j + p^loc_j and the outputs follow
+ * without the S recurrence.  Same prefixes, outputs and errors as
+ * hla_fwd_output (up to rounding); bf16 inputs with d = dv = 128 only.
+ */
+hla_status hla_fwd_output_from_p(const hla_problem* p, const void* q, const void* v,
+                                 const void* plocal, const hla_state* prefixes, float* o,
+                                 float* den, void* stream);
+
+/* Bytes of workspace with which hla_fwd also keeps the segment-local p of
+ * its spans and computes the outputs from it (hla_fwd_chunk_summaries_p +
+ * hla_scan + hla_fwd_output_from_p at chunk' = R * chunk): the summaries and
+ * the scan's scratch, rounded up to 256 bytes, plus hla_fwd_p_bytes at
+ * chunk'.  Equal to hla_fwd_workspace_bytes(p) for shapes without that path.
+ * Host-only; 0 for an invalid or empty problem. */
+size_t hla_fwd_p_workspace_bytes(const hla_problem* p);
+
 /*
  * Chunks per span of hla_fwd (a power of two R dividing n = T / chunk): each
  * workgroup of hla_fwd's summary and output kernels walks R consecutive
@@ -203,7 +245,10 @@ int32_t hla_fwd_span_chunks(const hla_problem* p);
  * writes the n / R span totals (each the combine, in order, of R chunk
  * summaries), hla_scan turns them into exclusive prefixes, and
  * hla_fwd_output walks each span from its prefix.  The summaries are kept in
- * `workspace` (hla_fwd_workspace_bytes(p) bytes).  o and den as in
+ * `workspace` (at least hla_fwd_workspace_bytes(p) bytes; with
+ * hla_fwd_p_workspace_bytes(p) bytes, for the shapes that have it, the
+ * summary kernel also keeps the segment-local p there and the outputs come
+ * from it: hla_fwd_chunk_summaries_p and hla_fwd_output_from_p).  o and den as in
  * hla_fwd_output; the results equal those of the three calls at `chunk` up
  * to fp32 rounding order.  If `final_state` is non-NULL its non-NULL fields
  * receive the state after all T tokens ([B, H, ...]), ready for

@@ -152,6 +152,38 @@ def test_noalloc_limits_and_checks(L):
     assert f(ctypes.byref(problem(T=0)), None, None, None, None, None, None, None) == OK
 
 
+def test_segment_local_p_sizes_and_checks(L):
+    # bf16 with d = dv = 128 only: [B, H, n, ceil(chunk / 64), d, 64] bf16
+    p = problem(B=1, H=2, T=576, d=128, dv=128, chunk=96)
+    assert L.hla_fwd_p_bytes(ctypes.byref(p)) == 2 * 6 * 2 * 128 * 64 * 2
+    for kw in (dict(d=64, dv=64), dict(d=128, dv=64), dict(in_dtype=hla.HLA_F32, d=64, dv=64),
+               dict(T=10)):
+        q = problem(**dict(dict(B=1, H=2, T=576, d=128, dv=128, chunk=96), **kw))
+        assert L.hla_fwd_p_bytes(ctypes.byref(q)) == 0, kw
+    # hla_fwd with room for p: the summaries and scan scratch rounded up to
+    # 256 bytes, then p over hla_fwd's spans (R = 1 here: 6 units of 2 segments)
+    base = L.hla_fwd_workspace_bytes(ctypes.byref(p))
+    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(p)) == (base + 255) // 256 * 256 + \
+        L.hla_fwd_p_bytes(ctypes.byref(p))
+    q64 = problem()
+    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(q64)) == L.hla_fwd_workspace_bytes(ctypes.byref(q64))
+    # argument checks before anything runs
+    st = ctypes.byref(state())
+    assert L.hla_fwd_chunk_summaries_p(ctypes.byref(q64), Q, K, V, st, DEN, None) == UNSUP
+    assert L.hla_fwd_chunk_summaries_p(ctypes.byref(p), Q, K, V, st, None, None) == NULLP
+    assert L.hla_fwd_chunk_summaries_p(ctypes.byref(p), Q, K, V, st, DEN + 8, None) == MISAL
+    assert L.hla_fwd_chunk_summaries_p(ctypes.byref(p), Q, K, V, st, Q, None) == ALIAS
+    assert L.hla_fwd_output_from_p(ctypes.byref(q64), Q, V, DEN, st, O, None, None) == UNSUP
+    assert L.hla_fwd_output_from_p(ctypes.byref(p), Q, V, None, st, O, None, None) == NULLP
+    assert L.hla_fwd_output_from_p(ctypes.byref(p), Q, V, DEN, st, O + 4, None, None) == MISAL
+    assert L.hla_fwd_output_from_p(ctypes.byref(p), Q, V, DEN, st, DEN, None, None) == ALIAS
+    assert L.hla_fwd_output_from_p(ctypes.byref(p), Q, V, DEN, st, O, Q, None) == ALIAS
+    # empty problems are no-ops
+    e = problem(T=0, d=128, dv=128)
+    assert L.hla_fwd_chunk_summaries_p(ctypes.byref(e), None, None, None, None, None, None) == OK
+    assert L.hla_fwd_output_from_p(ctypes.byref(e), None, None, None, None, None, None, None) == OK
+
+
 def test_run_prefix_scan_sizes_and_checks(L):
     per = 32 * 32 + 2 * 32 * 16 + 2 * 32
     # run length: n up to 16 is one run; above, the power of two R with R^2 >= n

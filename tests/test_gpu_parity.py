@@ -124,9 +124,11 @@ def test_stages_match_oracle(gpu, case):
         assert rel_err(host(on), ratio) <= 1e-5
 
     # the composed entry point gives the same bits as the three calls (these
-    # problems have too few units for spans of several chunks)
+    # problems have too few units for spans of several chunks; the minimum
+    # workspace keeps hla_fwd on these calls' plan for every shape)
     assert hla.fwd_span_chunks(q, v, chunk, g) == 1
-    o3, dn3, fs = hla.fwd(q, k, v, chunk, g, normalize=False, want_den=True, want_state=True)
+    o3, dn3, fs = hla.fwd(q, k, v, chunk, g, normalize=False, want_den=True, want_state=True,
+                          workspace=hla.fwd_workspace(q, v, chunk, g, with_p=False))
     torch.cuda.synchronize()
     assert torch.equal(o3, o) and torch.equal(dn3, dn)
     for key in FIELDS:
@@ -239,6 +241,107 @@ def test_fwd_spans_of_several_chunks(gpu, case):
     for key in FIELDS:
         e = rel_err(host(fs[key]).reshape(U, -1), fin[key].reshape(U, -1))
         assert e <= tol, ("final state", key, e)
+
+
+def local_p(uq, uk, ug, chunk):
+    """p_t = S_t q_t with S_t = sum_{i<=t} g^(t-i) k_i k_i^T restarted at every
+    segment start (the definition; fp64), [U, T, d]."""
+    U, T, d = uq.shape
+    q64, k64 = uq.astype(np.float64), uk.astype(np.float64)
+    g = np.ones(U) if ug is None else ug.astype(np.float64)
+    out = np.zeros((U, T, d))
+    S = np.zeros((U, d, d))
+    for t in range(T):
+        if t % chunk == 0:
+            S[:] = 0.0
+        S = g[:, None, None] * S + k64[:, t, :, None] * k64[:, t, None, :]
+        out[:, t] = np.einsum("uij,uj->ui", S, q64[:, t])
+    return out
+
+
+# (B, H, T, d, dv, chunk, dtype, decay, normalize): bf16, d = dv = 128, the
+# shape whose outputs come from the segment-local p
+PCASES = [
+    (2, 2, 512, 128, 128, 128, "bf16", True, False),
+    (1, 2, 288, 128, 128, 96, "bf16", True, True),     # a 32-token last tile per segment
+    (1, 1, 600, 128, 128, 200, "bf16", False, True),   # 3 tiles + ragged 8, gamma = 1
+    (1, 1, 544, 128, 128, 32, "bf16", True, False),    # n = 17, chunks shorter than a tile
+    (1, 2, 256, 128, 128, 256, "bf16", True, False),   # n = 1
+]
+
+
+@pytest.mark.parametrize("case", PCASES, ids=[case_id(c) for c in PCASES])
+def test_outputs_from_segment_local_p(gpu, case):
+    """hla_fwd_chunk_summaries_p writes the same summaries as
+    hla_fwd_chunk_summaries and the segment-local p of the definition (zeros
+    past each segment's end); hla_fwd_output_from_p gives the oracle's outputs;
+    hla_fwd with room for p gives the same bits as these three calls."""
+    torch = gpu
+    B, H, T, d, dv, chunk, dtype, decay, norm = case
+    say("case", case_id(case))
+    inp = synth.make_fwd_inputs(B, H, T, d, dv, dtype, seed=3500 + T + chunk, decay=decay)
+    q, k, v, g = to_dev(inp)
+    uq, uk, uv, ug = inp.units()
+    U, n, tol, eps = B * H, T // chunk, tol_of(dtype), 1e-6
+    ntiles = (chunk + 63) // 64
+    assert hla.p_bytes(q, v, chunk) == U * n * ntiles * d * 64 * 2
+    gs = hla.fwd_chunk_summaries(q, k, v, chunk, g)
+    gp, pl = hla.fwd_chunk_summaries_p(q, k, v, chunk, g)
+    torch.cuda.synchronize()
+    for key in FIELDS:
+        assert torch.equal(gs[key], gp[key]), key
+    # p: per tile, (column block cb, row block r) fragments of 64 groups of 4,
+    # group l = tokens 16 r + 4 (l // 16) + [0, 4) of column 16 cb + l % 16
+    blocks = host(pl.float()).reshape(U, n, ntiles, d // 16, 4, 4, 16, 4)   # [.., cb, r, lg, lr, j]
+    want = local_p(uq, uk, ug, chunk).reshape(U, n, chunk, d)
+    tiles = blocks.transpose(0, 1, 2, 4, 5, 7, 3, 6).reshape(U, n, ntiles, 64, d)   # [.., r, lg, j, cb, lr]
+    got = tiles.reshape(U, n, ntiles * 64, d)
+    e = rel_err(got[:, :, :chunk], want)
+    say(f"  segment-local p {e:.2e}")
+    assert e <= tol
+    assert not np.any(got[:, :, chunk:]), "rows past the segment end are zeros"
+    tot = hla.scan(gp, q.shape, dv, chunk, dcode(dtype), g, want_total=True)
+    o, dn = hla.fwd_output_from_p(q, v, pl, gp, chunk, g, normalize=False, want_den=True)
+    torch.cuda.synchronize()
+    num, den, fin = O.serial(uq, uk, uv, ug)
+    e_num = rel_err(host(o).reshape(U, T, dv), num)
+    e_den = rel_err(host(dn).reshape(U, T), den)
+    say(f"  num {e_num:.2e} den {e_den:.2e}")
+    assert e_num <= tol and e_den <= tol
+    # against the path with the S recurrence, at the tolerance
+    hla.scan(gs, q.shape, dv, chunk, dcode(dtype), g)
+    o_old, dn_old = hla.fwd_output(q, k, v, gs, chunk, g, normalize=False, want_den=True)
+    torch.cuda.synchronize()
+    assert rel_err(host(o), host(o_old)) <= tol and rel_err(host(dn), host(dn_old)) <= tol
+    if norm:
+        on, dn2 = hla.fwd_output_from_p(q, v, pl, gp, chunk, g, normalize=True, eps=eps,
+                                        want_den=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dn2, dn)
+        assert rel_err(host(on), host(o) / (host(dn)[..., None] + eps)) <= 1e-5
+    # hla_fwd with room for p: the same bits as the three calls above
+    assert hla.fwd_span_chunks(q, v, chunk, g) == 1
+    o3, dn3, fs = hla.fwd(q, k, v, chunk, g, normalize=False, want_den=True, want_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o) and torch.equal(dn3, dn)
+    for key in FIELDS:
+        assert torch.equal(fs[key], tot[key]), key
+
+
+def test_outputs_from_p_gamma_zero(gpu):
+    """gamma = 0 on the segment-local p path: each output is (q.k)^2 v of its own token."""
+    torch = gpu
+    inp = synth.make_fwd_inputs(1, 2, 256, 128, 128, "bf16", seed=71, decay=True)
+    inp.gamma = np.array([0.0, 0.5], np.float32)
+    q, k, v, g = to_dev(inp)
+    o, dn, _ = hla.fwd(q, k, v, 128, g, want_den=True)
+    torch.cuda.synchronize()
+    uq, uk, uv, ug = inp.units()
+    num, den, _ = O.serial(uq, uk, uv, ug)
+    s = np.sum(uq[0].astype(np.float64) * uk[0], axis=-1)
+    assert rel_err(num[0], (s * s)[:, None] * uv[0]) < 1e-12     # oracle special case
+    assert rel_err(host(o).reshape(2, 256, 128), num) <= 2e-2
+    assert rel_err(host(dn).reshape(2, 256), den) <= 2e-2
 
 
 def full_or_sampled(name, sample_units):

@@ -1,8 +1,10 @@
 """hla_fwd_noalloc (the forward with the library's own fixed scratch) against
 hla_fwd (the same forward with a caller workspace), through the C ABI: two
 calls in a row on one device, the second with a smaller problem, each equal
-bit for bit to hla_fwd on the same inputs (same kernels, same launches); the
-first also against the fp64 oracle at the bf16 tolerance."""
+bit for bit to hla_fwd on the same inputs given the minimum workspace (the
+same kernels and launches: without room for the segment-local p, hla_fwd
+takes the plan the fixed scratch holds); the first also against the fp64
+oracle at the bf16 tolerance."""
 
 import numpy as np
 import pytest
@@ -45,8 +47,10 @@ def one(torch, case, seed, check_oracle):
     import ctypes
     need = hla.lib().hla_fwd_workspace_bytes(ctypes.byref(p))
     assert 0 < need <= hla.lib().hla_fwd_noalloc_max_workspace_bytes()
+    ws = hla.fwd_workspace(q, v, chunk, g, with_p=False)
+    assert ws.numel() == need
     o1, d1, s1 = hla.fwd(q, k, v, chunk, g, normalize=norm, eps=1e-6, want_den=True,
-                         want_state=want_state)
+                         want_state=want_state, workspace=ws)
     o2, d2, s2 = hla.fwd_noalloc(q, k, v, chunk, g, normalize=norm, eps=1e-6, want_den=True,
                                  want_state=want_state)
     torch.cuda.synchronize()
