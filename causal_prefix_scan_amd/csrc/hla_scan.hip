@@ -474,27 +474,29 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
   }
 }
 
-// Step 4: C and m of every segment become their exclusive prefixes.  One
-// thread per f32x4 of (C | m) per (unit, run); blockIdx.x = (unit * runs +
+// Step 4: C and m (and, after the side-by-side rescan, S) of every segment
+// become their exclusive prefixes: elementwise decayed running sums.  One
+// thread per f32x4 of (S | C | m) per (unit, run); blockIdx.x = (unit * runs +
 // run) * NBLK + block.
-template <int D, int E>
+template <int D, int E, bool WITH_S>
 __global__ __launch_bounds__(256) void run_cm_kernel(RunArgs a) {
-  constexpr int VC = D * E / 4, VM = D / 4, NBLK = (VC + VM + 255) / 256;
+  constexpr int VS = WITH_S ? D * D / 4 : 0, VC = D * E / 4, VM = D / 4;
+  constexpr int NBLK = (VS + VC + VM + 255) / 256;
   const int grp = blockIdx.x / NBLK;
   const int e = (blockIdx.x % NBLK) * 256 + threadIdx.x;
-  if (e >= VC + VM) return;
+  if (e >= VS + VC + VM) return;
   const int unit = grp / a.runs, run = grp % a.runs;
   const int k0 = run * a.R;
   const int len = (a.n - k0) < a.R ? (a.n - k0) : a.R;
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
   const float al = gpow(g, log2f(g), a.chunk);
-  const bool isC = e < VC;
-  const int o = isC ? e : e - VC;
-  const size_t per = isC ? (size_t)D * E : (size_t)D;
-  f32x4* base = reinterpret_cast<f32x4*>(isC ? a.C : a.m);
+  const int fld = e < VS ? 0 : e < VS + VC ? 1 : 2;   // S, C, m
+  const int o = fld == 0 ? e : fld == 1 ? e - VS : e - VS - VC;
+  const size_t per = fld == 0 ? (size_t)D * D : fld == 1 ? (size_t)D * E : (size_t)D;
+  f32x4* base = reinterpret_cast<f32x4*>(fld == 0 ? a.S : fld == 1 ? a.C : a.m);
   f32x4 p = zero4();
   if (a.from_prefix) {
-    const float* pa = isC ? a.aC : a.am;
+    const float* pa = fld == 0 ? a.aS : fld == 1 ? a.aC : a.am;
     p = reinterpret_cast<const f32x4*>(pa + ((size_t)unit * a.runs + run) * per)[o];
   }
   constexpr int BATCH = 8;
@@ -511,8 +513,175 @@ __global__ __launch_bounds__(256) void run_cm_kernel(RunArgs a) {
       }
   }
   if (run == a.runs - 1) {
-    float* t = isC ? a.tC : a.tm;
+    float* t = fld == 0 ? a.tS : fld == 1 ? a.tC : a.tm;
     if (t) reinterpret_cast<f32x4*>(t + (size_t)unit * per)[o] = p;
+  }
+}
+
+// Step 3 with a run's segments side by side (runs of at most 16 segments).
+// Over a run the exclusive prefixes obey
+//   C_P(k+1) = a C_P(k) + C_k      (m and S likewise),
+//   G_P(k+1) = a^2 G_P(k) + X_k,   X_k = G_k + a S_k C_P(k),
+//   h_P(k+1) = a^2 h_P(k) + y_k,   y_k = h_k + a S_k m_P(k),
+// so the products S_k C_P(k) and S_k m_P(k) need only the elementwise
+// prefixes of C and m and do not depend on one another: every segment's
+// product runs at once instead of one link of a chain per segment.  One
+// workgroup per (unit, run, 16-row block, 16-column block) and one wave per
+// segment: the waves load their segments together, the C column block's and
+// m's prefixes are formed across the slots in LDS, each wave forms its X
+// block (and y rows in the column block 0 workgroups) on fp32 MFMA, and the G
+// (h) prefixes are formed across the slots and written in place.  S, C and m
+// are only read here (every workgroup of the run reads them);
+// run_cm_kernel<.., true> rewrites them afterwards.  The workgroups of one
+// (unit, run) share blockIdx.x mod 8, i.e. one XCD and its L2.
+template <int D, int E, int RM>
+__global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
+  constexpr int NT = 64 * RM, DT = D / 16, NCB = E / 16, NP = (D / 16) * NCB;
+  constexpr int LC = D + 4;   // floats per column of a slot's C block
+  // slot w: the C block's prefix, then (once wave w has read it) X's block in
+  // its first 256 floats and y in the next 16; only wave w touches its slot
+  // between the barriers
+  __shared__ __attribute__((aligned(16))) float sC[RM][16 * LC];
+  __shared__ float sm[RM][D];
+
+  const int bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
+  const int grp = xcd + 8 * (qb / NP), part = qb % NP;
+  if (grp >= a.units * a.runs) return;
+  const int rb = part / NCB, cb = part % NCB;
+  const int unit = grp / a.runs, run = grp % a.runs;
+  const int k0 = run * a.R;
+  const int len = (a.n - k0) < a.R ? (a.n - k0) : a.R;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg4 = lane >> 4;
+  const int r0 = 16 * rb, c0 = 16 * cb;
+  const bool hw = cb == 0;    // this workgroup also carries h, which needs m
+  const bool live = w < len;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float al = gpow(g, log2f(g), a.chunk), al2 = al * al;
+  const size_t pr = (size_t)unit * a.runs + run;
+  const size_t sl = (size_t)unit * a.n + k0 + w;
+
+  // 1. this wave's segment: C column block (rows 16 t + 4 lg4 + j, column
+  // c0 + lr), S rows r0 + lr as the A operand (columns 16 c + 4 lg4 .. + 3),
+  // G block (rows r0 + 4 lg4 + j, column c0 + lr), h row r0 + lr, m
+  f32x4 xC[DT], xS[DT], xG = zero4();
+  float xh = 0.f;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) xC[t] = xS[t] = zero4();
+  if (live) {
+    const float* pC = a.C + sl * D * E;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xC[t][j] = pC[(size_t)(16 * t + 4 * lg4 + j) * E + c0 + lr];
+    const f32x4* pS = reinterpret_cast<const f32x4*>(a.S + sl * D * D + (size_t)(r0 + lr) * D);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) xS[t] = pS[4 * t + lg4];
+    const float* pG = a.G + sl * D * E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xG[j] = pG[(size_t)(r0 + 4 * lg4 + j) * E + c0 + lr];
+    if (hw) {
+      xh = a.h[sl * D + r0 + lr];
+      for (int t = lane; t < D; t += 64) sm[w][t] = a.m[sl * D + t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+    *reinterpret_cast<f32x4*>(&sC[w][lr * LC + 16 * t + 4 * lg4]) = xC[t];
+  __syncthreads();
+
+  // 2. exclusive prefixes of the C column block and of m across the run
+  for (int e = tid; e < 16 * D; e += NT) {
+    const int row = e >> 4, col = e & 15;
+    float p = a.from_prefix ? a.aC[pr * D * E + (size_t)row * E + c0 + col] : 0.f;
+    // every slot is read and written (slots past the run's end are never
+    // used): no branch, so the reads issue together
+    float v[RM];
+#pragma unroll
+    for (int s = 0; s < RM; ++s) v[s] = sC[s][col * LC + row];
+#pragma unroll
+    for (int s = 0; s < RM; ++s) {
+      sC[s][col * LC + row] = p;
+      p = p * al + v[s];
+    }
+  }
+  if (hw) {
+    for (int e = tid; e < D; e += NT) {
+      float p = a.from_prefix ? a.am[pr * D + e] : 0.f;
+      float v[RM];
+#pragma unroll
+      for (int s = 0; s < RM; ++s) v[s] = sm[s][e];
+#pragma unroll
+      for (int s = 0; s < RM; ++s) {
+        sm[s][e] = p;
+        p = p * al + v[s];
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. X = G_k + a S_k C_P(k) for the block, y = h_k + a S_k m_P(k)
+  if (live) {
+    f32x4 cp[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) cp[t] = *reinterpret_cast<const f32x4*>(&sC[w][lr * LC + 16 * t + 4 * lg4]);
+    f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+    for (int kk = 0; kk < D / 4; ++kk) {
+      const float ak = xS[kk >> 2][kk & 3], bk = Frag<float>::acc_b(cp, kk);
+      if (kk & 1) acc1 = MM<float>::mma(ak, bk, acc1);
+      else acc0 = MM<float>::mma(ak, bk, acc0);
+    }
+    *reinterpret_cast<f32x4*>(&sC[w][4 * lane]) = xG + (acc0 + acc1) * al;
+    if (hw) {
+      float hp = 0.f;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hp += xS[t][i] * sm[w][16 * t + 4 * lg4 + i];
+      hp += __shfl_xor(hp, 16, 64);
+      hp += __shfl_xor(hp, 32, 64);
+      if (lg4 == 0) sC[w][256 + lr] = xh + al * hp;
+    }
+  }
+  __syncthreads();
+
+  // 4. exclusive prefixes of the G block and of h across the run, in place;
+  // the last run's inclusive totals
+  const bool last = run == a.runs - 1;
+  for (int e = tid; e < 256; e += NT) {
+    const int row = e >> 4, col = e & 15;
+    const int li = 4 * (16 * (row >> 2) + col) + (row & 3);   // lane 16 (row/4) + col, element row % 4
+    const size_t go = (size_t)(r0 + row) * E + c0 + col;
+    float p = a.from_prefix ? a.aG[pr * D * E + go] : 0.f;
+    float v[RM], o[RM];
+#pragma unroll
+    for (int s = 0; s < RM; ++s) v[s] = sC[s][li];
+#pragma unroll
+    for (int s = 0; s < RM; ++s) {
+      o[s] = p;
+      if (s < len) p = p * al2 + v[s];
+    }
+    float* pG = a.G + ((size_t)unit * a.n + k0) * D * E + go;
+#pragma unroll
+    for (int s = 0; s < RM; ++s)
+      if (s < len) pG[(size_t)s * D * E] = o[s];
+    if (last && a.tG) a.tG[(size_t)unit * D * E + go] = p;
+  }
+  if (hw && tid < 16) {
+    float p = a.from_prefix ? a.ah[pr * D + r0 + tid] : 0.f;
+    float v[RM], o[RM];
+#pragma unroll
+    for (int s = 0; s < RM; ++s) v[s] = sC[s][256 + tid];
+#pragma unroll
+    for (int s = 0; s < RM; ++s) {
+      o[s] = p;
+      if (s < len) p = p * al2 + v[s];
+    }
+    float* ph = a.h + ((size_t)unit * a.n + k0) * D + r0 + tid;
+#pragma unroll
+    for (int s = 0; s < RM; ++s)
+      if (s < len) ph[(size_t)s * D] = o[s];
+    if (last && a.th) a.th[(size_t)unit * D + r0 + tid] = p;
   }
 }
 
@@ -619,12 +788,30 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
     }
   }
   if (runs_only) return hipSuccess;
+  if constexpr (D <= 64) {
+    if (r.R <= 16) {
+      // runs of at most 16 segments: the segments of a run side by side, then S,
+      // C and m elementwise (measured at d = 64 with 16 segments per head: 25 ->
+      // 17 us and 32 -> 25 us; at d = 128, 4 segments per head, the walk below
+      // stays faster: 37 against 56 us)
+      constexpr int NP = (D / 16) * (E / 16);
+      if (r.R <= 4)
+        hipLaunchKernelGGL((run_flat_kernel<D, E, 4>), dim3(groups8 * NP), dim3(256), 0, s, r);
+      else
+        hipLaunchKernelGGL((run_flat_kernel<D, E, 16>), dim3(groups8 * NP), dim3(1024), 0, s, r);
+      if (hipError_t e = hipGetLastError()) return e;
+      constexpr int VSCM = (D * D + D * E + D) / 4;
+      hipLaunchKernelGGL((run_cm_kernel<D, E, true>), dim3((unsigned)(cnt * ((VSCM + 255) / 256))),
+                         dim3(256), 0, s, r);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((run_rows_kernel<D, E, false>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
   if (hipError_t e = hipGetLastError()) return e;
   if (NRR == 1) return hipSuccess;   // the rescan wrote C and m
   constexpr int VCM = (D * E + D) / 4;
-  hipLaunchKernelGGL((run_cm_kernel<D, E>), dim3((unsigned)(cnt * ((VCM + 255) / 256))), dim3(256), 0,
-                     s, r);
+  hipLaunchKernelGGL((run_cm_kernel<D, E, false>), dim3((unsigned)(cnt * ((VCM + 255) / 256))), dim3(256),
+                     0, s, r);
   return hipGetLastError();
 }
 
