@@ -1155,10 +1155,10 @@ struct Third {
   hla::LaOperand Q, K, V, ONE, Pq, U, UM;
   // one first-order sum over this problem's segments
   hla_status sum(hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
-                 float* y, int y_bf16, float* Hp, bool states_only) const {
+                 float* y, int y_bf16, float* Hp, bool states_only, float* Hout = nullptr) const {
     hla::LaArgs la;
     la.a = a; la.b = b; la.c = c;
-    la.y = y; la.Hp = Hp; la.gamma = p->gamma;
+    la.y = y; la.Hp = Hp; la.Hout = Hout; la.gamma = p->gamma;
     la.H = p->H; la.gexp = gexp;
     la.T = p->T; la.seg = p->chunk; la.nseg = (int)z.n;
     la.reverse = 0; la.accumulate = 0;
@@ -1182,15 +1182,13 @@ hla_status third_summaries(const Third& t, char* wb, const Ws3& w, float* S, flo
   float* umy = reinterpret_cast<float*>(wb + w.um);
   const size_t tok = (size_t)t.z.units * (size_t)t.p->T;
   if (hla_status x = from_hip(hla::launch_unit_channel(t.bf, wb + w.one, tok, t.s))) return x;
-  // local p, u, u_m: every segment from the zero state
-  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, py, t.bf, nullptr, false)) return x;
-  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, uy, t.bf, nullptr, false)) return x;
-  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, umy, t.bf, nullptr, false)) return x;
-  // the summaries as segment states
-  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, nullptr, 0, S, true)) return x;
+  // local p, u, u_m: every segment from the zero state; the same passes leave
+  // the segment states of their sums, the summaries S^K, P^KV and m^K
+  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, py, t.bf, nullptr, false, S)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, uy, t.bf, nullptr, false, P)) return x;
+  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, umy, t.bf, nullptr, false, m)) return x;
+  // the other summaries as segment states
   if (hla_status x = t.sum(t.Q, t.Q, t.Q, d, d, 1, nullptr, 0, Qm, true)) return x;
-  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, nullptr, 0, P, true)) return x;
-  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, nullptr, 0, m, true)) return x;
   if (hla_status x = t.sum(t.Q, t.Pq, t.Q, d, d, 2, nullptr, 0, V, true)) return x;
   if (hla_status x = t.sum(t.Q, t.Q, t.U, d, e, 2, nullptr, 0, Z, true)) return x;
   if (hla_status x = t.sum(t.Q, t.Q, t.UM, d, 16, 2, nullptr, 0, z, true)) return x;

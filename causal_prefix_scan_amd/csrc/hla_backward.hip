@@ -318,13 +318,12 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
     __syncthreads();
   }
 
-  if constexpr (!OUT) {
-    if (cols) {
+  float* Ho = OUT ? a.Hout : a.Hp;
+  if (Ho && cols) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a.Hp[hbase + (size_t)(16 * t + 4 * lg + j) * Dc + col] = Ht[t][j];
-    }
+      for (int j = 0; j < 4; ++j) Ho[hbase + (size_t)(16 * t + 4 * lg + j) * Dc + col] = Ht[t][j];
   }
 }
 

@@ -197,6 +197,10 @@ struct LaArgs {
   // it, rounded to bf16, here ([unit][T][Da]); after a summary pass the
   // output pass reads this copy instead of b
   void* b_copy = nullptr;
+  // when set (output pass): the state after each segment's last tile, from
+  // the state the segment started from, [unit][nseg][Da][Dc] (with Hp null:
+  // the segment's own state, the same values a summary pass writes)
+  float* Hout = nullptr;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
 // same b, c and lam as an earlier call), so only the output pass runs; with

@@ -58,6 +58,8 @@ SMALL = [
     (1, 2, 640, 32, 32, 32, "bf16", True, True),      # n = 20: runs 8, 8, 4; tree pads 3 -> 4
     (1, 1, 640, 16, 16, 16, "f32", True, False),      # n = 40: 5 runs, tree pads 5 -> 8
     (1, 1, 544, 128, 128, 32, "bf16", True, False),   # n = 17: runs 8, 8, 1
+    (1, 2, 1536, 64, 64, 64, "bf16", True, True),     # n = 24 at d = 64: runs of 8 side by side
+                                                      # (16-wave rescan, 8 waves idle), from prefixes
     (1, 2, 288, 128, 128, 96, "bf16", True, True),    # 8 waves, a 32-token last tile per segment
     (2, 1, 200, 128, 64, 100, "bf16", False, True),   # 8 waves, d > dv, 36-token last tile
     # more than 256 workgroups: the 4-wave d = 64 kernels (the cases above with
