@@ -1384,10 +1384,18 @@ hla_status hla3_fwd(const hla_problem* p, const void* q, const void* k, const vo
   a.tR = fs ? fs->R : nullptr; a.tr = fs ? fs->r : nullptr;
   a.gamma = p->gamma; a.H = p->H; a.seg = p->chunk; a.nseg = n; a.ldm = 16; a.units = (int)units;
   if (hla_status x = from_hip(hla::launch_r_scan(d, e, units, a, t.s))) return x;
-  // outputs: p, u, u_m from their moments' prefixes, then num and den from R, r
-  if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, F(w.p), t.bf, F(w.S), false)) return x;
-  if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, F(w.u), t.bf, F(w.P), false)) return x;
-  if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, F(w.um), t.bf, F(w.m), false)) return x;
+  // outputs: p, u, u_m are their segment-local parts (left in the workspace by
+  // the summaries) plus the prefix terms lam^(t-s0+1) q_t^T (S, P, m prefix);
+  // then num and den from R, r
+  if (n > 1) {
+    hla::PrefixTermArgs pa;
+    pa.a = t.Q;
+    pa.y[0] = wb + w.p; pa.y[1] = wb + w.u; pa.y[2] = wb + w.um;
+    pa.Hp[0] = F(w.S); pa.Hp[1] = F(w.P); pa.Hp[2] = F(w.m);
+    pa.gamma = p->gamma; pa.H = p->H; pa.gexp = 1; pa.T = p->T; pa.seg = p->chunk; pa.nseg = n;
+    pa.mfma_bf16 = t.bf;
+    if (hla_status x = from_hip(hla::launch_prefix_terms(d, e, units, pa, t.s))) return x;
+  }
   if (hla_status x = t.sum(t.Q, t.Pq, t.U, d, e, 3, o, 0, F(w.R), false)) return x;
   if (hla_status x = t.sum(t.Q, t.Pq, t.UM, d, 16, 3, F(w.den16), 0, F(w.r), false)) return x;
   return from_hip(hla::launch_finish3(o, F(w.den16), den, (size_t)units * p->T, e, p->normalize,

@@ -428,6 +428,133 @@ hipError_t launch_la_mode(int Da, int Dc, int units, const LaArgs& a, hipStream_
   return hipErrorInvalidValue;
 }
 
+// y_i += lam^(t - s0 + 1) a_t^T Hp_i for the three outputs of PrefixTermArgs:
+// the part of a first-order sum that the exclusive segment prefix adds to
+// the segment-local sum (the state at position t is lam^(t-s0+1) Hp plus the
+// local state), so a pass that already has the local outputs needs no scores
+// and no state recurrence for it.  One workgroup per (unit, segment); the 16-
+// column blocks of the three outputs are dealt to the waves two at a time,
+// each wave holding its blocks of Hp in registers for the whole segment.
+constexpr int pt_waves(int da, int e) { return (da / 16 + e / 16 + 2) / 2; }
+
+template <int Da, int E>
+struct PtShape {
+  static constexpr int NB0 = Da / 16, NB1 = E / 16, NB = NB0 + NB1 + 1;
+  static constexpr int NW = pt_waves(Da, E);
+};
+
+template <typename T, int Da, int E>
+__global__ __launch_bounds__(64 * pt_waves(Da, E)) void prefix_term_kernel(PrefixTermArgs a) {
+  using L = LLayout<T, Da, 16, false>;
+  using MMT = MM<T>;
+  using FR = Frag<T>;
+  using Sh = PtShape<Da, E>;
+  constexpr int NW = Sh::NW, NTHR = 64 * NW, LT = L::LT, TR = LT / 16, DT = Da / 16;
+  constexpr int KS = MMT::KS;
+  constexpr int QK = KS == 32 ? (DT + 1) / 2 : DT * 4;   // K steps over Da (as in la_kernel)
+  __shared__ __attribute__((aligned(16))) T As[LT * L::LDA];
+  __shared__ float w1[LT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int us = blockIdx.x;
+  const int unit = us / a.nseg, seg = us - unit * a.nseg;
+  float lam = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  lam = a.gexp == 3 ? lam * lam * lam : a.gexp == 2 ? lam * lam : lam;
+  const float lgl = log2f(lam);
+  const int nT = a.T;
+  const int s0 = seg * a.seg, s1 = s0 + a.seg < nT ? s0 + a.seg : nT;
+  const size_t urow = (size_t)unit * (size_t)nT;
+
+  // columns past Da (a zero-padded MFMA step) read as zeros
+  for (int i = tid; i < LT * L::LDA; i += NTHR) As[i] = (T)0.f;
+  if (tid < LT) w1[tid] = gpow(lam, lgl, tid + 1);
+
+  // this wave's two column blocks: output oi[b], block cbk[b] of it, width wd[b]
+  int oi[2], cbk[2], wd[2];
+  bool own[2];
+  f32x4 Ht[2][DT];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int gb = 2 * wave + b;
+    own[b] = gb < Sh::NB;
+    oi[b] = gb < Sh::NB0 ? 0 : gb < Sh::NB0 + Sh::NB1 ? 1 : 2;
+    cbk[b] = oi[b] == 0 ? gb : oi[b] == 1 ? gb - Sh::NB0 : 0;
+    wd[b] = oi[b] == 0 ? Da : oi[b] == 1 ? E : 16;
+    const float* hp = a.Hp[oi[b]] + (size_t)us * Da * wd[b];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        Ht[b][t][j] = own[b] ? hp[(size_t)(16 * t + 4 * lg + j) * wd[b] + 16 * cbk[b] + lr] : 0.f;
+  }
+  __syncthreads();
+
+  TileRows<Da, NTHR, LT, sizeof(T) == 4> ra;
+  ra.load(a.a, urow, nT, false, s0, s1, tid);
+  for (int t0 = s0; t0 < s1; t0 += LT) {
+    ra.store(As, L::LDA, tid);
+    __syncthreads();
+    if (t0 + LT < s1) ra.load(a.a, urow, nT, false, t0 + LT, s1, tid);
+    const float gt0 = gpow(lam, lgl, t0 - s0);
+    // y^T per row block (Hp's block is the A operand), so that a lane holds
+    // four adjacent columns of one token: 8- (bf16) or 16-byte (fp32) accesses.
+    // The local outputs of this wave's blocks are loaded first, in flight
+    // during the products.
+    using V = typename Vec4<T>::V;
+    V yl[2][TR];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const int l = t0 + 16 * r + lr;
+        yl[b][r] = V{};
+        if (own[b] && l < s1)
+          yl[b][r] = *reinterpret_cast<const V*>(reinterpret_cast<const T*>(a.y[oi[b]]) +
+                                                 (urow + l) * wd[b] + 16 * cbk[b] + 4 * lg);
+      }
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+      const float wt = gt0 * w1[16 * r + lr];
+      const int l = t0 + 16 * r + lr;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (!own[b]) continue;
+        f32x4 y = zero4();
+#pragma unroll
+        for (int kk = 0; kk < QK; ++kk) y = MMT::mma(FR::acc_b(Ht[b], kk), FR::perm(As, L::LDA, 16 * r, kk, lane), y);
+        if (l < s1) {
+          V o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = (T)((float)yl[b][r][j] + y[j] * wt);
+          *reinterpret_cast<V*>(reinterpret_cast<T*>(a.y[oi[b]]) + (urow + l) * wd[b] + 16 * cbk[b] + 4 * lg) = o;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int DA, int E>
+hipError_t launch_pt(int units, const PrefixTermArgs& a, hipStream_t s) {
+  // bf16 operands come from bf16 tensors, fp32 ones from fp32 tensors
+  if (a.a.bf16 != (sizeof(T) == 2 ? 1 : 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefix_term_kernel<T, DA, E>), dim3((unsigned)units * a.nseg),
+                     dim3(64 * pt_waves(DA, E)), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_pt_dims(int Da, int E, int units, const PrefixTermArgs& a, hipStream_t s) {
+#define HLA_CASE(DA, DE) \
+  if (Da == DA && E == DE) return launch_pt<T, DA, DE>(units, a, s);
+  HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(32, 16) HLA_CASE(32, 32) HLA_CASE(32, 64)
+  HLA_CASE(64, 32) HLA_CASE(64, 64) HLA_CASE(64, 128) HLA_CASE(128, 64) HLA_CASE(128, 128)
+#undef HLA_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int MODE>
 hipError_t launch_la(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {
   return a.mfma_bf16 ? launch_la_mode<__bf16, MODE>(Da, Dc, units, a, s)
@@ -488,6 +615,10 @@ hipError_t launch_to_bf16(const float* x, void* y, size_t n, hipStream_t s) {
   hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x,
                      (__bf16*)y, n);
   return hipGetLastError();
+}
+
+hipError_t launch_prefix_terms(int Da, int E, int units, const PrefixTermArgs& a, hipStream_t s) {
+  return a.mfma_bf16 ? launch_pt_dims<__bf16>(Da, E, units, a, s) : launch_pt_dims<float>(Da, E, units, a, s);
 }
 
 hipError_t launch_first_order_states(int Da, int Dc, int units, const LaArgs& a, hipStream_t s) {

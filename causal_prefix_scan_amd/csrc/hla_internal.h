@@ -212,6 +212,22 @@ hipError_t launch_first_order_sum(int Da, int Dc, int units, const LaArgs& a, hi
 // not read.
 hipError_t launch_first_order_states(int Da, int Dc, int units, const LaArgs& a, hipStream_t s);
 
+// The prefix terms of three first-order sums that share a and lam and whose
+// segment-local parts y already hold (every segment from the zero state):
+//   y_i[t] += lam^(t - s0 + 1) a_t^T Hp_i[seg]     (s0 = the segment's first token)
+// for outputs of widths Da (i = 0), E (1) and 16 (2); Hp_i the exclusive
+// segment prefixes [unit][nseg][Da][width] (fp32); y_i [unit][T][width] in
+// the MFMA operand type (bf16 with mfma_bf16, else fp32), updated in place.
+struct PrefixTermArgs {
+  LaOperand a;
+  void* y[3];
+  const float* Hp[3];
+  const float* gamma;
+  int H, gexp, T, seg, nseg;
+  int mfma_bf16;
+};
+hipError_t launch_prefix_terms(int Da, int E, int units, const PrefixTermArgs& a, hipStream_t s);
+
 // Upstream gradients of the ratio-normalised output from the unnormalised
 // num [tokens, dv] and den [tokens] (fp32): g_num [tokens, dv] = dO / (den +
 // eps); g_den [tokens, 16] holds -(dO . num) / (den + eps)^2 in column 0 and
