@@ -705,12 +705,12 @@ def hla3_bytes_per_token(d, dv, es, chunk):
     one = 16 * es
     passes = [
         # local p, u, q.m: read q, k (and v / the unit channel), write the result
+        # (and the S^K, P^KV, m^K summaries, counted with the states below)
         2 * d * es + d * es, 2 * d * es + dv * es + dv * es, 2 * d * es + one + one,
-        # summaries: read the two operands of each state
-        d * es, d * es, d * es + dv * es, d * es + one, 2 * d * es, d * es + dv * es,
-        d * es + one, d * es + dv * es, d * es + one,
-        # global p, u, q.m from the moments' prefixes
-        2 * d * es + d * es, 2 * d * es + dv * es + dv * es, 2 * d * es + one + one,
+        # the other summaries: read the two operands of each state (S^Q: q once)
+        d * es, 2 * d * es, d * es + dv * es, d * es + one, d * es + dv * es, d * es + one,
+        # global p, u, q.m: read q, read and rewrite the local p, u, q.m
+        d * es + 2 * d * es + 2 * dv * es + 2 * one,
         # num (fp32 out), den16 (fp32 out), den
         2 * d * es + dv * es + dv * 4, 2 * d * es + one + 16 * 4, 16 * 4 + 4,
     ]
