@@ -676,6 +676,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void chunk_kernel(ChunkAr
       }
     };
     uint4 xq[NXS];
+    // output kernel: the S waves (P, the B scores both roles wait for) issue
+    // first when both roles are ready (measured at B1 H32 T65536 d64: outputs
+    // 0.298 -> 0.293 ms; the summary kernel gains nothing either way)
+    if constexpr (!SUM) __builtin_amdgcn_s_setprio(2);
     if constexpr (L::PIPE) {
       finish_init();
       prologue();

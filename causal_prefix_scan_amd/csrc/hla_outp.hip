@@ -305,6 +305,10 @@ __global__ __launch_bounds__(1024, 1) void outp_kernel(ChunkArgs a) {
       }
     }
     prologue_tail();
+    // the M waves' chain (B V, the outputs, the M update, Q M) bounds the
+    // tile while the P waves wait at the barriers for it: they issue first
+    // when both are ready (measured: outputs 0.281 -> 0.270 ms)
+    __builtin_amdgcn_s_setprio(2);
     for (int ti = 0; ti < ntiles; ++ti) {
       const int p = ti & 1;
       const int t0 = ti * TT;
