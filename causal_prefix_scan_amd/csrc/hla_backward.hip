@@ -251,43 +251,38 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
       }
       __syncthreads();
       if (cols) {
-        // Y = lam^(tau+1) A H_prev + S C for this wave's 16 columns
+        // Y = lam^(tau+1) A H_prev + S C for this wave's 16 columns, as Y^T
+        // (the state and C blocks are the A operands): a lane holds columns
+        // 16 wave + 4 lg .. + 3 of token 16 r + lr and stores them at once
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
-          // (accumulating calls) the previous outputs of the row block, in
-          // flight during its products
-          float yold[4];
+          const int l = t0 + 16 * r + lr;
+          const size_t o = (urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + 16 * wave + 4 * lg;
+          // (accumulating calls) the previous outputs, in flight during the products
+          f32x4 yold = zero4();
           if constexpr (ACC) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int l = t0 + 16 * r + 4 * lg + j;
-              yold[j] = l < s1 ? a.y[(urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col] : 0.f;
-            }
+            if (l < s1) yold = *reinterpret_cast<const f32x4*>(a.y + o);
           }
           f32x4 y = zero4();
 #pragma unroll
-          for (int kk = 0; kk < QK; ++kk) y = MMT::mma(FR::perm(As, L::LDA, 16 * r, kk, lane), FR::acc_b(Ht, kk), y);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] *= w1[16 * r + 4 * lg + j];
+          for (int kk = 0; kk < QK; ++kk) y = MMT::mma(FR::acc_b(Ht, kk), FR::perm(As, L::LDA, 16 * r, kk, lane), y);
+          y *= w1[16 * r + lr];
 #pragma unroll
           for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-            y = MMT::mma(MMT::ld(Ss, L::LDS_, 16 * r, k0, lane), FR::tr(Cs, LDC, k0, 16 * wave, lane), y);
+            y = MMT::mma(FR::tr(Cs, LDC, k0, 16 * wave, lane), MMT::ld(Ss, L::LDS_, 16 * r, k0, lane), y);
           if constexpr (SYM) {
 #pragma unroll
             for (int k0 = 0; k0 < 16 * r + 16; k0 += KS)
-              y = MMT::mma(MMT::ld(Ss2, L::LDS_, 16 * r, k0, lane), FR::tr(Bs, L::LDA, k0, 16 * wave, lane), y);
+              y = MMT::mma(FR::tr(Bs, L::LDA, k0, 16 * wave, lane), MMT::ld(Ss2, L::LDS_, 16 * r, k0, lane), y);
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int l = t0 + 16 * r + 4 * lg + j;
-            if (l < s1) {
-              const size_t o = (urow + (size_t)(rev ? nT - 1 - l : l)) * Dc + col;
-              if constexpr (ACC)
-                a.y[o] = yold[j] + y[j];
-              else if (a.y_bf16)
-                reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)y[j];
-              else
-                a.y[o] = y[j];
+          if (l < s1) {
+            if constexpr (ACC) {
+              *reinterpret_cast<f32x4*>(a.y + o) = yold + y;
+            } else if (a.y_bf16) {
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.y) + o) =
+                  bf16x4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+            } else {
+              *reinterpret_cast<f32x4*>(a.y + o) = y;
             }
           }
         }
