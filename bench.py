@@ -97,8 +97,9 @@ def parse():
 # Per-call HIP events are recorded on every KERNEL_EVENT_EVERY-th timed step
 # only: each record is a marker in the stream that costs a few microseconds,
 # which the step time would otherwise carry (14 us of a 65 us step at B2 H8
-# T4096 d64).  The step time comes from one event pair around all timed steps.
-KERNEL_EVENT_EVERY = 10
+# T4096 d64; still 1.5 us per step on average with every 10th step sampled).
+# The step time comes from one event pair around all timed steps.
+KERNEL_EVENT_EVERY = 25
 
 
 def timing_events(torch, steps):
