@@ -181,8 +181,8 @@ def bench_fwd(args, torch, np):
     dcode = hla.HLA_BF16 if cfg["dtype"] == "bf16" else hla.HLA_F32
     L = hla.lib()
     # hla_fwd's plan: each workgroup walks a span of R chunks (forming and
-    # combining their summaries in order), hla_scan runs over the span totals,
-    # and the outputs walk each span from its prefix
+    # combining their summaries in order), the scan runs over the span totals
+    # (out of place where built), and the outputs walk each span from its prefix
     p0 = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
     R = L.hla_fwd_span_chunks(ctypes.byref(p0))
     span = chunk * R
@@ -203,6 +203,17 @@ def bench_fwd(args, torch, np):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    # the shapes that have it (d = dv <= 64, runs of at most 16 span totals)
+    # scan out of place, as hla_fwd does: the whole rescan in one launch
+    pre = hla.alloc_state((B, H, n), d, dv, "cuda")
+    st_pre = hla._state_struct(pre)
+    rc = L.hla_scan_into(ctypes.byref(p), ctypes.byref(st), ctypes.byref(st_pre), None, ptr(ws),
+                         ctypes.c_size_t(ws_bytes), sp)
+    if rc not in (0, 5):   # HLA_OK, HLA_ERR_UNSUPPORTED
+        raise RuntimeError(f"hla_scan_into failed: {rc}")
+    into = rc == 0
+    name_scan = "hla_scan_into" if into else "hla_scan"
+    st_out = st_pre if into else st
 
     def step(ev=None):
         if ev:
@@ -214,14 +225,18 @@ def bench_fwd(args, torch, np):
             r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
         if ev:
             ev[1].record(stream)
-        r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
+        if into:
+            r2 = L.hla_scan_into(ctypes.byref(p), ctypes.byref(st), ctypes.byref(st_pre), None, ptr(ws),
+                                 ctypes.c_size_t(ws_bytes), sp)
+        else:
+            r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
         if ev:
             ev[2].record(stream)
         if p_bytes:
-            r3 = L.hla_fwd_output_from_p(ctypes.byref(p), ptr(q), ptr(v), ptr(plocal), ctypes.byref(st),
+            r3 = L.hla_fwd_output_from_p(ctypes.byref(p), ptr(q), ptr(v), ptr(plocal), ctypes.byref(st_out),
                                          ptr(o), ptr(den), sp)
         else:
-            r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), ptr(o),
+            r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st_out), ptr(o),
                                   ptr(den), None, ctypes.c_size_t(0), sp)
         if ev:
             ev[3].record(stream)
@@ -256,7 +271,7 @@ def bench_fwd(args, torch, np):
     # place of k (bf16, 64-token tiles)
     kernels = {
         name_s: dict(ms=sum(k1) / len(k1), bytes=io_bytes + summ_bytes + p_bytes),
-        "hla_scan": dict(ms=sum(k2) / len(k2), bytes=None),
+        name_scan: dict(ms=sum(k2) / len(k2), bytes=None),
         name_o: dict(ms=sum(k3) / len(k3),
                      bytes=io_bytes - (tokens * d * es if p_bytes else 0) + p_bytes + prefix_bytes
                      + tokens * dv * 4 + (tokens * 4 if den is not None else 0)),
@@ -279,7 +294,7 @@ def bench_fwd(args, torch, np):
                    "normalize": cfg["normalize"],
                    "path": (f"hla_fwd's plan: {name_s} over spans of {R} chunk(s) "
                             f"({span} tokens; each workgroup forms its chunks' summaries and "
-                            f"combines them in order), hla_scan over the {n} span totals per "
+                            f"combines them in order), {name_scan} over the {n} span totals per "
                             f"(b, h), {name_o} walking each span from its prefix")},
         "mfma_credited": {"flops_per_token": round(f_tok), "credit_chunk": cfg["credit_chunk"],
                           "tflops": round(value * f_tok / 1e12, 1),

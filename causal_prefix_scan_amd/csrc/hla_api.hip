@@ -138,8 +138,11 @@ size_t scan_ws_bytes(const hla_problem* p) {
   return hla::scan_workspace_floats(z.units, (int)z.n, p->d, p->dv) * 4;
 }
 
+// The exclusive scan of `inout`'s segments, in place; with prefix_out the
+// prefixes go there instead and `inout` is only read (where
+// hla::scan_prefix_out_supported holds).
 hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state* total,
-                   void* ws, hipStream_t s) {
+                   void* ws, hipStream_t s, const hla_state* prefix_out = nullptr) {
   const Sizes z = sizes_of(p);
   hla::ScanPlan a;
   a.S = inout->S; a.C = inout->C; a.m = inout->m; a.G = inout->G; a.h = inout->h;
@@ -151,6 +154,10 @@ hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state
   a.gamma = p->gamma;
   a.units = (int)z.units; a.H = p->H; a.n = (int)z.n; a.chunk = p->chunk;
   a.d = p->d; a.dv = p->dv;
+  if (prefix_out) {
+    a.oS = prefix_out->S; a.oC = prefix_out->C; a.om = prefix_out->m;
+    a.oG = prefix_out->G; a.oh = prefix_out->h;
+  }
   return from_hip(hla::launch_scan(a, s));
 }
 
@@ -267,6 +274,45 @@ hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_stat
   if (empty_problem(p)) return HLA_OK;
   if (hla_status e = device_ready()) return e;
   return do_scan(p, inout, total_out, workspace, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return HLA_ERR_HIP;
+}
+
+hla_status hla_scan_into(const hla_problem* p, const hla_state* summaries,
+                         const hla_state* prefixes_out, const hla_state* total_out, void* workspace,
+                         size_t workspace_bytes, void* stream) try {
+  if (hla_status e = check_problem(p)) return e;
+  if (empty_problem(p)) return HLA_OK;
+  const Sizes z = sizes_of(p);
+  if (!hla::scan_prefix_out_supported((int)z.n, p->d, p->dv)) return HLA_ERR_UNSUPPORTED;
+  if (hla_status e = check_state(summaries, true, z.units * z.n, z, nullptr, nullptr, 0)) return e;
+  const size_t per[5] = {z.S * 4, z.C * 4, z.m * 4, z.C * 4, z.m * 4};
+  const void* ins[5] = {summaries->S, summaries->C, summaries->m, summaries->G, summaries->h};
+  size_t inb[5];
+  for (int j = 0; j < 5; ++j) inb[j] = z.units * z.n * per[j];
+  if (hla_status e = check_state(prefixes_out, true, z.units * z.n, z, ins, inb, 5)) return e;
+  const void* outs[5] = {prefixes_out->S, prefixes_out->C, prefixes_out->m, prefixes_out->G,
+                         prefixes_out->h};
+  if (total_out) {
+    const void* both[10];
+    size_t bb[10];
+    for (int j = 0; j < 5; ++j) {
+      both[j] = ins[j]; bb[j] = inb[j];
+      both[5 + j] = outs[j]; bb[5 + j] = inb[j];
+    }
+    if (hla_status e = check_state(total_out, false, z.units, z, both, bb, 10)) return e;
+  }
+  const size_t need = scan_ws_bytes(p);
+  if (workspace_bytes < need) return HLA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0) {
+    if (!workspace) return HLA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
+    for (int j = 0; j < 5; ++j)
+      if (overlap(workspace, need, ins[j], inb[j]) || overlap(workspace, need, outs[j], inb[j]))
+        return HLA_ERR_ALIASING;
+  }
+  if (hla_status e = device_ready()) return e;
+  return do_scan(p, summaries, total_out, workspace, static_cast<hipStream_t>(stream), prefixes_out);
 } catch (...) {
   return HLA_ERR_HIP;
 }
@@ -507,7 +553,21 @@ hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const
   hla_state sm;
   sm.S = w; sm.C = sm.S + cnt * z.S; sm.m = sm.C + cnt * z.C; sm.G = sm.m + cnt * z.m;
   sm.h = sm.G + cnt * z.C;
-  void* scan_ws = sm.h + cnt * z.m;
+  float* scan_ws = sm.h + cnt * z.m;
+  // With spans of several chunks the workspace (sized for one summary per
+  // chunk) has room past the span summaries and the scan's scratch for the
+  // prefixes, which the scan then forms in one launch (at d = dv <= 64)
+  hla_state po{};
+  const hla_state* prefix_out = nullptr;
+  float* const po0 = scan_ws + scan_ws_bytes(&ps) / 4;
+  const size_t po_bytes = cnt * (z.S + 2 * z.C + 2 * z.m) * 4;
+  if (hla::scan_prefix_out_supported((int)z.n, p->d, p->dv) &&
+      (size_t)(reinterpret_cast<char*>(po0) - static_cast<char*>(workspace)) + po_bytes <=
+          hla_fwd_workspace_bytes(p)) {
+    po.S = po0; po.C = po.S + cnt * z.S; po.m = po.C + cnt * z.C; po.G = po.m + cnt * z.m;
+    po.h = po.G + cnt * z.C;
+    prefix_out = &po;
+  }
   // the segment-local p after the summaries and the scan's scratch, when the
   // workspace holds it: the output kernel then carries no S recurrence
   void* plocal = fwd_used_bytes(p, workspace_bytes) > hla_fwd_workspace_bytes(p)
@@ -517,7 +577,8 @@ hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const
   a1.pl = plocal;
   if (hla_status e = from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))
     return e;
-  if (hla_status e = do_scan(&ps, &sm, final_state, scan_ws, s)) return e;
+  if (hla_status e = do_scan(&ps, &sm, final_state, scan_ws, s, prefix_out)) return e;
+  if (prefix_out) sm = po;
   ChunkArgs a3 = chunk_args(&ps, q, k, v, &sm, o, den);
   if (plocal) {
     a3.pl = plocal;

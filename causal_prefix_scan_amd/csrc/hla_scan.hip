@@ -256,6 +256,8 @@ struct RunArgs {
   float *S, *C, *m, *G, *h;        // segments [units, n, ...]
   float *aS, *aC, *am, *aG, *ah;   // run totals / exclusive run prefixes [units, runs, ...]
   float *tS, *tC, *tm, *tG, *th;   // inclusive totals [units, ...], each may be nullptr
+  float *oS, *oC, *om, *oG, *oh;   // exclusive prefixes [units, n, ...] (side-by-side rescan
+                                   // with its prefixes out of place), else nullptr
   const float* gamma;
   int H, n, R, runs, chunk, units;
   int from_prefix;                 // rescan starts from a*[run] (else from the identity)
@@ -531,17 +533,27 @@ __global__ __launch_bounds__(256) void run_cm_kernel(RunArgs a) {
 // m's prefixes are formed across the slots in LDS, each wave forms its X
 // block (and y rows in the column block 0 workgroups) on fp32 MFMA, and the G
 // (h) prefixes are formed across the slots and written in place.  S, C and m
-// are only read here (every workgroup of the run reads them);
-// run_cm_kernel<.., true> rewrites them afterwards.  The workgroups of one
-// (unit, run) share blockIdx.x mod 8, i.e. one XCD and its L2.
-template <int D, int E, int RM>
-__global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
+// are only read here (every workgroup of the run reads them), so in place
+// run_cm_kernel<.., true> rewrites them afterwards.  With PO (d = dv) every
+// prefix goes to arrays of their own instead, the segments are only read,
+// and this launch is the whole rescan: the workgroup of (row block, column
+// block) writes that block of G's and C's prefixes (its rows of the column
+// block it forms anyway), of S's (its slot's block staged in LDS once the
+// products are done) and, in the column block 0 workgroups, its rows of h's
+// and m's.  The workgroups of one (unit, run) share blockIdx.x mod 8, i.e.
+// one XCD and its L2.
+template <int D, int E, int RM, bool PO>
+// (at most 64 VGPRs: two 16-wave workgroups per CU)
+__global__ __launch_bounds__(64 * RM) __attribute__((amdgpu_waves_per_eu(8))) void run_flat_kernel(RunArgs a) {
+  static_assert(!PO || (D == E && RM == 16), "prefixes out of place: d = dv, 16 waves");
   constexpr int NT = 64 * RM, DT = D / 16, NCB = E / 16, NP = (D / 16) * NCB;
   constexpr int LC = D + 4;   // floats per column of a slot's C block
+  constexpr int SO = 272;     // (PO) the slot's S block, after X and y
+  constexpr int SLOT = PO && 16 * LC < SO + 256 ? SO + 256 : 16 * LC;
   // slot w: the C block's prefix, then (once wave w has read it) X's block in
   // its first 256 floats and y in the next 16; only wave w touches its slot
   // between the barriers
-  __shared__ __attribute__((aligned(16))) float sC[RM][16 * LC];
+  __shared__ __attribute__((aligned(16))) float sC[RM][SLOT];
   __shared__ float sm[RM][D];
 
   const int bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
@@ -559,6 +571,7 @@ __global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
   const float al = gpow(g, log2f(g), a.chunk), al2 = al * al;
   const size_t pr = (size_t)unit * a.runs + run;
   const size_t sl = (size_t)unit * a.n + k0 + w;
+  const bool last = run == a.runs - 1;
 
   // 1. this wave's segment: C column block (rows 16 t + 4 lg4 + j, column
   // c0 + lr), S rows r0 + lr as the A operand (columns 16 c + 4 lg4 .. + 3),
@@ -601,20 +614,26 @@ __global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
 #pragma unroll
     for (int s = 0; s < RM; ++s) {
       sC[s][col * LC + row] = p;
-      p = p * al + v[s];
+      const float nx = p * al + v[s];
+      p = !PO || s < len ? nx : p;   // (PO) the run's total stops at its end
     }
+    if (PO && last && a.tC && (row >> 4) == rb) a.tC[(size_t)unit * D * E + (size_t)row * E + c0 + col] = p;
   }
   if (hw) {
     for (int e = tid; e < D; e += NT) {
       float p = a.from_prefix ? a.am[pr * D + e] : 0.f;
+      const bool mine = PO && (e >> 4) == rb;
       float v[RM];
 #pragma unroll
       for (int s = 0; s < RM; ++s) v[s] = sm[s][e];
 #pragma unroll
       for (int s = 0; s < RM; ++s) {
         sm[s][e] = p;
-        p = p * al + v[s];
+        if (mine && s < len) a.om[((size_t)unit * a.n + k0 + s) * D + e] = p;
+        const float nx = p * al + v[s];
+        p = !PO || s < len ? nx : p;
       }
+      if (mine && last && a.tm) a.tm[(size_t)unit * D + e] = p;
     }
   }
   __syncthreads();
@@ -624,6 +643,16 @@ __global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
     f32x4 cp[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) cp[t] = *reinterpret_cast<const f32x4*>(&sC[w][lr * LC + 16 * t + 4 * lg4]);
+    if constexpr (PO) {
+      // this slot's C prefix, rows r0 + 4 lg4 + j of column c0 + lr
+      f32x4 cb4 = cp[0];
+#pragma unroll
+      for (int t = 1; t < DT; ++t)
+        if (t == rb) cb4 = cp[t];
+      float* pc = a.oC + sl * D * E + c0 + lr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pc[(size_t)(r0 + 4 * lg4 + j) * E] = cb4[j];
+    }
     f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
     for (int kk = 0; kk < D / 4; ++kk) {
@@ -644,10 +673,41 @@ __global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
     }
   }
   __syncthreads();
+  if constexpr (PO) {
+    // every wave has read its C prefix: the slot's S block (rows r0 + lr,
+    // columns c0 + 4 lg4 + j) goes after X and y
+    if (live) {
+      f32x4 sb = xS[0];
+#pragma unroll
+      for (int t = 1; t < DT; ++t)
+        if (t == cb) sb = xS[t];
+      *reinterpret_cast<f32x4*>(&sC[w][SO + 16 * lr + 4 * lg4]) = sb;
+    }
+    __syncthreads();
+    // exclusive prefixes of the S block across the run, on threads 256..511
+    // (those of G on 0..255 and of h on 512..527 below, at the same time)
+    if (tid >= 256 && tid < 512) {
+      const int e = tid - 256, row = e >> 4, col = e & 15;
+      const size_t so = (size_t)(r0 + row) * D + c0 + col;
+      float p = a.from_prefix ? a.aS[pr * D * D + so] : 0.f;
+      float v[RM], o[RM];
+#pragma unroll
+      for (int s = 0; s < RM; ++s) v[s] = sC[s][SO + e];
+#pragma unroll
+      for (int s = 0; s < RM; ++s) {
+        o[s] = p;
+        if (s < len) p = p * al + v[s];
+      }
+      float* pS = a.oS + ((size_t)unit * a.n + k0) * D * D + so;
+#pragma unroll
+      for (int s = 0; s < RM; ++s)
+        if (s < len) pS[(size_t)s * D * D] = o[s];
+      if (last && a.tS) a.tS[(size_t)unit * D * D + so] = p;
+    }
+  }
 
   // 4. exclusive prefixes of the G block and of h across the run, in place;
   // the last run's inclusive totals
-  const bool last = run == a.runs - 1;
   for (int e = tid; e < 256; e += NT) {
     const int row = e >> 4, col = e & 15;
     const int li = 4 * (16 * (row >> 2) + col) + (row & 3);   // lane 16 (row/4) + col, element row % 4
@@ -661,27 +721,28 @@ __global__ __launch_bounds__(64 * RM) void run_flat_kernel(RunArgs a) {
       o[s] = p;
       if (s < len) p = p * al2 + v[s];
     }
-    float* pG = a.G + ((size_t)unit * a.n + k0) * D * E + go;
+    float* pG = (PO ? a.oG : a.G) + ((size_t)unit * a.n + k0) * D * E + go;
 #pragma unroll
     for (int s = 0; s < RM; ++s)
       if (s < len) pG[(size_t)s * D * E] = o[s];
     if (last && a.tG) a.tG[(size_t)unit * D * E + go] = p;
   }
-  if (hw && tid < 16) {
-    float p = a.from_prefix ? a.ah[pr * D + r0 + tid] : 0.f;
+  const int ht = PO ? tid - 512 : tid;
+  if (hw && ht >= 0 && ht < 16) {
+    float p = a.from_prefix ? a.ah[pr * D + r0 + ht] : 0.f;
     float v[RM], o[RM];
 #pragma unroll
-    for (int s = 0; s < RM; ++s) v[s] = sC[s][256 + tid];
+    for (int s = 0; s < RM; ++s) v[s] = sC[s][256 + ht];
 #pragma unroll
     for (int s = 0; s < RM; ++s) {
       o[s] = p;
       if (s < len) p = p * al2 + v[s];
     }
-    float* ph = a.h + ((size_t)unit * a.n + k0) * D + r0 + tid;
+    float* ph = (PO ? a.oh : a.h) + ((size_t)unit * a.n + k0) * D + r0 + ht;
 #pragma unroll
     for (int s = 0; s < RM; ++s)
       if (s < len) ph[(size_t)s * D] = o[s];
-    if (last && a.th) a.th[(size_t)unit * D + r0 + tid] = p;
+    if (last && a.th) a.th[(size_t)unit * D + r0 + ht] = p;
   }
 }
 
@@ -690,6 +751,10 @@ int scan_run_length(int n) {
   int r = 1;
   while (r * r < n) r *= 2;
   return r;
+}
+
+bool scan_prefix_out_supported(int n, int d, int dv) {
+  return d == dv && (d == 16 || d == 32 || d == 64) && scan_run_length(n) <= 16;
 }
 
 size_t scan_workspace_floats(int64_t units, int n, int d, int dv) {
@@ -717,9 +782,12 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   constexpr int NRB = D / 16, VEC = (D * D + 2 * D * E + 2 * D) / 4;
   constexpr int NRR = D / (16 * RunRT<D>::value);   // row blocks of the run kernels
   const int units = p.units;
+  if (p.oS && (p.rS || !p.oC || !p.om || !p.oG || !p.oh || !scan_prefix_out_supported(p.n, D, E)))
+    return hipErrorInvalidValue;
   RunArgs r;
   r.S = p.S; r.C = p.C; r.m = p.m; r.G = p.G; r.h = p.h;
   r.tS = p.tS; r.tC = p.tC; r.tm = p.tm; r.tG = p.tG; r.th = p.th;
+  r.oS = p.oS; r.oC = p.oC; r.om = p.om; r.oG = p.oG; r.oh = p.oh;
   r.gamma = p.gamma; r.H = p.H; r.n = p.n; r.chunk = p.chunk; r.units = units;
   r.R = scan_run_length(p.n);
   r.runs = (p.n + r.R - 1) / r.R;
@@ -795,10 +863,16 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
       // 17 us and 32 -> 25 us; at d = 128, 4 segments per head, the walk below
       // stays faster: 37 against 56 us)
       constexpr int NP = (D / 16) * (E / 16);
+      if constexpr (D == E) {
+        if (r.oS) {   // one launch: the prefixes of S, C and m out of place
+          hipLaunchKernelGGL((run_flat_kernel<D, E, 16, true>), dim3(groups8 * NP), dim3(1024), 0, s, r);
+          return hipGetLastError();
+        }
+      }
       if (r.R <= 4)
-        hipLaunchKernelGGL((run_flat_kernel<D, E, 4>), dim3(groups8 * NP), dim3(256), 0, s, r);
+        hipLaunchKernelGGL((run_flat_kernel<D, E, 4, false>), dim3(groups8 * NP), dim3(256), 0, s, r);
       else
-        hipLaunchKernelGGL((run_flat_kernel<D, E, 16>), dim3(groups8 * NP), dim3(1024), 0, s, r);
+        hipLaunchKernelGGL((run_flat_kernel<D, E, 16, false>), dim3(groups8 * NP), dim3(1024), 0, s, r);
       if (hipError_t e = hipGetLastError()) return e;
       constexpr int VSCM = (D * D + D * E + D) / 4;
       hipLaunchKernelGGL((run_cm_kernel<D, E, true>), dim3((unsigned)(cnt * ((VSCM + 255) / 256))),

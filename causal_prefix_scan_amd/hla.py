@@ -23,7 +23,8 @@ STATUS = {
 
 EXPORTS = (
     "hla_status_string", "hla_version", "hla_fwd_chunk_summaries", "hla_scan_workspace_bytes",
-    "hla_scan", "hla_scan_run_length", "hla_scan_runs_workspace_bytes", "hla_scan_runs",
+    "hla_scan", "hla_scan_into", "hla_scan_run_length", "hla_scan_runs_workspace_bytes",
+    "hla_scan_runs",
     "hla_fwd_span_chunks",
     "hla_fwd_output_workspace_bytes", "hla_fwd_output", "hla_fwd_workspace_bytes",
     "hla_fwd_p_bytes", "hla_fwd_chunk_summaries_p", "hla_fwd_output_from_p",
@@ -90,6 +91,7 @@ def lib():
     L.hla_fwd_chunk_summaries.argtypes = [pp, vp, vp, vp, ps, vp]
     L.hla_scan_workspace_bytes.argtypes, L.hla_scan_workspace_bytes.restype = [pp], sz
     L.hla_scan.argtypes = [pp, ps, ps, vp, sz, vp]
+    L.hla_scan_into.argtypes = [pp, ps, ps, ps, vp, sz, vp]
     L.hla_scan_run_length.argtypes, L.hla_scan_run_length.restype = [pp], i32
     L.hla_fwd_span_chunks.argtypes, L.hla_fwd_span_chunks.restype = [pp], i32
     L.hla_scan_runs_workspace_bytes.argtypes, L.hla_scan_runs_workspace_bytes.restype = [pp], sz
@@ -238,6 +240,27 @@ def scan(summaries, q_shape, dv, chunk, dtype_code, gamma=None, want_total=False
                           ctypes.byref(tt) if tt is not None else None,
                           _ptr(ws), ctypes.c_size_t(nbytes), _stream()), "hla_scan")
     return total
+
+
+def scan_into(summaries, q_shape, dv, chunk, dtype_code, gamma=None, want_total=False,
+              prefixes=None):
+    """hla_scan_into: the exclusive prefixes of `summaries` (only read) in a
+    new state dict (or `prefixes`); returns (prefixes, inclusive total or None)."""
+    torch = _torch()
+    B, H, T, d = q_shape
+    p = Problem(B, H, T, d, dv, int(chunk), dtype_code, 0, 0.0,
+                None if gamma is None else gamma.data_ptr())
+    dev = summaries["S"].device
+    if prefixes is None:
+        prefixes = alloc_state((B, H, T // int(chunk)), d, dv, dev)
+    total = alloc_state((B, H), d, dv, dev) if want_total else None
+    nbytes = lib().hla_scan_workspace_bytes(ctypes.byref(p))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st, po, tt = _state_struct(summaries), _state_struct(prefixes), _state_struct(total)
+    _check(lib().hla_scan_into(ctypes.byref(p), ctypes.byref(st), ctypes.byref(po),
+                               ctypes.byref(tt) if tt is not None else None,
+                               _ptr(ws), ctypes.c_size_t(nbytes), _stream()), "hla_scan_into")
+    return prefixes, total
 
 
 def scan_run_length(T, chunk):

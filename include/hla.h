@@ -137,6 +137,23 @@ size_t hla_scan_workspace_bytes(const hla_problem* p);
 hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_state* total_out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The exclusive scan of hla_scan (method section 4, as above) out of place:
+ * `summaries` (as hla_fwd_chunk_summaries writes them) is only read, and
+ * `prefixes_out` ([B, H, n, ...], all fields required, overlapping neither
+ * `summaries` nor `workspace`) receives what hla_scan would leave in `inout`,
+ * bit for bit.  With the segments left alone the whole rescan of a run is one
+ * launch: the segments of a run are taken side by side and every prefix is
+ * written where no other workgroup still reads it.  Built for d = dv in
+ * {16, 32, 64} with runs of at most 16 segments (hla_scan_run_length(p) <=
+ * 16, i.e. n <= 256); other problems return HLA_ERR_UNSUPPORTED (use
+ * hla_scan).  total_out, workspace (hla_scan_workspace_bytes(p) bytes) and the
+ * remaining errors as for hla_scan.
+ */
+hla_status hla_scan_into(const hla_problem* p, const hla_state* summaries,
+                         const hla_state* prefixes_out, const hla_state* total_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Segments per run of the blocked scan: n when n <= 16, else the smallest
  * power of two R with R*R >= n (n = T / chunk).  Host-only; 0 for an
  * invalid problem. */

@@ -209,6 +209,33 @@ def test_run_prefix_scan_sizes_and_checks(L):
                            0x7000000000, 1 << 20, None) == ALIAS
 
 
+def test_out_of_place_scan_checks(L):
+    pre = state(base=0x7100000000)
+    # built for d = dv in {16, 32, 64} with runs of at most 16 segments
+    for kw in (dict(d=128, dv=128), dict(d=64, dv=32), dict(d=32, dv=64),
+               dict(T=512 * 16, chunk=16)):   # n = 512: runs of 32
+        p = problem(**kw)
+        assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(pre), None,
+                               None, 0, None) == UNSUP, kw
+    p = problem()
+    assert L.hla_scan_into(ctypes.byref(p), None, ctypes.byref(pre), None, None, 0, None) == NULLP
+    assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), None, None, None, 0, None) == NULLP
+    # prefixes over the summaries, or a total over the prefixes
+    assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(state()), None,
+                           None, 0, None) == ALIAS
+    assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(pre),
+                           ctypes.byref(pre), None, 0, None) == ALIAS
+    # n = 64: four runs of 16, whose totals need scratch
+    p = problem(T=64 * 64)
+    assert L.hla_scan_workspace_bytes(ctypes.byref(p)) > 0
+    assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(pre), None,
+                           0x7000000000, 16, None) == WS
+    if no_gpu():
+        p = problem()
+        assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(pre), None,
+                               None, 0, None) == HIP
+
+
 def test_empty_problem_is_a_no_op(L):
     for kw in (dict(T=0), dict(B=0), dict(H=0)):
         assert summaries(L, problem(**kw)) == OK

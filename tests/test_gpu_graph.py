@@ -28,6 +28,7 @@ def gpu():
 FWD_CASES = [
     (1, 2, 2048, 128, 128, 512, "bf16", True, False),   # segment-local p path, 4 segments
     (1, 2, 1024, 64, 64, 64, "bf16", False, True),      # spans of chunks, ratio-normalised
+    (2, 8, 1024, 64, 64, 16, "bf16", True, True),       # spans of 4 chunks: the one-launch rescan
     (1, 1, 256, 16, 16, 32, "f32", True, True),         # fp32, 8 segments
 ]
 
