@@ -18,9 +18,10 @@
 //     moments: X = a X_A + X_B,
 //     R = a^3 R_A + R_B + a S_A Z_B + M P_A,  r = a^3 r_A + r_B + a S_A z_B + M m_A,
 //     M = a^2 S_A Q_B + a V_B   (the segment map, applied to P_A and m_A).
-// The exclusive scan walks each unit's segments in order: the moments by an
-// elementwise decayed running sum, then R and r by the combine above with
-// the moments' prefixes in place of the running S_A, P_A, m_A.
+// The exclusive scan: the moments by an elementwise decayed running sum over
+// each unit's segments; then every segment's own term of R's and r's combine
+// at once (the moments' prefixes in place of S_A, P_A, m_A), and an
+// elementwise decayed running sum of those terms.
 //
 // The m, z, r and unit-channel arrays are kept as [.., d][16] with the value
 // in column 0 (the layout of a first-order sum whose value operand is 16
@@ -62,180 +63,172 @@ __global__ __launch_bounds__(256) void moments_scan_kernel(float* x, float* tota
   if (total) total[(size_t)unit * elems + e] = run;
 }
 
-// R and r through the segments of one unit, one workgroup per (unit, block
-// of 16 rows), four waves.  On entry R, r hold the segment summaries; on exit
-// their exclusive prefixes (each step reads its segment's rows before writing
-// the prefix over them).  Sp, Pp, mp: the moments' exclusive prefixes; Q, V,
-// Z, z: the segments' summaries.  All products on fp32 MFMA.  Per segment:
-// the 16 rows of S_A go to registers in the A-operand layout; Q_B is staged
-// in LDS with 16-byte loads and the map's rows M = a^2 S_A Q_B + a V_B are
-// formed; then Z_B (in Q_B's buffer) and P_A are staged and the R rows take
-// a S_A Z_B + M P_A.  The staged matrices' rows are padded by 16 floats, which
-// makes the MFMA B-operand reads (four rows of 16 columns) hit distinct banks.
-// blockIdx.x is laid out so that the row blocks of one unit share blockIdx.x
-// mod 8 and so run on one XCD, whose L2 then serves the Q_B, Z_B and P_A they
-// all read (with consecutive numbering each of them fetched its own copy).
+// The R and r terms of every segment at once.  Over a unit's segments the
+// exclusive prefixes obey
+//     R_P(k+1) = a^3 R_P(k) + X_k,   X_k = R_k + a S_P(k) Z_k + M_k P_P(k),
+//     M_k = a^2 S_P(k) Q_k + a V_k   (r likewise with z_k and m_P(k)),
+// so once the moments' prefixes are known no X_k waits for another: one
+// workgroup per (unit, segment) forms X_k and x_k in place of R_k and r_k,
+// and r_prefix_kernel then turns them into the prefixes by an elementwise
+// decayed running sum.  Segment 0 has zero prefixes, so X_0 = R_0 (nothing to
+// do).  Wave w owns rows 16 w .. 16 w + 15.  Z_k, then Q_k, share one LDS
+// buffer and P_P(k) has its own, so every operand matrix is read from HBM
+// once per segment and shared by all waves; the staged rows are padded by 16
+// floats, which makes the fp32 MFMA reads of four rows of 16 columns hit
+// distinct banks.  Every product is formed transposed (the staged matrix as
+// the A operand, the wave's S_P rows as the B operand): a lane then holds
+// four adjacent columns of one row, so M's transposed block is already the
+// operand of M P_P(k) (its K order 16 c + 4 (lane / 16) + jj is the one P_P(k)
+// is read in), and X's rows are read and written 16 bytes at a time.  All
+// products on fp32 MFMA.
 template <int D, int E>
-__global__ __launch_bounds__(256) void r_scan_kernel(R3ScanArgs a) {
-  constexpr int NT = 256, LQ = D + 16, LZ = E + 16, LS = D + 4;
-  constexpr int BQ = (D * LQ > D * LZ) ? D * LQ : D * LZ;
-  __shared__ __attribute__((aligned(16))) float bQZ[BQ];      // Q_B, then Z_B
-  __shared__ __attribute__((aligned(16))) float bP[D * LZ];   // P_A
-  __shared__ float Mk[16 * LS];                                // the map's 16 rows
-  __shared__ float rrun[16];
-  constexpr int nrb = D / 16;
-  const int bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
-  const int unit = xcd + 8 * (qb / nrb), rb = qb % nrb, r0 = 16 * rb;
-  if (unit >= a.units) return;
+__global__ __launch_bounds__(4 * D) void r_x_kernel(R3ScanArgs a) {
+  constexpr int NT = 4 * D, LQ = D + 16, LZ = E + 16;
+  constexpr int BA = (D * LQ > D * LZ) ? D * LQ : D * LZ;
+  __shared__ __attribute__((aligned(16))) float bA[BA];      // Z_k, then Q_k
+  __shared__ __attribute__((aligned(16))) float bP[D * LZ];  // P_P(k)
+  const int unit = blockIdx.x / a.nseg, s = blockIdx.x - unit * a.nseg;
+  if (s == 0) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int r0 = 16 * wave;
   const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
-  const float a1 = gpow(g, log2f(g), a.seg), a2 = a1 * a1, a3 = a2 * a1;
-  constexpr int NCE = (E / 16 + 3) / 4;   // column blocks of R per wave
-  constexpr int NCD = (D / 16 + 3) / 4;   // column blocks of the map per wave
+  const float a1 = gpow(g, log2f(g), a.seg), a2 = a1 * a1;
   constexpr int KD = D / 4;               // K steps of a product over D
-  f32x4 Rrun[NCE];
-#pragma unroll
-  for (int i = 0; i < NCE; ++i) Rrun[i] = zero4();
-  if (tid < 16) rrun[tid] = 0.f;
-  const int row = tid >> 4, part = tid & 15;   // the r update: 16 lanes per row
+  constexpr int CD = D / 16, CE = E / 16;  // column blocks of the map and of R
+  const size_t us = (size_t)unit * a.nseg + s;
+  const float* SA = a.Sp + us * D * D + (size_t)r0 * D;     // 16 rows of S_P(k)
+  const float* QB = a.Q + us * D * D;
+  const float* VB = a.V + us * D * D + (size_t)r0 * D;
+  const float* ZB = a.Z + us * D * E;
+  const float* PA = a.Pp + us * D * E;
+  const float* mA = a.mp + us * D * a.ldm;
+  const float* zB = a.z + us * D * a.ldm;
+  float* RB = a.R + us * D * E + (size_t)r0 * E;
+  float* rB = a.r + us * D * a.ldm + (size_t)r0 * a.ldm;
+
   // a row-major [D][W] fp32 matrix: loads to registers (16 bytes per thread
   // and load), then stores to LDS with row stride LW
-  constexpr int PQ = (D * D / 4 + NT - 1) / NT, PZ = (D * E / 4 + NT - 1) / NT;
   auto load_mat = [&](const float* src, f32x4* x, auto Wc) {
-    constexpr int W = decltype(Wc)::value, N4 = D * W / 4, PER = (N4 + NT - 1) / NT;
+    constexpr int W = decltype(Wc)::value, PER = D * W / 4 / NT;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + NT * u;
-      if (i < N4) x[u] = reinterpret_cast<const f32x4*>(src)[i];
-    }
+    for (int u = 0; u < PER; ++u) x[u] = reinterpret_cast<const f32x4*>(src)[tid + NT * u];
   };
   auto store_mat = [&](const f32x4* x, float* dst, auto Wc, auto LWc) {
-    constexpr int W = decltype(Wc)::value, LW = decltype(LWc)::value;
-    constexpr int N4 = D * W / 4, PER = (N4 + NT - 1) / NT;
+    constexpr int W = decltype(Wc)::value, LW = decltype(LWc)::value, PER = D * W / 4 / NT;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int i = tid + NT * u;
-      if (i < N4) {
-        const int rr = i / (W / 4), c4 = i - rr * (W / 4);
-        *reinterpret_cast<f32x4*>(dst + rr * LW + 4 * c4) = x[u];
-      }
+      const int i = tid + NT * u, rr = i / (W / 4), c4 = i - rr * (W / 4);
+      *reinterpret_cast<f32x4*>(dst + rr * LW + 4 * c4) = x[u];
     }
   };
   using DC = std::integral_constant<int, D>;
   using EC = std::integral_constant<int, E>;
   using LQC = std::integral_constant<int, LQ>;
   using LZC = std::integral_constant<int, LZ>;
-  constexpr int NRU = D / 16;   // r update: products per lane
-  for (int s = 0; s < a.nseg; ++s) {
-    const size_t us = (size_t)unit * a.nseg + s;
-    const float* SA = a.Sp + us * D * D + (size_t)r0 * D;     // 16 rows of S_A
-    const float* QB = a.Q + us * D * D;
-    const float* VB = a.V + us * D * D + (size_t)r0 * D;
-    const float* ZB = a.Z + us * D * E;
-    const float* PA = a.Pp + us * D * E;
-    const float* mA = a.mp + us * D * a.ldm;
-    const float* zB = a.z + us * D * a.ldm;
-    float* RB = a.R + us * D * E + (size_t)r0 * E;
-    float* rB = a.r + us * D * a.ldm + (size_t)r0 * a.ldm;
-    // every global read of the segment, issued together: S_A rows as the A
-    // operand (lane: row lr, K slots 4 j + lg), Q_B, Z_B, P_A, V_B's and R_B's
-    // elements of this lane, the r update's operands
-    float sa[KD];
+  constexpr int PQ = D * D / 4 / NT, PZ = D * E / 4 / NT;
+
+  // S_P rows as the B operand (lane: row lr, K slots 4 j + lg); Z_k and
+  // P_P(k) staged in LDS; S_P z_k's part of x
+  float sa[KD];
 #pragma unroll
-    for (int j = 0; j < KD; ++j) sa[j] = SA[(size_t)lr * D + 4 * j + lg];
-    f32x4 xq[PQ], xz[PZ], xp[PZ];
-    load_mat(QB, xq, DC{});
+  for (int j = 0; j < KD; ++j) sa[j] = SA[(size_t)lr * D + 4 * j + lg];
+  {
+    f32x4 xz[PZ], xp[PZ];
     load_mat(ZB, xz, EC{});
     load_mat(PA, xp, EC{});
-    f32x4 vb[NCD], rb4[NCE];
-#pragma unroll
-    for (int i = 0; i < NCD; ++i) {
-      const int cb = wave + 4 * i;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) vb[i][jj] = cb < D / 16 ? VB[(size_t)(4 * lg + jj) * D + 16 * cb + lr] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < NCE; ++i) {
-      const int ce = wave + 4 * i;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rb4[i][j] = ce < E / 16 ? RB[(size_t)(4 * lg + j) * E + 16 * ce + lr] : 0.f;
-    }
-    float su[NRU], zu[NRU], mu[NRU];
-#pragma unroll
-    for (int i = 0; i < NRU; ++i) {
-      const int c = part + 16 * i;
-      su[i] = SA[(size_t)row * D + c];
-      zu[i] = zB[(size_t)c * a.ldm];
-      mu[i] = mA[(size_t)c * a.ldm];
-    }
-    const float rbv = part == 0 ? rB[(size_t)row * a.ldm] : 0.f;
-    store_mat(xq, bQZ, DC{}, LQC{});
-    __syncthreads();
-    // the map's rows: M = a^2 S_A Q_B + a V_B
-#pragma unroll
-    for (int i = 0; i < NCD; ++i) {
-      const int cb = wave + 4 * i;
-      if (cb < D / 16) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int j = 0; j < KD; ++j)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], bQZ[(4 * j + lg) * LQ + 16 * cb + lr], acc, 0, 0, 0);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) Mk[(4 * lg + jj) * LS + 16 * cb + lr] = a2 * acc[jj] + a1 * vb[i][jj];
-      }
-    }
-    __syncthreads();
-    store_mat(xz, bQZ, EC{}, LZC{});
+    store_mat(xz, bA, EC{}, LZC{});
     store_mat(xp, bP, EC{}, LZC{});
-    __syncthreads();
-    // R rows: a^3 R_A + R_B + a S_A Z_B + M P_A; the prefix is R_A
+  }
+  float sz = 0.f;
 #pragma unroll
-    for (int i = 0; i < NCE; ++i) {
-      const int ce = wave + 4 * i;
-      if (ce < E / 16) {
-        f32x4 t1 = zero4(), t2 = zero4();
+  for (int j = 0; j < KD; ++j) sz += sa[j] * zB[(size_t)(4 * j + lg) * a.ldm];
+  const float rbv = lg == 0 ? rB[(size_t)lr * a.ldm] : 0.f;
+  f32x4 xq[PQ];
+  load_mat(QB, xq, DC{});   // in flight during S_P Z_k
+  __syncthreads();
+
+  // (S_P(k) Z_k)^T: lane holds row lr, columns 16 c + 4 lg + jj
+  f32x4 t1[CE];
 #pragma unroll
-        for (int j = 0; j < KD; ++j) {
-          const int kr = 4 * j + lg;
-          t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], bQZ[kr * LZ + 16 * ce + lr], t1, 0, 0, 0);
-          t2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Mk[lr * LS + kr], bP[kr * LZ + 16 * ce + lr], t2, 0, 0, 0);
-        }
+  for (int c = 0; c < CE; ++c) {
+    f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) RB[(size_t)(4 * lg + j) * E + 16 * ce + lr] = Rrun[i][j];
-        Rrun[i] = Rrun[i] * a3 + rb4[i] + t1 * a1 + t2;
+    for (int j = 0; j < KD; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bA[(4 * j + lg) * LZ + 16 * c + lr], sa[j], acc, 0, 0, 0);
+    t1[c] = acc;
+  }
+  __syncthreads();
+  store_mat(xq, bA, DC{}, LQC{});
+  __syncthreads();
+  // the map's rows transposed, M^T = a^2 (S_P(k) Q_k)^T + a V_k^T: lane holds
+  // M[16 w + lr][16 c + 4 lg + jj]
+  f32x4 mt[CD];
+#pragma unroll
+  for (int c = 0; c < CD; ++c) {
+    const f32x4 vb = *reinterpret_cast<const f32x4*>(VB + (size_t)lr * D + 16 * c + 4 * lg);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int j = 0; j < KD; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bA[(4 * j + lg) * LQ + 16 * c + lr], sa[j], acc, 0, 0, 0);
+    mt[c] = acc * a2 + vb * a1;
+  }
+  // X rows = R_k + a t1 + M P_P(k), in place: (M P_P(k))^T with P_P(k)'s rows
+  // taken in M^T's K order (K step 4 c + jj: row 16 c + 4 lg + jj)
+#pragma unroll
+  for (int ce = 0; ce < CE; ++ce) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int c = 0; c < CD; ++c)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bP[(16 * c + 4 * lg + jj) * LZ + 16 * ce + lr], mt[c][jj],
+                                                   acc, 0, 0, 0);
+    f32x4* px = reinterpret_cast<f32x4*>(RB + (size_t)lr * E + 16 * ce + 4 * lg);
+    *px = *px + t1[ce] * a1 + acc;
+  }
+  // x rows = r_k + a S_P(k) z_k + M m_P(k)
+  float mm = 0.f;
+#pragma unroll
+  for (int c = 0; c < CD; ++c)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) mm += mt[c][jj] * mA[(size_t)(16 * c + 4 * lg + jj) * a.ldm];
+  float xr = a1 * sz + mm;
+  xr += __shfl_xor(xr, 16, 64);
+  xr += __shfl_xor(xr, 32, 64);
+  if (lg == 0) rB[(size_t)lr * a.ldm] = rbv + xr;
+}
+
+// R_k, r_k (holding X_k, x_k) become their exclusive prefixes:
+// R_P(k) = sum_{j<k} a^(3(k-1-j)) X_j, elementwise, one thread per element of
+// R and of r (row stride ldm); the inclusive totals to tR, tr when set.
+template <int D, int E>
+__global__ __launch_bounds__(256) void r_prefix_kernel(R3ScanArgs a) {
+  constexpr int ER = D * E, ALL = ER + D, PER = (ALL + 255) / 256;
+  const int unit = blockIdx.x / PER;
+  const int e = (blockIdx.x - unit * PER) * 256 + threadIdx.x;
+  if (e >= ALL) return;
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float a1 = gpow(g, log2f(g), a.seg), a3 = a1 * a1 * a1;
+  const bool isR = e < ER;
+  const size_t stride = isR ? (size_t)ER : (size_t)D * a.ldm;
+  float* p = isR ? a.R + (size_t)unit * a.nseg * ER + e
+                 : a.r + (size_t)unit * a.nseg * D * a.ldm + (size_t)(e - ER) * a.ldm;
+  float run = 0.f;
+  constexpr int NB = 8;   // loads of eight segments in flight
+  for (int s0 = 0; s0 < a.nseg; s0 += NB) {
+    float v[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) v[i] = s0 + i < a.nseg ? p[(size_t)(s0 + i) * stride] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (s0 + i < a.nseg) {
+        p[(size_t)(s0 + i) * stride] = run;
+        run = a3 * run + v[i];
       }
     }
-    // r rows: a^3 r_A + r_B + a S_A z_B + M m_A
-    float sz = 0.f, mm = 0.f;
-#pragma unroll
-    for (int i = 0; i < NRU; ++i) {
-      const int c = part + 16 * i;
-      sz += su[i] * zu[i];
-      mm += Mk[row * LS + c] * mu[i];
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off *= 2) {
-      sz += __shfl_xor(sz, off, 64);
-      mm += __shfl_xor(mm, off, 64);
-    }
-    if (part == 0) {
-      rB[(size_t)row * a.ldm] = rrun[row];
-      rrun[row] = a3 * rrun[row] + rbv + a1 * sz + mm;
-    }
-    __syncthreads();
   }
-  if (a.tR) {
-#pragma unroll
-    for (int i = 0; i < NCE; ++i) {
-      const int ce = wave + 4 * i;
-      if (ce < E / 16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          a.tR[(size_t)unit * D * E + (size_t)(r0 + 4 * lg + j) * E + 16 * ce + lr] = Rrun[i][j];
-      }
-    }
-  }
-  if (a.tr && tid < 16) a.tr[(size_t)unit * D + r0 + tid] = rrun[tid];
+  float* t = isR ? a.tR : a.tr;
+  if (t) t[isR ? (size_t)unit * ER + e : (size_t)unit * D + (e - ER)] = run;
 }
 
 // The unit channel: one[t][0] = 1, one[t][1..15] = 0 (bf16 or fp32).
@@ -420,11 +413,16 @@ hipError_t launch_moments_scan(float* x, float* total, const float* gamma, int H
 }
 
 hipError_t launch_r_scan(int d, int dv, int units, const R3ScanArgs& a, hipStream_t s) {
-  // units rounded up to a multiple of 8 (the XCD-aware numbering); the extra
-  // workgroups return at once
-  const dim3 grid((unsigned)((units + 7) / 8 * 8 * (d / 16)));
-#define HLA_CASE(D, E) \
-  if (d == D && dv == E) { hipLaunchKernelGGL((r_scan_kernel<D, E>), grid, dim3(256), 0, s, a); return hipGetLastError(); }
+  // every segment's X at once, then the elementwise prefixes
+  const dim3 gx((unsigned)units * (unsigned)a.nseg);
+#define HLA_CASE(D, E)                                                                              \
+  if (d == D && dv == E) {                                                                          \
+    hipLaunchKernelGGL((r_x_kernel<D, E>), gx, dim3(4 * D), 0, s, a);                               \
+    if (hipError_t e = hipGetLastError()) return e;                                                 \
+    const unsigned per = (unsigned)((D * E + D + 255) / 256);                                        \
+    hipLaunchKernelGGL((r_prefix_kernel<D, E>), dim3((unsigned)units * per), dim3(256), 0, s, a);   \
+    return hipGetLastError();                                                                       \
+  }
   HLA_CASE(16, 16) HLA_CASE(16, 32) HLA_CASE(32, 16) HLA_CASE(32, 32) HLA_CASE(32, 64)
   HLA_CASE(64, 32) HLA_CASE(64, 64) HLA_CASE(64, 128) HLA_CASE(128, 64) HLA_CASE(128, 128)
 #undef HLA_CASE

@@ -48,6 +48,8 @@ CASES = [
     (1, 2, 256, 128, 64, 256, "bf16", True),    # n = 1
     (1, 1, 192, 32, 32, 48, "f32", True),       # fp32, n = 4, ragged 16
     (1, 2, 600, 64, 128, 200, "bf16", True),    # 3 tiles + ragged 8, d < dv
+    (1, 2, 768, 32, 32, 64, "bf16", True),      # n = 12
+    (1, 1, 576, 128, 128, 64, "bf16", True),    # n = 9 at d = 128 (eight waves per segment)
 ]
 
 
