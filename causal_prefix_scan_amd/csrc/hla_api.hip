@@ -139,8 +139,7 @@ size_t scan_ws_bytes(const hla_problem* p) {
 }
 
 // The exclusive scan of `inout`'s segments, in place; with prefix_out the
-// prefixes go there instead and `inout` is only read (where
-// hla::scan_prefix_out_supported holds).
+// prefixes go there instead and `inout` is only read.
 hla_status do_scan(const hla_problem* p, const hla_state* inout, const hla_state* total,
                    void* ws, hipStream_t s, const hla_state* prefix_out = nullptr) {
   const Sizes z = sizes_of(p);
@@ -200,11 +199,53 @@ size_t fwd_span_p_bytes(const hla_problem* p) {
   return hla::outp_plocal_bytes(sizes_of(p).units, p->T, (int)span, p->d);
 }
 
-// Bytes of a workspace of workspace_bytes that hla_fwd uses: the summaries
-// and the scan's scratch, plus the segment-local p when it fits.
-size_t fwd_used_bytes(const hla_problem* p, size_t workspace_bytes) {
-  const size_t base = hla_fwd_workspace_bytes(p), pb = fwd_span_p_bytes(p);
-  return (pb && workspace_bytes >= align256(base) + pb) ? align256(base) + pb : base;
+// Where hla_fwd keeps what in a workspace of workspace_bytes (byte offsets
+// from its start).  The summaries of the spans and the scan's scratch come
+// first, in the room of hla_fwd_workspace_bytes(p), which is sized for one
+// summary per chunk; then the segment-local p, when the shape has that path
+// and the workspace holds it; the exclusive prefixes go out of place (the
+// scan then forms them without a separate C, m pass) into the rest of that
+// first room when spans of several chunks leave enough of it, else after p
+// when the workspace holds them, else the scan runs in place.
+struct FwdPlan {
+  size_t base;       // hla_fwd_workspace_bytes(p)
+  size_t scan_ws;    // the scan's scratch, after the span summaries
+  size_t p_off;      // the segment-local p, or 0 (none)
+  size_t po_off;     // the out-of-place prefixes, or 0 (scan in place)
+  size_t end;        // bytes used
+};
+
+FwdPlan fwd_plan(const hla_problem* p, size_t workspace_bytes) {
+  FwdPlan f;
+  f.base = hla_fwd_workspace_bytes(p);
+  hla_problem ps = *p;
+  ps.chunk = (int32_t)(p->chunk * fwd_span_chunks(p));
+  const Sizes z = sizes_of(&ps);
+  const size_t cnt = (size_t)z.units * (size_t)z.n;
+  const size_t summ = cnt * (z.S + 2 * z.C + 2 * z.m) * 4;
+  f.scan_ws = summ;
+  const size_t in_base = summ + scan_ws_bytes(&ps);
+  const size_t pb = fwd_span_p_bytes(p);
+  f.p_off = 0;
+  f.end = f.base;
+  if (pb && workspace_bytes >= align256(f.base) + pb) {
+    f.p_off = align256(f.base);
+    f.end = f.p_off + pb;
+  }
+  f.po_off = 0;
+  if (in_base + summ <= f.base) {
+    f.po_off = in_base;
+  } else if (workspace_bytes >= align256(f.end) + summ) {
+    f.po_off = align256(f.end);
+    f.end = f.po_off + summ;
+  }
+  return f;
+}
+
+// The bytes of hla_fwd's fastest plan: the segment-local p where the shape
+// has it, the prefixes out of place.
+size_t fwd_full_bytes(const hla_problem* p) {
+  return fwd_plan(p, ~(size_t)0).end;
 }
 
 }  // namespace
@@ -284,7 +325,6 @@ hla_status hla_scan_into(const hla_problem* p, const hla_state* summaries,
   if (hla_status e = check_problem(p)) return e;
   if (empty_problem(p)) return HLA_OK;
   const Sizes z = sizes_of(p);
-  if (!hla::scan_prefix_out_supported((int)z.n, p->d, p->dv)) return HLA_ERR_UNSUPPORTED;
   if (hla_status e = check_state(summaries, true, z.units * z.n, z, nullptr, nullptr, 0)) return e;
   const size_t per[5] = {z.S * 4, z.C * 4, z.m * 4, z.C * 4, z.m * 4};
   const void* ins[5] = {summaries->S, summaries->C, summaries->m, summaries->G, summaries->h};
@@ -418,8 +458,7 @@ size_t hla_fwd_workspace_bytes(const hla_problem* p) {
 
 size_t hla_fwd_p_workspace_bytes(const hla_problem* p) {
   if (check_problem(p) != HLA_OK || empty_problem(p)) return 0;
-  const size_t base = hla_fwd_workspace_bytes(p), pb = fwd_span_p_bytes(p);
-  return pb ? align256(base) + pb : base;
+  return fwd_full_bytes(p);
 }
 
 size_t hla_fwd_p_bytes(const hla_problem* p) {
@@ -519,7 +558,7 @@ hla_status fwd_validate(const hla_problem* p, const void* q, const void* k, cons
     if (!aligned16(workspace)) return HLA_ERR_MISALIGNED;
   }
   // the part of the workspace the chosen plan uses
-  const size_t need = check_ws ? fwd_used_bytes(p, workspace_bytes) : 0;
+  const size_t need = check_ws ? fwd_plan(p, workspace_bytes).end : 0;
   const void* ins[4] = {q, k, v, workspace};
   const size_t inb[4] = {z.qk_bytes, z.qk_bytes, z.v_bytes, need};
   for (int j = 0; j < 4; ++j) {
@@ -553,26 +592,20 @@ hla_status fwd_enqueue(const hla_problem* p, const void* q, const void* k, const
   hla_state sm;
   sm.S = w; sm.C = sm.S + cnt * z.S; sm.m = sm.C + cnt * z.C; sm.G = sm.m + cnt * z.m;
   sm.h = sm.G + cnt * z.C;
-  float* scan_ws = sm.h + cnt * z.m;
-  // With spans of several chunks the workspace (sized for one summary per
-  // chunk) has room past the span summaries and the scan's scratch for the
-  // prefixes, which the scan then forms in one launch (at d = dv <= 64)
+  const FwdPlan f = fwd_plan(p, workspace_bytes);
+  char* const wb = static_cast<char*>(workspace);
+  void* scan_ws = wb + f.scan_ws;
+  // the exclusive prefixes out of place when the workspace has room for them
   hla_state po{};
   const hla_state* prefix_out = nullptr;
-  float* const po0 = scan_ws + scan_ws_bytes(&ps) / 4;
-  const size_t po_bytes = cnt * (z.S + 2 * z.C + 2 * z.m) * 4;
-  if (hla::scan_prefix_out_supported((int)z.n, p->d, p->dv) &&
-      (size_t)(reinterpret_cast<char*>(po0) - static_cast<char*>(workspace)) + po_bytes <=
-          hla_fwd_workspace_bytes(p)) {
-    po.S = po0; po.C = po.S + cnt * z.S; po.m = po.C + cnt * z.C; po.G = po.m + cnt * z.m;
-    po.h = po.G + cnt * z.C;
+  if (f.po_off) {
+    po.S = reinterpret_cast<float*>(wb + f.po_off); po.C = po.S + cnt * z.S; po.m = po.C + cnt * z.C;
+    po.G = po.m + cnt * z.m; po.h = po.G + cnt * z.C;
     prefix_out = &po;
   }
-  // the segment-local p after the summaries and the scan's scratch, when the
-  // workspace holds it: the output kernel then carries no S recurrence
-  void* plocal = fwd_used_bytes(p, workspace_bytes) > hla_fwd_workspace_bytes(p)
-                     ? static_cast<char*>(workspace) + align256(hla_fwd_workspace_bytes(p))
-                     : nullptr;
+  // the segment-local p, when the workspace holds it: the output kernel then
+  // carries no S recurrence
+  void* plocal = f.p_off ? wb + f.p_off : nullptr;
   ChunkArgs a1 = chunk_args(&ps, q, k, v, &sm, nullptr, nullptr);
   a1.pl = plocal;
   if (hla_status e = from_hip(hla::launch_chunk_summaries(p->in_dtype, p->d, p->dv, (int)z.units, a1, s)))

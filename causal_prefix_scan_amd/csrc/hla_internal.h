@@ -50,10 +50,9 @@ struct ScanPlan {
                                         // scan_runs_workspace_floats(...) with rS
   const float* gamma;
   int units, H, n, chunk, d, dv;
-  // With oS set (only where scan_prefix_out_supported(n, d, dv)): the
-  // exclusive prefixes go to oS, oC, om, oG, oh ([units, n, ...], disjoint
-  // from the segments, all set), the segments are only read, and the whole
-  // rescan is one launch.
+  // With oS set: the exclusive prefixes go to oS, oC, om, oG, oh ([units,
+  // n, ...], disjoint from the segments, all set) and the segments are only
+  // read; the rescan then writes every prefix itself (no separate C, m pass).
   float *oS = nullptr, *oC = nullptr, *om = nullptr, *oG = nullptr, *oh = nullptr;
 };
 
@@ -88,9 +87,6 @@ int scan_run_length(int n);
 size_t scan_workspace_floats(int64_t units, int n, int d, int dv);
 // Scratch of the run-prefix scan: the tree's padding slots only.
 size_t scan_runs_workspace_floats(int64_t units, int n, int d, int dv);
-// Whether a plan may send the prefixes to arrays of their own
-// (ScanPlan::oS): d = dv <= 64 with runs of at most 16 segments.
-bool scan_prefix_out_supported(int n, int d, int dv);
 // Runs the whole exclusive scan (every launch, in order, on stream s).
 hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 

@@ -278,9 +278,14 @@ struct RunRT {
 // Steps 1 (REDUCE) and 3: one workgroup per (unit, run, block of 16 RT rows),
 // E/16 waves; wave w owns column block w of C and G.  blockIdx.x is laid out
 // so that the row blocks of one (unit, run) share blockIdx.x mod 8 and so run
-// on one XCD, where the C and m they all read stay in one L2.
-template <int D, int E, bool REDUCE>
+// on one XCD, where the C and m they all read stay in one L2.  With PO (step 3
+// out of place) every prefix goes to the arrays of RunArgs::oS.. and the
+// segments are only read, so each workgroup also writes its rows of C's and
+// m's prefixes (it carries the whole running C and m) and step 4 is not
+// needed.
+template <int D, int E, bool REDUCE, bool PO>
 __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
+  static_assert(!(REDUCE && PO), "the reduce step writes run totals only");
   constexpr int RT = RunRT<D>::value, RB = 16 * RT;
   constexpr int NW = E / 16, NT = 64 * NW, DT = D / 16, NRB = D / RB, LS = D + 4;
   constexpr int SV = RB * D / 4;            // f32x4 in RB rows of S
@@ -406,18 +411,31 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
       // the segment's own rows become its exclusive prefix: the running state
       // before this segment (the segment itself was read a step earlier)
       const size_t sl = (size_t)unit * a.n + k0 + k;
+      float* const dG = PO ? a.oG : a.G;
+      float* const dS = PO ? a.oS : a.S;
+      float* const dh = PO ? a.oh : a.h;
 #pragma unroll
       for (int q = 0; q < RT; ++q)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          a.G[sl * D * E + (size_t)(r0 + 16 * q + 4 * lg4 + j) * E + 16 * w + lr] = Gb[q][j];
+          dG[sl * D * E + (size_t)(r0 + 16 * q + 4 * lg4 + j) * E + 16 * w + lr] = Gb[q][j];
 #pragma unroll
       for (int i = 0; i < SPT; ++i) {
         const int e = tid + NT * i;
-        if (e < SV) reinterpret_cast<f32x4*>(a.S + sl * D * D + (size_t)r0 * D)[e] = Sb[i];
+        if (e < SV) reinterpret_cast<f32x4*>(dS + sl * D * D + (size_t)r0 * D)[e] = Sb[i];
       }
-      if (hown) a.h[sl * D + r0 + hrow] = hb;
-      if constexpr (CM) {
+      if (hown) dh[sl * D + r0 + hrow] = hb;
+      if constexpr (PO) {
+        // this workgroup's rows of C's and m's prefixes
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          if (16 * t >= r0 && 16 * t < r0 + RB) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              a.oC[sl * D * E + (size_t)(16 * t + 4 * lg4 + j) * E + 16 * w + lr] = Cb[t][j];
+          }
+        if (tid < RB) a.om[sl * D + r0 + tid] = sm[cur][r0 + tid];
+      } else if constexpr (CM) {
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -534,22 +552,24 @@ __global__ __launch_bounds__(256) void run_cm_kernel(RunArgs a) {
 // block (and y rows in the column block 0 workgroups) on fp32 MFMA, and the G
 // (h) prefixes are formed across the slots and written in place.  S, C and m
 // are only read here (every workgroup of the run reads them), so in place
-// run_cm_kernel<.., true> rewrites them afterwards.  With PO (d = dv) every
-// prefix goes to arrays of their own instead, the segments are only read,
-// and this launch is the whole rescan: the workgroup of (row block, column
-// block) writes that block of G's and C's prefixes (its rows of the column
-// block it forms anyway), of S's (its slot's block staged in LDS once the
-// products are done) and, in the column block 0 workgroups, its rows of h's
-// and m's.  The workgroups of one (unit, run) share blockIdx.x mod 8, i.e.
-// one XCD and its L2.
+// run_cm_kernel<.., true> rewrites them afterwards.  With PO every prefix
+// goes to arrays of their own instead, the segments are only read, and this
+// launch is the whole rescan: the workgroup of (row block rb, column block
+// cb) writes that block of G's and C's prefixes (its rows of the column block
+// it forms anyway), S's blocks (rb, cb + k E/16) (its slot's blocks staged in
+// LDS once the products are done) and, in the column block 0 workgroups, its
+// rows of h's and m's.  The workgroups of one (unit, run) share blockIdx.x
+// mod 8, i.e. one XCD and its L2.
 template <int D, int E, int RM, bool PO>
 // (at most 64 VGPRs: two 16-wave workgroups per CU)
 __global__ __launch_bounds__(64 * RM) __attribute__((amdgpu_waves_per_eu(8))) void run_flat_kernel(RunArgs a) {
-  static_assert(!PO || (D == E && RM == 16), "prefixes out of place: d = dv, 16 waves");
+  static_assert(!PO || RM == 16, "prefixes out of place: 16 waves");
   constexpr int NT = 64 * RM, DT = D / 16, NCB = E / 16, NP = (D / 16) * NCB;
   constexpr int LC = D + 4;   // floats per column of a slot's C block
-  constexpr int SO = 272;     // (PO) the slot's S block, after X and y
-  constexpr int SLOT = PO && 16 * LC < SO + 256 ? SO + 256 : 16 * LC;
+  constexpr int NSB = (DT + NCB - 1) / NCB;   // (PO) S blocks per workgroup, at most 2
+  constexpr int SO = 272;     // (PO) the slot's S blocks, after X and y
+  constexpr int SLOT = PO && 16 * LC < SO + 256 * NSB ? SO + 256 * NSB : 16 * LC;
+  static_assert(!PO || 256 + 256 * NSB + 16 <= NT, "threads for the S, G and h walks");
   // slot w: the C block's prefix, then (once wave w has read it) X's block in
   // its first 256 floats and y in the next 16; only wave w touches its slot
   // between the barriers
@@ -674,25 +694,31 @@ __global__ __launch_bounds__(64 * RM) __attribute__((amdgpu_waves_per_eu(8))) vo
   }
   __syncthreads();
   if constexpr (PO) {
-    // every wave has read its C prefix: the slot's S block (rows r0 + lr,
-    // columns c0 + 4 lg4 + j) goes after X and y
+    // every wave has read its C prefix: the slot's S blocks (rows r0 + lr,
+    // columns 16 sb + 4 lg4 + j, sb = cb + NCB i) go after X and y
     if (live) {
-      f32x4 sb = xS[0];
 #pragma unroll
-      for (int t = 1; t < DT; ++t)
-        if (t == cb) sb = xS[t];
-      *reinterpret_cast<f32x4*>(&sC[w][SO + 16 * lr + 4 * lg4]) = sb;
+      for (int i = 0; i < NSB; ++i) {
+        const int sbk = cb + NCB * i;
+        f32x4 sv = xS[0];
+#pragma unroll
+        for (int t = 1; t < DT; ++t)
+          if (t == sbk) sv = xS[t];
+        if (sbk < DT) *reinterpret_cast<f32x4*>(&sC[w][SO + 256 * i + 16 * lr + 4 * lg4]) = sv;
+      }
     }
     __syncthreads();
-    // exclusive prefixes of the S block across the run, on threads 256..511
-    // (those of G on 0..255 and of h on 512..527 below, at the same time)
-    if (tid >= 256 && tid < 512) {
-      const int e = tid - 256, row = e >> 4, col = e & 15;
-      const size_t so = (size_t)(r0 + row) * D + c0 + col;
+    // exclusive prefixes of the S blocks across the run, on threads 256 ..
+    // 256 + 256 NSB - 1 (those of G on 0..255 and of h after the S threads
+    // below, at the same time)
+    const int se = tid - 256, sbk = cb + NCB * (se >> 8);
+    if (se >= 0 && se < 256 * NSB && sbk < DT) {
+      const int row = (se & 255) >> 4, col = se & 15;
+      const size_t so = (size_t)(r0 + row) * D + 16 * sbk + col;
       float p = a.from_prefix ? a.aS[pr * D * D + so] : 0.f;
       float v[RM], o[RM];
 #pragma unroll
-      for (int s = 0; s < RM; ++s) v[s] = sC[s][SO + e];
+      for (int s = 0; s < RM; ++s) v[s] = sC[s][SO + se];
 #pragma unroll
       for (int s = 0; s < RM; ++s) {
         o[s] = p;
@@ -727,7 +753,7 @@ __global__ __launch_bounds__(64 * RM) __attribute__((amdgpu_waves_per_eu(8))) vo
       if (s < len) pG[(size_t)s * D * E] = o[s];
     if (last && a.tG) a.tG[(size_t)unit * D * E + go] = p;
   }
-  const int ht = PO ? tid - 512 : tid;
+  const int ht = PO ? tid - (256 + 256 * NSB) : tid;
   if (hw && ht >= 0 && ht < 16) {
     float p = a.from_prefix ? a.ah[pr * D + r0 + ht] : 0.f;
     float v[RM], o[RM];
@@ -753,9 +779,6 @@ int scan_run_length(int n) {
   return r;
 }
 
-bool scan_prefix_out_supported(int n, int d, int dv) {
-  return d == dv && (d == 16 || d == 32 || d == 64) && scan_run_length(n) <= 16;
-}
 
 size_t scan_workspace_floats(int64_t units, int n, int d, int dv) {
   const int R = scan_run_length(n);
@@ -782,8 +805,7 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   constexpr int NRB = D / 16, VEC = (D * D + 2 * D * E + 2 * D) / 4;
   constexpr int NRR = D / (16 * RunRT<D>::value);   // row blocks of the run kernels
   const int units = p.units;
-  if (p.oS && (p.rS || !p.oC || !p.om || !p.oG || !p.oh || !scan_prefix_out_supported(p.n, D, E)))
-    return hipErrorInvalidValue;
+  if (p.oS && (p.rS || !p.oC || !p.om || !p.oG || !p.oh)) return hipErrorInvalidValue;
   RunArgs r;
   r.S = p.S; r.C = p.C; r.m = p.m; r.G = p.G; r.h = p.h;
   r.tS = p.tS; r.tC = p.tC; r.tm = p.tm; r.tG = p.tG; r.th = p.th;
@@ -817,7 +839,7 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
   }
   const unsigned groups8 = (unsigned)((cnt + 7) / 8 * 8);
   if (r.runs > 1) {
-    hipLaunchKernelGGL((run_rows_kernel<D, E, true>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
+    hipLaunchKernelGGL((run_rows_kernel<D, E, true, false>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
     if (hipError_t e = hipGetLastError()) return e;
     // exclusive Blelloch scan of the run totals; padding slots follow them
     ScanArgs a;
@@ -856,6 +878,19 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
     }
   }
   if (runs_only) return hipSuccess;
+  if (r.oS) {
+    // out of place: the side-by-side rescan (d <= 64, runs of at most 16
+    // segments, as in place) or the walk, each writing every prefix itself
+    if constexpr (D <= 64) {
+      if (r.R <= 16) {
+        hipLaunchKernelGGL((run_flat_kernel<D, E, 16, true>), dim3(groups8 * (D / 16) * (E / 16)), dim3(1024),
+                           0, s, r);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((run_rows_kernel<D, E, false, true>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
+    return hipGetLastError();
+  }
   if constexpr (D <= 64) {
     if (r.R <= 16) {
       // runs of at most 16 segments: the segments of a run side by side, then S,
@@ -863,12 +898,6 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
       // 17 us and 32 -> 25 us; at d = 128, 4 segments per head, the walk below
       // stays faster: 37 against 56 us)
       constexpr int NP = (D / 16) * (E / 16);
-      if constexpr (D == E) {
-        if (r.oS) {   // one launch: the prefixes of S, C and m out of place
-          hipLaunchKernelGGL((run_flat_kernel<D, E, 16, true>), dim3(groups8 * NP), dim3(1024), 0, s, r);
-          return hipGetLastError();
-        }
-      }
       if (r.R <= 4)
         hipLaunchKernelGGL((run_flat_kernel<D, E, 4, false>), dim3(groups8 * NP), dim3(256), 0, s, r);
       else
@@ -880,7 +909,7 @@ static hipError_t run_scan(const ScanPlan& p, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((run_rows_kernel<D, E, false>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
+  hipLaunchKernelGGL((run_rows_kernel<D, E, false, false>), dim3(groups8 * NRR), dim3(64 * (E / 16)), 0, s, r);
   if (hipError_t e = hipGetLastError()) return e;
   if (NRR == 1) return hipSuccess;   // the rescan wrote C and m
   constexpr int VCM = (D * E + D) / 4;

@@ -142,13 +142,11 @@ hla_status hla_scan(const hla_problem* p, const hla_state* inout, const hla_stat
  * `summaries` (as hla_fwd_chunk_summaries writes them) is only read, and
  * `prefixes_out` ([B, H, n, ...], all fields required, overlapping neither
  * `summaries` nor `workspace`) receives what hla_scan would leave in `inout`,
- * bit for bit.  With the segments left alone the whole rescan of a run is one
- * launch: the segments of a run are taken side by side and every prefix is
- * written where no other workgroup still reads it.  Built for d = dv in
- * {16, 32, 64} with runs of at most 16 segments (hla_scan_run_length(p) <=
- * 16, i.e. n <= 256); other problems return HLA_ERR_UNSUPPORTED (use
- * hla_scan).  total_out, workspace (hla_scan_workspace_bytes(p) bytes) and the
- * remaining errors as for hla_scan.
+ * bit for bit.  With the segments left alone, the rescan writes every prefix
+ * itself: in place, C and m of a segment are still read by other workgroups
+ * when its prefix is known, so hla_scan rewrites them in a launch of its own.
+ * total_out, workspace (hla_scan_workspace_bytes(p) bytes) and errors as for
+ * hla_scan.
  */
 hla_status hla_scan_into(const hla_problem* p, const hla_state* summaries,
                          const hla_state* prefixes_out, const hla_state* total_out, void* workspace,
@@ -236,11 +234,15 @@ hla_status hla_fwd_output_from_p(const hla_problem* p, const void* q, const void
                                  const void* plocal, const hla_state* prefixes, float* o,
                                  float* den, void* stream);
 
-/* Bytes of workspace with which hla_fwd also keeps the segment-local p of
- * its spans and computes the outputs from it (hla_fwd_chunk_summaries_p +
- * hla_scan + hla_fwd_output_from_p at chunk' = R * chunk): the summaries and
- * the scan's scratch, rounded up to 256 bytes, plus hla_fwd_p_bytes at
- * chunk'.  Equal to hla_fwd_workspace_bytes(p) for shapes without that path.
+/* Bytes of workspace for hla_fwd's fastest plan.  With the summaries and
+ * the scan's scratch (hla_fwd_workspace_bytes(p)) rounded up to 256 bytes,
+ * then hla_fwd_p_bytes at chunk' = R * chunk, hla_fwd also keeps the
+ * segment-local p of its spans and computes the outputs from it
+ * (hla_fwd_chunk_summaries_p + hla_fwd_output_from_p); with room for the
+ * n / R exclusive prefixes as well, it scans out of place (hla_scan_into)
+ * instead of in place.  That room is found inside hla_fwd_workspace_bytes(p)
+ * when spans of several chunks leave enough of it (it is sized for one
+ * summary per chunk); otherwise it comes last, rounded up to 256 bytes.
  * Host-only; 0 for an invalid or empty problem. */
 size_t hla_fwd_p_workspace_bytes(const hla_problem* p);
 
@@ -263,9 +265,10 @@ int32_t hla_fwd_span_chunks(const hla_problem* p);
  * summaries), hla_scan turns them into exclusive prefixes, and
  * hla_fwd_output walks each span from its prefix.  The summaries are kept in
  * `workspace` (at least hla_fwd_workspace_bytes(p) bytes; with
- * hla_fwd_p_workspace_bytes(p) bytes, for the shapes that have it, the
- * summary kernel also keeps the segment-local p there and the outputs come
- * from it: hla_fwd_chunk_summaries_p and hla_fwd_output_from_p).  o and den as in
+ * hla_fwd_p_workspace_bytes(p) bytes the fastest plan: for the shapes that
+ * have it, the summary kernel also keeps the segment-local p there and the
+ * outputs come from it, hla_fwd_chunk_summaries_p and hla_fwd_output_from_p,
+ * and the scan runs out of place, hla_scan_into).  o and den as in
  * hla_fwd_output; the results equal those of the three calls at `chunk` up
  * to fp32 rounding order.  If `final_state` is non-NULL its non-NULL fields
  * receive the state after all T tokens ([B, H, ...]), ready for

@@ -160,13 +160,22 @@ def test_segment_local_p_sizes_and_checks(L):
                dict(T=10)):
         q = problem(**dict(dict(B=1, H=2, T=576, d=128, dv=128, chunk=96), **kw))
         assert L.hla_fwd_p_bytes(ctypes.byref(q)) == 0, kw
-    # hla_fwd with room for p: the summaries and scan scratch rounded up to
-    # 256 bytes, then p over hla_fwd's spans (R = 1 here: 6 units of 2 segments)
+    # hla_fwd's fastest plan: the summaries (and scan scratch, none here)
+    # rounded up to 256 bytes, then p over hla_fwd's spans, then room for the
+    # exclusive prefixes out of place, as large as the summaries (R = 1 here:
+    # 2 units of 6 segments, so the summaries fill the minimum workspace)
+    r256 = lambda x: (x + 255) // 256 * 256
     base = L.hla_fwd_workspace_bytes(ctypes.byref(p))
-    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(p)) == (base + 255) // 256 * 256 + \
-        L.hla_fwd_p_bytes(ctypes.byref(p))
-    q64 = problem()
-    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(q64)) == L.hla_fwd_workspace_bytes(ctypes.byref(q64))
+    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(p)) == \
+        r256(r256(base) + L.hla_fwd_p_bytes(ctypes.byref(p))) + base
+    q64 = problem()   # no p path; spans of one chunk
+    base = L.hla_fwd_workspace_bytes(ctypes.byref(q64))
+    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(q64)) == r256(base) + base
+    # spans of 4 chunks: the minimum workspace, sized for one summary per
+    # chunk, has room for the span prefixes
+    w = problem(B=4, H=16, T=4096, d=64, dv=64, chunk=64)
+    assert L.hla_fwd_span_chunks(ctypes.byref(w)) == 4
+    assert L.hla_fwd_p_workspace_bytes(ctypes.byref(w)) == L.hla_fwd_workspace_bytes(ctypes.byref(w))
     # argument checks before anything runs
     st = ctypes.byref(state())
     assert L.hla_fwd_chunk_summaries_p(ctypes.byref(q64), Q, K, V, st, DEN, None) == UNSUP
@@ -211,12 +220,9 @@ def test_run_prefix_scan_sizes_and_checks(L):
 
 def test_out_of_place_scan_checks(L):
     pre = state(base=0x7100000000)
-    # built for d = dv in {16, 32, 64} with runs of at most 16 segments
-    for kw in (dict(d=128, dv=128), dict(d=64, dv=32), dict(d=32, dv=64),
-               dict(T=512 * 16, chunk=16)):   # n = 512: runs of 32
-        p = problem(**kw)
-        assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(pre), None,
-                               None, 0, None) == UNSUP, kw
+    p = problem(d=128, dv=96)   # a head size that is not built
+    assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), ctypes.byref(pre), None,
+                           None, 0, None) == UNSUP
     p = problem()
     assert L.hla_scan_into(ctypes.byref(p), None, ctypes.byref(pre), None, None, 0, None) == NULLP
     assert L.hla_scan_into(ctypes.byref(p), ctypes.byref(state()), None, None, None, 0, None) == NULLP
