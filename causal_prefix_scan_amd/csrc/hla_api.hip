@@ -1404,15 +1404,13 @@ hla_status hla3_scan(const hla_problem* p, const hla3_summary* inout, const hla3
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = p->d, e = p->dv, units = (int)z.units, n = (int)z.n;
   const hla3_state* t = total_out;
-  if (hla_status x = from_hip(hla::launch_moments_scan(inout->S, t ? t->S : nullptr, p->gamma, p->H,
-                                                       p->chunk, n, d * d, units, s)))
-    return x;
-  if (hla_status x = from_hip(hla::launch_moments_scan(inout->P, t ? t->P : nullptr, p->gamma, p->H,
-                                                       p->chunk, n, d * e, units, s)))
-    return x;
-  if (hla_status x = from_hip(hla::launch_moments_scan(inout->m, t ? t->m : nullptr, p->gamma, p->H,
-                                                       p->chunk, n, d, units, s)))
-    return x;
+  {
+    float* const xs[3] = {inout->S, inout->P, inout->m};
+    float* const ts[3] = {t ? t->S : nullptr, t ? t->P : nullptr, t ? t->m : nullptr};
+    const int el[3] = {d * d, d * e, d};
+    if (hla_status x = from_hip(hla::launch_moments_scan(xs, ts, el, p->gamma, p->H, p->chunk, n, units, s)))
+      return x;
+  }
   hla::R3ScanArgs a;
   a.Sp = inout->S; a.Pp = inout->P; a.mp = inout->m; a.Q = inout->Q; a.V = inout->V;
   a.Z = inout->Z; a.z = inout->z; a.R = inout->R; a.r = inout->r;
@@ -1459,16 +1457,14 @@ hla_status hla3_fwd(const hla_problem* p, const void* q, const void* k, const vo
   if (hla_status x = third_summaries(t, wb, w, F(w.S), F(w.Q), F(w.V), F(w.P), F(w.Z), F(w.R))) return x;
   // the scan: the moments elementwise, then R and r with the segment map
   const hla3_state* fs = final_state;
-  if (hla_status x = from_hip(hla::launch_moments_scan(F(w.S), fs ? fs->S : nullptr, p->gamma, p->H,
-                                                       p->chunk, n, d * d, units, t.s)))
-    return x;
-  if (hla_status x = from_hip(hla::launch_moments_scan(F(w.P), fs ? fs->P : nullptr, p->gamma, p->H,
-                                                       p->chunk, n, d * e, units, t.s)))
-    return x;
   const bool want_m = fs && fs->m;
-  if (hla_status x = from_hip(hla::launch_moments_scan(F(w.m), want_m ? F(w.tm16) : nullptr, p->gamma,
-                                                       p->H, p->chunk, n, d * 16, units, t.s)))
-    return x;
+  {
+    float* const xs[3] = {F(w.S), F(w.P), F(w.m)};
+    float* const ts[3] = {fs ? fs->S : nullptr, fs ? fs->P : nullptr, want_m ? F(w.tm16) : nullptr};
+    const int el[3] = {d * d, d * e, d * 16};
+    if (hla_status x = from_hip(hla::launch_moments_scan(xs, ts, el, p->gamma, p->H, p->chunk, n, units, t.s)))
+      return x;
+  }
   if (want_m) {
     if (hla_status x = from_hip(hla::launch_gather_col0(F(w.tm16), fs->m, (size_t)units * d, t.s))) return x;
   }

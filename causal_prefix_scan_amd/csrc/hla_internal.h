@@ -145,9 +145,11 @@ struct Decode3Args {
   float eps;
 };
 // Exclusive decayed running sum (a = gamma^seg) over each unit's nseg
-// segments of `elems` floats, in place; totals [units, elems] when not null.
-hipError_t launch_moments_scan(float* x, float* total, const float* gamma, int H, int seg, int nseg,
-                               int elems, int units, hipStream_t s);
+// segments of elems[i] floats of x[i] (up to three arrays, a null x[i]
+// skipped), in place, in one launch; totals [units, elems[i]] to total[i]
+// when not null.
+hipError_t launch_moments_scan(float* const x[3], float* const total[3], const int elems[3],
+                               const float* gamma, int H, int seg, int nseg, int units, hipStream_t s);
 hipError_t launch_r_scan(int d, int dv, int units, const R3ScanArgs& a, hipStream_t s);
 // [tokens][16] rows of (1, 0, ..., 0), bf16 (bf16 != 0) or fp32.
 hipError_t launch_unit_channel(int bf16, void* one, size_t tokens, hipStream_t s);

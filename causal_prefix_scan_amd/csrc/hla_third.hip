@@ -35,17 +35,38 @@ namespace hla {
 namespace {
 
 // Exclusive decayed running sum over each unit's nseg segments, in place
-// (x_s <- sum_{r<s} a^(s-1-r) x_r, a = g^seg), one thread per element; the
-// inclusive total of every element goes to `total` when it is not null.
-__global__ __launch_bounds__(256) void moments_scan_kernel(float* x, float* total, const float* gamma,
-                                                           int H, int seg, int nseg, int elems) {
-  const int per = (elems + 255) / 256;
+// (x_s <- sum_{r<s} a^(s-1-r) x_r, a = g^seg), one thread per element, for
+// up to three arrays in one launch (per unit, blockIdx.x runs over the
+// blocks of x[0], then x[1], then x[2]); the inclusive total of every
+// element goes to total[i] when it is not null.
+struct MomentsScanArgs {
+  float* x[3];
+  float* total[3];
+  int elems[3], nb[3];
+  const float* gamma;
+  int H, seg, nseg;
+};
+
+__global__ __launch_bounds__(256) void moments_scan_kernel(MomentsScanArgs m) {
+  const int per = m.nb[0] + m.nb[1] + m.nb[2];
   const int unit = blockIdx.x / per;
-  const int e = (blockIdx.x - unit * per) * 256 + threadIdx.x;
+  int b = blockIdx.x - unit * per, f = 0;
+  if (b >= m.nb[0]) {
+    b -= m.nb[0];
+    f = 1;
+    if (b >= m.nb[1]) {
+      b -= m.nb[1];
+      f = 2;
+    }
+  }
+  const int elems = m.elems[f];
+  const int e = b * 256 + threadIdx.x;
   if (e >= elems) return;
-  const float g = gamma ? gamma[unit % H] : 1.f;
-  const float a = gpow(g, log2f(g), seg);
-  float* p = x + (size_t)unit * nseg * elems + e;
+  const int nseg = m.nseg;
+  const float g = m.gamma ? m.gamma[unit % m.H] : 1.f;
+  const float a = gpow(g, log2f(g), m.seg);
+  float* total = m.total[f];
+  float* p = m.x[f] + (size_t)unit * nseg * elems + e;
   float run = 0.f;
   constexpr int NB = 8;   // loads of eight segments in flight
   for (int s0 = 0; s0 < nseg; s0 += NB) {
@@ -404,11 +425,20 @@ __global__ __launch_bounds__(512) void decode3_kernel(Decode3Args a) {
 
 }  // namespace
 
-hipError_t launch_moments_scan(float* x, float* total, const float* gamma, int H, int seg, int nseg,
-                               int elems, int units, hipStream_t s) {
-  const int per = (elems + 255) / 256;
-  hipLaunchKernelGGL(moments_scan_kernel, dim3((unsigned)(units * per)), dim3(256), 0, s, x, total,
-                     gamma, H, seg, nseg, elems);
+hipError_t launch_moments_scan(float* const x[3], float* const total[3], const int elems[3],
+                               const float* gamma, int H, int seg, int nseg, int units, hipStream_t s) {
+  MomentsScanArgs m;
+  int per = 0;
+  for (int i = 0; i < 3; ++i) {
+    m.x[i] = x[i];
+    m.total[i] = total[i];
+    m.elems[i] = x[i] ? elems[i] : 0;
+    m.nb[i] = (m.elems[i] + 255) / 256;
+    per += m.nb[i];
+  }
+  m.gamma = gamma; m.H = H; m.seg = seg; m.nseg = nseg;
+  if (per == 0) return hipSuccess;
+  hipLaunchKernelGGL(moments_scan_kernel, dim3((unsigned)(units * per)), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

@@ -534,22 +534,48 @@ __global__ __launch_bounds__(64 * NW) void unmasked_kernel(ChunkArgs a) {
 }
 
 // Exclusive decayed running sum over the n segments of each unit, in place:
-// X[s] <- sum_{r<s} a^(s-1-r) X[r], a = g^chunk (the unmasked combine).
-// X is [units, n, F]; each thread owns four consecutive floats.
-__global__ __launch_bounds__(256) void unmasked_scan_kernel(float* X, int F, int n, const float* gamma,
-                                                            int H, int chunk) {
+// X[s] <- sum_{r<s} a^(s-1-r) X[r], a = g^chunk (the unmasked combine), for
+// the three moments S, C, m ([units, n, F_i] each) in one launch: blockIdx.x
+// runs over the blocks of S, then of C, then of m; each thread owns four
+// consecutive floats and keeps eight segments' loads in flight.
+struct UScanArgs {
+  float* X[3];
+  int F[3], nb[3];    // floats per segment, blocks of 256 threads
+  const float* gamma;
+  int H, n, chunk;
+};
+
+__global__ __launch_bounds__(256) void unmasked_scan_kernel(UScanArgs a) {
   const int unit = blockIdx.y;
-  const int e4 = blockIdx.x * 256 + threadIdx.x;
+  int b = blockIdx.x, f = 0;
+  if (b >= a.nb[0]) {
+    b -= a.nb[0];
+    f = 1;
+    if (b >= a.nb[1]) {
+      b -= a.nb[1];
+      f = 2;
+    }
+  }
+  const int F = a.F[f];
+  const int e4 = b * 256 + threadIdx.x;
   if (4 * e4 >= F) return;
-  const float g = gamma ? gamma[unit % H] : 1.f;
-  const float sa = gpow(g, log2f(g), chunk);
+  const float g = a.gamma ? a.gamma[unit % a.H] : 1.f;
+  const float sa = gpow(g, log2f(g), a.chunk);
   f32x4 run = zero4();
-  f32x4* p = reinterpret_cast<f32x4*>(X + (size_t)unit * n * F) + e4;
-  const int step = F / 4;
-  for (int s = 0; s < n; ++s) {
-    const f32x4 x = p[(size_t)s * step];
-    p[(size_t)s * step] = run;
-    run = run * sa + x;
+  f32x4* p = reinterpret_cast<f32x4*>(a.X[f] + (size_t)unit * a.n * F) + e4;
+  const size_t step = F / 4;
+  constexpr int NB = 8;
+  for (int s0 = 0; s0 < a.n; s0 += NB) {
+    f32x4 x[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) x[i] = s0 + i < a.n ? p[(size_t)(s0 + i) * step] : zero4();
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (s0 + i < a.n) {
+        p[(size_t)(s0 + i) * step] = run;
+        run = run * sa + x[i];
+      }
+    }
   }
 }
 
@@ -714,16 +740,14 @@ hipError_t launch_unmasked_decode(int dtype, int d, int dv, int units, const Dec
 }
 
 hipError_t launch_unmasked_scan(const ChunkArgs& a, int units, int d, int dv, hipStream_t s) {
-  float* fields[3] = {a.S, a.C, a.m};
-  const int F[3] = {d * d, d * dv, d};
-  for (int i = 0; i < 3; ++i) {
-    const dim3 grid((unsigned)((F[i] / 4 + 255) / 256), (unsigned)units);
-    hipLaunchKernelGGL(unmasked_scan_kernel, grid, dim3(256), 0, s, fields[i], F[i], a.nspan,
-                       a.gamma, a.H, a.chunk);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  UScanArgs u;
+  u.X[0] = a.S; u.X[1] = a.C; u.X[2] = a.m;
+  u.F[0] = d * d; u.F[1] = d * dv; u.F[2] = d;
+  for (int i = 0; i < 3; ++i) u.nb[i] = (u.F[i] / 4 + 255) / 256;
+  u.gamma = a.gamma; u.H = a.H; u.n = a.nspan; u.chunk = a.chunk;
+  const dim3 grid((unsigned)(u.nb[0] + u.nb[1] + u.nb[2]), (unsigned)units);
+  hipLaunchKernelGGL(unmasked_scan_kernel, grid, dim3(256), 0, s, u);
+  return hipGetLastError();
 }
 
 }  // namespace hla
