@@ -25,14 +25,17 @@
 // The run-prefix form stops after step 2 (the run totals reduced into the
 // caller's run-prefix arrays and scanned there; segments only read): a
 // forward pass whose output kernel walks whole runs needs nothing more, as it
-// carries the state from one segment of a run to the next itself.
+// carries the state from one segment of a run to the next itself.  The
+// out-of-place form writes every prefix to arrays of its own and leaves the
+// segments as they were, so step 3 also writes C's and m's prefixes and
+// step 4 is not needed.
 //
 // Steps 1 and 3 split a run's state over workgroups by 16-row blocks: a
 // workgroup owns rows [r0, r0 + 16) of S, G and h, and keeps the whole
 // running C and m, which its rows of the cross terms S_B C_A, S_B m_A need.
-// C and m are therefore only read in step 3 (every workgroup of the run
-// reads them) and rewritten in step 4.  The cross term runs on fp32 MFMA with
-// the running C as the B operand straight from registers.
+// In place, C and m are therefore only read in step 3 (every workgroup of the
+// run reads them) and rewritten in step 4.  The cross term runs on fp32 MFMA
+// with the running C as the B operand straight from registers.
 #include "hla_device.h"
 #include "hla_internal.h"
 
