@@ -182,7 +182,7 @@ def bench_fwd(args, torch, np):
     L = hla.lib()
     # hla_fwd's plan: each workgroup walks a span of R chunks (forming and
     # combining their summaries in order), the scan runs over the span totals
-    # (out of place where built), and the outputs walk each span from its prefix
+    # (out of place), and the outputs walk each span from its prefix
     p0 = hla.make_problem(q, v, chunk, g, cfg["normalize"], cfg["eps"])
     R = L.hla_fwd_span_chunks(ctypes.byref(p0))
     span = chunk * R
@@ -203,17 +203,11 @@ def bench_fwd(args, torch, np):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    # the shapes that have it (d = dv <= 64, runs of at most 16 span totals)
-    # scan out of place, as hla_fwd does: the whole rescan in one launch
+    # the scan out of place, as hla_fwd's fastest plan runs it: the rescan
+    # writes every prefix itself (no separate C, m pass)
     pre = hla.alloc_state((B, H, n), d, dv, "cuda")
     st_pre = hla._state_struct(pre)
-    rc = L.hla_scan_into(ctypes.byref(p), ctypes.byref(st), ctypes.byref(st_pre), None, ptr(ws),
-                         ctypes.c_size_t(ws_bytes), sp)
-    if rc not in (0, 5):   # HLA_OK, HLA_ERR_UNSUPPORTED
-        raise RuntimeError(f"hla_scan_into failed: {rc}")
-    into = rc == 0
-    name_scan = "hla_scan_into" if into else "hla_scan"
-    st_out = st_pre if into else st
+    name_scan = "hla_scan_into"
 
     def step(ev=None):
         if ev:
@@ -225,18 +219,15 @@ def bench_fwd(args, torch, np):
             r1 = L.hla_fwd_chunk_summaries(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st), sp)
         if ev:
             ev[1].record(stream)
-        if into:
-            r2 = L.hla_scan_into(ctypes.byref(p), ctypes.byref(st), ctypes.byref(st_pre), None, ptr(ws),
-                                 ctypes.c_size_t(ws_bytes), sp)
-        else:
-            r2 = L.hla_scan(ctypes.byref(p), ctypes.byref(st), None, ptr(ws), ctypes.c_size_t(ws_bytes), sp)
+        r2 = L.hla_scan_into(ctypes.byref(p), ctypes.byref(st), ctypes.byref(st_pre), None, ptr(ws),
+                             ctypes.c_size_t(ws_bytes), sp)
         if ev:
             ev[2].record(stream)
         if p_bytes:
-            r3 = L.hla_fwd_output_from_p(ctypes.byref(p), ptr(q), ptr(v), ptr(plocal), ctypes.byref(st_out),
+            r3 = L.hla_fwd_output_from_p(ctypes.byref(p), ptr(q), ptr(v), ptr(plocal), ctypes.byref(st_pre),
                                          ptr(o), ptr(den), sp)
         else:
-            r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st_out), ptr(o),
+            r3 = L.hla_fwd_output(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ctypes.byref(st_pre), ptr(o),
                                   ptr(den), None, ctypes.c_size_t(0), sp)
         if ev:
             ev[3].record(stream)
