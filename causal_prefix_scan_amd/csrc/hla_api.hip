@@ -1208,11 +1208,11 @@ hla_status hla_bwd(const hla_problem* p, const void* q, const void* k, const voi
 
 namespace {
 
-// Workspace of the third-order calls: the unit channel, p, u and u_m (local,
-// then global; the MFMA operand type), the segment summaries (fp32; m, z, r
-// in the 16-wide layout), den16 and the 16-wide total of m.
+// Workspace of the third-order calls: p, u and u_m (local, then global; the
+// MFMA operand type), the segment summaries (fp32; m, z, r in the 16-wide
+// layout), den16 and the 16-wide total of m.
 struct Ws3 {
-  size_t one, p, u, um, S, Q, V, P, Z, R, m, z, r, den16, tm16, total;
+  size_t p, u, um, S, Q, V, P, Z, R, m, z, r, den16, tm16, total;
 };
 
 Ws3 ws3_of(const hla_problem* p) {
@@ -1222,7 +1222,6 @@ Ws3 ws3_of(const hla_problem* p) {
   Ws3 w;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align16(bytes); return at; };
-  w.one = take(tok * 16 * es);
   w.p = take(tok * d * es);
   w.u = take(tok * e * es);
   w.um = take(tok * 16 * es);
@@ -1274,8 +1273,6 @@ hla_status third_summaries(const Third& t, char* wb, const Ws3& w, float* S, flo
   float* py = reinterpret_cast<float*>(wb + w.p);
   float* uy = reinterpret_cast<float*>(wb + w.u);
   float* umy = reinterpret_cast<float*>(wb + w.um);
-  const size_t tok = (size_t)t.z.units * (size_t)t.p->T;
-  if (hla_status x = from_hip(hla::launch_unit_channel(t.bf, wb + w.one, tok, t.s))) return x;
   // local p, u, u_m: every segment from the zero state; the same passes leave
   // the segment states of their sums, the summaries S^K, P^KV and m^K
   if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, py, t.bf, nullptr, false, S)) return x;
@@ -1299,7 +1296,8 @@ hla_status third_setup(const hla_problem* p, const void* q, const void* k, const
   w = ws3_of(p);
   char* wb = static_cast<char*>(workspace);
   t.Q = {q, t.bf}; t.K = {k, t.bf}; t.V = {v, t.bf};
-  t.ONE = {wb + w.one, t.bf}; t.Pq = {wb + w.p, t.bf}; t.U = {wb + w.u, t.bf};
+  t.ONE = {nullptr, t.bf};   // the unit channel, formed by the kernels
+  t.Pq = {wb + w.p, t.bf}; t.U = {wb + w.u, t.bf};
   t.UM = {wb + w.um, t.bf};
   return HLA_OK;
 }

@@ -80,10 +80,22 @@ struct TileRows {
   using R = typename std::conditional<F32, uint4, uint2>::type;
   R r[N];
 
+  // A null operand is the unit channel: rows (1, 0, ..., 0), formed here
+  // rather than read.
   __device__ __forceinline__ void load(const LaOperand& op, size_t urow, int nT, bool rev, int t0,
                                        int end, int tid) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const E* base = reinterpret_cast<const E*>(op.p);
+    if (!base) {
+      R one{};
+      one.x = F32 ? 0x3F800000u : 0x3F80u;   // 1.0 in the first element
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int idx = tid + NTHR * i, row = idx / G, l = t0 + row;
+        r[i] = (idx < LT * G && l < end && idx % G == 0) ? one : R{};
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = tid + NTHR * i, row = idx / G, col = (idx % G) * 4, l = t0 + row;

@@ -151,8 +151,6 @@ struct Decode3Args {
 hipError_t launch_moments_scan(float* const x[3], float* const total[3], const int elems[3],
                                const float* gamma, int H, int seg, int nseg, int units, hipStream_t s);
 hipError_t launch_r_scan(int d, int dv, int units, const R3ScanArgs& a, hipStream_t s);
-// [tokens][16] rows of (1, 0, ..., 0), bf16 (bf16 != 0) or fp32.
-hipError_t launch_unit_channel(int bf16, void* one, size_t tokens, hipStream_t s);
 // den[t] = den16[t][0] (den may be null); with normalize, o[t] /= den + eps.
 hipError_t launch_finish3(float* o, const float* den16, float* den, size_t tokens, int dv,
                           int normalize, float eps, hipStream_t s);

@@ -23,7 +23,7 @@
 // at once (the moments' prefixes in place of S_A, P_A, m_A), and an
 // elementwise decayed running sum of those terms.
 //
-// The m, z, r and unit-channel arrays are kept as [.., d][16] with the value
+// The m, z, r arrays (and the unit channel) are kept as [.., d][16] with the value
 // in column 0 (the layout of a first-order sum whose value operand is 16
 // wide); `ldm` is their row stride (16, or 1 for plain [.., d] arrays).
 #include <type_traits>
@@ -252,13 +252,6 @@ __global__ __launch_bounds__(256) void r_prefix_kernel(R3ScanArgs a) {
   if (t) t[isR ? (size_t)unit * ER + e : (size_t)unit * D + (e - ER)] = run;
 }
 
-// The unit channel: one[t][0] = 1, one[t][1..15] = 0 (bf16 or fp32).
-template <typename T>
-__global__ __launch_bounds__(256) void unit_channel_kernel(T* one, size_t tokens) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < tokens * 16) one[i] = (T)((i & 15) == 0 ? 1.f : 0.f);
-}
-
 // den[t] = den16[t][0]; with normalize, o[t][:] /= den[t] + eps.
 __global__ __launch_bounds__(256) void finish_kernel(float* o, const float* den16, float* den,
                                                      size_t tokens, int E, int normalize, float eps) {
@@ -457,15 +450,6 @@ hipError_t launch_r_scan(int d, int dv, int units, const R3ScanArgs& a, hipStrea
   HLA_CASE(64, 32) HLA_CASE(64, 64) HLA_CASE(64, 128) HLA_CASE(128, 64) HLA_CASE(128, 128)
 #undef HLA_CASE
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_unit_channel(int bf16, void* one, size_t tokens, hipStream_t s) {
-  const dim3 grid((unsigned)((tokens * 16 + 255) / 256));
-  if (bf16)
-    hipLaunchKernelGGL(unit_channel_kernel<__bf16>, grid, dim3(256), 0, s, (__bf16*)one, tokens);
-  else
-    hipLaunchKernelGGL(unit_channel_kernel<float>, grid, dim3(256), 0, s, (float*)one, tokens);
-  return hipGetLastError();
 }
 
 hipError_t launch_finish3(float* o, const float* den16, float* den, size_t tokens, int dv,
