@@ -1,5 +1,6 @@
-"""The forward and the decode step captured in a HIP graph (torch.cuda.CUDAGraph
-over the C-ABI calls on the capturing stream) and replayed: every replay,
+"""The forward, the decode step, the backward and the third-order forward
+captured in a HIP graph (torch.cuda.CUDAGraph over the C-ABI calls on the
+capturing stream) and replayed: every replay,
 with eager work and synchronisations between replays, must give the same
 bits as the same calls launched directly.  The library records no
 hipMemsetAsync (its scratch is cleared by its own kernels), allocates nothing
@@ -118,3 +119,57 @@ def test_decode_graph_replays_match_eager(gpu):
         assert torch.equal(den, outs[s][1]), ("step", s, "den")
     for key in st_g:
         assert torch.equal(st_g[key], st_e[key]), ("state", key)
+
+
+def test_backward_graph_replays_match_eager(gpu):
+    """hla_bwd (its 14 launches, the workspace passed in) captured once and
+    replayed: the same bits as the eager call on every replay."""
+    import ctypes
+
+    import numpy as np
+    torch = gpu
+    B, H, T, d, dv, chunk = 1, 2, 512, 64, 64, 128
+    say("backward graph", (B, H, T, d, dv, chunk))
+    q, k, v, g = to_dev(synth.make_fwd_inputs(B, H, T, d, dv, "bf16", seed=4400, decay=True))
+    rng = np.random.default_rng(4401)
+    dout = torch.from_numpy(rng.standard_normal((B, H, T, dv)).astype(np.float32)).cuda()
+    dout2 = torch.from_numpy(rng.standard_normal((B, H, T, dv)).astype(np.float32)).cuda()
+    p = hla.make_problem(q, v, chunk, g)
+    ws = torch.empty(max(hla.lib().hla_bwd_workspace_bytes(ctypes.byref(p)), 16), dtype=torch.uint8,
+                     device="cuda")
+    ref = [x.clone() for x in hla.bwd(q, k, v, dout, chunk, g, workspace=ws)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(x) for x in ref]
+    graph = _capture(torch, lambda: hla.bwd(q, k, v, dout, chunk, g, workspace=ws, dq=outs[0], dk=outs[1],
+                                            dv=outs[2]))
+    for rep in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        hla.bwd(q, k, v, dout2, chunk, g, workspace=ws)   # eager work through the same workspace
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("dq", "dk", "dv"), outs, ref):
+            assert torch.equal(got, want), ("replay", rep, name)
+
+
+def test_third_order_graph_replays_match_eager(gpu):
+    """hla3_fwd captured once and replayed: the same bits as the eager call."""
+    torch = gpu
+    B, H, T, d, dv, chunk = 1, 2, 768, 64, 64, 128
+    say("third-order graph", (B, H, T, d, dv, chunk))
+    q, k, v, g = to_dev(synth.make_fwd_inputs(B, H, T, d, dv, "bf16", seed=4500, decay=True))
+    o_ref, den_ref, _ = hla.hla3_fwd(q, k, v, chunk, g, want_den=True)
+    torch.cuda.synchronize()
+    o_ref, den_ref = o_ref.clone(), den_ref.clone()
+    o = torch.empty_like(o_ref)
+    den = torch.empty_like(den_ref)
+    graph = _capture(torch, lambda: hla.hla3_fwd(q, k, v, chunk, g, want_den=True, o=o, den=den))
+    for rep in range(3):
+        o.fill_(float("nan"))
+        den.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), ("replay", rep, "o")
+        assert torch.equal(den, den_ref), ("replay", rep, "den")
