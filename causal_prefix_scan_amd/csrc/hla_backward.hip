@@ -538,6 +538,16 @@ __global__ __launch_bounds__(64 * pt_waves(Da, E)) void prefix_term_kernel(Prefi
       for (int j = 0; j < 4; ++j)
         Ht[b][t][j] = own[b] ? hp[(size_t)(16 * t + 4 * lg + j) * wd[b] + 16 * cbk[b] + lr] : 0.f;
   }
+  // bf16: the blocks as MFMA operands in the natural K order, formed once, so
+  // that a's rows are read with plain 16-byte row reads
+  constexpr bool NATK = sizeof(T) == 2;
+  typename MMT::F hb[2][NATK ? QK : 1];
+  if constexpr (NATK) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk) hb[b][kk] = FR::acc_b_nat(Ht[b], kk);
+  }
   __syncthreads();
 
   T* const y0 = reinterpret_cast<T*>(a.y[0]);
@@ -579,7 +589,12 @@ __global__ __launch_bounds__(64 * pt_waves(Da, E)) void prefix_term_kernel(Prefi
         if (!own[b]) continue;
         f32x4 y = zero4();
 #pragma unroll
-        for (int kk = 0; kk < QK; ++kk) y = MMT::mma(FR::acc_b(Ht[b], kk), FR::perm(As, L::LDA, 16 * r, kk, lane), y);
+        for (int kk = 0; kk < QK; ++kk) {
+          if constexpr (NATK)
+            y = MMT::mma(hb[b][kk], MMT::ld(As, L::LDA, 16 * r, 32 * kk, lane), y);
+          else
+            y = MMT::mma(FR::acc_b(Ht[b], kk), FR::perm(As, L::LDA, 16 * r, kk, lane), y);
+        }
         T* const yb = oi[b] == 0 ? Y0 : oi[b] == 1 ? Y1 : Y2;
         const int ly = oi[b] == 0 ? L0 : oi[b] == 1 ? L1 : L2;
         V* const slot = reinterpret_cast<V*>(yb + (16 * r + lr) * ly + 16 * cbk[b] + 4 * lg);
