@@ -1246,11 +1246,24 @@ struct Third {
   hipStream_t s;
   int bf;
   hla::LaOperand Q, K, V, ONE, Pq, U, UM;
-  // one first-order sum over this problem's segments
+  // the scalar channel of a summary pass: a second sum with the same a, b
+  // and lam whose value is column 0 of c2 (16 wide), its segment states Hp2
+  // (16 wide)
+  struct Channel {
+    hla::LaOperand c2{nullptr, 0};
+    float* Hp2 = nullptr;
+  };
+  // one first-order sum over this problem's segments (with `ch`, a summary
+  // pass, its channel in the same pass)
   hla_status sum(hla::LaOperand a, hla::LaOperand b, hla::LaOperand c, int Da, int Dc, int gexp,
-                 float* y, int y_bf16, float* Hp, bool states_only, float* Hout = nullptr) const {
+                 float* y, int y_bf16, float* Hp, bool states_only, float* Hout = nullptr,
+                 const Channel* ch = nullptr) const {
     hla::LaArgs la;
     la.a = a; la.b = b; la.c = c;
+    if (ch) {
+      la.ch = 1;
+      la.c2 = ch->c2; la.Hp2 = ch->Hp2;
+    }
     la.y = y; la.Hp = Hp; la.Hout = Hout; la.gamma = p->gamma;
     la.H = p->H; la.gexp = gexp;
     la.T = p->T; la.seg = p->chunk; la.nseg = (int)z.n;
@@ -1278,13 +1291,16 @@ hla_status third_summaries(const Third& t, char* wb, const Ws3& w, float* S, flo
   if (hla_status x = t.sum(t.Q, t.K, t.K, d, d, 1, py, t.bf, nullptr, false, S)) return x;
   if (hla_status x = t.sum(t.Q, t.K, t.V, d, e, 1, uy, t.bf, nullptr, false, P)) return x;
   if (hla_status x = t.sum(t.Q, t.K, t.ONE, d, 16, 1, umy, t.bf, nullptr, false, m)) return x;
-  // the other summaries as segment states
+  // the other summaries as segment states; z and r ride on Z's and R's
+  // passes (the same a, b and lam) as their scalar channels
   if (hla_status x = t.sum(t.Q, t.Q, t.Q, d, d, 1, nullptr, 0, Qm, true)) return x;
   if (hla_status x = t.sum(t.Q, t.Pq, t.Q, d, d, 2, nullptr, 0, V, true)) return x;
-  if (hla_status x = t.sum(t.Q, t.Q, t.U, d, e, 2, nullptr, 0, Z, true)) return x;
-  if (hla_status x = t.sum(t.Q, t.Q, t.UM, d, 16, 2, nullptr, 0, z, true)) return x;
-  if (hla_status x = t.sum(t.Q, t.Pq, t.U, d, e, 3, nullptr, 0, R, true)) return x;
-  return t.sum(t.Q, t.Pq, t.UM, d, 16, 3, nullptr, 0, r, true);
+  Third::Channel cz;
+  cz.c2 = t.UM; cz.Hp2 = z;
+  if (hla_status x = t.sum(t.Q, t.Q, t.U, d, e, 2, nullptr, 0, Z, true, nullptr, &cz)) return x;
+  Third::Channel cr;
+  cr.c2 = t.UM; cr.Hp2 = r;
+  return t.sum(t.Q, t.Pq, t.U, d, e, 3, nullptr, 0, R, true, nullptr, &cr);
 }
 
 hla_status third_setup(const hla_problem* p, const void* q, const void* k, const void* v,

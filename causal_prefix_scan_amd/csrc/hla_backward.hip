@@ -155,7 +155,7 @@ struct TileRows {
 // and, with bit 3, that c is the same tensor as b.
 // The bf16 kernels fit 128 VGPRs without spills, which lets two 8-wave
 // workgroups share a CU.
-template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF, bool ACC>
+template <typename T, int Da, int Dc, int MODE, int NW, bool SYM, int SRCF, bool ACC, bool CH>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaArgs a) {
   using L = LLayout<T, Da, Dc, SYM>;
@@ -180,6 +180,9 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
   float* pw = reinterpret_cast<float*>(smem + L::W);
   float* w1 = pw + LT;
   float* wS = w1 + LT;
+  // (CH) the scalar channel: its values in the tile, its state by tile parity
+  __shared__ float c2s[CH ? LT : 1];
+  __shared__ float h2s[2][CH ? Da : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,6 +206,13 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   if (tid < LT) pw[tid] = gpow(lam, lgl, tid);
   if (tid < LT) w1[tid] = gpow(lam, lgl, tid + 1);
+  // (CH, summary passes) a second sum with the same a, b and lam whose value
+  // is the scalar in column 0 of c2's 16-wide rows: its state rides along
+  constexpr bool ch = CH;
+  static_assert(!CH || MODE == L_SUMMARY, "the scalar channel is for summary passes");
+  if constexpr (ch) {
+    for (int k = tid; k < Da; k += NTHR) h2s[0][k] = 0.f;
+  }
   __syncthreads();
 
   // this wave's columns of the state: H[16 t + 4 lg + j][col]
@@ -219,11 +229,23 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
   TileRows<Da, NTHR, LT, (SRCF & 1) != 0> ra;
   TileRows<Da, NTHR, LT, (SRCF & 2) != 0> rb;
   TileRows<Dc, NTHR, LT, (SRCF & 4) != 0> rc;
+  float c2v = 0.f;   // (ch) this thread's token's channel value, a tile ahead
   auto load_tile = [&](int t0) {
     if (OUT) ra.load(a.a, urow, nT, rev, t0, s1, tid);
     rb.load(a.b, urow, nT, rev, t0, s1, tid);
     if constexpr (!CB) rc.load(a.c, urow, nT, rev, t0, s1, tid);
+    if constexpr (ch) {
+      if (tid < LT) {
+      const int l = t0 + tid;
+      const size_t o = (urow + (size_t)(rev ? nT - 1 - l : l)) * 16;
+      c2v = l >= s1 ? 0.f
+            : !a.c2.p ? 1.f
+            : a.c2.bf16 ? (float)reinterpret_cast<const __bf16*>(a.c2.p)[o]
+                        : reinterpret_cast<const float*>(a.c2.p)[o];
+      }
+    }
   };
+  int par = 0;   // tile parity: the channel's state is h2s[par]
   load_tile(s0);
   for (int t0 = s0; t0 < s1; t0 += LT) {
     const int Lt = s1 - t0 < LT ? s1 - t0 : LT;
@@ -234,6 +256,9 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
     }
     if constexpr (!CB) rc.store(Cs, LDC, tid);
     if (tid < LT) wS[tid] = tid < Lt ? gpow(lam, lgl, Lt - 1 - tid) : 0.f;
+    if constexpr (ch) {
+      if (tid < LT) c2s[tid] = c2v;
+    }
     __syncthreads();
     // the next tile's loads, which stay in flight during the products
     if (t0 + LT < s1) load_tile(t0 + LT);
@@ -322,6 +347,23 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
         Ht[t] = h;
       }
     }
+    if constexpr (ch) {
+      // the channel's state: h2 <- lam^Lt h2 + B^T diag(w) c2, P consecutive
+      // threads per row of h2
+      constexpr int P = NTHR / Da, SQ = LT / P;
+      static_assert(NTHR % Da == 0 && LT % P == 0, "channel state threads");
+      const int k = tid / P, part = tid % P;
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < SQ; ++i) {
+        const int sx = part * SQ + i;
+        v += (float)Bs[sx * L::LDA + k] * (wS[sx] * c2s[sx]);
+      }
+#pragma unroll
+      for (int off = 1; off < P; off *= 2) v += __shfl_xor(v, off, 64);
+      if (part == 0) h2s[par ^ 1][k] = gpow(lam, lgl, Lt) * h2s[par][k] + v;
+    }
+    if constexpr (ch) par ^= 1;
     __syncthreads();
   }
 
@@ -331,6 +373,10 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void la_kernel(LaAr
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) Ho[hbase + (size_t)(16 * t + 4 * lg + j) * Dc + col] = Ht[t][j];
+  }
+  if (ch && a.Hp2) {
+    for (int i = tid; i < Da * 16; i += NTHR)
+      a.Hp2[(size_t)us * Da * 16 + i] = (i & 15) == 0 ? h2s[par][i >> 4] : 0.f;
   }
 }
 
@@ -363,10 +409,10 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int elems) {
   }
 }
 
-template <typename T, int DA, int DC, int MODE, bool SYM, int SRCF, bool ACC = false>
+template <typename T, int DA, int DC, int MODE, bool SYM, int SRCF, bool ACC = false, bool CH = false>
 hipError_t launch_k(int units, const LaArgs& a, hipStream_t s) {
   constexpr int NW = LWaves<DC>::value;
-  hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, SYM, SRCF, ACC>), dim3((unsigned)units * a.nseg),
+  hipLaunchKernelGGL((la_kernel<T, DA, DC, MODE, NW, SYM, SRCF, ACC, CH>), dim3((unsigned)units * a.nseg),
                      dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
@@ -379,6 +425,15 @@ template <typename T, int DA, int DC, int MODE>
 hipError_t launch_dims(int units, const LaArgs& a, hipStream_t s) {
   int srcf = (a.a.bf16 ? 0 : 1) | (a.b.bf16 ? 0 : 2) | (a.c.bf16 ? 0 : 4);
   if (MODE == L_SUMMARY) srcf &= 6;   // a is not read
+  if (a.ch) {   // the scalar channel (summary passes): sources of the MFMA type, plain sums
+    if constexpr (MODE == L_SUMMARY) {
+      constexpr int F = sizeof(T) == 4 ? 6 : 0;
+      if (a.sym || a.reverse || a.b_copy || srcf != F || a.c2.bf16 != (sizeof(T) == 2 ? 1 : 0))
+        return hipErrorInvalidValue;
+      return launch_k<T, DA, DC, MODE, false, F, false, true>(units, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   // c the same tensor as b (k in p = S q and S dp): its tile is staged once
   const bool cb = sizeof(T) == 2 && DA == DC && !a.sym && srcf == 0 && a.c.p == a.b.p &&
                   a.c.bf16 == a.b.bf16;

@@ -205,6 +205,14 @@ struct LaArgs {
   // the state the segment started from, [unit][nseg][Da][Dc] (with Hp null:
   // the segment's own state, the same values a summary pass writes)
   float* Hout = nullptr;
+  // with ch (summary passes only): a second sum with the same a, b and lam
+  // whose value is the scalar in column 0 of the 16-wide rows of c2 (c2.p
+  // null: the unit channel), formed by every thread beside the main one; its
+  // segment states go to Hp2, [unit][nseg][Da][16], column 0 (the rest
+  // written zero).  Not with sym, reverse or b_copy.
+  int ch = 0;
+  LaOperand c2{nullptr, 0};
+  float* Hp2 = nullptr;
 };
 // prefixes_ready: Hp already holds this sum's exclusive segment prefixes (the
 // same b, c and lam as an earlier call), so only the output pass runs; with
