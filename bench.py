@@ -711,11 +711,13 @@ def hla3_bytes_per_token(d, dv, es, chunk):
     segment's tokens."""
     one = 16 * es
     passes = [
-        # local p, u, q.m: read q, k (and v / the unit channel), write the result
-        # (and the S^K, P^KV, m^K summaries, counted with the states below)
-        2 * d * es + d * es, 2 * d * es + dv * es + dv * es, 2 * d * es + one + one,
-        # the other summaries: read the two operands of each state (S^Q: q once)
-        d * es, 2 * d * es, d * es + dv * es, d * es + one, d * es + dv * es, d * es + one,
+        # local p, u, q.m: read q, k (and v), write the result (the unit
+        # channel is formed, not read; the S^K, P^KV, m^K summaries are
+        # counted with the states below)
+        2 * d * es + d * es, 2 * d * es + dv * es + dv * es, 2 * d * es + one,
+        # the other summaries: read the operands of each state (S^Q: q once;
+        # z and r ride on Z's and R's passes, which read q.m besides)
+        d * es, 2 * d * es, d * es + dv * es + one, d * es + dv * es + one,
         # global p, u, q.m: read q, read and rewrite the local p, u, q.m
         d * es + 2 * d * es + 2 * dv * es + 2 * one,
         # num (fp32 out), den16 (fp32 out), den
