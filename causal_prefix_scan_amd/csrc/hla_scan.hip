@@ -366,53 +366,31 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
     xm = tid < D ? a.m[sl * D + tid] : 0.f;
   };
 
+  // The running state after a run's last segment is written only as a total
+  // (step 1's run totals, or the last run's inclusive total when asked for);
+  // otherwise that segment is neither loaded nor combined: the walk's last
+  // step only writes its prefix.
+  const bool keep_last =
+      REDUCE || (run == a.runs - 1 && (a.tS || a.tC || a.tm || a.tG || a.th));
+  const int walk = (keep_last || len == 0) ? len : len - 1;
   int cur = 0;
-  if (len > 0) load(0);
+  if (walk > 0) load(0);
   __syncthreads();
   for (int k = 0; k < len; ++k) {
+    const bool comb = k < walk;   // uniform
     // S rows of segment k to LDS: the A operand of S_B C_A and S_B m_A
+    if (comb) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int e = tid + NT * i;
-      if (e < SV) *reinterpret_cast<f32x4*>(sS + (e / (D / 4)) * LS + 4 * (e % (D / 4))) = xS[i];
-    }
-    __syncthreads();
-    f32x4 cS[DT], cG[RT], cSr[SPT];
-    float ch = xh, cm = xm;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) cS[t] = xC[t];
-#pragma unroll
-    for (int q = 0; q < RT; ++q) cG[q] = xG[q];
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) cSr[i] = xS[i];
-    if (k + 1 < len) load(k + 1);
-
-    // G rows += a S_B C_A (C_A = running C, before this segment); RT
-    // independent accumulator chains (two when RT = 1)
-    f32x4 acc[RT], acc1 = zero4();
-#pragma unroll
-    for (int q = 0; q < RT; ++q) acc[q] = zero4();
-#pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk) {
-      const float bk = Frag<float>::acc_b(Cb, kk);
-#pragma unroll
-      for (int q = 0; q < RT; ++q) {
-        const float ak = sS[(16 * q + lr) * LS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)];
-        if (RT == 1 && (kk & 1)) acc1 = MM<float>::mma(ak, bk, acc1);
-        else acc[q] = MM<float>::mma(ak, bk, acc[q]);
+      for (int i = 0; i < SPT; ++i) {
+        const int e = tid + NT * i;
+        if (e < SV) *reinterpret_cast<f32x4*>(sS + (e / (D / 4)) * LS + 4 * (e % (D / 4))) = xS[i];
       }
     }
-    if (RT == 1) acc[0] += acc1;
-    // h rows += a S_B m_A: PH lanes per row, D / PH products each
-    float hm = 0.f;
-#pragma unroll
-    for (int c = hpart; c < D; c += PH) hm += sS[hrow * LS + c] * sm[cur][c];
-#pragma unroll
-    for (int off = 1; off < PH; off *= 2) hm += __shfl_xor(hm, off, 64);
-
+    __syncthreads();
     if (!REDUCE) {
-      // the segment's own rows become its exclusive prefix: the running state
-      // before this segment (the segment itself was read a step earlier)
+      // the segment's own rows become its exclusive prefix, the running state
+      // before this segment (in place, each thread overwrites the elements it
+      // read a step earlier)
       const size_t sl = (size_t)unit * a.n + k0 + k;
       float* const dG = PO ? a.oG : a.G;
       float* const dS = PO ? a.oS : a.S;
@@ -447,11 +425,46 @@ __global__ __launch_bounds__(64 * (E / 16)) void run_rows_kernel(RunArgs a) {
         if (tid < D) a.m[sl * D + tid] = sm[cur][tid];
       }
     }
+    if (!comb) break;
+    // the segment's S, G and h enter the running state now, its C after the
+    // product, which reads the running C before this segment
 #pragma unroll
-    for (int q = 0; q < RT; ++q) Gb[q] = Gb[q] * al2 + cG[q] + acc[q] * al;
+    for (int i = 0; i < SPT; ++i) Sb[i] = Sb[i] * al + xS[i];
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) Sb[i] = Sb[i] * al + cSr[i];
-    hb = al2 * hb + ch + al * hm;
+    for (int q = 0; q < RT; ++q) Gb[q] = Gb[q] * al2 + xG[q];
+    hb = al2 * hb + xh;
+    const float cm = xm;
+    f32x4 cS[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) cS[t] = xC[t];
+    if (k + 1 < walk) load(k + 1);
+
+    // G rows += a S_B C_A (C_A = running C, before this segment); RT
+    // independent accumulator chains (two when RT = 1)
+    f32x4 acc[RT], acc1 = zero4();
+#pragma unroll
+    for (int q = 0; q < RT; ++q) acc[q] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < D / 4; ++kk) {
+      const float bk = Frag<float>::acc_b(Cb, kk);
+#pragma unroll
+      for (int q = 0; q < RT; ++q) {
+        const float ak = sS[(16 * q + lr) * LS + 16 * (kk >> 2) + 4 * lg4 + (kk & 3)];
+        if (RT == 1 && (kk & 1)) acc1 = MM<float>::mma(ak, bk, acc1);
+        else acc[q] = MM<float>::mma(ak, bk, acc[q]);
+      }
+    }
+    if (RT == 1) acc[0] += acc1;
+    // h rows += a S_B m_A: PH lanes per row, D / PH products each
+    float hm = 0.f;
+#pragma unroll
+    for (int c = hpart; c < D; c += PH) hm += sS[hrow * LS + c] * sm[cur][c];
+#pragma unroll
+    for (int off = 1; off < PH; off *= 2) hm += __shfl_xor(hm, off, 64);
+
+#pragma unroll
+    for (int q = 0; q < RT; ++q) Gb[q] = Gb[q] + acc[q] * al;
+    hb = hb + al * hm;
 #pragma unroll
     for (int t = 0; t < DT; ++t) Cb[t] = Cb[t] * al + cS[t];
     if (tid < D) sm[cur ^ 1][tid] = al * sm[cur][tid] + cm;
