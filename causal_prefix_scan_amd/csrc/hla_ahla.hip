@@ -439,7 +439,9 @@ __global__ __launch_bounds__(64 * NW) void ahla_kernel(AhlaArgs a) {
 // Exclusive scan of the AHLA summaries of each unit, in order, for one
 // 16-column block of (P, E) (block ET: m, n as a single column):
 // prefix_s = run; run <- a run + x_s, E picking up a X_s P_run (a = g^chunk).
-// In place; X is only read.  One workgroup of 4 waves per (unit, block): X_s
+// In place; X is only read.  The state after the last segment is not wanted,
+// so that segment's X is neither loaded nor multiplied.  One workgroup of 4
+// waves per (unit, block): X_s
 // is staged in LDS and X_s P_run runs on fp32 MFMA, each wave owning row tiles
 // of the block; the running E stays in the owning lanes' registers.
 template <int D, int E>
@@ -471,9 +473,10 @@ __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
       if (i < D * D / 4) xr[k] = X[i];
     }
   };
-  if (n > 0) load_x(0);
+  if (n > 1) load_x(0);
   for (int s = 0; s < n; ++s) {
     const size_t sidx = (size_t)unit * n + s;
+    const bool last = s == n - 1;   // uniform
     // this segment's summary entries of the lanes' own rows, read before the
     // products so that their loads overlap them
     float px[RB][4], ex[RB][4];
@@ -484,21 +487,23 @@ __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
       for (int j = 0; j < 4; ++j) {
         const int row = 16 * t + 4 * lg4 + j;
         px[b][j] = ex[b][j] = 0.f;
-        if (t < DT && col_ok) {
+        if (t < DT && col_ok && !last) {
           px[b][j] = mblk ? a.m[sidx * D + row] : a.P[(sidx * D + row) * E + 16 * cb + lr];
           ex[b][j] = mblk ? a.n[sidx * D + row] : a.E[(sidx * D + row) * E + 16 * cb + lr];
         }
       }
     }
+    if (!last) {
 #pragma unroll
-    for (int k = 0; k < NXR; ++k) {
-      const int i = tid + 256 * k;
-      if (i < D * D / 4) {
-        const int r = (4 * i) / D, c = (4 * i) % D;
-        *reinterpret_cast<f32x4*>(Xs + r * LX + c) = xr[k];
+      for (int k = 0; k < NXR; ++k) {
+        const int i = tid + 256 * k;
+        if (i < D * D / 4) {
+          const int r = (4 * i) / D, c = (4 * i) % D;
+          *reinterpret_cast<f32x4*>(Xs + r * LX + c) = xr[k];
+        }
       }
     }
-    if (s + 1 < n) load_x(s + 1);
+    if (s + 2 < n) load_x(s + 1);
     __syncthreads();
     f32x4 cross[RB], pold[RB];
 #pragma unroll
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(256) void ahla_scan_kernel(AhlaArgs a) {
       const int t = wave + 4 * b;
       cross[b] = zero4();
       if (t < DT) {
-        cross[b] = gemm_f32_tile<D>(Xs, LX, Pr, 16, 16 * t, 0, lane, cross[b]);
+        if (!last) cross[b] = gemm_f32_tile<D>(Xs, LX, Pr, 16, 16 * t, 0, lane, cross[b]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) pold[b][j] = Pr[(16 * t + 4 * lg4 + j) * 16 + lr];
       }
