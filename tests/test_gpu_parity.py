@@ -118,6 +118,16 @@ def test_stages_match_oracle(gpu, case):
         assert torch.equal(pre2[key], gs[key]), ("scan_into", key)
         assert torch.equal(tot2[key], total[key]), ("scan_into total", key)
         assert torch.equal(gs0[key], keep[key]), ("scan_into wrote its input", key)
+    # without a total the walk neither loads nor combines a unit's last
+    # segment: the prefixes are the same bits
+    pre3, tot3 = hla.scan_into(gs0, q.shape, dv, chunk, dcode(dtype), g, want_total=False)
+    gs3 = {key: val.clone() for key, val in keep.items()}
+    tot4 = hla.scan(gs3, q.shape, dv, chunk, dcode(dtype), g, want_total=False)
+    torch.cuda.synchronize()
+    assert tot3 is None and tot4 is None
+    for key in FIELDS:
+        assert torch.equal(pre3[key], gs[key]), ("scan_into without a total", key)
+        assert torch.equal(gs3[key], gs[key]), ("scan without a total", key)
 
     o, dn = hla.fwd_output(q, k, v, gs, chunk, g, normalize=False, want_den=True)
     torch.cuda.synchronize()
